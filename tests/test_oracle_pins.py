@@ -1,0 +1,369 @@
+"""Pins for the fp64 oracle, checked against things other than itself.
+
+Each test fixes the oracle to something the pages or the mathematics decide:
+a closed form written as products of the decayed erase steps (not the
+token recurrence), special cases with exact answers, a hand-worked example,
+and invariants (chaining, summary composition, batch and head grouping).
+The definition being pinned is the Gated DeltaNet step with the state stored
+K x V and read after each token's update; the span transition is the product
+of decayed erase steps ("Linear Attention" page, Semantics worth knowing,
+"Summaries").
+"""
+import dataclasses
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Oracle, rel_l2
+from workloads import Problem, custom_problem, make_problem
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers (numpy, independent of the oracle's C code)
+
+def _np(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def _unit_vec(x):
+    return x / np.linalg.norm(x)
+
+
+def closed_form(problem, scale=None):
+    """S_t = P_{t<-0} S_0 + sum_{s<=t} P_{t<-s} beta_s k_s v_s^T, with
+    P_{t<-s} = M_t ... M_{s+1} and M_t = exp(g_t) (I - beta_t k_t k_t^T).
+    Returns o [T, HV, V], final [N, HV, K, V] and transition [N, HV, K, K]
+    (transition = (M_T ... M_1)^T)."""
+    cu = problem.cu_seqlens.tolist()
+    N = len(cu) - 1
+    k = _np(problem.k)
+    v = _np(problem.v)
+    q = _np(problem.q) if problem.q is not None else None
+    g = _np(problem.g)
+    beta = _np(problem.beta)
+    HK, K = k.shape[1], k.shape[2]
+    HV, V = v.shape[1], v.shape[2]
+    sc = K ** -0.5 if scale is None else scale
+    T = k.shape[0]
+    o = np.zeros((T, HV, V))
+    fin = np.zeros((N, HV, K, V))
+    trans = np.zeros((N, HV, K, K))
+    for n in range(N):
+        for h in range(HV):
+            hk = h // (HV // HK)
+            s0 = _np(problem.state[n, h]) if problem.state is not None else np.zeros((K, V))
+            ts = list(range(cu[n], cu[n + 1]))
+            ks = [(_unit_vec(k[t, hk]) if problem.l2norm else k[t, hk]) for t in ts]
+            qs = [((_unit_vec(q[t, hk]) if problem.l2norm else q[t, hk]) if q is not None else None)
+                  for t in ts]
+            Ms = [math.exp(g[t, h]) * (np.eye(K) - beta[t, h] * np.outer(kk, kk))
+                  for t, kk in zip(ts, ks)]
+
+            def prod(hi, lo):  # M_hi ... M_{lo+1} over local indices (1-based hi)
+                P = np.eye(K)
+                for j in range(lo, hi):
+                    P = Ms[j] @ P
+                return P
+
+            S = None
+            for i in range(len(ts)):
+                S = prod(i + 1, 0) @ s0
+                for s in range(i + 1):
+                    S = S + prod(i + 1, s + 1) @ (beta[ts[s], h] * np.outer(ks[s], v[ts[s], h]))
+                if qs[i] is not None:
+                    o[ts[i], h] = sc * S.T @ qs[i]
+            fin[n, h] = S if S is not None else s0
+            trans[n, h] = prod(len(ts), 0).T
+    return o, fin, trans
+
+
+def make(lengths, hk=1, hv=1, dk=4, dv=4, seed=0, state=True, l2norm=True, **kw):
+    return custom_problem(lengths, hk, hv, dk, dv, seed=seed, with_state=state, l2norm=l2norm, **kw)
+
+
+# ----------------------------------------------------------------------------
+# closed form on tiny inputs
+
+@pytest.mark.parametrize("l2norm", [True, False])
+@pytest.mark.parametrize("shape", [((5, 11, 1), 1, 1, 4, 4), ((9, 7), 2, 4, 4, 3), ((16,), 1, 2, 3, 5)])
+def test_closed_form_tiny(shape, l2norm):
+    lengths, hk, hv, dk, dv = shape
+    p = make(lengths, hk, hv, dk, dv, seed=3, l2norm=l2norm)
+    o_ref, s_ref, t_ref = closed_form(p)
+    r = Oracle(p).run_all(want_transition=True)
+    # the oracle's norm adds 1e-6 under the square root and numpy's does not; at
+    # these tiny head dims sum(x^2) can be ~0.1, a relative difference up to ~5e-6
+    tol = 2e-5 if l2norm else 1e-12
+    assert rel_l2(r["o"], o_ref) < tol
+    assert rel_l2(r["state"], s_ref) < tol
+    assert rel_l2(r["transition"], t_ref) < tol
+
+
+def test_closed_form_catches_planted_mistakes():
+    """Non-vacuity: plausible mistakes in the recurrence fail the closed form."""
+    p = make((12,), 1, 1, 4, 4, seed=5)
+    o_ref, s_ref, _ = closed_form(p)
+
+    def recur(variant):
+        k = _np(p.k)[:, 0]
+        k = k / np.linalg.norm(k, axis=1, keepdims=True)
+        q = _np(p.q)[:, 0]
+        q = q / np.linalg.norm(q, axis=1, keepdims=True)
+        v, g, b = _np(p.v)[:, 0], _np(p.g)[:, 0], _np(p.beta)[:, 0]
+        S = _np(p.state[0, 0]).copy()
+        o = []
+        for t in range(12):
+            Sd = math.exp(g[t]) * S
+            if variant == "erase_undecayed":
+                S = Sd + b[t] * np.outer(k[t], v[t] - S.T @ k[t])
+            elif variant == "output_before_update":
+                o.append(0.5 * Sd.T @ q[t])
+                S = Sd + b[t] * np.outer(k[t], v[t] - Sd.T @ k[t])
+                continue
+            elif variant == "write_decayed":
+                S = math.exp(g[t]) * (S + b[t] * np.outer(k[t], v[t] - S.T @ k[t]))
+            else:
+                S = Sd + b[t] * np.outer(k[t], v[t] - Sd.T @ k[t])
+            o.append(0.5 * S.T @ q[t])
+        return np.array(o), S
+
+    o_ok, s_ok = recur("ok")
+    assert rel_l2(o_ok, o_ref[:, 0]) < 1e-12 and rel_l2(s_ok, s_ref[0, 0]) < 1e-12
+    for bad in ("erase_undecayed", "output_before_update", "write_decayed"):
+        o_b, s_b = recur(bad)
+        assert rel_l2(o_b, o_ref[:, 0]) > 1e-3 or rel_l2(s_b, s_ref[0, 0]) > 1e-3, bad
+
+
+# ----------------------------------------------------------------------------
+# special cases with exact answers
+
+def test_beta_zero_is_pure_decay():
+    p = make((7, 13), 2, 2, 8, 6, seed=1)
+    p.beta.zero_()
+    r = Oracle(p).run_all()
+    g = _np(p.g)
+    q = _np(p.q)
+    cu = p.cu_seqlens.tolist()
+    for n in range(2):
+        for h in range(2):
+            s0 = _np(p.state[n, h])
+            gam = np.cumsum(g[cu[n]:cu[n + 1], h])
+            np.testing.assert_allclose(r["state"][n, h], math.exp(gam[-1]) * s0, rtol=1e-12, atol=0)
+            for i, t in enumerate(range(cu[n], cu[n + 1])):
+                qn = _unit_vec(q[t, h])
+                ref = 8 ** -0.5 * math.exp(gam[i]) * s0.T @ qn
+                np.testing.assert_allclose(r["o"][t, h], ref, rtol=2e-6, atol=1e-12)
+
+
+def test_orthonormal_keys_overwrite_exactly():
+    """g = 0, beta = 1, k_t = e_pi(t): row pi(t) of S becomes v_t exactly."""
+    K, V, T = 8, 5, 6
+    perm = [3, 0, 7, 1, 5, 2]
+    p = make((T,), 1, 1, K, V, seed=2, l2norm=False)
+    k = torch.zeros(T, 1, K)
+    for t, j in enumerate(perm):
+        k[t, 0, j] = 1.0
+    p = dataclasses.replace(p, k=k.to(torch.bfloat16), g=torch.zeros(T, 1), beta=torch.ones(T, 1))
+    r = Oracle(p).run_all()
+    s0 = _np(p.state[0, 0])
+    v = _np(p.v)[:, 0]
+    expect = s0.copy()
+    for t, j in enumerate(perm):
+        expect[j] = v[t]
+    np.testing.assert_allclose(r["state"][0, 0], expect, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("scale", [None, 0.37])
+def test_q_equal_k_beta_one_returns_scaled_v(scale):
+    """q_t = k_t, beta = 1, any gate: S_t^T k_t = v_t, so o_t = scale * v_t."""
+    p = make((9, 4), 2, 4, 16, 8, seed=4)
+    p = dataclasses.replace(p, q=p.k.clone(), beta=torch.ones_like(p.beta))
+    r = Oracle(p, scale=scale).run_all()
+    sc = 16 ** -0.5 if scale is None else scale
+    # |k^|^2 = s / (s + 1e-6) rather than 1: an absolute error ~1e-7 * |v|
+    np.testing.assert_allclose(r["o"], sc * _np(p.v), rtol=1e-6, atol=1e-6)
+
+
+def test_l2norm_matches_numpy_norm():
+    """One token from S_0 = 0 with g = 0: S = beta k^ v^T and o = scale (q^.k^) beta v."""
+    p = make((1,), 1, 1, 32, 4, seed=6, state=False)
+    p.g.zero_()
+    r = Oracle(p).run_all()
+    k = _np(p.k)[0, 0]
+    q = _np(p.q)[0, 0]
+    b = float(p.beta[0, 0])
+    kh, qh = k / np.linalg.norm(k), q / np.linalg.norm(q)
+    np.testing.assert_allclose(r["state"][0, 0], b * np.outer(kh, _np(p.v)[0, 0]), rtol=1e-7)
+    np.testing.assert_allclose(r["o"][0, 0], 32 ** -0.5 * b * (qh @ kh) * _np(p.v)[0, 0], rtol=1e-7)
+
+
+def test_golden_worked_example():
+    vals = {}
+    with open(os.path.join(GOLDEN, "worked_example_2tok.txt")) as f:
+        for line in f:
+            if line.startswith("#") or "=" not in line:
+                continue
+            name, rhs = line.split("=", 1)
+            vals[name.strip()] = np.array([float(x) for x in rhs.split()])
+    k = torch.tensor(vals["k"].reshape(2, 1, 2), dtype=torch.bfloat16)
+    v = torch.tensor(vals["v"].reshape(2, 1, 2), dtype=torch.bfloat16)
+    q = torch.tensor(vals["q"].reshape(2, 1, 2), dtype=torch.bfloat16)
+    g = torch.tensor(vals["g"].reshape(2, 1), dtype=torch.float32)
+    beta = torch.tensor(vals["beta"].reshape(2, 1), dtype=torch.float32)
+    cu = torch.tensor([0, 2], dtype=torch.int32)
+    base = Problem("golden", cu, q, k, v, g, beta, None, l2norm=False)
+    r0 = Oracle(base, scale=1.0).run_all(want_transition=True)
+    # fp32 ln(1/2) is not exactly ln(1/2): 1e-7 relative slack
+    np.testing.assert_allclose(r0["o"].ravel(), vals["o_zero_start"], rtol=1e-7, atol=1e-7)
+    np.testing.assert_allclose(r0["state"].ravel(), vals["state_zero_start"], rtol=1e-7, atol=1e-7)
+    np.testing.assert_allclose(r0["transition"].ravel(), vals["transition"], rtol=1e-7, atol=1e-7)
+    ident = torch.eye(2, dtype=torch.float32).reshape(1, 1, 2, 2)
+    r1 = Oracle(dataclasses.replace(base, state=ident), scale=1.0).run_all()
+    np.testing.assert_allclose(r1["o"].ravel(), vals["o_identity_start"], rtol=1e-7, atol=1e-7)
+    np.testing.assert_allclose(r1["state"].ravel(), vals["state_identity_start"], rtol=1e-7, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# invariants
+
+def _contract(s_init, trans):
+    """S_init * transition, contracting the state's key axis: [.., K, V] x [.., K, K] -> [.., K, V]."""
+    return np.einsum("...iv,...ij->...jv", s_init, trans)
+
+
+def test_initial_state_linearity():
+    """final(S0) - final(0) = S0 * transition;  o(S0) - o(0) = scale * (P_t S0)^T q_t."""
+    p = make((40, 23), 2, 2, 8, 8, seed=7, g_div=64.0)
+    with_s = Oracle(p).run_all(want_transition=True)
+    without = Oracle(p, use_initial_state=False).run_all()
+    s0 = _np(p.state)
+    np.testing.assert_allclose(with_s["state"] - without["state"], _contract(s0, with_s["transition"]),
+                               rtol=1e-10, atol=1e-12)
+    # the output difference at the last token of each sequence is scale * transition-mapped S0 read by q
+    q = _np(p.q)
+    cu = p.cu_seqlens.tolist()
+    for n in range(2):
+        t = cu[n + 1] - 1
+        for h in range(2):
+            d = with_s["o"][t, h] - without["o"][t, h]
+            ref = 8 ** -0.5 * _contract(s0[n, h], with_s["transition"][n, h]).T @ _unit_vec(q[t, h])
+            np.testing.assert_allclose(d, ref, rtol=2e-6, atol=1e-12)
+
+
+@pytest.mark.parametrize("split", [64, 37, 1])
+def test_state_round_trip(split):
+    """Chaining final_state -> initial_state over a split equals one pass."""
+    p = make((150,), 2, 4, 8, 6, seed=8, g_div=16.0)
+    whole = Oracle(p).run_all()
+    cut = [0, split, 150]
+    a = Problem("a", torch.tensor(cut[:2], dtype=torch.int32), p.q[:split], p.k[:split], p.v[:split],
+                p.g[:split], p.beta[:split], p.state, l2norm=True)
+    ra = Oracle(a).run_all()
+    b = Problem("b", torch.tensor([0, 150 - split], dtype=torch.int32), p.q[split:], p.k[split:],
+                p.v[split:], p.g[split:], p.beta[split:],
+                torch.tensor(ra["state"], dtype=torch.float32), l2norm=True)
+    rb = Oracle(b).run_all()
+    # the chained state passes through fp32, so allow fp32 rounding of the state
+    assert rel_l2(np.concatenate([ra["o"], rb["o"]]), whole["o"]) < 1e-6
+    assert rel_l2(rb["state"], whole["state"]) < 1e-6
+
+
+def test_summary_composition_slow_decay():
+    """X_0 = S_init; X_{i+1} = X_i * T_i + S_span,i equals the unsplit run."""
+    spans = [48, 64, 17, 90]
+    p = make(spans, 2, 2, 8, 8, seed=9, g_div=256.0, beta_div=4.0)
+    whole = make((sum(spans),), 2, 2, 8, 8, seed=9, g_div=256.0, beta_div=4.0)
+    whole = dataclasses.replace(whole, state=p.state[:1].clone())
+    ref = Oracle(whole).run_all(want_o=False)["state"][0]
+    spans_res = Oracle(p, use_initial_state=False).run_all(want_o=False, want_transition=True)
+    X = _np(p.state[0])
+    for i in range(len(spans)):
+        X = _contract(X, spans_res["transition"][i]) + spans_res["state"][i]
+    np.testing.assert_allclose(X, ref, rtol=1e-10, atol=1e-12)
+    # the transition is far from zero here, and not symmetric, so the check is not vacuous
+    tr = spans_res["transition"]
+    assert np.abs(tr).max() > 0.1
+    assert np.linalg.norm(tr - np.swapaxes(tr, -1, -2)) > 1e-2 * np.linalg.norm(tr)
+    Xwrong = _np(p.state[0])
+    for i in range(len(spans)):
+        Xwrong = _contract(Xwrong, np.swapaxes(spans_res["transition"][i], -1, -2)) + spans_res["state"][i]
+    assert rel_l2(Xwrong, ref) > 1e-3
+
+
+def test_empty_sequence():
+    p = make((5, 0, 3), 1, 2, 4, 4, seed=10)
+    r = Oracle(p).run_all(want_transition=True)
+    np.testing.assert_array_equal(r["state"][1], _np(p.state[1]))
+    np.testing.assert_array_equal(r["transition"][1], np.broadcast_to(np.eye(4), (2, 4, 4)))
+
+
+def test_batch_invariance_bitwise():
+    p = make((13, 30, 2), 1, 2, 8, 8, seed=11)
+    r = Oracle(p).run_all()
+    cu = p.cu_seqlens.tolist()
+    for n in range(3):
+        sl = slice(cu[n], cu[n + 1])
+        alone = Problem("alone", torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32), p.q[sl],
+                        p.k[sl], p.v[sl], p.g[sl], p.beta[sl], p.state[n:n + 1], l2norm=True)
+        ra = Oracle(alone).run_all()
+        np.testing.assert_array_equal(ra["o"], r["o"][sl])
+        np.testing.assert_array_equal(ra["state"][0], r["state"][n])
+
+
+def test_grouped_heads_equal_duplicated_heads():
+    p = make((20, 9), 2, 6, 8, 4, seed=12)
+    r = Oracle(p).run_all(want_transition=True)
+    rep = torch.arange(6) // 3
+    dup = dataclasses.replace(p, q=p.q[:, rep].contiguous(), k=p.k[:, rep].contiguous())
+    rd = Oracle(dup).run_all(want_transition=True)
+    np.testing.assert_array_equal(r["o"], rd["o"])
+    np.testing.assert_array_equal(r["state"], rd["state"])
+    np.testing.assert_array_equal(r["transition"], rd["transition"])
+
+
+def test_sampled_units_equal_full_run():
+    p = make((33, 70, 5), 1, 3, 8, 8, seed=13)
+    o = Oracle(p)
+    full = o.run_all(want_transition=True)
+    units = [(1, 2), (0, 0), (2, 1)]
+    part = o.run_units(units, want_transition=True)
+    cu = p.cu_seqlens.tolist()
+    for (n, h), oo, ss, tt in zip(units, part["o"], part["state"], part["transition"]):
+        np.testing.assert_array_equal(oo, full["o"][cu[n]:cu[n + 1], h])
+        np.testing.assert_array_equal(ss, full["state"][n, h])
+        np.testing.assert_array_equal(tt, full["transition"][n, h])
+
+
+def test_oracle_rejects_bad_arguments():
+    p = make((4,), 1, 1, 4, 4)
+    o = Oracle(p)
+    with pytest.raises(ValueError):
+        o.run_units([(1, 0)])
+    with pytest.raises(ValueError):
+        o.run_units([(0, 1)])
+    # the C entry point checks its own arguments too
+    bad = np.array([5], dtype=np.int32)
+    zero = np.array([0], dtype=np.int32)
+    lib = oracle._load()
+    rc = lib.gdn_oracle_run(oracle.ctypes.byref(o._st), 1, bad.ctypes.data, zero.ctypes.data,
+                            None, None, None, None, 1)
+    assert rc == -2
+
+
+def test_config_vacuity_findings():
+    """Under config 5's gate the span transition underflows to zero and the
+    initial state barely reaches config 3's output; the slow-decay companions
+    exist to make those checks bite.  (Small slices of the configs.)"""
+    g5 = make_problem(1).g  # same gate distribution
+    assert float(g5.double().mean()) < -0.5
+    # an 8192-token span at mean gate -0.8 decays by exp(-6500) = 0 in fp64
+    assert math.exp(-0.8 * 8192) == 0.0
+    p = make((512,), 1, 1, 16, 16, seed=14, g_div=4096.0, beta_div=64.0)
+    tr = Oracle(p, use_initial_state=False).run_all(want_o=False, want_transition=True)["transition"]
+    assert 1e-3 < np.abs(tr).max() < 2.0

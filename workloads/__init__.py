@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for the Gated DeltaNet forward and span summary.
+
+This module only draws random numbers and lays them out. It holds none of the
+method's arithmetic, so both the fp64 oracle and the GPU path may use it.
+
+The shapes and distributions follow the example call on the cuDNN
+"Linear Attention" page (section "Example"): packed THD tensors q, k, v of
+N(0, 1) values stored as bf16, a log-space gate g = -softplus(N(0, 1)) and
+beta = sigmoid(N(0, 1)), both fp32 and laid out [T, heads], and int32
+cu_seqlens.  Initial (start) states are fp32 N(0, 0.1^2).
+
+Draw order is fixed so a seed always gives the same tensors:
+lengths -> q -> k -> v -> g_raw -> beta_raw -> state.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import torch
+
+__all__ = ["Problem", "CONFIGS", "make_problem", "custom_problem", "config_lengths"]
+
+
+@dataclasses.dataclass
+class Problem:
+    """One synthetic problem, all tensors on the CPU unless moved."""
+
+    name: str
+    cu_seqlens: torch.Tensor          # int32 [N + 1]
+    q: Optional[torch.Tensor]         # bf16 [T, HK, K] (None for a summary)
+    k: torch.Tensor                   # bf16 [T, HK, K]
+    v: torch.Tensor                   # bf16 [T, HV, V]
+    g: torch.Tensor                   # fp32 [T, HV], natural-log gate
+    beta: torch.Tensor                # fp32 [T, HV]
+    state: Optional[torch.Tensor]     # fp32 [N, HV, K, V] or None (zero start)
+    l2norm: bool = True
+    summary: bool = False
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.cu_seqlens.numel()) - 1
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.k.shape[0])
+
+    @property
+    def num_qk_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
+    def num_v_heads(self) -> int:
+        return int(self.v.shape[1])
+
+    @property
+    def head_dim_k(self) -> int:
+        return int(self.k.shape[2])
+
+    @property
+    def head_dim_v(self) -> int:
+        return int(self.v.shape[2])
+
+    def lengths(self) -> List[int]:
+        cu = self.cu_seqlens.tolist()
+        return [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+
+    def to(self, device) -> "Problem":
+        def mv(x):
+            return None if x is None else x.to(device)
+        return dataclasses.replace(
+            self, cu_seqlens=mv(self.cu_seqlens), q=mv(self.q), k=mv(self.k), v=mv(self.v),
+            g=mv(self.g), beta=mv(self.beta), state=mv(self.state))
+
+
+# The five workloads.  "lengths" is a list, or "ragged" for the case whose
+# lengths are drawn from the generator.  Companion variants (slow decay: g/4096, beta/64) exist for
+# 3 and 5, because under the plain gate the transition underflows to zero and
+# the initial state barely reaches the output.
+CONFIGS: Dict[int, dict] = {
+    1: dict(name="tiny: T=256, N=1, H=2, K=V=64", lengths=[256], hk=2, hv=2, dk=64, dv=64,
+            state=False, summary=False),
+    2: dict(name="varlen: T=4096, N=3 (1000,1500,1596), H=16, K=V=128",
+            lengths=[1000, 1500, 1596], hk=16, hv=16, dk=128, dv=128, state=False, summary=False),
+    3: dict(name="dense batch: 8 x 4096, HK=4, HV=16, K=V=128, initial state",
+            lengths=[4096] * 8, hk=4, hv=16, dk=128, dv=128, state=True, summary=False),
+    4: dict(name="ragged long context: 64 x U[1,4096] + 65536, H=32, K=V=128",
+            lengths="ragged", hk=32, hv=32, dk=128, dv=128, state=False, summary=False),
+    5: dict(name="span summary: 32 x 8192, H=16, K=V=128, start state",
+            lengths=[8192] * 32, hk=16, hv=16, dk=128, dv=128, state=True, summary=True),
+}
+
+
+def _ragged_lengths(gen: torch.Generator) -> List[int]:
+    lens = torch.randint(1, 4097, (64,), generator=gen).tolist()
+    lens[0] = 1          # a length-1 sequence
+    lens[1] = 64         # exactly one chunk
+    assert any(x % 64 for x in lens)
+    return lens + [65536]
+
+
+def config_lengths(cfg_id: int, seed: Optional[int] = None) -> List[int]:
+    """Sequence lengths of a config (draws only the lengths)."""
+    cfg = CONFIGS[cfg_id]
+    if cfg["lengths"] == "ragged":
+        gen = torch.Generator().manual_seed(cfg_id if seed is None else seed)
+        return _ragged_lengths(gen)
+    return list(cfg["lengths"])
+
+
+def _draw(gen, lengths, hk, hv, dk, dv, with_state, with_q, device):
+    T = int(sum(lengths))
+    N = len(lengths)
+    cu = torch.zeros(N + 1, dtype=torch.int64)
+    if N:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    cu = cu.to(torch.int32)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+
+    q = randn(T, hk, dk).to(torch.bfloat16)
+    k = randn(T, hk, dk).to(torch.bfloat16)
+    v = randn(T, hv, dv).to(torch.bfloat16)
+    g = -torch.nn.functional.softplus(randn(T, hv))
+    beta = torch.sigmoid(randn(T, hv))
+    state = (0.1 * randn(N, hv, dk, dv)) if with_state else None
+    if not with_q:
+        q = None
+    return cu, q, k, v, g, beta, state
+
+
+def make_problem(cfg_id: int, companion: bool = False, seed: Optional[int] = None,
+                 device: str = "cpu") -> Problem:
+    """Inputs of config `cfg_id` (1..5).
+
+    companion=True gives the slow-decay variant (g / 4096, beta / 64, seed
+    100 + id) on which the transition and the initial state are far from zero.
+    `device` is where the random numbers are drawn; the CPU is the default so
+    the oracle and the GPU see the same tensors.
+    """
+    cfg = CONFIGS[cfg_id]
+    if seed is None:
+        seed = (100 + cfg_id) if companion else cfg_id
+    gen = torch.Generator(device=device).manual_seed(seed)
+    if cfg["lengths"] == "ragged":
+        lengths = _ragged_lengths(torch.Generator().manual_seed(seed))
+    else:
+        lengths = list(cfg["lengths"])
+    cu, q, k, v, g, beta, state = _draw(gen, lengths, cfg["hk"], cfg["hv"], cfg["dk"], cfg["dv"],
+                                        cfg["state"], not cfg["summary"], device)
+    if companion:
+        g = g / 4096.0
+        beta = beta / 64.0
+    name = cfg["name"] + (" (slow-decay companion)" if companion else "")
+    return Problem(name=name, cu_seqlens=cu.to(device), q=q, k=k, v=v,
+                   g=g, beta=beta, state=state, l2norm=True, summary=cfg["summary"])
+
+
+def custom_problem(lengths, hk, hv, dk, dv, seed=0, with_state=False, summary=False,
+                   l2norm=True, g_div=1.0, beta_div=1.0, device="cpu") -> Problem:
+    """A problem of arbitrary shape with the same distributions."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    cu, q, k, v, g, beta, state = _draw(gen, list(lengths), hk, hv, dk, dv, with_state,
+                                        not summary, device)
+    return Problem(name=f"custom{tuple(lengths)}", cu_seqlens=cu.to(device), q=q, k=k, v=v, g=g / g_div,
+                   beta=beta / beta_div, state=state, l2norm=l2norm, summary=summary)
