@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked Gated DeltaNet forward on one MI355X.
+
+One step = one la_gdn_fwd call (scheduler, prologue, intra-chunk and
+inter-chunk kernels) over the varlen workload T = 4096, cu_seqlens =
+[0, 1000, 2500, 4096], H = 16, K = V = 128, bf16, in-kernel q/k L2 norm,
+zero initial state, output o and final states (the example call of the cuDNN
+"Linear Attention" page).  Inputs are seeded synthetic tensors already
+resident in HBM.  Steps rotate over several copies of the inputs, outputs and
+workspaces (more bytes than the 256 MiB Infinity Cache holds), so each step
+reads its operands from HBM rather than from the cache.
+
+Prints one JSON line: tokens/s of the whole job, the roofline of the dominant
+kernel (k_inter) from per-kernel HIP-event timing on the launch stream, and
+the fp64 CPU oracle timed on the host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd tokens/s (H=16,K=V=128,bf16) + % of MFMA/HBM roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+CHUNK = 64
+
+
+def algorithmic_counts(lengths, HK, HV, K, V, with_init, with_final):
+    """Bytes and flops the method must move and compute (intermediates excluded).
+
+    bytes: q, k (bf16, per qk-head), v, o (bf16, per v-head), g, beta (fp32 per
+    v-head), plus the fp32 states read/written.  flops: per qk-head token the
+    two chunk Gram products (k k^T and q k^T, 2 * 2 C K); per v-head token the
+    W / U~ products, the masked P U_new, W S, Q S and the state update
+    (2 (3 K V + C (K + 2 V)))."""
+    T = sum(lengths)
+    N = len(lengths)
+    by = T * (2 * HK * K * 2 + 2 * HV * V * 2 + 2 * HV * 4) + N * HV * K * V * 4 * (int(with_init) + int(with_final))
+    fl = T * (HK * 2 * 2 * CHUNK * K + HV * 2 * (3 * K * V + CHUNK * (K + 2 * V)))
+    # bytes the inter-chunk kernel must move by the definition of its step:
+    # q, k, v read, o written, states read/written (g and beta are read earlier)
+    inter_by = T * (2 * HK * K * 2 + 2 * HV * V * 2) + N * HV * K * V * 4 * (int(with_init) + int(with_final))
+    return by, fl, inter_by
+
+
+def cpu_baseline(problem):
+    """The fp64 oracle over the whole workload (all 48 units), on the host cores."""
+    import oracle
+    o = oracle.Oracle(problem)
+    nt = oracle.default_threads()
+    o.run_units([(0, 0)], num_threads=1)   # load the library outside the timing
+    t0 = time.perf_counter()
+    o.run_all(num_threads=nt)
+    dt = time.perf_counter() - t0
+    return {"value": problem.total_tokens / dt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"the whole workload: all {problem.num_seqs * problem.num_v_heads} (sequence, head) "
+                      f"units, {problem.total_tokens} tokens, fp64 token recurrence, {dt:.2f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="input/output sets rotated over (cache-cold steps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences and heads are independent, so more GPUs would shard them with no exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import gated_delta_rule_50_amd as la
+    from workloads import make_problem
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    la.load_library()
+
+    prob = make_problem(2)
+    lengths = prob.lengths()
+    T, HK, HV, K, V = prob.total_tokens, prob.num_qk_heads, prob.num_v_heads, prob.head_dim_k, prob.head_dim_v
+    N = prob.num_seqs
+
+    sets = []
+    for _ in range(max(1, args.copies)):
+        g = prob.to(dev)
+        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=dev)
+        fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
+        desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out)
+        ws = la.alloc_workspace(desc, False, dev)
+        sets.append((g, out, fin, ws))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        g, out, fin, ws = sets[i % len(sets)]
+        la.la_gdn_fwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=None, out=out,
+                      final_state=fin, l2norm=True, workspace=ws, stream=stream)
+
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if la.la_gdn_device_status(sets[0][3]) != la.LA_DEVICE_OK:
+        print("device status reports malformed cu_seqlens", file=sys.stderr)
+        return 1
+
+    # timed region, with per-kernel HIP events recorded on the launch stream
+    la.la_gdn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = {}
+    for kid in range(la.LA_KERNEL_COUNT):
+        ms, n = la.la_gdn_profile_read(kid)
+        kern[la.la_gdn_kernel_name(kid)] = {"avg_us": 1e3 * ms / max(n, 1), "launches": n}
+    la.la_gdn_profile_enable(False)
+
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = T * args.steps / elapsed
+
+    by, fl, inter_by = algorithmic_counts(lengths, HK, HV, K, V, with_init=False, with_final=True)
+    inter_us = kern["k_inter"]["avg_us"]
+    achieved = inter_by / (inter_us * 1e-6) / 1e9
+    step_s = ms_per_step * 1e-3
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "varlen GDN fwd, T=4096, cu_seqlens=[0,1000,2500,4096], H=16, K=V=128, "
+                               "in-kernel q/k L2 norm, zero initial state, o + final state",
+                   "T": T, "N": N, "HK": HK, "HV": HV, "K": K, "V": V, "copies_rotated": len(sets),
+                   "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "k_inter", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": inter_by, "avg_launch_us": inter_us},
+        "path": {"algorithmic_bytes": by, "algorithmic_flops": fl,
+                 "hbm_frac": by / step_s / (HBM_PEAK_GBS * 1e9),
+                 "mfma_frac": fl / step_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                 "kernels": kern},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(prob)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,410 @@
+// C-ABI layer of la_gdn: argument validation, workspace carving, per-kernel
+// timing hooks.  Every check here runs before any HIP call, so a rejected call
+// touches neither the device nor any output.
+//
+// The validation rules mirror the cuDNN "Linear Attention" page ("Layout":
+// rank-3 THD views with a contiguous innermost axis; "Engines": unsupported
+// head dims are declined with an error) and the alignment contract of the
+// 128-bit loads named in the cudnn-frontend PR "Further reduce FROST LA CPU
+// overhead + fully support all L2norm, beta, gate fusion" (review of the state
+// downcast and l2norm launchers: 16-byte base pointers, outer strides that keep
+// 16-byte alignment).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "la_gdn.h"
+#include "la_gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+la_status fail(la_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Descriptor checks shared by both calls and by the workspace query.
+la_status check_desc(const la_gdn_desc *d)
+{
+    if (!d) return fail(LA_ERR_INVALID_ARGUMENT, "desc is NULL");
+    if (d->num_seqs < 0) return fail(LA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0, got %d", d->num_seqs);
+    if (d->total_tokens < 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "total_tokens must be >= 0, got %lld", (long long)d->total_tokens);
+    if (d->total_tokens > INT32_MAX - 64)
+        return fail(LA_ERR_UNSUPPORTED, "total_tokens %lld exceeds the int32 token index range",
+                    (long long)d->total_tokens);
+    if (d->num_qk_heads < 1) return fail(LA_ERR_INVALID_ARGUMENT, "num_qk_heads must be >= 1, got %d", d->num_qk_heads);
+    if (d->num_v_heads < 1) return fail(LA_ERR_INVALID_ARGUMENT, "num_v_heads must be >= 1, got %d", d->num_v_heads);
+    if (d->num_v_heads % d->num_qk_heads != 0)
+        return fail(LA_ERR_UNSUPPORTED, "num_v_heads (%d) must be a multiple of num_qk_heads (%d)",
+                    d->num_v_heads, d->num_qk_heads);
+    if (d->head_dim_k != 64 && d->head_dim_k != 128)
+        return fail(LA_ERR_UNSUPPORTED, "head_dim_k must be 64 or 128, got %d", d->head_dim_k);
+    if (d->head_dim_v != 64 && d->head_dim_v != 128)
+        return fail(LA_ERR_UNSUPPORTED, "head_dim_v must be 64 or 128, got %d", d->head_dim_v);
+    const int64_t max_chunks = (d->total_tokens + 63) / 64 + d->num_seqs;
+    if (max_chunks > INT32_MAX / 2)
+        return fail(LA_ERR_UNSUPPORTED, "too many chunks (%lld)", (long long)max_chunks);
+    const int64_t units = (int64_t)d->num_seqs * d->num_v_heads * 16;
+    if (units > INT32_MAX)
+        return fail(LA_ERR_UNSUPPORTED, "num_seqs * num_v_heads too large (%lld)", (long long)units / 16);
+    return LA_OK;
+}
+
+// A bf16 [T, heads, dim] operand: 16-byte base, unit innermost stride (implied),
+// outer strides multiples of 8 elements and large enough not to overlap rows.
+la_status check_thd(const char *name, const void *ptr, int64_t st_t, int64_t st_h, int heads, int dim,
+                    int64_t T)
+{
+    if (!ptr) return fail(LA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (!aligned16(ptr)) return fail(LA_ERR_INVALID_ARGUMENT, "%s base pointer is not 16-byte aligned", name);
+    if (st_h % 8 != 0 || st_t % 8 != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT,
+                    "%s strides (t=%lld, h=%lld) must be multiples of 8 elements (16 bytes)", name,
+                    (long long)st_t, (long long)st_h);
+    if (heads > 1 && st_h < dim)
+        return fail(LA_ERR_INVALID_ARGUMENT, "%s head stride %lld is smaller than the head dim %d", name,
+                    (long long)st_h, dim);
+    if (T > 1 && st_t < (int64_t)(heads - 1) * st_h + dim)
+        return fail(LA_ERR_INVALID_ARGUMENT, "%s token stride %lld overlaps its heads", name, (long long)st_t);
+    return LA_OK;
+}
+
+la_status check_rows(const char *name, const void *ptr, int64_t st_t, int heads, int64_t T)
+{
+    if (!ptr) return fail(LA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (!aligned4(ptr)) return fail(LA_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", name);
+    if (T > 1 && st_t < heads)
+        return fail(LA_ERR_INVALID_ARGUMENT, "%s token stride %lld is smaller than num_v_heads %d", name,
+                    (long long)st_t, heads);
+    return LA_OK;
+}
+
+la_status check_f32(const char *name, const void *ptr, bool required)
+{
+    if (!ptr) return required ? fail(LA_ERR_INVALID_ARGUMENT, "%s is NULL", name) : LA_OK;
+    if (!aligned4(ptr)) return fail(LA_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", name);
+    return LA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// per-kernel timing
+
+struct Profiler {
+    std::mutex mu;
+    bool enabled = false;
+    struct Pending {
+        int id;
+        hipEvent_t a, b;
+    };
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> free_events;
+    hipEvent_t open[LA_KERNEL_COUNT] = {};
+    double total_ms[LA_KERNEL_COUNT] = {};
+    int64_t launches[LA_KERNEL_COUNT] = {};
+    hipError_t err = hipSuccess;
+
+    hipEvent_t get()
+    {
+        if (!free_events.empty()) {
+            hipEvent_t e = free_events.back();
+            free_events.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) err = r;
+        return e;
+    }
+};
+
+Profiler &profiler()
+{
+    static Profiler p;
+    return p;
+}
+
+void prof_before(int id, hipStream_t s, void *)
+{
+    Profiler &P = profiler();
+    std::lock_guard<std::mutex> g(P.mu);
+    hipEvent_t e = P.get();
+    if (!e) return;
+    const hipError_t r = hipEventRecord(e, s);
+    if (r != hipSuccess) P.err = r;
+    P.open[id] = e;
+}
+
+void prof_after(int id, hipStream_t s, void *)
+{
+    Profiler &P = profiler();
+    std::lock_guard<std::mutex> g(P.mu);
+    if (!P.open[id]) return;
+    hipEvent_t e = P.get();
+    if (!e) return;
+    const hipError_t r = hipEventRecord(e, s);
+    if (r != hipSuccess) P.err = r;
+    P.pending.push_back({id, P.open[id], e});
+    P.open[id] = nullptr;
+}
+
+const la::LaunchHook *current_hook()
+{
+    static const la::LaunchHook hook = {prof_before, prof_after, nullptr};
+    Profiler &P = profiler();
+    std::lock_guard<std::mutex> g(P.mu);
+    return P.enabled ? &hook : nullptr;
+}
+
+la::Prob make_prob(const la_gdn_desc *d, int l2norm)
+{
+    la::Prob p{};
+    p.N = d->num_seqs;
+    p.T = d->total_tokens;
+    p.HK = d->num_qk_heads;
+    p.HV = d->num_v_heads;
+    p.K = d->head_dim_k;
+    p.V = d->head_dim_v;
+    p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim_k);
+    p.l2norm = l2norm ? 1 : 0;
+    p.max_chunks = (int32_t)((d->total_tokens + 63) / 64 + d->num_seqs);
+    p.qst = d->q_stride_t;
+    p.qsh = d->q_stride_h;
+    p.kst = d->k_stride_t;
+    p.ksh = d->k_stride_h;
+    p.vst = d->v_stride_t;
+    p.vsh = d->v_stride_h;
+    p.ost = d->o_stride_t;
+    p.osh = d->o_stride_h;
+    p.gst = d->g_stride_t;
+    p.bst = d->beta_stride_t;
+    return p;
+}
+
+la_status launch(const la::Prob &p, void *workspace, size_t workspace_bytes, bool summary, hipStream_t stream)
+{
+    const la::WsLayout L = la::workspace_layout(p.N, p.T, p.HK, p.HV, p.K, p.V, summary);
+    if (p.N == 0) return LA_OK;  // nothing to compute and nothing to write
+    if (!workspace) return fail(LA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.total)
+        return fail(LA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+    const la::Ws w = la::carve_workspace(workspace, L, summary);
+    const hipError_t e = la::run_pipeline(p, w, summary, stream, current_hook());
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
+}  // namespace
+
+namespace la {
+
+WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V, bool summary)
+{
+    (void)V;
+    WsLayout L{};
+    const int64_t max_chunks = (T + 63) / 64 + N;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    L.hdr = take(256);
+    L.seq_info = take(sizeof(int4) * (size_t)N);
+    L.chunks = take(sizeof(int4) * (size_t)max_chunks);
+    L.order = take(sizeof(int32_t) * (size_t)N);
+    L.rq = take(summary ? 0 : sizeof(float) * (size_t)(T * HK));
+    L.rk = take(sizeof(float) * (size_t)(T * HK));
+    L.gam = take(sizeof(float) * (size_t)(T * HV));
+    L.W = take(2 * (size_t)(HV * T * K));
+    L.TU = take(2 * (size_t)(HV * T * 128));
+    L.P = take(summary ? 0 : 2 * (size_t)(HV * T * 64));
+    L.total = off;
+    return L;
+}
+
+Ws carve_workspace(void *base, const WsLayout &L, bool summary)
+{
+    char *b = static_cast<char *>(base);
+    Ws w{};
+    w.hdr = reinterpret_cast<int32_t *>(b + L.hdr);
+    w.seq_info = reinterpret_cast<int4 *>(b + L.seq_info);
+    w.chunks = reinterpret_cast<int4 *>(b + L.chunks);
+    w.order = reinterpret_cast<int32_t *>(b + L.order);
+    w.rq = summary ? nullptr : reinterpret_cast<float *>(b + L.rq);
+    w.rk = reinterpret_cast<float *>(b + L.rk);
+    w.gam = reinterpret_cast<float *>(b + L.gam);
+    w.W = reinterpret_cast<__bf16 *>(b + L.W);
+    w.TU = reinterpret_cast<__bf16 *>(b + L.TU);
+    w.P = summary ? nullptr : reinterpret_cast<__bf16 *>(b + L.P);
+    return w;
+}
+
+}  // namespace la
+
+extern "C" {
+
+size_t la_gdn_workspace_bytes(const la_gdn_desc *desc, int is_summary)
+{
+    if (check_desc(desc) != LA_OK) return 0;
+    return la::workspace_layout(desc->num_seqs, desc->total_tokens, desc->num_qk_heads, desc->num_v_heads,
+                                desc->head_dim_k, desc->head_dim_v, is_summary != 0)
+        .total;
+}
+
+la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
+                     float *final_state, int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    g_error.clear();
+    la_status st = check_desc(desc);
+    if (st != LA_OK) return st;
+    const la_gdn_desc &d = *desc;
+    const int64_t T = d.total_tokens;
+    if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
+    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
+    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
+    if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
+    if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if ((st = check_rows("beta", beta, d.beta_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+    if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((st = check_f32("initial_state", initial_state, false)) != LA_OK) return st;
+    if ((st = check_f32("final_state", final_state, false)) != LA_OK) return st;
+
+    la::Prob p = make_prob(desc, l2norm);
+    p.q = static_cast<const __bf16 *>(q);
+    p.k = static_cast<const __bf16 *>(k);
+    p.v = static_cast<const __bf16 *>(v);
+    p.g = g;
+    p.beta = beta;
+    p.cu = cu_seqlens;
+    p.s0 = initial_state;
+    p.o = static_cast<__bf16 *>(out);
+    p.sT = final_state;
+    p.trans = nullptr;
+    return launch(p, workspace, workspace_bytes, false, stream);
+}
+
+la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, const float *g, const float *beta,
+                         const int32_t *cu_seqlens, const float *start_state, float *end_state, float *transition,
+                         int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    g_error.clear();
+    la_status st = check_desc(desc);
+    if (st != LA_OK) return st;
+    const la_gdn_desc &d = *desc;
+    const int64_t T = d.total_tokens;
+    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
+    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
+    if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if ((st = check_rows("beta", beta, d.beta_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+    if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((st = check_f32("start_state", start_state, false)) != LA_OK) return st;
+    if ((st = check_f32("end_state", end_state, true)) != LA_OK) return st;
+    if ((st = check_f32("transition", transition, true)) != LA_OK) return st;
+
+    la::Prob p = make_prob(desc, l2norm);
+    p.q = nullptr;
+    p.k = static_cast<const __bf16 *>(k);
+    p.v = static_cast<const __bf16 *>(v);
+    p.g = g;
+    p.beta = beta;
+    p.cu = cu_seqlens;
+    p.s0 = start_state;
+    p.o = nullptr;
+    p.sT = end_state;
+    p.trans = transition;
+    return launch(p, workspace, workspace_bytes, true, stream);
+}
+
+int32_t la_gdn_device_status(const void *workspace, hipStream_t stream)
+{
+    if (!workspace) {
+        fail(LA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+        return -1;
+    }
+    int32_t h = -1;
+    hipError_t e = hipMemcpyAsync(&h, workspace, sizeof h, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        fail(LA_ERR_HIP, "status read failed: %s", hipGetErrorString(e));
+        return -1;
+    }
+    return h;
+}
+
+const char *la_last_error_message(void) { return g_error.c_str(); }
+
+la_status la_gdn_profile_enable(int enable)
+{
+    Profiler &P = profiler();
+    std::lock_guard<std::mutex> g(P.mu);
+    for (auto &pd : P.pending) {
+        P.free_events.push_back(pd.a);
+        P.free_events.push_back(pd.b);
+    }
+    P.pending.clear();
+    for (int i = 0; i < LA_KERNEL_COUNT; ++i) {
+        P.total_ms[i] = 0.0;
+        P.launches[i] = 0;
+        P.open[i] = nullptr;
+    }
+    P.err = hipSuccess;
+    P.enabled = enable != 0;
+    return LA_OK;
+}
+
+la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *launches)
+{
+    if (kernel_id < 0 || kernel_id >= LA_KERNEL_COUNT)
+        return fail(LA_ERR_INVALID_ARGUMENT, "kernel_id %d out of range", kernel_id);
+    if (!total_ms || !launches) return fail(LA_ERR_INVALID_ARGUMENT, "output pointer is NULL");
+    Profiler &P = profiler();
+    std::lock_guard<std::mutex> g(P.mu);
+    for (auto &pd : P.pending) {
+        hipError_t e = hipEventSynchronize(pd.b);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, pd.a, pd.b);
+        if (e != hipSuccess) return fail(LA_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
+        P.total_ms[pd.id] += ms;
+        P.launches[pd.id] += 1;
+        P.free_events.push_back(pd.a);
+        P.free_events.push_back(pd.b);
+    }
+    P.pending.clear();
+    if (P.err != hipSuccess) return fail(LA_ERR_HIP, "event record failed: %s", hipGetErrorString(P.err));
+    *total_ms = P.total_ms[kernel_id];
+    *launches = P.launches[kernel_id];
+    return LA_OK;
+}
+
+const char *la_gdn_kernel_name(int32_t kernel_id)
+{
+    static const char *names[LA_KERNEL_COUNT] = {"k_sched", "k_prologue", "k_intra", "k_inter"};
+    return (kernel_id >= 0 && kernel_id < LA_KERNEL_COUNT) ? names[kernel_id] : "";
+}
+
+}  // extern "C"

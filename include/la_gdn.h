@@ -1,0 +1,158 @@
+/*
+ * la_gdn — chunked Gated DeltaNet forward and span summary for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named "device" is device memory on the current
+ * HIP device; host pointers are named as such.  The caller allocates and frees
+ * every buffer, including the workspace, and owns the stream.  The library
+ * keeps no pointer after a call returns, allocates no device memory and never
+ * synchronises the host with the device (except la_gdn_device_status and
+ * la_gdn_profile_read, which exist to do exactly that).  All kernels are
+ * enqueued on the caller's stream, so the two compute calls may be captured
+ * into a HIP graph.
+ *
+ * Problem ("Linear Attention" page of the cuDNN docs: opening paragraph,
+ * "Layout", "Semantics worth knowing", "Example").  For each sequence n of a
+ * packed batch and each value head h the recurrent K x V state S evolves over
+ * the sequence's tokens t as
+ *       S <- exp(g_t) S;   S <- S + beta_t k_t (v_t - S^T k_t)^T;   o_t = scale S^T q_t
+ * (the Gated DeltaNet step), with q and k optionally L2-normalised
+ * (x / sqrt(sum x^2 + 1e-6)) before use and scale applied after the norm.
+ * Value head h reads q/k head h / (HV / HK).  Tokens are grouped in chunks of
+ * 64 that restart at every sequence start, so each sequence's result does not
+ * depend on the rest of the batch (the page's "batch_invariant" item), bit
+ * for bit.
+ *
+ * Layouts (the page's "Layout" section: packed THD, strided views with a
+ * contiguous innermost axis):
+ *   q, k        bf16 [T, HK, K]   strides (q|k)_stride_t, (q|k)_stride_h in elements, innermost 1
+ *   v, out      bf16 [T, HV, V]   strides (v|o)_stride_t, (v|o)_stride_h, innermost 1
+ *   g, beta     fp32 [T, HV]      stride g_stride_t / beta_stride_t, innermost 1; g is the
+ *                                 natural-log gate (decay exp(g) per token)
+ *   cu_seqlens  int32 [N + 1]     0 = cu[0] <= cu[1] <= ... <= cu[N] = T
+ *   states      fp32 [N, HV, K, V] contiguous
+ *   transition  fp32 [N, HV, K, K] contiguous
+ * Alignment: q, k, v, out base pointers 16-byte aligned and their outer strides
+ * multiples of 8 elements (the library issues 128-bit loads and stores);
+ * g, beta, states and transition 4-byte aligned.
+ *
+ * Errors: host-side checks run before any launch and leave every output
+ * untouched; la_last_error_message() names the offending argument.  A
+ * malformed cu_seqlens can only be seen on the device: the first kernel
+ * detects it, no kernel then writes any output, and la_gdn_device_status()
+ * reports LA_DEVICE_BAD_CU_SEQLENS.
+ */
+#ifndef LA_GDN_H
+#define LA_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad stride or size */
+    LA_ERR_UNSUPPORTED = 2,        /* a decline: head dims outside {64, 128}, HV % HK != 0 */
+    LA_ERR_WORKSPACE_TOO_SMALL = 3,
+    LA_ERR_HIP = 4                 /* a HIP runtime call failed */
+} la_status;
+
+/* Device status bits written by the kernels into the workspace. */
+#define LA_DEVICE_OK 0
+#define LA_DEVICE_BAD_CU_SEQLENS 1
+
+typedef struct {
+    int32_t num_seqs;        /* N >= 0; cu_seqlens has N + 1 entries */
+    int64_t total_tokens;    /* T >= 0; must equal cu_seqlens[N] (checked on the device) */
+    int32_t num_qk_heads;    /* HK >= 1 */
+    int32_t num_v_heads;     /* HV >= 1, a multiple of HK; output heads = HV */
+    int32_t head_dim_k;      /* K in {64, 128} */
+    int32_t head_dim_v;      /* V in {64, 128} */
+    float scale;             /* multiplies the (normalised) q; <= 0 means K^-1/2 */
+    int64_t q_stride_t, q_stride_h;   /* elements */
+    int64_t k_stride_t, k_stride_h;
+    int64_t v_stride_t, v_stride_h;
+    int64_t o_stride_t, o_stride_h;
+    int64_t g_stride_t, beta_stride_t;
+} la_gdn_desc;
+
+/*
+ * Workspace bytes needed by la_gdn_fwd (is_summary = 0) or la_gdn_summary
+ * (is_summary = 1) for this descriptor.  Depends only on N, T, HK, HV, K, V.
+ * Returns 0 for an invalid descriptor (see la_last_error_message).
+ */
+size_t la_gdn_workspace_bytes(const la_gdn_desc *desc, int is_summary);
+
+/*
+ * Gated DeltaNet forward ("Linear Attention" page, "Example" and "States and
+ * checkpoints": output_final_state, use_qk_l2norm_in_kernel).
+ *   q, k, v        device, bf16, layouts above
+ *   g, beta        device, fp32 [T, HV]
+ *   cu_seqlens     device, int32 [N + 1]
+ *   initial_state  device, fp32 [N, HV, K, V], or NULL for zeros
+ *   out            device, bf16 [T, HV, V] (written)
+ *   final_state    device, fp32 [N, HV, K, V] (written), or NULL to skip
+ *   l2norm         nonzero: L2-normalise q and k rows in the kernels
+ *   workspace      device, at least la_gdn_workspace_bytes(desc, 0) bytes, 256-byte aligned;
+ *                  its contents need no initialisation and are overwritten
+ *   stream         HIP stream the kernels are enqueued on
+ * An empty sequence (cu[n] == cu[n+1]) gets final = initial (or zeros).
+ * N = 0 launches nothing.
+ */
+la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, const int32_t *cu_seqlens,
+                     const float *initial_state, void *out, float *final_state, int l2norm,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Span summary ("Linear Attention" page, "Summaries"): for every sequence
+ * (span) and value head, the end state reached from start_state and the fp32
+ * K x K transition, the transpose of the product of the span's decayed erase
+ * steps P = M_T ... M_1 with M_t = exp(g_t)(I - beta_t k_t k_t^T), so that
+ *     end_state[j][v] = sum_i start_state[i][v] * transition[i][j] + S_span[j][v]
+ * where S_span is the end state from a zero start.  q is not used; the q
+ * strides of desc are ignored and o strides likewise.
+ *   start_state  device, fp32 [N, HV, K, V], or NULL for zeros
+ *   end_state    device, fp32 [N, HV, K, V] (written)
+ *   transition   device, fp32 [N, HV, K, K] (written)
+ * An empty span gets end = start (or zeros) and transition = I.
+ */
+la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
+                         const float *beta, const int32_t *cu_seqlens, const float *start_state,
+                         float *end_state, float *transition, int l2norm, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Reads the status word the last call on this workspace left (LA_DEVICE_*
+ * bits).  Synchronises the stream.  Returns -1 if the read itself failed.
+ */
+int32_t la_gdn_device_status(const void *workspace, hipStream_t stream);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *la_last_error_message(void);
+
+/*
+ * Optional per-kernel timing with HIP events recorded on the caller's stream
+ * around each launch.  Off by default; la_gdn_profile_enable(1) turns it on
+ * for the calling process and clears the totals.  la_gdn_profile_read waits
+ * for the recorded events and returns the summed milliseconds and the launch
+ * count of one kernel (ids below).
+ */
+#define LA_KERNEL_SCHED 0
+#define LA_KERNEL_PROLOGUE 1
+#define LA_KERNEL_INTRA 2
+#define LA_KERNEL_INTER 3
+#define LA_KERNEL_COUNT 4
+la_status la_gdn_profile_enable(int enable);
+la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *launches);
+const char *la_gdn_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_GDN_H */

@@ -1,0 +1,53 @@
+"""Shared helpers of the GPU tests: run the HIP path on a workloads.Problem
+through the C ABI, and compare with the fp64 oracle."""
+import dataclasses
+import sys
+
+import numpy as np
+import torch
+
+import gated_delta_rule_50_amd as la
+from oracle import Oracle, rel_l2
+
+TOL_O = 1e-2       # bf16 output, rel-L2
+TOL_STATE = 5e-3   # fp32 final / end state and transition, rel-L2
+
+
+def note(msg: str):
+    """Names the case on stdout before a GPU step (flushed)."""
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def gpu_fwd(p, dev="cuda", initial_state=True, scale=None, **kw):
+    g = p.to(dev)
+    s0 = g.state if initial_state else None
+    out, fin = la.la_gdn_fwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=s0,
+                             l2norm=p.l2norm, scale=scale, **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def gpu_summary(p, dev="cuda", start_state=True, **kw):
+    g = p.to(dev)
+    s0 = g.state if start_state else None
+    end, tr = la.la_gdn_summary(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=s0,
+                                l2norm=p.l2norm, **kw)
+    torch.cuda.synchronize()
+    return end, tr
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_fwd_full(p, tol_o=TOL_O, tol_s=TOL_STATE, initial_state=True):
+    """Whole-tensor rel-L2 of o and final state against the oracle."""
+    note(f"fwd full: {p.name} T={p.total_tokens} N={p.num_seqs}")
+    out, fin = gpu_fwd(p, initial_state=initial_state)
+    ref = Oracle(p, use_initial_state=initial_state).run_all()
+    eo = rel_l2(f64(out), ref["o"])
+    es = rel_l2(f64(fin), ref["state"])
+    assert np.isfinite(eo) and np.isfinite(es)
+    assert eo <= tol_o, f"o rel-L2 {eo:.3e} > {tol_o}"
+    assert es <= tol_s, f"final state rel-L2 {es:.3e} > {tol_s}"
+    return out, fin, ref, eo, es

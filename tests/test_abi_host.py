@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device.
+
+No call here reaches a HIP API: every argument set is invalid, and the checks
+run first (the header states that a rejected call launches nothing).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gated_delta_rule_50_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        from gated_delta_rule_50_amd import build
+        build.build()
+    return la.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(la.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # exported with C linkage (no mangling), checked with nm when available
+    import shutil
+    import subprocess
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True).stdout
+        syms = set(line.split()[-1] for line in out.splitlines() if line.strip())
+        for name in declared_functions():
+            assert name in syms, name
+
+
+def _desc(N=2, T=100, HK=2, HV=4, K=128, V=128, **over):
+    d = la.Desc(N, T, HK, HV, K, V, 0.0,
+                HK * K, K, HK * K, K, HV * V, V, HV * V, V, HV, HV)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_workspace_bytes(lib):
+    d = _desc()
+    fwd = la.la_gdn_workspace_bytes(d, False)
+    summ = la.la_gdn_workspace_bytes(d, True)
+    assert fwd > 0 and summ > 0
+    # intermediates: W (K), T hi|lo (128), P (64) bf16 per (token, v-head) plus small tables
+    assert fwd >= 2 * 100 * 4 * (128 + 128 + 64)
+    assert summ < fwd                      # no P, no q norms
+    bigger = la.la_gdn_workspace_bytes(_desc(T=1000), False)
+    assert bigger > fwd
+    assert la.la_gdn_workspace_bytes(_desc(N=0, T=0), False) > 0
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("head_dim_k", 96, la.LA_ERR_UNSUPPORTED, "head_dim_k"),
+    ("head_dim_v", 256, la.LA_ERR_UNSUPPORTED, "head_dim_v"),
+    ("num_v_heads", 3, la.LA_ERR_UNSUPPORTED, "multiple"),
+    ("num_qk_heads", 0, la.LA_ERR_INVALID_ARGUMENT, "num_qk_heads"),
+    ("num_seqs", -1, la.LA_ERR_INVALID_ARGUMENT, "num_seqs"),
+    ("total_tokens", -5, la.LA_ERR_INVALID_ARGUMENT, "total_tokens"),
+])
+def test_descriptor_declines(lib, field, value, status, needle):
+    d = _desc(**{field: value})
+    assert lib.la_gdn_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert needle in la.la_last_error_message()
+    A = 1 << 20   # a fake, aligned address: never dereferenced because the call is rejected first
+    rc = lib.la_gdn_fwd(ctypes.byref(d), A, A, A, A, A, A, None, A, A, 1, A, 1 << 30, None)
+    assert rc == status
+    assert needle in la.la_last_error_message()
+    rc = lib.la_gdn_summary(ctypes.byref(d), A, A, A, A, A, None, A, A, 1, A, 1 << 30, None)
+    assert rc == status
+
+
+def _fwd_args(**over):
+    A = 1 << 20
+    args = dict(q=A, k=A, v=A, g=A, beta=A, cu=A, s0=None, out=A, fin=A, ws=A, wsb=1 << 30)
+    args.update(over)
+    return args
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(q=None), la.LA_ERR_INVALID_ARGUMENT, "q is NULL"),
+    (dict(k=(1 << 20) + 8), la.LA_ERR_INVALID_ARGUMENT, "k base pointer"),
+    (dict(v=None), la.LA_ERR_INVALID_ARGUMENT, "v is NULL"),
+    (dict(out=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "out base pointer"),
+    (dict(g=None), la.LA_ERR_INVALID_ARGUMENT, "g is NULL"),
+    (dict(beta=(1 << 20) + 1), la.LA_ERR_INVALID_ARGUMENT, "beta"),
+    (dict(cu=None), la.LA_ERR_INVALID_ARGUMENT, "cu_seqlens"),
+    (dict(s0=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "initial_state"),
+    (dict(fin=(1 << 20) + 1), la.LA_ERR_INVALID_ARGUMENT, "final_state"),
+    (dict(ws=None), la.LA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
+    (dict(ws=(1 << 20) + 128), la.LA_ERR_INVALID_ARGUMENT, "256-byte"),
+    (dict(wsb=1024), la.LA_ERR_WORKSPACE_TOO_SMALL, "needed"),
+])
+def test_fwd_argument_checks(lib, over, status, needle):
+    a = _fwd_args(**over)
+    d = _desc()
+    rc = lib.la_gdn_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["s0"],
+                        a["out"], a["fin"], 1, a["ws"], a["wsb"], None)
+    assert rc == status, la.la_last_error_message()
+    assert needle in la.la_last_error_message()
+
+
+@pytest.mark.parametrize("field,value,needle", [
+    ("q_stride_t", 100, "q strides"),
+    ("k_stride_h", 4, "k strides"),
+    ("v_stride_h", 64, "head stride"),
+    ("o_stride_t", 8, "overlaps"),
+    ("g_stride_t", 2, "g token stride"),
+])
+def test_stride_checks(lib, field, value, needle):
+    a = _fwd_args()
+    d = _desc(**{field: value})
+    rc = lib.la_gdn_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None,
+                        a["out"], a["fin"], 1, a["ws"], a["wsb"], None)
+    assert rc == la.LA_ERR_INVALID_ARGUMENT
+    assert needle in la.la_last_error_message()
+
+
+def test_summary_requires_outputs(lib):
+    A = 1 << 20
+    d = _desc()
+    rc = lib.la_gdn_summary(ctypes.byref(d), A, A, A, A, A, None, None, A, 1, A, 1 << 30, None)
+    assert rc == la.LA_ERR_INVALID_ARGUMENT and "end_state" in la.la_last_error_message()
+    rc = lib.la_gdn_summary(ctypes.byref(d), A, A, A, A, A, None, A, None, 1, A, 1 << 30, None)
+    assert rc == la.LA_ERR_INVALID_ARGUMENT and "transition" in la.la_last_error_message()
+
+
+def test_empty_batch_is_a_noop(lib):
+    A = 1 << 20
+    d = _desc(N=0, T=0)
+    rc = lib.la_gdn_fwd(ctypes.byref(d), A, A, A, A, A, A, None, A, A, 1, None, 0, None)
+    assert rc == la.LA_OK
+
+
+def test_binding_checks_layout():
+    k = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
+    v = torch.zeros(10, 2, 128, dtype=torch.bfloat16).transpose(1, 2).contiguous().transpose(1, 2)
+    g = torch.zeros(10, 2)
+    with pytest.raises(ValueError, match="innermost"):
+        la.make_desc(k, v, g, g, 1)
+    d = la.make_desc(k, torch.zeros(10, 2, 128, dtype=torch.bfloat16), g, g, 1)
+    assert (d.head_dim_k, d.head_dim_v, d.num_v_heads) == (64, 128, 2)
+
+
+def test_profiler_ids(lib):
+    names = [la.la_gdn_kernel_name(i) for i in range(la.LA_KERNEL_COUNT)]
+    assert names == ["k_sched", "k_prologue", "k_intra", "k_inter"]
+    assert la.la_gdn_kernel_name(99) == ""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.la_gdn_profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == la.LA_ERR_INVALID_ARGUMENT
