@@ -34,8 +34,8 @@ LA_ERR_WORKSPACE_TOO_SMALL = 3
 LA_ERR_HIP = 4
 LA_DEVICE_OK = 0
 LA_DEVICE_BAD_CU_SEQLENS = 1
-LA_KERNEL_SCHED, LA_KERNEL_PROLOGUE, LA_KERNEL_INTRA, LA_KERNEL_INTER = 0, 1, 2, 3
-LA_KERNEL_COUNT = 4
+LA_KERNEL_SCHED, LA_KERNEL_INTRA, LA_KERNEL_INTER = 0, 1, 2
+LA_KERNEL_COUNT = 3
 
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (

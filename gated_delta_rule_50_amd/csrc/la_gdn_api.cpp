@@ -175,6 +175,20 @@ const la::LaunchHook *current_hook()
     return P.enabled ? &hook : nullptr;
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cu_count()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 la::Prob make_prob(const la_gdn_desc *d, int l2norm)
 {
     la::Prob p{};
@@ -187,6 +201,7 @@ la::Prob make_prob(const la_gdn_desc *d, int l2norm)
     p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim_k);
     p.l2norm = l2norm ? 1 : 0;
     p.max_chunks = (int32_t)((d->total_tokens + 63) / 64 + d->num_seqs);
+    p.intra_grid = 2 * device_cu_count();
     p.qst = d->q_stride_t;
     p.qsh = d->q_stride_h;
     p.kst = d->k_stride_t;
@@ -221,9 +236,9 @@ namespace la {
 
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V, bool summary)
 {
-    (void)V;
+    (void)HK;
     WsLayout L{};
-    const int64_t max_chunks = (T + 63) / 64 + N;
+    const int64_t C = (T + 63) / 64 + N;   // chunk ids
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -232,14 +247,12 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     };
     L.hdr = take(256);
     L.seq_info = take(sizeof(int4) * (size_t)N);
-    L.chunks = take(sizeof(int4) * (size_t)max_chunks);
+    L.chunks = take(sizeof(int4) * (size_t)C);
     L.order = take(sizeof(int32_t) * (size_t)N);
-    L.rq = take(summary ? 0 : sizeof(float) * (size_t)(T * HK));
-    L.rk = take(sizeof(float) * (size_t)(T * HK));
-    L.gam = take(sizeof(float) * (size_t)(T * HV));
-    L.W = take(2 * (size_t)(HV * T * K));
-    L.TU = take(2 * (size_t)(HV * T * 128));
-    L.P = take(summary ? 0 : 2 * (size_t)(HV * T * 64));
+    L.WF = take((size_t)(C * HV) * 64 * K * 2);           // 64 x K bf16
+    L.PF = take(summary ? 0 : (size_t)(C * HV) * 64 * 64 * 2);
+    L.UF = take((size_t)(C * HV) * 64 * V * 4);           // 64 x V fp32
+    L.SC = take((size_t)(C * HV) * la::kScalars * 4);
     L.total = off;
     return L;
 }
@@ -252,12 +265,10 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.seq_info = reinterpret_cast<int4 *>(b + L.seq_info);
     w.chunks = reinterpret_cast<int4 *>(b + L.chunks);
     w.order = reinterpret_cast<int32_t *>(b + L.order);
-    w.rq = summary ? nullptr : reinterpret_cast<float *>(b + L.rq);
-    w.rk = reinterpret_cast<float *>(b + L.rk);
-    w.gam = reinterpret_cast<float *>(b + L.gam);
-    w.W = reinterpret_cast<__bf16 *>(b + L.W);
-    w.TU = reinterpret_cast<__bf16 *>(b + L.TU);
-    w.P = summary ? nullptr : reinterpret_cast<__bf16 *>(b + L.P);
+    w.WF = reinterpret_cast<uint4 *>(b + L.WF);
+    w.PF = summary ? nullptr : reinterpret_cast<uint4 *>(b + L.PF);
+    w.UF = reinterpret_cast<float4 *>(b + L.UF);
+    w.SC = reinterpret_cast<float *>(b + L.SC);
     return w;
 }
 
@@ -403,7 +414,7 @@ la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *laun
 
 const char *la_gdn_kernel_name(int32_t kernel_id)
 {
-    static const char *names[LA_KERNEL_COUNT] = {"k_sched", "k_prologue", "k_intra", "k_inter"};
+    static const char *names[LA_KERNEL_COUNT] = {"k_sched", "k_intra", "k_inter"};
     return (kernel_id >= 0 && kernel_id < LA_KERNEL_COUNT) ? names[kernel_id] : "";
 }
 

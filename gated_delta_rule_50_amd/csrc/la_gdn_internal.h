@@ -9,6 +9,9 @@ namespace la {
 
 constexpr int kChunk = 64;            // tokens per chunk; chunks restart at every sequence start
 constexpr int kSortMax = 8192;        // sequences the scheduler orders longest-first (more: batch order)
+constexpr int kFrag = 64 * 16;        // bytes of one MFMA operand fragment (64 lanes x 16 bytes)
+constexpr int kScalars = 256;         // fp32 per (chunk, v-head): sq[64], d[64], gl, zeros (one fragment)
+constexpr int kZeroOffset = 64;       // byte offset in hdr of a 64-byte block of zeros
 
 // Problem description as the kernels see it (element strides, device pointers).
 struct Prob {
@@ -18,6 +21,7 @@ struct Prob {
     float scale;
     int32_t l2norm;
     int32_t max_chunks;               // upper bound on chunks: ceil(T / 64) + N
+    int32_t intra_grid;               // workgroups of the persistent intra-chunk kernel
     const __bf16 *q, *k, *v;
     int64_t qst, qsh, kst, ksh, vst, vsh, ost, osh, gst, bst;
     const float *g, *beta;
@@ -28,22 +32,24 @@ struct Prob {
     float *trans;                     // transition (summary) or null
 };
 
-// Workspace regions (carved by the host from the caller's buffer).
+// Workspace regions (carved by the host from the caller's buffer).  The
+// per-chunk operands that the intra-chunk pass hands to the inter-chunk pass
+// are stored in MFMA fragment order, one 16-byte piece per lane, so that every
+// fragment is one coalesced 1 KiB load.  Chunk ids index the chunk table.
 struct Ws {
-    int32_t *hdr;      // [0] device status, [1] number of chunks
+    int32_t *hdr;      // [0] device status, [1] number of chunks, bytes 64..127 zeros
     int4 *seq_info;    // [N]  (start token, length, first chunk id, unused)
     int4 *chunks;      // [max_chunks]  (sequence, start token, length, chunk index in sequence)
     int32_t *order;    // [N]  sequences, longest first (ties: lower index first)
-    float *rq, *rk;    // [T, HK]  inverse L2 norms of q and k rows (1 when l2norm is off)
-    float *gam;        // [T, HV]  chunk-local inclusive cumsum of g * log2(e)
-    __bf16 *W;         // [HV, T, K]  W = T diag(beta 2^gam r_k) K per chunk
-    __bf16 *TU;        // [HV, T, 128] rows of T diag(beta): bf16 high part | low part
-    __bf16 *P;         // [HV, T, 64]  masked, decayed, scaled q k^T per chunk (forward only)
+    uint4 *WF;         // [chunk, HV]  W = T diag(beta 2^gam r_k) K as permuted A fragments (4 x K/32)
+    uint4 *PF;         // [chunk, HV]  masked decayed scaled q k^T as permuted A fragments (4 x 2), forward only
+    float4 *UF;        // [chunk, HV]  U~ = T diag(beta) V (fp32) as accumulator fragments (V/16 x 4)
+    float *SC;         // [chunk, HV, kScalars]  sq = scale r_q 2^gam, d = 2^(gam_n - gam) r_k, gl = 2^gam_n
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, rq, rk, gam, W, TU, P, total;
+    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
                           bool summary);
@@ -56,7 +62,7 @@ struct LaunchHook {
     void *ctx;
 };
 
-// Enqueues the whole pipeline (scheduler, prologue, intra, inter) on `stream`.
+// Enqueues the whole pipeline (scheduler, intra, inter) on `stream`.
 hipError_t run_pipeline(const Prob &p, const Ws &w, bool summary, hipStream_t stream,
                         const LaunchHook *hook);
 

@@ -142,11 +142,10 @@ const char *la_last_error_message(void);
  * for the recorded events and returns the summed milliseconds and the launch
  * count of one kernel (ids below).
  */
-#define LA_KERNEL_SCHED 0
-#define LA_KERNEL_PROLOGUE 1
-#define LA_KERNEL_INTRA 2
-#define LA_KERNEL_INTER 3
-#define LA_KERNEL_COUNT 4
+#define LA_KERNEL_SCHED 0   /* cu_seqlens validation, chunk table, longest-first order */
+#define LA_KERNEL_INTRA 1   /* prologue (q/k norms, gate cumsum) + intra-chunk UT/WY */
+#define LA_KERNEL_INTER 2   /* sequential inter-chunk state and output pass */
+#define LA_KERNEL_COUNT 3
 la_status la_gdn_profile_enable(int enable);
 la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *launches);
 const char *la_gdn_kernel_name(int32_t kernel_id);
