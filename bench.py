@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the chunked Gated DeltaNet forward on one MI355X.
 
-One step = one la_gdn_fwd call (scheduler, prologue, intra-chunk and
-inter-chunk kernels) over the varlen workload T = 4096, cu_seqlens =
+One step = one la_gdn_fwd call (scheduler, intra-chunk pass with its fused
+prologue, inter-chunk pass) over the varlen workload T = 4096, cu_seqlens =
 [0, 1000, 2500, 4096], H = 16, K = V = 128, bf16, in-kernel q/k L2 norm,
 zero initial state, output o and final states (the example call of the cuDNN
 "Linear Attention" page).  Inputs are seeded synthetic tensors already
