@@ -34,22 +34,26 @@ struct Prob {
 
 // Workspace regions (carved by the host from the caller's buffer).  The
 // per-chunk operands that the intra-chunk pass hands to the inter-chunk pass
-// are stored in MFMA fragment order, one 16-byte piece per lane, so that every
-// fragment is one coalesced 1 KiB load.  Chunk ids index the chunk table.
+// are stored in the lane order of 32 x 32 x 16 MFMA operands, one 16-byte piece
+// per lane, so that every fragment is one coalesced 1 KiB load; reductions over
+// state rows or tokens are in accumulator order (rows 16 s + 4 hh + i and
+// 16 s + 8 + 4 hh + i of step s in slots i and 4 + i).  Chunk ids index the
+// chunk table.
 struct Ws {
     int32_t *hdr;      // [0] device status, [1] number of chunks, bytes 64..127 zeros
     int4 *seq_info;    // [N]  (start token, length, first chunk id, unused)
     int4 *chunks;      // [max_chunks]  (sequence, start token, length, chunk index in sequence)
     int32_t *order;    // [N]  sequences, longest first (ties: lower index first)
-    uint4 *WF;         // [chunk, HV]  W = T diag(beta 2^gam r_k) K as permuted A fragments (4 x K/32)
-    uint4 *PF;         // [chunk, HV]  masked decayed scaled q k^T as permuted A fragments (4 x 2), forward only
-    float4 *UF;        // [chunk, HV]  U~ = T diag(beta) V (fp32) as accumulator fragments (V/16 x 4)
-    float *SC;         // [chunk, HV, kScalars]  sq = scale r_q 2^gam, d = 2^(gam_n - gam) r_k, gl = 2^gam_n
+    uint4 *WF;         // [chunk, HV][key half][token tile][step]  -W, W = T diag(beta 2^gam r_k) K, A fragments
+    uint4 *KF;         // [chunk, HV][key half][row tile][token step]  (K diag(2^(gam_n - gam) r_k))^T, A fragments
+    uint4 *PF;         // [chunk, HV][6]  P^T (masked decayed scaled q k^T), B fragments, forward only
+    float4 *UF;        // [chunk, HV][V/32][token tile][4]  U~ = T diag(beta) V, fp32 accumulator tiles
+    float *SC;         // [chunk, HV, kScalars]  sq = scale r_q 2^gam per token, then gl = 2^gam_n
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, total;
+    size_t hdr, seq_info, chunks, order, WF, KF, PF, UF, SC, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
                           bool summary);

@@ -235,6 +235,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
 
 __device__ __forceinline__ uint2 lds_tr(const void *p)
 {
@@ -268,6 +273,89 @@ __device__ __forceinline__ int swz(int row, int col)
 __device__ __forceinline__ void lds_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
+// v_mfma_f32_32x32x16_bf16, with c = lane % 32 and hh = lane / 32:
+//   A (32 x 16): lane holds row c, reduction slots 8 hh .. 8 hh + 7
+//   B (16 x 32): lane holds column c, reduction slots 8 hh .. 8 hh + 7
+//   C (32 x 32): lane holds column c, rows 8 j + 4 hh + i in register 4 j + i
+// A product that reduces over the rows of an accumulator tile takes them in
+// register order: step s (s = 0, 1) of a 32-row tile puts rows 16 s + 4 hh + i
+// in slots i and rows 16 s + 8 + 4 hh + i in slots 4 + i (i < 4), which are
+// registers 8 s .. 8 s + 7 of the lane, so the tile feeds the next product
+// without leaving registers ("accumulator order").
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Registers 8 s .. 8 s + 7 of an accumulator tile as a bf16 operand (accumulator order).
+__device__ __forceinline__ bf16x8 pack32(const f32x16 &c, int s)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = f2bf(c[8 * s + e]);
+    return r;
+}
+
+// Sign flip of eight packed bf16 values.
+__device__ __forceinline__ uint4 neg_bf16(bf16x8 x)
+{
+    uint4 u = __builtin_bit_cast(uint4, x);
+    u.x ^= 0x80008000u;
+    u.y ^= 0x80008000u;
+    u.z ^= 0x80008000u;
+    u.w ^= 0x80008000u;
+    return u;
+}
+
+// Operand of a product reducing over the rows of a row-major bf16 tile M (row
+// stride ld elements): lane (c, hh) gets M[t0 + 8 hh + e][c0 + c], e = 0..7 (plain
+// order).  As an A operand this is M^T (rows c0 .., reduction t0 ..); as a B
+// operand it is M itself.  Two transposed 8-byte reads.
+__device__ __forceinline__ bf16x8 lds_tr32(const __bf16 *base, int ld, int t0, int c0, int lane)
+{
+    const int lam = lane & 15;
+    const __bf16 *p = base + (t0 + 8 * (lane >> 5) + (lam >> 2)) * ld + c0 + 16 * ((lane >> 4) & 1) + 4 * (lam & 3);
+    const uint2 lo = lds_tr(p), hi = lds_tr(p + 4 * ld);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Same in accumulator order: lane (c, hh) gets M[t0 + 4 hh + i][c0 + c] in slot i
+// and M[t0 + 8 + 4 hh + i][c0 + c] in slot 4 + i.
+__device__ __forceinline__ bf16x8 lds_tr32p(const __bf16 *base, int ld, int t0, int c0, int lane)
+{
+    const int lam = lane & 15;
+    const __bf16 *p = base + (t0 + 4 * (lane >> 5) + (lam >> 2)) * ld + c0 + 16 * ((lane >> 4) & 1) + 4 * (lam & 3);
+    const uint2 lo = lds_tr(p), hi = lds_tr(p + 8 * ld);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Workgroup barrier for LDS data exchanged between waves: waits for this wave's
+// LDS accesses, then s_barrier (the asm clobbers memory, so no access moves
+// across it).  Loads into LDS that are still in flight stay in flight: a
+// __syncthreads, or a fence that covers LDS, would wait for them as well.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Buffer resource (four scalar registers) for raw byte-addressed buffer loads.
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+constexpr int kBufferWord3 = 0x00020000;   // raw (unswizzled, unformatted) buffer, CDNA
+
+// Waits until at most N vector memory operations of this wave are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
 // k_intra: one workgroup of 4 waves per (chunk, value head).
 //
 // Phase 1 is the prologue (the fused prologue of the cudnn-frontend PR: q/k L2
@@ -290,18 +378,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NK = 64 * KPR / 256, NV = 64 * VPR / 256;
     constexpr int NA = K / 32;
     // LDS: sK raw k rows | sX q rows, later v rows | sA A^T (fp32) with the solve's
-    // scratch, later Tw, Thi, Tlo (bf16) | sT P (bf16), then T (fp32), then W (bf16)
+    // scratch, later Tw, Thi, Tlo (bf16) | sT P (bf16), then T (fp32)
     constexpr int SA_BYTES = (64 * AP * 4 + 7 * 1024 > 3 * 64 * TP * 2) ? 64 * AP * 4 + 7 * 1024 : 3 * 64 * TP * 2;
     __shared__ __attribute__((aligned(16))) __bf16 sK[64 * KP];
     __shared__ __attribute__((aligned(16))) __bf16 sX[64 * XP];
     __shared__ __attribute__((aligned(16))) float sA[SA_BYTES / 4];
     __shared__ __attribute__((aligned(16))) float sT[64 * AP];
     __shared__ float s_rk[64], s_rq[64], s_gam[64], s_beta[64], s_fw[64];
+    __shared__ __attribute__((aligned(16))) float s_d[64];
     __bf16 *const sTw = reinterpret_cast<__bf16 *>(sA);
     __bf16 *const sThi = sTw + 64 * TP;
     __bf16 *const sTlo = sThi + 64 * TP;
     __bf16 *const sP = reinterpret_cast<__bf16 *>(sT);
-    __bf16 *const sW = reinterpret_cast<__bf16 *>(sT);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -388,7 +476,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         if (next < items) load_kq(next);      // k, q registers are free again
         __syncthreads();
-        if (tid < 64) s_fw[tid] = s_beta[tid] * exp2f(s_gam[tid]) * s_rk[tid];
+        if (tid < 64) {
+            s_fw[tid] = s_beta[tid] * exp2f(s_gam[tid]) * s_rk[tid];
+            s_d[tid] = exp2f(s_gam[len - 1] - s_gam[tid]) * s_rk[tid];   // 0 past the end (r_k = 0)
+        }
 
         // ---- phase 2: A (strictly lower, stored transposed) and P (lower incl. diagonal).
         // Wave m computes row tile m against column tiles n <= m; all operand fragments
@@ -434,12 +525,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __syncthreads();
 
-        // ---- phase 2b: P fragments; v rows into sX (q rows are dead)
+        // ---- phase 2b: P^T fragments (B operands, reduction over source tokens in
+        // accumulator order): fragment f < 2 is token tile 0, step f; 2 + s is token tile
+        // 1, step s (P is causal, so tile 0 needs steps 0 and 1 only); v rows into sX
         if (FWD) {
-#pragma unroll
-            for (int f2 = 0; f2 < 2; ++f2) {
-                const int f = 2 * wave + f2, m = f >> 1, a = f & 1;
-                w.PF[(ch_h * 8 + f) * 64 + lane] = lds_rowperm(sP, TP, 16 * m + r16, 32 * a, q4);
+            const int c = lane & 31, hh = lane >> 5;
+            for (int f = wave; f < 6; f += 4) {
+                const int nt = f < 2 ? 0 : 1, s = f < 2 ? f : f - 2;
+                const __bf16 *pp = sP + (32 * nt + c) * TP + 16 * s + 4 * hh;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(pp);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(pp + 8);
+                w.PF[(ch_h * 6 + f) * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
         }
 #pragma unroll
@@ -551,271 +647,282 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __syncthreads();
 
-        // ---- phase 4: W = Tw K (to LDS, bf16) and U~ = Thi V + Tlo V (fp32 fragments)
+        // ---- phase 4: on 32 x 32 tiles, from registers to the workspace in the operand
+        // order of the inter-chunk pass (accumulator order over the key half's rows):
+        //   -W, as W^T = K^T Tw^T (rows: key columns, columns: tokens), whose registers
+        //       8 s .. 8 s + 7 are exactly the A operand rows of W for one reduction step;
+        //   U~ = Thi V + Tlo V (tokens x value columns, fp32 accumulator tiles);
+        //   (K diag(d))^T, d = 2^(gam_n - gam) r_k, as A operands reducing over tokens.
         {
-            const int m = wave;
-            const bf16x8 aw0 = lds_op(sTw, TP, 16 * m + r16, 0, q4), aw1 = lds_op(sTw, TP, 16 * m + r16, 32, q4);
-            const bf16x8 ah0 = lds_op(sThi, TP, 16 * m + r16, 0, q4), ah1 = lds_op(sThi, TP, 16 * m + r16, 32, q4);
-            const bf16x8 al0 = lds_op(sTlo, TP, 16 * m + r16, 0, q4), al1 = lds_op(sTlo, TP, 16 * m + r16, 32, q4);
+            constexpr int NKS = K / 32;          // reduction steps over a key half
+            constexpr int NR = K / 64;           // 32-row tiles of a key half
+            const int c = lane & 31, hh = lane >> 5;
 #pragma unroll
-            for (int n = 0; n < K / 16; ++n) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma16(aw0, lds_b_tr(sK, KP, 0, 16 * n, lane), acc);
-                acc = mfma16(aw1, lds_b_tr(sK, KP, 32, 16 * n, lane), acc);
+            for (int i = 0; i < (2 * (K / 32)) / 4; ++i) {
+                const int pr = 4 * i + wave, nb = pr >> 1, m = pr & 1;
+                f32x16 acc = {};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sW[(16 * m + 4 * q4 + j) * KP + 16 * n + r16] = f2bf(acc[j]);
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 ka = lds_tr32(sK, KP, 16 * s, 32 * nb, lane);
+                    const bf16x8 tb = *reinterpret_cast<const bf16x8 *>(sTw + (32 * m + c) * TP + 16 * s + 8 * hh);
+                    acc = mfma32(ka, tb, acc);
+                }
+#pragma unroll
+                for (int js = 0; js < 2; ++js) {
+                    const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
+                    w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+                }
             }
 #pragma unroll
-            for (int n = 0; n < V / 16; ++n) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const bf16x8 b0 = lds_b_tr(sX, XP, 0, 16 * n, lane), b1 = lds_b_tr(sX, XP, 32, 16 * n, lane);
-                acc = mfma16(ah0, b0, acc);
-                acc = mfma16(al0, b0, acc);
-                acc = mfma16(ah1, b1, acc);
-                acc = mfma16(al1, b1, acc);
-                w.UF[((ch_h * (V / 16) + n) * 4 + m) * 64 + lane] = float4(acc[0], acc[1], acc[2], acc[3]);
-            }
-        }
-        // per-token factors of the inter-chunk pass
-        {
-            float v = 0.f;
-            const int t = tid & 63;
-            const bool ok = t < len;
-            if (tid < 64) v = (ok && FWD) ? p.scale * s_rq[t] * exp2f(s_gam[t]) : 0.f;
-            else if (tid < 128) v = ok ? exp2f(gl - s_gam[t]) * s_rk[t] : 0.f;
-            else if (tid == 128) v = exp2f(gl);
-            w.SC[ch_h * kScalars + tid] = v;
-        }
-        __syncthreads();
-
-        // ---- phase 5: W fragments
-        {
-            constexpr int FW = 4 * NA;
+            for (int i = 0; i < (2 * (V / 32)) / 4; ++i) {
+                const int pr = 4 * i + wave, ct = pr >> 1, m = pr & 1;
+                f32x16 acc = {};
 #pragma unroll
-            for (int f2 = 0; f2 < FW / 4; ++f2) {
-                const int f = (FW / 4) * wave + f2, m = f / NA, a = f % NA;
-                w.WF[(ch_h * FW + f) * 64 + lane] = lds_rowperm(sW, KP, 16 * m + r16, 32 * a, q4);
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 vb = lds_tr32(sX, XP, 16 * s, 32 * ct, lane);
+                    const int ro = (32 * m + c) * TP + 16 * s + 8 * hh;
+                    acc = mfma32(*reinterpret_cast<const bf16x8 *>(sThi + ro), vb, acc);
+                    acc = mfma32(*reinterpret_cast<const bf16x8 *>(sTlo + ro), vb, acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w.UF[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] =
+                        make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+            }
+#pragma unroll
+            for (int i = 0; i < (K / 8) / 4; ++i) {
+                const int f = 4 * i + wave, kh = f / (4 * NR), r = (f / 4) % NR, s = f % 4;
+                const bf16x8 kt = lds_tr32p(sK, KP, 16 * s, kh * (K / 2) + 32 * r, lane);
+                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(s_d + 16 * s + 4 * hh);
+                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(s_d + 16 * s + 8 + 4 * hh);
+                bf16x8 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[e] = f2bf(bf2f(kt[e]) * d0[e]);
+                    o[4 + e] = f2bf(bf2f(kt[4 + e]) * d1[e]);
+                }
+                w.KF[(ch_h * (K / 8) + f) * 64 + lane] = __builtin_bit_cast(uint4, o);
             }
         }
-        __syncthreads();   // sW, sK and the scalars are rewritten by the next item
+        // per-chunk scalars of the inter-chunk pass: sq = scale r_q 2^gam per token, 2^(gam_n)
+        if (tid < 64) w.SC[ch_h * kScalars + tid] = (FWD && tid < len) ? p.scale * s_rq[tid] * exp2f(s_gam[tid]) : 0.f;
+        else if (tid == 64) w.SC[ch_h * kScalars + 64] = exp2f(gl);
+        __syncthreads();   // sK, sX and the scalars are rewritten by the next item
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_inter: one workgroup of 2 waves per (sequence, value head, 32 state
-// columns); each wave owns 16 columns and keeps them as 8 accumulator tiles.
-// The chunk loop is sequential.  Each chunk's operands (W, P and U~ fragments,
-// per-token factors, raw q and k tiles) go straight from memory into one of two
-// LDS buffers with direct-to-LDS loads issued a chunk ahead; the raw q/k tiles
-// are XOR-swizzled (through the choice of source address) so that the
-// fragment reads from them are free of bank conflicts.  Rows past a chunk's
-// end load from a zero block.  For the summary the state is widened to [S | P]
-// (K x (V + K)): the P columns start at the identity and see U~ = 0, so they
-// evolve as the product of the decayed erase steps.
+// k_inter: one workgroup of 6 waves per (sequence, value head, 32 state columns),
+// on 32 x 32 MFMA tiles, with three roles:
+//   state waves kh = 0, 1 (waves 0, 1) own the state rows of key half kh (K/2 x 32
+//     as accumulator tiles) and carry the chunk recurrence;
+//   output waves t = 0, 1 (waves 2, 3) produce the outputs of 32-token tile t;
+//   loader waves (waves 4, 5) issue every load of the chunk operands into LDS.
+// Per chunk, with S the chunk's start state:
+//   state wave kh:  X_kh = [U~ if kh = 0] + (-W)_kh S_kh  (its half of the
+//                   reduction); the X partials are swapped through LDS so that
+//                   both hold U_new = X_0 + X_1 (fp32 addition commutes: the same
+//                   bits in both); S_kh <- 2^(gam_n) S_kh + (K diag(d))_kh^T U_new,
+//                   d = 2^(gam_n - gam) r_k.  It also publishes S (bf16) and its
+//                   token tile of U_new (bf16) for the output waves.
+//   output wave t:  Y^T = S^T Q_t^T over all state rows (after the first barrier),
+//                   then at the start of the next chunk
+//                   O^T = diag(sq) Y^T + U_new^T P_t^T, sq = scale r_q 2^gam
+//                   (P causal: tile 0 needs U_new rows 0..31 only), and stores it.
+// The reduction index of every product over state rows or tokens is in
+// accumulator order, so S and U_new go from accumulators to operands in
+// registers; the intra-chunk pass writes -W, (K diag(d))^T, P^T and U~ in that
+// order.  Two barriers per chunk: B1 after the X partials and S are published,
+// B2 at the end of the chunk.
+//
+// Loads: the loader waves keep two LDS buffers of each group in flight: the
+// early group (-W, U~, raw q, P^T, per-chunk scalars), read before B1, and the
+// late group ((K diag(d))^T), read after it.  The early loads of chunk c + 2 are
+// issued right after B1 of chunk c and the late loads of chunk c + 1 right after
+// B2 of chunk c - 1, so each group has about one and a half chunk steps to land.
+// They are buffer loads into LDS written as asm: the compiler neither tracks them
+// nor adds waits for them; the loader waves issue nothing else, so each wait
+// counts exactly the loads issued after the ones it needs (loads complete in
+// issue order).  Rows of q past a chunk's end are out of the buffer's range and
+// load as zeros.  The barriers order LDS only.
+// For the summary the state is widened to [S | P] (K x (V + K)): the P columns
+// start at the identity and see U~ = 0, so they evolve as the product of the
+// decayed erase steps; there are no outputs.
 
 template <int K, int V, bool SUMMARY>
 struct InterCfg {
     static constexpr bool FWD = !SUMMARY;
-    static constexpr int NW = 2, BV = 16 * NW;
     static constexpr int VA = SUMMARY ? V + K : V;
-    static constexpr int NT = VA / BV;
-    static constexpr int NA = K / 32;
-    static constexpr int PPR = K / 8;             // 16-byte pieces per q/k row
-    static constexpr int FW = 4 * NA;             // fragments (1 KiB each) per buffer region
-    static constexpr int FP = FWD ? 8 : 0;
-    static constexpr int FU = 2 * 4;
-    static constexpr int FS = 1;
-    static constexpr int FQ = FWD ? 64 * PPR / 64 : 0;
-    static constexpr int FK = 64 * PPR / 64;
-    static constexpr int oW = 0, oP = oW + FW, oU = oP + FP, oS = oU + FU, oQ = oS + FS, oK = oQ + FQ;
-    static constexpr int NF = oK + FK;
+    static constexpr int NT = VA / 32;            // workgroups (32-column tiles) per (sequence, head)
+    static constexpr int KH = K / 2;              // state rows per state wave
+    static constexpr int NR = KH / 32;            // 32-row accumulator tiles per state wave
+    static constexpr int NKS = KH / 16;           // reduction steps over a key half
+    static constexpr int PPR = K / 8;             // 16-byte pieces per q row
+    // early group (1 KiB fragments): -W [kh][token tile][step], U~ [token tile][j],
+    // raw q (64 x K bf16, pieces swizzled by row), P^T (tile 0 steps 0..1, tile 1
+    // steps 0..3), scalars (sq[64], then 2^(gam_n) at 64)
+    static constexpr int FW = 4 * NKS, FU = 8, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
+    static constexpr int oW = 0, oU = oW + FW, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
+    // late group: (K diag(d))^T [kh][row tile][token step]
+    static constexpr int FK = 4 * NKS, oK = 0, NFL = FK;
+    static constexpr int NQ = FWD ? FQ / 2 : 1;   // q tile loads per loader wave
 };
 
-// Per-lane, chunk-invariant parts of the addresses of the raw q/k tile pieces.
-template <int K, int V, bool SUMMARY>
-struct InterLane {
-    uint32_t offk[InterCfg<K, V, SUMMARY>::FK / 2];   // byte offsets from the chunk's first k row
-    uint32_t offq[InterCfg<K, V, SUMMARY>::FK / 2];
-    int32_t row[InterCfg<K, V, SUMMARY>::FK / 2];     // tile row each piece belongs to
-};
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);   // stride 0: raw byte addressing
+    r[2] = (int)bytes;                              // loads at or past this offset read zeros
+    r[3] = kBufferWord3;
+    return r;
+}
+
+// One 16-byte-per-lane buffer load into LDS fragment `f` of `buf` (lane l's 16
+// bytes land at fragment byte 16 l).  Written as asm so that the compiler neither
+// tracks these loads nor adds waits for them: every wait for them is explicit.
+// M0 needs one wait state before the load that uses it.
+__device__ __forceinline__ void b2l(i32x4 rsrc, lds_u32x4 *buf, int f, uint32_t voff, uint32_t soff)
+{
+    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(buf + f * 64);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(dst), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Waits until at most n (wave-uniform, < 64) vector memory operations of this
+// wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait_upto(int n)
+{
+    if constexpr (N >= 0) {
+        if (n == N) vm_wait<N>();
+        else vm_wait_upto<N - 1>(n);
+    }
+}
+__device__ __forceinline__ void vm_wait_n(int n)
+{
+    if (n >= 32) vm_wait_upto<63>(n);
+    else if (n >= 16) vm_wait_upto<31>(n);
+    else vm_wait_upto<15>(n);
+}
 
 template <int K, int V, bool SUMMARY>
-__device__ __forceinline__ void inter_lane_init(const Prob &p, int hk, int wave, int lane,
-                                                InterLane<K, V, SUMMARY> &L)
+struct InterCtx {
+    int nch, seq_start, seq_len, cid0, h, hk, tile, lane;
+    bool ptile;
+};
+
+// Loader wave lh: its half of chunk ci's early group into `eb`.  Returns the number of loads.
+template <int K, int V, bool SUMMARY>
+__device__ __forceinline__ int inter_issue_early(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
+                                                 const InterCtx<K, V, SUMMARY> &x, const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ])
 {
     using C = InterCfg<K, V, SUMMARY>;
+    const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
+    const uint32_t lo16 = (uint32_t)x.lane * 16u;
+    int n = 0;
+    const i32x4 rW = make_rsrc(reinterpret_cast<const char *>(w.WF) + chh * C::FW * kFrag, C::FW * kFrag);
+#pragma unroll
+    for (int i = 0; i < C::FW / 2; ++i) {
+        const int f = lh * (C::FW / 2) + i;
+        b2l(rW, eb, C::oW + f, lo16, f * kFrag);
+    }
+    n += C::FW / 2;
+    if (!x.ptile) {
+        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UF) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
+                                   C::FU * kFrag);
+#pragma unroll
+        for (int i = 0; i < C::FU / 2; ++i) {
+            const int f = lh * (C::FU / 2) + i;
+            b2l(rU, eb, C::oU + f, lo16, f * kFrag);
+        }
+        n += C::FU / 2;
+    }
+    if (C::FWD) {
+        const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
+        const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)x.hk * p.qsh,
+                                   (uint32_t)len * 2u * (uint32_t)p.qst);
+#pragma unroll
+        for (int i = 0; i < C::FQ / 2; ++i) b2l(rQ, eb, C::oQ + 2 * i + lh, qoff[i], 0);
+        const i32x4 rP = make_rsrc(reinterpret_cast<const char *>(w.PF) + chh * 6 * kFrag, 6 * kFrag);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) b2l(rP, eb, C::oP + 3 * lh + i, lo16, (3 * lh + i) * kFrag);
+        n += C::FQ / 2 + 3;
+    }
+    if (lh == 0) {
+        const i32x4 rS = make_rsrc(w.SC + chh * kScalars, kScalars * 4);
+        b2l(rS, eb, C::oS, lo16, 0);
+        n += 1;
+    }
+    return n;
+}
+
+// Loader wave lh: its half of chunk ci's late group into `lb`.  Returns the number of loads.
+template <int K, int V, bool SUMMARY>
+__device__ __forceinline__ int inter_issue_late(const Prob &p, const Ws &w, lds_u32x4 *lb, int ci, int lh,
+                                                const InterCtx<K, V, SUMMARY> &x)
+{
+    using C = InterCfg<K, V, SUMMARY>;
+    const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
+    const uint32_t lo16 = (uint32_t)x.lane * 16u;
+    const i32x4 rK = make_rsrc(reinterpret_cast<const char *>(w.KF) + chh * C::FK * kFrag, C::FK * kFrag);
 #pragma unroll
     for (int i = 0; i < C::FK / 2; ++i) {
-        const int s = (2 * i + wave) * 64 + lane;
-        const int row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
-        L.row[i] = row;
-        L.offk[i] = (uint32_t)(2 * (row * p.kst + hk * p.ksh + 8 * pc));
-        L.offq[i] = C::FWD ? (uint32_t)(2 * (row * p.qst + hk * p.qsh + 8 * pc)) : 0u;
+        const int f = lh * (C::FK / 2) + i;
+        b2l(rK, lb, C::oK + f, lo16, f * kFrag);
     }
+    return C::FK / 2;
 }
 
-// Issues the direct-to-LDS loads of one chunk's operands into `buf`.  `wave` is
-// wave-uniform (read with readfirstlane) so every LDS destination is a scalar.
+// Output wave t: O^T of its token tile of the chunk whose Y^T it holds, stored
+// to o.  Lane (c, hh) holds value columns 8 j + 4 hh .. + 3 of token 32 t + c.
 template <int K, int V, bool SUMMARY>
-__device__ __forceinline__ void inter_issue(const Prob &p, const Ws &w, u32x4 *buf, int cid, int start, int len,
-                                            int h, int tile, bool ptile, int wave, int lane,
-                                            const InterLane<K, V, SUMMARY> &L)
+__device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU, const f32x16 &Y, const bf16x8 (&Pf)[4],
+                                             float sq, int t, int o_start, int o_len, const InterCtx<K, V, SUMMARY> &x)
 {
-    using C = InterCfg<K, V, SUMMARY>;
-    const int64_t chh = (int64_t)cid * p.HV + h;
-    auto g2l = [&](const void *src, int f) {
-        __builtin_amdgcn_global_load_lds((glb_void *)(src), (lds_void *)(buf + f * 64), 16, 0, 0);
-    };
-    // fragments written by k_intra, already in lane order
-    const uint32_t lo16 = (uint32_t)lane * 16u;
-    const char *gW = reinterpret_cast<const char *>(w.WF) + (chh * C::FW + wave) * kFrag;
+    const int lane = x.lane, c = lane & 31, hh = lane >> 5;
+    f32x16 O;
 #pragma unroll
-    for (int i = 0; i < C::FW / 2; ++i) g2l(gW + lo16 + i * 2 * kFrag, C::oW + 2 * i + wave);
-    if (C::FWD) {
-        const char *gP = reinterpret_cast<const char *>(w.PF) + (chh * 8 + wave) * kFrag;
-#pragma unroll
-        for (int i = 0; i < C::FP / 2; ++i) g2l(gP + lo16 + i * 2 * kFrag, C::oP + 2 * i + wave);
+    for (int e = 0; e < 16; ++e) O[e] = sq * Y[e];
+    O = mfma32(__builtin_bit_cast(bf16x8, xU[0 * 64 + lane]), Pf[0], O);
+    O = mfma32(__builtin_bit_cast(bf16x8, xU[1 * 64 + lane]), Pf[1], O);
+    if (t != 0) {
+        O = mfma32(__builtin_bit_cast(bf16x8, xU[2 * 64 + lane]), Pf[2], O);
+        O = mfma32(__builtin_bit_cast(bf16x8, xU[3 * 64 + lane]), Pf[3], O);
     }
-    if (!ptile) {
-        const char *gU = reinterpret_cast<const char *>(w.UF) + ((chh * (V / 16) + tile * C::NW) * 4 + wave) * kFrag;
-#pragma unroll
-        for (int i = 0; i < C::FU / 2; ++i) g2l(gU + lo16 + i * 2 * kFrag, C::oU + 2 * i + wave);
-    }
-    if (wave == 0) g2l(reinterpret_cast<const char *>(w.SC + chh * kScalars) + lo16, C::oS);
-    // raw q and k tiles, pieces XOR-swizzled by row; rows past the end read zeros
-    const char *kb = reinterpret_cast<const char *>(p.k + (int64_t)start * p.kst);
-    const char *qb = C::FWD ? reinterpret_cast<const char *>(p.q + (int64_t)start * p.qst) : nullptr;
-    const void *zero = reinterpret_cast<const char *>(w.hdr) + kZeroOffset;
-    if (len == kChunk) {
-#pragma unroll
-        for (int i = 0; i < C::FK / 2; ++i) {
-            g2l(kb + L.offk[i], C::oK + 2 * i + wave);
-            if (C::FWD) g2l(qb + L.offq[i], C::oQ + 2 * i + wave);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C::FK / 2; ++i) {
-            const bool ok = L.row[i] < len;
-            g2l(ok ? (const void *)(kb + L.offk[i]) : zero, C::oK + 2 * i + wave);
-            if (C::FWD) g2l(ok ? (const void *)(qb + L.offq[i]) : zero, C::oQ + 2 * i + wave);
-        }
-    }
-}
-
-template <int K, int V, bool SUMMARY>
-__device__ __forceinline__ void inter_chunk(const Prob &p, const u32x4 *buf, f32x4 (&S)[K / 16], bool ptile,
-                                            int wave, int lane, f32x4 (&O)[4])
-{
-    using C = InterCfg<K, V, SUMMARY>;
-    constexpr int NA = C::NA;
-    const int q4 = lane >> 4, r16 = lane & 15;
-    const float *sc = reinterpret_cast<const float *>(buf + C::oS * 64);
-    const char *tq = reinterpret_cast<const char *>(buf + C::oQ * 64);
-    const char *tk = reinterpret_cast<const char *>(buf + C::oK * 64);
-
-    // ---- all LDS reads of the chunk first (independent of S), so their latency
-    // overlaps instead of stalling each product
-    const int g = q4, rho = r16;
-    bf16x8 Wf[4][NA], Qf[4][NA], Kf[K / 16][2], Pf[4][2];
-    f32x4 Ut[4], d4[4], sq4[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            Wf[m][a] = __builtin_bit_cast(bf16x8, buf[(C::oW + m * NA + a) * 64 + lane]);
-            if (C::FWD) {
-                const int row = 16 * m + r16, c0 = 32 * a + 4 * q4;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(tq + swz<C::PPR>(row, c0));
-                const uint2 hi = *reinterpret_cast<const uint2 *>(tq + swz<C::PPR>(row, c0 + 16));
-                Qf[m][a] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            }
-        }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        Ut[m] = ptile ? f32x4{0.f, 0.f, 0.f, 0.f}
-                      : __builtin_bit_cast(f32x4, buf[(C::oU + wave * 4 + m) * 64 + lane]);
-        d4[m] = *reinterpret_cast<const f32x4 *>(sc + 64 + 16 * m + 4 * q4);
-        if (C::FWD) sq4[m] = *reinterpret_cast<const f32x4 *>(sc + 16 * m + 4 * q4);
-    }
-    const float gl = sc[128];
-#pragma unroll
-    for (int r = 0; r < K / 16; ++r)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            // K^T fragments: transposed reads of the raw k tile
-            const int t = 32 * a + 4 * g + (rho >> 2), cc = 16 * r + 4 * (rho & 3);
-            const uint2 lo = lds_tr(tk + swz<C::PPR>(t, cc));
-            const uint2 hi = lds_tr(tk + swz<C::PPR>(t + 16, cc));
-            Kf[r][a] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        }
-    if (C::FWD) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int a = 0; a < 2; ++a) Pf[m][a] = __builtin_bit_cast(bf16x8, buf[(C::oP + 2 * m + a) * 64 + lane]);
-    }
-
-    // ---- X = W S and Y = Q S
-    bf16x8 Sb[NA];
-#pragma unroll
-    for (int a = 0; a < NA; ++a) Sb[a] = pack_b(S[2 * a], S[2 * a + 1]);
-    f32x4 X[4], Y[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Y[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            X[m] = mfma16(Wf[m][a], Sb[a], X[m]);
-            if (C::FWD) Y[m] = mfma16(Qf[m][a], Sb[a], Y[m]);
-        }
-    // ---- U_new = U~ - X;  Ud = diag(2^(gam_n - gam) r_k) U_new
-    f32x4 Un[4], Ud[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
+    const int tok = 32 * t + c;
+    if (tok < o_len) {
+        __bf16 *ob = p.o + (int64_t)(o_start + tok) * p.ost + (int64_t)x.h * p.osh + 32 * x.tile + 4 * hh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float un = Ut[m][j] - X[m][j];
-            Un[m][j] = un;
-            Ud[m][j] = d4[m][j] * un;
-        }
-    const bf16x8 Ud0 = pack_b(Ud[0], Ud[1]), Ud1 = pack_b(Ud[2], Ud[3]);
-    // ---- S <- 2^(gam_n) S + K^T Ud
-#pragma unroll
-    for (int r = 0; r < K / 16; ++r) {
-        f32x4 dS = {0.f, 0.f, 0.f, 0.f};
-        dS = mfma16(Kf[r][0], Ud0, dS);
-        dS = mfma16(Kf[r][1], Ud1, dS);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[r][j] = fmaf(gl, S[r][j], dS[j]);
-    }
-    // ---- O = diag(scale r_q 2^gam) Q S0 + P U_new
-    if (C::FWD) {
-        const bf16x8 Ub0 = pack_b(Un[0], Un[1]), Ub1 = pack_b(Un[2], Un[3]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = sq4[m][j] * Y[m][j];
-            o = mfma16(Pf[m][0], Ub0, o);
-            o = mfma16(Pf[m][1], Ub1, o);
-            O[m] = o;
+            const f32x4 o4 = {O[4 * j], O[4 * j + 1], O[4 * j + 2], O[4 * j + 3]};
+            const uint4 u = __builtin_bit_cast(uint4, pack_b(o4, o4));
+            *reinterpret_cast<uint2 *>(ob + 8 * j) = make_uint2(u.x, u.y);
         }
     }
 }
 
 template <int K, int V, bool SUMMARY>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_inter(Prob p, Ws w)
+__global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 {
     using C = InterCfg<K, V, SUMMARY>;
-    __shared__ u32x4 buf0[C::NF * 64];
-    __shared__ u32x4 buf1[C::NF * 64];
+    constexpr int NR = C::NR, NKS = C::NKS;
+    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64];   // early group, two buffers
+    __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // late group, two buffers
+    __shared__ u32x4 sX[2 * 8 * 64];                       // X partials: [kh][m][j][lane]
+    __shared__ u32x4 sS[C::FWD ? 2 * NKS * 64 : 1];        // S (bf16 operands): [kh][step][lane]
+    __shared__ u32x4 sU[C::FWD ? 4 * 64 : 1];              // U_new (bf16 operands): [token step][lane]
+    lds_u32x4 *const e0 = (lds_u32x4 *)sE0, *const e1 = (lds_u32x4 *)sE1;
+    lds_u32x4 *const l0 = (lds_u32x4 *)sL0, *const l1 = (lds_u32x4 *)sL1;
+    lds_u32x4 *const xX = (lds_u32x4 *)sX, *const xS = (lds_u32x4 *)sS, *const xU = (lds_u32x4 *)sU;
 
     if (w.hdr[0] != LA_DEVICE_OK) return;
     const int U = p.N * p.HV;
+    // blocks of 8 units x NT tiles; consecutive blocks go to different XCDs, and
+    // the NT tiles of one unit (which read the same W, K, P and q) to the same one
     const int b = blockIdx.x;
     const int grp = b / (8 * C::NT), rem = b % (8 * C::NT);
     const int ug = min(8, U - 8 * grp);
@@ -823,107 +930,244 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int u = 8 * grp + rem % ug;
     const int n = w.order[u / p.HV];
     const int h = u % p.HV;
-    const int hk = h / (p.HV / p.HK);
     const int4 si = w.seq_info[n];
-    const int seq_start = si.x, seq_len = si.y, cid0 = si.z;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q4 = lane >> 4, r16 = lane & 15;
-    const int tcol0 = tile * C::BV;
-    const bool ptile = SUMMARY && tcol0 >= V;
-    InterLane<K, V, SUMMARY> L;
-    inter_lane_init<K, V, SUMMARY>(p, hk, wave, lane, L);
-    const int col = tcol0 + 16 * wave + r16;
+    InterCtx<K, V, SUMMARY> x;
+    x.seq_start = si.x;
+    x.seq_len = si.y;
+    x.cid0 = si.z;
+    x.nch = (x.seq_len + kChunk - 1) / kChunk;
+    x.h = h;
+    x.hk = h / (p.HV / p.HK);
+    x.tile = tile;
+    x.lane = threadIdx.x & 63;
+    x.ptile = SUMMARY && 32 * tile >= V;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = x.lane, c = lane & 31, hh = lane >> 5;
+    const int nch = x.nch;
+
+    if (wave >= 4) {
+        // ------------------------------------------------------------ loader waves
+        const int lh = wave - 4;
+        uint32_t qoff[C::NQ];
+        if (C::FWD) {
+#pragma unroll
+            for (int i = 0; i < C::FQ / 2; ++i) {
+                const int s = (2 * i + lh) * 64 + lane;
+                const int row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
+                qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
+            }
+        }
+        int ne0 = 0, nl = 0, ne1 = 0;
+        if (nch > 0) {
+            ne0 = inter_issue_early<K, V, SUMMARY>(p, w, e0, 0, lh, x, qoff);
+            nl = inter_issue_late<K, V, SUMMARY>(p, w, l0, 0, lh, x);
+            if (nch > 1) ne1 = inter_issue_early<K, V, SUMMARY>(p, w, e1, 1, lh, x, qoff);
+            vm_wait_n(nl + ne1);                              // early group of chunk 0
+        }
+        (void)ne0;
+        lds_barrier();                                        // chunk 0's early group is in
+        const int ne = ne1;                                   // early loads per chunk (same for every chunk)
+        for (int ci = 0; ci < nch; ++ci) {
+            const bool more1 = ci + 1 < nch, more2 = ci + 2 < nch;
+            lds_u32x4 *eb = (ci & 1) ? e1 : e0;
+            lds_u32x4 *nlb = (ci & 1) ? l0 : l1;
+            if (more1) inter_issue_late<K, V, SUMMARY>(p, w, nlb, ci + 1, lh, x);
+            vm_wait_n(more1 ? ne + nl : 0);                   // late group of chunk ci
+            lds_barrier();                                    // B1
+            if (more2) inter_issue_early<K, V, SUMMARY>(p, w, eb, ci + 2, lh, x, qoff);
+            vm_wait_n((more1 ? nl : 0) + (more2 ? ne : 0));   // early group of chunk ci + 1
+            lds_barrier();                                    // B2
+        }
+        return;
+    }
+
+    if (wave >= 2) {
+        // ------------------------------------------------------------ output waves
+        if (!C::FWD) {
+            lds_barrier();
+            for (int ci = 0; ci < nch; ++ci) {
+                lds_barrier();
+                lds_barrier();
+            }
+            return;
+        }
+        const int t = wave - 2;
+        f32x16 Y = {};
+        bf16x8 Pf[4], Pn[4];
+        float sq = 0.f, sqn = 0.f;
+        int o_start = 0, o_len = 0;
+        lds_barrier();
+        for (int ci = 0; ci < nch; ++ci) {
+            const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
+            // operands of chunk ci from the early group: q as B operands over all state
+            // rows (accumulator order within each 32-row tile), P^T of tile t, sq
+            bf16x8 Qf[2 * NKS];
+            {
+                const lds_u32x2 *ew = reinterpret_cast<const lds_u32x2 *>(eb);
+                const int row = 32 * t + c;
+#pragma unroll
+                for (int kk = 0; kk < 2 * NKS; ++kk) {
+                    const int col = 16 * kk + 4 * hh;
+                    const u32x2 a0 = ew[C::oQ * 128 + (swz<C::PPR>(row, col) >> 3)];
+                    const u32x2 a1 = ew[C::oQ * 128 + (swz<C::PPR>(row, col + 8) >> 3)];
+                    Qf[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    Pn[s] = (s < 2 || t != 0) ? __builtin_bit_cast(bf16x8, eb[(C::oP + (t != 0 ? 2 : 0) + s) * 64 + lane])
+                                              : bf16x8{};
+                sqn = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[32 * t + c];
+            }
+            // the previous chunk's output (its U_new was published before the last B2)
+            if (ci > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+            lds_barrier();                                    // B1: S of chunk ci is published
+            Y = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 2 * NKS; ++kk)
+                Y = mfma32(__builtin_bit_cast(bf16x8, xS[kk * 64 + lane]), Qf[kk], Y);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Pf[s] = Pn[s];
+            sq = sqn;
+            o_start = x.seq_start + kChunk * ci;
+            o_len = min(kChunk, x.seq_len - kChunk * ci);
+            lds_barrier();                                    // B2: U_new of chunk ci is published
+        }
+        if (nch > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+        return;
+    }
+
+    // ---------------------------------------------------------------- state waves
+    const int kh = wave;
+    const int col = 32 * tile + c;                      // this lane's state column
+    const int row0 = kh * C::KH;                        // first state row of this wave
     const int64_t unit = (int64_t)n * p.HV + h;
-
-    f32x4 S[K / 16];
-    if (!ptile) {
+    f32x16 S[NR];
+    if (!x.ptile) {
         if (p.s0) {
             const float *s0 = p.s0 + unit * K * V;
 #pragma unroll
-            for (int r = 0; r < K / 16; ++r)
+            for (int r = 0; r < NR; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) S[r][j] = s0[(int64_t)(16 * r + 4 * q4 + j) * V + col];
+                for (int e = 0; e < 16; ++e)
+                    S[r][e] = s0[(int64_t)(row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V + col];
         } else {
 #pragma unroll
-            for (int r = 0; r < K / 16; ++r) S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < NR; ++r) S[r] = f32x16{};
         }
     } else {
         const int pc = col - V;
 #pragma unroll
-        for (int r = 0; r < K / 16; ++r)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) S[r][j] = (16 * r + 4 * q4 + j == pc) ? 1.f : 0.f;
+            for (int e = 0; e < 16; ++e) S[r][e] = (row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3) == pc) ? 1.f : 0.f;
     }
-
-    const int nch = (seq_len + kChunk - 1) / kChunk;
-    f32x4 O[4];
-    int o_start = 0, o_len = 0;   // rows of O waiting to be stored (chunk just computed)
-    auto store_o = [&]() {
-        if (C::FWD && o_len > 0) {
-            __bf16 *ob = p.o + (int64_t)o_start * p.ost + (int64_t)h * p.osh + col;
-            if (o_len == kChunk) {
+    lds_barrier();
+    for (int ci = 0; ci < nch; ++ci) {
+        const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
+        const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
+        // ---- early operands: -W of this key half, U~ into X (kh = 0), 2^(gam_n)
+        bf16x8 Wf[2][NKS];
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ob[(int64_t)(16 * m + 4 * q4 + j) * p.ost] = f2bf(O[m][j]);
+            for (int kk = 0; kk < NKS; ++kk)
+                Wf[m][kk] = __builtin_bit_cast(bf16x8, eb[(C::oW + (kh * 2 + m) * NKS + kk) * 64 + lane]);
+        const float gl = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[64];
+        f32x16 X[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            if (kh == 0 && !x.ptile) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u4 = __builtin_bit_cast(f32x4, eb[(C::oU + 4 * m + j) * 64 + lane]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) X[m][4 * j + e] = u4[e];
+                }
             } else {
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int t = 16 * m + 4 * q4 + j;
-                        if (t < o_len) ob[(int64_t)t * p.ost] = f2bf(O[m][j]);
-                    }
+                X[m] = f32x16{};
             }
         }
-        o_len = 0;
-    };
-    auto chunk_start = [&](int ci) { return seq_start + kChunk * ci; };
-    auto chunk_len = [&](int ci) { return min(kChunk, seq_len - kChunk * ci); };
-
-    if (nch > 0)
-        inter_issue<K, V, SUMMARY>(p, w, buf0, cid0, chunk_start(0), chunk_len(0), h, tile, ptile, wave, lane, L);
-    lds_wait_vm();
-    __syncthreads();
-    for (int ci = 0; ci < nch; ci += 2) {
-        if (ci + 1 < nch)
-            inter_issue<K, V, SUMMARY>(p, w, buf1, cid0 + ci + 1, chunk_start(ci + 1), chunk_len(ci + 1), h,
-                                       tile, ptile, wave, lane, L);
-        store_o();
-        inter_chunk<K, V, SUMMARY>(p, buf0, S, ptile, wave, lane, O);
-        o_start = chunk_start(ci);
-        o_len = chunk_len(ci);
-        lds_wait_vm();
-        __syncthreads();
-        if (ci + 1 >= nch) break;
-        if (ci + 2 < nch)
-            inter_issue<K, V, SUMMARY>(p, w, buf0, cid0 + ci + 2, chunk_start(ci + 2), chunk_len(ci + 2), h,
-                                       tile, ptile, wave, lane, L);
-        store_o();
-        inter_chunk<K, V, SUMMARY>(p, buf1, S, ptile, wave, lane, O);
-        o_start = chunk_start(ci + 1);
-        o_len = chunk_len(ci + 1);
-        lds_wait_vm();
-        __syncthreads();
+        // ---- S as bf16 operands, published for the output waves
+        bf16x8 Sb[NKS];
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) {
+            Sb[kk] = pack32(S[kk >> 1], kk & 1);
+            if (C::FWD) xS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
+        }
+        // ---- X_kh = [U~] + (-W)_kh S_kh, published for the other state wave
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) X[m] = mfma32(Wf[m][kk], Sb[kk], X[m]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xX[((kh * 2 + m) * 4 + j) * 64 + lane] =
+                    __builtin_bit_cast(u32x4, f32x4{X[m][4 * j], X[m][4 * j + 1], X[m][4 * j + 2], X[m][4 * j + 3]});
+        lds_barrier();                                        // B1
+        // ---- U_new = X_0 + X_1; this wave publishes token tile kh of it
+        bf16x8 Kf[NR][4];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                Kf[r][s] = __builtin_bit_cast(bf16x8, lb[(C::oK + (kh * NR + r) * 4 + s) * 64 + lane]);
+        bf16x8 Ub[4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            f32x16 un;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 xo = __builtin_bit_cast(f32x4, xX[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) un[4 * j + e] = X[m][4 * j + e] + xo[e];
+            }
+            Ub[2 * m] = pack32(un, 0);
+            Ub[2 * m + 1] = pack32(un, 1);
+        }
+        if (C::FWD) {
+            // (a branch on the wave-uniform kh: indexing Ub with it would select element-wise)
+            if (kh == 0) {
+                xU[0 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[0]);
+                xU[1 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[1]);
+            } else {
+                xU[2 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[2]);
+                xU[3 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[3]);
+            }
+        }
+        // ---- own rows: S <- 2^(gam_n) S + (K diag(d))^T U_new
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            f32x16 d = {};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) d = mfma32(Kf[r][s], Ub[s], d);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S[r][e] = fmaf(gl, S[r][e], d[e]);
+        }
+        lds_barrier();                                        // B2
     }
-    store_o();
 
-    if (!ptile) {
+    if (!x.ptile) {
         if (p.sT) {
             float *dst = p.sT + unit * K * V;
 #pragma unroll
-            for (int r = 0; r < K / 16; ++r)
+            for (int r = 0; r < NR; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dst[(int64_t)(16 * r + 4 * q4 + j) * V + col] = S[r][j];
+                for (int e = 0; e < 16; ++e)
+                    dst[(int64_t)(row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V + col] = S[r][e];
         }
     } else {
         // transition[i][j] = P[j][i]: P column pc is transition row pc
         const int pc = col - V;
-        float *dst = p.trans + (unit * K + pc) * K;
+        float *dst = p.trans + (unit * K + pc) * K + row0 + 4 * hh;
 #pragma unroll
-        for (int r = 0; r < K / 16; ++r) *reinterpret_cast<f32x4 *>(dst + 16 * r + 4 * q4) = S[r];
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4 *>(dst + 32 * r + 8 * j) =
+                    f32x4{S[r][4 * j], S[r][4 * j + 1], S[r][4 * j + 2], S[r][4 * j + 3]};
     }
 }
 
@@ -952,7 +1196,7 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
     const int64_t blocks = (int64_t)p.N * p.HV * InterCfg<K, V, SUMMARY>::NT;
     if (blocks > 0) {
         before(LA_KERNEL_INTER);
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter<K, V, SUMMARY>), dim3((unsigned)blocks), dim3(128), 0, s, p, w);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter<K, V, SUMMARY>), dim3((unsigned)blocks), dim3(384), 0, s, p, w);
         after(LA_KERNEL_INTER);
     }
     return hipGetLastError();
