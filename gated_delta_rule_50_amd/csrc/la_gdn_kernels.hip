@@ -21,14 +21,16 @@
 // exponent above is <= 0, so no factor can overflow.
 //
 // Three kernels, all on the caller's stream:
-//   k_sched     one workgroup: validates cu_seqlens, builds the chunk table and
-//               the longest-first order of sequences
+//   k_sched     one workgroup (k_sched_small for at most 64 sequences): validates
+//               cu_seqlens, builds the chunk table and the longest-first order
+//               of sequences
 //   k_intra     per (chunk, value head): the prologue (row norms r_q, r_k and
 //               the chunk-local gate cumsum), A and P on MFMA, T by forward
 //               substitution in LDS, W and U~ on MFMA; writes the operands of the
 //               inter-chunk pass in MFMA fragment order
 //   k_inter     per (sequence, value head, 32 value columns): the sequential chunk
-//               loop; S stays in registers as MFMA accumulator tiles
+//               loop, split over state, output and loader waves; S stays in
+//               registers as MFMA accumulator tiles
 //
 // MFMA: v_mfma_f32_16x16x32_bf16.  Operand layout for one 64-lane wave, with
 // q4 = lane / 16 and r16 = lane % 16:
@@ -106,6 +108,78 @@ __device__ __forceinline__ bf16x8 pack_b(f32x4 a, f32x4 b)
         r[4 + j] = f2bf(b[j]);
     }
     return r;
+}
+
+// ---------------------------------------------------------------------------
+// k_sched_small: the scheduler for at most 64 sequences, one workgroup of 4
+// waves.  Wave 0 validates cu_seqlens, scans the chunk counts and orders the
+// sequences with cross-lane operations (lane i holds sequence i); then all four
+// waves fill the chunk table.  Its outputs are those of k_sched.
+
+__global__ __launch_bounds__(256) void k_sched_small(Prob p, Ws w)
+{
+    __shared__ int s_first[64], s_start[64], s_len[64];
+    __shared__ int s_total;
+    const int tid = threadIdx.x;
+    const int N = p.N;
+    if (tid < 16) w.hdr[kZeroOffset / 4 + tid] = 0;   // the zero block rows past a chunk's end load from
+    if (tid < 64) {
+        const int i = tid;
+        int start = 0, end = 0;
+        bool bad = false;
+        if (i < N) {
+            // cu_seqlens must start at 0, never decrease and end at T
+            start = p.cu[i];
+            end = p.cu[i + 1];
+            bad = start < 0 || (int64_t)start > p.T || end < start;
+            if (i == 0 && start != 0) bad = true;
+            if (i == N - 1 && (int64_t)end != p.T) bad = true;
+        }
+        const bool anybad = __any(bad);
+        const int len = (i < N && !anybad) ? end - start : 0;
+        if (anybad) start = 0;
+        const int nc = (len + kChunk - 1) / kChunk;
+        int incl = nc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (i >= off) incl += y;
+        }
+        const int first = incl - nc;
+        const int total = __shfl(incl, 63, 64);
+        // longest first, ties by index: the rank of (len, i) in that order
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = __shfl(len, j, 64);
+            rank += (lj > len || (lj == len && j < i)) ? 1 : 0;
+        }
+        if (i < N) {
+            w.seq_info[i] = make_int4(start, len, first, 0);
+            w.order[rank] = i;
+            s_first[i] = first;
+            s_start[i] = start;
+            s_len[i] = len;
+        }
+        if (i == 0) {
+            w.hdr[0] = anybad ? LA_DEVICE_BAD_CU_SEQLENS : LA_DEVICE_OK;
+            w.hdr[1] = total;
+            s_total = total;
+        }
+    }
+    __syncthreads();
+    // chunk c belongs to the last sequence whose first chunk id is <= c (never an
+    // empty one: an empty sequence shares its first id with the next)
+    const int total = s_total;
+    for (int c = tid; c < total; c += blockDim.x) {
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_first[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        const int j = c - s_first[lo];
+        const int st = s_start[lo] + kChunk * j;
+        w.chunks[c] = make_int4(lo, st, min(kChunk, s_start[lo] + s_len[lo] - st), j);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -719,8 +793,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //   output waves t = 0, 1 (waves 2, 3) produce the outputs of 32-token tile t;
 //   loader waves (waves 4, 5) issue every load of the chunk operands into LDS.
 // Per chunk, with S the chunk's start state:
-//   state wave kh:  X_kh = [U~ if kh = 0] + (-W)_kh S_kh  (its half of the
-//                   reduction); the X partials are swapped through LDS so that
+//   state wave kh:  X_kh = U~_kh + (-W)_kh S_kh  (its half of the reduction; U~
+//                   rows of token tile kh, zero elsewhere); the X partials are swapped through LDS so that
 //                   both hold U_new = X_0 + X_1 (fp32 addition commutes: the same
 //                   bits in both); S_kh <- 2^(gam_n) S_kh + (K diag(d))_kh^T U_new,
 //                   d = 2^(gam_n - gam) r_k.  It also publishes S (bf16) and its
@@ -735,16 +809,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // order.  Two barriers per chunk: B1 after the X partials and S are published,
 // B2 at the end of the chunk.
 //
-// Loads: the loader waves keep two LDS buffers of each group in flight: the
-// early group (-W, U~, raw q, P^T, per-chunk scalars), read before B1, and the
-// late group ((K diag(d))^T), read after it.  The early loads of chunk c + 2 are
-// issued right after B1 of chunk c and the late loads of chunk c + 1 right after
-// B2 of chunk c - 1, so each group has about one and a half chunk steps to land.
-// They are buffer loads into LDS written as asm: the compiler neither tracks them
-// nor adds waits for them; the loader waves issue nothing else, so each wait
-// counts exactly the loads issued after the ones it needs (loads complete in
-// issue order).  Rows of q past a chunk's end are out of the buffer's range and
-// load as zeros.  The barriers order LDS only.
+// Loads: the loader waves keep the operands of two chunks in LDS buffers.  Every
+// operand of chunk c is read before B1 of chunk c (the state waves read -W, U~ and
+// (K diag(d))^T at the start of the chunk), so right after that barrier the
+// loaders issue the state operands of chunk c + 2 into the same buffers, and
+// after B2 the output operands (raw q, P^T, scalars); before B2 of chunk c they
+// wait for all of chunk c + 1's.  Issue is spread over both halves of the chunk,
+// and each load has one to one and a half chunk steps to land.  The loads are
+// buffer loads into LDS written as asm: the compiler neither tracks them nor adds
+// waits for them; the loader waves issue nothing else, so each wait counts
+// exactly the loads issued after the ones it needs (loads complete in issue
+// order).  Rows of q past a chunk's end are out of the buffer's range and load as
+// zeros.  The barriers order LDS only.
 // For the summary the state is widened to [S | P] (K x (V + K)): the P columns
 // start at the identity and see U~ = 0, so they evolve as the product of the
 // decayed erase steps; there are no outputs.
@@ -758,12 +834,12 @@ struct InterCfg {
     static constexpr int NR = KH / 32;            // 32-row accumulator tiles per state wave
     static constexpr int NKS = KH / 16;           // reduction steps over a key half
     static constexpr int PPR = K / 8;             // 16-byte pieces per q row
-    // early group (1 KiB fragments): -W [kh][token tile][step], U~ [token tile][j],
-    // raw q (64 x K bf16, pieces swizzled by row), P^T (tile 0 steps 0..1, tile 1
-    // steps 0..3), scalars (sq[64], then 2^(gam_n) at 64)
+    // state operands (1 KiB fragments): -W [kh][token tile][step], U~ [token tile][j]
+    // and, in their own array, (K diag(d))^T [kh][row tile][token step]; output
+    // operands: raw q (64 x K bf16, pieces swizzled by row), P^T (tile 0 steps 0..1,
+    // tile 1 steps 0..3), scalars (sq[64], then 2^(gam_n) at 64)
     static constexpr int FW = 4 * NKS, FU = 8, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
     static constexpr int oW = 0, oU = oW + FW, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
-    // late group: (K diag(d))^T [kh][row tile][token step]
     static constexpr int FK = 4 * NKS, oK = 0, NFL = FK;
     static constexpr int NQ = FWD ? FQ / 2 : 1;   // q tile loads per loader wave
 };
@@ -815,10 +891,11 @@ struct InterCtx {
     bool ptile;
 };
 
-// Loader wave lh: its half of chunk ci's early group into `eb`.  Returns the number of loads.
+// Loader wave lh, its half of chunk ci's state operands: -W and U~ into `eb`,
+// (K diag(d))^T into `lb`.  Returns the number of loads.
 template <int K, int V, bool SUMMARY>
-__device__ __forceinline__ int inter_issue_early(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
-                                                 const InterCtx<K, V, SUMMARY> &x, const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ])
+__device__ __forceinline__ int inter_issue_state(const Prob &p, const Ws &w, lds_u32x4 *eb, lds_u32x4 *lb, int ci,
+                                                 int lh, const InterCtx<K, V, SUMMARY> &x)
 {
     using C = InterCfg<K, V, SUMMARY>;
     const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
@@ -831,6 +908,13 @@ __device__ __forceinline__ int inter_issue_early(const Prob &p, const Ws &w, lds
         b2l(rW, eb, C::oW + f, lo16, f * kFrag);
     }
     n += C::FW / 2;
+    const i32x4 rK = make_rsrc(reinterpret_cast<const char *>(w.KF) + chh * C::FK * kFrag, C::FK * kFrag);
+#pragma unroll
+    for (int i = 0; i < C::FK / 2; ++i) {
+        const int f = lh * (C::FK / 2) + i;
+        b2l(rK, lb, C::oK + f, lo16, f * kFrag);
+    }
+    n += C::FK / 2;
     if (!x.ptile) {
         const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UF) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
                                    C::FU * kFrag);
@@ -841,6 +925,20 @@ __device__ __forceinline__ int inter_issue_early(const Prob &p, const Ws &w, lds
         }
         n += C::FU / 2;
     }
+    return n;
+}
+
+// Loader wave lh, its half of chunk ci's output operands (raw q, P^T) and the
+// scalars (loader 0) into `eb`.  Returns the number of loads.
+template <int K, int V, bool SUMMARY>
+__device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
+                                                  const InterCtx<K, V, SUMMARY> &x,
+                                                  const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ])
+{
+    using C = InterCfg<K, V, SUMMARY>;
+    const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
+    const uint32_t lo16 = (uint32_t)x.lane * 16u;
+    int n = 0;
     if (C::FWD) {
         const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
         const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)x.hk * p.qsh,
@@ -858,23 +956,6 @@ __device__ __forceinline__ int inter_issue_early(const Prob &p, const Ws &w, lds
         n += 1;
     }
     return n;
-}
-
-// Loader wave lh: its half of chunk ci's late group into `lb`.  Returns the number of loads.
-template <int K, int V, bool SUMMARY>
-__device__ __forceinline__ int inter_issue_late(const Prob &p, const Ws &w, lds_u32x4 *lb, int ci, int lh,
-                                                const InterCtx<K, V, SUMMARY> &x)
-{
-    using C = InterCfg<K, V, SUMMARY>;
-    const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
-    const uint32_t lo16 = (uint32_t)x.lane * 16u;
-    const i32x4 rK = make_rsrc(reinterpret_cast<const char *>(w.KF) + chh * C::FK * kFrag, C::FK * kFrag);
-#pragma unroll
-    for (int i = 0; i < C::FK / 2; ++i) {
-        const int f = lh * (C::FK / 2) + i;
-        b2l(rK, lb, C::oK + f, lo16, f * kFrag);
-    }
-    return C::FK / 2;
 }
 
 // Output wave t: O^T of its token tile of the chunk whose Y^T it holds, stored
@@ -910,8 +991,8 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 {
     using C = InterCfg<K, V, SUMMARY>;
     constexpr int NR = C::NR, NKS = C::NKS;
-    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64];   // early group, two buffers
-    __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // late group, two buffers
+    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64];   // -W, U~, q, P^T, scalars: two buffers
+    __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // (K diag(d))^T: two buffers
     __shared__ u32x4 sX[2 * 8 * 64];                       // X partials: [kh][m][j][lane]
     __shared__ u32x4 sS[C::FWD ? 2 * NKS * 64 : 1];        // S (bf16 operands): [kh][step][lane]
     __shared__ u32x4 sU[C::FWD ? 4 * 64 : 1];              // U_new (bf16 operands): [token step][lane]
@@ -958,27 +1039,31 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                 qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
             }
         }
-        int ne0 = 0, nl = 0, ne1 = 0;
+        // chunk c's operands land in buffer c % 2.  After B1 of chunk c (every wave
+        // has read chunk c's operands by then) the state operands of chunk c + 2 are
+        // issued, after B2 of chunk c its output operands; before B2 of chunk c the
+        // loaders wait for all of chunk c + 1's, so that the state waves can read
+        // them as soon as chunk c + 1 starts.
+        int na = 0, nb = 0;
         if (nch > 0) {
-            ne0 = inter_issue_early<K, V, SUMMARY>(p, w, e0, 0, lh, x, qoff);
-            nl = inter_issue_late<K, V, SUMMARY>(p, w, l0, 0, lh, x);
-            if (nch > 1) ne1 = inter_issue_early<K, V, SUMMARY>(p, w, e1, 1, lh, x, qoff);
-            vm_wait_n(nl + ne1);                              // early group of chunk 0
+            na = inter_issue_state<K, V, SUMMARY>(p, w, e0, l0, 0, lh, x);
+            nb = inter_issue_output<K, V, SUMMARY>(p, w, e0, 0, lh, x, qoff);
+            if (nch > 1) inter_issue_state<K, V, SUMMARY>(p, w, e1, l1, 1, lh, x);
+            vm_wait_n(nch > 1 ? na : 0);                      // all of chunk 0
         }
-        (void)ne0;
-        lds_barrier();                                        // chunk 0's early group is in
-        const int ne = ne1;                                   // early loads per chunk (same for every chunk)
+        lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const bool more1 = ci + 1 < nch, more2 = ci + 2 < nch;
             lds_u32x4 *eb = (ci & 1) ? e1 : e0;
-            lds_u32x4 *nlb = (ci & 1) ? l0 : l1;
-            if (more1) inter_issue_late<K, V, SUMMARY>(p, w, nlb, ci + 1, lh, x);
-            vm_wait_n(more1 ? ne + nl : 0);                   // late group of chunk ci
+            lds_u32x4 *lb = (ci & 1) ? l1 : l0;
+            lds_u32x4 *neb = (ci & 1) ? e0 : e1;
+            if (more1) inter_issue_output<K, V, SUMMARY>(p, w, neb, ci + 1, lh, x, qoff);
             lds_barrier();                                    // B1
-            if (more2) inter_issue_early<K, V, SUMMARY>(p, w, eb, ci + 2, lh, x, qoff);
-            vm_wait_n((more1 ? nl : 0) + (more2 ? ne : 0));   // early group of chunk ci + 1
+            if (more2) inter_issue_state<K, V, SUMMARY>(p, w, eb, lb, ci + 2, lh, x);
+            vm_wait_n(more2 ? na : 0);                        // all of chunk ci + 1
             lds_barrier();                                    // B2
         }
+        (void)nb;
         return;
     }
 
@@ -994,14 +1079,18 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         }
         const int t = wave - 2;
         f32x16 Y = {};
-        bf16x8 Pf[4], Pn[4];
-        float sq = 0.f, sqn = 0.f;
+        bf16x8 Pf[4];
+        float sq = 0.f;
         int o_start = 0, o_len = 0;
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
-            // operands of chunk ci from the early group: q as B operands over all state
-            // rows (accumulator order within each 32-row tile), P^T of tile t, sq
+            // the previous chunk's output (its U_new was published before the last B2)
+            if (ci > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+            lds_barrier();                                    // B1: S of chunk ci is published
+            // operands of chunk ci (they stay in their buffer until the next chunk
+            // starts): q as B operands over all state rows (accumulator order within
+            // each 32-row tile), P^T of tile t, sq
             bf16x8 Qf[2 * NKS];
             {
                 const lds_u32x2 *ew = reinterpret_cast<const lds_u32x2 *>(eb);
@@ -1015,20 +1104,14 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    Pn[s] = (s < 2 || t != 0) ? __builtin_bit_cast(bf16x8, eb[(C::oP + (t != 0 ? 2 : 0) + s) * 64 + lane])
+                    Pf[s] = (s < 2 || t != 0) ? __builtin_bit_cast(bf16x8, eb[(C::oP + (t != 0 ? 2 : 0) + s) * 64 + lane])
                                               : bf16x8{};
-                sqn = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[32 * t + c];
+                sq = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[32 * t + c];
             }
-            // the previous chunk's output (its U_new was published before the last B2)
-            if (ci > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
-            lds_barrier();                                    // B1: S of chunk ci is published
             Y = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 2 * NKS; ++kk)
                 Y = mfma32(__builtin_bit_cast(bf16x8, xS[kk * 64 + lane]), Qf[kk], Y);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Pf[s] = Pn[s];
-            sq = sqn;
             o_start = x.seq_start + kChunk * ci;
             o_len = min(kChunk, x.seq_len - kChunk * ci);
             lds_barrier();                                    // B2: U_new of chunk ci is published
@@ -1038,6 +1121,8 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     }
 
     // ---------------------------------------------------------------- state waves
+    // (they carry the sequential chain: first claim on their SIMDs' issue slots)
+    __builtin_amdgcn_s_setprio(3);
     const int kh = wave;
     const int col = 32 * tile + c;                      // this lane's state column
     const int row0 = kh * C::KH;                        // first state row of this wave
@@ -1066,7 +1151,7 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     for (int ci = 0; ci < nch; ++ci) {
         const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
         const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
-        // ---- early operands: -W of this key half, U~ into X (kh = 0), 2^(gam_n)
+        // ---- operands: -W and (K diag(d))^T of this key half, U~ of token tile kh, 2^(gam_n)
         bf16x8 Wf[2][NKS];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -1074,10 +1159,11 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
             for (int kk = 0; kk < NKS; ++kk)
                 Wf[m][kk] = __builtin_bit_cast(bf16x8, eb[(C::oW + (kh * 2 + m) * NKS + kk) * 64 + lane]);
         const float gl = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[64];
+        // U~ enters through the accumulator of the wave whose token tile it is
         f32x16 X[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            if (kh == 0 && !x.ptile) {
+            if (m == kh && !x.ptile) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const f32x4 u4 = __builtin_bit_cast(f32x4, eb[(C::oU + 4 * m + j) * 64 + lane]);
@@ -1100,6 +1186,15 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
             for (int m = 0; m < 2; ++m) X[m] = mfma32(Wf[m][kk], Sb[kk], X[m]);
+        // (K diag(d))^T: read while the X products run (needed after B1)
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 Kf[NR][4];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                Kf[r][s] = __builtin_bit_cast(bf16x8, lb[(C::oK + (kh * NR + r) * 4 + s) * 64 + lane]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1108,12 +1203,6 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                     __builtin_bit_cast(u32x4, f32x4{X[m][4 * j], X[m][4 * j + 1], X[m][4 * j + 2], X[m][4 * j + 3]});
         lds_barrier();                                        // B1
         // ---- U_new = X_0 + X_1; this wave publishes token tile kh of it
-        bf16x8 Kf[NR][4];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                Kf[r][s] = __builtin_bit_cast(bf16x8, lb[(C::oK + (kh * NR + r) * 4 + s) * 64 + lane]);
         bf16x8 Ub[4];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -1183,7 +1272,10 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
     auto after = [&](int id) { if (hook) hook->after(id, s, hook->ctx); };
 
     before(LA_KERNEL_SCHED);
-    hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, s, p, w);
+    if (p.N <= 64)
+        hipLaunchKernelGGL(k_sched_small, dim3(1), dim3(256), 0, s, p, w);
+    else
+        hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, s, p, w);
     after(LA_KERNEL_SCHED);
     if (p.max_chunks > 0) {
         // persistent: at most two resident workgroups per CU, each walking (chunk, head) items
