@@ -315,6 +315,12 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) float lds_float;
 
+__device__ __forceinline__ uint2 lds_tr(const lds_char *p)
+{
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
 __device__ __forceinline__ uint2 lds_tr(const void *p)
 {
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
@@ -430,345 +436,313 @@ __device__ __forceinline__ void vm_wait()
 }
 
 // ---------------------------------------------------------------------------
-// k_intra: one workgroup of 4 waves per (chunk, value head).
-//
-// Phase 1 is the prologue (the fused prologue of the cudnn-frontend PR: q/k L2
-// norm and the chunk-local gate cumsum, in log2 units): every value it produces
-// is consumed in this workgroup or stored with the operands it scales, so it
-// runs here rather than as a separate pass over q and k.  Then A and P (MFMA),
-// T = (I + A)^-1 (forward substitution, fp32), W and U~ (MFMA; T diag(beta) is
-// split into bf16 high and low parts so that U~ keeps fp32 accuracy), and the
-// operands of the inter-chunk pass are written in fragment order.
+// Buffer loads into LDS and waits shared by both passes.
+
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);   // stride 0: raw byte addressing
+    r[2] = (int)bytes;                              // loads at or past this offset read zeros
+    r[3] = kBufferWord3;
+    return r;
+}
+
+// One 16-byte-per-lane buffer load into LDS fragment `f` of `buf` (lane l's 16
+// bytes land at fragment byte 16 l).  Written as asm so that the compiler neither
+// tracks these loads nor adds waits for them: every wait for them is explicit.
+// M0 needs one wait state before the load that uses it.
+__device__ __forceinline__ void b2l(i32x4 rsrc, lds_u32x4 *buf, int f, uint32_t voff, uint32_t soff)
+{
+    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(buf + f * 64);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(dst), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Waits until at most n (wave-uniform, < 64) vector memory operations of this
+// wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait_upto(int n)
+{
+    if constexpr (N >= 0) {
+        if (n == N) vm_wait<N>();
+        else vm_wait_upto<N - 1>(n);
+    }
+}
+__device__ __forceinline__ void vm_wait_n(int n)
+{
+    if (n >= 32) vm_wait_upto<63>(n);
+    else if (n >= 16) vm_wait_upto<31>(n);
+    else vm_wait_upto<15>(n);
+}
+
+// ---------------------------------------------------------------------------
+// k_intra: one workgroup of 4 waves per (chunk, value head) item, persistent
+// (two workgroups per CU walk the items chunk-major).  Per item:
+//   1. k, q (forward), g and beta of the chunk go straight into LDS with buffer
+//      loads (rows past the chunk's end are out of the buffer's range and read as
+//      zeros; the 16-byte pieces of a row are XOR-swizzled by the row, through the
+//      choice of source address, so that the operand reads below are free of bank
+//      conflicts).
+//   2. the Gram tiles G = K K^T (32 x 32 tiles on or below the diagonal) and,
+//      forward, P^T = K Q^T (on or above it) on bf16 MFMA; r_k from the diagonal
+//      of G, r_q from the q rows, the chunk-local inclusive gate cumsum gam (log2
+//      units).  Then A = [s < t] beta_t 2^(gam_t - gam_s) r_k,t r_k,s G goes to LDS
+//      as A^T, and P^T, scaled by scale r_q,t r_k,s 2^(gam_t - gam_s) and masked
+//      to s <= t, is written out from registers as the inter pass's operands.
+//      v is loaded into q's space meanwhile.
+//   3. T = (I + A)^-1: the 16 x 16 diagonal blocks D_b by forward substitution
+//      (one wave, one lane per column of each block), then block rows 1..3 of
+//          T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj
+//      on fp32 MFMA (16 x 16 x 4), one block per wave; the sum stays in
+//      registers, reduced over in accumulator order by the product with D_i.  T
+//      (on and below the diagonal) and A^T (above it) share one fp32 array.
+//      Meanwhile the other waves write (K diag(d))^T, d = 2^(gam_n - gam) r_k.
+//   4. Tw = T diag(beta 2^gam r_k) and T diag(beta) = Thi + Tlo, in bf16.
+//   5. -W (from W^T = K^T Tw^T) and U~ = (Thi + Tlo) V on bf16 MFMA, written from
+//      registers in the inter pass's operand order.
+
+// One 4-byte-per-lane buffer load into LDS (lane l's 4 bytes land at byte 4 l of `dst`).
+__device__ __forceinline__ void b2l_dword(i32x4 rsrc, lds_float *dst, uint32_t voff)
+{
+    const uint32_t d = (uint32_t)reinterpret_cast<uintptr_t>(dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(d), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// Loads a 64-row bf16 tile (rows start at `base`, `rs` bytes apart, `len` of them
+// valid) into `dst` as 16-byte pieces swizzled by row; instructions are shared
+// round-robin by `nw` waves.
+template <int D>
+__device__ __forceinline__ void intra_load_tile(lds_u32x4 *dst, const void *base, uint32_t rs, int len, int wave,
+                                                int lane, int nw)
+{
+    constexpr int PPR = D / 8;
+    const i32x4 r = make_rsrc(base, (uint32_t)len * rs);
+    for (int i = wave; i < PPR; i += nw) {
+        const int s = 64 * i + lane, row = s / PPR, pp = s % PPR;
+        b2l(r, dst, i, (uint32_t)row * rs + 16u * (uint32_t)(pp ^ (row % PPR)), 0);
+    }
+}
+
+// 16-byte operand read from a swizzled bf16 tile: row `row`, columns c0 .. c0 + 7 (c0 % 8 == 0).
+template <int PPR>
+__device__ __forceinline__ bf16x8 lds_row8(const lds_u32x4 *tile, int row, int c0)
+{
+    return __builtin_bit_cast(bf16x8, tile[row * PPR + ((c0 >> 3) ^ (row % PPR))]);
+}
+
+// Transposed reads from a swizzled bf16 tile M (64 rows, PPR pieces per row):
+// lane (c, hh) gets M[t0 + 8 hh + e][c0 + c], e = 0..7 (plain order; perm = false)
+// or M[t0 + 4 hh + i][c0 + c] in slot i and M[t0 + 8 + 4 hh + i][c0 + c] in slot
+// 4 + i (accumulator order; perm = true).
+template <int PPR, bool PERM>
+__device__ __forceinline__ bf16x8 lds_tr32s(const lds_u32x4 *tile, int t0, int c0, int lane)
+{
+    const lds_char *b = reinterpret_cast<const lds_char *>(tile);
+    const int lam = lane & 15, hh = lane >> 5;
+    const int row = t0 + (PERM ? 4 : 8) * hh + (lam >> 2);
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lam & 3);
+    const int row2 = row + (PERM ? 8 : 4);
+    const uint2 lo = lds_tr(b + swz<PPR>(row, col)), hi = lds_tr(b + swz<PPR>(row2, col));
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <int K, int V, bool FWD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_intra(Prob p, Ws w)
 {
-    constexpr int KP = K + 8;              // row stride of [token][k] bf16 tiles
-    constexpr int VP = V + 8;
-    constexpr int XP = KP > VP ? KP : VP;
-    constexpr int TP = 64 + 8;             // row stride of [token][token] bf16 tiles
-    constexpr int AP = 68;                 // row stride of [token][token] fp32 tiles
-    constexpr int KPR = K / 8, VPR = V / 8;  // 16-byte pieces per row
-    constexpr int NK = 64 * KPR / 256, NV = 64 * VPR / 256;
-    constexpr int NA = K / 32;
-    // LDS: sK raw k rows | sX q rows, later v rows | sA A^T (fp32) with the solve's
-    // scratch, later Tw, Thi, Tlo (bf16) | sT P (bf16), then T (fp32)
-    constexpr int SA_BYTES = (64 * AP * 4 + 7 * 1024 > 3 * 64 * TP * 2) ? 64 * AP * 4 + 7 * 1024 : 3 * 64 * TP * 2;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[64 * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 sX[64 * XP];
-    __shared__ __attribute__((aligned(16))) float sA[SA_BYTES / 4];
-    __shared__ __attribute__((aligned(16))) float sT[64 * AP];
-    __shared__ float s_rk[64], s_rq[64], s_gam[64], s_beta[64], s_fw[64];
-    __shared__ __attribute__((aligned(16))) float s_d[64];
-    __bf16 *const sTw = reinterpret_cast<__bf16 *>(sA);
-    __bf16 *const sThi = sTw + 64 * TP;
-    __bf16 *const sTlo = sThi + 64 * TP;
-    __bf16 *const sP = reinterpret_cast<__bf16 *>(sT);
+    constexpr int PK = K / 8, PV = V / 8;           // 16-byte pieces per k / v row
+    constexpr int DX = K > V ? K : V;
+    constexpr int PX = DX / 8;
+    constexpr int TS = 68;                          // row stride of the fp32 A^T / T array
+    constexpr int TP = 72;                          // row stride of the bf16 Tw, Thi, Tlo arrays
+    constexpr int NKS = K / 32;                     // reduction steps over a key half (inter pass)
+    constexpr int NR = K / 64;                      // 32-row tiles of a key half
+    __shared__ u32x4 sK_[64 * PK];                  // raw k rows, swizzled
+    __shared__ u32x4 sX_[64 * PX];                  // raw q rows (forward), then raw v rows, swizzled
+    __shared__ float sAT_[64 * TS];                 // A^T above the diagonal, T on and below it
+    __shared__ __attribute__((aligned(16))) __bf16 sTb_[3 * 64 * TP];   // Tw, Thi, Tlo
+    __shared__ __attribute__((aligned(16))) float sc_[7 * 64];          // per-token scalars
+    lds_u32x4 *const sK = (lds_u32x4 *)sK_;
+    lds_u32x4 *const sX = (lds_u32x4 *)sX_;
+    lds_float *const sAT = (lds_float *)sAT_;
+    lds_bf16 *const sTw = (lds_bf16 *)sTb_;
+    lds_bf16 *const sThi = sTw + 64 * TP;
+    lds_bf16 *const sTlo = sThi + 64 * TP;
+    lds_float *const s_g = (lds_float *)sc_;        // loaded g (0 past the end)
+    lds_float *const s_b = s_g + 64;                // loaded beta (0 past the end)
+    lds_float *const s_rk = s_g + 128;
+    lds_float *const s_rq = s_g + 192;
+    lds_float *const s_gam = s_g + 256;
+    lds_float *const s_fw = s_g + 320;              // beta 2^gam r_k
+    lds_float *const s_d = s_g + 384;               // 2^(gam_n - gam) r_k
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q4 = lane >> 4, r16 = lane & 15;
+    const int c = lane & 31, hh = lane >> 5;
     const int G = p.HV / p.HK;
-    const int items = w.hdr[1] * p.HV;      // (chunk, value head) pairs, chunk-major
+    const int items = w.hdr[1] * p.HV;              // (chunk, value head) pairs, chunk-major
 
-    // per-thread staging of the next item's rows (prefetched while the current one computes)
-    u32x4 kr[NK], qr[NK], vr[NV];
-    float gv = 0.f, bv = 0.f;
-    auto load_kq = [&](int it) {
-        const int4 ch = w.chunks[it / p.HV];
-        const int hk_ = (it % p.HV) / G;
-#pragma unroll
-        for (int j = 0; j < NK; ++j) {
-            const int e = tid + 256 * j, t = e / KPR, pc = e % KPR;
-            const int64_t tg = ch.y + t;
-            kr[j] = u32x4{0u, 0u, 0u, 0u};
-            qr[j] = u32x4{0u, 0u, 0u, 0u};
-            if (t < ch.z) {
-                kr[j] = *reinterpret_cast<const u32x4 *>(p.k + tg * p.kst + (int64_t)hk_ * p.ksh + 8 * pc);
-                if (FWD) qr[j] = *reinterpret_cast<const u32x4 *>(p.q + tg * p.qst + (int64_t)hk_ * p.qsh + 8 * pc);
-            }
-        }
-    };
-    auto load_vgb = [&](int it) {
-        const int4 ch = w.chunks[it / p.HV];
-        const int h_ = it % p.HV;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = tid + 256 * j, t = e / VPR, pc = e % VPR;
-            vr[j] = u32x4{0u, 0u, 0u, 0u};
-            if (t < ch.z)
-                vr[j] = *reinterpret_cast<const u32x4 *>(p.v + (int64_t)(ch.y + t) * p.vst + (int64_t)h_ * p.vsh + 8 * pc);
-        }
-        gv = 0.f;
-        bv = 0.f;
-        if (tid < ch.z) {
-            gv = p.g[(int64_t)(ch.y + tid) * p.gst + h_];
-            bv = p.beta[(int64_t)(ch.y + tid) * p.bst + h_];
-        }
-    };
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int ci = it / p.HV, h = it % p.HV, hk = h / G;
+        const int4 ch = w.chunks[ci];
+        const int start = ch.y, len = ch.z;
+        const int64_t ch_h = (int64_t)ci * p.HV + h;
 
-    int it = blockIdx.x;
-    if (it < items) {
-        load_kq(it);
-        load_vgb(it);
-    }
-    for (; it < items; it += gridDim.x) {
-        const int next = it + gridDim.x;
-        const int c = it / p.HV, h = it % p.HV;
-        const int len = w.chunks[c].z;
-        const int64_t ch_h = (int64_t)c * p.HV + h;
-
-        // ---- phase 1 (prologue): row norms, gate cumsum; k and q rows into LDS
-#pragma unroll
-        for (int j = 0; j < NK; ++j) {
-            const int e = tid + 256 * j, t = e / KPR, pc = e % KPR;
-            float sk = sumsq8(__builtin_bit_cast(uint4, kr[j]));
-            float sq = FWD ? sumsq8(__builtin_bit_cast(uint4, qr[j])) : 0.f;
-#pragma unroll
-            for (int off = 1; off < KPR; off <<= 1) {
-                sk += __shfl_xor(sk, off, KPR);
-                if (FWD) sq += __shfl_xor(sq, off, KPR);
-            }
-            if (pc == 0) {
-                const bool ok = t < len;
-                s_rk[t] = ok ? (p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.f;
-                s_rq[t] = (ok && FWD) ? (p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) : 0.f;
-            }
-            *reinterpret_cast<u32x4 *>(sK + t * KP + 8 * pc) = kr[j];
-            if (FWD) *reinterpret_cast<u32x4 *>(sX + t * XP + 8 * pc) = qr[j];
+        // ---- 1: k, q, g, beta into LDS
+        intra_load_tile<K>(sK, p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst, len, wave,
+                           lane, 4);
+        if (FWD)
+            intra_load_tile<K>(sX, p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst, len,
+                               wave, lane, 4);
+        if (wave == 3) {
+            const i32x4 rg = make_rsrc(p.g + (int64_t)start * p.gst + h, (uint32_t)len * 4u * (uint32_t)p.gst);
+            b2l_dword(rg, s_g, (uint32_t)lane * 4u * (uint32_t)p.gst);
+            const i32x4 rb = make_rsrc(p.beta + (int64_t)start * p.bst + h, (uint32_t)len * 4u * (uint32_t)p.bst);
+            b2l_dword(rb, s_b, (uint32_t)lane * 4u * (uint32_t)p.bst);
         }
-        if (wave == 0) {
-            // inclusive scan of g * log2(e) over the chunk (zeros past its end)
-            float x = gv * kLog2e;
+        vm_wait<0>();
+        lds_barrier();
+
+        // ---- 2a: r_q from the q rows (16 rows per wave, 4 lanes per row)
+        if (FWD) {
+            const int row = 16 * wave + (lane >> 2);
+            float s2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < PK / 4; ++i)
+                s2 += sumsq8(__builtin_bit_cast(uint4, lds_row8<PK>(sX, row, 8 * (4 * i + (lane & 3)))));
+            s2 += __shfl_xor(s2, 1, 64);
+            s2 += __shfl_xor(s2, 2, 64);
+            if ((lane & 3) == 0) s_rq[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f) : 0.f;
+        }
+        // ---- 2b: Gram tiles.  wave 0: G(0,0), P^T(0,0); wave 1: G(1,0); wave 2: G(1,1),
+        // P^T(1,1); wave 3: P^T(0,1) and the gate cumsum.  Tile (m, n): rows 32 m.., columns 32 n..
+        f32x16 Gt = {}, Pt = {};
+        const int gm = wave == 2 ? 1 : (wave == 1 ? 1 : 0), gn = wave == 2 ? 1 : 0;   // G tile of waves 0..2
+        const int pm = wave == 2 ? 1 : 0, pn = wave == 0 ? 0 : 1;                     // P^T tile of waves 0, 2, 3
+        if (wave < 3) {
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s)
+                Gt = mfma32(lds_row8<PK>(sK, 32 * gm + c, 16 * s + 8 * hh), lds_row8<PK>(sK, 32 * gn + c, 16 * s + 8 * hh), Gt);
+        }
+        if (FWD && wave != 1) {
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s)
+                Pt = mfma32(lds_row8<PK>(sK, 32 * pm + c, 16 * s + 8 * hh), lds_row8<PK>(sX, 32 * pn + c, 16 * s + 8 * hh), Pt);
+        }
+        if (wave == 3) {
+            // inclusive scan of g log2(e) (zeros past the end), beta
+            float xg = s_g[lane] * kLog2e;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
+                const float y = __shfl_up(xg, off, 64);
+                if (lane >= off) xg += y;
             }
-            s_gam[lane] = x;
-            s_beta[lane] = bv;
+            s_gam[lane] = xg;
         }
-        if (next < items) load_kq(next);      // k, q registers are free again
-        __syncthreads();
-        if (tid < 64) {
-            s_fw[tid] = s_beta[tid] * exp2f(s_gam[tid]) * s_rk[tid];
-            s_d[tid] = exp2f(s_gam[len - 1] - s_gam[tid]) * s_rk[tid];   // 0 past the end (r_k = 0)
+        // r_k from the diagonal of the diagonal G tiles: lane (c, hh) holds row c of its
+        // tile in register 4 j + i with 8 j + 4 hh + i = c
+        if (wave == 0 || wave == 2) {
+            float dg = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (8 * (e >> 2) + 4 * hh + (e & 3) == c) dg = Gt[e];
+            const int row = 32 * gm + c;
+            if (((c >> 2) & 1) == hh) s_rk[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(dg + 1e-6f) : 1.0f) : 0.f;
         }
+        lds_barrier();
 
-        // ---- phase 2: A (strictly lower, stored transposed) and P (lower incl. diagonal).
-        // Wave m computes row tile m against column tiles n <= m; all operand fragments
-        // are read first.
-        {
-            const int m = wave;
-            bf16x8 fa[NA], fq[NA];
-#pragma unroll
-            for (int kb = 0; kb < NA; ++kb) {
-                fa[kb] = lds_op(sK, KP, 16 * m + r16, 32 * kb, q4);
-                if (FWD) fq[kb] = lds_op(sX, XP, 16 * m + r16, 32 * kb, q4);
-            }
-            const float rq4[4] = {s_rq[16 * m + 4 * q4], s_rq[16 * m + 4 * q4 + 1], s_rq[16 * m + 4 * q4 + 2], s_rq[16 * m + 4 * q4 + 3]};
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                f32x4 av = {0.f, 0.f, 0.f, 0.f};
-                if (n <= m) {
-                    bf16x8 fb[NA];
-#pragma unroll
-                    for (int kb = 0; kb < NA; ++kb) fb[kb] = lds_op(sK, KP, 16 * n + r16, 32 * kb, q4);
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    f32x4 accq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < NA; ++kb) {
-                        acc = mfma16(fa[kb], fb[kb], acc);
-                        if (FWD) accq = mfma16(fq[kb], fb[kb], accq);
-                    }
-                    const int s = 16 * n + r16;
-                    const float gs = s_gam[s], rks = s_rk[s];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int t = 16 * m + 4 * q4 + j;
-                        const float dec = exp2f(fminf(s_gam[t] - gs, 0.f));
-                        av[j] = (s < t) ? s_beta[t] * dec * s_rk[t] * rks * acc[j] : 0.f;
-                        if (FWD) sP[t * TP + s] = f2bf((s <= t) ? p.scale * rq4[j] * rks * dec * accq[j] : 0.f);
-                    }
-                } else if (FWD) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sP[(16 * m + 4 * q4 + j) * TP + 16 * n + r16] = f2bf(0.f);
-                }
-                *reinterpret_cast<f32x4 *>(sA + (16 * n + r16) * AP + 16 * m + 4 * q4) = av;
-            }
-        }
-        __syncthreads();
-
-        // ---- phase 2b: P^T fragments (B operands, reduction over source tokens in
-        // accumulator order): fragment f < 2 is token tile 0, step f; 2 + s is token tile
-        // 1, step s (P is causal, so tile 0 needs steps 0 and 1 only); v rows into sX
-        if (FWD) {
-            const int c = lane & 31, hh = lane >> 5;
-            for (int f = wave; f < 6; f += 4) {
-                const int nt = f < 2 ? 0 : 1, s = f < 2 ? f : f - 2;
-                const __bf16 *pp = sP + (32 * nt + c) * TP + 16 * s + 4 * hh;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(pp);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(pp + 8);
-                w.PF[(ch_h * 6 + f) * 64 + lane] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int e = tid + 256 * j, t = e / VPR, pc = e % VPR;
-            *reinterpret_cast<u32x4 *>(sX + t * XP + 8 * pc) = vr[j];
-        }
+        // ---- 2c: v into q's space (every q read is done); per-token factors; A^T; P^T out
+        intra_load_tile<V>(sX, p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst, len, wave,
+                           lane, 4);
         const float gl = s_gam[len - 1];
-        if (next < items) load_vgb(next);     // v, g, beta registers are free again
-        __syncthreads();
-
-        // ---- phase 3: T = (I + A)^-1 in 16 x 16 blocks.  T is unit lower triangular
-        // with diagonal blocks D_i = (I + A_ii)^-1 and, below them,
-        //     T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj          (i > j, T_jj = D_j)
-        // (block forward substitution).  Wave b inverts D_b by forward substitution
-        // (lane c of the first 16 computes column c); then wave j fills block column
-        // j, top to bottom.  All in fp32.
-        {
-            float *sDT = sA + 64 * AP;            // D_i^T, [4][16][16]
-            float *sR = sDT + 4 * 256;            // per-wave 16 x 16 scratch
-            const int b = wave;
-            {
-                // D_b by column-oriented forward substitution: once row j is final, it is
-                // subtracted from every later row (A^T row j gives A[i][j] for all i).
-                const int cc = lane & 15;
-                float acc[16];
+        if (wave == 1) {
+            const int t = lane;
+            const float gm_t = s_gam[t], rk = s_rk[t];
+            s_fw[t] = s_b[t] * exp2f(gm_t) * rk;
+            s_d[t] = exp2f(gl - gm_t) * rk;   // 0 past the end (r_k = 0)
+            w.SC[ch_h * kScalars + t] = (FWD && t < len) ? p.scale * s_rq[t] * exp2f(gm_t) : 0.f;
+            if (t == 0) w.SC[ch_h * kScalars + 64] = exp2f(gl);
+        }
+        if (wave < 3) {
+            // A[t][s] for this lane's column s and rows t = 32 gm + 8 j + 4 hh + i, stored as A^T[s][t..]
+            const int s = 32 * gn + c;
+            const float gs = s_gam[s], rs = s_rk[s];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] = (i == cc) ? 1.f : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                const int t0 = 32 * gm + 8 * j + 4 * hh;
+                const f32x4 gt = *reinterpret_cast<const lds_f32x4 *>(s_gam + t0);
+                const f32x4 rt = *reinterpret_cast<const lds_f32x4 *>(s_rk + t0);
+                const f32x4 bt = *reinterpret_cast<const lds_f32x4 *>(s_b + t0);
+                f32x4 a;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float tj = acc[j];
-                    const float *arow = sA + (16 * b + j) * AP + 16 * b;   // A^T row j: A[i][j] for all i
-#pragma unroll
-                    for (int i = j + 1; i < 16; ++i) acc[i] = fmaf(-arow[i], tj, acc[i]);
-                }
-                if (lane < 16) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        sT[(16 * b + i) * AP + 16 * b + cc] = acc[i];
-                        sDT[b * 256 + cc * 16 + i] = acc[i];
-                    }
-                }
-            }
-            __syncthreads();
-            if (wave < 3) {
-                const int j = wave;
-                const int r4 = lane >> 4, cc = lane & 15;   // this lane: rows 4 r4 .. 4 r4 + 3, column cc
-                float *R = sR + wave * 256;
-                for (int i = j + 1; i < 4; ++i) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    for (int k = j; k < i; ++k) {
-#pragma unroll
-                        for (int x0 = 0; x0 < 16; x0 += 8) {
-                            f32x4 a4[8];
-                            float tk[8];
-#pragma unroll
-                            for (int x = 0; x < 8; ++x) {
-                                a4[x] = *reinterpret_cast<const f32x4 *>(sA + (16 * k + x0 + x) * AP + 16 * i + 4 * r4);
-                                tk[x] = sT[(16 * k + x0 + x) * AP + 16 * j + cc];
-                            }
-#pragma unroll
-                            for (int x = 0; x < 8; ++x)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) acc[e] = fmaf(a4[x][e], tk[x], acc[e]);
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) R[(4 * r4 + e) * 16 + cc] = acc[e];
-                    f32x4 tv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int x0 = 0; x0 < 16; x0 += 8) {
-                        f32x4 d4[8];
-                        float rx[8];
-#pragma unroll
-                        for (int x = 0; x < 8; ++x) {
-                            d4[x] = *reinterpret_cast<const f32x4 *>(sDT + i * 256 + (x0 + x) * 16 + 4 * r4);
-                            rx[x] = R[(x0 + x) * 16 + cc];
-                        }
-#pragma unroll
-                        for (int x = 0; x < 8; ++x)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) tv[e] = fmaf(-d4[x][e], rx[x], tv[e]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * r4 + e) * AP + 16 * j + cc] = tv[e];
-                }
-            } else {
-                // zeros above the diagonal blocks
-                for (int e = lane; e < 6 * 256; e += 64) {
-                    const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-                    const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-                    const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-                    sT[(16 * bi + r) * AP + 16 * bj + cc] = 0.f;
-                }
+                for (int i = 0; i < 4; ++i)
+                    a[i] = (s < t0 + i) ? bt[i] * exp2f(gt[i] - gs) * rt[i] * rs * Gt[4 * j + i] : 0.f;
+                *reinterpret_cast<lds_f32x4 *>(sAT + s * TS + t0) = a;
             }
         }
-        __syncthreads();
-
-        // ---- phase 3b: Tw = T diag(beta 2^gam r_k), T diag(beta) = Thi + Tlo (bf16)
+        if (FWD && wave != 1) {
+            // P^T tile (pm, pn): lane (c, hh) holds column t = 32 pn + c, rows s = 32 pm + 8 j + 4 hh + i;
+            // registers 8 js .. 8 js + 7 are the B operand of token tile pn, step 2 pm + js
+            const int t = 32 * pn + c;
+            const float gt = s_gam[t], rq = s_rq[t] * p.scale;
+            f32x16 pv;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int e = tid + 256 * j, i = e >> 6, col = e & 63;
-            const float tv = sT[i * AP + col];
-            const float tu = tv * s_beta[col];
-            const __bf16 hi = f2bf(tu);
-            sTw[i * TP + col] = f2bf(tv * s_fw[col]);
-            sThi[i * TP + col] = hi;
-            sTlo[i * TP + col] = f2bf(tu - bf2f(hi));
+            for (int j = 0; j < 4; ++j) {
+                const int s0 = 32 * pm + 8 * j + 4 * hh;
+                const f32x4 gs = *reinterpret_cast<const lds_f32x4 *>(s_gam + s0);
+                const f32x4 rs = *reinterpret_cast<const lds_f32x4 *>(s_rk + s0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pv[4 * j + i] = (s0 + i <= t) ? rq * rs[i] * exp2f(fminf(gt - gs[i], 0.f)) * Pt[4 * j + i] : 0.f;
+            }
+#pragma unroll
+            for (int js = 0; js < 2; ++js) {
+                const int f = (pn == 0 ? 0 : 2) + 2 * pm + js;
+                w.PF[(ch_h * 6 + f) * 64 + lane] = __builtin_bit_cast(uint4, pack32(pv, js));
+            }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- phase 4: on 32 x 32 tiles, from registers to the workspace in the operand
-        // order of the inter-chunk pass (accumulator order over the key half's rows):
-        //   -W, as W^T = K^T Tw^T (rows: key columns, columns: tokens), whose registers
-        //       8 s .. 8 s + 7 are exactly the A operand rows of W for one reduction step;
-        //   U~ = Thi V + Tlo V (tokens x value columns, fp32 accumulator tiles);
-        //   (K diag(d))^T, d = 2^(gam_n - gam) r_k, as A operands reducing over tokens.
-        {
-            constexpr int NKS = K / 32;          // reduction steps over a key half
-            constexpr int NR = K / 64;           // 32-row tiles of a key half
-            const int c = lane & 31, hh = lane >> 5;
+        // ---- 3a: diagonal blocks D_b = (I + A_bb)^-1 (wave 0; lane 16 b + cc holds column cc
+        // of D_b); (K diag(d))^T fragments (waves 1..3)
+        if (wave == 0) {
+            const int b = lane >> 4, cc = lane & 15, o = 16 * b;
+            float x[16];
 #pragma unroll
-            for (int i = 0; i < (2 * (K / 32)) / 4; ++i) {
-                const int pr = 4 * i + wave, nb = pr >> 1, m = pr & 1;
-                f32x16 acc = {};
+            for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8 ka = lds_tr32(sK, KP, 16 * s, 32 * nb, lane);
-                    const bf16x8 tb = *reinterpret_cast<const bf16x8 *>(sTw + (32 * m + c) * TP + 16 * s + 8 * hh);
-                    acc = mfma32(ka, tb, acc);
-                }
+            for (int k = 0; k < 15; ++k) {
+                // A[o + i][o + k] for i > k is A^T[o + k][o + i]
+                const lds_float *ar = sAT + (o + k) * TS + o;
+                const float xk = x[k];
 #pragma unroll
-                for (int js = 0; js < 2; ++js) {
-                    const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
-                    w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
-                }
+                for (int i = k + 1; i < 16; ++i) x[i] = fmaf(-ar[i], xk, x[i]);
             }
 #pragma unroll
-            for (int i = 0; i < (2 * (V / 32)) / 4; ++i) {
-                const int pr = 4 * i + wave, ct = pr >> 1, m = pr & 1;
-                f32x16 acc = {};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8 vb = lds_tr32(sX, XP, 16 * s, 32 * ct, lane);
-                    const int ro = (32 * m + c) * TP + 16 * s + 8 * hh;
-                    acc = mfma32(*reinterpret_cast<const bf16x8 *>(sThi + ro), vb, acc);
-                    acc = mfma32(*reinterpret_cast<const bf16x8 *>(sTlo + ro), vb, acc);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    w.UF[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] =
-                        make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-            }
-#pragma unroll
-            for (int i = 0; i < (K / 8) / 4; ++i) {
-                const int f = 4 * i + wave, kh = f / (4 * NR), r = (f / 4) % NR, s = f % 4;
-                const bf16x8 kt = lds_tr32p(sK, KP, 16 * s, kh * (K / 2) + 32 * r, lane);
-                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(s_d + 16 * s + 4 * hh);
-                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(s_d + 16 * s + 8 + 4 * hh);
+            for (int i = 0; i < 16; ++i) sAT[(o + i) * TS + o + cc] = x[i];
+        } else {
+            for (int f = wave - 1; f < K / 8; f += 3) {
+                const int kh = f / (4 * NR), r = (f / 4) % NR, s = f % 4;
+                const bf16x8 kt = lds_tr32s<PK, true>(sK, 16 * s, kh * (K / 2) + 32 * r, lane);
+                const f32x4 d0 = *reinterpret_cast<const lds_f32x4 *>(s_d + 16 * s + 4 * hh);
+                const f32x4 d1 = *reinterpret_cast<const lds_f32x4 *>(s_d + 16 * s + 8 + 4 * hh);
                 bf16x8 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -778,10 +752,103 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 w.KF[(ch_h * (K / 8) + f) * 64 + lane] = __builtin_bit_cast(uint4, o);
             }
         }
-        // per-chunk scalars of the inter-chunk pass: sq = scale r_q 2^gam per token, 2^(gam_n)
-        if (tid < 64) w.SC[ch_h * kScalars + tid] = (FWD && tid < len) ? p.scale * s_rq[tid] * exp2f(s_gam[tid]) : 0.f;
-        else if (tid == 64) w.SC[ch_h * kScalars + 64] = exp2f(gl);
-        __syncthreads();   // sK, sX and the scalars are rewritten by the next item
+        lds_barrier();
+
+        // ---- 3b: block rows 1..3.  Block (i, j), wave (i - 1 - j): R = sum_k A_ik T_kj, then
+        // T_ij = -D_i R with R's rows taken in accumulator order (lane (col cc, quad q) holds
+        // R[4 q + e][cc] in register e, which step e of the product reads as row 4 q + e).
+        {
+            const int cc = lane & 15, q = lane >> 4;
+#pragma unroll
+            for (int i = 1; i < 4; ++i) {
+                const int j = i - 1 - wave;
+                if (j >= 0) {
+                    f32x4 R = {0.f, 0.f, 0.f, 0.f};
+                    for (int k = j; k < i; ++k) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            // A_ik[cc][4 s + q] = A^T[16 k + 4 s + q][16 i + cc];  T_kj[4 s + q][cc]
+                            const float a = sAT[(16 * k + 4 * s + q) * TS + 16 * i + cc];
+                            const float t = sAT[(16 * k + 4 * s + q) * TS + 16 * j + cc];
+                            R = mfma_f32(a, t, R);
+                        }
+                    }
+                    f32x4 Tij = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        // -D_i[cc][4 q + s] pairs with R[4 q + s][.] held in register s
+                        const float dneg = -sAT[(16 * i + cc) * TS + 16 * i + 4 * q + s];
+                        Tij = mfma_f32(dneg, R[s], Tij);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sAT[(16 * i + 4 * q + e) * TS + 16 * j + cc] = Tij[e];
+                }
+                lds_barrier();
+            }
+        }
+
+        // ---- 4: Tw = T diag(fw), T diag(beta) = Thi + Tlo (bf16); T is zero above the diagonal
+        {
+            const int t = tid >> 2, s0 = 16 * (tid & 3);
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int s = s0 + 4 * g4;
+                const f32x4 tv = *reinterpret_cast<const lds_f32x4 *>(sAT + t * TS + s);
+                const f32x4 fw = *reinterpret_cast<const lds_f32x4 *>(s_fw + s);
+                const f32x4 bt = *reinterpret_cast<const lds_f32x4 *>(s_b + s);
+                bf16x4 ow, oh, ol;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float tt = (s + e <= t) ? tv[e] : 0.f;
+                    const float tu = tt * bt[e];
+                    const __bf16 hi = f2bf(tu);
+                    ow[e] = f2bf(tt * fw[e]);
+                    oh[e] = hi;
+                    ol[e] = f2bf(tu - bf2f(hi));
+                }
+                *reinterpret_cast<lds_bf16x4 *>(sTw + t * TP + s) = ow;
+                *reinterpret_cast<lds_bf16x4 *>(sThi + t * TP + s) = oh;
+                *reinterpret_cast<lds_bf16x4 *>(sTlo + t * TP + s) = ol;
+            }
+        }
+        vm_wait<0>();   // v
+        lds_barrier();
+
+        // ---- 5: -W (W^T = K^T Tw^T: rows key columns, columns tokens; registers 8 js ..
+        // 8 js + 7 are the A operand rows of W for one reduction step) and U~ = Thi V + Tlo V
+#pragma unroll
+        for (int i = 0; i < (2 * (K / 32)) / 4; ++i) {
+            const int pr = 4 * i + wave, nb = pr >> 1, m = pr & 1;
+            f32x16 acc = {};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 ka = lds_tr32s<PK, false>(sK, 16 * s, 32 * nb, lane);
+                const bf16x8 tb = *reinterpret_cast<const lds_bf16x8 *>(sTw + (32 * m + c) * TP + 16 * s + 8 * hh);
+                acc = mfma32(ka, tb, acc);
+            }
+#pragma unroll
+            for (int js = 0; js < 2; ++js) {
+                const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
+                w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < (2 * (V / 32)) / 4; ++i) {
+            const int pr = 4 * i + wave, ct = pr >> 1, m = pr & 1;
+            f32x16 acc = {};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 vb = lds_tr32s<PV, false>(sX, 16 * s, 32 * ct, lane);
+                const int ro = (32 * m + c) * TP + 16 * s + 8 * hh;
+                acc = mfma32(*reinterpret_cast<const lds_bf16x8 *>(sThi + ro), vb, acc);
+                acc = mfma32(*reinterpret_cast<const lds_bf16x8 *>(sTlo + ro), vb, acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w.UF[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] =
+                    make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+        }
+        lds_barrier();   // the next item's loads overwrite sK, sX and the scalars
     }
 }
 
@@ -843,47 +910,6 @@ struct InterCfg {
     static constexpr int FK = 4 * NKS, oK = 0, NFL = FK;
     static constexpr int NQ = FWD ? FQ / 2 : 1;   // q tile loads per loader wave
 };
-
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);   // stride 0: raw byte addressing
-    r[2] = (int)bytes;                              // loads at or past this offset read zeros
-    r[3] = kBufferWord3;
-    return r;
-}
-
-// One 16-byte-per-lane buffer load into LDS fragment `f` of `buf` (lane l's 16
-// bytes land at fragment byte 16 l).  Written as asm so that the compiler neither
-// tracks these loads nor adds waits for them: every wait for them is explicit.
-// M0 needs one wait state before the load that uses it.
-__device__ __forceinline__ void b2l(i32x4 rsrc, lds_u32x4 *buf, int f, uint32_t voff, uint32_t soff)
-{
-    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(buf + f * 64);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(dst), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
-}
-
-// Waits until at most n (wave-uniform, < 64) vector memory operations of this
-// wave are outstanding.
-template <int N>
-__device__ __forceinline__ void vm_wait_upto(int n)
-{
-    if constexpr (N >= 0) {
-        if (n == N) vm_wait<N>();
-        else vm_wait_upto<N - 1>(n);
-    }
-}
-__device__ __forceinline__ void vm_wait_n(int n)
-{
-    if (n >= 32) vm_wait_upto<63>(n);
-    else if (n >= 16) vm_wait_upto<31>(n);
-    else vm_wait_upto<15>(n);
-}
 
 template <int K, int V, bool SUMMARY>
 struct InterCtx {
