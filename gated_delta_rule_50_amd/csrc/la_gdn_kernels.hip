@@ -32,17 +32,12 @@
 //               loop, split over state, output and loader waves; S stays in
 //               registers as MFMA accumulator tiles
 //
-// MFMA: v_mfma_f32_16x16x32_bf16.  Operand layout for one 64-lane wave, with
-// q4 = lane / 16 and r16 = lane % 16:
-//   A (16 x 32): lane holds row r16, reduction slots 8 q4 .. 8 q4 + 7
-//   B (32 x 16): lane holds column r16, reduction slots 8 q4 .. 8 q4 + 7
-//   C (16 x 16): lane holds column r16, rows 4 q4 .. 4 q4 + 3
-// A reduction over 32 rows that are held as two C tiles (rows 16a..16a+15 and
-// 16a+16..16a+31) feeds the B operand straight from the accumulators when the
-// reduction index is permuted: slot 8 q4 + j is row 4 q4 + j of the first tile
-// for j < 4 and row 4 q4 + j - 4 of the second for j >= 4.  The A operand then
-// reads the matching columns, 32a + 4 q4 + {0..3} and 32a + 16 + 4 q4 + {0..3}.
-// This keeps S and U_new in registers between the products of the chain.
+// MFMA: v_mfma_f32_32x32x16_bf16 for the bf16 products and v_mfma_f32_16x16x4_f32
+// for the fp32 block products of the triangular solve (lane layouts with the
+// helpers below).  Products that reduce over the rows of an accumulator tile take
+// them in accumulator order, so S, U_new and the solve's partial sums feed the
+// next product without leaving registers, and the intra-chunk pass writes the
+// operands of the inter-chunk pass in that order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,11 +52,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ __bf16 f2bf(float x) { return static_cast<__bf16>(x); }
@@ -79,23 +69,6 @@ __device__ __forceinline__ float sumsq8(uint4 u)
         s = fmaf(hi, hi, s);
     }
     return s;
-}
-
-// Two 8-byte LDS reads: columns c0 + 4 q4 + {0..3} and c0 + 16 + 4 q4 + {0..3}
-// of row `row` (row stride `ld` elements): the permuted A operand.
-__device__ __forceinline__ bf16x8 lds_a_perm(const __bf16 *base, int ld, int row, int c0, int q4)
-{
-    const __bf16 *p = base + row * ld + c0 + 4 * q4;
-    const uint2 lo = *reinterpret_cast<const uint2 *>(p);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(p + 16);
-    uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-// One 16-byte LDS read: columns c0 + 8 q4 .. + 7 of row `row`: the plain operand.
-__device__ __forceinline__ bf16x8 lds_op(const __bf16 *base, int ld, int row, int c0, int q4)
-{
-    return *reinterpret_cast<const bf16x8 *>(base + row * ld + c0 + 8 * q4);
 }
 
 // Packs two accumulator tiles (rows 4 q4 + j of each) into a permuted B operand.
@@ -327,21 +300,6 @@ __device__ __forceinline__ uint2 lds_tr(const void *p)
     return __builtin_bit_cast(uint2, r);
 }
 
-// B operand reducing over rows: lane (g, r16) gets M[s0 + 8 g + i][c0 + r16], i = 0..7,
-// for a row-major bf16 tile with row stride ld (elements; ld * 2 a multiple of 8).
-__device__ __forceinline__ bf16x8 lds_b_tr(const __bf16 *base, int ld, int s0, int c0, int lane)
-{
-    const int g = lane >> 4, rho = lane & 15;
-    const __bf16 *p = base + (s0 + 8 * g + (rho >> 2)) * ld + c0 + 4 * (rho & 3);
-    const uint2 lo = lds_tr(p), hi = lds_tr(p + 4 * ld);
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
-__device__ __forceinline__ uint4 lds_rowperm(const __bf16 *base, int ld, int row, int c0, int q4)
-{
-    return __builtin_bit_cast(uint4, lds_a_perm(base, ld, row, c0, q4));
-}
-
 // Byte offset of element (row, col) (col a multiple of 4) in a 64 x (8 PPR) bf16
 // tile stored as 16-byte pieces with the piece index XOR-swizzled by the row.
 template <int PPR>
@@ -350,7 +308,6 @@ __device__ __forceinline__ int swz(int row, int col)
     return (row * PPR + ((col >> 3) ^ (row % PPR))) * 16 + ((col & 7) >> 2) * 8;
 }
 
-__device__ __forceinline__ void lds_wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // v_mfma_f32_32x32x16_bf16, with c = lane % 32 and hh = lane / 32:
@@ -388,28 +345,6 @@ __device__ __forceinline__ uint4 neg_bf16(bf16x8 x)
     u.z ^= 0x80008000u;
     u.w ^= 0x80008000u;
     return u;
-}
-
-// Operand of a product reducing over the rows of a row-major bf16 tile M (row
-// stride ld elements): lane (c, hh) gets M[t0 + 8 hh + e][c0 + c], e = 0..7 (plain
-// order).  As an A operand this is M^T (rows c0 .., reduction t0 ..); as a B
-// operand it is M itself.  Two transposed 8-byte reads.
-__device__ __forceinline__ bf16x8 lds_tr32(const __bf16 *base, int ld, int t0, int c0, int lane)
-{
-    const int lam = lane & 15;
-    const __bf16 *p = base + (t0 + 8 * (lane >> 5) + (lam >> 2)) * ld + c0 + 16 * ((lane >> 4) & 1) + 4 * (lam & 3);
-    const uint2 lo = lds_tr(p), hi = lds_tr(p + 4 * ld);
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
-// Same in accumulator order: lane (c, hh) gets M[t0 + 4 hh + i][c0 + c] in slot i
-// and M[t0 + 8 + 4 hh + i][c0 + c] in slot 4 + i.
-__device__ __forceinline__ bf16x8 lds_tr32p(const __bf16 *base, int ld, int t0, int c0, int lane)
-{
-    const int lam = lane & 15;
-    const __bf16 *p = base + (t0 + 4 * (lane >> 5) + (lam >> 2)) * ld + c0 + 16 * ((lane >> 4) & 1) + 4 * (lam & 3);
-    const uint2 lo = lds_tr(p), hi = lds_tr(p + 8 * ld);
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 // Workgroup barrier for LDS data exchanged between waves: waits for this wave's
