@@ -201,7 +201,7 @@ la::Prob make_prob(const la_gdn_desc *d, int l2norm)
     p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim_k);
     p.l2norm = l2norm ? 1 : 0;
     p.max_chunks = (int32_t)((d->total_tokens + 63) / 64 + d->num_seqs);
-    p.intra_grid = 2 * device_cu_count();
+    p.intra_grid = 3 * device_cu_count();
     p.qst = d->q_stride_t;
     p.qsh = d->q_stride_h;
     p.kst = d->k_stride_t;

@@ -422,7 +422,7 @@ __device__ __forceinline__ void vm_wait_n(int n)
 
 // ---------------------------------------------------------------------------
 // k_intra: one workgroup of 4 waves per (chunk, value head) item, persistent
-// (two workgroups per CU walk the items chunk-major).  Per item:
+// (three workgroups per CU walk the items chunk-major).  Per item:
 //   1. k, q (forward), g and beta of the chunk go straight into LDS with buffer
 //      loads (rows past the chunk's end are out of the buffer's range and read as
 //      zeros; the 16-byte pieces of a row are XOR-swizzled by the row, through the
@@ -500,26 +500,21 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
 }
 
 template <int K, int V, bool FWD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_intra(Prob p, Ws w)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_intra(Prob p, Ws w)
 {
     constexpr int PK = K / 8, PV = V / 8;           // 16-byte pieces per k / v row
     constexpr int DX = K > V ? K : V;
     constexpr int PX = DX / 8;
     constexpr int TS = 68;                          // row stride of the fp32 A^T / T array
-    constexpr int TP = 72;                          // row stride of the bf16 Tw, Thi, Tlo arrays
     constexpr int NKS = K / 32;                     // reduction steps over a key half (inter pass)
     constexpr int NR = K / 64;                      // 32-row tiles of a key half
     __shared__ u32x4 sK_[64 * PK];                  // raw k rows, swizzled
     __shared__ u32x4 sX_[64 * PX];                  // raw q rows (forward), then raw v rows, swizzled
     __shared__ float sAT_[64 * TS];                 // A^T above the diagonal, T on and below it
-    __shared__ __attribute__((aligned(16))) __bf16 sTb_[3 * 64 * TP];   // Tw, Thi, Tlo
     __shared__ __attribute__((aligned(16))) float sc_[7 * 64];          // per-token scalars
     lds_u32x4 *const sK = (lds_u32x4 *)sK_;
     lds_u32x4 *const sX = (lds_u32x4 *)sX_;
     lds_float *const sAT = (lds_float *)sAT_;
-    lds_bf16 *const sTw = (lds_bf16 *)sTb_;
-    lds_bf16 *const sThi = sTw + 64 * TP;
-    lds_bf16 *const sTlo = sThi + 64 * TP;
     lds_float *const s_g = (lds_float *)sc_;        // loaded g (0 past the end)
     lds_float *const s_b = s_g + 64;                // loaded beta (0 past the end)
     lds_float *const s_rk = s_g + 128;
@@ -722,66 +717,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
 
-        // ---- 4: Tw = T diag(fw), T diag(beta) = Thi + Tlo (bf16); T is zero above the diagonal
-        {
-            const int t = tid >> 2, s0 = 16 * (tid & 3);
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int s = s0 + 4 * g4;
-                const f32x4 tv = *reinterpret_cast<const lds_f32x4 *>(sAT + t * TS + s);
-                const f32x4 fw = *reinterpret_cast<const lds_f32x4 *>(s_fw + s);
-                const f32x4 bt = *reinterpret_cast<const lds_f32x4 *>(s_b + s);
-                bf16x4 ow, oh, ol;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float tt = (s + e <= t) ? tv[e] : 0.f;
-                    const float tu = tt * bt[e];
-                    const __bf16 hi = f2bf(tu);
-                    ow[e] = f2bf(tt * fw[e]);
-                    oh[e] = hi;
-                    ol[e] = f2bf(tu - bf2f(hi));
-                }
-                *reinterpret_cast<lds_bf16x4 *>(sTw + t * TP + s) = ow;
-                *reinterpret_cast<lds_bf16x4 *>(sThi + t * TP + s) = oh;
-                *reinterpret_cast<lds_bf16x4 *>(sTlo + t * TP + s) = ol;
-            }
-        }
         vm_wait<0>();   // v
         lds_barrier();
 
-        // ---- 5: -W (W^T = K^T Tw^T: rows key columns, columns tokens; registers 8 js ..
-        // 8 js + 7 are the A operand rows of W for one reduction step) and U~ = Thi V + Tlo V
+        // ---- 4: -W (W^T = K^T Tw^T: rows key columns, columns tokens; registers 8 js ..
+        // 8 js + 7 are the A operand rows of W for one reduction step) and U~ = Thi V + Tlo V,
+        // with Tw = T diag(beta 2^gam r_k) and T diag(beta) = Thi + Tlo (bf16) formed in
+        // registers: wave w only needs rows 32 m .. 32 m + 31 of them, m = w & 1, and both
+        // products read them at (row 32 m + c, columns 16 s + 8 hh .. + 7).  T is zero above
+        // the diagonal (the array holds A^T there).
+        {
+            const int m = wave & 1, t = 32 * m + c;
+            // T[t][16 s + 8 hh + e] (zero above the diagonal), times the per-column factor f
+            auto trow = [&](int s, const lds_float *f, float (&o)[8]) {
+                const int s0 = 16 * s + 8 * hh;
+                const f32x4 t0 = *reinterpret_cast<const lds_f32x4 *>(sAT + t * TS + s0);
+                const f32x4 t1 = *reinterpret_cast<const lds_f32x4 *>(sAT + t * TS + s0 + 4);
+                const f32x4 f0 = *reinterpret_cast<const lds_f32x4 *>(f + s0);
+                const f32x4 f1 = *reinterpret_cast<const lds_f32x4 *>(f + s0 + 4);
 #pragma unroll
-        for (int i = 0; i < (2 * (K / 32)) / 4; ++i) {
-            const int pr = 4 * i + wave, nb = pr >> 1, m = pr & 1;
-            f32x16 acc = {};
+                for (int e = 0; e < 8; ++e)
+                    o[e] = (s0 + e <= t) ? (e < 4 ? t0[e] * f0[e] : t1[e - 4] * f1[e - 4]) : 0.f;
+            };
+            {
+                bf16x8 tw[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float o[8];
+                    trow(s, s_fw, o);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tw[s][e] = f2bf(o[e]);
+                }
+#pragma unroll
+                for (int i = 0; i < (2 * (K / 32)) / 4; ++i) {
+                    const int nb = 2 * i + (wave >> 1);
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc = mfma32(lds_tr32s<PK, false>(sK, 16 * s, 32 * nb, lane), tw[s], acc);
+#pragma unroll
+                    for (int js = 0; js < 2; ++js) {
+                        const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
+                        w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+                    }
+                }
+            }
+            bf16x8 th[4], tl[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8 ka = lds_tr32s<PK, false>(sK, 16 * s, 32 * nb, lane);
-                const bf16x8 tb = *reinterpret_cast<const lds_bf16x8 *>(sTw + (32 * m + c) * TP + 16 * s + 8 * hh);
-                acc = mfma32(ka, tb, acc);
+                float o[8];
+                trow(s, s_b, o);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const __bf16 hi = f2bf(o[e]);
+                    th[s][e] = hi;
+                    tl[s][e] = f2bf(o[e] - bf2f(hi));
+                }
             }
 #pragma unroll
-            for (int js = 0; js < 2; ++js) {
-                const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
-                w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+            for (int i = 0; i < (2 * (V / 32)) / 4; ++i) {
+                const int ct = 2 * i + (wave >> 1);
+                f32x16 acc = {};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 vb = lds_tr32s<PV, false>(sX, 16 * s, 32 * ct, lane);
+                    acc = mfma32(th[s], vb, acc);
+                    acc = mfma32(tl[s], vb, acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w.UF[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] =
+                        make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
             }
-        }
-#pragma unroll
-        for (int i = 0; i < (2 * (V / 32)) / 4; ++i) {
-            const int pr = 4 * i + wave, ct = pr >> 1, m = pr & 1;
-            f32x16 acc = {};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 vb = lds_tr32s<PV, false>(sX, 16 * s, 32 * ct, lane);
-                const int ro = (32 * m + c) * TP + 16 * s + 8 * hh;
-                acc = mfma32(*reinterpret_cast<const lds_bf16x8 *>(sThi + ro), vb, acc);
-                acc = mfma32(*reinterpret_cast<const lds_bf16x8 *>(sTlo + ro), vb, acc);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                w.UF[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] =
-                    make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
         }
         lds_barrier();   // the next item's loads overwrite sK, sX and the scalars
     }
@@ -1239,7 +1245,7 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
         hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, s, p, w);
     after(LA_KERNEL_SCHED);
     if (p.max_chunks > 0) {
-        // persistent: at most two resident workgroups per CU, each walking (chunk, head) items
+        // persistent: at most three resident workgroups per CU, each walking (chunk, head) items
         const int64_t items = (int64_t)p.max_chunks * p.HV;
         const int grid = (int)(items < p.intra_grid ? items : p.intra_grid);
         before(LA_KERNEL_INTRA);
