@@ -34,9 +34,9 @@ def build(verbose: bool = False) -> str:
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    os.replace(tmp, LIB_PATH)
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
 

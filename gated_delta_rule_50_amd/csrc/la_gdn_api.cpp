@@ -250,7 +250,6 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     L.chunks = take(sizeof(int4) * (size_t)C);
     L.order = take(sizeof(int32_t) * (size_t)N);
     L.WF = take((size_t)(C * HV) * 64 * K * 2);           // 64 x K bf16
-    L.KF = take((size_t)(C * HV) * 64 * K * 2);           // K x 64 bf16
     L.PF = take(summary ? 0 : (size_t)(C * HV) * 6 * la::kFrag);
     L.UF = take((size_t)(C * HV) * 64 * V * 4);           // 64 x V fp32
     L.SC = take((size_t)(C * HV) * la::kScalars * 4);
@@ -267,7 +266,6 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.chunks = reinterpret_cast<int4 *>(b + L.chunks);
     w.order = reinterpret_cast<int32_t *>(b + L.order);
     w.WF = reinterpret_cast<uint4 *>(b + L.WF);
-    w.KF = reinterpret_cast<uint4 *>(b + L.KF);
     w.PF = summary ? nullptr : reinterpret_cast<uint4 *>(b + L.PF);
     w.UF = reinterpret_cast<float4 *>(b + L.UF);
     w.SC = reinterpret_cast<float *>(b + L.SC);

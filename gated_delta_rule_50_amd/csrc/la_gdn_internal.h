@@ -10,8 +10,7 @@ namespace la {
 constexpr int kChunk = 64;            // tokens per chunk; chunks restart at every sequence start
 constexpr int kSortMax = 8192;        // sequences the scheduler orders longest-first (more: batch order)
 constexpr int kFrag = 64 * 16;        // bytes of one MFMA operand fragment (64 lanes x 16 bytes)
-constexpr int kScalars = 256;         // fp32 per (chunk, v-head): sq[64], d[64], gl, zeros (one fragment)
-constexpr int kZeroOffset = 64;       // byte offset in hdr of a 64-byte block of zeros
+constexpr int kScalars = 256;         // fp32 per (chunk, v-head): d[64], sq[64], gl (one fragment)
 
 // Problem description as the kernels see it (element strides, device pointers).
 struct Prob {
@@ -40,20 +39,20 @@ struct Prob {
 // 16 s + 8 + 4 hh + i of step s in slots i and 4 + i).  Chunk ids index the
 // chunk table.
 struct Ws {
-    int32_t *hdr;      // [0] device status, [1] number of chunks, bytes 64..127 zeros
+    int32_t *hdr;      // [0] device status, [1] number of chunks
     int4 *seq_info;    // [N]  (start token, length, first chunk id, unused)
     int4 *chunks;      // [max_chunks]  (sequence, start token, length, chunk index in sequence)
     int32_t *order;    // [N]  sequences, longest first (ties: lower index first)
     uint4 *WF;         // [chunk, HV][key half][token tile][step]  -W, W = T diag(beta 2^gam r_k) K, A fragments
-    uint4 *KF;         // [chunk, HV][key half][row tile][token step]  (K diag(2^(gam_n - gam) r_k))^T, A fragments
     uint4 *PF;         // [chunk, HV][6]  P^T (masked decayed scaled q k^T), B fragments, forward only
     float4 *UF;        // [chunk, HV][V/32][token tile][4]  U~ = T diag(beta) V, fp32 accumulator tiles
-    float *SC;         // [chunk, HV, kScalars]  sq = scale r_q 2^gam per token, then gl = 2^gam_n
+    float *SC;         // [chunk, HV, kScalars]  per token: d = 2^(gam_n - gam) r_k at 0,
+                       // sq = scale r_q 2^gam at 64 (forward); gl = 2^gam_n at 192
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, WF, KF, PF, UF, SC, total;
+    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
                           bool summary);

@@ -21,16 +21,18 @@
 // exponent above is <= 0, so no factor can overflow.
 //
 // Three kernels, all on the caller's stream:
-//   k_sched     one workgroup (k_sched_small for at most 64 sequences): validates
-//               cu_seqlens, builds the chunk table and the longest-first order
-//               of sequences
-//   k_intra     per (chunk, value head): the prologue (row norms r_q, r_k and
-//               the chunk-local gate cumsum), A and P on MFMA, T by forward
-//               substitution in LDS, W and U~ on MFMA; writes the operands of the
-//               inter-chunk pass in MFMA fragment order
+//   k_sched     one workgroup, for more than 64 sequences: validates cu_seqlens,
+//               builds the chunk table and the longest-first order of sequences
+//               (for at most 64, every wave of k_intra maps its own chunks from
+//               cu_seqlens and one wave writes the tables)
+//   k_intra     per (chunk, value head): the prologue (row norms r_k and the
+//               chunk-local gate cumsum), A on MFMA, T by forward substitution in
+//               LDS, W and U~ on MFMA; writes -W and U~ in MFMA fragment order and
+//               the per-token scalars
 //   k_inter     per (sequence, value head, 32 value columns): the sequential chunk
 //               loop, split over state, output and loader waves; S stays in
-//               registers as MFMA accumulator tiles
+//               registers as MFMA accumulator tiles; r_q and P are formed here,
+//               from the raw q and k rows
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 for the bf16 products and v_mfma_f32_16x16x4_f32
 // for the fp32 block products of the triangular solve (lane layouts with the
@@ -52,6 +54,14 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// 2^x on the hardware exponential (v_exp_f32): one instruction, about 1 ulp; results
+// below the normal range flush to zero, and 2^-inf = 0.  The masked entries of the
+// decay factors pass -inf, so that masking is a select on the exponent and never a
+// branch.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ __bf16 f2bf(float x) { return static_cast<__bf16>(x); }
@@ -84,42 +94,45 @@ __device__ __forceinline__ bf16x8 pack_b(f32x4 a, f32x4 b)
 }
 
 // ---------------------------------------------------------------------------
-// k_sched_small: the scheduler for at most 64 sequences, one workgroup of 4
-// waves.  Wave 0 validates cu_seqlens, scans the chunk counts and orders the
-// sequences with cross-lane operations (lane i holds sequence i); then all four
-// waves fill the chunk table.  Its outputs are those of k_sched.
+// The scheduler for at most 64 sequences, run by every wave of the intra-chunk
+// pass instead of a kernel of its own: lane i holds sequence i.  Validates
+// cu_seqlens, scans the chunk counts and, in one wave of the grid, writes what
+// the inter-chunk pass reads (status, sequence table, longest-first order).
 
-__global__ __launch_bounds__(256) void k_sched_small(Prob p, Ws w)
+struct SmallMap {
+    int start, end, first;   // this lane's sequence: tokens [start, end), first chunk id
+    int total;               // chunks of the batch (0 if cu_seqlens is malformed)
+};
+
+__device__ __forceinline__ SmallMap small_map(const Prob &p, const Ws &w, bool publish)
 {
-    __shared__ int s_first[64], s_start[64], s_len[64];
-    __shared__ int s_total;
-    const int tid = threadIdx.x;
-    const int N = p.N;
-    if (tid < 16) w.hdr[kZeroOffset / 4 + tid] = 0;   // the zero block rows past a chunk's end load from
-    if (tid < 64) {
-        const int i = tid;
-        int start = 0, end = 0;
-        bool bad = false;
-        if (i < N) {
-            // cu_seqlens must start at 0, never decrease and end at T
-            start = p.cu[i];
-            end = p.cu[i + 1];
-            bad = start < 0 || (int64_t)start > p.T || end < start;
-            if (i == 0 && start != 0) bad = true;
-            if (i == N - 1 && (int64_t)end != p.T) bad = true;
-        }
-        const bool anybad = __any(bad);
-        const int len = (i < N && !anybad) ? end - start : 0;
-        if (anybad) start = 0;
-        const int nc = (len + kChunk - 1) / kChunk;
-        int incl = nc;
+    const int i = threadIdx.x & 63, N = p.N;
+    int start = 0, end = 0;
+    bool bad = false;
+    if (i < N) {
+        // cu_seqlens must start at 0, never decrease and end at T
+        start = p.cu[i];
+        end = p.cu[i + 1];
+        bad = start < 0 || (int64_t)start > p.T || end < start;
+        if (i == 0 && start != 0) bad = true;
+        if (i == N - 1 && (int64_t)end != p.T) bad = true;
+    }
+    const bool anybad = __any(bad);
+    if (anybad) start = end = 0;
+    const int len = end - start;
+    const int nc = (len + kChunk - 1) / kChunk;
+    int incl = nc;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off, 64);
-            if (i >= off) incl += y;
-        }
-        const int first = incl - nc;
-        const int total = __shfl(incl, 63, 64);
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (i >= off) incl += y;
+    }
+    SmallMap m;
+    m.start = start;
+    m.end = end;
+    m.first = incl - nc;
+    m.total = __shfl(incl, 63, 64);
+    if (publish) {
         // longest first, ties by index: the rank of (len, i) in that order
         int rank = 0;
         for (int j = 0; j < N; ++j) {
@@ -127,32 +140,15 @@ __global__ __launch_bounds__(256) void k_sched_small(Prob p, Ws w)
             rank += (lj > len || (lj == len && j < i)) ? 1 : 0;
         }
         if (i < N) {
-            w.seq_info[i] = make_int4(start, len, first, 0);
+            w.seq_info[i] = make_int4(start, len, m.first, 0);
             w.order[rank] = i;
-            s_first[i] = first;
-            s_start[i] = start;
-            s_len[i] = len;
         }
         if (i == 0) {
             w.hdr[0] = anybad ? LA_DEVICE_BAD_CU_SEQLENS : LA_DEVICE_OK;
-            w.hdr[1] = total;
-            s_total = total;
+            w.hdr[1] = m.total;
         }
     }
-    __syncthreads();
-    // chunk c belongs to the last sequence whose first chunk id is <= c (never an
-    // empty one: an empty sequence shares its first id with the next)
-    const int total = s_total;
-    for (int c = tid; c < total; c += blockDim.x) {
-        int lo = 0, hi = N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_first[mid] <= c) lo = mid; else hi = mid - 1;
-        }
-        const int j = c - s_first[lo];
-        const int st = s_start[lo] + kChunk * j;
-        w.chunks[c] = make_int4(lo, st, min(kChunk, s_start[lo] + s_len[lo] - st), j);
-    }
+    return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -170,7 +166,6 @@ __global__ __launch_bounds__(1024) void k_sched(Prob p, Ws w)
     const int N = p.N;
     const bool small = N <= kSortMax;
     if (tid == 0) s_bad = 0;
-    if (tid < 16) w.hdr[kZeroOffset / 4 + tid] = 0;   // the zero block rows past a chunk's end load from
     __syncthreads();
 
     // cu_seqlens must start at 0, never decrease and end at T.
@@ -423,30 +418,27 @@ __device__ __forceinline__ void vm_wait_n(int n)
 // ---------------------------------------------------------------------------
 // k_intra: one workgroup of 4 waves per (chunk, value head) item, persistent
 // (three workgroups per CU walk the items chunk-major).  Per item:
-//   1. k, q (forward), g and beta of the chunk go straight into LDS with buffer
-//      loads (rows past the chunk's end are out of the buffer's range and read as
-//      zeros; the 16-byte pieces of a row are XOR-swizzled by the row, through the
-//      choice of source address, so that the operand reads below are free of bank
-//      conflicts).
-//   2. the Gram tiles G = K K^T (32 x 32 tiles on or below the diagonal) and,
-//      forward, P^T = K Q^T (on or above it) on bf16 MFMA; r_k from the diagonal
-//      of G, r_q from the q rows, the chunk-local inclusive gate cumsum gam (log2
-//      units).  Then A = [s < t] beta_t 2^(gam_t - gam_s) r_k,t r_k,s G goes to LDS
-//      as A^T, and P^T, scaled by scale r_q,t r_k,s 2^(gam_t - gam_s) and masked
-//      to s <= t, is written out from registers as the inter pass's operands.
-//      v is loaded into q's space meanwhile.
+//   1. k, v, g and beta of the chunk go straight into LDS with buffer loads (rows
+//      past the chunk's end are out of the buffer's range and read as zeros; the
+//      16-byte pieces of a row are XOR-swizzled by the row, through the choice of
+//      source address, so that the operand reads below are free of bank
+//      conflicts).  Only k, g and beta are waited for here: v lands during 2 and 3.
+//   2. the Gram tiles G = K K^T (32 x 32 tiles on or below the diagonal) on bf16
+//      MFMA; r_k from the diagonal of G; the chunk-local inclusive gate cumsum gam
+//      (log2 units).  Then A = [s < t] beta_t 2^(gam_t - gam_s) r_k,t r_k,s G goes
+//      to LDS as A^T, and the per-token scalars of the inter pass (d = 2^(gam_n -
+//      gam) r_k, gam, r_k, 2^gam_n) are written out.
 //   3. T = (I + A)^-1: the 16 x 16 diagonal blocks D_b by forward substitution
 //      (one wave, one lane per column of each block), then block rows 1..3 of
 //          T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj
 //      on fp32 MFMA (16 x 16 x 4), one block per wave; the sum stays in
 //      registers, reduced over in accumulator order by the product with D_i.  T
 //      (on and below the diagonal) and A^T (above it) share one fp32 array.
-//      Meanwhile the other waves write (K diag(d))^T, d = 2^(gam_n - gam) r_k.
-//   4. Tw = T diag(beta 2^gam r_k) and T diag(beta) = Thi + Tlo, in bf16.
-//   5. -W (from W^T = K^T Tw^T) and U~ = (Thi + Tlo) V on bf16 MFMA, written from
-//      registers in the inter pass's operand order.
+//   4. -W (from W^T = K^T Tw^T) and U~ = (Thi + Tlo) V on bf16 MFMA, with Tw = T
+//      diag(beta 2^gam r_k) and T diag(beta) = Thi + Tlo (bf16) formed in
+//      registers; both are written from registers in the inter pass's operand
+//      order.
 
-// One 4-byte-per-lane buffer load into LDS (lane l's 4 bytes land at byte 4 l of `dst`).
 __device__ __forceinline__ void b2l_dword(i32x4 rsrc, lds_float *dst, uint32_t voff)
 {
     const uint32_t d = (uint32_t)reinterpret_cast<uintptr_t>(dst);
@@ -507,11 +499,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     constexpr int PX = DX / 8;
     constexpr int TS = 68;                          // row stride of the fp32 A^T / T array
     constexpr int NKS = K / 32;                     // reduction steps over a key half (inter pass)
-    constexpr int NR = K / 64;                      // 32-row tiles of a key half
     __shared__ u32x4 sK_[64 * PK];                  // raw k rows, swizzled
     __shared__ u32x4 sX_[64 * PX];                  // raw q rows (forward), then raw v rows, swizzled
     __shared__ float sAT_[64 * TS];                 // A^T above the diagonal, T on and below it
-    __shared__ __attribute__((aligned(16))) float sc_[7 * 64];          // per-token scalars
+    __shared__ __attribute__((aligned(16))) float sc_[6 * 64];          // per-token scalars
     lds_u32x4 *const sK = (lds_u32x4 *)sK_;
     lds_u32x4 *const sX = (lds_u32x4 *)sX_;
     lds_float *const sAT = (lds_float *)sAT_;
@@ -521,18 +512,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     lds_float *const s_rq = s_g + 192;
     lds_float *const s_gam = s_g + 256;
     lds_float *const s_fw = s_g + 320;              // beta 2^gam r_k
-    lds_float *const s_d = s_g + 384;               // 2^(gam_n - gam) r_k
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, hh = lane >> 5;
     const int G = p.HV / p.HK;
-    const int items = w.hdr[1] * p.HV;              // (chunk, value head) pairs, chunk-major
+    // chunk table: from cu_seqlens in registers for at most 64 sequences, else the scheduler's
+    const bool small = p.N <= 64;
+    SmallMap sm{};
+    if (small) sm = small_map(p, w, blockIdx.x == 0 && wave == 0);
+    const int items = (small ? sm.total : w.hdr[1]) * p.HV;   // (chunk, value head) pairs, chunk-major
 
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int ci = it / p.HV, h = it % p.HV, hk = h / G;
-        const int4 ch = w.chunks[ci];
-        const int start = ch.y, len = ch.z;
+        int start, len;
+        if (small) {
+            // chunk ci belongs to the last sequence whose first chunk id is <= ci (never an
+            // empty one: an empty sequence shares its first id with the next)
+            const uint64_t owns = __ballot(lane < p.N && sm.first <= ci);
+            const int n = 63 - __builtin_clzll(owns);
+            start = __builtin_amdgcn_readfirstlane(__shfl(sm.start, n, 64) + kChunk * (ci - __shfl(sm.first, n, 64)));
+            len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, n, 64) - start));
+        } else {
+            const int4 ch = w.chunks[ci];
+            start = ch.y;
+            len = ch.z;
+        }
         const int64_t ch_h = (int64_t)ci * p.HV + h;
 
         // ---- 1: k, q, g, beta into LDS
@@ -564,8 +569,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // ---- 2b: Gram tiles.  wave 0: G(0,0), P^T(0,0); wave 1: G(1,0); wave 2: G(1,1),
         // P^T(1,1); wave 3: P^T(0,1) and the gate cumsum.  Tile (m, n): rows 32 m.., columns 32 n..
         f32x16 Gt = {}, Pt = {};
-        const int gm = wave == 2 ? 1 : (wave == 1 ? 1 : 0), gn = wave == 2 ? 1 : 0;   // G tile of waves 0..2
-        const int pm = wave == 2 ? 1 : 0, pn = wave == 0 ? 0 : 1;                     // P^T tile of waves 0, 2, 3
+        const int gm = wave == 0 ? 0 : 1, gn = wave == 2 ? 1 : 0;   // G tile of waves 0..2
+        const int pm = wave == 2 ? 1 : 0, pn = wave == 0 ? 0 : 1;   // P^T tile of waves 0, 2, 3
         if (wave < 3) {
 #pragma unroll
             for (int s = 0; s < K / 16; ++s)
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 Pt = mfma32(lds_row8<PK>(sK, 32 * pm + c, 16 * s + 8 * hh), lds_row8<PK>(sX, 32 * pn + c, 16 * s + 8 * hh), Pt);
         }
         if (wave == 3) {
-            // inclusive scan of g log2(e) (zeros past the end), beta
+            // inclusive scan of g log2(e) (zeros past the end)
             float xg = s_g[lane] * kLog2e;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -598,17 +603,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         lds_barrier();
 
-        // ---- 2c: v into q's space (every q read is done); per-token factors; A^T; P^T out
+        // ---- 2c: v into q's space (every q read is done); per-token factors and the inter
+        // pass's scalars (wave 1); A^T (waves 0..2); P^T out (waves 0, 2, 3)
         intra_load_tile<V>(sX, p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst, len, wave,
                            lane, 4);
         const float gl = s_gam[len - 1];
         if (wave == 1) {
             const int t = lane;
             const float gm_t = s_gam[t], rk = s_rk[t];
-            s_fw[t] = s_b[t] * exp2f(gm_t) * rk;
-            s_d[t] = exp2f(gl - gm_t) * rk;   // 0 past the end (r_k = 0)
-            w.SC[ch_h * kScalars + t] = (FWD && t < len) ? p.scale * s_rq[t] * exp2f(gm_t) : 0.f;
-            if (t == 0) w.SC[ch_h * kScalars + 64] = exp2f(gl);
+            s_fw[t] = s_b[t] * exp2_hw(gm_t) * rk;
+            float *sc = w.SC + ch_h * kScalars;
+            sc[t] = exp2_hw(gl - gm_t) * rk;                                         // d (0 past the end)
+            sc[64 + t] = (FWD && t < len) ? p.scale * s_rq[t] * exp2_hw(gm_t) : 0.f;   // sq
+            if (t == 0) sc[192] = exp2_hw(gl);
         }
         if (wave < 3) {
             // A[t][s] for this lane's column s and rows t = 32 gm + 8 j + 4 hh + i, stored as A^T[s][t..]
@@ -622,8 +629,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const f32x4 bt = *reinterpret_cast<const lds_f32x4 *>(s_b + t0);
                 f32x4 a;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a[i] = (s < t0 + i) ? bt[i] * exp2f(gt[i] - gs) * rt[i] * rs * Gt[4 * j + i] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const float e = exp2_hw(s < t0 + i ? gt[i] - gs : kNegInf);
+                    a[i] = bt[i] * rt[i] * rs * e * Gt[4 * j + i];
+                }
                 *reinterpret_cast<lds_f32x4 *>(sAT + s * TS + t0) = a;
             }
         }
@@ -639,8 +648,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const f32x4 gs = *reinterpret_cast<const lds_f32x4 *>(s_gam + s0);
                 const f32x4 rs = *reinterpret_cast<const lds_f32x4 *>(s_rk + s0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pv[4 * j + i] = (s0 + i <= t) ? rq * rs[i] * exp2f(fminf(gt - gs[i], 0.f)) * Pt[4 * j + i] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const float e = exp2_hw(s0 + i <= t ? gt - gs[i] : kNegInf);
+                    pv[4 * j + i] = rq * rs[i] * e * Pt[4 * j + i];
+                }
             }
 #pragma unroll
             for (int js = 0; js < 2; ++js) {
@@ -650,8 +661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         lds_barrier();
 
-        // ---- 3a: diagonal blocks D_b = (I + A_bb)^-1 (wave 0; lane 16 b + cc holds column cc
-        // of D_b); (K diag(d))^T fragments (waves 1..3)
+        // ---- 3a: diagonal blocks D_b = (I + A_bb)^-1 (wave 0; lane 16 b + cc holds column cc of D_b)
         if (wave == 0) {
             const int b = lane >> 4, cc = lane & 15, o = 16 * b;
             float x[16];
@@ -667,20 +677,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) sAT[(o + i) * TS + o + cc] = x[i];
-        } else {
-            for (int f = wave - 1; f < K / 8; f += 3) {
-                const int kh = f / (4 * NR), r = (f / 4) % NR, s = f % 4;
-                const bf16x8 kt = lds_tr32s<PK, true>(sK, 16 * s, kh * (K / 2) + 32 * r, lane);
-                const f32x4 d0 = *reinterpret_cast<const lds_f32x4 *>(s_d + 16 * s + 4 * hh);
-                const f32x4 d1 = *reinterpret_cast<const lds_f32x4 *>(s_d + 16 * s + 8 + 4 * hh);
-                bf16x8 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o[e] = f2bf(bf2f(kt[e]) * d0[e]);
-                    o[4 + e] = f2bf(bf2f(kt[4 + e]) * d1[e]);
-                }
-                w.KF[(ch_h * (K / 8) + f) * 64 + lane] = __builtin_bit_cast(uint4, o);
-            }
         }
         lds_barrier();
 
@@ -713,12 +709,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sAT[(16 * i + 4 * q + e) * TS + 16 * j + cc] = Tij[e];
                 }
+                if (i == 3) vm_wait<0>();   // v (this wave's share), before the last barrier
                 lds_barrier();
             }
         }
-
-        vm_wait<0>();   // v
-        lds_barrier();
 
         // ---- 4: -W (W^T = K^T Tw^T: rows key columns, columns tokens; registers 8 js ..
         // 8 js + 7 are the A operand rows of W for one reduction step) and U~ = Thi V + Tlo V,
@@ -804,31 +798,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 //   state wave kh:  X_kh = U~_kh + (-W)_kh S_kh  (its half of the reduction; U~
 //                   rows of token tile kh, zero elsewhere); the X partials are swapped through LDS so that
 //                   both hold U_new = X_0 + X_1 (fp32 addition commutes: the same
-//                   bits in both); S_kh <- 2^(gam_n) S_kh + (K diag(d))_kh^T U_new,
-//                   d = 2^(gam_n - gam) r_k.  It also publishes S (bf16) and its
-//                   token tile of U_new (bf16) for the output waves.
+//                   bits in both); S_kh <- 2^(gam_n) S_kh + K_kh^T (diag(d) U_new),
+//                   d = 2^(gam_n - gam) r_k, with K^T read from the raw k rows by
+//                   LDS transpose reads.  It also publishes S (bf16) and its token
+//                   tile of U_new (bf16) for the output waves.
 //   output wave t:  Y^T = S^T Q_t^T over all state rows (after the first barrier),
 //                   then at the start of the next chunk
 //                   O^T = diag(sq) Y^T + U_new^T P_t^T, sq = scale r_q 2^gam
 //                   (P causal: tile 0 needs U_new rows 0..31 only), and stores it.
 // The reduction index of every product over state rows or tokens is in
 // accumulator order, so S and U_new go from accumulators to operands in
-// registers; the intra-chunk pass writes -W, (K diag(d))^T, P^T and U~ in that
-// order.  Two barriers per chunk: B1 after the X partials and S are published,
-// B2 at the end of the chunk.
+// registers; the intra-chunk pass writes -W, P^T and U~ in that order.  Two barriers
+// per chunk: B1 after the X partials and S are published, B2 at the end of the
+// chunk.
 //
 // Loads: the loader waves keep the operands of two chunks in LDS buffers.  Every
-// operand of chunk c is read before B1 of chunk c (the state waves read -W, U~ and
-// (K diag(d))^T at the start of the chunk), so right after that barrier the
-// loaders issue the state operands of chunk c + 2 into the same buffers, and
-// after B2 the output operands (raw q, P^T, scalars); before B2 of chunk c they
+// state operand of chunk c is read before B1 of chunk c (the state waves read -W,
+// U~ and K^T at the start of the chunk), so right after that barrier the loaders
+// issue the state operands (-W, U~, raw k) of chunk c + 2 into the same buffers,
+// and after B2 the output operands (raw q, P^T, scalars); before B2 of chunk c they
 // wait for all of chunk c + 1's.  Issue is spread over both halves of the chunk,
 // and each load has one to one and a half chunk steps to land.  The loads are
 // buffer loads into LDS written as asm: the compiler neither tracks them nor adds
 // waits for them; the loader waves issue nothing else, so each wait counts
 // exactly the loads issued after the ones it needs (loads complete in issue
-// order).  Rows of q past a chunk's end are out of the buffer's range and load as
-// zeros.  The barriers order LDS only.
+// order).  Rows of k and q past a chunk's end are out of the buffer's range and
+// load as zeros.  The barriers order LDS only.
 // For the summary the state is widened to [S | P] (K x (V + K)): the P columns
 // start at the identity and see U~ = 0, so they evolve as the product of the
 // decayed erase steps; there are no outputs.
@@ -841,15 +836,16 @@ struct InterCfg {
     static constexpr int KH = K / 2;              // state rows per state wave
     static constexpr int NR = KH / 32;            // 32-row accumulator tiles per state wave
     static constexpr int NKS = KH / 16;           // reduction steps over a key half
-    static constexpr int PPR = K / 8;             // 16-byte pieces per q row
+    static constexpr int PPR = K / 8;             // 16-byte pieces per k or q row
     // state operands (1 KiB fragments): -W [kh][token tile][step], U~ [token tile][j]
-    // and, in their own array, (K diag(d))^T [kh][row tile][token step]; output
-    // operands: raw q (64 x K bf16, pieces swizzled by row), P^T (tile 0 steps 0..1,
-    // tile 1 steps 0..3), scalars (sq[64], then 2^(gam_n) at 64)
+    // and, in their own array, raw k (64 x K bf16, pieces swizzled by row); output
+    // operands: raw q (same layout), P^T (tile 0 steps 0..1, tile 1 steps 0..3),
+    // scalars (d[64], sq[64], 2^(gam_n) at 192)
     static constexpr int FW = 4 * NKS, FU = 8, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
     static constexpr int oW = 0, oU = oW + FW, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
-    static constexpr int FK = 4 * NKS, oK = 0, NFL = FK;
-    static constexpr int NQ = FWD ? FQ / 2 : 1;   // q tile loads per loader wave
+    static constexpr int FK = K / 8, oK = 0, NFL = FK;
+    static constexpr int NKL = FK / 2;            // k tile loads per loader wave
+    static constexpr int NQ = NKL;                // q tile loads per loader wave (forward)
 };
 
 template <int K, int V, bool SUMMARY>
@@ -859,10 +855,11 @@ struct InterCtx {
 };
 
 // Loader wave lh, its half of chunk ci's state operands: -W and U~ into `eb`,
-// (K diag(d))^T into `lb`.  Returns the number of loads.
+// raw k into `lb`.  Returns the number of loads.
 template <int K, int V, bool SUMMARY>
 __device__ __forceinline__ int inter_issue_state(const Prob &p, const Ws &w, lds_u32x4 *eb, lds_u32x4 *lb, int ci,
-                                                 int lh, const InterCtx<K, V, SUMMARY> &x)
+                                                 int lh, const InterCtx<K, V, SUMMARY> &x,
+                                                 const uint32_t (&koff)[InterCfg<K, V, SUMMARY>::NKL])
 {
     using C = InterCfg<K, V, SUMMARY>;
     const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
@@ -875,13 +872,14 @@ __device__ __forceinline__ int inter_issue_state(const Prob &p, const Ws &w, lds
         b2l(rW, eb, C::oW + f, lo16, f * kFrag);
     }
     n += C::FW / 2;
-    const i32x4 rK = make_rsrc(reinterpret_cast<const char *>(w.KF) + chh * C::FK * kFrag, C::FK * kFrag);
+    {
+        const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
+        const i32x4 rK = make_rsrc(p.k + (int64_t)start * p.kst + (int64_t)x.hk * p.ksh,
+                                   (uint32_t)len * 2u * (uint32_t)p.kst);
 #pragma unroll
-    for (int i = 0; i < C::FK / 2; ++i) {
-        const int f = lh * (C::FK / 2) + i;
-        b2l(rK, lb, C::oK + f, lo16, f * kFrag);
+        for (int i = 0; i < C::NKL; ++i) b2l(rK, lb, C::oK + 2 * i + lh, koff[i], 0);
     }
-    n += C::FK / 2;
+    n += C::NKL;
     if (!x.ptile) {
         const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UF) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
                                    C::FU * kFrag);
@@ -958,8 +956,8 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 {
     using C = InterCfg<K, V, SUMMARY>;
     constexpr int NR = C::NR, NKS = C::NKS;
-    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64];   // -W, U~, q, P^T, scalars: two buffers
-    __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // (K diag(d))^T: two buffers
+    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64];   // -W, U~, q, scalars: two buffers
+    __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // raw k: two buffers
     __shared__ u32x4 sX[2 * 8 * 64];                       // X partials: [kh][m][j][lane]
     __shared__ u32x4 sS[C::FWD ? 2 * NKS * 64 : 1];        // S (bf16 operands): [kh][step][lane]
     __shared__ u32x4 sU[C::FWD ? 4 * 64 : 1];              // U_new (bf16 operands): [token step][lane]
@@ -970,7 +968,7 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     if (w.hdr[0] != LA_DEVICE_OK) return;
     const int U = p.N * p.HV;
     // blocks of 8 units x NT tiles; consecutive blocks go to different XCDs, and
-    // the NT tiles of one unit (which read the same W, K, P and q) to the same one
+    // the NT tiles of one unit (which read the same W, k and q) to the same one
     const int b = blockIdx.x;
     const int grp = b / (8 * C::NT), rem = b % (8 * C::NT);
     const int ug = min(8, U - 8 * grp);
@@ -997,14 +995,15 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     if (wave >= 4) {
         // ------------------------------------------------------------ loader waves
         const int lh = wave - 4;
-        uint32_t qoff[C::NQ];
-        if (C::FWD) {
+        // source offsets of this lane's 16-byte pieces of the k and q tiles (LDS piece
+        // (row, j) holds source piece j ^ (row % PPR) of the row)
+        uint32_t qoff[C::NQ], koff[C::NKL];
 #pragma unroll
-            for (int i = 0; i < C::FQ / 2; ++i) {
-                const int s = (2 * i + lh) * 64 + lane;
-                const int row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
-                qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
-            }
+        for (int i = 0; i < C::NKL; ++i) {
+            const int s = (2 * i + lh) * 64 + lane;
+            const int row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
+            koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
+            if (C::FWD) qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
         }
         // chunk c's operands land in buffer c % 2.  After B1 of chunk c (every wave
         // has read chunk c's operands by then) the state operands of chunk c + 2 are
@@ -1013,9 +1012,9 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         // them as soon as chunk c + 1 starts.
         int na = 0, nb = 0;
         if (nch > 0) {
-            na = inter_issue_state<K, V, SUMMARY>(p, w, e0, l0, 0, lh, x);
+            na = inter_issue_state<K, V, SUMMARY>(p, w, e0, l0, 0, lh, x, koff);
             nb = inter_issue_output<K, V, SUMMARY>(p, w, e0, 0, lh, x, qoff);
-            if (nch > 1) inter_issue_state<K, V, SUMMARY>(p, w, e1, l1, 1, lh, x);
+            if (nch > 1) inter_issue_state<K, V, SUMMARY>(p, w, e1, l1, 1, lh, x, koff);
             vm_wait_n(nch > 1 ? na : 0);                      // all of chunk 0
         }
         lds_barrier();
@@ -1026,7 +1025,7 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
             lds_u32x4 *neb = (ci & 1) ? e0 : e1;
             if (more1) inter_issue_output<K, V, SUMMARY>(p, w, neb, ci + 1, lh, x, qoff);
             lds_barrier();                                    // B1
-            if (more2) inter_issue_state<K, V, SUMMARY>(p, w, eb, lb, ci + 2, lh, x);
+            if (more2) inter_issue_state<K, V, SUMMARY>(p, w, eb, lb, ci + 2, lh, x, koff);
             vm_wait_n(more2 ? na : 0);                        // all of chunk ci + 1
             lds_barrier();                                    // B2
         }
@@ -1073,7 +1072,7 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                 for (int s = 0; s < 4; ++s)
                     Pf[s] = (s < 2 || t != 0) ? __builtin_bit_cast(bf16x8, eb[(C::oP + (t != 0 ? 2 : 0) + s) * 64 + lane])
                                               : bf16x8{};
-                sq = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[32 * t + c];
+                sq = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[64 + 32 * t + c];
             }
             Y = f32x16{};
 #pragma unroll
@@ -1118,14 +1117,15 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     for (int ci = 0; ci < nch; ++ci) {
         const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
         const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
-        // ---- operands: -W and (K diag(d))^T of this key half, U~ of token tile kh, 2^(gam_n)
+        // ---- operands: -W and K^T of this key half, U~ of token tile kh, 2^(gam_n)
         bf16x8 Wf[2][NKS];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int kk = 0; kk < NKS; ++kk)
                 Wf[m][kk] = __builtin_bit_cast(bf16x8, eb[(C::oW + (kh * 2 + m) * NKS + kk) * 64 + lane]);
-        const float gl = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[64];
+        const lds_float *scl = reinterpret_cast<const lds_float *>(eb + C::oS * 64);
+        const float gl = scl[192];
         // U~ enters through the accumulator of the wave whose token tile it is
         f32x16 X[2];
 #pragma unroll
@@ -1153,14 +1153,14 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
             for (int m = 0; m < 2; ++m) X[m] = mfma32(Wf[m][kk], Sb[kk], X[m]);
-        // (K diag(d))^T: read while the X products run (needed after B1)
+        // K^T of this key half (A operands: state rows, tokens in accumulator order), read
+        // from the raw k rows while the X products run (needed after B1)
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 Kf[NR][4];
 #pragma unroll
         for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                Kf[r][s] = __builtin_bit_cast(bf16x8, lb[(C::oK + (kh * NR + r) * 4 + s) * 64 + lane]);
+            for (int s = 0; s < 4; ++s) Kf[r][s] = lds_tr32s<C::PPR, true>(lb + C::oK * 64, 16 * s, row0 + 32 * r, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -1169,36 +1169,36 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                 xX[((kh * 2 + m) * 4 + j) * 64 + lane] =
                     __builtin_bit_cast(u32x4, f32x4{X[m][4 * j], X[m][4 * j + 1], X[m][4 * j + 2], X[m][4 * j + 3]});
         lds_barrier();                                        // B1
-        // ---- U_new = X_0 + X_1; this wave publishes token tile kh of it
-        bf16x8 Ub[4];
+        // ---- U_new = X_0 + X_1; this wave publishes token tile kh of it, and takes
+        // diag(d) U_new (rows in accumulator order) as the B operand of the update
+        bf16x8 Ud[4];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            f32x16 un;
+            f32x16 un, ud;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x4 xo = __builtin_bit_cast(f32x4, xX[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
+                const f32x4 dj = *reinterpret_cast<const lds_f32x4 *>(scl + 32 * m + 8 * j + 4 * hh);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) un[4 * j + e] = X[m][4 * j + e] + xo[e];
+                for (int e = 0; e < 4; ++e) {
+                    un[4 * j + e] = X[m][4 * j + e] + xo[e];
+                    ud[4 * j + e] = un[4 * j + e] * dj[e];
+                }
             }
-            Ub[2 * m] = pack32(un, 0);
-            Ub[2 * m + 1] = pack32(un, 1);
-        }
-        if (C::FWD) {
-            // (a branch on the wave-uniform kh: indexing Ub with it would select element-wise)
-            if (kh == 0) {
-                xU[0 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[0]);
-                xU[1 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[1]);
-            } else {
-                xU[2 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[2]);
-                xU[3 * 64 + lane] = __builtin_bit_cast(u32x4, Ub[3]);
+            Ud[2 * m] = pack32(ud, 0);
+            Ud[2 * m + 1] = pack32(ud, 1);
+            // (a branch on the wave-uniform kh: indexing with it would select element-wise)
+            if (C::FWD && m == kh) {
+                xU[(2 * m) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
+                xU[(2 * m + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
             }
         }
-        // ---- own rows: S <- 2^(gam_n) S + (K diag(d))^T U_new
+        // ---- own rows: S <- 2^(gam_n) S + K^T diag(d) U_new
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             f32x16 d = {};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) d = mfma32(Kf[r][s], Ub[s], d);
+            for (int s = 0; s < 4; ++s) d = mfma32(Kf[r][s], Ud[s], d);
 #pragma unroll
             for (int e = 0; e < 16; ++e) S[r][e] = fmaf(gl, S[r][e], d[e]);
         }
@@ -1238,12 +1238,12 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
     auto before = [&](int id) { if (hook) hook->before(id, s, hook->ctx); };
     auto after = [&](int id) { if (hook) hook->after(id, s, hook->ctx); };
 
-    before(LA_KERNEL_SCHED);
-    if (p.N <= 64)
-        hipLaunchKernelGGL(k_sched_small, dim3(1), dim3(256), 0, s, p, w);
-    else
+    // at most 64 sequences: the intra-chunk pass maps its own chunks and writes the tables
+    if (p.N > 64) {
+        before(LA_KERNEL_SCHED);
         hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, s, p, w);
-    after(LA_KERNEL_SCHED);
+        after(LA_KERNEL_SCHED);
+    }
     if (p.max_chunks > 0) {
         // persistent: at most three resident workgroups per CU, each walking (chunk, head) items
         const int64_t items = (int64_t)p.max_chunks * p.HV;
