@@ -812,18 +812,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // per chunk: B1 after the X partials and S are published, B2 at the end of the
 // chunk.
 //
-// Loads: the loader waves keep the operands of two chunks in LDS buffers.  Every
-// state operand of chunk c is read before B1 of chunk c (the state waves read -W,
-// U~ and K^T at the start of the chunk), so right after that barrier the loaders
-// issue the state operands (-W, U~, raw k) of chunk c + 2 into the same buffers,
-// and after B2 the output operands (raw q, P^T, scalars); before B2 of chunk c they
-// wait for all of chunk c + 1's.  Issue is spread over both halves of the chunk,
-// and each load has one to one and a half chunk steps to land.  The loads are
-// buffer loads into LDS written as asm: the compiler neither tracks them nor adds
-// waits for them; the loader waves issue nothing else, so each wait counts
-// exactly the loads issued after the ones it needs (loads complete in issue
-// order).  Rows of k and q past a chunk's end are out of the buffer's range and
-// load as zeros.  The barriers order LDS only.
+// Loads: -W and U~ are stored in fragment order, so each state wave loads its own
+// straight into registers (one coalesced 1 KiB load per fragment), two chunks
+// ahead, into two register sets used by alternate chunks (U~ one chunk ahead).
+// The loader waves keep the LDS operands in rotating buffers: raw k in two (read
+// by the state waves at the start of chunk c, so right after B1 of chunk c the
+// loaders issue the k rows of chunk c + 2 into the same buffer) and raw q, P^T and
+// the scalars in three (those of chunk c + 2 are issued at the start of chunk c);
+// before B2 of chunk c they wait for all of chunk c + 1's.  The k loads have one
+// and a half chunk steps to land, the others two.  The loader loads are buffer
+// loads into LDS written as asm:
+// the compiler neither tracks them nor adds waits for them; the loader waves issue
+// nothing else, so each wait counts exactly the loads issued after the ones it
+// needs (loads complete in issue order).  Rows of k and q past a chunk's end are
+// out of the buffer's range and load as zeros.  The barriers order LDS only.
 // For the summary the state is widened to [S | P] (K x (V + K)): the P columns
 // start at the identity and see U~ = 0, so they evolve as the product of the
 // decayed erase steps; there are no outputs.
@@ -837,12 +839,14 @@ struct InterCfg {
     static constexpr int NR = KH / 32;            // 32-row accumulator tiles per state wave
     static constexpr int NKS = KH / 16;           // reduction steps over a key half
     static constexpr int PPR = K / 8;             // 16-byte pieces per k or q row
-    // state operands (1 KiB fragments): -W [kh][token tile][step], U~ [token tile][j]
-    // and, in their own array, raw k (64 x K bf16, pieces swizzled by row); output
-    // operands: raw q (same layout), P^T (tile 0 steps 0..1, tile 1 steps 0..3),
-    // scalars (d[64], sq[64], 2^(gam_n) at 192)
+    // operands in the workspace, per (chunk, head), in 1 KiB fragments: -W
+    // [kh][token tile][step] (FW), U~ [value tile][token tile][j] (FU per value tile),
+    // both loaded by the state waves straight into registers.  In LDS: raw k (64 x K
+    // bf16, pieces swizzled by row) in its own array; raw q (same layout), P^T (tile
+    // 0 steps 0..1, tile 1 steps 0..3) and the scalars (d[64], sq[64], 2^(gam_n) at
+    // 192) in the other.
     static constexpr int FW = 4 * NKS, FU = 8, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
-    static constexpr int oW = 0, oU = oW + FW, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
+    static constexpr int oQ = 0, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
     static constexpr int FK = K / 8, oK = 0, NFL = FK;
     static constexpr int NKL = FK / 2;            // k tile loads per loader wave
     static constexpr int NQ = NKL;                // q tile loads per loader wave (forward)
@@ -854,43 +858,19 @@ struct InterCtx {
     bool ptile;
 };
 
-// Loader wave lh, its half of chunk ci's state operands: -W and U~ into `eb`,
-// raw k into `lb`.  Returns the number of loads.
+// Loader wave lh, its half of chunk ci's raw k rows into `lb`.  Returns the
+// number of loads.
 template <int K, int V, bool SUMMARY>
-__device__ __forceinline__ int inter_issue_state(const Prob &p, const Ws &w, lds_u32x4 *eb, lds_u32x4 *lb, int ci,
-                                                 int lh, const InterCtx<K, V, SUMMARY> &x,
-                                                 const uint32_t (&koff)[InterCfg<K, V, SUMMARY>::NKL])
+__device__ __forceinline__ int inter_issue_k(const Prob &p, lds_u32x4 *lb, int ci, int lh,
+                                             const InterCtx<K, V, SUMMARY> &x,
+                                             const uint32_t (&koff)[InterCfg<K, V, SUMMARY>::NKL])
 {
     using C = InterCfg<K, V, SUMMARY>;
-    const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
-    const uint32_t lo16 = (uint32_t)x.lane * 16u;
-    int n = 0;
-    const i32x4 rW = make_rsrc(reinterpret_cast<const char *>(w.WF) + chh * C::FW * kFrag, C::FW * kFrag);
+    const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
+    const i32x4 rK = make_rsrc(p.k + (int64_t)start * p.kst + (int64_t)x.hk * p.ksh, (uint32_t)len * 2u * (uint32_t)p.kst);
 #pragma unroll
-    for (int i = 0; i < C::FW / 2; ++i) {
-        const int f = lh * (C::FW / 2) + i;
-        b2l(rW, eb, C::oW + f, lo16, f * kFrag);
-    }
-    n += C::FW / 2;
-    {
-        const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
-        const i32x4 rK = make_rsrc(p.k + (int64_t)start * p.kst + (int64_t)x.hk * p.ksh,
-                                   (uint32_t)len * 2u * (uint32_t)p.kst);
-#pragma unroll
-        for (int i = 0; i < C::NKL; ++i) b2l(rK, lb, C::oK + 2 * i + lh, koff[i], 0);
-    }
-    n += C::NKL;
-    if (!x.ptile) {
-        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UF) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
-                                   C::FU * kFrag);
-#pragma unroll
-        for (int i = 0; i < C::FU / 2; ++i) {
-            const int f = lh * (C::FU / 2) + i;
-            b2l(rU, eb, C::oU + f, lo16, f * kFrag);
-        }
-        n += C::FU / 2;
-    }
-    return n;
+    for (int i = 0; i < C::NKL; ++i) b2l(rK, lb, C::oK + 2 * i + lh, koff[i], 0);
+    return C::NKL;
 }
 
 // Loader wave lh, its half of chunk ci's output operands (raw q, P^T) and the
@@ -956,12 +936,13 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 {
     using C = InterCfg<K, V, SUMMARY>;
     constexpr int NR = C::NR, NKS = C::NKS;
-    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64];   // -W, U~, q, scalars: two buffers
+    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64], sE2[C::NFE * 64];   // q, P^T, scalars: three buffers
     __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // raw k: two buffers
     __shared__ u32x4 sX[2 * 8 * 64];                       // X partials: [kh][m][j][lane]
     __shared__ u32x4 sS[C::FWD ? 2 * NKS * 64 : 1];        // S (bf16 operands): [kh][step][lane]
     __shared__ u32x4 sU[C::FWD ? 4 * 64 : 1];              // U_new (bf16 operands): [token step][lane]
-    lds_u32x4 *const e0 = (lds_u32x4 *)sE0, *const e1 = (lds_u32x4 *)sE1;
+    lds_u32x4 *const e0 = (lds_u32x4 *)sE0, *const e1 = (lds_u32x4 *)sE1, *const e2 = (lds_u32x4 *)sE2;
+    auto ebuf = [&](int c) { const int r = c % 3; return r == 0 ? e0 : (r == 1 ? e1 : e2); };
     lds_u32x4 *const l0 = (lds_u32x4 *)sL0, *const l1 = (lds_u32x4 *)sL1;
     lds_u32x4 *const xX = (lds_u32x4 *)sX, *const xS = (lds_u32x4 *)sS, *const xU = (lds_u32x4 *)sU;
 
@@ -1005,31 +986,30 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
             koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
             if (C::FWD) qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
         }
-        // chunk c's operands land in buffer c % 2.  After B1 of chunk c (every wave
-        // has read chunk c's operands by then) the state operands of chunk c + 2 are
-        // issued, after B2 of chunk c its output operands; before B2 of chunk c the
-        // loaders wait for all of chunk c + 1's, so that the state waves can read
-        // them as soon as chunk c + 1 starts.
+        // chunk c's k rows land in k buffer c % 2, its output operands in buffer c % 3.
+        // At the start of chunk c (after B2 of chunk c - 1, when chunk c - 1's output
+        // operands are dead) the output operands of chunk c + 2 are issued, after B1 of
+        // chunk c (the state waves have read chunk c's k by then) its k rows; before B2
+        // of chunk c the loaders wait for all of chunk c + 1's.
         int na = 0, nb = 0;
         if (nch > 0) {
-            na = inter_issue_state<K, V, SUMMARY>(p, w, e0, l0, 0, lh, x, koff);
+            na = inter_issue_k<K, V, SUMMARY>(p, l0, 0, lh, x, koff);
             nb = inter_issue_output<K, V, SUMMARY>(p, w, e0, 0, lh, x, qoff);
-            if (nch > 1) inter_issue_state<K, V, SUMMARY>(p, w, e1, l1, 1, lh, x, koff);
-            vm_wait_n(nch > 1 ? na : 0);                      // all of chunk 0
+            if (nch > 1) {
+                inter_issue_k<K, V, SUMMARY>(p, l1, 1, lh, x, koff);
+                inter_issue_output<K, V, SUMMARY>(p, w, e1, 1, lh, x, qoff);
+            }
+            vm_wait_n(nch > 1 ? na + nb : 0);                 // all of chunk 0
         }
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
-            const bool more1 = ci + 1 < nch, more2 = ci + 2 < nch;
-            lds_u32x4 *eb = (ci & 1) ? e1 : e0;
-            lds_u32x4 *lb = (ci & 1) ? l1 : l0;
-            lds_u32x4 *neb = (ci & 1) ? e0 : e1;
-            if (more1) inter_issue_output<K, V, SUMMARY>(p, w, neb, ci + 1, lh, x, qoff);
+            const bool more2 = ci + 2 < nch;
+            if (more2) inter_issue_output<K, V, SUMMARY>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff);
             lds_barrier();                                    // B1
-            if (more2) inter_issue_state<K, V, SUMMARY>(p, w, eb, lb, ci + 2, lh, x, koff);
-            vm_wait_n(more2 ? na : 0);                        // all of chunk ci + 1
+            if (more2) inter_issue_k<K, V, SUMMARY>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff);
+            vm_wait_n(more2 ? na + nb : 0);                   // all of chunk ci + 1
             lds_barrier();                                    // B2
         }
-        (void)nb;
         return;
     }
 
@@ -1050,7 +1030,7 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         int o_start = 0, o_len = 0;
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
-            const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
+            const lds_u32x4 *eb = ebuf(ci);
             // the previous chunk's output (its U_new was published before the last B2)
             if (ci > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
             lds_barrier();                                    // B1: S of chunk ci is published
@@ -1113,34 +1093,64 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 #pragma unroll
             for (int e = 0; e < 16; ++e) S[r][e] = (row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3) == pc) ? 1.f : 0.f;
     }
-    lds_barrier();
-    for (int ci = 0; ci < nch; ++ci) {
-        const lds_u32x4 *eb = (ci & 1) ? e1 : e0;
-        const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
-        // ---- operands: -W and K^T of this key half, U~ of token tile kh, 2^(gam_n)
-        bf16x8 Wf[2][NKS];
+    // Token tiles in this wave's order: o = 0 is its own tile (kh), o = 1 the other one
+    // (only addresses depend on kh, never a register selection).  -W and U~ are stored
+    // in fragment order, so this wave loads its own straight into registers: -W two
+    // chunks ahead into two register sets used by alternate chunks, U~ (its own token
+    // tile) one chunk ahead, as soon as the current one has entered the accumulator.
+    struct StateOps {
+        bf16x8 W[2][NKS];
+    };
+    auto load_w = [&](StateOps &R, int cj) {
+        const int64_t chh = (int64_t)(x.cid0 + cj) * p.HV + x.h;
+        const uint4 *wsrc = w.WF + chh * C::FW * 64 + lane;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int o = 0; o < 2; ++o)
 #pragma unroll
             for (int kk = 0; kk < NKS; ++kk)
-                Wf[m][kk] = __builtin_bit_cast(bf16x8, eb[(C::oW + (kh * 2 + m) * NKS + kk) * 64 + lane]);
-        const lds_float *scl = reinterpret_cast<const lds_float *>(eb + C::oS * 64);
-        const float gl = scl[192];
-        // U~ enters through the accumulator of the wave whose token tile it is
-        f32x16 X[2];
+                R.W[o][kk] = __builtin_bit_cast(bf16x8, wsrc[((kh * 2 + (o ^ kh)) * NKS + kk) * 64]);
+    };
+    f32x16 Un = {};
+    auto load_u = [&](int cj) {
+        if (!x.ptile) {
+            const int64_t chh = (int64_t)(x.cid0 + cj) * p.HV + x.h;
+            const float4 *usrc = w.UF + ((chh * (V / 32) + x.tile) * C::FU + 4 * kh) * 64 + lane;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            if (m == kh && !x.ptile) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 u4 = __builtin_bit_cast(f32x4, eb[(C::oU + 4 * m + j) * 64 + lane]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) X[m][4 * j + e] = u4[e];
-                }
-            } else {
-                X[m] = f32x16{};
+            for (int j = 0; j < 4; ++j) {
+                const float4 u4 = usrc[j * 64];
+                Un[4 * j] = u4.x;
+                Un[4 * j + 1] = u4.y;
+                Un[4 * j + 2] = u4.z;
+                Un[4 * j + 3] = u4.w;
             }
         }
+    };
+    StateOps opA, opB;
+    if (nch > 0) {
+        load_w(opA, 0);
+        load_u(0);
+    }
+    if (nch > 1) load_w(opB, 1);
+    lds_barrier();
+    auto chunk_step = [&](int ci, StateOps &R) {
+        const lds_u32x4 *eb = ebuf(ci);
+        const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
+        // ---- K^T of this key half (A operands: state rows, tokens in accumulator order,
+        // own token tile first), read from the raw k rows while the X products run
+        bf16x8 Kf[NR][4];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int o = 0; o < 2; ++o)
+#pragma unroll
+                for (int js = 0; js < 2; ++js)
+                    Kf[r][2 * o + js] =
+                        lds_tr32s<C::PPR, true>(lb + C::oK * 64, 16 * (2 * (o ^ kh) + js), row0 + 32 * r, lane);
+        // U~ enters through the accumulator of the wave whose token tile it is
+        f32x16 X[2];
+        X[0] = Un;
+        X[1] = f32x16{};
+        if (ci + 1 < nch) load_u(ci + 1);
         // ---- S as bf16 operands, published for the output waves
         bf16x8 Sb[NKS];
 #pragma unroll
@@ -1152,28 +1162,23 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) X[m] = mfma32(Wf[m][kk], Sb[kk], X[m]);
-        // K^T of this key half (A operands: state rows, tokens in accumulator order), read
-        // from the raw k rows while the X products run (needed after B1)
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 Kf[NR][4];
+            for (int o = 0; o < 2; ++o) X[o] = mfma32(R.W[o][kk], Sb[kk], X[o]);
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Kf[r][s] = lds_tr32s<C::PPR, true>(lb + C::oK * 64, 16 * s, row0 + 32 * r, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int o = 0; o < 2; ++o)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xX[((kh * 2 + m) * 4 + j) * 64 + lane] =
-                    __builtin_bit_cast(u32x4, f32x4{X[m][4 * j], X[m][4 * j + 1], X[m][4 * j + 2], X[m][4 * j + 3]});
+                xX[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
+                    __builtin_bit_cast(u32x4, f32x4{X[o][4 * j], X[o][4 * j + 1], X[o][4 * j + 2], X[o][4 * j + 3]});
         lds_barrier();                                        // B1
-        // ---- U_new = X_0 + X_1; this wave publishes token tile kh of it, and takes
+        if (ci + 2 < nch) load_w(R, ci + 2);
+        const lds_float *scl = reinterpret_cast<const lds_float *>(eb + C::oS * 64);
+        const float gl = scl[192];
+        // ---- U_new = X_0 + X_1; this wave publishes its own token tile of it, and takes
         // diag(d) U_new (rows in accumulator order) as the B operand of the update
         bf16x8 Ud[4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int o = 0; o < 2; ++o) {
+            const int m = o ^ kh;                             // the token tile
             f32x16 un, ud;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1181,28 +1186,32 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                 const f32x4 dj = *reinterpret_cast<const lds_f32x4 *>(scl + 32 * m + 8 * j + 4 * hh);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    un[4 * j + e] = X[m][4 * j + e] + xo[e];
+                    un[4 * j + e] = X[o][4 * j + e] + xo[e];
                     ud[4 * j + e] = un[4 * j + e] * dj[e];
                 }
             }
-            Ud[2 * m] = pack32(ud, 0);
-            Ud[2 * m + 1] = pack32(ud, 1);
-            // (a branch on the wave-uniform kh: indexing with it would select element-wise)
-            if (C::FWD && m == kh) {
-                xU[(2 * m) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
-                xU[(2 * m + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
+            Ud[2 * o] = pack32(ud, 0);
+            Ud[2 * o + 1] = pack32(ud, 1);
+            if (C::FWD && o == 0) {
+                xU[(2 * kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
+                xU[(2 * kh + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
             }
         }
         // ---- own rows: S <- 2^(gam_n) S + K^T diag(d) U_new
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            f32x16 d = {};
+            f32x16 d;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) d[e] = gl * S[r][e];
 #pragma unroll
             for (int s = 0; s < 4; ++s) d = mfma32(Kf[r][s], Ud[s], d);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) S[r][e] = fmaf(gl, S[r][e], d[e]);
+            S[r] = d;
         }
         lds_barrier();                                        // B2
+    };
+    for (int ci = 0; ci < nch; ci += 2) {
+        chunk_step(ci, opA);
+        if (ci + 1 < nch) chunk_step(ci + 1, opB);
     }
 
     if (!x.ptile) {
