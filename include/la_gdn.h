@@ -142,7 +142,9 @@ const char *la_last_error_message(void);
  * for the recorded events and returns the summed milliseconds and the launch
  * count of one kernel (ids below).
  */
-#define LA_KERNEL_SCHED 0   /* cu_seqlens validation, chunk table, longest-first order */
+#define LA_KERNEL_SCHED 0   /* cu_seqlens validation, chunk table, longest-first order (its own
+                               kernel only for more than 64 sequences; otherwise k_intra does
+                               it and this id counts no launches) */
 #define LA_KERNEL_INTRA 1   /* prologue (q/k norms, gate cumsum) + intra-chunk UT/WY */
 #define LA_KERNEL_INTER 2   /* sequential inter-chunk state and output pass */
 #define LA_KERNEL_COUNT 3
