@@ -669,11 +669,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
 #pragma unroll
             for (int k = 0; k < 15; ++k) {
-                // A[o + i][o + k] for i > k is A^T[o + k][o + i]
-                const lds_float *ar = sAT + (o + k) * TS + o;
+                // A[o + i][o + k] for i > k is A^T[o + k][o + i]: the row in four 16-byte
+                // reads (independent of x, so they can be issued ahead of the chain)
+                const lds_f32x4 *ar = reinterpret_cast<const lds_f32x4 *>(sAT + (o + k) * TS + o);
+                float a[16];
+#pragma unroll
+                for (int q = (k + 1) / 4; q < 4; ++q) {
+                    const f32x4 v = ar[q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[4 * q + e] = v[e];
+                }
                 const float xk = x[k];
 #pragma unroll
-                for (int i = k + 1; i < 16; ++i) x[i] = fmaf(-ar[i], xk, x[i]);
+                for (int i = k + 1; i < 16; ++i) x[i] = fmaf(-a[i], xk, x[i]);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) sAT[(o + i) * TS + o + cc] = x[i];
