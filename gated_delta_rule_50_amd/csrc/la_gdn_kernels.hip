@@ -1171,6 +1171,16 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
             for (int o = 0; o < 2; ++o) X[o] = mfma32(R.W[o][kk], Sb[kk], X[o]);
+        // the decay of S ahead of the barrier, in the shadow of the X products (S is
+        // not needed again before its update: its bf16 copy is already taken)
+        const lds_float *scl = reinterpret_cast<const lds_float *>(eb + C::oS * 64);
+        const float gl = scl[192];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S[r][e] *= gl;
+            asm volatile("" : "+v"(S[r]));   // keeps the scaling ahead of the barrier
+        }
 #pragma unroll
         for (int o = 0; o < 2; ++o)
 #pragma unroll
@@ -1179,8 +1189,6 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                     __builtin_bit_cast(u32x4, f32x4{X[o][4 * j], X[o][4 * j + 1], X[o][4 * j + 2], X[o][4 * j + 3]});
         lds_barrier();                                        // B1
         if (ci + 2 < nch) load_w(R, ci + 2);
-        const lds_float *scl = reinterpret_cast<const lds_float *>(eb + C::oS * 64);
-        const float gl = scl[192];
         // ---- U_new = X_0 + X_1; this wave publishes its own token tile of it, and takes
         // diag(d) U_new (rows in accumulator order) as the B operand of the update
         bf16x8 Ud[4];
@@ -1205,16 +1213,11 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                 xU[(2 * kh + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
             }
         }
-        // ---- own rows: S <- 2^(gam_n) S + K^T diag(d) U_new
+        // ---- own rows: S <- (2^(gam_n) S) + K^T diag(d) U_new
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            f32x16 d;
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) d[e] = gl * S[r][e];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) d = mfma32(Kf[r][s], Ud[s], d);
-            S[r] = d;
-        }
+            for (int s = 0; s < 4; ++s) S[r] = mfma32(Kf[r][s], Ud[s], S[r]);
         lds_barrier();                                        // B2
     };
     for (int ci = 0; ci < nch; ci += 2) {
