@@ -854,7 +854,7 @@ struct InterCfg {
     // 0 steps 0..1, tile 1 steps 0..3) and the scalars (d[64], sq[64], 2^(gam_n) at
     // 192) in the other.
     static constexpr int FW = 4 * NKS, FU = 8, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
-    static constexpr int oQ = 0, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
+    static constexpr int oU = 0, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
     static constexpr int FK = K / 8, oK = 0, NFL = FK;
     static constexpr int NKL = FK / 2;            // k tile loads per loader wave
     static constexpr int NQ = NKL;                // q tile loads per loader wave (forward)
@@ -902,6 +902,16 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
 #pragma unroll
         for (int i = 0; i < 3; ++i) b2l(rP, eb, C::oP + 3 * lh + i, lo16, (3 * lh + i) * kFrag);
         n += C::FQ / 2 + 3;
+    }
+    if (!x.ptile) {
+        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UF) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
+                                   C::FU * kFrag);
+#pragma unroll
+        for (int i = 0; i < C::FU / 2; ++i) {
+            const int f = lh * (C::FU / 2) + i;
+            b2l(rU, eb, C::oU + f, lo16, f * kFrag);
+        }
+        n += C::FU / 2;
     }
     if (lh == 0) {
         const i32x4 rS = make_rsrc(w.SC + chh * kScalars, kScalars * 4);
@@ -1103,9 +1113,9 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     }
     // Token tiles in this wave's order: o = 0 is its own tile (kh), o = 1 the other one
     // (only addresses depend on kh, never a register selection).  -W and U~ are stored
-    // in fragment order, so this wave loads its own straight into registers: -W two
-    // chunks ahead into two register sets used by alternate chunks, U~ (its own token
-    // tile) one chunk ahead, as soon as the current one has entered the accumulator.
+    // in fragment order: this wave loads its -W straight into registers, two chunks
+    // ahead into two register sets used by alternate chunks; U~ comes through LDS with
+    // the output operands.
     struct StateOps {
         bf16x8 W[2][NKS];
     };
@@ -1118,26 +1128,8 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
             for (int kk = 0; kk < NKS; ++kk)
                 R.W[o][kk] = __builtin_bit_cast(bf16x8, wsrc[((kh * 2 + (o ^ kh)) * NKS + kk) * 64]);
     };
-    f32x16 Un = {};
-    auto load_u = [&](int cj) {
-        if (!x.ptile) {
-            const int64_t chh = (int64_t)(x.cid0 + cj) * p.HV + x.h;
-            const float4 *usrc = w.UF + ((chh * (V / 32) + x.tile) * C::FU + 4 * kh) * 64 + lane;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 u4 = usrc[j * 64];
-                Un[4 * j] = u4.x;
-                Un[4 * j + 1] = u4.y;
-                Un[4 * j + 2] = u4.z;
-                Un[4 * j + 3] = u4.w;
-            }
-        }
-    };
     StateOps opA, opB;
-    if (nch > 0) {
-        load_w(opA, 0);
-        load_u(0);
-    }
+    if (nch > 0) load_w(opA, 0);
     if (nch > 1) load_w(opB, 1);
     lds_barrier();
     auto chunk_step = [&](int ci, StateOps &R) {
@@ -1156,9 +1148,17 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
                         lds_tr32s<C::PPR, true>(lb + C::oK * 64, 16 * (2 * (o ^ kh) + js), row0 + 32 * r, lane);
         // U~ enters through the accumulator of the wave whose token tile it is
         f32x16 X[2];
-        X[0] = Un;
         X[1] = f32x16{};
-        if (ci + 1 < nch) load_u(ci + 1);
+        if (!x.ptile) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 u4 = __builtin_bit_cast(f32x4, eb[(C::oU + 4 * kh + j) * 64 + lane]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) X[0][4 * j + e] = u4[e];
+            }
+        } else {
+            X[0] = f32x16{};
+        }
         // ---- S as bf16 operands, published for the output waves
         bf16x8 Sb[NKS];
 #pragma unroll
