@@ -17,6 +17,7 @@ the fp64 CPU oracle timed on the host cores as a baseline.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -30,21 +31,43 @@ METRIC = "GDN fwd tokens/s (H=16,K=V=128,bf16) + % of MFMA/HBM roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 CHUNK = 64
+WORKLOADS = {
+    1: "tiny GDN fwd, T=256, one sequence, H=2, K=V=64, in-kernel q/k L2 norm, zero initial state, "
+       "o + final state",
+    2: "varlen GDN fwd, T=4096, cu_seqlens=[0,1000,2500,4096], H=16, K=V=128, in-kernel q/k L2 norm, "
+       "zero initial state, o + final state",
+    3: "dense batch GDN fwd, 8 x 4096 tokens, HK=4, HV=16, K=V=128, in-kernel q/k L2 norm, initial state, "
+       "o + final state",
+    4: "ragged long-context GDN fwd, 64 sequences of U[1,4096] tokens + one of 65536, H=32, K=V=128, "
+       "in-kernel q/k L2 norm, zero initial state, o + final state",
+    5: "GDN span summary, 32 spans x 8192 tokens, H=16, K=V=128, in-kernel k L2 norm, start state, "
+       "end state + transition",
+}
 
 
-def algorithmic_counts(lengths, HK, HV, K, V, with_init, with_final):
+def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final):
     """Bytes and flops the method must move and compute (intermediates excluded).
 
-    bytes: q, k (bf16, per qk-head), v, o (bf16, per v-head), g, beta (fp32 per
-    v-head), plus the fp32 states read/written: 1032 bytes per token-head at
-    H = 16, K = V = 128.  flops: per qk-head token the two chunk Gram products
-    (k k^T and q k^T, 2 * 2 C K); per v-head token the W / U~ products, the
-    masked P U_new, W S, Q S and the state update (2 (3 K V + C (K + 2 V))),
-    180,224 per token-head at H = 16, K = V = 128."""
+    Forward bytes: q, k (bf16, per qk-head), v, o (bf16, per v-head), g, beta
+    (fp32 per v-head), plus the fp32 states read/written: 1032 bytes per
+    token-head at H = 16, K = V = 128.  Forward flops: per qk-head token the two
+    chunk Gram products (k k^T and q k^T, 2 * 2 C K); per v-head token the W / U~
+    products, the masked P U_new, W S, Q S and the state update
+    (2 (3 K V + C (K + 2 V))), 180,224 per token-head at H = 16, K = V = 128.
+    Span summary: no q and no o; bytes add the start, end and transition states;
+    flops are the k k^T Gram product, W, U~, W S and the state update for the
+    widened state [S | P] (K x (V + K)): also 180,224 per token-head at
+    K = V = 128."""
     T = sum(lengths)
     N = len(lengths)
-    by = T * (2 * HK * K * 2 + 2 * HV * V * 2 + 2 * HV * 4) + N * HV * K * V * 4 * (int(with_init) + int(with_final))
-    fl = T * (HK * 2 * 2 * CHUNK * K + HV * 2 * (3 * K * V + CHUNK * (K + 2 * V)))
+    C = CHUNK
+    if summary:
+        by = T * (HK * K * 2 + HV * V * 2 + 2 * HV * 4) + N * HV * 4 * (K * V * (int(with_init) + 1) + K * K)
+        VA = V + K
+        fl = T * (HK * 2 * C * K + HV * 2 * (C * (K + V) + 2 * K * VA))
+    else:
+        by = T * (2 * HK * K * 2 + 2 * HV * V * 2 + 2 * HV * 4) + N * HV * K * V * 4 * (int(with_init) + int(with_final))
+        fl = T * (HK * 2 * 2 * C * K + HV * 2 * (3 * K * V + C * (K + 2 * V)))
     return by, fl
 
 
@@ -91,6 +114,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4, help="input/output sets rotated over (cache-cold steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="the workload timed: 2 (default) is the bench line; 1, 3, 4 (forward) and 5 (span "
+                         "summary) report the same fields for the other configurations, with inputs drawn on "
+                         "the device and no CPU baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -112,25 +139,45 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     la.load_library()
 
-    prob = make_problem(2)
+    wl = args.workload
+    prob = make_problem(wl) if wl == 2 else make_problem(wl, device="cuda")
+    summary = prob.summary
     lengths = prob.lengths()
     T, HK, HV, K, V = prob.total_tokens, prob.num_qk_heads, prob.num_v_heads, prob.head_dim_k, prob.head_dim_v
     N = prob.num_seqs
 
+    # one copy is enough once a copy alone is larger than the Infinity Cache
+    by0, _ = algorithmic_counts(lengths, HK, HV, K, V, summary, prob.state is not None, True)
+
+    def fresh_copy(pr):
+        def cl(x):
+            return None if x is None else x.to(dev).clone()
+        return dataclasses.replace(pr, cu_seqlens=cl(pr.cu_seqlens), q=cl(pr.q), k=cl(pr.k), v=cl(pr.v),
+                                   g=cl(pr.g), beta=cl(pr.beta), state=cl(pr.state))
+
+    copies = max(1, args.copies) if by0 < (1 << 30) else 1
     sets = []
-    for _ in range(max(1, args.copies)):
-        g = prob.to(dev)
-        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=dev)
+    for ic in range(copies):
+        g = fresh_copy(prob)
+        if summary:
+            out = torch.empty((N, HV, K, K), dtype=torch.float32, device=dev)   # transition
+            desc = la.make_desc(g.k, g.v, g.g, g.beta, N)
+        else:
+            out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=dev)
+            desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out)
         fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
-        desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out)
-        ws = la.alloc_workspace(desc, False, dev)
+        ws = la.alloc_workspace(desc, summary, dev)
         sets.append((g, out, fin, ws))
     stream = torch.cuda.current_stream()
 
     def step(i):
         g, out, fin, ws = sets[i % len(sets)]
-        la.la_gdn_fwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=None, out=out,
-                      final_state=fin, l2norm=True, workspace=ws, stream=stream)
+        if summary:
+            la.la_gdn_summary(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state, end_state=fin,
+                              transition=out, l2norm=True, workspace=ws, stream=stream)
+        else:
+            la.la_gdn_fwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state, out=out,
+                          final_state=fin, l2norm=True, workspace=ws, stream=stream)
 
     if args.calibrate_copy_mib > 0:
         nbytes = args.calibrate_copy_mib << 20
@@ -174,13 +221,24 @@ def main(argv=None):
     ms_per_step = 1e3 * elapsed / args.steps
     value = T * args.steps / elapsed
 
-    by, fl = algorithmic_counts(lengths, HK, HV, K, V, with_init=False, with_final=True)
+    by, fl = algorithmic_counts(lengths, HK, HV, K, V, summary, prob.state is not None, True)
     inter_us = kern["k_inter"]["avg_us"]
-    # the dominant kernel's roofline: the forward's algorithmic bytes (one launch
-    # processes every token-head of the batch) over that kernel's launch time
-    achieved = by / (inter_us * 1e-6) / 1e9
+    # the dominant kernel's roofline: the path's algorithmic bytes (one launch
+    # processes every token-head of the batch) over that kernel's launch time;
+    # the span summary sits at the ridge and is priced on bf16 MFMA flops
     step_s = ms_per_step * 1e-3
-    traffic = measured_traffic(os.path.join(ROOT, "gated_delta_rule_50_amd", "csrc", "la_gdn_kernels.hip"))
+    if summary:
+        roof = {"bound": "mfma", "kernel": "k_inter", "achieved": fl / (inter_us * 1e-6) / 1e12,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "kernel": "k_inter", "achieved": by / (inter_us * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    # the committed counter record covers the default workload only
+    roof["traffic"] = measured_traffic(os.path.join(ROOT, "gated_delta_rule_50_amd", "csrc",
+                                                    "la_gdn_kernels.hip")) if wl == 2 else None
+    roof.update({"algorithmic_bytes_per_launch": by, "algorithmic_flops_per_launch": fl,
+                 "avg_launch_us": inter_us})
 
     rec = {
         "metric": METRIC,
@@ -195,19 +253,16 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "varlen GDN fwd, T=4096, cu_seqlens=[0,1000,2500,4096], H=16, K=V=128, "
-                               "in-kernel q/k L2 norm, zero initial state, o + final state",
+        "config": {"workload": WORKLOADS[wl],
                    "T": T, "N": N, "HK": HK, "HV": HV, "K": K, "V": V, "copies_rotated": len(sets),
                    "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "k_inter", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": by, "avg_launch_us": inter_us},
+        "roofline": roof,
         "path": {"algorithmic_bytes": by, "algorithmic_flops": fl,
                  "hbm_frac": by / step_s / (HBM_PEAK_GBS * 1e9),
                  "mfma_frac": fl / step_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                  "kernels": kern},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl == 2:
         rec["cpu_baseline"] = cpu_baseline(prob)
     print(json.dumps(rec), flush=True)
     return 0
