@@ -857,6 +857,10 @@ struct InterCfg {
     static constexpr int oU = 0, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
     static constexpr int FK = K / 8, oK = 0, NFL = FK;
     static constexpr int NKL = FK / 2;            // k tile loads per loader wave
+    // waves: 0, 1 state, (forward) 2, 3 output, then the two loader waves; the summary has
+    // no outputs, so its workgroup is 4 waves and two fit on a CU (LDS 75 KiB at K = V = 128)
+    static constexpr int LW = FWD ? 4 : 2;        // first loader wave
+    static constexpr int THREADS = 64 * (LW + 2);
     static constexpr int NQ = NKL;                // q tile loads per loader wave (forward)
 };
 
@@ -950,7 +954,7 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
 }
 
 template <int K, int V, bool SUMMARY>
-__global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
+__device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     using C = InterCfg<K, V, SUMMARY>;
     constexpr int NR = C::NR, NKS = C::NKS;
@@ -991,9 +995,9 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     const int lane = x.lane, c = lane & 31, hh = lane >> 5;
     const int nch = x.nch;
 
-    if (wave >= 4) {
+    if (wave >= C::LW) {
         // ------------------------------------------------------------ loader waves
-        const int lh = wave - 4;
+        const int lh = wave - C::LW;
         // source offsets of this lane's 16-byte pieces of the k and q tiles (LDS piece
         // (row, j) holds source piece j ^ (row % PPR) of the row)
         uint32_t qoff[C::NQ], koff[C::NKL];
@@ -1031,16 +1035,8 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
         return;
     }
 
-    if (wave >= 2) {
+    if (C::FWD && wave >= 2) {
         // ------------------------------------------------------------ output waves
-        if (!C::FWD) {
-            lds_barrier();
-            for (int ci = 0; ci < nch; ++ci) {
-                lds_barrier();
-                lds_barrier();
-            }
-            return;
-        }
         const int t = wave - 2;
         f32x16 Y = {};
         bf16x8 Pf[4];
@@ -1247,6 +1243,22 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     }
 }
 
+// The forward's workgroup (6 waves) takes 153 KiB of LDS at K = V = 128, one per CU.
+// The summary's (4 waves: no output waves) takes 75 KiB, two per CU.
+template <int K, int V>
+__global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
+{
+    static_assert(InterCfg<K, V, false>::THREADS == 384, "forward: 6 waves");
+    inter_body<K, V, false>(p, w);
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(256) void k_inter_sum(Prob p, Ws w)
+{
+    static_assert(InterCfg<K, V, true>::THREADS == 256, "summary: 4 waves");
+    inter_body<K, V, true>(p, w);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch sequence.
 
@@ -1275,7 +1287,11 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
     const int64_t blocks = (int64_t)p.N * p.HV * InterCfg<K, V, SUMMARY>::NT;
     if (blocks > 0) {
         before(LA_KERNEL_INTER);
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter<K, V, SUMMARY>), dim3((unsigned)blocks), dim3(384), 0, s, p, w);
+        const dim3 threads(InterCfg<K, V, SUMMARY>::THREADS);
+        if (SUMMARY)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         after(LA_KERNEL_INTER);
     }
     return hipGetLastError();
