@@ -523,8 +523,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (small) sm = small_map(p, w, blockIdx.x == 0 && wave == 0);
     const int items = (small ? sm.total : w.hdr[1]) * p.HV;   // (chunk, value head) pairs, chunk-major
 
+    // Item order: the G value heads that share a q/k head (consecutive items) go to
+    // workgroups 8 apart, which the dispatcher places on one XCD, so that their k and q
+    // loads share that XCD's L2.  A bijection on the first 8 G floor(groups / 8) items
+    // (the rest keep their index); with G = 1 it is the identity.
+    const int groups = items / G, full = (groups & ~7) * G;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int ci = it / p.HV, h = it % p.HV, hk = h / G;
+        int r = it;
+        if (G > 1 && it < full) {
+            const int u = it >> 3;
+            r = __builtin_amdgcn_readfirstlane((8 * (u / G) + (it & 7)) * G + u % G);
+        }
+        const int ci = __builtin_amdgcn_readfirstlane(r / p.HV);
+        const int h = __builtin_amdgcn_readfirstlane(r % p.HV), hk = __builtin_amdgcn_readfirstlane(h / G);
         int start, len;
         if (small) {
             // chunk ci belongs to the last sequence whose first chunk id is <= ci (never an
