@@ -203,6 +203,17 @@ def main(argv=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    # host time of one call (argument checks, workspace carving, two or three
+    # launches, the Python binding): the calls are enqueued back to back and timed
+    # on the host only
+    torch.cuda.synchronize()
+    n_host = min(args.steps, 50)
+    h0 = time.perf_counter()
+    for i in range(n_host):
+        step(i)
+    h1 = time.perf_counter()
+    torch.cuda.synchronize()
+
     # second timed region of the same K steps with per-kernel HIP events recorded
     # by the library around each launch on the launch stream (the events add
     # their own gaps, so the throughput above comes from the clean region)
@@ -258,6 +269,7 @@ def main(argv=None):
                    "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roof,
         "path": {"algorithmic_bytes": by, "algorithmic_flops": fl,
+                 "host_us_per_call": 1e6 * (h1 - h0) / n_host,
                  "hbm_frac": by / step_s / (HBM_PEAK_GBS * 1e9),
                  "mfma_frac": fl / step_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                  "kernels": kern},

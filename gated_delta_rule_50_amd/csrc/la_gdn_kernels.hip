@@ -845,9 +845,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // nothing else, so each wait counts exactly the loads issued after the ones it
 // needs (loads complete in issue order).  Rows of k and q past a chunk's end are
 // out of the buffer's range and load as zeros.  The barriers order LDS only.
-// For the summary the state is widened to [S | P] (K x (V + K)): the P columns
-// start at the identity and see U~ = 0, so they evolve as the product of the
-// decayed erase steps; there are no outputs.
+// For the summary (k_inter_sum) the state is widened to [S | P] (K x (V + K)): the
+// P columns start at the identity and see U~ = 0, so they evolve as the product of
+// the decayed erase steps; there are no outputs and no output waves (the loader
+// waves are waves 2, 3).
 
 template <int K, int V, bool SUMMARY>
 struct InterCfg {
