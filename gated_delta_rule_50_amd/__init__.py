@@ -13,6 +13,9 @@ Entry points with the C names take torch tensors:
     la_gdn_summary(k, v, g, beta, cu_seqlens, start_state=None, end_state=None,
                    transition=None, l2norm=True, workspace=None, stream=None)
         -> (end_state, transition)
+    la_gdn_fwd_fused(..., beta_sigmoid=False, a_log=None, dt_bias=None, ...),
+    la_gdn_summary_fused(..., beta_sigmoid=False, a_log=None, dt_bias=None, ...):
+        the same with the gate / beta transforms fused into the kernels
     la_gdn_workspace_bytes(...), la_gdn_device_status(workspace),
     la_last_error_message(), la_gdn_profile_enable(on), la_gdn_profile_read(id)
 """
@@ -39,7 +42,8 @@ LA_KERNEL_COUNT = 3
 
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
-    "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_device_status",
+    "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_fused", "la_gdn_summary_fused",
+    "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
 
@@ -67,6 +71,14 @@ class Desc(ctypes.Structure):
     ]
 
 
+class Fusion(ctypes.Structure):
+    _fields_ = [
+        ("beta_sigmoid", ctypes.c_int32),
+        ("a_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -88,6 +100,11 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     lib.la_gdn_summary.restype = ctypes.c_int
     lib.la_gdn_summary.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    fp = ctypes.POINTER(Fusion)
+    lib.la_gdn_fwd_fused.restype = ctypes.c_int
+    lib.la_gdn_fwd_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, fp, vp, sz, vp]
+    lib.la_gdn_summary_fused.restype = ctypes.c_int
+    lib.la_gdn_summary_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, fp, vp, sz, vp]
     lib.la_gdn_device_status.restype = i32
     lib.la_gdn_device_status.argtypes = [vp, vp]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -193,6 +210,66 @@ def la_gdn_summary(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, 
     _check(lib.la_gdn_summary(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                               _ptr(cu_seqlens), _ptr(start_state), _ptr(end_state), _ptr(transition),
                               int(bool(l2norm)), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return end_state, transition
+
+
+def _fusion(beta: torch.Tensor, beta_sigmoid: bool, a_log, dt_bias) -> Fusion:
+    want = torch.bfloat16 if beta_sigmoid else torch.float32
+    if beta.dtype != want:
+        raise ValueError(f"beta must be {want} with beta_sigmoid={beta_sigmoid}, got {beta.dtype}")
+    for name, t in (("a_log", a_log), ("dt_bias", dt_bias)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 [HV] tensor")
+    return Fusion(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias))
+
+
+def la_gdn_fwd_fused(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final_state=None,
+                     output_final_state: bool = True, l2norm: bool = True, scale: Optional[float] = None,
+                     beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
+                     dt_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward with the gate / beta transforms fused into the kernels: beta is bf16
+    logits when beta_sigmoid, g is the raw gate when a_log is given."""
+    lib = load_library()
+    fusion = _fusion(beta, beta_sigmoid, a_log, dt_bias)
+    N = cu_seqlens.numel() - 1
+    T, HV, V = v.shape
+    K = k.shape[2]
+    if out is None:
+        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
+    desc = make_desc(k, v, g, beta, N, q=q, out=out, scale=scale)
+    if workspace is None:
+        workspace = alloc_workspace(desc, False, v.device)
+    _check(lib.la_gdn_fwd_fused(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                int(bool(l2norm)), ctypes.byref(fusion), _ptr(workspace), workspace.numel(),
+                                _stream(stream)))
+    return out, final_state
+
+
+def la_gdn_summary_fused(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, transition=None,
+                         l2norm: bool = True, beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
+                         dt_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Span summary with the gate / beta transforms fused into the kernels."""
+    lib = load_library()
+    fusion = _fusion(beta, beta_sigmoid, a_log, dt_bias)
+    N = cu_seqlens.numel() - 1
+    HV, V = v.shape[1], v.shape[2]
+    K = k.shape[2]
+    if end_state is None:
+        end_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
+    if transition is None:
+        transition = torch.empty((N, HV, K, K), dtype=torch.float32, device=v.device)
+    desc = make_desc(k, v, g, beta, N)
+    if workspace is None:
+        workspace = alloc_workspace(desc, True, v.device)
+    _check(lib.la_gdn_summary_fused(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(cu_seqlens), _ptr(start_state), _ptr(end_state), _ptr(transition),
+                                    int(bool(l2norm)), ctypes.byref(fusion), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
     return end_state, transition
 
 

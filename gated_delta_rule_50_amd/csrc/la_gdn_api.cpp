@@ -106,6 +106,33 @@ la_status check_f32(const char *name, const void *ptr, bool required)
     return LA_OK;
 }
 
+// beta (fp32, or bf16 logits under the in-kernel sigmoid) and the safe-gate parameters.
+la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la_gdn_fusion *f)
+{
+    const int64_t T = d.total_tokens;
+    const bool logits = f && f->beta_sigmoid;
+    if (!beta) return fail(LA_ERR_INVALID_ARGUMENT, "beta is NULL");
+    if (logits ? (reinterpret_cast<uintptr_t>(beta) & 1u) != 0 : !aligned4(beta))
+        return fail(LA_ERR_INVALID_ARGUMENT, "beta is not %d-byte aligned", logits ? 2 : 4);
+    if (T > 1 && d.beta_stride_t < d.num_v_heads)
+        return fail(LA_ERR_INVALID_ARGUMENT, "beta token stride %lld is smaller than num_v_heads %d",
+                    (long long)d.beta_stride_t, d.num_v_heads);
+    if (!f) return LA_OK;
+    if (f->dt_bias && !f->a_log) return fail(LA_ERR_INVALID_ARGUMENT, "dt_bias is given without a_log");
+    la_status st = check_f32("a_log", f->a_log, false);
+    if (st == LA_OK) st = check_f32("dt_bias", f->dt_bias, false);
+    return st;
+}
+
+void set_beta_and_fusion(la::Prob &p, const void *beta, const la_gdn_fusion *f)
+{
+    const bool logits = f && f->beta_sigmoid;
+    p.beta = logits ? nullptr : static_cast<const float *>(beta);
+    p.beta16 = logits ? static_cast<const __bf16 *>(beta) : nullptr;
+    p.a_log = f ? f->a_log : nullptr;
+    p.dt_bias = f ? f->dt_bias : nullptr;
+}
+
 // ---------------------------------------------------------------------------
 // per-kernel timing
 
@@ -288,6 +315,15 @@ la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, cons
                      const float *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
                      float *final_state, int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
+    return la_gdn_fwd_fused(desc, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, l2norm, nullptr,
+                            workspace, workspace_bytes, stream);
+}
+
+la_status la_gdn_fwd_fused(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                           const void *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
+                           float *final_state, int l2norm, const la_gdn_fusion *fusion, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream)
+{
     g_error.clear();
     la_status st = check_desc(desc);
     if (st != LA_OK) return st;
@@ -298,7 +334,7 @@ la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, cons
     if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
     if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
-    if ((st = check_rows("beta", beta, d.beta_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
     if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
     if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
     if ((st = check_f32("initial_state", initial_state, false)) != LA_OK) return st;
@@ -309,7 +345,7 @@ la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, cons
     p.k = static_cast<const __bf16 *>(k);
     p.v = static_cast<const __bf16 *>(v);
     p.g = g;
-    p.beta = beta;
+    set_beta_and_fusion(p, beta, fusion);
     p.cu = cu_seqlens;
     p.s0 = initial_state;
     p.o = static_cast<__bf16 *>(out);
@@ -322,6 +358,15 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
                          const int32_t *cu_seqlens, const float *start_state, float *end_state, float *transition,
                          int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
+    return la_gdn_summary_fused(desc, k, v, g, beta, cu_seqlens, start_state, end_state, transition, l2norm, nullptr,
+                                workspace, workspace_bytes, stream);
+}
+
+la_status la_gdn_summary_fused(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
+                               const void *beta, const int32_t *cu_seqlens, const float *start_state,
+                               float *end_state, float *transition, int l2norm, const la_gdn_fusion *fusion,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
     g_error.clear();
     la_status st = check_desc(desc);
     if (st != LA_OK) return st;
@@ -330,7 +375,7 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
     if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
     if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
-    if ((st = check_rows("beta", beta, d.beta_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
     if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
     if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
     if ((st = check_f32("start_state", start_state, false)) != LA_OK) return st;
@@ -342,7 +387,7 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
     p.k = static_cast<const __bf16 *>(k);
     p.v = static_cast<const __bf16 *>(v);
     p.g = g;
-    p.beta = beta;
+    set_beta_and_fusion(p, beta, fusion);
     p.cu = cu_seqlens;
     p.s0 = start_state;
     p.o = nullptr;

@@ -23,7 +23,9 @@ struct Prob {
     int32_t intra_grid;               // workgroups of the persistent intra-chunk kernel
     const __bf16 *q, *k, *v;
     int64_t qst, qsh, kst, ksh, vst, vsh, ost, osh, gst, bst;
-    const float *g, *beta;
+    const float *g, *beta;            // beta: fp32, or null when beta16 is set
+    const __bf16 *beta16;             // beta logits in bf16 (beta = sigmoid(logit) in the kernel), or null
+    const float *a_log, *dt_bias;     // safe gate g = -exp(a_log[h]) softplus(g + dt_bias[h]), or null
     const int32_t *cu;
     const float *s0;                  // initial / start state or null
     __bf16 *o;                        // forward output or null (summary)

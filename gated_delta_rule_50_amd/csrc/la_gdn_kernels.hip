@@ -557,11 +557,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         if (FWD)
             intra_load_tile<K>(sX, p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst, len,
                                wave, lane, 4);
+        float blogit = 0.f;   // beta logit of token `lane` (beta16 only)
         if (wave == 3) {
             const i32x4 rg = make_rsrc(p.g + (int64_t)start * p.gst + h, (uint32_t)len * 4u * (uint32_t)p.gst);
             b2l_dword(rg, s_g, (uint32_t)lane * 4u * (uint32_t)p.gst);
-            const i32x4 rb = make_rsrc(p.beta + (int64_t)start * p.bst + h, (uint32_t)len * 4u * (uint32_t)p.bst);
-            b2l_dword(rb, s_b, (uint32_t)lane * 4u * (uint32_t)p.bst);
+            if (p.beta16) {
+                if (lane < len) blogit = bf2f(p.beta16[(int64_t)(start + lane) * p.bst + h]);
+            } else {
+                const i32x4 rb = make_rsrc(p.beta + (int64_t)start * p.bst + h, (uint32_t)len * 4u * (uint32_t)p.bst);
+                b2l_dword(rb, s_b, (uint32_t)lane * 4u * (uint32_t)p.bst);
+            }
         }
         vm_wait<0>();
         lds_barrier();
@@ -593,8 +598,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 Pt = mfma32(lds_row8<PK>(sK, 32 * pm + c, 16 * s + 8 * hh), lds_row8<PK>(sX, 32 * pn + c, 16 * s + 8 * hh), Pt);
         }
         if (wave == 3) {
+            // the gate and beta transforms fused into the prologue (the cudnn-frontend PR
+            // "Further reduce FROST LA CPU overhead + fully support all L2norm, beta, gate
+            // fusion", commit notes: safe_gate with a_log / dt_bias, use_beta_sigmoid_in_kernel)
+            float gr = s_g[lane];
+            if (p.a_log) {
+                const float x = gr + (p.dt_bias ? p.dt_bias[h] : 0.f);
+                const float softplus = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+                gr = lane < len ? -expf(p.a_log[h]) * softplus : 0.f;
+            }
+            if (p.beta16) s_b[lane] = lane < len ? 1.f / (1.f + expf(-blogit)) : 0.f;
             // inclusive scan of g log2(e) (zeros past the end)
-            float xg = s_g[lane] * kLog2e;
+            float xg = gr * kLog2e;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(xg, off, 64);

@@ -127,6 +127,46 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Gate and beta transforms fused into the kernels (the cudnn-frontend pull
+ * request "Further reduce FROST LA CPU overhead + fully support all L2norm,
+ * beta, gate fusion", commit notes on gated_delta_net: use_beta_sigmoid_in_kernel,
+ * and safe_gate with a_log / dt_bias, computing -exp(a_log) * softplus(g + dt_bias)
+ * with a zero dt_bias when none is given; beta arrives in the io dtype under the
+ * in-kernel sigmoid, else in fp32).
+ *   beta_sigmoid  nonzero: `beta` is bf16 [T, HV] logits (stride beta_stride_t,
+ *                 2-byte aligned) and the kernels use beta = 1 / (1 + exp(-logit));
+ *                 zero: `beta` is fp32 [T, HV] as for la_gdn_fwd
+ *   a_log         device, fp32 [HV], or NULL for the plain natural-log gate; when
+ *                 given, `g` is the raw gate and the kernels use, per token t and
+ *                 value head h, g = -exp(a_log[h]) * log(1 + exp(g_raw[t][h] + dt_bias[h]))
+ *   dt_bias       device, fp32 [HV], or NULL for zeros; only with a_log
+ * The transforms run in fp32 in the prologue; everything after them is as
+ * for la_gdn_fwd / la_gdn_summary.
+ */
+typedef struct {
+    int32_t beta_sigmoid;
+    const float *a_log;
+    const float *dt_bias;
+} la_gdn_fusion;
+
+/*
+ * la_gdn_fwd and la_gdn_summary with the transforms above (fusion NULL: the
+ * plain calls).  Arguments, errors and outputs are those of the plain calls;
+ * `beta` is bf16 or fp32 as fusion->beta_sigmoid says.  A dt_bias without a_log,
+ * or a misaligned a_log, dt_bias or beta, is LA_ERR_INVALID_ARGUMENT.
+ */
+la_status la_gdn_fwd_fused(const la_gdn_desc *desc, const void *q, const void *k, const void *v,
+                           const float *g, const void *beta, const int32_t *cu_seqlens,
+                           const float *initial_state, void *out, float *final_state, int l2norm,
+                           const la_gdn_fusion *fusion, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+la_status la_gdn_summary_fused(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
+                               const void *beta, const int32_t *cu_seqlens, const float *start_state,
+                               float *end_state, float *transition, int l2norm,
+                               const la_gdn_fusion *fusion, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * Reads the status word the last call on this workspace left (LA_DEVICE_*
  * bits).  Synchronises the stream.  Returns -1 if the read itself failed.
  */

@@ -52,6 +52,9 @@ class _Problem(ctypes.Structure):
         ("g", ctypes.c_void_p),
         ("beta", ctypes.c_void_p),
         ("initial_state", ctypes.c_void_p),
+        ("beta_logit", ctypes.c_void_p),
+        ("a_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
     ]
 
 
@@ -112,7 +115,13 @@ class Oracle:
         self.k = _bits(p.k)
         self.v = _bits(p.v)
         self.g = _f32(p.g)
-        self.beta = _f32(p.beta)
+        # gate and beta transforms: a problem with beta_sigmoid carries bf16 beta logits;
+        # one with a_log carries the raw gate (see gdn_oracle.c)
+        fused_beta = bool(getattr(p, "beta_sigmoid", False))
+        self.beta = None if fused_beta else _f32(p.beta)
+        self.beta_logit = _bits(p.beta) if fused_beta else None
+        self.a_log = _f32(getattr(p, "a_log", None))
+        self.dt_bias = _f32(getattr(p, "dt_bias", None))
         st = p.state if initial_state is None else initial_state
         self.s0 = _f32(st) if use_initial_state else None
         self.N = len(self.cu) - 1
@@ -124,7 +133,8 @@ class Oracle:
         self.l2norm = bool(p.l2norm)
         self._st = _Problem(self.N, self.HK, self.HV, self.K, self.V, int(self.l2norm), self.scale,
                             _ptr(self.cu), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.g),
-                            _ptr(self.beta), _ptr(self.s0))
+                            _ptr(self.beta), _ptr(self.s0), _ptr(self.beta_logit), _ptr(self.a_log),
+                            _ptr(self.dt_bias))
 
     def lengths(self) -> List[int]:
         return [int(self.cu[i + 1] - self.cu[i]) for i in range(self.N)]

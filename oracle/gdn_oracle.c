@@ -36,6 +36,12 @@
  *     S_final[j][v] = sum_i S_init[i][v] * transition[i][j] + S_span[j][v].
  *   - An empty sequence (start == end) leaves the state as it was and the
  *     transition equal to the identity.
+ *   - Gate and beta transforms (the cudnn-frontend PR's commit notes on
+ *     gated_delta_net: use_beta_sigmoid_in_kernel, and safe_gate with a_log /
+ *     dt_bias, -exp(a_log) * softplus(g + dt_bias), dt_bias zero when absent):
+ *     with beta logits given, beta_t = 1 / (1 + exp(-logit_t)); with a_log
+ *     given, the gate is g_t = -exp(a_log[h]) * log(1 + exp(g_t + dt_bias[h]))
+ *     in place of the natural-log gate.  Both in double precision.
  *
  * Inputs are taken exactly: bf16 bit patterns are widened to double, fp32
  * values are widened to double.  Every sum is a plain left-to-right loop.
@@ -102,8 +108,15 @@ static int run_unit(const gdn_oracle_problem *p, int32_t seq, int32_t head,
         load_row(p->k, t, HK, hk, K, k);
         load_row(p->v, t, HV, head, V, v);
         if (p->l2norm) l2_normalise(k, K);
-        const double a = exp((double)p->g[t * HV + head]);
-        const double b = (double)p->beta[t * HV + head];
+        double gt = (double)p->g[t * HV + head];
+        if (p->a_log) {
+            const double x = gt + (p->dt_bias ? (double)p->dt_bias[head] : 0.0);
+            const double softplus = x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+            gt = -exp((double)p->a_log[head]) * softplus;
+        }
+        const double a = exp(gt);
+        const double b = p->beta_logit ? 1.0 / (1.0 + exp(-bf16_bits_to_double(p->beta_logit[t * HV + head])))
+                                       : (double)p->beta[t * HV + head];
 
         /* decay */
         for (int64_t i = 0; i < (int64_t)K * V; ++i) S[i] *= a;
@@ -156,7 +169,8 @@ int gdn_oracle_run(const gdn_oracle_problem *p, int32_t n_units, const int32_t *
 {
     if (!p || n_units < 0 || (n_units > 0 && (!unit_seq || !unit_head))) return -2;
     if (p->num_qk_heads <= 0 || p->num_v_heads <= 0 || p->num_v_heads % p->num_qk_heads) return -2;
-    if (p->head_dim_k <= 0 || p->head_dim_v <= 0 || !p->k || !p->v || !p->g || !p->beta) return -2;
+    if (p->head_dim_k <= 0 || p->head_dim_v <= 0 || !p->k || !p->v || !p->g || (!p->beta && !p->beta_logit)) return -2;
+    if (p->dt_bias && !p->a_log) return -2;
     if (o && (!p->q || !o_offset)) return -2;
     for (int32_t u = 0; u < n_units; ++u) {
         if (unit_seq[u] < 0 || unit_seq[u] >= p->num_seqs) return -2;

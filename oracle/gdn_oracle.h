@@ -29,6 +29,10 @@ typedef struct {
     const float *g;                /* [T, HV], natural-log gate */
     const float *beta;             /* [T, HV] */
     const float *initial_state;    /* [N, HV, K, V] or NULL for zeros */
+    /* gate and beta transforms (see gdn_oracle.c); all NULL for the plain inputs */
+    const uint16_t *beta_logit;    /* bf16 bits [T, HV]: beta = 1 / (1 + exp(-logit)); replaces beta */
+    const float *a_log;            /* [HV]: g = -exp(a_log) * softplus(g + dt_bias) */
+    const float *dt_bias;          /* [HV] or NULL for zeros (with a_log only) */
 } gdn_oracle_problem;
 
 /*

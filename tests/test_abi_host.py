@@ -169,3 +169,37 @@ def test_profiler_ids(lib):
     assert la.la_gdn_kernel_name(99) == ""
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.la_gdn_profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == la.LA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("fusion,beta,status,needle", [
+    (dict(beta_sigmoid=0, a_log=None, dt_bias=1 << 20), 1 << 20, la.LA_ERR_INVALID_ARGUMENT, "without a_log"),
+    (dict(beta_sigmoid=0, a_log=(1 << 20) + 2, dt_bias=None), 1 << 20, la.LA_ERR_INVALID_ARGUMENT, "a_log"),
+    (dict(beta_sigmoid=0, a_log=1 << 20, dt_bias=(1 << 20) + 1), 1 << 20, la.LA_ERR_INVALID_ARGUMENT, "dt_bias"),
+    (dict(beta_sigmoid=1, a_log=None, dt_bias=None), (1 << 20) + 1, la.LA_ERR_INVALID_ARGUMENT, "2-byte"),
+    (dict(beta_sigmoid=0, a_log=None, dt_bias=None), (1 << 20) + 2, la.LA_ERR_INVALID_ARGUMENT, "4-byte"),
+    (dict(beta_sigmoid=1, a_log=None, dt_bias=None), None, la.LA_ERR_INVALID_ARGUMENT, "beta is NULL"),
+])
+def test_fused_argument_checks(lib, fusion, beta, status, needle):
+    """The gate / beta transform options are checked on the host before any launch:
+    bf16 beta logits need 2-byte alignment (fp32 beta 4), a_log and dt_bias 4, and
+    dt_bias only comes with a_log."""
+    a = _fwd_args()
+    d = _desc()
+    f = la.Fusion(fusion["beta_sigmoid"], fusion["a_log"], fusion["dt_bias"])
+    rc = lib.la_gdn_fwd_fused(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
+                              a["fin"], 1, ctypes.byref(f), a["ws"], a["wsb"], None)
+    assert rc == status, la.la_last_error_message()
+    assert needle in la.la_last_error_message()
+    rc = lib.la_gdn_summary_fused(ctypes.byref(d), a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
+                                  a["fin"], 1, ctypes.byref(f), a["ws"], a["wsb"], None)
+    assert rc == status, la.la_last_error_message()
+
+
+def test_fused_binding_checks_beta_dtype():
+    t = torch.zeros(4, 2)
+    with pytest.raises(ValueError, match="bfloat16"):
+        la._fusion(t, True, None, None)
+    with pytest.raises(ValueError, match="float32"):
+        la._fusion(t.to(torch.bfloat16), False, None, None)
+    with pytest.raises(ValueError, match="a_log"):
+        la._fusion(t, False, torch.zeros(2, dtype=torch.float64), None)

@@ -1,0 +1,76 @@
+"""GPU parity of the gate and beta transforms fused into the kernels
+(la_gdn_fwd_fused / la_gdn_summary_fused): beta as bf16 logits with the
+sigmoid in the kernel, and the safe gate -exp(a_log) softplus(g + dt_bias),
+against the fp64 oracle, which applies the same transforms in double
+precision.  Tolerances as for the plain calls."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_50_amd as la
+from oracle import Oracle, rel_l2
+from workloads import fused_problem
+
+from gpu_helpers import TOL_O, TOL_STATE, f64, note
+
+pytestmark = pytest.mark.gpu
+
+
+def fwd_fused(p, **kw):
+    g = p.to("cuda")
+    out, fin = la.la_gdn_fwd_fused(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                   beta_sigmoid=p.beta_sigmoid, a_log=g.a_log, dt_bias=g.dt_bias, **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def check(p):
+    note(f"fused fwd: {p.name} beta_sigmoid={p.beta_sigmoid} safe_gate={p.a_log is not None}")
+    out, fin = fwd_fused(p)
+    ref = Oracle(p).run_all()
+    eo, es = rel_l2(f64(out), ref["o"]), rel_l2(f64(fin), ref["state"])
+    assert eo <= TOL_O and es <= TOL_STATE, (eo, es)
+    return out, fin
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128)])
+def test_fused_gate_and_beta_ragged(dk, dv):
+    check(fused_problem((1, 63, 64, 65, 130, 200), hk=2, hv=4, dk=dk, dv=dv, seed=51, with_state=True))
+
+
+@pytest.mark.parametrize("beta_sigmoid,safe_gate", [(True, False), (False, True)])
+def test_one_transform_at_a_time(beta_sigmoid, safe_gate):
+    check(fused_problem((70, 300), hk=1, hv=2, dk=128, dv=128, seed=52, with_state=True,
+                        beta_sigmoid=beta_sigmoid, safe_gate=safe_gate))
+
+
+def test_fused_varlen_h16_full_size():
+    # the varlen workload's shapes (T = 4096, 1000/1500/1596, H = 16, K = V = 128)
+    check(fused_problem((1000, 1500, 1596), hk=16, hv=16, dk=128, dv=128, seed=53))
+
+
+def test_dt_bias_null_equals_zero_bias_bitwise():
+    p = fused_problem((100, 257), hk=2, hv=4, dk=128, dv=128, seed=54, with_state=True)
+    a = dataclasses.replace(p, dt_bias=None)
+    b = dataclasses.replace(p, dt_bias=torch.zeros_like(p.dt_bias))
+    note("dt_bias NULL vs zeros")
+    o1, f1 = fwd_fused(a)
+    o2, f2 = fwd_fused(b)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_fused_summary_slow_decay():
+    # a_log shifted by log(1/4096) and beta logits by -4: a transition far from zero
+    p = fused_problem((1, 64, 100, 300), hk=2, hv=2, dk=128, dv=128, seed=55, with_state=True, summary=True,
+                      a_log_shift=-np.log(4096.0), beta_logit_shift=-4.0)
+    g = p.to("cuda")
+    note("fused summary slow decay")
+    end, tr = la.la_gdn_summary_fused(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state,
+                                      beta_sigmoid=True, a_log=g.a_log, dt_bias=g.dt_bias)
+    torch.cuda.synchronize()
+    ref = Oracle(p).run_all(want_o=False, want_transition=True)
+    assert rel_l2(f64(end), ref["state"]) <= TOL_STATE
+    assert rel_l2(f64(tr), ref["transition"]) <= TOL_STATE
+    assert np.abs(ref["transition"]).max() > 0.05   # not vacuous

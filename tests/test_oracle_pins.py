@@ -367,3 +367,70 @@ def test_config_vacuity_findings():
     p = make((512,), 1, 1, 16, 16, seed=14, g_div=4096.0, beta_div=64.0)
     tr = Oracle(p, use_initial_state=False).run_all(want_o=False, want_transition=True)["transition"]
     assert 1e-3 < np.abs(tr).max() < 2.0
+
+
+# ----------------------------------------------------------------------------
+# gate and beta transforms (the cudnn-frontend PR's commit notes: safe_gate with
+# a_log / dt_bias, -exp(a_log) * softplus(g + dt_bias); use_beta_sigmoid_in_kernel).
+# The plain-input oracle is pinned above; these pin the transforms against it, with
+# the gate and beta computed by torch's own softplus and sigmoid.
+
+from workloads import fused_problem  # noqa: E402
+
+
+def _plain_from(p, g, beta):
+    return dataclasses.replace(p, g=g.to(torch.float32), beta=beta.to(torch.float32), beta_sigmoid=False,
+                               a_log=None, dt_bias=None)
+
+
+def _run(p):
+    r = Oracle(p).run_all(want_o=p.q is not None, want_transition=p.summary)
+    return r
+
+
+@pytest.mark.parametrize("summary", [False, True])
+def test_safe_gate_and_beta_sigmoid_match_library_transforms(summary):
+    p = fused_problem((5, 70, 129), hk=1, hv=2, dk=16, dv=8, seed=41, with_state=True, summary=summary)
+    raw = p.g.double() + p.dt_bias.double()[None, :]
+    g = -torch.exp(p.a_log.double())[None, :] * torch.nn.functional.softplus(raw)
+    beta = torch.sigmoid(p.beta.double())
+    fused, plain = _run(p), _run(_plain_from(p, g, beta))
+    for key in fused:
+        # the plain oracle reads fp32 gates and betas: agreement to their rounding
+        assert rel_l2(fused[key], plain[key]) < 1e-6, key
+    assert np.abs(g.numpy()).max() > 1e-3   # the gate is not vacuous
+
+
+def test_safe_gate_with_unit_a_log_and_zero_bias_is_minus_softplus():
+    p = fused_problem((40, 90), hk=1, hv=2, dk=16, dv=8, seed=42, with_state=True, beta_sigmoid=False)
+    p = dataclasses.replace(p, a_log=torch.zeros(2), dt_bias=None)
+    plain = _plain_from(p, -torch.nn.functional.softplus(p.g.double()), p.beta)
+    a, b = _run(p), _run(plain)
+    assert rel_l2(a["o"], b["o"]) < 1e-6 and rel_l2(a["state"], b["state"]) < 1e-6
+
+
+def test_dt_bias_shifts_the_raw_gate():
+    p = fused_problem((33, 64), hk=1, hv=2, dk=8, dv=8, seed=43, with_state=True)
+    shifted = dataclasses.replace(p, g=(p.g.double() + p.dt_bias.double()[None, :]).float(), dt_bias=None)
+    a, b = _run(p), _run(shifted)
+    assert rel_l2(a["o"], b["o"]) < 1e-6 and rel_l2(a["state"], b["state"]) < 1e-6
+
+
+def test_a_log_scales_the_log_decay():
+    # a_log + log 2 doubles every log-decay: the same as the plain gate 2 g
+    p = fused_problem((33, 64), hk=1, hv=2, dk=8, dv=8, seed=44, with_state=True, beta_sigmoid=False)
+    doubled = dataclasses.replace(p, a_log=p.a_log + math.log(2.0))
+    raw = p.g.double() + p.dt_bias.double()[None, :]
+    g2 = -2.0 * torch.exp(p.a_log.double())[None, :] * torch.nn.functional.softplus(raw)
+    a, b = _run(doubled), _run(_plain_from(p, g2, p.beta))
+    assert rel_l2(a["o"], b["o"]) < 1e-6 and rel_l2(a["state"], b["state"]) < 1e-6
+
+
+def test_beta_logits_at_large_magnitude():
+    # sigmoid saturates cleanly: logits of +-80 give beta 1 and 0 without overflow
+    p = fused_problem((20,), hk=1, hv=1, dk=8, dv=8, seed=45, with_state=False, safe_gate=False)
+    big = torch.where(torch.arange(20)[:, None] % 2 == 0, torch.tensor(80.0), torch.tensor(-80.0))
+    p = dataclasses.replace(p, beta=big.to(torch.bfloat16))
+    plain = _plain_from(p, p.g, torch.where(big > 0, torch.tensor(1.0), torch.tensor(0.0)))
+    a, b = _run(p), _run(plain)
+    assert np.isfinite(a["o"]).all() and rel_l2(a["o"], b["o"]) < 1e-12

@@ -17,6 +17,7 @@ from __future__ import annotations
 import dataclasses
 from typing import Dict, List, Optional
 
+import numpy as np
 import torch
 
 __all__ = ["Problem", "CONFIGS", "make_problem", "custom_problem", "config_lengths"]
@@ -36,6 +37,11 @@ class Problem:
     state: Optional[torch.Tensor]     # fp32 [N, HV, K, V] or None (zero start)
     l2norm: bool = True
     summary: bool = False
+    # gate and beta transforms: with beta_sigmoid, `beta` holds bf16 logits; with a_log,
+    # `g` holds the raw gate and g = -exp(a_log) softplus(g + dt_bias) per value head
+    beta_sigmoid: bool = False
+    a_log: Optional[torch.Tensor] = None     # fp32 [HV]
+    dt_bias: Optional[torch.Tensor] = None   # fp32 [HV] or None
 
     @property
     def num_seqs(self) -> int:
@@ -70,7 +76,8 @@ class Problem:
             return None if x is None else x.to(device)
         return dataclasses.replace(
             self, cu_seqlens=mv(self.cu_seqlens), q=mv(self.q), k=mv(self.k), v=mv(self.v),
-            g=mv(self.g), beta=mv(self.beta), state=mv(self.state))
+            g=mv(self.g), beta=mv(self.beta), state=mv(self.state), a_log=mv(self.a_log),
+            dt_bias=mv(self.dt_bias))
 
 
 # The five workloads.  "lengths" is a list, or "ragged" for the case whose
@@ -165,3 +172,42 @@ def custom_problem(lengths, hk, hv, dk, dv, seed=0, with_state=False, summary=Fa
                                         not summary, device)
     return Problem(name=f"custom{tuple(lengths)}", cu_seqlens=cu.to(device), q=q, k=k, v=v, g=g / g_div,
                    beta=beta / beta_div, state=state, l2norm=l2norm, summary=summary)
+
+
+def fused_problem(lengths, hk, hv, dk, dv, seed=0, with_state=False, summary=False, beta_sigmoid=True,
+                  safe_gate=True, with_dt_bias=True, a_log_shift=0.0, beta_logit_shift=0.0,
+                  device="cpu") -> Problem:
+    """Inputs for the gate and beta transforms fused into the kernels.
+
+    q, k, v and the state as in custom_problem.  The raw gate is N(0,1) fp32 and
+    the beta logits N(0,1) rounded to bf16 (plus beta_logit_shift).  Per value
+    head, a_log = log(A) with A ~ U(1, 16) (plus a_log_shift) and dt_bias the
+    inverse softplus of dt, log dt ~ U(log 1e-3, log 1e-1): the shapes of the
+    usual Gated DeltaNet layer's initialisation, so that the effective gate
+    -exp(a_log) softplus(g + dt_bias) is about -0.1 per token.  Draw order: the
+    custom_problem draws, then raw gate, beta logits, A, dt.
+    """
+    gen = torch.Generator(device=device).manual_seed(seed)
+    cu, q, k, v, _, _, state = _draw(gen, list(lengths), hk, hv, dk, dv, with_state, not summary, device)
+    T = int(sum(lengths))
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+
+    def rand(*shape):
+        return torch.rand(*shape, generator=gen, dtype=torch.float32, device=device)
+
+    g_raw = randn(T, hv)
+    logits = (randn(T, hv) + beta_logit_shift).to(torch.bfloat16)
+    A = 1.0 + 15.0 * rand(hv)
+    dt = torch.exp(np.log(1e-3) + (np.log(1e-1) - np.log(1e-3)) * rand(hv))
+    a_log = (torch.log(A) + a_log_shift) if safe_gate else None
+    dt_bias = (dt + torch.log(-torch.expm1(-dt))) if (safe_gate and with_dt_bias) else None
+    if safe_gate:
+        g = g_raw
+    else:
+        g = -torch.nn.functional.softplus(g_raw)
+    beta = logits if beta_sigmoid else torch.sigmoid(logits.float())
+    return Problem(name=f"fused{tuple(lengths)}", cu_seqlens=cu.to(device), q=q, k=k, v=v, g=g, beta=beta,
+                   state=state, l2norm=True, summary=summary, beta_sigmoid=beta_sigmoid, a_log=a_log,
+                   dt_bias=dt_bias)
