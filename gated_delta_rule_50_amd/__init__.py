@@ -13,9 +13,12 @@ Entry points with the C names take torch tensors:
     la_gdn_summary(k, v, g, beta, cu_seqlens, start_state=None, end_state=None,
                    transition=None, l2norm=True, workspace=None, stream=None)
         -> (end_state, transition)
-    la_gdn_fwd_fused(..., beta_sigmoid=False, a_log=None, dt_bias=None, ...),
-    la_gdn_summary_fused(..., beta_sigmoid=False, a_log=None, dt_bias=None, ...):
-        the same with the gate / beta transforms fused into the kernels
+    la_gdn_fwd_ex(..., beta_sigmoid=False, a_log=None, dt_bias=None,
+                  checkpoint_every_n_tokens=0, checkpoint_dtype=torch.bfloat16, ...)
+        -> (out, final_state, checkpoints or None)
+    la_gdn_summary_ex(..., beta_sigmoid=False, a_log=None, dt_bias=None, ...):
+        the same with the gate / beta transforms fused into the kernels and, for the
+        forward, the state series
     la_gdn_workspace_bytes(...), la_gdn_device_status(workspace),
     la_last_error_message(), la_gdn_profile_enable(on), la_gdn_profile_read(id)
 """
@@ -42,7 +45,7 @@ LA_KERNEL_COUNT = 3
 
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
-    "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_fused", "la_gdn_summary_fused",
+    "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex",
     "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
@@ -71,11 +74,15 @@ class Desc(ctypes.Structure):
     ]
 
 
-class Fusion(ctypes.Structure):
+class Options(ctypes.Structure):
     _fields_ = [
         ("beta_sigmoid", ctypes.c_int32),
         ("a_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p),
+        ("checkpoint_every_n_tokens", ctypes.c_int32),
+        ("checkpoint_fp32", ctypes.c_int32),
+        ("checkpoints", ctypes.c_void_p),
+        ("checkpoint_capacity", ctypes.c_int64),
     ]
 
 
@@ -100,11 +107,11 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     lib.la_gdn_summary.restype = ctypes.c_int
     lib.la_gdn_summary.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
-    fp = ctypes.POINTER(Fusion)
-    lib.la_gdn_fwd_fused.restype = ctypes.c_int
-    lib.la_gdn_fwd_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, fp, vp, sz, vp]
-    lib.la_gdn_summary_fused.restype = ctypes.c_int
-    lib.la_gdn_summary_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, fp, vp, sz, vp]
+    op = ctypes.POINTER(Options)
+    lib.la_gdn_fwd_ex.restype = ctypes.c_int
+    lib.la_gdn_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
+    lib.la_gdn_summary_ex.restype = ctypes.c_int
+    lib.la_gdn_summary_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
     lib.la_gdn_device_status.restype = i32
     lib.la_gdn_device_status.argtypes = [vp, vp]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -213,25 +220,34 @@ def la_gdn_summary(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, 
     return end_state, transition
 
 
-def _fusion(beta: torch.Tensor, beta_sigmoid: bool, a_log, dt_bias) -> Fusion:
+def _options(beta: torch.Tensor, beta_sigmoid: bool, a_log, dt_bias) -> Options:
     want = torch.bfloat16 if beta_sigmoid else torch.float32
     if beta.dtype != want:
         raise ValueError(f"beta must be {want} with beta_sigmoid={beta_sigmoid}, got {beta.dtype}")
     for name, t in (("a_log", a_log), ("dt_bias", dt_bias)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 [HV] tensor")
-    return Fusion(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias))
+    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0)
 
 
-def la_gdn_fwd_fused(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final_state=None,
-                     output_final_state: bool = True, l2norm: bool = True, scale: Optional[float] = None,
-                     beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
-                     dt_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Forward with the gate / beta transforms fused into the kernels: beta is bf16
-    logits when beta_sigmoid, g is the raw gate when a_log is given."""
+def checkpoint_entries(cu_seqlens: torch.Tensor, every_n_tokens: int) -> int:
+    """Entries of the state series: sum over sequences of ceil(length / n) (reads cu_seqlens)."""
+    lens = (cu_seqlens[1:] - cu_seqlens[:-1]).to(torch.int64)
+    return int(((lens + every_n_tokens - 1) // every_n_tokens).sum().item())
+
+
+def la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final_state=None,
+                  output_final_state: bool = True, l2norm: bool = True, scale: Optional[float] = None,
+                  beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
+                  dt_bias: Optional[torch.Tensor] = None, checkpoint_every_n_tokens: int = 0,
+                  checkpoint_dtype=torch.bfloat16, checkpoints: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """Forward with the options of la_gdn_fwd_ex: beta is bf16 logits when beta_sigmoid,
+    g is the raw gate when a_log is given, and checkpoint_every_n_tokens > 0 also returns
+    the state series [E, HV, K, V] (checkpoint_dtype bf16 or fp32).  Returns
+    (out, final_state, checkpoints or None)."""
     lib = load_library()
-    fusion = _fusion(beta, beta_sigmoid, a_log, dt_bias)
+    opts = _options(beta, beta_sigmoid, a_log, dt_bias)
     N = cu_seqlens.numel() - 1
     T, HV, V = v.shape
     K = k.shape[2]
@@ -239,23 +255,33 @@ def la_gdn_fwd_fused(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None,
         out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
+    if checkpoint_every_n_tokens:
+        if checkpoint_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("checkpoint_dtype must be torch.bfloat16 or torch.float32")
+        if checkpoints is None:
+            E = checkpoint_entries(cu_seqlens, checkpoint_every_n_tokens) if checkpoint_every_n_tokens > 0 else 0
+            checkpoints = torch.empty((E, HV, K, V), dtype=checkpoint_dtype, device=v.device)
+        opts.checkpoint_every_n_tokens = int(checkpoint_every_n_tokens)
+        opts.checkpoint_fp32 = int(checkpoints.dtype == torch.float32)
+        opts.checkpoints = _ptr(checkpoints)
+        opts.checkpoint_capacity = int(checkpoints.shape[0])
     desc = make_desc(k, v, g, beta, N, q=q, out=out, scale=scale)
     if workspace is None:
         workspace = alloc_workspace(desc, False, v.device)
-    _check(lib.la_gdn_fwd_fused(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
-                                int(bool(l2norm)), ctypes.byref(fusion), _ptr(workspace), workspace.numel(),
-                                _stream(stream)))
-    return out, final_state
+    _check(lib.la_gdn_fwd_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                             int(bool(l2norm)), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
+                             _stream(stream)))
+    return out, final_state, checkpoints
 
 
-def la_gdn_summary_fused(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, transition=None,
-                         l2norm: bool = True, beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
-                         dt_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+def la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, transition=None,
+                      l2norm: bool = True, beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
+                      dt_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Span summary with the gate / beta transforms fused into the kernels."""
     lib = load_library()
-    fusion = _fusion(beta, beta_sigmoid, a_log, dt_bias)
+    opts = _options(beta, beta_sigmoid, a_log, dt_bias)
     N = cu_seqlens.numel() - 1
     HV, V = v.shape[1], v.shape[2]
     K = k.shape[2]
@@ -266,10 +292,10 @@ def la_gdn_summary_fused(k, v, g, beta, cu_seqlens, start_state=None, end_state=
     desc = make_desc(k, v, g, beta, N)
     if workspace is None:
         workspace = alloc_workspace(desc, True, v.device)
-    _check(lib.la_gdn_summary_fused(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                    _ptr(cu_seqlens), _ptr(start_state), _ptr(end_state), _ptr(transition),
-                                    int(bool(l2norm)), ctypes.byref(fusion), _ptr(workspace), workspace.numel(),
-                                    _stream(stream)))
+    _check(lib.la_gdn_summary_ex(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(cu_seqlens), _ptr(start_state), _ptr(end_state), _ptr(transition),
+                                 int(bool(l2norm)), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
     return end_state, transition
 
 

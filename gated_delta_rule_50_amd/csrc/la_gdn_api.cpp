@@ -107,7 +107,7 @@ la_status check_f32(const char *name, const void *ptr, bool required)
 }
 
 // beta (fp32, or bf16 logits under the in-kernel sigmoid) and the safe-gate parameters.
-la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la_gdn_fusion *f)
+la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la_gdn_options *f)
 {
     const int64_t T = d.total_tokens;
     const bool logits = f && f->beta_sigmoid;
@@ -124,13 +124,38 @@ la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la
     return st;
 }
 
-void set_beta_and_fusion(la::Prob &p, const void *beta, const la_gdn_fusion *f)
+// The state series options ("Linear Attention" page, "States and checkpoints").
+la_status check_checkpoints(const la_gdn_options *f, bool summary)
+{
+    if (!f || f->checkpoint_every_n_tokens == 0) return LA_OK;
+    if (summary) return fail(LA_ERR_UNSUPPORTED, "the summary returns no state series (checkpoint_every_n_tokens)");
+    const int n = f->checkpoint_every_n_tokens;
+    if (n < 0) return fail(LA_ERR_INVALID_ARGUMENT, "checkpoint_every_n_tokens must be >= 0, got %d", n);
+    if (n % 64 != 0)
+        return fail(LA_ERR_UNSUPPORTED, "checkpoint_every_n_tokens must be a multiple of the 64-token chunk, got %d",
+                    n);
+    if (f->checkpoint_capacity < 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "checkpoint_capacity must be >= 0");
+    if (f->checkpoint_capacity > 0 && !f->checkpoints)
+        return fail(LA_ERR_INVALID_ARGUMENT, "checkpoints is NULL");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(f->checkpoints);
+    if ((a & (f->checkpoint_fp32 ? 3u : 1u)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "checkpoints is not %d-byte aligned", f->checkpoint_fp32 ? 4 : 2);
+    return LA_OK;
+}
+
+void set_beta_and_fusion(la::Prob &p, const void *beta, const la_gdn_options *f)
 {
     const bool logits = f && f->beta_sigmoid;
     p.beta = logits ? nullptr : static_cast<const float *>(beta);
     p.beta16 = logits ? static_cast<const __bf16 *>(beta) : nullptr;
     p.a_log = f ? f->a_log : nullptr;
     p.dt_bias = f ? f->dt_bias : nullptr;
+    const bool series = f && f->checkpoint_every_n_tokens > 0 && f->checkpoint_capacity > 0;
+    p.ck_every = series ? f->checkpoint_every_n_tokens : 0;
+    p.ck_fp32 = series && f->checkpoint_fp32 ? 1 : 0;
+    p.ck = series ? f->checkpoints : nullptr;
+    p.ck_cap = series ? f->checkpoint_capacity : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -315,13 +340,13 @@ la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, cons
                      const float *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
                      float *final_state, int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    return la_gdn_fwd_fused(desc, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, l2norm, nullptr,
+    return la_gdn_fwd_ex(desc, q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, l2norm, nullptr,
                             workspace, workspace_bytes, stream);
 }
 
-la_status la_gdn_fwd_fused(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
                            const void *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
-                           float *final_state, int l2norm, const la_gdn_fusion *fusion, void *workspace,
+                           float *final_state, int l2norm, const la_gdn_options *fusion, void *workspace,
                            size_t workspace_bytes, hipStream_t stream)
 {
     g_error.clear();
@@ -339,6 +364,7 @@ la_status la_gdn_fwd_fused(const la_gdn_desc *desc, const void *q, const void *k
     if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
     if ((st = check_f32("initial_state", initial_state, false)) != LA_OK) return st;
     if ((st = check_f32("final_state", final_state, false)) != LA_OK) return st;
+    if ((st = check_checkpoints(fusion, false)) != LA_OK) return st;
 
     la::Prob p = make_prob(desc, l2norm);
     p.q = static_cast<const __bf16 *>(q);
@@ -358,13 +384,13 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
                          const int32_t *cu_seqlens, const float *start_state, float *end_state, float *transition,
                          int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    return la_gdn_summary_fused(desc, k, v, g, beta, cu_seqlens, start_state, end_state, transition, l2norm, nullptr,
+    return la_gdn_summary_ex(desc, k, v, g, beta, cu_seqlens, start_state, end_state, transition, l2norm, nullptr,
                                 workspace, workspace_bytes, stream);
 }
 
-la_status la_gdn_summary_fused(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
+la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
                                const void *beta, const int32_t *cu_seqlens, const float *start_state,
-                               float *end_state, float *transition, int l2norm, const la_gdn_fusion *fusion,
+                               float *end_state, float *transition, int l2norm, const la_gdn_options *fusion,
                                void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     g_error.clear();
@@ -381,6 +407,7 @@ la_status la_gdn_summary_fused(const la_gdn_desc *desc, const void *k, const voi
     if ((st = check_f32("start_state", start_state, false)) != LA_OK) return st;
     if ((st = check_f32("end_state", end_state, true)) != LA_OK) return st;
     if ((st = check_f32("transition", transition, true)) != LA_OK) return st;
+    if ((st = check_checkpoints(fusion, true)) != LA_OK) return st;
 
     la::Prob p = make_prob(desc, l2norm);
     p.q = nullptr;

@@ -26,6 +26,10 @@ struct Prob {
     const float *g, *beta;            // beta: fp32, or null when beta16 is set
     const __bf16 *beta16;             // beta logits in bf16 (beta = sigmoid(logit) in the kernel), or null
     const float *a_log, *dt_bias;     // safe gate g = -exp(a_log[h]) softplus(g + dt_bias[h]), or null
+    int32_t ck_every;                 // state series every ck_every tokens (a multiple of 64), 0: none
+    int32_t ck_fp32;                  // series rows in fp32 (else bf16)
+    void *ck;                         // [ck_cap, HV, K, V] series, sequences in batch order
+    int64_t ck_cap;                   // entries the caller allocated
     const int32_t *cu;
     const float *s0;                  // initial / start state or null
     __bf16 *o;                        // forward output or null (summary)

@@ -980,7 +980,7 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
     }
 }
 
-template <int K, int V, bool SUMMARY>
+template <int K, int V, bool SUMMARY, bool CK = false>
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     using C = InterCfg<K, V, SUMMARY>;
@@ -1155,9 +1155,35 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     if (nch > 0) load_w(opA, 0);
     if (nch > 1) load_w(opB, 1);
     lds_barrier();
+    // State series (forward only): the state at the start of every chunk whose first
+    // token is a multiple of ck_every tokens into the sequence is entry ck_base + j of
+    // the series, j = that multiple; ck_base counts the entries of the sequences before
+    // this one (ceil(length / ck_every) each), summed across the wave.
+    int64_t ck_base = 0;
+    if (CK) {
+        int64_t part = 0;
+        for (int s = lane; s < n; s += 64) part += (p.cu[s + 1] - p.cu[s] + p.ck_every - 1) / p.ck_every;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+        ck_base = part;
+    }
     auto chunk_step = [&](int ci, StateOps &R) {
         const lds_u32x4 *eb = ebuf(ci);
         const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
+        if (CK && (kChunk * ci) % p.ck_every == 0) {
+            const int64_t e = ck_base + (int64_t)kChunk * ci / p.ck_every;
+            if (e < p.ck_cap) {
+                const int64_t base = ((e * p.HV + h) * K) * V;
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int ee = 0; ee < 16; ++ee) {
+                        const int64_t at = base + (int64_t)(row0 + 32 * r + 8 * (ee >> 2) + 4 * hh + (ee & 3)) * V + col;
+                        if (p.ck_fp32) static_cast<float *>(p.ck)[at] = S[r][ee];
+                        else static_cast<__bf16 *>(p.ck)[at] = f2bf(S[r][ee]);
+                    }
+            }
+        }
         // ---- K^T of this key half (A operands: state rows, tokens in accumulator order,
         // own token tile first), read from the raw k rows while the X products run
         bf16x8 Kf[NR][4];
@@ -1279,6 +1305,14 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     inter_body<K, V, false>(p, w);
 }
 
+// The forward with the state series (a kernel of its own, so that the plain
+// forward's chunk loop carries none of its stores).
+template <int K, int V>
+__global__ __launch_bounds__(384) void k_inter_ck(Prob p, Ws w)
+{
+    inter_body<K, V, false, true>(p, w);
+}
+
 template <int K, int V>
 __global__ __launch_bounds__(256) void k_inter_sum(Prob p, Ws w)
 {
@@ -1317,6 +1351,8 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
         const dim3 threads(InterCfg<K, V, SUMMARY>::THREADS);
         if (SUMMARY)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else if (p.ck_every > 0)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         after(LA_KERNEL_INTER);

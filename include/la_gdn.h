@@ -127,12 +127,14 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Options of the extended calls.
+ *
  * Gate and beta transforms fused into the kernels (the cudnn-frontend pull
  * request "Further reduce FROST LA CPU overhead + fully support all L2norm,
  * beta, gate fusion", commit notes on gated_delta_net: use_beta_sigmoid_in_kernel,
  * and safe_gate with a_log / dt_bias, computing -exp(a_log) * softplus(g + dt_bias)
  * with a zero dt_bias when none is given; beta arrives in the io dtype under the
- * in-kernel sigmoid, else in fp32).
+ * in-kernel sigmoid, else in fp32):
  *   beta_sigmoid  nonzero: `beta` is bf16 [T, HV] logits (stride beta_stride_t,
  *                 2-byte aligned) and the kernels use beta = 1 / (1 + exp(-logit));
  *                 zero: `beta` is fp32 [T, HV] as for la_gdn_fwd
@@ -140,31 +142,52 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
  *                 given, `g` is the raw gate and the kernels use, per token t and
  *                 value head h, g = -exp(a_log[h]) * log(1 + exp(g_raw[t][h] + dt_bias[h]))
  *   dt_bias       device, fp32 [HV], or NULL for zeros; only with a_log
- * The transforms run in fp32 in the prologue; everything after them is as
- * for la_gdn_fwd / la_gdn_summary.
+ * The transforms run in fp32 in the prologue; everything after them is as for
+ * la_gdn_fwd / la_gdn_summary.
+ *
+ * State series (forward only; the "Linear Attention" page, "States and
+ * checkpoints": checkpoint_every_n_tokens returns the state series, one entry
+ * every n tokens strictly before each sequence end, in the io dtype or, with
+ * checkpoint_dtype float32, in fp32):
+ *   checkpoint_every_n_tokens  n > 0, a multiple of 64 (the chunk; other values
+ *                 are declined with LA_ERR_UNSUPPORTED), or 0 for no series.  Entry
+ *                 j of a sequence is the state after its first j n tokens, for
+ *                 every j n < length (entry 0 is the initial state); a sequence of
+ *                 length L has ceil(L / n) entries, an empty one none
+ *   checkpoint_fp32   nonzero: fp32 rows; zero: bf16 rows (round to nearest even)
+ *   checkpoints       device, [checkpoint_capacity, HV, K, V] in that dtype, written:
+ *                 the entries of sequence 0, then of sequence 1, ...
+ *   checkpoint_capacity  entries allocated; entries at or beyond it are not
+ *                 written (pass sum over sequences of ceil(L / n))
  */
 typedef struct {
     int32_t beta_sigmoid;
     const float *a_log;
     const float *dt_bias;
-} la_gdn_fusion;
+    int32_t checkpoint_every_n_tokens;
+    int32_t checkpoint_fp32;
+    void *checkpoints;
+    int64_t checkpoint_capacity;
+} la_gdn_options;
 
 /*
- * la_gdn_fwd and la_gdn_summary with the transforms above (fusion NULL: the
+ * la_gdn_fwd and la_gdn_summary with the options above (options NULL: the
  * plain calls).  Arguments, errors and outputs are those of the plain calls;
- * `beta` is bf16 or fp32 as fusion->beta_sigmoid says.  A dt_bias without a_log,
- * or a misaligned a_log, dt_bias or beta, is LA_ERR_INVALID_ARGUMENT.
+ * `beta` is bf16 or fp32 as options->beta_sigmoid says.  A dt_bias without
+ * a_log, a misaligned a_log, dt_bias, beta or checkpoints, or a series without
+ * a buffer, is LA_ERR_INVALID_ARGUMENT; a series requested from the summary,
+ * or every n that is not a multiple of 64, is LA_ERR_UNSUPPORTED.
  */
-la_status la_gdn_fwd_fused(const la_gdn_desc *desc, const void *q, const void *k, const void *v,
-                           const float *g, const void *beta, const int32_t *cu_seqlens,
-                           const float *initial_state, void *out, float *final_state, int l2norm,
-                           const la_gdn_fusion *fusion, void *workspace, size_t workspace_bytes,
-                           hipStream_t stream);
-la_status la_gdn_summary_fused(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
-                               const void *beta, const int32_t *cu_seqlens, const float *start_state,
-                               float *end_state, float *transition, int l2norm,
-                               const la_gdn_fusion *fusion, void *workspace, size_t workspace_bytes,
-                               hipStream_t stream);
+la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, const void *v,
+                        const float *g, const void *beta, const int32_t *cu_seqlens,
+                        const float *initial_state, void *out, float *final_state, int l2norm,
+                        const la_gdn_options *options, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
+                            const void *beta, const int32_t *cu_seqlens, const float *start_state,
+                            float *end_state, float *transition, int l2norm,
+                            const la_gdn_options *options, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /*
  * Reads the status word the last call on this workspace left (LA_DEVICE_*

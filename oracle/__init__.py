@@ -55,6 +55,9 @@ class _Problem(ctypes.Structure):
         ("beta_logit", ctypes.c_void_p),
         ("a_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p),
+        ("checkpoint_every", ctypes.c_int32),
+        ("checkpoints", ctypes.c_void_p),
+        ("checkpoint_offset", ctypes.c_void_p),
     ]
 
 
@@ -144,8 +147,10 @@ class Oracle:
 
     def run_units(self, units: Sequence[Tuple[int, int]], want_o: bool = True,
                   want_state: bool = True, want_transition: bool = False,
-                  num_threads: Optional[int] = None) -> Dict[str, list]:
-        """Runs the listed (seq, v-head) units; returns per-unit fp64 arrays."""
+                  num_threads: Optional[int] = None, checkpoint_every: int = 0) -> Dict[str, list]:
+        """Runs the listed (seq, v-head) units; returns per-unit fp64 arrays
+        (with checkpoint_every = n > 0 also each unit's state series,
+        [ceil(len / n), K, V])."""
         lib = _load()
         units = list(units)
         nu = len(units)
@@ -164,6 +169,14 @@ class Oracle:
         st = np.empty((nu, self.K, self.V), dtype=np.float64) if want_state else None
         tr = np.empty((nu, self.K, self.K), dtype=np.float64) if want_transition else None
         nt = default_threads() if num_threads is None else num_threads
+        n_ck = -(-lens // checkpoint_every) if checkpoint_every > 0 else np.zeros(nu, dtype=np.int64)
+        ck_offs = np.zeros(nu, dtype=np.int64)
+        if nu:
+            ck_offs[1:] = np.cumsum(n_ck * self.K * self.V)[:-1]
+        ck = np.empty(max(1, int(n_ck.sum()) * self.K * self.V), dtype=np.float64)
+        self._st.checkpoint_every = int(checkpoint_every)
+        self._st.checkpoints = _ptr(ck) if checkpoint_every > 0 else None
+        self._st.checkpoint_offset = _ptr(ck_offs) if checkpoint_every > 0 else None
         rc = lib.gdn_oracle_run(ctypes.byref(self._st), nu, _ptr(seq), _ptr(head),
                                 _ptr(offs) if want_o else None, _ptr(o), _ptr(st), _ptr(tr), nt)
         if rc != 0:
@@ -176,16 +189,21 @@ class Oracle:
             out["state"] = [st[i] for i in range(nu)]
         if want_transition:
             out["transition"] = [tr[i] for i in range(nu)]
+        if checkpoint_every > 0:
+            out["checkpoints"] = [ck[ck_offs[i]:ck_offs[i] + n_ck[i] * self.K * self.V].reshape(
+                int(n_ck[i]), self.K, self.V) for i in range(nu)]
         return out
 
     def run_all(self, want_o: bool = True, want_state: bool = True,
-                want_transition: bool = False, num_threads: Optional[int] = None
-                ) -> Dict[str, np.ndarray]:
-        """Every unit, assembled: o [T, HV, V], state [N, HV, K, V], transition [N, HV, K, K]."""
+                want_transition: bool = False, num_threads: Optional[int] = None,
+                checkpoint_every: int = 0) -> Dict[str, np.ndarray]:
+        """Every unit, assembled: o [T, HV, V], state [N, HV, K, V], transition [N, HV, K, K],
+        and with checkpoint_every = n > 0 the state series [E, HV, K, V]: sequences in batch
+        order, ceil(len / n) entries each, entry j the state after j n tokens."""
         units = self.all_units()
         # longest sequences first so the dynamic schedule balances
         units.sort(key=lambda u: -(self.cu[u[0] + 1] - self.cu[u[0]]))
-        res = self.run_units(units, want_o, want_state, want_transition, num_threads)
+        res = self.run_units(units, want_o, want_state, want_transition, num_threads, checkpoint_every)
         out: Dict[str, np.ndarray] = {}
         T = int(self.cu[-1]) if self.N else 0
         if want_o:
@@ -203,6 +221,13 @@ class Oracle:
             for (n, h), arr in zip(units, res["transition"]):
                 t[n, h] = arr
             out["transition"] = t
+        if checkpoint_every > 0:
+            n_ck = [-(-l // checkpoint_every) for l in self.lengths()]
+            base = np.concatenate([[0], np.cumsum(n_ck)]).astype(np.int64)
+            c = np.zeros((int(base[-1]), self.HV, self.K, self.V), dtype=np.float64)
+            for (n, h), arr in zip(units, res["checkpoints"]):
+                c[base[n]:base[n + 1], h] = arr
+            out["checkpoints"] = c
         return out
 
 

@@ -42,6 +42,11 @@
  *     with beta logits given, beta_t = 1 / (1 + exp(-logit_t)); with a_log
  *     given, the gate is g_t = -exp(a_log[h]) * log(1 + exp(g_t + dt_bias[h]))
  *     in place of the natural-log gate.  Both in double precision.
+ *   - State series ("Linear Attention" page, "States and checkpoints":
+ *     checkpoint_every_n_tokens returns the state series, one entry every n
+ *     tokens strictly before each sequence end): entry j of a sequence is the
+ *     state after its first j n tokens, for every j n < length; entry 0 is the
+ *     initial state.
  *
  * Inputs are taken exactly: bf16 bit patterns are widened to double, fp32
  * values are widened to double.  Every sum is a plain left-to-right loop.
@@ -78,7 +83,7 @@ static void l2_normalise(double *x, int dim)
 
 /* One (sequence, v-head) unit.  Returns 0 on success, -1 on allocation failure. */
 static int run_unit(const gdn_oracle_problem *p, int32_t seq, int32_t head,
-                    double *o, double *state_out, double *transition_out)
+                    double *o, double *state_out, double *transition_out, double *checkpoints)
 {
     const int K = p->head_dim_k, V = p->head_dim_v;
     const int HK = p->num_qk_heads, HV = p->num_v_heads;
@@ -105,6 +110,9 @@ static int run_unit(const gdn_oracle_problem *p, int32_t seq, int32_t head,
         for (int i = 0; i < K; ++i) P[(int64_t)i * K + i] = 1.0;
 
     for (int64_t t = t0; t < t1; ++t) {
+        if (checkpoints && (t - t0) % p->checkpoint_every == 0)
+            memcpy(checkpoints + ((t - t0) / p->checkpoint_every) * (int64_t)K * V, S,
+                   sizeof(double) * (size_t)K * V);
         load_row(p->k, t, HK, hk, K, k);
         load_row(p->v, t, HV, head, V, v);
         if (p->l2norm) l2_normalise(k, K);
@@ -171,6 +179,8 @@ int gdn_oracle_run(const gdn_oracle_problem *p, int32_t n_units, const int32_t *
     if (p->num_qk_heads <= 0 || p->num_v_heads <= 0 || p->num_v_heads % p->num_qk_heads) return -2;
     if (p->head_dim_k <= 0 || p->head_dim_v <= 0 || !p->k || !p->v || !p->g || (!p->beta && !p->beta_logit)) return -2;
     if (p->dt_bias && !p->a_log) return -2;
+    if (p->checkpoint_every < 0 || (p->checkpoint_every > 0 && (!p->checkpoints || !p->checkpoint_offset)))
+        return -2;
     if (o && (!p->q || !o_offset)) return -2;
     for (int32_t u = 0; u < n_units; ++u) {
         if (unit_seq[u] < 0 || unit_seq[u] >= p->num_seqs) return -2;
@@ -185,7 +195,8 @@ int gdn_oracle_run(const gdn_oracle_problem *p, int32_t n_units, const int32_t *
         double *ou = o ? o + o_offset[u] : NULL;
         double *su = state_out ? state_out + u * kv : NULL;
         double *tu = transition_out ? transition_out + u * kk : NULL;
-        if (run_unit(p, unit_seq[u], unit_head[u], ou, su, tu) != 0) failed |= 1;
+        double *cu_ = p->checkpoint_every > 0 ? p->checkpoints + p->checkpoint_offset[u] : NULL;
+        if (run_unit(p, unit_seq[u], unit_head[u], ou, su, tu, cu_) != 0) failed |= 1;
     }
     return failed ? -1 : 0;
 }

@@ -33,6 +33,12 @@ typedef struct {
     const uint16_t *beta_logit;    /* bf16 bits [T, HV]: beta = 1 / (1 + exp(-logit)); replaces beta */
     const float *a_log;            /* [HV]: g = -exp(a_log) * softplus(g + dt_bias) */
     const float *dt_bias;          /* [HV] or NULL for zeros (with a_log only) */
+    /* state series: with checkpoint_every = n > 0, unit u writes the state after each
+       multiple j n of tokens strictly before its sequence end (j = 0 is the initial state)
+       to checkpoints + checkpoint_offset[u] + j K V */
+    int32_t checkpoint_every;
+    double *checkpoints;
+    const int64_t *checkpoint_offset;
 } gdn_oracle_problem;
 
 /*

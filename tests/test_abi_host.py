@@ -185,12 +185,12 @@ def test_fused_argument_checks(lib, fusion, beta, status, needle):
     dt_bias only comes with a_log."""
     a = _fwd_args()
     d = _desc()
-    f = la.Fusion(fusion["beta_sigmoid"], fusion["a_log"], fusion["dt_bias"])
-    rc = lib.la_gdn_fwd_fused(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
+    f = la.Options(fusion["beta_sigmoid"], fusion["a_log"], fusion["dt_bias"], 0, 0, None, 0)
+    rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
                               a["fin"], 1, ctypes.byref(f), a["ws"], a["wsb"], None)
     assert rc == status, la.la_last_error_message()
     assert needle in la.la_last_error_message()
-    rc = lib.la_gdn_summary_fused(ctypes.byref(d), a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
+    rc = lib.la_gdn_summary_ex(ctypes.byref(d), a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
                                   a["fin"], 1, ctypes.byref(f), a["ws"], a["wsb"], None)
     assert rc == status, la.la_last_error_message()
 
@@ -198,8 +198,37 @@ def test_fused_argument_checks(lib, fusion, beta, status, needle):
 def test_fused_binding_checks_beta_dtype():
     t = torch.zeros(4, 2)
     with pytest.raises(ValueError, match="bfloat16"):
-        la._fusion(t, True, None, None)
+        la._options(t, True, None, None)
     with pytest.raises(ValueError, match="float32"):
-        la._fusion(t.to(torch.bfloat16), False, None, None)
+        la._options(t.to(torch.bfloat16), False, None, None)
     with pytest.raises(ValueError, match="a_log"):
-        la._fusion(t, False, torch.zeros(2, dtype=torch.float64), None)
+        la._options(t, False, torch.zeros(2, dtype=torch.float64), None)
+
+
+@pytest.mark.parametrize("every,cap,ck,fp32,summary,status,needle", [
+    (96, 4, 1 << 20, 0, False, la.LA_ERR_UNSUPPORTED, "multiple of the 64-token chunk"),
+    (-64, 4, 1 << 20, 0, False, la.LA_ERR_INVALID_ARGUMENT, "checkpoint_every_n_tokens"),
+    (64, 4, None, 0, False, la.LA_ERR_INVALID_ARGUMENT, "checkpoints is NULL"),
+    (64, 4, (1 << 20) + 2, 1, False, la.LA_ERR_INVALID_ARGUMENT, "4-byte"),
+    (64, 4, (1 << 20) + 1, 0, False, la.LA_ERR_INVALID_ARGUMENT, "2-byte"),
+    (64, -1, 1 << 20, 0, False, la.LA_ERR_INVALID_ARGUMENT, "checkpoint_capacity"),
+    (64, 4, 1 << 20, 0, True, la.LA_ERR_UNSUPPORTED, "no state series"),
+])
+def test_checkpoint_argument_checks(lib, every, cap, ck, fp32, summary, status, needle):
+    a = _fwd_args()
+    d = _desc()
+    o = la.Options(0, None, None, every, fp32, ck, cap)
+    if summary:
+        rc = lib.la_gdn_summary_ex(ctypes.byref(d), a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["out"],
+                                   a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    else:
+        rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None,
+                               a["out"], a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    assert rc == status, la.la_last_error_message()
+    assert needle in la.la_last_error_message()
+
+
+def test_checkpoint_entries_count():
+    cu = torch.tensor([0, 1, 65, 65, 300], dtype=torch.int32)
+    assert la.checkpoint_entries(cu, 64) == 1 + 1 + 0 + 4
+    assert la.checkpoint_entries(cu, 128) == 1 + 1 + 0 + 2

@@ -1,5 +1,5 @@
 """GPU parity of the gate and beta transforms fused into the kernels
-(la_gdn_fwd_fused / la_gdn_summary_fused): beta as bf16 logits with the
+(la_gdn_fwd_ex / la_gdn_summary_ex): beta as bf16 logits with the
 sigmoid in the kernel, and the safe gate -exp(a_log) softplus(g + dt_bias),
 against the fp64 oracle, which applies the same transforms in double
 precision.  Tolerances as for the plain calls."""
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 def fwd_fused(p, **kw):
     g = p.to("cuda")
-    out, fin = la.la_gdn_fwd_fused(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+    out, fin, _ = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
                                    beta_sigmoid=p.beta_sigmoid, a_log=g.a_log, dt_bias=g.dt_bias, **kw)
     torch.cuda.synchronize()
     return out, fin
@@ -67,7 +67,7 @@ def test_fused_summary_slow_decay():
                       a_log_shift=-np.log(4096.0), beta_logit_shift=-4.0)
     g = p.to("cuda")
     note("fused summary slow decay")
-    end, tr = la.la_gdn_summary_fused(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state,
+    end, tr = la.la_gdn_summary_ex(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state,
                                       beta_sigmoid=True, a_log=g.a_log, dt_bias=g.dt_bias)
     torch.cuda.synchronize()
     ref = Oracle(p).run_all(want_o=False, want_transition=True)

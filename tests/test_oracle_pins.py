@@ -434,3 +434,42 @@ def test_beta_logits_at_large_magnitude():
     plain = _plain_from(p, p.g, torch.where(big > 0, torch.tensor(1.0), torch.tensor(0.0)))
     a, b = _run(p), _run(plain)
     assert np.isfinite(a["o"]).all() and rel_l2(a["o"], b["o"]) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# state series ("Linear Attention" page, "States and checkpoints": one entry every n
+# tokens strictly before each sequence end).  Pinned against the final state of the
+# same sequences cut after j n tokens, and against the initial state.
+
+@pytest.mark.parametrize("n_every", [64, 128, 3])
+def test_checkpoints_are_final_states_of_prefixes(n_every):
+    lengths = (1, 64, 65, 200, 0, 130)
+    p = custom_problem(lengths, hk=1, hv=2, dk=8, dv=8, seed=61, with_state=True)
+    r = Oracle(p).run_all(checkpoint_every=n_every)
+    ck = r["checkpoints"]
+    counts = [-(-L // n_every) for L in lengths]
+    assert ck.shape[0] == sum(counts)
+    cu = p.cu_seqlens.tolist()
+    base = 0
+    for s, L in enumerate(lengths):
+        for j in range(counts[s]):
+            m = j * n_every
+            if m == 0:
+                np.testing.assert_array_equal(ck[base], _np(p.state[s]))
+                continue
+            # the same sequence cut after m tokens, alone
+            a = cu[s]
+            cut = dataclasses.replace(
+                p, cu_seqlens=torch.tensor([0, m], dtype=torch.int32), q=p.q[a:a + m], k=p.k[a:a + m],
+                v=p.v[a:a + m], g=p.g[a:a + m], beta=p.beta[a:a + m], state=p.state[s:s + 1])
+            fin = Oracle(cut).run_all(want_o=False)["state"][0]
+            np.testing.assert_allclose(ck[base + j], fin, rtol=0, atol=1e-12)
+        base += counts[s]
+
+
+def test_checkpoints_leave_outputs_unchanged():
+    p = custom_problem((70, 130), hk=1, hv=2, dk=8, dv=8, seed=62, with_state=True)
+    a = Oracle(p).run_all()
+    b = Oracle(p).run_all(checkpoint_every=64)
+    np.testing.assert_array_equal(a["o"], b["o"])
+    np.testing.assert_array_equal(a["state"], b["state"])
