@@ -58,6 +58,7 @@ class _Problem(ctypes.Structure):
         ("checkpoint_every", ctypes.c_int32),
         ("checkpoints", ctypes.c_void_p),
         ("checkpoint_offset", ctypes.c_void_p),
+        ("num_householder", ctypes.c_int32),
     ]
 
 
@@ -134,10 +135,11 @@ class Oracle:
         self.V = int(p.v.shape[2])
         self.scale = float(self.K ** -0.5 if scale is None or scale <= 0 else scale)
         self.l2norm = bool(p.l2norm)
+        self.nh = int(getattr(p, "num_householder", 1) or 1)
         self._st = _Problem(self.N, self.HK, self.HV, self.K, self.V, int(self.l2norm), self.scale,
                             _ptr(self.cu), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.g),
                             _ptr(self.beta), _ptr(self.s0), _ptr(self.beta_logit), _ptr(self.a_log),
-                            _ptr(self.dt_bias))
+                            _ptr(self.dt_bias), 0, None, None, self.nh)
 
     def lengths(self) -> List[int]:
         return [int(self.cu[i + 1] - self.cu[i]) for i in range(self.N)]

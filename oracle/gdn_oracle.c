@@ -42,6 +42,12 @@
  *     with beta logits given, beta_t = 1 / (1 + exp(-logit_t)); with a_log
  *     given, the gate is g_t = -exp(a_log[h]) * log(1 + exp(g_t + dt_bias[h]))
  *     in place of the natural-log gate.  Both in double precision.
+ *   - Gated Delta Product (the "Linear Attention" page, its description of GDP:
+ *     q and g one row per token, k, v and beta n rows per token, update-major;
+ *     n = 1 is exactly GDN): per token, the decay exp(g_t) once, then the n
+ *     delta-rule updates of that token in order, each on the state the previous
+ *     one left, then the output from the state after all of them.  The span
+ *     transition is the product of the same steps.
  *   - State series ("Linear Attention" page, "States and checkpoints":
  *     checkpoint_every_n_tokens returns the state series, one entry every n
  *     tokens strictly before each sequence end): entry j of a sequence is the
@@ -109,13 +115,11 @@ static int run_unit(const gdn_oracle_problem *p, int32_t seq, int32_t head,
     if (want_transition)
         for (int i = 0; i < K; ++i) P[(int64_t)i * K + i] = 1.0;
 
+    const int nh = p->num_householder > 1 ? p->num_householder : 1;
     for (int64_t t = t0; t < t1; ++t) {
         if (checkpoints && (t - t0) % p->checkpoint_every == 0)
             memcpy(checkpoints + ((t - t0) / p->checkpoint_every) * (int64_t)K * V, S,
                    sizeof(double) * (size_t)K * V);
-        load_row(p->k, t, HK, hk, K, k);
-        load_row(p->v, t, HV, head, V, v);
-        if (p->l2norm) l2_normalise(k, K);
         double gt = (double)p->g[t * HV + head];
         if (p->a_log) {
             const double x = gt + (p->dt_bias ? (double)p->dt_bias[head] : 0.0);
@@ -123,20 +127,40 @@ static int run_unit(const gdn_oracle_problem *p, int32_t seq, int32_t head,
             gt = -exp((double)p->a_log[head]) * softplus;
         }
         const double a = exp(gt);
-        const double b = p->beta_logit ? 1.0 / (1.0 + exp(-bf16_bits_to_double(p->beta_logit[t * HV + head])))
-                                       : (double)p->beta[t * HV + head];
 
-        /* decay */
+        /* decay (state and, for the summary, the span operator) */
         for (int64_t i = 0; i < (int64_t)K * V; ++i) S[i] *= a;
-        /* u = v - S^T k  (S already decayed) */
-        for (int j = 0; j < V; ++j) {
-            double acc = 0.0;
-            for (int i = 0; i < K; ++i) acc += S[(int64_t)i * V + j] * k[i];
-            u[j] = v[j] - acc;
+        if (want_transition)
+            for (int64_t i = 0; i < (int64_t)K * K; ++i) P[i] *= a;
+
+        for (int r = 0; r < nh; ++r) {
+            const int64_t row = t * nh + r;   /* update row of k, v and beta */
+            load_row(p->k, row, HK, hk, K, k);
+            load_row(p->v, row, HV, head, V, v);
+            if (p->l2norm) l2_normalise(k, K);
+            const double b = p->beta_logit
+                                 ? 1.0 / (1.0 + exp(-bf16_bits_to_double(p->beta_logit[row * HV + head])))
+                                 : (double)p->beta[row * HV + head];
+            /* u = v - S^T k  (S already decayed) */
+            for (int j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i) acc += S[(int64_t)i * V + j] * k[i];
+                u[j] = v[j] - acc;
+            }
+            /* S += beta k u^T */
+            for (int i = 0; i < K; ++i)
+                for (int j = 0; j < V; ++j) S[(int64_t)i * V + j] += b * k[i] * u[j];
+            if (want_transition) {
+                /* P <- (I - beta k k^T) P */
+                for (int j = 0; j < K; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < K; ++i) acc += k[i] * P[(int64_t)i * K + j];
+                    u[j] = acc;
+                }
+                for (int i = 0; i < K; ++i)
+                    for (int j = 0; j < K; ++j) P[(int64_t)i * K + j] -= b * k[i] * u[j];
+            }
         }
-        /* S += beta k u^T */
-        for (int i = 0; i < K; ++i)
-            for (int j = 0; j < V; ++j) S[(int64_t)i * V + j] += b * k[i] * u[j];
 
         if (o) {
             load_row(p->q, t, HK, hk, K, q);
@@ -147,18 +171,6 @@ static int run_unit(const gdn_oracle_problem *p, int32_t seq, int32_t head,
                 for (int i = 0; i < K; ++i) acc += S[(int64_t)i * V + j] * q[i];
                 orow[j] = p->scale * acc;
             }
-        }
-
-        if (want_transition) {
-            /* P <- exp(g) (I - beta k k^T) P */
-            for (int64_t i = 0; i < (int64_t)K * K; ++i) P[i] *= a;
-            for (int j = 0; j < K; ++j) {
-                double acc = 0.0;
-                for (int i = 0; i < K; ++i) acc += k[i] * P[(int64_t)i * K + j];
-                u[j] = acc;
-            }
-            for (int i = 0; i < K; ++i)
-                for (int j = 0; j < K; ++j) P[(int64_t)i * K + j] -= b * k[i] * u[j];
         }
     }
 

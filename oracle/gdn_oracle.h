@@ -39,6 +39,10 @@ typedef struct {
     int32_t checkpoint_every;
     double *checkpoints;
     const int64_t *checkpoint_offset;
+    /* Gated Delta Product: n >= 1 Householder updates per token (0 or 1: the plain op).
+       k, v and beta (or beta_logit) then have n rows per token, update-major: the updates
+       of token t are rows t n .. t n + n - 1; q and g keep one row per token. */
+    int32_t num_householder;
 } gdn_oracle_problem;
 
 /*

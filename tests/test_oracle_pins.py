@@ -473,3 +473,45 @@ def test_checkpoints_leave_outputs_unchanged():
     b = Oracle(p).run_all(checkpoint_every=64)
     np.testing.assert_array_equal(a["o"], b["o"])
     np.testing.assert_array_equal(a["state"], b["state"])
+
+
+# ----------------------------------------------------------------------------
+# Gated Delta Product ("Linear Attention" page: n Householder updates per token,
+# k, v and beta update-major, n = 1 exactly GDN).  Pinned against the numpy closed
+# form run on the update sequence, with each token's gate at its first update and
+# its output read after its last.
+
+from workloads import gdp_problem  # noqa: E402
+
+
+def _expanded(p):
+    """The update sequence as a plain problem: gate at each token's first update, q at its last."""
+    nh = p.num_householder
+    T = p.total_tokens
+    g = torch.zeros(T * nh, p.g.shape[1])
+    g[::nh] = p.g
+    q = None
+    if p.q is not None:   # rows that are never read out hold copies (any value would do)
+        q = p.q.repeat_interleave(nh, dim=0)
+    return dataclasses.replace(p, cu_seqlens=p.cu_seqlens * nh, q=q, g=g, num_householder=1)
+
+
+@pytest.mark.parametrize("nh", [2, 3])
+def test_gdp_matches_closed_form_on_the_update_sequence(nh):
+    # without the L2 norm (the closed form normalises without the epsilon), like the GDN pins
+    p = dataclasses.replace(gdp_problem((3, 5), nh, hk=1, hv=2, dk=4, dv=4, seed=81, with_state=True),
+                            l2norm=False)
+    p = dataclasses.replace(p, k=(p.k.float() * 0.5).to(torch.bfloat16))   # a contractive recurrence
+    r = Oracle(p).run_all(want_transition=True)
+    ref_o, ref_s, ref_t = closed_form(_expanded(p))
+    np.testing.assert_allclose(r["o"], ref_o[nh - 1::nh], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["state"], ref_s, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["transition"], ref_t, rtol=1e-10, atol=1e-12)
+
+
+def test_gdp_with_one_update_is_gdn():
+    p = gdp_problem((7, 70), 1, hk=1, hv=2, dk=8, dv=8, seed=82, with_state=True)
+    q = custom_problem((7, 70), hk=1, hv=2, dk=8, dv=8, seed=82, with_state=True)
+    a, b = Oracle(p).run_all(), Oracle(q).run_all()
+    np.testing.assert_array_equal(a["o"], b["o"])
+    np.testing.assert_array_equal(a["state"], b["state"])

@@ -42,6 +42,8 @@ class Problem:
     beta_sigmoid: bool = False
     a_log: Optional[torch.Tensor] = None     # fp32 [HV]
     dt_bias: Optional[torch.Tensor] = None   # fp32 [HV] or None
+    # Gated Delta Product: k, v and beta have num_householder rows per token (update-major)
+    num_householder: int = 1
 
     @property
     def num_seqs(self) -> int:
@@ -49,7 +51,7 @@ class Problem:
 
     @property
     def total_tokens(self) -> int:
-        return int(self.k.shape[0])
+        return int(self.k.shape[0]) // self.num_householder
 
     @property
     def num_qk_heads(self) -> int:
@@ -211,3 +213,22 @@ def fused_problem(lengths, hk, hv, dk, dv, seed=0, with_state=False, summary=Fal
     return Problem(name=f"fused{tuple(lengths)}", cu_seqlens=cu.to(device), q=q, k=k, v=v, g=g, beta=beta,
                    state=state, l2norm=True, summary=summary, beta_sigmoid=beta_sigmoid, a_log=a_log,
                    dt_bias=dt_bias)
+
+
+def gdp_problem(lengths, nh, hk, hv, dk, dv, seed=0, with_state=False, summary=False, g_div=1.0,
+                beta_div=1.0, device="cpu") -> Problem:
+    """Gated Delta Product inputs: q and g one row per token, k, v and beta nh rows
+    per token (update-major: the updates of token t are rows t nh .. t nh + nh - 1).
+    Distributions as in custom_problem.  Draw order: the custom_problem draws over the
+    T nh update rows (q, g and the state drawn that way and q, g cut to the first T
+    rows), so nh = 1 gives custom_problem's tensors."""
+    T = int(sum(lengths))
+    gen = torch.Generator(device=device).manual_seed(seed)
+    rows = [L * nh for L in lengths]
+    cu_u, q, k, v, g, beta, state = _draw(gen, rows, hk, hv, dk, dv, with_state, not summary, device)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(list(lengths), dtype=torch.int64), 0).to(torch.int32)
+    return Problem(name=f"gdp{nh}{tuple(lengths)}", cu_seqlens=cu.to(device),
+                   q=None if q is None else q[:T].contiguous(), k=k, v=v, g=(g[:T] / g_div).contiguous(),
+                   beta=beta / beta_div, state=state, l2norm=True, summary=summary, num_householder=nh)
