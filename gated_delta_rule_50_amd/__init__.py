@@ -45,7 +45,7 @@ LA_KERNEL_COUNT = 3
 
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
-    "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex",
+    "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex", "la_gdn_workspace_bytes_ex",
     "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
@@ -83,6 +83,7 @@ class Options(ctypes.Structure):
         ("checkpoint_fp32", ctypes.c_int32),
         ("checkpoints", ctypes.c_void_p),
         ("checkpoint_capacity", ctypes.c_int64),
+        ("num_householder", ctypes.c_int32),
     ]
 
 
@@ -108,6 +109,8 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_summary.restype = ctypes.c_int
     lib.la_gdn_summary.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     op = ctypes.POINTER(Options)
+    lib.la_gdn_workspace_bytes_ex.restype = sz
+    lib.la_gdn_workspace_bytes_ex.argtypes = [dp, ctypes.c_int, op]
     lib.la_gdn_fwd_ex.restype = ctypes.c_int
     lib.la_gdn_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
     lib.la_gdn_summary_ex.restype = ctypes.c_int
@@ -147,15 +150,19 @@ def _stream(stream) -> Optional[int]:
 
 def make_desc(k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
               num_seqs: int, q: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              scale: Optional[float] = None) -> Desc:
-    """Descriptor from tensor shapes and strides (no data is read)."""
+              scale: Optional[float] = None, num_householder: int = 1) -> Desc:
+    """Descriptor from tensor shapes and strides (no data is read).  With
+    num_householder = n > 1, k, v and beta hold n update rows per token."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t is not None and (t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1)):
             raise ValueError(f"{name} must be rank 3 [T, heads, dim] with a contiguous innermost axis")
     for name, t in (("g", g), ("beta", beta)):
         if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
             raise ValueError(f"{name} must be rank 2 [T, HV] with a contiguous innermost axis")
-    T, HK, K = k.shape
+    TU, HK, K = k.shape
+    if TU % max(1, num_householder):
+        raise ValueError("k must hold num_householder update rows per token")
+    T = TU // max(1, num_householder)
     HV, V = v.shape[1], v.shape[2]
     qq = q if q is not None else k
     oo = out if out is not None else v
@@ -227,7 +234,15 @@ def _options(beta: torch.Tensor, beta_sigmoid: bool, a_log, dt_bias) -> Options:
     for name, t in (("a_log", a_log), ("dt_bias", dt_bias)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 [HV] tensor")
-    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0)
+    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0, 1)
+
+
+def la_gdn_workspace_bytes_ex(desc: Desc, is_summary: bool = False, num_householder: int = 1) -> int:
+    opts = Options(0, None, None, 0, 0, None, 0, int(num_householder))
+    n = load_library().la_gdn_workspace_bytes_ex(ctypes.byref(desc), int(bool(is_summary)), ctypes.byref(opts))
+    if n == 0:
+        raise LaError(LA_ERR_INVALID_ARGUMENT, la_last_error_message())
+    return int(n)
 
 
 def checkpoint_entries(cu_seqlens: torch.Tensor, every_n_tokens: int) -> int:
@@ -241,15 +256,17 @@ def la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, fi
                   beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
                   dt_bias: Optional[torch.Tensor] = None, checkpoint_every_n_tokens: int = 0,
                   checkpoint_dtype=torch.bfloat16, checkpoints: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  num_householder: int = 1, workspace: Optional[torch.Tensor] = None, stream=None):
     """Forward with the options of la_gdn_fwd_ex: beta is bf16 logits when beta_sigmoid,
     g is the raw gate when a_log is given, and checkpoint_every_n_tokens > 0 also returns
     the state series [E, HV, K, V] (checkpoint_dtype bf16 or fp32).  Returns
     (out, final_state, checkpoints or None)."""
     lib = load_library()
     opts = _options(beta, beta_sigmoid, a_log, dt_bias)
+    opts.num_householder = int(num_householder)
     N = cu_seqlens.numel() - 1
-    T, HV, V = v.shape
+    T = q.shape[0]
+    HV, V = v.shape[1], v.shape[2]
     K = k.shape[2]
     if out is None:
         out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
@@ -265,9 +282,10 @@ def la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, fi
         opts.checkpoint_fp32 = int(checkpoints.dtype == torch.float32)
         opts.checkpoints = _ptr(checkpoints)
         opts.checkpoint_capacity = int(checkpoints.shape[0])
-    desc = make_desc(k, v, g, beta, N, q=q, out=out, scale=scale)
+    desc = make_desc(k, v, g, beta, N, q=q, out=out, scale=scale, num_householder=num_householder)
     if workspace is None:
-        workspace = alloc_workspace(desc, False, v.device)
+        workspace = torch.empty(la_gdn_workspace_bytes_ex(desc, False, num_householder), dtype=torch.uint8,
+                                device=v.device)
     _check(lib.la_gdn_fwd_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
                              int(bool(l2norm)), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
@@ -277,11 +295,13 @@ def la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, fi
 
 def la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, transition=None,
                       l2norm: bool = True, beta_sigmoid: bool = False, a_log: Optional[torch.Tensor] = None,
-                      dt_bias: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Span summary with the gate / beta transforms fused into the kernels."""
+                      dt_bias: Optional[torch.Tensor] = None, num_householder: int = 1,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Span summary with the gate / beta transforms fused into the kernels (and, with
+    num_householder > 1, the Gated Delta Product's n update rows per token)."""
     lib = load_library()
     opts = _options(beta, beta_sigmoid, a_log, dt_bias)
+    opts.num_householder = int(num_householder)
     N = cu_seqlens.numel() - 1
     HV, V = v.shape[1], v.shape[2]
     K = k.shape[2]
@@ -289,9 +309,10 @@ def la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state=None, end_state=Non
         end_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
     if transition is None:
         transition = torch.empty((N, HV, K, K), dtype=torch.float32, device=v.device)
-    desc = make_desc(k, v, g, beta, N)
+    desc = make_desc(k, v, g, beta, N, num_householder=num_householder)
     if workspace is None:
-        workspace = alloc_workspace(desc, True, v.device)
+        workspace = torch.empty(la_gdn_workspace_bytes_ex(desc, True, num_householder), dtype=torch.uint8,
+                                device=v.device)
     _check(lib.la_gdn_summary_ex(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(cu_seqlens), _ptr(start_state), _ptr(end_state), _ptr(transition),
                                  int(bool(l2norm)), ctypes.byref(opts), _ptr(workspace), workspace.numel(),

@@ -124,6 +124,23 @@ la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la
     return st;
 }
 
+int householder(const la_gdn_options *f) { return f && f->num_householder > 1 ? f->num_householder : 1; }
+
+// Gated Delta Product: n update rows per token, within the int32 row range.
+la_status check_householder(const la_gdn_desc &d, const la_gdn_options *f)
+{
+    if (!f) return LA_OK;
+    if (f->num_householder < 0 || f->num_householder > 64)
+        return fail(LA_ERR_UNSUPPORTED, "num_householder must be in 0..64, got %d", f->num_householder);
+    const int64_t rows = d.total_tokens * householder(f);
+    if (rows > INT32_MAX - 64 || (rows + 63) / 64 + d.num_seqs > INT32_MAX / 2)
+        return fail(LA_ERR_UNSUPPORTED, "total_tokens * num_householder (%lld) exceeds the int32 row range",
+                    (long long)rows);
+    if (householder(f) > 1 && f->checkpoint_every_n_tokens != 0)
+        return fail(LA_ERR_UNSUPPORTED, "the state series is not available with num_householder > 1");
+    return LA_OK;
+}
+
 // The state series options ("Linear Attention" page, "States and checkpoints").
 la_status check_checkpoints(const la_gdn_options *f, bool summary)
 {
@@ -151,6 +168,8 @@ void set_beta_and_fusion(la::Prob &p, const void *beta, const la_gdn_options *f)
     p.beta16 = logits ? static_cast<const __bf16 *>(beta) : nullptr;
     p.a_log = f ? f->a_log : nullptr;
     p.dt_bias = f ? f->dt_bias : nullptr;
+    p.nh = householder(f);
+    p.max_chunks = (int32_t)((p.T * p.nh + 63) / 64 + p.N);
     const bool series = f && f->checkpoint_every_n_tokens > 0 && f->checkpoint_capacity > 0;
     p.ck_every = series ? f->checkpoint_every_n_tokens : 0;
     p.ck_fp32 = series && f->checkpoint_fp32 ? 1 : 0;
@@ -252,6 +271,7 @@ la::Prob make_prob(const la_gdn_desc *d, int l2norm)
     p.V = d->head_dim_v;
     p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim_k);
     p.l2norm = l2norm ? 1 : 0;
+    p.nh = 1;
     p.max_chunks = (int32_t)((d->total_tokens + 63) / 64 + d->num_seqs);
     p.intra_grid = 3 * device_cu_count();
     p.qst = d->q_stride_t;
@@ -269,7 +289,7 @@ la::Prob make_prob(const la_gdn_desc *d, int l2norm)
 
 la_status launch(const la::Prob &p, void *workspace, size_t workspace_bytes, bool summary, hipStream_t stream)
 {
-    const la::WsLayout L = la::workspace_layout(p.N, p.T, p.HK, p.HV, p.K, p.V, summary);
+    const la::WsLayout L = la::workspace_layout(p.N, p.T * p.nh, p.HK, p.HV, p.K, p.V, summary);
     if (p.N == 0) return LA_OK;  // nothing to compute and nothing to write
     if (!workspace) return fail(LA_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -336,6 +356,14 @@ size_t la_gdn_workspace_bytes(const la_gdn_desc *desc, int is_summary)
         .total;
 }
 
+size_t la_gdn_workspace_bytes_ex(const la_gdn_desc *desc, int is_summary, const la_gdn_options *options)
+{
+    if (check_desc(desc) != LA_OK || check_householder(*desc, options) != LA_OK) return 0;
+    return la::workspace_layout(desc->num_seqs, desc->total_tokens * householder(options), desc->num_qk_heads,
+                                desc->num_v_heads, desc->head_dim_k, desc->head_dim_v, is_summary != 0)
+        .total;
+}
+
 la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
                      const float *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
                      float *final_state, int l2norm, void *workspace, size_t workspace_bytes, hipStream_t stream)
@@ -354,9 +382,11 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     if (st != LA_OK) return st;
     const la_gdn_desc &d = *desc;
     const int64_t T = d.total_tokens;
+    if ((st = check_householder(d, fusion)) != LA_OK) return st;
+    const int64_t TU = T * householder(fusion);   // update rows of k, v and beta
     if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
-    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
-    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
+    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, TU)) != LA_OK) return st;
+    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, TU)) != LA_OK) return st;
     if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
@@ -398,8 +428,10 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
     if (st != LA_OK) return st;
     const la_gdn_desc &d = *desc;
     const int64_t T = d.total_tokens;
-    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
-    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
+    if ((st = check_householder(d, fusion)) != LA_OK) return st;
+    const int64_t TU = T * householder(fusion);   // update rows of k, v and beta
+    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, TU)) != LA_OK) return st;
+    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, TU)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
     if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");

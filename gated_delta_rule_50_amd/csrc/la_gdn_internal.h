@@ -19,13 +19,17 @@ struct Prob {
     int32_t HK, HV, K, V;
     float scale;
     int32_t l2norm;
-    int32_t max_chunks;               // upper bound on chunks: ceil(T / 64) + N
+    int32_t max_chunks;               // upper bound on chunks: ceil(T nh / 64) + N
     int32_t intra_grid;               // workgroups of the persistent intra-chunk kernel
     const __bf16 *q, *k, *v;
     int64_t qst, qsh, kst, ksh, vst, vsh, ost, osh, gst, bst;
     const float *g, *beta;            // beta: fp32, or null when beta16 is set
     const __bf16 *beta16;             // beta logits in bf16 (beta = sigmoid(logit) in the kernel), or null
     const float *a_log, *dt_bias;     // safe gate g = -exp(a_log[h]) softplus(g + dt_bias[h]), or null
+    int32_t nh;                       // Householder updates per token (Gated Delta Product; 1: GDN).
+                                      // T and cu_seqlens count tokens; k, v and beta have nh update
+                                      // rows per token (update-major), q, g and o one row per token;
+                                      // the kernels work in update rows, chunks of 64 updates
     int32_t ck_every;                 // state series every ck_every tokens (a multiple of 64), 0: none
     int32_t ck_fp32;                  // series rows in fp32 (else bf16)
     void *ck;                         // [ck_cap, HV, K, V] series, sequences in batch order

@@ -119,6 +119,8 @@ __device__ __forceinline__ SmallMap small_map(const Prob &p, const Ws &w, bool p
     }
     const bool anybad = __any(bad);
     if (anybad) start = end = 0;
+    start *= p.nh;   // update rows from here on (Gated Delta Product: nh per token)
+    end *= p.nh;
     const int len = end - start;
     const int nc = (len + kChunk - 1) / kChunk;
     int incl = nc;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(1024) void k_sched(Prob p, Ws w)
         if (i == N && (int64_t)c != p.T) bad = true;
         if (i < N && p.cu[i + 1] < c) bad = true;
         if (bad) atomicOr(&s_bad, 1);
-        if (small) s_start[i] = c;
+        if (small) s_start[i] = c * p.nh;   // update rows from here on
     }
     __syncthreads();
     const int bad = s_bad;
@@ -188,8 +190,8 @@ __global__ __launch_bounds__(1024) void k_sched(Prob p, Ws w)
         const int i = base + tid;
         int start = 0, len = 0, nc = 0;
         if (i < N && !bad) {
-            start = small ? s_start[i] : p.cu[i];
-            len = (small ? s_start[i + 1] : p.cu[i + 1]) - start;
+            start = small ? s_start[i] : p.cu[i] * p.nh;
+            len = (small ? s_start[i + 1] : p.cu[i + 1] * p.nh) - start;
             nc = (len + kChunk - 1) / kChunk;
         }
         s_scan[tid] = nc;
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(1024) void k_sched(Prob p, Ws w)
             const int mid = (lo + hi + 1) >> 1;
             if ((small ? s_first[mid] : w.seq_info[mid].z) <= c) lo = mid; else hi = mid - 1;
         }
-        const int st0 = small ? s_start[lo] : p.cu[lo];
-        const int len = (small ? s_start[lo + 1] : p.cu[lo + 1]) - st0;
+        const int st0 = small ? s_start[lo] : p.cu[lo] * p.nh;
+        const int len = (small ? s_start[lo + 1] : p.cu[lo + 1] * p.nh) - st0;
         const int j = c - (small ? s_first[lo] : w.seq_info[lo].z);
         const int st = st0 + kChunk * j;
         w.chunks[c] = make_int4(lo, st, min(kChunk, st0 + len - st), j);
@@ -463,6 +465,24 @@ __device__ __forceinline__ void intra_load_tile(lds_u32x4 *dst, const void *base
     }
 }
 
+// Gated Delta Product: the q tile of a chunk of update rows.  Update row start + s
+// reads q row (start + s) / nh when it is its token's last update, and zeros
+// otherwise (its offset is put past the buffer's range).  `base` points at token
+// tb = start / nh, `nrec` bytes of it are in range.
+template <int D>
+__device__ __forceinline__ void intra_load_qrows(lds_u32x4 *dst, const void *base, uint32_t rs, uint32_t nrec,
+                                                 int start, int len, int nh, int tb, int wave, int lane, int nw)
+{
+    constexpr int PPR = D / 8;
+    const i32x4 r = make_rsrc(base, nrec);
+    for (int i = wave; i < PPR; i += nw) {
+        const int s = 64 * i + lane, row = s / PPR, pp = s % PPR;
+        const int u = start + row;
+        const bool last = row < len && u % nh == nh - 1;
+        b2l(r, dst, i, last ? (uint32_t)(u / nh - tb) * rs + 16u * (uint32_t)(pp ^ (row % PPR)) : nrec, 0);
+    }
+}
+
 // 16-byte operand read from a swizzled bf16 tile: row `row`, columns c0 .. c0 + 7 (c0 % 8 == 0).
 template <int PPR>
 __device__ __forceinline__ bf16x8 lds_row8(const lds_u32x4 *tile, int row, int c0)
@@ -491,7 +511,7 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int K, int V, bool FWD>
+template <int K, int V, bool FWD, bool GDP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_intra(Prob p, Ws w)
 {
     constexpr int PK = K / 8, PV = V / 8;           // 16-byte pieces per k / v row
@@ -546,21 +566,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, n, 64) - start));
         } else {
             const int4 ch = w.chunks[ci];
-            start = ch.y;
-            len = ch.z;
+            start = __builtin_amdgcn_readfirstlane(ch.y);
+            len = __builtin_amdgcn_readfirstlane(ch.z);
         }
         const int64_t ch_h = (int64_t)ci * p.HV + h;
 
         // ---- 1: k, q, g, beta into LDS
         intra_load_tile<K>(sK, p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst, len, wave,
                            lane, 4);
-        if (FWD)
-            intra_load_tile<K>(sX, p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst, len,
-                               wave, lane, 4);
-        float blogit = 0.f;   // beta logit of token `lane` (beta16 only)
+        if (FWD) {
+            if (!GDP) {
+                intra_load_tile<K>(sX, p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
+                                   len, wave, lane, 4);
+            } else {
+                const int tb = __builtin_amdgcn_readfirstlane(start / p.nh);
+                intra_load_qrows<K>(sX, p.q + (int64_t)tb * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
+                                    (uint32_t)(p.T - tb) * 2u * (uint32_t)p.qst, start, len, p.nh, tb, wave, lane, 4);
+            }
+        }
+        float blogit = 0.f;   // beta logit of update row `lane` (beta16 only)
+        float graw = 0.f;     // Gated Delta Product: the gate of update row `lane`'s token at its first update
+        bool gfirst = true;   // update row `lane` is its token's first update (always, for GDN)
         if (wave == 3) {
-            const i32x4 rg = make_rsrc(p.g + (int64_t)start * p.gst + h, (uint32_t)len * 4u * (uint32_t)p.gst);
-            b2l_dword(rg, s_g, (uint32_t)lane * 4u * (uint32_t)p.gst);
+            if (!GDP) {
+                const i32x4 rg = make_rsrc(p.g + (int64_t)start * p.gst + h, (uint32_t)len * 4u * (uint32_t)p.gst);
+                b2l_dword(rg, s_g, (uint32_t)lane * 4u * (uint32_t)p.gst);
+            } else {
+                const int u = start + lane;
+                gfirst = u % p.nh == 0;
+                if (lane < len && gfirst) graw = p.g[(int64_t)(u / p.nh) * p.gst + h];
+            }
             if (p.beta16) {
                 if (lane < len) blogit = bf2f(p.beta16[(int64_t)(start + lane) * p.bst + h]);
             } else {
@@ -601,11 +636,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             // the gate and beta transforms fused into the prologue (the cudnn-frontend PR
             // "Further reduce FROST LA CPU overhead + fully support all L2norm, beta, gate
             // fusion", commit notes: safe_gate with a_log / dt_bias, use_beta_sigmoid_in_kernel)
-            float gr = s_g[lane];
+            float gr = GDP ? graw : s_g[lane];
             if (p.a_log) {
                 const float x = gr + (p.dt_bias ? p.dt_bias[h] : 0.f);
                 const float softplus = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-                gr = lane < len ? -expf(p.a_log[h]) * softplus : 0.f;
+                gr = (lane < len && gfirst) ? -expf(p.a_log[h]) * softplus : 0.f;
             }
             if (p.beta16) s_b[lane] = lane < len ? 1.f / (1.f + expf(-blogit)) : 0.f;
             // inclusive scan of g log2(e) (zeros past the end)
@@ -914,7 +949,7 @@ __device__ __forceinline__ int inter_issue_k(const Prob &p, lds_u32x4 *lb, int c
 
 // Loader wave lh, its half of chunk ci's output operands (raw q, P^T) and the
 // scalars (loader 0) into `eb`.  Returns the number of loads.
-template <int K, int V, bool SUMMARY>
+template <int K, int V, bool SUMMARY, bool GDP>
 __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
                                                   const InterCtx<K, V, SUMMARY> &x,
                                                   const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ])
@@ -925,10 +960,25 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
     int n = 0;
     if (C::FWD) {
         const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
-        const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)x.hk * p.qsh,
-                                   (uint32_t)len * 2u * (uint32_t)p.qst);
+        if (!GDP) {
+            const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)x.hk * p.qsh,
+                                       (uint32_t)len * 2u * (uint32_t)p.qst);
 #pragma unroll
-        for (int i = 0; i < C::FQ / 2; ++i) b2l(rQ, eb, C::oQ + 2 * i + lh, qoff[i], 0);
+            for (int i = 0; i < C::FQ / 2; ++i) b2l(rQ, eb, C::oQ + 2 * i + lh, qoff[i], 0);
+        } else {
+            // Gated Delta Product: update row start + row reads q row (start + row) / nh at its
+            // token's last update, zeros otherwise (offset past the buffer's range)
+            const int tb = __builtin_amdgcn_readfirstlane(start / p.nh);
+            const uint32_t rs = 2u * (uint32_t)p.qst, nrec = (uint32_t)(p.T - tb) * rs;
+            const i32x4 rQ = make_rsrc(p.q + (int64_t)tb * p.qst + (int64_t)x.hk * p.qsh, nrec);
+#pragma unroll
+            for (int i = 0; i < C::FQ / 2; ++i) {
+                const int s = (2 * i + lh) * 64 + x.lane, row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
+                const int u = start + row;
+                const bool last = row < len && u % p.nh == p.nh - 1;
+                b2l(rQ, eb, C::oQ + 2 * i + lh, last ? (uint32_t)(u / p.nh - tb) * rs + 16u * (uint32_t)pc : nrec, 0);
+            }
+        }
         const i32x4 rP = make_rsrc(reinterpret_cast<const char *>(w.PF) + chh * 6 * kFrag, 6 * kFrag);
 #pragma unroll
         for (int i = 0; i < 3; ++i) b2l(rP, eb, C::oP + 3 * lh + i, lo16, (3 * lh + i) * kFrag);
@@ -954,7 +1004,7 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
 
 // Output wave t: O^T of its token tile of the chunk whose Y^T it holds, stored
 // to o.  Lane (c, hh) holds value columns 8 j + 4 hh .. + 3 of token 32 t + c.
-template <int K, int V, bool SUMMARY>
+template <int K, int V, bool SUMMARY, bool GDP>
 __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU, const f32x16 &Y, const bf16x8 (&Pf)[4],
                                              float sq, int t, int o_start, int o_len, const InterCtx<K, V, SUMMARY> &x)
 {
@@ -969,8 +1019,15 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
         O = mfma32(__builtin_bit_cast(bf16x8, xU[3 * 64 + lane]), Pf[3], O);
     }
     const int tok = 32 * t + c;
+    // o row: the token itself, or (Gated Delta Product) the token whose last update it is
+    const int u = o_start + tok;
+    int orow = -1;
     if (tok < o_len) {
-        __bf16 *ob = p.o + (int64_t)(o_start + tok) * p.ost + (int64_t)x.h * p.osh + 32 * x.tile + 4 * hh;
+        if (!GDP) orow = u;
+        else if (u % p.nh == p.nh - 1) orow = u / p.nh;
+    }
+    if (orow >= 0) {
+        __bf16 *ob = p.o + (int64_t)orow * p.ost + (int64_t)x.h * p.osh + 32 * x.tile + 4 * hh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 o4 = {O[4 * j], O[4 * j + 1], O[4 * j + 2], O[4 * j + 3]};
@@ -980,7 +1037,7 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
     }
 }
 
-template <int K, int V, bool SUMMARY, bool CK = false>
+template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false>
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     using C = InterCfg<K, V, SUMMARY>;
@@ -1043,17 +1100,17 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         int na = 0, nb = 0;
         if (nch > 0) {
             na = inter_issue_k<K, V, SUMMARY>(p, l0, 0, lh, x, koff);
-            nb = inter_issue_output<K, V, SUMMARY>(p, w, e0, 0, lh, x, qoff);
+            nb = inter_issue_output<K, V, SUMMARY, GDP>(p, w, e0, 0, lh, x, qoff);
             if (nch > 1) {
                 inter_issue_k<K, V, SUMMARY>(p, l1, 1, lh, x, koff);
-                inter_issue_output<K, V, SUMMARY>(p, w, e1, 1, lh, x, qoff);
+                inter_issue_output<K, V, SUMMARY, GDP>(p, w, e1, 1, lh, x, qoff);
             }
             vm_wait_n(nch > 1 ? na + nb : 0);                 // all of chunk 0
         }
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const bool more2 = ci + 2 < nch;
-            if (more2) inter_issue_output<K, V, SUMMARY>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff);
+            if (more2) inter_issue_output<K, V, SUMMARY, GDP>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff);
             lds_barrier();                                    // B1
             if (more2) inter_issue_k<K, V, SUMMARY>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff);
             vm_wait_n(more2 ? na + nb : 0);                   // all of chunk ci + 1
@@ -1073,7 +1130,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         for (int ci = 0; ci < nch; ++ci) {
             const lds_u32x4 *eb = ebuf(ci);
             // the previous chunk's output (its U_new was published before the last B2)
-            if (ci > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+            if (ci > 0) inter_output<K, V, SUMMARY, GDP>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
             lds_barrier();                                    // B1: S of chunk ci is published
             // operands of chunk ci (they stay in their buffer until the next chunk
             // starts): q as B operands over all state rows (accumulator order within
@@ -1103,7 +1160,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             o_len = min(kChunk, x.seq_len - kChunk * ci);
             lds_barrier();                                    // B2: U_new of chunk ci is published
         }
-        if (nch > 0) inter_output<K, V, SUMMARY>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+        if (nch > 0) inter_output<K, V, SUMMARY, GDP>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
         return;
     }
 
@@ -1305,6 +1362,14 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
     inter_body<K, V, false>(p, w);
 }
 
+// The Gated Delta Product's forward: q rows and o rows mapped from update rows to
+// tokens (a kernel of its own, so that the plain forward carries none of it).
+template <int K, int V>
+__global__ __launch_bounds__(384) void k_inter_gdp(Prob p, Ws w)
+{
+    inter_body<K, V, false, false, true>(p, w);
+}
+
 // The forward with the state series (a kernel of its own, so that the plain
 // forward's chunk loop carries none of its stores).
 template <int K, int V>
@@ -1342,7 +1407,10 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
         const int64_t items = (int64_t)p.max_chunks * p.HV;
         const int grid = (int)(items < p.intra_grid ? items : p.intra_grid);
         before(LA_KERNEL_INTRA);
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<K, V, !SUMMARY>), dim3(grid), dim3(256), 0, s, p, w);
+        if (p.nh > 1)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<K, V, !SUMMARY, true>), dim3(grid), dim3(256), 0, s, p, w);
+        else
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<K, V, !SUMMARY, false>), dim3(grid), dim3(256), 0, s, p, w);
         after(LA_KERNEL_INTRA);
     }
     const int64_t blocks = (int64_t)p.N * p.HV * InterCfg<K, V, SUMMARY>::NT;
@@ -1351,6 +1419,8 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
         const dim3 threads(InterCfg<K, V, SUMMARY>::THREADS);
         if (SUMMARY)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else if (p.nh > 1)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_gdp<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else if (p.ck_every > 0)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else

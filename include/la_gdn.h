@@ -159,6 +159,18 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
  *                 the entries of sequence 0, then of sequence 1, ...
  *   checkpoint_capacity  entries allocated; entries at or beyond it are not
  *                 written (pass sum over sequences of ceil(L / n))
+ *
+ * Gated Delta Product (the "Linear Attention" page's description of GDP: q and g
+ * one row per token, k, v and beta n rows per token, update-major, and n = 1
+ * exactly GDN):
+ *   num_householder  n >= 1 (0 means 1).  desc->total_tokens and cu_seqlens count
+ *                 tokens; k, v and beta hold n update rows per token, the updates
+ *                 of token t being rows t n .. t n + n - 1 (k_stride_t, v_stride_t
+ *                 and beta_stride_t step one update row); q, g and out one row per
+ *                 token.  Per token the state is decayed once by exp(g_t), then the
+ *                 n delta-rule updates run in order, then o_t is read.  The
+ *                 workspace is sized by la_gdn_workspace_bytes_ex.  Not combined
+ *                 with the state series (LA_ERR_UNSUPPORTED).
  */
 typedef struct {
     int32_t beta_sigmoid;
@@ -168,7 +180,12 @@ typedef struct {
     int32_t checkpoint_fp32;
     void *checkpoints;
     int64_t checkpoint_capacity;
+    int32_t num_householder;
 } la_gdn_options;
+
+/* Workspace bytes for la_gdn_fwd_ex / la_gdn_summary_ex with these options (NULL:
+   as la_gdn_workspace_bytes); 0 for an invalid descriptor or options. */
+size_t la_gdn_workspace_bytes_ex(const la_gdn_desc *desc, int is_summary, const la_gdn_options *options);
 
 /*
  * la_gdn_fwd and la_gdn_summary with the options above (options NULL: the

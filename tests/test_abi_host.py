@@ -185,7 +185,7 @@ def test_fused_argument_checks(lib, fusion, beta, status, needle):
     dt_bias only comes with a_log."""
     a = _fwd_args()
     d = _desc()
-    f = la.Options(fusion["beta_sigmoid"], fusion["a_log"], fusion["dt_bias"], 0, 0, None, 0)
+    f = la.Options(fusion["beta_sigmoid"], fusion["a_log"], fusion["dt_bias"], 0, 0, None, 0, 1)
     rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], beta, a["cu"], None, a["out"],
                               a["fin"], 1, ctypes.byref(f), a["ws"], a["wsb"], None)
     assert rc == status, la.la_last_error_message()
@@ -217,7 +217,7 @@ def test_fused_binding_checks_beta_dtype():
 def test_checkpoint_argument_checks(lib, every, cap, ck, fp32, summary, status, needle):
     a = _fwd_args()
     d = _desc()
-    o = la.Options(0, None, None, every, fp32, ck, cap)
+    o = la.Options(0, None, None, every, fp32, ck, cap, 1)
     if summary:
         rc = lib.la_gdn_summary_ex(ctypes.byref(d), a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["out"],
                                    a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
@@ -232,3 +232,19 @@ def test_checkpoint_entries_count():
     cu = torch.tensor([0, 1, 65, 65, 300], dtype=torch.int32)
     assert la.checkpoint_entries(cu, 64) == 1 + 1 + 0 + 4
     assert la.checkpoint_entries(cu, 128) == 1 + 1 + 0 + 2
+
+
+def test_householder_options(lib):
+    """Gated Delta Product: the workspace grows with the update rows, n > 64 is declined,
+    and the state series is not combined with n > 1."""
+    d = _desc(T=1000)
+    one = la.la_gdn_workspace_bytes_ex(d, False, 1)
+    assert one == la.la_gdn_workspace_bytes(d, False)
+    assert la.la_gdn_workspace_bytes_ex(d, False, 3) > one
+    with pytest.raises(la.LaError, match="num_householder"):
+        la.la_gdn_workspace_bytes_ex(d, False, 65)
+    a = _fwd_args()
+    o = la.Options(0, None, None, 64, 0, 1 << 20, 4, 2)
+    rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["out"],
+                           a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    assert rc == la.LA_ERR_UNSUPPORTED and "num_householder" in la.la_last_error_message()

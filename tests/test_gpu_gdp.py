@@ -1,0 +1,66 @@
+"""GPU parity of the Gated Delta Product (la_gdn_fwd_ex / la_gdn_summary_ex with
+num_householder = n: k, v and beta n update rows per token, update-major; q, g
+and o one row per token) against the fp64 oracle's token recurrence with n
+updates per token.  Tolerances as for GDN."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_50_amd as la
+from oracle import Oracle, rel_l2
+from workloads import gdp_problem
+
+from gpu_helpers import TOL_O, TOL_STATE, f64, gpu_fwd, note
+
+pytestmark = pytest.mark.gpu
+
+
+def gdp_fwd(p):
+    g = p.to("cuda")
+    out, fin, _ = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                   num_householder=p.num_householder)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def check(p):
+    note(f"gdp fwd: {p.name} n={p.num_householder}")
+    out, fin = gdp_fwd(p)
+    ref = Oracle(p).run_all()
+    eo, es = rel_l2(f64(out), ref["o"]), rel_l2(f64(fin), ref["state"])
+    assert eo <= TOL_O and es <= TOL_STATE, (eo, es)
+    return out, fin
+
+
+@pytest.mark.parametrize("nh", [2, 3])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128)])
+def test_gdp_ragged(nh, dk, dv):
+    # lengths in tokens: chunks of 64 update rows then start inside a token for n = 3
+    check(gdp_problem((1, 21, 32, 33, 100, 150), nh, hk=2, hv=4, dk=dk, dv=dv, seed=91, with_state=True))
+
+
+def test_gdp_larger():
+    check(gdp_problem((700, 1300), 2, hk=4, hv=8, dk=128, dv=128, seed=92, with_state=True))
+
+
+def test_gdp_one_update_is_the_plain_call_bitwise():
+    p = gdp_problem((100, 257), 1, hk=2, hv=4, dk=128, dv=128, seed=93, with_state=True)
+    note("gdp n=1 vs plain")
+    o1, f1 = gdp_fwd(p)
+    o2, f2 = gpu_fwd(p)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_gdp_summary_slow_decay():
+    p = gdp_problem((1, 40, 100, 150), 2, hk=2, hv=2, dk=128, dv=128, seed=94, with_state=True, summary=True,
+                    g_div=4096.0, beta_div=64.0)
+    g = p.to("cuda")
+    note("gdp summary n=2")
+    end, tr = la.la_gdn_summary_ex(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state, num_householder=2)
+    torch.cuda.synchronize()
+    ref = Oracle(p).run_all(want_o=False, want_transition=True)
+    assert rel_l2(f64(end), ref["state"]) <= TOL_STATE
+    assert rel_l2(f64(tr), ref["transition"]) <= TOL_STATE
+    assert np.abs(ref["transition"]).max() > 0.05
