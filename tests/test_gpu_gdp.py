@@ -64,3 +64,22 @@ def test_gdp_summary_slow_decay():
     assert rel_l2(f64(end), ref["state"]) <= TOL_STATE
     assert rel_l2(f64(tr), ref["transition"]) <= TOL_STATE
     assert np.abs(ref["transition"]).max() > 0.05
+
+
+def test_gdp_with_fused_gate_and_beta():
+    # raw gate per token, bf16 beta logits per update row, safe-gate parameters per value head
+    p = gdp_problem((1, 30, 50, 130), 2, hk=2, hv=4, dk=128, dv=128, seed=95, with_state=True)
+    gen = torch.Generator().manual_seed(96)
+    g_raw = torch.randn(p.g.shape, generator=gen)
+    logits = torch.randn(p.beta.shape, generator=gen).to(torch.bfloat16)
+    a_log = torch.log(1.0 + 15.0 * torch.rand(4, generator=gen))
+    dt = torch.exp(np.log(1e-3) + (np.log(1e-1) - np.log(1e-3)) * torch.rand(4, generator=gen))
+    dt_bias = dt + torch.log(-torch.expm1(-dt))
+    p = dataclasses.replace(p, g=g_raw, beta=logits, beta_sigmoid=True, a_log=a_log, dt_bias=dt_bias)
+    g = p.to("cuda")
+    note("gdp n=2 with fused gate and beta")
+    out, fin, _ = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                   num_householder=2, beta_sigmoid=True, a_log=g.a_log, dt_bias=g.dt_bias)
+    torch.cuda.synchronize()
+    ref = Oracle(p).run_all()
+    assert rel_l2(f64(out), ref["o"]) <= TOL_O and rel_l2(f64(fin), ref["state"]) <= TOL_STATE
