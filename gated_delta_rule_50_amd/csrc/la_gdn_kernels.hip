@@ -20,19 +20,24 @@
 // the chunked result equals the token-by-token one up to rounding.  Every
 // exponent above is <= 0, so no factor can overflow.
 //
-// Three kernels, all on the caller's stream:
+// The kernels, all on the caller's stream:
 //   k_sched     one workgroup, for more than 64 sequences: validates cu_seqlens,
 //               builds the chunk table and the longest-first order of sequences
 //               (for at most 64, every wave of k_intra maps its own chunks from
 //               cu_seqlens and one wave writes the tables)
-//   k_intra     per (chunk, value head): the prologue (row norms r_k and the
-//               chunk-local gate cumsum), A on MFMA, T by forward substitution in
-//               LDS, W and U~ on MFMA; writes -W and U~ in MFMA fragment order and
-//               the per-token scalars
+//   k_intra     per (chunk, value head): the prologue (row norms r_q, r_k, the
+//               chunk-local gate cumsum, and optionally the fused beta sigmoid and
+//               safe gate), A and P^T on MFMA, T by forward substitution in LDS, W
+//               and U~ on MFMA; writes -W, U~ and P^T in MFMA fragment order and the
+//               per-token scalars
 //   k_inter     per (sequence, value head, 32 value columns): the sequential chunk
 //               loop, split over state, output and loader waves; S stays in
-//               registers as MFMA accumulator tiles; r_q and P are formed here,
-//               from the raw q and k rows
+//               registers as MFMA accumulator tiles.  Compile-time variants of the
+//               same body: k_inter_sum (span summary: no output waves, the state
+//               widened by the transition columns), k_inter_ck (with the state
+//               series) and k_inter_gdp (Gated Delta Product: q and o rows mapped
+//               from update rows to tokens); k_intra has a Gated Delta Product
+//               variant in the same way
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 for the bf16 products and v_mfma_f32_16x16x4_f32
 // for the fp32 block products of the triangular solve (lane layouts with the

@@ -226,7 +226,8 @@ const char *la_last_error_message(void);
                                kernel only for more than 64 sequences; otherwise k_intra does
                                it and this id counts no launches) */
 #define LA_KERNEL_INTRA 1   /* prologue (q/k norms, gate cumsum) + intra-chunk UT/WY */
-#define LA_KERNEL_INTER 2   /* sequential inter-chunk state and output pass */
+#define LA_KERNEL_INTER 2   /* sequential inter-chunk state and output pass (any of its variants:
+                               forward, summary, with the state series, Gated Delta Product) */
 #define LA_KERNEL_COUNT 3
 la_status la_gdn_profile_enable(int enable);
 la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *launches);
