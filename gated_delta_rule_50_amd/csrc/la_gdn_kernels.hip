@@ -1084,6 +1084,22 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     const int lane = x.lane, c = lane & 31, hh = lane >> 5;
     const int nch = x.nch;
 
+    // State series (forward only): the state at the start of every chunk whose first
+    // token is a multiple of ck_every tokens into the sequence is entry ck_base + j of
+    // the series, j = that multiple; ck_base counts the entries of the sequences before
+    // this one (ceil(length / ck_every) each), summed across the wave.  bf16 rows are
+    // written by the output waves from the bf16 copy of S they read anyway (off the
+    // state waves' chain, whose next loop-head wait would otherwise cover the stores);
+    // fp32 rows by the state waves.
+    int64_t ck_base = 0;
+    if (CK && wave < C::LW) {
+        int64_t part = 0;
+        for (int s = lane; s < n; s += 64) part += (p.cu[s + 1] - p.cu[s] + p.ck_every - 1) / p.ck_every;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+        ck_base = part;
+    }
+
     if (wave >= C::LW) {
         // ------------------------------------------------------------ loader waves
         const int lh = wave - C::LW;
@@ -1161,6 +1177,23 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 #pragma unroll
             for (int kk = 0; kk < 2 * NKS; ++kk)
                 Y = mfma32(__builtin_bit_cast(bf16x8, xS[kk * 64 + lane]), Qf[kk], Y);
+            if (CK && !p.ck_fp32 && (kChunk * ci) % p.ck_every == 0) {
+                // the chunk-start state as bf16 rows: output wave t writes key steps
+                // t NKS .. t NKS + NKS - 1; lane (c, hh) of step kk holds column c, keys
+                // 16 kk + 4 hh + e (slots e) and 16 kk + 8 + 4 hh + e (slots 4 + e)
+                const int64_t e = ck_base + (int64_t)kChunk * ci / p.ck_every;
+                if (e < p.ck_cap) {
+                    __bf16 *dst = static_cast<__bf16 *>(p.ck) + ((e * p.HV + x.h) * K) * V + 32 * x.tile + c;
+#pragma unroll
+                    for (int i = 0; i < NKS; ++i) {
+                        const int kk = t * NKS + i;
+                        const bf16x8 sv = __builtin_bit_cast(bf16x8, xS[kk * 64 + lane]);
+#pragma unroll
+                        for (int slot = 0; slot < 8; ++slot)
+                            dst[(int64_t)(16 * kk + 8 * (slot >> 2) + 4 * hh + (slot & 3)) * V] = sv[slot];
+                    }
+                }
+            }
             o_start = x.seq_start + kChunk * ci;
             o_len = min(kChunk, x.seq_len - kChunk * ci);
             lds_barrier();                                    // B2: U_new of chunk ci is published
@@ -1217,22 +1250,10 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     if (nch > 0) load_w(opA, 0);
     if (nch > 1) load_w(opB, 1);
     lds_barrier();
-    // State series (forward only): the state at the start of every chunk whose first
-    // token is a multiple of ck_every tokens into the sequence is entry ck_base + j of
-    // the series, j = that multiple; ck_base counts the entries of the sequences before
-    // this one (ceil(length / ck_every) each), summed across the wave.
-    int64_t ck_base = 0;
-    if (CK) {
-        int64_t part = 0;
-        for (int s = lane; s < n; s += 64) part += (p.cu[s + 1] - p.cu[s] + p.ck_every - 1) / p.ck_every;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-        ck_base = part;
-    }
     auto chunk_step = [&](int ci, StateOps &R) {
         const lds_u32x4 *eb = ebuf(ci);
         const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
-        if (CK && (kChunk * ci) % p.ck_every == 0) {
+        if (CK && p.ck_fp32 && (kChunk * ci) % p.ck_every == 0) {
             const int64_t e = ck_base + (int64_t)kChunk * ci / p.ck_every;
             if (e < p.ck_cap) {
                 const int64_t base = ((e * p.HV + h) * K) * V;
@@ -1241,8 +1262,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 #pragma unroll
                     for (int ee = 0; ee < 16; ++ee) {
                         const int64_t at = base + (int64_t)(row0 + 32 * r + 8 * (ee >> 2) + 4 * hh + (ee & 3)) * V + col;
-                        if (p.ck_fp32) static_cast<float *>(p.ck)[at] = S[r][ee];
-                        else static_cast<__bf16 *>(p.ck)[at] = f2bf(S[r][ee]);
+                        static_cast<float *>(p.ck)[at] = S[r][ee];
                     }
             }
         }
