@@ -575,6 +575,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             len = __builtin_amdgcn_readfirstlane(ch.z);
         }
         const int64_t ch_h = (int64_t)ci * p.HV + h;
+        // The lane index for the lane masks of this item (the scan, the diagonal of G and
+        // the causal masks of A, P^T and T) goes through an empty asm, so that the compiler
+        // forms those masks where they are used instead of hoisting all of them out of the
+        // item loop, where they do not fit in the scalar registers and are spilled.
+        int lm = lane;
+        asm volatile("" : "+v"(lm));
+        const int cm = lm & 31, hm = lm >> 5;
 
         // ---- 1: k, q, g, beta into LDS
         intra_load_tile<K>(sK, p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst, len, wave,
@@ -653,7 +660,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(xg, off, 64);
-                if (lane >= off) xg += y;
+                if (lm >= off) xg += y;
             }
             s_gam[lane] = xg;
         }
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             float dg = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                if (8 * (e >> 2) + 4 * hh + (e & 3) == c) dg = Gt[e];
+                if (8 * (e >> 2) + 4 * hm + (e & 3) == cm) dg = Gt[e];
             const int row = 32 * gm + c;
             if (((c >> 2) & 1) == hh) s_rk[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(dg + 1e-6f) : 1.0f) : 0.f;
         }
@@ -696,7 +703,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 f32x4 a;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = exp2_hw(s < t0 + i ? gt[i] - gs : kNegInf);
+                    const float e = exp2_hw(32 * gn + cm < 32 * gm + 8 * j + 4 * hm + i ? gt[i] - gs : kNegInf);
                     a[i] = bt[i] * rt[i] * rs * e * Gt[4 * j + i];
                 }
                 *reinterpret_cast<lds_f32x4 *>(sAT + s * TS + t0) = a;
@@ -715,7 +722,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const f32x4 rs = *reinterpret_cast<const lds_f32x4 *>(s_rk + s0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = exp2_hw(s0 + i <= t ? gt - gs[i] : kNegInf);
+                    const float e = exp2_hw(32 * pm + 8 * j + 4 * hm + i <= 32 * pn + cm ? gt - gs[i] : kNegInf);
                     pv[4 * j + i] = rq * rs[i] * e * Pt[4 * j + i];
                 }
             }
@@ -732,7 +739,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const int b = lane >> 4, cc = lane & 15, o = 16 * b;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i == (lm & 15)) ? 1.f : 0.f;
 #pragma unroll
             for (int k = 0; k < 15; ++k) {
                 // A[o + i][o + k] for i > k is A^T[o + k][o + i]: the row in four 16-byte
@@ -796,6 +803,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // the diagonal (the array holds A^T there).
         {
             const int m = wave & 1, t = 32 * m + c;
+            const int tm = 32 * m + cm - 8 * hm;   // the mask below: column 16 s + e <= row t
             // T[t][16 s + 8 hh + e] (zero above the diagonal), times the per-column factor f
             auto trow = [&](int s, const lds_float *f, float (&o)[8]) {
                 const int s0 = 16 * s + 8 * hh;
@@ -805,7 +813,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const f32x4 f1 = *reinterpret_cast<const lds_f32x4 *>(f + s0 + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    o[e] = (s0 + e <= t) ? (e < 4 ? t0[e] * f0[e] : t1[e - 4] * f1[e - 4]) : 0.f;
+                    o[e] = (16 * s + e <= tm) ? (e < 4 ? t0[e] * f0[e] : t1[e - 4] * f1[e - 4]) : 0.f;
             };
             {
                 bf16x8 tw[4];
