@@ -43,9 +43,19 @@ WORKLOADS = {
     5: "GDN span summary, 32 spans x 8192 tokens, H=16, K=V=128, in-kernel k L2 norm, start state, "
        "end state + transition",
 }
+# options of the forward (la_gdn_fwd_ex), timed on a forward workload's shape
+VARIANTS = {
+    "plain": "",
+    "fused": "beta as bf16 logits with the sigmoid in the kernel, and the safe gate "
+             "-exp(a_log) softplus(g + dt_bias) from the raw gate",
+    "series64": "with the state series every 64 tokens (bf16 rows)",
+    "series64-fp32": "with the state series every 64 tokens (fp32 rows)",
+    "gdp2": "Gated Delta Product, 2 Householder updates per token (k, v, beta update-major)",
+}
 
 
-def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final):
+def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final, nh=1, beta_bytes=4,
+                       series_bytes=0):
     """Bytes and flops the method must move and compute (intermediates excluded).
 
     Forward bytes: q, k (bf16, per qk-head), v, o (bf16, per v-head), g, beta
@@ -57,7 +67,13 @@ def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final):
     Span summary: no q and no o; bytes add the start, end and transition states;
     flops are the k k^T Gram product, W, U~, W S and the state update for the
     widened state [S | P] (K x (V + K)): also 180,224 per token-head at
-    K = V = 128."""
+    K = V = 128.
+
+    Forward options: beta_bytes = 2 for bf16 beta logits; series_bytes = the
+    state series written; nh > 1 (Gated Delta Product) reads nh rows of k, v and
+    beta per token, and its flops are those of the chunked method over the T nh
+    update rows (the q rows of a token's other updates are zeros, and the masked
+    tiles are counted whole as above)."""
     T = sum(lengths)
     N = len(lengths)
     C = CHUNK
@@ -66,8 +82,9 @@ def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final):
         VA = V + K
         fl = T * (HK * 2 * C * K + HV * 2 * (C * (K + V) + 2 * K * VA))
     else:
-        by = T * (2 * HK * K * 2 + 2 * HV * V * 2 + 2 * HV * 4) + N * HV * K * V * 4 * (int(with_init) + int(with_final))
-        fl = T * (HK * 2 * 2 * C * K + HV * 2 * (3 * K * V + C * (K + 2 * V)))
+        by = (T * (HK * K * 2 * (1 + nh) + HV * V * 2 * (nh + 1) + HV * (4 + beta_bytes * nh))
+              + N * HV * K * V * 4 * (int(with_init) + int(with_final)) + series_bytes)
+        fl = T * nh * (HK * 2 * 2 * C * K + HV * 2 * (3 * K * V + C * (K + 2 * V)))
     return by, fl
 
 
@@ -118,6 +135,9 @@ def main(argv=None):
                     help="the workload timed: 2 (default) is the bench line; 1, 3, 4 (forward) and 5 (span "
                          "summary) report the same fields for the other configurations, with inputs drawn on "
                          "the device and no CPU baseline")
+    ap.add_argument("--variant", default="plain", choices=sorted(VARIANTS),
+                    help="forward options timed on the workload's shape (forward workloads only): "
+                         + "; ".join(f"{k}: {v}" for k, v in VARIANTS.items() if v))
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -130,7 +150,7 @@ def main(argv=None):
 
     import torch
     import gated_delta_rule_50_amd as la
-    from workloads import make_problem
+    from workloads import fused_problem, gdp_problem, make_problem
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -140,20 +160,38 @@ def main(argv=None):
     la.load_library()
 
     wl = args.workload
+    variant = args.variant
     prob = make_problem(wl) if wl == 2 else make_problem(wl, device="cuda")
     summary = prob.summary
+    if variant != "plain" and summary:
+        print("--variant applies to the forward workloads (1 to 4)", file=sys.stderr)
+        return 2
     lengths = prob.lengths()
     T, HK, HV, K, V = prob.total_tokens, prob.num_qk_heads, prob.num_v_heads, prob.head_dim_k, prob.head_dim_v
     N = prob.num_seqs
+    # the variants draw their own inputs of the same shape (seeded by the workload number)
+    gen_dev = "cpu" if wl == 2 else "cuda"
+    with_init = prob.state is not None
+    if variant == "fused":
+        prob = fused_problem(lengths, HK, HV, K, V, seed=wl, with_state=with_init, device=gen_dev)
+    elif variant == "gdp2":
+        prob = gdp_problem(lengths, 2, HK, HV, K, V, seed=wl, with_state=with_init, device=gen_dev)
+    nh = 2 if variant == "gdp2" else 1
+    every = 64 if variant.startswith("series64") else 0
+    ck_dtype = torch.float32 if variant == "series64-fp32" else torch.bfloat16
+    n_ck = la.checkpoint_entries(prob.cu_seqlens, every) if every else 0
+    count_kw = {"nh": nh, "beta_bytes": 2 if variant == "fused" else 4,
+                "series_bytes": n_ck * HV * K * V * (4 if ck_dtype == torch.float32 else 2)}
 
     # one copy is enough once a copy alone is larger than the Infinity Cache
-    by0, _ = algorithmic_counts(lengths, HK, HV, K, V, summary, prob.state is not None, True)
+    by0, _ = algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, True, **count_kw)
 
     def fresh_copy(pr):
         def cl(x):
             return None if x is None else x.to(dev).clone()
         return dataclasses.replace(pr, cu_seqlens=cl(pr.cu_seqlens), q=cl(pr.q), k=cl(pr.k), v=cl(pr.v),
-                                   g=cl(pr.g), beta=cl(pr.beta), state=cl(pr.state))
+                                   g=cl(pr.g), beta=cl(pr.beta), state=cl(pr.state), a_log=cl(pr.a_log),
+                                   dt_bias=cl(pr.dt_bias))
 
     copies = max(1, args.copies) if by0 < (1 << 30) else 1
     sets = []
@@ -164,20 +202,26 @@ def main(argv=None):
             desc = la.make_desc(g.k, g.v, g.g, g.beta, N)
         else:
             out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=dev)
-            desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out)
+            desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out, num_householder=nh)
         fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
-        ws = la.alloc_workspace(desc, summary, dev)
-        sets.append((g, out, fin, ws))
+        ws = torch.empty(la.la_gdn_workspace_bytes_ex(desc, summary, nh), dtype=torch.uint8, device=dev)
+        ck = torch.empty((n_ck, HV, K, V), dtype=ck_dtype, device=dev) if every else None
+        sets.append((g, out, fin, ws, ck))
     stream = torch.cuda.current_stream()
 
     def step(i):
-        g, out, fin, ws = sets[i % len(sets)]
+        g, out, fin, ws, ck = sets[i % len(sets)]
         if summary:
             la.la_gdn_summary(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state, end_state=fin,
                               transition=out, l2norm=True, workspace=ws, stream=stream)
-        else:
+        elif variant == "plain":
             la.la_gdn_fwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state, out=out,
                           final_state=fin, l2norm=True, workspace=ws, stream=stream)
+        else:
+            la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state, out=out,
+                             final_state=fin, l2norm=True, beta_sigmoid=g.beta_sigmoid, a_log=g.a_log,
+                             dt_bias=g.dt_bias, checkpoint_every_n_tokens=every, checkpoints=ck,
+                             num_householder=nh, workspace=ws, stream=stream)
 
     if args.calibrate_copy_mib > 0:
         nbytes = args.calibrate_copy_mib << 20
@@ -232,7 +276,7 @@ def main(argv=None):
     ms_per_step = 1e3 * elapsed / args.steps
     value = T * args.steps / elapsed
 
-    by, fl = algorithmic_counts(lengths, HK, HV, K, V, summary, prob.state is not None, True)
+    by, fl = algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, True, **count_kw)
     inter_us = kern["k_inter"]["avg_us"]
     # the dominant kernel's roofline: the path's algorithmic bytes (one launch
     # processes every token-head of the batch) over that kernel's launch time;
@@ -247,7 +291,7 @@ def main(argv=None):
     roof["frac"] = roof["achieved"] / roof["peak"]
     # the committed counter record covers the default workload only
     roof["traffic"] = measured_traffic(os.path.join(ROOT, "gated_delta_rule_50_amd", "csrc",
-                                                    "la_gdn_kernels.hip")) if wl == 2 else None
+                                                    "la_gdn_kernels.hip")) if wl == 2 and variant == "plain" else None
     roof.update({"algorithmic_bytes_per_launch": by, "algorithmic_flops_per_launch": fl,
                  "avg_launch_us": inter_us})
 
@@ -264,7 +308,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[wl],
+        "config": {"workload": WORKLOADS[wl] + (f"; {VARIANTS[variant]}" if VARIANTS[variant] else ""),
                    "T": T, "N": N, "HK": HK, "HV": HV, "K": K, "V": V, "copies_rotated": len(sets),
                    "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roof,
@@ -274,7 +318,7 @@ def main(argv=None):
                  "mfma_frac": fl / step_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                  "kernels": kern},
     }
-    if not args.no_cpu_baseline and wl == 2:
+    if not args.no_cpu_baseline and wl == 2 and variant == "plain":
         rec["cpu_baseline"] = cpu_baseline(prob)
     print(json.dumps(rec), flush=True)
     return 0
