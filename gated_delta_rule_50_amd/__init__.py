@@ -84,6 +84,10 @@ class Options(ctypes.Structure):
         ("checkpoints", ctypes.c_void_p),
         ("checkpoint_capacity", ctypes.c_int64),
         ("num_householder", ctypes.c_int32),
+        ("householder_token_major", ctypes.c_int32),
+        ("k_stride_update", ctypes.c_int64),
+        ("v_stride_update", ctypes.c_int64),
+        ("beta_stride_update", ctypes.c_int64),
     ]
 
 
@@ -152,13 +156,28 @@ def make_desc(k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Ten
               num_seqs: int, q: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
               scale: Optional[float] = None, num_householder: int = 1) -> Desc:
     """Descriptor from tensor shapes and strides (no data is read).  With
-    num_householder = n > 1, k, v and beta hold n update rows per token."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
-        if t is not None and (t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1)):
-            raise ValueError(f"{name} must be rank 3 [T, heads, dim] with a contiguous innermost axis")
-    for name, t in (("g", g), ("beta", beta)):
-        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-            raise ValueError(f"{name} must be rank 2 [T, HV] with a contiguous innermost axis")
+    num_householder = n > 1, k, v and beta hold n update rows per token: update-major
+    (k [T n, HK, K], v [T n, HV, V], beta [T n, HV]) or token-major (k [T, n, HK, K],
+    v [T, n, HV, V], beta [T, n, HV]; the token strides go in the descriptor, the
+    update strides in the options, see token_major_strides)."""
+    tm = k.dim() == 4
+    kv_rank, b_rank = (4, 3) if tm else (3, 2)
+    for name, t, r in (("q", q, 3), ("k", k, kv_rank), ("v", v, kv_rank), ("out", out, 3)):
+        if t is not None and (t.dim() != r or (t.shape[-1] > 1 and t.stride(-1) != 1)):
+            raise ValueError(f"{name} must be rank {r} with a contiguous innermost axis")
+    for name, t, r in (("g", g, 2), ("beta", beta, b_rank)):
+        if t.dim() != r or (t.shape[-1] > 1 and t.stride(-1) != 1):
+            raise ValueError(f"{name} must be rank {r} with a contiguous innermost axis")
+    if tm:
+        T, n, HK, K = k.shape
+        if n != num_householder or v.shape[:2] != (T, n) or beta.shape[:2] != (T, n):
+            raise ValueError("token-major k, v and beta must be [T, num_householder, ...]")
+        HV, V = v.shape[2], v.shape[3]
+        qq = q if q is not None else k[:, 0]
+        oo = out if out is not None else v[:, 0]
+        return Desc(num_seqs, T, HK, HV, K, V, float(scale) if scale else 0.0,
+                    qq.stride(0), qq.stride(1), k.stride(0), k.stride(2), v.stride(0), v.stride(2),
+                    oo.stride(0), oo.stride(1), g.stride(0), beta.stride(0))
     TU, HK, K = k.shape
     if TU % max(1, num_householder):
         raise ValueError("k must hold num_householder update rows per token")
@@ -234,11 +253,21 @@ def _options(beta: torch.Tensor, beta_sigmoid: bool, a_log, dt_bias) -> Options:
     for name, t in (("a_log", a_log), ("dt_bias", dt_bias)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 [HV] tensor")
-    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0, 1)
+    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0, 1, 0, 0, 0, 0)
+
+
+def token_major_strides(opts: Options, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor):
+    """Fills the token-major fields of the options from rank-4 k, v and rank-3 beta
+    (no-op for update-major operands)."""
+    if k.dim() == 4:
+        opts.householder_token_major = 1
+        opts.k_stride_update = k.stride(1)
+        opts.v_stride_update = v.stride(1)
+        opts.beta_stride_update = beta.stride(1)
 
 
 def la_gdn_workspace_bytes_ex(desc: Desc, is_summary: bool = False, num_householder: int = 1) -> int:
-    opts = Options(0, None, None, 0, 0, None, 0, int(num_householder))
+    opts = Options(0, None, None, 0, 0, None, 0, int(num_householder), 0, 0, 0, 0)
     n = load_library().la_gdn_workspace_bytes_ex(ctypes.byref(desc), int(bool(is_summary)), ctypes.byref(opts))
     if n == 0:
         raise LaError(LA_ERR_INVALID_ARGUMENT, la_last_error_message())
@@ -264,10 +293,11 @@ def la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, fi
     lib = load_library()
     opts = _options(beta, beta_sigmoid, a_log, dt_bias)
     opts.num_householder = int(num_householder)
+    token_major_strides(opts, k, v, beta)
     N = cu_seqlens.numel() - 1
     T = q.shape[0]
-    HV, V = v.shape[1], v.shape[2]
-    K = k.shape[2]
+    HV, V = v.shape[-2], v.shape[-1]
+    K = k.shape[-1]
     if out is None:
         out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
     if final_state is None and output_final_state:
@@ -302,9 +332,10 @@ def la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state=None, end_state=Non
     lib = load_library()
     opts = _options(beta, beta_sigmoid, a_log, dt_bias)
     opts.num_householder = int(num_householder)
+    token_major_strides(opts, k, v, beta)
     N = cu_seqlens.numel() - 1
-    HV, V = v.shape[1], v.shape[2]
-    K = k.shape[2]
+    HV, V = v.shape[-2], v.shape[-1]
+    K = k.shape[-1]
     if end_state is None:
         end_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
     if transition is None:

@@ -106,6 +106,9 @@ la_status check_f32(const char *name, const void *ptr, bool required)
     return LA_OK;
 }
 
+int householder(const la_gdn_options *f);
+bool token_major(const la_gdn_options *f);
+
 // beta (fp32, or bf16 logits under the in-kernel sigmoid) and the safe-gate parameters.
 la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la_gdn_options *f)
 {
@@ -114,7 +117,7 @@ la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la
     if (!beta) return fail(LA_ERR_INVALID_ARGUMENT, "beta is NULL");
     if (logits ? (reinterpret_cast<uintptr_t>(beta) & 1u) != 0 : !aligned4(beta))
         return fail(LA_ERR_INVALID_ARGUMENT, "beta is not %d-byte aligned", logits ? 2 : 4);
-    if (T > 1 && d.beta_stride_t < d.num_v_heads)
+    if (T > 1 && !token_major(f) && d.beta_stride_t < d.num_v_heads)
         return fail(LA_ERR_INVALID_ARGUMENT, "beta token stride %lld is smaller than num_v_heads %d",
                     (long long)d.beta_stride_t, d.num_v_heads);
     if (!f) return LA_OK;
@@ -139,6 +142,84 @@ la_status check_householder(const la_gdn_desc &d, const la_gdn_options *f)
     if (householder(f) > 1 && f->checkpoint_every_n_tokens != 0)
         return fail(LA_ERR_UNSUPPORTED, "the state series is not available with num_householder > 1");
     return LA_OK;
+}
+
+bool token_major(const la_gdn_options *f) { return householder(f) > 1 && f->householder_token_major != 0; }
+
+// Gated Delta Product, token-major operands ("Linear Attention" page, its description of
+// GDP): n update rows of `heads` x `dim` per token, su apart, the tokens st apart.
+la_status check_update_rows(const char *name, int64_t st, int64_t su, int64_t row_extent, int n, int64_t T,
+                            bool vec16)
+{
+    if (vec16 && su % 8 != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "%s update stride %lld must be a multiple of 8 elements (16 bytes)",
+                    name, (long long)su);
+    if (su < row_extent)
+        return fail(LA_ERR_INVALID_ARGUMENT, "%s update stride %lld overlaps its heads", name, (long long)su);
+    if (T > 1 && st < (int64_t)(n - 1) * su + row_extent)
+        return fail(LA_ERR_INVALID_ARGUMENT, "%s token stride %lld overlaps its %d update rows", name,
+                    (long long)st, n);
+    if (st >= (1 << 23) || su >= (1 << 23))
+        return fail(LA_ERR_UNSUPPORTED, "%s strides of 2^23 elements or more are not supported", name);
+    return LA_OK;
+}
+
+// The kernels address a chunk's update rows with 32-bit offsets from its first token:
+// 64 token strides plus 64 update strides stay below 2^30 elements.
+la_status check_update_major_range(const char *name, int64_t row_stride, int n)
+{
+    if (n > 1 && row_stride * n >= (1 << 23))
+        return fail(LA_ERR_UNSUPPORTED, "%s: row stride * num_householder of 2^23 elements or more is not supported",
+                    name);
+    return LA_OK;
+}
+
+// k, v and beta of either layout; `TU` = update rows.
+la_status check_kvb(const la_gdn_desc &d, const void *k, const void *v, const la_gdn_options *f)
+{
+    const int64_t T = d.total_tokens;
+    la_status st;
+    if (!token_major(f)) {
+        const int64_t TU = T * householder(f);   // update rows of k, v and beta
+        if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, TU)) != LA_OK)
+            return st;
+        if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, TU)) != LA_OK)
+            return st;
+        const int n = householder(f);
+        if ((st = check_update_major_range("k", d.k_stride_t, n)) != LA_OK) return st;
+        if ((st = check_update_major_range("v", d.v_stride_t, n)) != LA_OK) return st;
+        return check_update_major_range("beta", d.beta_stride_t, n);
+    }
+    const int n = householder(f);
+    // pointers and the head strides as for one row, then the update and token strides
+    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, 1)) != LA_OK) return st;
+    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, 1)) != LA_OK) return st;
+    if ((st = check_update_rows("k", d.k_stride_t, f->k_stride_update,
+                                (int64_t)(d.num_qk_heads - 1) * d.k_stride_h + d.head_dim_k, n, T, true)) != LA_OK)
+        return st;
+    if ((st = check_update_rows("v", d.v_stride_t, f->v_stride_update,
+                                (int64_t)(d.num_v_heads - 1) * d.v_stride_h + d.head_dim_v, n, T, true)) != LA_OK)
+        return st;
+    return check_update_rows("beta", d.beta_stride_t, f->beta_stride_update, d.num_v_heads, n, T, false);
+}
+
+// Row strides of k, v and beta as the kernels take them: for n > 1, token strides plus the
+// stride between the updates of one token.
+void set_update_strides(la::Prob &p, const la_gdn_options *f)
+{
+    p.kstu = p.kst;
+    p.vstu = p.vst;
+    p.bstu = p.bst;
+    if (p.nh == 1) return;
+    if (token_major(f)) {
+        p.kstu = f->k_stride_update;
+        p.vstu = f->v_stride_update;
+        p.bstu = f->beta_stride_update;
+    } else {
+        p.kst *= p.nh;
+        p.vst *= p.nh;
+        p.bst *= p.nh;
+    }
 }
 
 // The state series options ("Linear Attention" page, "States and checkpoints").
@@ -169,6 +250,7 @@ void set_beta_and_fusion(la::Prob &p, const void *beta, const la_gdn_options *f)
     p.a_log = f ? f->a_log : nullptr;
     p.dt_bias = f ? f->dt_bias : nullptr;
     p.nh = householder(f);
+    p.inv_nh = 1.0f / (float)p.nh;
     p.max_chunks = (int32_t)((p.T * p.nh + 63) / 64 + p.N);
     const bool series = f && f->checkpoint_every_n_tokens > 0 && f->checkpoint_capacity > 0;
     p.ck_every = series ? f->checkpoint_every_n_tokens : 0;
@@ -383,10 +465,8 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     const la_gdn_desc &d = *desc;
     const int64_t T = d.total_tokens;
     if ((st = check_householder(d, fusion)) != LA_OK) return st;
-    const int64_t TU = T * householder(fusion);   // update rows of k, v and beta
     if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
-    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, TU)) != LA_OK) return st;
-    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, TU)) != LA_OK) return st;
+    if ((st = check_kvb(d, k, v, fusion)) != LA_OK) return st;
     if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
@@ -402,6 +482,7 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     p.v = static_cast<const __bf16 *>(v);
     p.g = g;
     set_beta_and_fusion(p, beta, fusion);
+    set_update_strides(p, fusion);
     p.cu = cu_seqlens;
     p.s0 = initial_state;
     p.o = static_cast<__bf16 *>(out);
@@ -429,9 +510,7 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
     const la_gdn_desc &d = *desc;
     const int64_t T = d.total_tokens;
     if ((st = check_householder(d, fusion)) != LA_OK) return st;
-    const int64_t TU = T * householder(fusion);   // update rows of k, v and beta
-    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, TU)) != LA_OK) return st;
-    if ((st = check_thd("v", v, d.v_stride_t, d.v_stride_h, d.num_v_heads, d.head_dim_v, TU)) != LA_OK) return st;
+    if ((st = check_kvb(d, k, v, fusion)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
     if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
@@ -447,6 +526,7 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
     p.v = static_cast<const __bf16 *>(v);
     p.g = g;
     set_beta_and_fusion(p, beta, fusion);
+    set_update_strides(p, fusion);
     p.cu = cu_seqlens;
     p.s0 = start_state;
     p.o = nullptr;

@@ -30,6 +30,10 @@ struct Prob {
                                       // T and cu_seqlens count tokens; k, v and beta have nh update
                                       // rows per token (update-major), q, g and o one row per token;
                                       // the kernels work in update rows, chunks of 64 updates
+    float inv_nh;                     // 1 / nh
+    int64_t kstu, vstu, bstu;         // nh > 1: element stride between the update rows of one token;
+                                      // kst, vst and bst are then token strides (update-major rows:
+                                      // kst = nh kstu; token-major [T, nh, H, D] views: any)
     int32_t ck_every;                 // state series every ck_every tokens (a multiple of 64), 0: none
     int32_t ck_fp32;                  // series rows in fp32 (else bf16)
     void *ck;                         // [ck_cap, HV, K, V] series, sequences in batch order

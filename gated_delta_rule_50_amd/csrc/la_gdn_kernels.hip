@@ -36,8 +36,9 @@
 //               same body: k_inter_sum (span summary: no output waves, the state
 //               widened by the transition columns), k_inter_ck (with the state
 //               series) and k_inter_gdp (Gated Delta Product: q and o rows mapped
-//               from update rows to tokens); k_intra has a Gated Delta Product
-//               variant in the same way
+//               from update rows to tokens, k rows by token and update) and
+//               k_inter_sum_gdp (its summary); k_intra has a Gated Delta Product
+//               variant in the same way (k, v and beta rows by token and update)
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 for the bf16 products and v_mfma_f32_16x16x4_f32
 // for the fp32 block products of the triangular solve (lane layouts with the
@@ -488,6 +489,36 @@ __device__ __forceinline__ void intra_load_qrows(lds_u32x4 *dst, const void *bas
     }
 }
 
+// Gated Delta Product: element offset of update row tb nh + rel (0 <= rel < 128) from row
+// 0 of token tb: rel / nh tokens of stride st and rel % nh updates of stride su (update-major
+// rows: st = nh su).  The quotient goes through the reciprocal: (rel + 1/2) / nh lies at
+// least 1 / (2 nh) >= 1/128 from an integer, far beyond the float product's rounding.  The
+// host keeps 64 st + 64 su below 2^30, so the offset fits in 32 bits.
+__device__ __forceinline__ uint32_t upd_off(int rel, int nh, float inv_nh, int st, int su)
+{
+    const int t = (int)(((float)rel + 0.5f) * inv_nh);
+    return (uint32_t)(t * st + (rel - t * nh) * su);
+}
+
+// Gated Delta Product: the 64 update rows of a chunk of a bf16 tile (k or v), `len` of them
+// valid, from `tok0` = row 0 of the chunk's first token; `phase` = the chunk's first update
+// row within that token.  Rows past the end get an offset past the buffer's range and load
+// as zeros.  Same LDS layout as intra_load_tile.
+template <int D>
+__device__ __forceinline__ void intra_load_urows(lds_u32x4 *dst, const __bf16 *tok0, int st, int su, int phase,
+                                                 int len, int nh, float inv_nh, int wave, int lane, int nw)
+{
+    constexpr int PPR = D / 8;
+    // (uniform; the float quotient is formed in vector registers)
+    const uint32_t nrec = __builtin_amdgcn_readfirstlane(2u * (upd_off(phase + len - 1, nh, inv_nh, st, su) + D));
+    const i32x4 r = make_rsrc(tok0, nrec);
+    for (int i = wave; i < PPR; i += nw) {
+        const int s = 64 * i + lane, row = s / PPR, pp = s % PPR;
+        b2l(r, dst, i,
+            row < len ? 2u * upd_off(phase + row, nh, inv_nh, st, su) + 16u * (uint32_t)(pp ^ (row % PPR)) : nrec, 0);
+    }
+}
+
 // 16-byte operand read from a swizzled bf16 tile: row `row`, columns c0 .. c0 + 7 (c0 % 8 == 0).
 template <int PPR>
 __device__ __forceinline__ bf16x8 lds_row8(const lds_u32x4 *tile, int row, int c0)
@@ -584,14 +615,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         const int cm = lm & 31, hm = lm >> 5;
 
         // ---- 1: k, q, g, beta into LDS
-        intra_load_tile<K>(sK, p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst, len, wave,
-                           lane, 4);
+        // Gated Delta Product: the chunk's first token and its first update row within it
+        const int tb = GDP ? __builtin_amdgcn_readfirstlane(start / p.nh) : start;
+        const int phase = start - tb * p.nh;
+        if (!GDP)
+            intra_load_tile<K>(sK, p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst, len,
+                               wave, lane, 4);
+        else
+            intra_load_urows<K>(sK, p.k + (int64_t)tb * p.kst + (int64_t)hk * p.ksh, (int)p.kst, (int)p.kstu, phase,
+                                len, p.nh, p.inv_nh, wave, lane, 4);
         if (FWD) {
             if (!GDP) {
                 intra_load_tile<K>(sX, p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
                                    len, wave, lane, 4);
             } else {
-                const int tb = __builtin_amdgcn_readfirstlane(start / p.nh);
                 intra_load_qrows<K>(sX, p.q + (int64_t)tb * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
                                     (uint32_t)(p.T - tb) * 2u * (uint32_t)p.qst, start, len, p.nh, tb, wave, lane, 4);
             }
@@ -608,11 +645,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 gfirst = u % p.nh == 0;
                 if (lane < len && gfirst) graw = p.g[(int64_t)(u / p.nh) * p.gst + h];
             }
-            if (p.beta16) {
-                if (lane < len) blogit = bf2f(p.beta16[(int64_t)(start + lane) * p.bst + h]);
+            if (!GDP) {
+                if (p.beta16) {
+                    if (lane < len) blogit = bf2f(p.beta16[(int64_t)(start + lane) * p.bst + h]);
+                } else {
+                    const i32x4 rb = make_rsrc(p.beta + (int64_t)start * p.bst + h, (uint32_t)len * 4u * (uint32_t)p.bst);
+                    b2l_dword(rb, s_b, (uint32_t)lane * 4u * (uint32_t)p.bst);
+                }
             } else {
-                const i32x4 rb = make_rsrc(p.beta + (int64_t)start * p.bst + h, (uint32_t)len * 4u * (uint32_t)p.bst);
-                b2l_dword(rb, s_b, (uint32_t)lane * 4u * (uint32_t)p.bst);
+                // update row start + lane, from row 0 of token tb
+                const uint32_t bo = upd_off(phase + lane, p.nh, p.inv_nh, (int)p.bst, (int)p.bstu);
+                if (p.beta16) {
+                    if (lane < len) blogit = bf2f(p.beta16[(int64_t)tb * p.bst + bo + h]);
+                } else {
+                    const uint32_t nrec = __builtin_amdgcn_readfirstlane(
+                        4u * (upd_off(phase + len - 1, p.nh, p.inv_nh, (int)p.bst, (int)p.bstu) + 1));
+                    const i32x4 rb = make_rsrc(p.beta + (int64_t)tb * p.bst + h, nrec);
+                    b2l_dword(rb, s_b, lane < len ? 4u * bo : nrec);
+                }
             }
         }
         vm_wait<0>();
@@ -678,8 +728,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
         // ---- 2c: v into q's space (every q read is done); per-token factors and the inter
         // pass's scalars (wave 1); A^T (waves 0..2); P^T out (waves 0, 2, 3)
-        intra_load_tile<V>(sX, p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst, len, wave,
-                           lane, 4);
+        if (!GDP)
+            intra_load_tile<V>(sX, p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst, len,
+                               wave, lane, 4);
+        else
+            intra_load_urows<V>(sX, p.v + (int64_t)tb * p.vst + (int64_t)h * p.vsh, (int)p.vst, (int)p.vstu, phase,
+                                len, p.nh, p.inv_nh, wave, lane, 4);
         const float gl = s_gam[len - 1];
         if (wave == 1) {
             const int t = lane;
@@ -947,25 +1001,63 @@ struct InterCtx {
 
 // Loader wave lh, its half of chunk ci's raw k rows into `lb`.  Returns the
 // number of loads.
-template <int K, int V, bool SUMMARY>
+// Gated Delta Product: where a chunk of update rows starts, token tb and update `phase`
+// of it (uniform).  A sequence starts at a token's first update; each chunk is 64 updates
+// on, so the loaders step the cursor instead of dividing by nh per chunk.
+struct UCursor {
+    int tb, phase;
+    __device__ void advance(int q64, int r64, int nh)   // q64 = 64 / nh, r64 = 64 % nh
+    {
+        tb += q64;
+        phase += r64;
+        if (phase >= nh) { phase -= nh; ++tb; }
+    }
+};
+
+// Gated Delta Product: koff holds the offsets of the pieces' rows for a chunk that starts at
+// its token's first update (row = a nh + b: a tokens and b updates on), kb the b of each row.
+template <int K, int V, bool SUMMARY, bool GDP>
 __device__ __forceinline__ int inter_issue_k(const Prob &p, lds_u32x4 *lb, int ci, int lh,
                                              const InterCtx<K, V, SUMMARY> &x,
-                                             const uint32_t (&koff)[InterCfg<K, V, SUMMARY>::NKL])
+                                             const uint32_t (&koff)[InterCfg<K, V, SUMMARY>::NKL],
+                                             const int (&kb)[InterCfg<K, V, SUMMARY>::NKL], UCursor cur)
 {
     using C = InterCfg<K, V, SUMMARY>;
     const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
-    const i32x4 rK = make_rsrc(p.k + (int64_t)start * p.kst + (int64_t)x.hk * p.ksh, (uint32_t)len * 2u * (uint32_t)p.kst);
+    if (!GDP) {
+        const i32x4 rK = make_rsrc(p.k + (int64_t)start * p.kst + (int64_t)x.hk * p.ksh,
+                                   (uint32_t)len * 2u * (uint32_t)p.kst);
 #pragma unroll
-    for (int i = 0; i < C::NKL; ++i) b2l(rK, lb, C::oK + 2 * i + lh, koff[i], 0);
+        for (int i = 0; i < C::NKL; ++i) b2l(rK, lb, C::oK + 2 * i + lh, koff[i], 0);
+    } else {
+        // Gated Delta Product: the chunk starts `phase` updates into token tb, so row a nh + b
+        // is a tokens and b + phase updates on, or a + 1 tokens and b + phase - nh updates
+        // once b + phase >= nh.  Offsets grow with the row (the token stride covers a token's
+        // updates), so rows past the end lie past the range and load as zeros.
+        const int tb = __builtin_amdgcn_readfirstlane(cur.tb), phase = __builtin_amdgcn_readfirstlane(cur.phase);
+        const int st = (int)p.kst, su = (int)p.kstu;
+        // the last row: lt tokens and phase + len - 1 - lt nh updates on (a quotient below 128)
+        const int lt = __builtin_amdgcn_readfirstlane((int)(((float)(phase + len - 1) + 0.5f) * p.inv_nh));
+        const uint32_t nrec = __builtin_amdgcn_readfirstlane(2u * (uint32_t)(lt * st + (phase + len - 1 - lt * p.nh) * su + K));
+        const i32x4 rK = make_rsrc(p.k + (int64_t)tb * p.kst + (int64_t)x.hk * p.ksh, nrec);
+        const uint32_t u0 = 2u * (uint32_t)(phase * su), u1 = u0 + 2u * (uint32_t)(st - p.nh * su);
+        const int thr = p.nh - phase;
+#pragma unroll
+        for (int i = 0; i < C::NKL; ++i) b2l(rK, lb, C::oK + 2 * i + lh, koff[i] + (kb[i] >= thr ? u1 : u0), 0);
+    }
     return C::NKL;
 }
 
 // Loader wave lh, its half of chunk ci's output operands (raw q, P^T) and the
 // scalars (loader 0) into `eb`.  Returns the number of loads.
+// Gated Delta Product: qoff holds the token offsets of the pieces' rows (a of row = a nh + b)
+// for a chunk that starts at its token's first update, kb the b and krow the row of each.
 template <int K, int V, bool SUMMARY, bool GDP>
 __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
                                                   const InterCtx<K, V, SUMMARY> &x,
-                                                  const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ])
+                                                  const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ],
+                                                  const int (&kb)[InterCfg<K, V, SUMMARY>::NKL],
+                                                  const int (&krow)[InterCfg<K, V, SUMMARY>::NKL], UCursor cur)
 {
     using C = InterCfg<K, V, SUMMARY>;
     const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
@@ -980,16 +1072,18 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
             for (int i = 0; i < C::FQ / 2; ++i) b2l(rQ, eb, C::oQ + 2 * i + lh, qoff[i], 0);
         } else {
             // Gated Delta Product: update row start + row reads q row (start + row) / nh at its
-            // token's last update, zeros otherwise (offset past the buffer's range)
-            const int tb = __builtin_amdgcn_readfirstlane(start / p.nh);
+            // token's last update, zeros otherwise (offset past the buffer's range).  Row
+            // a nh + b is update b + phase of token tb + a, or, once b + phase >= nh, update
+            // b + phase - nh of token tb + a + 1.
+            const int tb = __builtin_amdgcn_readfirstlane(cur.tb), phase = __builtin_amdgcn_readfirstlane(cur.phase);
+            const int thr = p.nh - phase;
             const uint32_t rs = 2u * (uint32_t)p.qst, nrec = (uint32_t)(p.T - tb) * rs;
             const i32x4 rQ = make_rsrc(p.q + (int64_t)tb * p.qst + (int64_t)x.hk * p.qsh, nrec);
 #pragma unroll
             for (int i = 0; i < C::FQ / 2; ++i) {
-                const int s = (2 * i + lh) * 64 + x.lane, row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
-                const int u = start + row;
-                const bool last = row < len && u % p.nh == p.nh - 1;
-                b2l(rQ, eb, C::oQ + 2 * i + lh, last ? (uint32_t)(u / p.nh - tb) * rs + 16u * (uint32_t)pc : nrec, 0);
+                const bool wrap = kb[i] >= thr;
+                const bool last = krow[i] < len && kb[i] + phase - (wrap ? p.nh : 0) == p.nh - 1;
+                b2l(rQ, eb, C::oQ + 2 * i + lh, last ? qoff[i] + (wrap ? rs : 0u) : nrec, 0);
             }
         }
         const i32x4 rP = make_rsrc(reinterpret_cast<const char *>(w.PF) + chh * 6 * kFrag, 6 * kFrag);
@@ -1114,13 +1208,27 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         // source offsets of this lane's 16-byte pieces of the k and q tiles (LDS piece
         // (row, j) holds source piece j ^ (row % PPR) of the row)
         uint32_t qoff[C::NQ], koff[C::NKL];
+        int kb[C::NKL], krow[C::NKL];
 #pragma unroll
         for (int i = 0; i < C::NKL; ++i) {
             const int s = (2 * i + lh) * 64 + lane;
             const int row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
-            koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
-            if (C::FWD) qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
+            krow[i] = row;
+            if (!GDP) {
+                kb[i] = 0;
+                koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
+                if (C::FWD) qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
+            } else {
+                const int a = row / p.nh;
+                kb[i] = row - a * p.nh;
+                koff[i] = 2u * (uint32_t)(a * (int)p.kst + kb[i] * (int)p.kstu) + 16u * (uint32_t)pc;
+                if (C::FWD) qoff[i] = (uint32_t)a * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
+            }
         }
+        // Gated Delta Product: the cursor of the next chunk to issue (chunk 0 starts at the
+        // sequence's first token; every chunk is 64 update rows)
+        const int q64 = GDP ? 64 / p.nh : 0, r64 = GDP ? 64 - q64 * p.nh : 0;
+        UCursor cur{GDP ? __builtin_amdgcn_readfirstlane(x.seq_start / p.nh) : 0, 0};
         // chunk c's k rows land in k buffer c % 2, its output operands in buffer c % 3.
         // At the start of chunk c (after B2 of chunk c - 1, when chunk c - 1's output
         // operands are dead) the output operands of chunk c + 2 are issued, after B1 of
@@ -1128,20 +1236,25 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         // of chunk c the loaders wait for all of chunk c + 1's.
         int na = 0, nb = 0;
         if (nch > 0) {
-            na = inter_issue_k<K, V, SUMMARY>(p, l0, 0, lh, x, koff);
-            nb = inter_issue_output<K, V, SUMMARY, GDP>(p, w, e0, 0, lh, x, qoff);
+            na = inter_issue_k<K, V, SUMMARY, GDP>(p, l0, 0, lh, x, koff, kb, cur);
+            nb = inter_issue_output<K, V, SUMMARY, GDP>(p, w, e0, 0, lh, x, qoff, kb, krow, cur);
+            if (GDP) cur.advance(q64, r64, p.nh);
             if (nch > 1) {
-                inter_issue_k<K, V, SUMMARY>(p, l1, 1, lh, x, koff);
-                inter_issue_output<K, V, SUMMARY, GDP>(p, w, e1, 1, lh, x, qoff);
+                inter_issue_k<K, V, SUMMARY, GDP>(p, l1, 1, lh, x, koff, kb, cur);
+                inter_issue_output<K, V, SUMMARY, GDP>(p, w, e1, 1, lh, x, qoff, kb, krow, cur);
+                if (GDP) cur.advance(q64, r64, p.nh);
             }
             vm_wait_n(nch > 1 ? na + nb : 0);                 // all of chunk 0
         }
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const bool more2 = ci + 2 < nch;
-            if (more2) inter_issue_output<K, V, SUMMARY, GDP>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff);
+            if (more2) inter_issue_output<K, V, SUMMARY, GDP>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff, kb, krow, cur);
             lds_barrier();                                    // B1
-            if (more2) inter_issue_k<K, V, SUMMARY>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff);
+            if (more2) {
+                inter_issue_k<K, V, SUMMARY, GDP>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff, kb, cur);
+                if (GDP) cur.advance(q64, r64, p.nh);
+            }
             vm_wait_n(more2 ? na + nb : 0);                   // all of chunk ci + 1
             lds_barrier();                                    // B2
         }
@@ -1418,6 +1531,13 @@ __global__ __launch_bounds__(256) void k_inter_sum(Prob p, Ws w)
     inter_body<K, V, true>(p, w);
 }
 
+// The Gated Delta Product's summary: k rows addressed by token and update.
+template <int K, int V>
+__global__ __launch_bounds__(256) void k_inter_sum_gdp(Prob p, Ws w)
+{
+    inter_body<K, V, true, false, true>(p, w);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch sequence.
 
@@ -1450,7 +1570,9 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
     if (blocks > 0) {
         before(LA_KERNEL_INTER);
         const dim3 threads(InterCfg<K, V, SUMMARY>::THREADS);
-        if (SUMMARY)
+        if (SUMMARY && p.nh > 1)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum_gdp<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else if (SUMMARY)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else if (p.nh > 1)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_gdp<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);

@@ -171,6 +171,19 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
  *                 n delta-rule updates run in order, then o_t is read.  The
  *                 workspace is sized by la_gdn_workspace_bytes_ex.  Not combined
  *                 with the state series (LA_ERR_UNSUPPORTED).
+ *   householder_token_major  nonzero: k, v and beta come token-major instead
+ *                 (the same page: k [T, n, HK, K], v [T, n, HV, V], beta [T, n, HV]
+ *                 with the caller's token stride, so that the per-token column slices
+ *                 of a joint projection [T, n * H * D], viewed as [T, n, H, D], are read
+ *                 in place): update r of token t is at t * k_stride_t +
+ *                 r * k_stride_update (likewise v and beta), and k_stride_t, v_stride_t
+ *                 and beta_stride_t step one token.  Zero: update-major as above.
+ *   k_stride_update, v_stride_update, beta_stride_update  elements between the
+ *                 update rows of one token (token-major only).  k and v: multiples
+ *                 of 8, covering the heads of a row; the token stride covers all n
+ *                 rows; otherwise LA_ERR_INVALID_ARGUMENT.  Token or update strides of
+ *                 2^23 elements or more (update-major: the row stride times n) are
+ *                 declined with LA_ERR_UNSUPPORTED.
  */
 typedef struct {
     int32_t beta_sigmoid;
@@ -181,6 +194,10 @@ typedef struct {
     void *checkpoints;
     int64_t checkpoint_capacity;
     int32_t num_householder;
+    int32_t householder_token_major;
+    int64_t k_stride_update;
+    int64_t v_stride_update;
+    int64_t beta_stride_update;
 } la_gdn_options;
 
 /* Workspace bytes for la_gdn_fwd_ex / la_gdn_summary_ex with these options (NULL:

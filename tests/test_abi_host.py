@@ -248,3 +248,61 @@ def test_householder_options(lib):
     rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["out"],
                            a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
     assert rc == la.LA_ERR_UNSUPPORTED and "num_householder" in la.la_last_error_message()
+
+
+def _tm_options(n=2, ks=None, vs=None, bs=None, HK=2, HV=4, K=128, V=128):
+    """Token-major Gated Delta Product options: update strides default to one row of heads."""
+    return la.Options(0, None, None, 0, 0, None, 0, n, 1, HK * K if ks is None else ks,
+                      HV * V if vs is None else vs, HV if bs is None else bs)
+
+
+@pytest.mark.parametrize("desc_over,opt_over,status,needle", [
+    # an update stride that is not a multiple of 8 elements
+    (dict(), dict(ks=2 * 128 + 4), la.LA_ERR_INVALID_ARGUMENT, "k"),
+    # updates of one token that overlap their heads
+    (dict(), dict(vs=4 * 128 - 8), la.LA_ERR_INVALID_ARGUMENT, "v update stride"),
+    # a token stride that does not cover the token's n update rows
+    (dict(k_stride_t=2 * 128), dict(), la.LA_ERR_INVALID_ARGUMENT, "k token stride"),
+    (dict(beta_stride_t=4), dict(), la.LA_ERR_INVALID_ARGUMENT, "beta token stride"),
+    (dict(), dict(bs=3), la.LA_ERR_INVALID_ARGUMENT, "beta update stride"),
+    # strides beyond the 32-bit offsets of one chunk's loads
+    (dict(v_stride_t=1 << 23), dict(), la.LA_ERR_UNSUPPORTED, "2^23"),
+])
+def test_token_major_strides_checked(lib, desc_over, opt_over, status, needle):
+    """Gated Delta Product, token-major k, v and beta: the token and update strides are
+    checked before any launch."""
+    n = 2
+    base = dict(k_stride_t=n * 2 * 128, v_stride_t=n * 4 * 128, beta_stride_t=n * 4)
+    base.update(desc_over)
+    d = _desc(**base)
+    o = _tm_options(n=n, **opt_over)
+    a = _fwd_args()
+    rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["out"],
+                           a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    assert rc == status and needle in la.la_last_error_message(), la.la_last_error_message()
+    rc = lib.la_gdn_summary_ex(ctypes.byref(d), a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["fin"],
+                               a["out"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    assert rc == status and needle in la.la_last_error_message(), la.la_last_error_message()
+
+
+def test_token_major_descriptor_from_views():
+    """make_desc and the options from rank-4 k, v and rank-3 beta views of joint
+    per-token buffers: token strides in the descriptor, update strides in the options."""
+    T, n, HK, HV, K, V = 5, 3, 2, 4, 64, 128
+    joint = torch.zeros(T, n * HV * V + n * HK * K + 8, dtype=torch.bfloat16)
+    v = joint[:, :n * HV * V].view(T, n, HV, V)
+    k = joint[:, n * HV * V:n * HV * V + n * HK * K].view(T, n, HK, K)
+    bj = torch.zeros(T, n * HV + 4)
+    beta = bj[:, :n * HV].view(T, n, HV)
+    q = torch.zeros(T, HK, K, dtype=torch.bfloat16)
+    g = torch.zeros(T, HV)
+    d = la.make_desc(k, v, g, beta, 1, q=q, num_householder=n)
+    W = joint.stride(0)
+    assert (d.total_tokens, d.num_qk_heads, d.num_v_heads, d.head_dim_k, d.head_dim_v) == (T, HK, HV, K, V)
+    assert (d.k_stride_t, d.k_stride_h, d.v_stride_t, d.v_stride_h, d.beta_stride_t) == (W, K, W, V, n * HV + 4)
+    o = la.Options()
+    la.token_major_strides(o, k, v, beta)
+    assert (o.householder_token_major, o.k_stride_update, o.v_stride_update, o.beta_stride_update) == (
+        1, HK * K, HV * V, HV)
+    with pytest.raises(ValueError, match="num_householder"):
+        la.make_desc(k, v, g, beta, 1, q=q, num_householder=2)

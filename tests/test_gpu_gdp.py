@@ -1,5 +1,5 @@
 """GPU parity of the Gated Delta Product (la_gdn_fwd_ex / la_gdn_summary_ex with
-num_householder = n: k, v and beta n update rows per token, update-major; q, g
+num_householder = n: k, v and beta n update rows per token, update-major or token-major; q, g
 and o one row per token) against the fp64 oracle's token recurrence with n
 updates per token.  Tolerances as for GDN."""
 import dataclasses
@@ -83,3 +83,67 @@ def test_gdp_with_fused_gate_and_beta():
     torch.cuda.synchronize()
     ref = Oracle(p).run_all()
     assert rel_l2(f64(out), ref["o"]) <= TOL_O and rel_l2(f64(fin), ref["state"]) <= TOL_STATE
+
+
+def token_major(p, pad=8):
+    """k, v and beta of an update-major problem on the GPU as token-major views into joint
+    per-token buffers ([T, n HV V | n HK K | pad] for v and k, [T, n HV | pad] for beta), the
+    layout of per-token column slices of one projection: neither token stride is n times
+    its update stride."""
+    T, n = p.total_tokens, p.num_householder
+    HK, K, HV, V = p.k.shape[1], p.k.shape[2], p.v.shape[1], p.v.shape[2]
+    wv, wk = n * HV * V, n * HK * K
+    joint = torch.zeros(T, wv + wk + pad, dtype=torch.bfloat16, device="cuda")
+    joint[:, :wv] = p.v.reshape(T, wv).cuda()
+    joint[:, wv:wv + wk] = p.k.reshape(T, wk).cuda()
+    bj = torch.zeros(T, n * HV + pad // 2, dtype=p.beta.dtype, device="cuda")
+    bj[:, :n * HV] = p.beta.reshape(T, n * HV).cuda()
+    return (joint[:, wv:wv + wk].view(T, n, HK, K), joint[:, :wv].view(T, n, HV, V),
+            bj[:, :n * HV].view(T, n, HV))
+
+
+@pytest.mark.parametrize("nh", [2, 3])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128)])
+def test_gdp_token_major_forward(nh, dk, dv):
+    """Token-major k, v and beta (the pages' second GDP layout) give the update-major
+    call's results bit for bit, and so the oracle's."""
+    p = gdp_problem((1, 21, 33, 100, 150), nh, hk=2, hv=4, dk=dk, dv=dv, seed=97, with_state=True)
+    out_u, fin_u = check(p)
+    g = p.to("cuda")
+    k, v, beta = token_major(p)
+    assert k.stride(0) != nh * k.stride(1)
+    note(f"gdp token-major fwd n={nh} dk={dk} dv={dv}")
+    out, fin, _ = la.la_gdn_fwd_ex(g.q, k, v, g.g, beta, g.cu_seqlens, initial_state=g.state, num_householder=nh)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_u) and torch.equal(fin, fin_u)
+
+
+def test_gdp_token_major_summary_and_fused_beta():
+    """The summary from token-major operands, and the forward with token-major bf16 beta
+    logits, against their update-major calls bit for bit."""
+    p = gdp_problem((1, 40, 100, 150), 3, hk=2, hv=2, dk=128, dv=128, seed=98, with_state=True, summary=True,
+                    g_div=4096.0, beta_div=64.0)
+    g = p.to("cuda")
+    k, v, beta = token_major(p)
+    note("gdp token-major summary n=3")
+    end_u, tr_u = la.la_gdn_summary_ex(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state, num_householder=3)
+    end, tr = la.la_gdn_summary_ex(k, v, g.g, beta, g.cu_seqlens, start_state=g.state, num_householder=3)
+    torch.cuda.synchronize()
+    ref = Oracle(p).run_all(want_o=False, want_transition=True)
+    assert rel_l2(f64(end_u), ref["state"]) <= TOL_STATE and rel_l2(f64(tr_u), ref["transition"]) <= TOL_STATE
+    assert torch.equal(end, end_u) and torch.equal(tr, tr_u)
+
+    q = gdp_problem((1, 30, 130), 2, hk=2, hv=4, dk=128, dv=128, seed=99, with_state=True)
+    logits = torch.randn(q.beta.shape, generator=torch.Generator().manual_seed(100)).to(torch.bfloat16)
+    q = dataclasses.replace(q, beta=logits, beta_sigmoid=True)
+    gq = q.to("cuda")
+    k, v, beta = token_major(q)
+    note("gdp token-major fwd n=2 with bf16 beta logits")
+    o_u, f_u, _ = la.la_gdn_fwd_ex(gq.q, gq.k, gq.v, gq.g, gq.beta, gq.cu_seqlens, initial_state=gq.state,
+                                   beta_sigmoid=True, num_householder=2)
+    o_t, f_t, _ = la.la_gdn_fwd_ex(gq.q, k, v, gq.g, beta, gq.cu_seqlens, initial_state=gq.state,
+                                   beta_sigmoid=True, num_householder=2)
+    torch.cuda.synchronize()
+    ref = Oracle(q).run_all()
+    assert rel_l2(f64(o_u), ref["o"]) <= TOL_O and rel_l2(f64(f_u), ref["state"]) <= TOL_STATE
+    assert torch.equal(o_t, o_u) and torch.equal(f_t, f_u)
