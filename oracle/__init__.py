@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Gated DeltaNet forward and span summary.
+"""fp64 CPU oracle for the Gated DeltaNet forward, span summary and backward.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package.  The GPU library
@@ -72,6 +72,9 @@ def _load():
         lib.gdn_oracle_run.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.gdn_oracle_backward.restype = ctypes.c_int
+        lib.gdn_oracle_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32] + [ctypes.c_void_p] * 11 + [
+            ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -231,6 +234,61 @@ class Oracle:
                 c[base[n]:base[n + 1], h] = arr
             out["checkpoints"] = c
         return out
+
+
+def backward(problem, d_o=None, d_final=None, scale: Optional[float] = None,
+             num_threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Gradients of the forward (plain inputs: fp32 beta, natural-log gate, n = 1) for
+    upstream gradients d_o [T, HV, V] and d_final [N, HV, K, V] (None: zeros): dq, dk
+    [T, HK, K] (summed over the value heads of each q/k head), dv [T, HV, V], dg, dbeta
+    [T, HV] and d_init [N, HV, K, V], all fp64 (see gdn_oracle.c)."""
+    o = Oracle(problem, scale=scale)
+    if o.beta_logit is not None or o.a_log is not None or o.nh != 1:
+        raise ValueError("oracle backward: plain inputs only")
+    lib = _load()
+    N, HK, HV, K, V = o.N, o.HK, o.HV, o.K, o.V
+    T = int(o.cu[-1]) if N else 0
+    units = o.all_units()
+    lens = np.array([o.cu[n + 1] - o.cu[n] for n, _ in units], dtype=np.int64)
+    offs = np.zeros(len(units), dtype=np.int64)
+    if units:
+        offs[1:] = np.cumsum(lens)[:-1]
+    rows = int(lens.sum())
+    seq = np.array([u[0] for u in units], dtype=np.int32)
+    head = np.array([u[1] for u in units], dtype=np.int32)
+    dop = None
+    if d_o is not None:
+        d_o = np.asarray(d_o, dtype=np.float64)
+        dop = np.ascontiguousarray(np.concatenate(
+            [d_o[o.cu[n]:o.cu[n + 1], h, :] for n, h in units], axis=0) if units else np.zeros((0, V)))
+    dfp = None
+    if d_final is not None:
+        d_final = np.asarray(d_final, dtype=np.float64)
+        dfp = np.ascontiguousarray(np.stack([d_final[n, h] for n, h in units]) if units else np.zeros((0, K, V)))
+    dq = np.zeros((max(rows, 1), K))
+    dk = np.zeros((max(rows, 1), K))
+    dv = np.zeros((max(rows, 1), V))
+    dg = np.zeros(max(rows, 1))
+    db = np.zeros(max(rows, 1))
+    di = np.zeros((max(len(units), 1), K, V))
+    nt = default_threads() if num_threads is None else num_threads
+    rc = lib.gdn_oracle_backward(ctypes.byref(o._st), len(units), _ptr(seq), _ptr(head), _ptr(offs), _ptr(dop),
+                                 _ptr(dfp), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(di), nt)
+    if rc != 0:
+        raise RuntimeError(f"gdn_oracle_backward failed with {rc}")
+    out = {"dq": np.zeros((T, HK, K)), "dk": np.zeros((T, HK, K)), "dv": np.zeros((T, HV, V)),
+           "dg": np.zeros((T, HV)), "dbeta": np.zeros((T, HV)), "d_init": np.zeros((N, HV, K, V))}
+    G = HV // HK
+    for i, (n, h) in enumerate(units):
+        a, b = o.cu[n], o.cu[n + 1]
+        r = slice(offs[i], offs[i] + lens[i])
+        out["dq"][a:b, h // G] += dq[r]
+        out["dk"][a:b, h // G] += dk[r]
+        out["dv"][a:b, h] = dv[r]
+        out["dg"][a:b, h] = dg[r]
+        out["dbeta"][a:b, h] = db[r]
+        out["d_init"][n, h] = di[i]
+    return out
 
 
 def rel_l2(x, ref) -> float:

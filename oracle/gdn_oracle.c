@@ -212,3 +212,175 @@ int gdn_oracle_run(const gdn_oracle_problem *p, int32_t n_units, const int32_t *
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Backward (the "Linear Attention" page: every variant has a full backward; the gradients
+ * of q, k, v, g, beta and the initial state).  Reverse-mode differentiation of the token
+ * step above, with S_prev the state before token t, a = exp(g_t) and the normalised rows
+ * q^, k^:
+ *     S' = a S_prev,   u = v - S'^T k^,   S = S' + beta k^ u^T,   o = scale S^T q^
+ * Going back from dS (the gradient of the state after token t, starting at d_final):
+ *     dS     += scale q^ do^T          dq^    = scale S do
+ *     dbeta   = k^T dS u               du     = beta dS^T k^      dv = du
+ *     dk^     = beta dS u - S' du      dS'    = dS - k^ du^T
+ *     dg      = a (S_prev . dS')       dS_prev = a dS'
+ * and through x^ = x / sqrt(sum x^2 + eps):  dx = r (dx^ - x^ (x^ . dx^)), r = 1 / sqrt(..).
+ * The states after every token are kept from a forward pass over the unit.
+ */
+static int run_unit_bwd(const gdn_oracle_problem *p, int32_t seq, int32_t head, const double *d_o,
+                        const double *d_final, double *dq, double *dk, double *dv, double *dg,
+                        double *dbeta, double *d_init)
+{
+    const int K = p->head_dim_k, V = p->head_dim_v;
+    const int HK = p->num_qk_heads, HV = p->num_v_heads;
+    const int hk = head / (HV / HK);
+    const int64_t t0 = p->cu_seqlens[seq], len = p->cu_seqlens[seq + 1] - t0;
+    const int64_t KV = (int64_t)K * V;
+
+    double *St = (double *)malloc(sizeof(double) * (size_t)((len + 1) * KV));   /* state after token i - 1 */
+    double *qh = (double *)malloc(sizeof(double) * (size_t)(len * K + 1));
+    double *kh = (double *)malloc(sizeof(double) * (size_t)(len * K + 1));
+    double *rq = (double *)malloc(sizeof(double) * (size_t)(len + 1));
+    double *rk = (double *)malloc(sizeof(double) * (size_t)(len + 1));
+    double *dS = (double *)calloc((size_t)KV, sizeof(double));
+    double *Sp = (double *)malloc(sizeof(double) * (size_t)KV);
+    double *vv = (double *)malloc(sizeof(double) * (size_t)V);
+    double *u = (double *)malloc(sizeof(double) * (size_t)V);
+    double *du = (double *)malloc(sizeof(double) * (size_t)V);
+    double *dqh = (double *)malloc(sizeof(double) * (size_t)K);
+    double *dkh = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!St || !qh || !kh || !rq || !rk || !dS || !Sp || !vv || !u || !du || !dqh || !dkh) {
+        free(St); free(qh); free(kh); free(rq); free(rk); free(dS); free(Sp); free(vv); free(u); free(du);
+        free(dqh); free(dkh);
+        return -1;
+    }
+
+    /* forward over the unit, keeping every state */
+    if (p->initial_state) {
+        const float *s0 = p->initial_state + ((int64_t)seq * HV + head) * KV;
+        for (int64_t i = 0; i < KV; ++i) St[i] = (double)s0[i];
+    } else {
+        memset(St, 0, sizeof(double) * (size_t)KV);
+    }
+    for (int64_t i = 0; i < len; ++i) {
+        const int64_t t = t0 + i;
+        double *qi = qh + i * K, *ki = kh + i * K;
+        load_row(p->q, t, HK, hk, K, qi);
+        load_row(p->k, t, HK, hk, K, ki);
+        rq[i] = rk[i] = 1.0;
+        if (p->l2norm) {
+            double sq = 0.0, sk = 0.0;
+            for (int c = 0; c < K; ++c) { sq += qi[c] * qi[c]; sk += ki[c] * ki[c]; }
+            rq[i] = 1.0 / sqrt(sq + GDN_ORACLE_L2_EPS);
+            rk[i] = 1.0 / sqrt(sk + GDN_ORACLE_L2_EPS);
+            for (int c = 0; c < K; ++c) { qi[c] *= rq[i]; ki[c] *= rk[i]; }
+        }
+        const double a = exp((double)p->g[t * HV + head]), b = (double)p->beta[t * HV + head];
+        const double *S0 = St + i * KV;
+        double *S1 = St + (i + 1) * KV;
+        load_row(p->v, t, HV, head, V, vv);
+        for (int64_t e = 0; e < KV; ++e) S1[e] = a * S0[e];
+        for (int j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < K; ++c) acc += S1[(int64_t)c * V + j] * ki[c];
+            u[j] = vv[j] - acc;
+        }
+        for (int c = 0; c < K; ++c)
+            for (int j = 0; j < V; ++j) S1[(int64_t)c * V + j] += b * ki[c] * u[j];
+    }
+
+    /* backward */
+    if (d_final) memcpy(dS, d_final, sizeof(double) * (size_t)KV);
+    for (int64_t i = len - 1; i >= 0; --i) {
+        const int64_t t = t0 + i;
+        const double *qi = qh + i * K, *ki = kh + i * K;
+        const double a = exp((double)p->g[t * HV + head]), b = (double)p->beta[t * HV + head];
+        const double *S0 = St + i * KV, *S1 = St + (i + 1) * KV;
+        /* recompute S' and u */
+        load_row(p->v, t, HV, head, V, vv);
+        for (int64_t e = 0; e < KV; ++e) Sp[e] = a * S0[e];
+        for (int j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < K; ++c) acc += Sp[(int64_t)c * V + j] * ki[c];
+            u[j] = vv[j] - acc;
+        }
+        /* output */
+        const double *doi = d_o ? d_o + i * V : NULL;
+        for (int c = 0; c < K; ++c) {
+            double acc = 0.0;
+            if (doi)
+                for (int j = 0; j < V; ++j) acc += S1[(int64_t)c * V + j] * doi[j];
+            dqh[c] = p->scale * acc;
+        }
+        if (doi)
+            for (int c = 0; c < K; ++c)
+                for (int j = 0; j < V; ++j) dS[(int64_t)c * V + j] += p->scale * qi[c] * doi[j];
+        /* delta-rule update */
+        double db = 0.0;
+        for (int c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < V; ++j) acc += dS[(int64_t)c * V + j] * u[j];
+            db += ki[c] * acc;
+            dkh[c] = b * acc;
+        }
+        for (int j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < K; ++c) acc += dS[(int64_t)c * V + j] * ki[c];
+            du[j] = b * acc;
+        }
+        for (int c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < V; ++j) acc += Sp[(int64_t)c * V + j] * du[j];
+            dkh[c] -= acc;
+        }
+        for (int c = 0; c < K; ++c)
+            for (int j = 0; j < V; ++j) dS[(int64_t)c * V + j] -= ki[c] * du[j];
+        /* decay */
+        double da = 0.0;
+        for (int64_t e = 0; e < KV; ++e) da += S0[e] * dS[e];
+        for (int64_t e = 0; e < KV; ++e) dS[e] *= a;
+        /* outputs of this token, through the row norms */
+        double pq = 0.0, pk = 0.0;
+        for (int c = 0; c < K; ++c) { pq += qi[c] * dqh[c]; pk += ki[c] * dkh[c]; }
+        for (int c = 0; c < K; ++c) {
+            dq[i * K + c] = p->l2norm ? rq[i] * (dqh[c] - qi[c] * pq) : dqh[c];
+            dk[i * K + c] = p->l2norm ? rk[i] * (dkh[c] - ki[c] * pk) : dkh[c];
+        }
+        for (int j = 0; j < V; ++j) dv[i * V + j] = du[j];
+        dg[i] = a * da;
+        dbeta[i] = db;
+    }
+    memcpy(d_init, dS, sizeof(double) * (size_t)KV);
+
+    free(St); free(qh); free(kh); free(rq); free(rk); free(dS); free(Sp); free(vv); free(u); free(du);
+    free(dqh); free(dkh);
+    return 0;
+}
+
+int gdn_oracle_backward(const gdn_oracle_problem *p, int32_t n_units, const int32_t *unit_seq,
+                        const int32_t *unit_head, const int64_t *tok_offset, const double *d_o,
+                        const double *d_final, double *dq, double *dk, double *dv, double *dg,
+                        double *dbeta, double *d_init, int num_threads)
+{
+    if (!p || n_units < 0 || (n_units > 0 && (!unit_seq || !unit_head || !tok_offset))) return -2;
+    if (p->num_qk_heads <= 0 || p->num_v_heads <= 0 || p->num_v_heads % p->num_qk_heads) return -2;
+    if (p->head_dim_k <= 0 || p->head_dim_v <= 0 || !p->q || !p->k || !p->v || !p->g || !p->beta) return -2;
+    if (p->beta_logit || p->a_log || p->num_householder > 1) return -2;   /* plain inputs only */
+    if (!dq || !dk || !dv || !dg || !dbeta || !d_init) return -2;
+    for (int32_t u = 0; u < n_units; ++u) {
+        if (unit_seq[u] < 0 || unit_seq[u] >= p->num_seqs) return -2;
+        if (unit_head[u] < 0 || unit_head[u] >= p->num_v_heads) return -2;
+        if (p->cu_seqlens[unit_seq[u] + 1] < p->cu_seqlens[unit_seq[u]]) return -2;
+    }
+    const int K = p->head_dim_k, V = p->head_dim_v;
+    const int64_t KV = (int64_t)K * V;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : 1) reduction(| : failed)
+    for (int32_t u = 0; u < n_units; ++u) {
+        const int64_t r = tok_offset[u];
+        if (run_unit_bwd(p, unit_seq[u], unit_head[u], d_o ? d_o + r * V : NULL, d_final ? d_final + u * KV : NULL,
+                         dq + r * K, dk + r * K, dv + r * V, dg + r, dbeta + r, d_init + u * KV) != 0)
+            failed |= 1;
+    }
+    return failed ? -1 : 0;
+}

@@ -1,5 +1,5 @@
 /*
- * fp64 CPU oracle for the Gated DeltaNet forward and span summary.
+ * fp64 CPU oracle for the Gated DeltaNet forward, span summary and backward.
  * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
  * benchmark's CPU baseline, never by the GPU library.
  */
@@ -56,6 +56,23 @@ typedef struct {
 int gdn_oracle_run(const gdn_oracle_problem *p, int32_t n_units, const int32_t *unit_seq,
                    const int32_t *unit_head, const int64_t *o_offset, double *o,
                    double *state_out, double *transition_out, int num_threads);
+
+/*
+ * Backward of gdn_oracle_run's forward (the plain inputs: beta, the natural-log gate,
+ * n = 1), by reverse-mode differentiation of the token recurrence.  Per unit u, its
+ * len tokens at row tok_offset[u] of the packed per-unit arrays:
+ *   d_o      : [*, V] upstream gradient of o (row tok_offset[u] + i for token i), or NULL
+ *   d_final  : [n_units, K, V] upstream gradient of the final state, or NULL
+ *   dq, dk   : [*, K] gradients of the raw q and k rows of this unit's v-head (the
+ *              caller sums the v-heads that share a q/k head)
+ *   dv       : [*, V];  dg, dbeta : [*]
+ *   d_init   : [n_units, K, V] gradient of the initial state
+ * Returns 0, -1 on allocation failure, -2 on invalid arguments.
+ */
+int gdn_oracle_backward(const gdn_oracle_problem *p, int32_t n_units, const int32_t *unit_seq,
+                        const int32_t *unit_head, const int64_t *tok_offset, const double *d_o,
+                        const double *d_final, double *dq, double *dk, double *dv, double *dg,
+                        double *dbeta, double *d_init, int num_threads);
 
 #ifdef __cplusplus
 }

@@ -515,3 +515,140 @@ def test_gdp_with_one_update_is_gdn():
     a, b = Oracle(p).run_all(), Oracle(q).run_all()
     np.testing.assert_array_equal(a["o"], b["o"])
     np.testing.assert_array_equal(a["state"], b["state"])
+
+
+# ---------------------------------------------------------------------------
+# Backward (oracle.backward): pinned by torch autograd through a float64 token loop
+# (itself pinned to the C forward first), and by central differences of the C forward
+# in the fp32 inputs g, beta and the initial state.
+
+def _torch_forward(q, k, v, g, beta, s0, cu, scale, l2norm, G):
+    """float64 token recurrence in torch (differentiable), o [T, HV, V] and final states."""
+    T, HV, V = v.shape
+    K = k.shape[2]
+    o = []
+    finals = []
+    rows = [None] * T
+    for n in range(len(cu) - 1):
+        per_head = []
+        for h in range(HV):
+            S = s0[n, h]
+            for t in range(int(cu[n]), int(cu[n + 1])):
+                qt, kt = q[t, h // G], k[t, h // G]
+                if l2norm:
+                    qt = qt / torch.sqrt((qt * qt).sum() + 1e-6)
+                    kt = kt / torch.sqrt((kt * kt).sum() + 1e-6)
+                S = torch.exp(g[t, h]) * S
+                u = v[t, h] - S.T @ kt
+                S = S + beta[t, h] * torch.outer(kt, u)
+                if rows[t] is None:
+                    rows[t] = [None] * HV
+                rows[t][h] = scale * (S.T @ qt)
+            per_head.append(S)
+        finals.append(torch.stack(per_head))
+    o = torch.stack([torch.stack(r) for r in rows])
+    return o, torch.stack(finals)
+
+
+def _grad_problem(lengths=(3, 0, 6), hk=1, hv=2, dk=8, dv=4, seed=31):
+    p = custom_problem(lengths, hk=hk, hv=hv, dk=dk, dv=dv, seed=seed, with_state=True)
+    # a slower decay and smaller beta keep every term of the gradient in play
+    return dataclasses.replace(p, g=p.g / 8.0, beta=p.beta / 2.0)
+
+
+@pytest.mark.parametrize("l2norm", [True, False])
+def test_backward_matches_autograd(l2norm):
+    p = dataclasses.replace(_grad_problem(), l2norm=l2norm)
+    cu = p.cu_seqlens.tolist()
+    T, HV, V = p.v.shape
+    K, G = p.k.shape[2], p.v.shape[1] // p.k.shape[1]
+    scale = K ** -0.5
+    leaves = [x.double().requires_grad_(True) for x in (p.q, p.k, p.v, p.g, p.beta, p.state)]
+    o, fin = _torch_forward(*leaves, cu, scale, l2norm, G)
+    ref = Oracle(p).run_all()
+    # the torch loop computes the oracle's forward
+    assert np.abs(o.detach().numpy() - ref["o"]).max() < 1e-12
+    assert np.abs(fin.detach().numpy() - ref["state"]).max() < 1e-12
+    gen = torch.Generator().manual_seed(5)
+    w_o = torch.randn(o.shape, generator=gen, dtype=torch.float64)
+    w_s = torch.randn(fin.shape, generator=gen, dtype=torch.float64)
+    ((o * w_o).sum() + (fin * w_s).sum()).backward()
+    got = oracle.backward(p, d_o=w_o.numpy(), d_final=w_s.numpy())
+    for name, leaf in zip(("dq", "dk", "dv", "dg", "dbeta", "d_init"), leaves):
+        want = leaf.grad.numpy()
+        assert np.abs(got[name] - want).max() <= 1e-10 * max(1.0, np.abs(want).max()), name
+
+
+def test_backward_matches_central_differences_of_the_c_forward():
+    """d(loss)/d(g, beta, initial state) against central differences of the C oracle's
+    forward, the perturbation taken as the fp32 difference actually applied."""
+    p = _grad_problem(lengths=(5, 4), hk=1, hv=2, dk=8, dv=4, seed=32)
+    gen = np.random.default_rng(6)
+    w_o = gen.standard_normal(p.v.shape)
+    w_s = gen.standard_normal((2, 2, 8, 4))
+
+    def loss(pp):
+        r = Oracle(pp).run_all()
+        return float((r["o"] * w_o).sum() + (r["state"] * w_s).sum())
+
+    got = oracle.backward(p, d_o=w_o, d_final=w_s)
+    checks = [("g", (1, 0)), ("g", (7, 1)), ("beta", (0, 1)), ("beta", (8, 0)),
+              ("state", (0, 1, 3, 2)), ("state", (1, 0, 0, 0))]
+    for name, idx in checks:
+        base = getattr(p, name)
+        h = 1e-3 * max(1.0, abs(float(base[idx])))
+        plus, minus = base.clone(), base.clone()
+        plus[idx] = plus[idx] + h
+        minus[idx] = minus[idx] - h
+        step = float(plus[idx]) - float(minus[idx])
+        fd = (loss(dataclasses.replace(p, **{name: plus})) - loss(dataclasses.replace(p, **{name: minus}))) / step
+        key = {"g": "dg", "beta": "dbeta", "state": "d_init"}[name]
+        an = float(got[key][idx])
+        assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, idx, fd, an)
+
+
+def test_backward_catches_planted_mistakes():
+    """The autograd pin tells a correct backward from one with a sign, a transposed
+    operand or a dropped term (mistakes planted in a Python copy of the oracle's
+    backward steps, run on one unit)."""
+    p = _grad_problem(lengths=(6,), hk=1, hv=1, dk=4, dv=3, seed=33)
+    K, V = 4, 3
+    q = p.q.double()[:, 0].numpy()
+    k = p.k.double()[:, 0].numpy()
+    v = p.v.double()[:, 0].numpy()
+    g = p.g.double()[:, 0].numpy()
+    b = p.beta.double()[:, 0].numpy()
+    s0 = p.state.double()[0, 0].numpy()
+    sc = K ** -0.5
+    gen = np.random.default_rng(7)
+    w_o = gen.standard_normal((6, V))
+
+    def bwd(mistake):
+        nrm = lambda x: x / np.sqrt((x * x).sum() + 1e-6)
+        qh = [nrm(x) for x in q]
+        kh = [nrm(x) for x in k]
+        S = [s0]
+        for t in range(6):
+            Sp = np.exp(g[t]) * S[-1]
+            u = v[t] - Sp.T @ kh[t]
+            S.append(Sp + b[t] * np.outer(kh[t], u))
+        dS = np.zeros((K, V))
+        dg = np.zeros(6)
+        for t in reversed(range(6)):
+            a = np.exp(g[t])
+            Sp = a * S[t]
+            u = v[t] - Sp.T @ kh[t]
+            dS = dS + sc * np.outer(qh[t], w_o[t])
+            du = b[t] * (dS.T @ kh[t]) if mistake != "transpose" else b[t] * (dS[:V, :V] @ kh[t][:V])
+            dSp = dS - np.outer(kh[t], du) if mistake != "sign" else dS + np.outer(kh[t], du)
+            dg[t] = a * (S[t] * dSp).sum() if mistake != "drop" else 0.0 * a
+            dS = a * dSp
+        return dg
+
+    leaves = [x.double().requires_grad_(True) for x in (p.q, p.k, p.v, p.g, p.beta, p.state)]
+    o, _ = _torch_forward(*leaves, [0, 6], sc, True, 1)
+    (o[:, 0] * torch.from_numpy(w_o)).sum().backward()
+    want = leaves[3].grad.numpy()[:, 0]
+    assert np.abs(bwd(None) - want).max() < 1e-10
+    for m in ("sign", "transpose", "drop"):
+        assert np.abs(bwd(m) - want).max() > 1e-4, m
