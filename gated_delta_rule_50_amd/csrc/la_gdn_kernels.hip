@@ -441,7 +441,8 @@ __device__ __forceinline__ void vm_wait_n(int n)
 //          T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj
 //      on fp32 MFMA (16 x 16 x 4), one block per wave; the sum stays in
 //      registers, reduced over in accumulator order by the product with D_i.  T
-//      (on and below the diagonal) and A^T (above it) share one fp32 array.
+//      (on and below the diagonal) and A^T (above it) share one fp32 array; the
+//      A^T blocks are zeroed once dead, all but block column 3 of rows 0..47.
 //   4. -W (from W^T = K^T Tw^T) and U~ = (Thi + Tlo) V on bf16 MFMA, with Tw = T
 //      diag(beta 2^gam r_k) and T diag(beta) = Thi + Tlo (bf16) formed in
 //      registers; both are written from registers in the inter pass's operand
@@ -844,6 +845,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sAT[(16 * i + 4 * q + e) * TS + 16 * j + cc] = Tij[e];
                 }
+                // The A^T blocks of finished block rows are dead: the idle wave zeroes them
+                // (block (0, 1) once row 1 is done, (0, 2) and (1, 2) once row 2 is), so that
+                // above the diagonal T reads as zero in step 4 except in block column 3.
+                if (i >= 2 && wave == i) {
+                    const int zr = lane >> 2, zc = 4 * (lane & 3);
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    for (int k = 0; k < i - 1; ++k)
+                        *reinterpret_cast<lds_f32x4 *>(sAT + (16 * k + zr) * TS + 16 * (i - 1) + zc) = z;
+                }
                 if (i == 3) vm_wait<0>();   // v (this wave's share), before the last barrier
                 lds_barrier();
             }
@@ -857,7 +867,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // the diagonal (the array holds A^T there).
         {
             const int m = wave & 1, t = 32 * m + c;
-            const int tm = 32 * m + cm - 8 * hm;   // the mask below: column 16 s + e <= row t
+            // Above the diagonal the array holds zeros (the diagonal blocks from 3a, blocks
+            // (0, 1), (0, 2), (1, 2) from 3b) except for block column 3 of rows 0 .. 47, which
+            // still holds A^T: masked here by the row.
+            const bool col3 = 32 * m + cm >= 48;
             // T[t][16 s + 8 hh + e] (zero above the diagonal), times the per-column factor f
             auto trow = [&](int s, const lds_float *f, float (&o)[8]) {
                 const int s0 = 16 * s + 8 * hh;
@@ -867,7 +880,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const f32x4 f1 = *reinterpret_cast<const lds_f32x4 *>(f + s0 + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    o[e] = (16 * s + e <= tm) ? (e < 4 ? t0[e] * f0[e] : t1[e - 4] * f1[e - 4]) : 0.f;
+                    o[e] = (s < 3 || col3) ? (e < 4 ? t0[e] * f0[e] : t1[e - 4] * f1[e - 4]) : 0.f;
             };
             {
                 bf16x8 tw[4];
