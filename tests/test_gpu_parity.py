@@ -15,7 +15,7 @@ import gated_delta_rule_50_amd as la
 from oracle import Oracle, rel_l2
 from workloads import Problem, custom_problem, make_problem
 
-from gpu_helpers import TOL_O, TOL_STATE, check_fwd_full, f64, gpu_fwd, gpu_summary, note
+from gpu_helpers import TOL_O, TOL_STATE, assert_rows_close, check_fwd_full, f64, gpu_fwd, gpu_summary, note
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +127,7 @@ def test_config4_ragged_long_context_sampled():
         eo = rel_l2(o64[cu[n]:cu[n + 1], h], ro)
         es = rel_l2(f64_[n, h], rs)
         assert eo <= TOL_O and es <= TOL_STATE, (n, h, lens[n], eo, es)
+        assert_rows_close(o64[cu[n]:cu[n + 1], h], ro, TOL_O, f"o rows of unit {(n, h)}")
 
 
 def test_config5_summary_sampled():
