@@ -62,6 +62,19 @@ def assert_rows_close(x, ref, tol, what):
                            f"worst err/norm {float(np.max(err / np.maximum(nrm, 1e-30))):.3e})")
 
 
+def assert_o_state(out, fin, ref, tol_o=TOL_O, tol_s=TOL_STATE):
+    """o and final states against the oracle's: whole-tensor rel-L2 and row by row
+    (fin may be None when only o is compared)."""
+    eo = rel_l2(f64(out), ref["o"])
+    assert eo <= tol_o, f"o rel-L2 {eo:.3e} > {tol_o}"
+    assert_rows_close(f64(out), ref["o"], tol_o, "o rows")
+    if fin is not None:
+        es = rel_l2(f64(fin), ref["state"])
+        assert es <= tol_s, f"final state rel-L2 {es:.3e} > {tol_s}"
+        K, V = ref["state"].shape[-2:]
+        assert_rows_close(f64(fin).reshape(-1, K * V), ref["state"].reshape(-1, K * V), tol_s, "final states")
+
+
 def check_fwd_full(p, tol_o=TOL_O, tol_s=TOL_STATE, initial_state=True):
     """Whole-tensor rel-L2 of o and final state against the oracle, and row by row."""
     note(f"fwd full: {p.name} T={p.total_tokens} N={p.num_seqs}")

@@ -13,7 +13,7 @@ import gated_delta_rule_50_amd as la
 from oracle import Oracle, rel_l2
 from workloads import fused_problem
 
-from gpu_helpers import TOL_O, TOL_STATE, f64, note
+from gpu_helpers import TOL_O, TOL_STATE, assert_o_state, f64, note
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +30,7 @@ def check(p):
     note(f"fused fwd: {p.name} beta_sigmoid={p.beta_sigmoid} safe_gate={p.a_log is not None}")
     out, fin = fwd_fused(p)
     ref = Oracle(p).run_all()
-    eo, es = rel_l2(f64(out), ref["o"]), rel_l2(f64(fin), ref["state"])
-    assert eo <= TOL_O and es <= TOL_STATE, (eo, es)
+    assert_o_state(out, fin, ref)
     return out, fin
 
 

@@ -12,7 +12,7 @@ import gated_delta_rule_50_amd as la
 from oracle import Oracle, rel_l2
 from workloads import gdp_problem
 
-from gpu_helpers import TOL_O, TOL_STATE, f64, gpu_fwd, note
+from gpu_helpers import TOL_O, TOL_STATE, assert_o_state, f64, gpu_fwd, note
 
 pytestmark = pytest.mark.gpu
 
@@ -29,8 +29,7 @@ def check(p):
     note(f"gdp fwd: {p.name} n={p.num_householder}")
     out, fin = gdp_fwd(p)
     ref = Oracle(p).run_all()
-    eo, es = rel_l2(f64(out), ref["o"]), rel_l2(f64(fin), ref["state"])
-    assert eo <= TOL_O and es <= TOL_STATE, (eo, es)
+    assert_o_state(out, fin, ref)
     return out, fin
 
 
@@ -82,7 +81,7 @@ def test_gdp_with_fused_gate_and_beta():
                                    num_householder=2, beta_sigmoid=True, a_log=g.a_log, dt_bias=g.dt_bias)
     torch.cuda.synchronize()
     ref = Oracle(p).run_all()
-    assert rel_l2(f64(out), ref["o"]) <= TOL_O and rel_l2(f64(fin), ref["state"]) <= TOL_STATE
+    assert_o_state(out, fin, ref)
 
 
 def token_major(p, pad=8):
@@ -145,5 +144,5 @@ def test_gdp_token_major_summary_and_fused_beta():
                                    beta_sigmoid=True, num_householder=2)
     torch.cuda.synchronize()
     ref = Oracle(q).run_all()
-    assert rel_l2(f64(o_u), ref["o"]) <= TOL_O and rel_l2(f64(f_u), ref["state"]) <= TOL_STATE
+    assert_o_state(o_u, f_u, ref)
     assert torch.equal(o_t, o_u) and torch.equal(f_t, f_u)
