@@ -313,6 +313,7 @@ def main(argv=None):
                    "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
         "roofline": roof,
         "path": {"algorithmic_bytes": by, "algorithmic_flops": fl,
+                 "token_heads_per_s": value * HV,
                  "host_us_per_call": 1e6 * (h1 - h0) / n_host,
                  "hbm_frac": by / step_s / (HBM_PEAK_GBS * 1e9),
                  "mfma_frac": fl / step_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
