@@ -146,3 +146,19 @@ def test_gdp_token_major_summary_and_fused_beta():
     ref = Oracle(q).run_all()
     assert_o_state(o_u, f_u, ref)
     assert torch.equal(o_t, o_u) and torch.equal(f_t, f_u)
+
+
+@pytest.mark.parametrize("nh", [5, 63, 64])
+def test_gdp_token_major_many_updates(nh):
+    """Chunks that start at every phase of a token (n = 5, 63) or always at a token's
+    first update (n = 64): token-major equal to update-major bit for bit, both against
+    the oracle."""
+    p = gdp_problem((1, 2, 7, 13), nh, hk=1, hv=2, dk=64, dv=128, seed=101, with_state=True, g_div=8.0,
+                    beta_div=4.0)
+    out_u, fin_u = check(p)
+    g = p.to("cuda")
+    k, v, beta = token_major(p)
+    note(f"gdp token-major fwd n={nh}")
+    out, fin, _ = la.la_gdn_fwd_ex(g.q, k, v, g.g, beta, g.cu_seqlens, initial_state=g.state, num_householder=nh)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_u) and torch.equal(fin, fin_u)
