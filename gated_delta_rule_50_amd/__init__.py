@@ -88,6 +88,7 @@ class Options(ctypes.Structure):
         ("k_stride_update", ctypes.c_int64),
         ("v_stride_update", ctypes.c_int64),
         ("beta_stride_update", ctypes.c_int64),
+        ("cu_seqlens_int64", ctypes.c_int32),
     ]
 
 
@@ -207,7 +208,13 @@ def la_gdn_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final
                output_final_state: bool = True, l2norm: bool = True, scale: Optional[float] = None,
                workspace: Optional[torch.Tensor] = None, stream=None
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Gated DeltaNet forward on the GPU; returns (out, final_state or None)."""
+    """Gated DeltaNet forward on the GPU; returns (out, final_state or None).
+    cu_seqlens is int32 or int64 (int64 goes through la_gdn_fwd_ex)."""
+    if cu_seqlens.dtype == torch.int64:
+        out, final_state, _ = la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state,
+                                            output_final_state, l2norm, scale, workspace=workspace,
+                                            stream=stream)
+        return out, final_state
     lib = load_library()
     N = cu_seqlens.numel() - 1
     T, HV, V = v.shape
@@ -228,7 +235,11 @@ def la_gdn_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final
 def la_gdn_summary(k, v, g, beta, cu_seqlens, start_state=None, end_state=None, transition=None,
                    l2norm: bool = True, workspace: Optional[torch.Tensor] = None, stream=None
                    ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Span summary on the GPU; returns (end_state, transition)."""
+    """Span summary on the GPU; returns (end_state, transition).  cu_seqlens is int32
+    or int64 (int64 goes through la_gdn_summary_ex)."""
+    if cu_seqlens.dtype == torch.int64:
+        return la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state, end_state, transition, l2norm,
+                                 workspace=workspace, stream=stream)
     lib = load_library()
     N = cu_seqlens.numel() - 1
     HV, V = v.shape[1], v.shape[2]
@@ -253,7 +264,7 @@ def _options(beta: torch.Tensor, beta_sigmoid: bool, a_log, dt_bias) -> Options:
     for name, t in (("a_log", a_log), ("dt_bias", dt_bias)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 [HV] tensor")
-    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0, 1, 0, 0, 0, 0)
+    return Options(int(bool(beta_sigmoid)), _ptr(a_log), _ptr(dt_bias), 0, 0, None, 0, 1, 0, 0, 0, 0, 0)
 
 
 def token_major_strides(opts: Options, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor):
@@ -266,8 +277,14 @@ def token_major_strides(opts: Options, k: torch.Tensor, v: torch.Tensor, beta: t
         opts.beta_stride_update = beta.stride(1)
 
 
+def _cu_int64(cu_seqlens: torch.Tensor) -> int:
+    if cu_seqlens.dtype not in (torch.int32, torch.int64) or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 or int64 tensor")
+    return int(cu_seqlens.dtype == torch.int64)
+
+
 def la_gdn_workspace_bytes_ex(desc: Desc, is_summary: bool = False, num_householder: int = 1) -> int:
-    opts = Options(0, None, None, 0, 0, None, 0, int(num_householder), 0, 0, 0, 0)
+    opts = Options(0, None, None, 0, 0, None, 0, int(num_householder), 0, 0, 0, 0, 0)
     n = load_library().la_gdn_workspace_bytes_ex(ctypes.byref(desc), int(bool(is_summary)), ctypes.byref(opts))
     if n == 0:
         raise LaError(LA_ERR_INVALID_ARGUMENT, la_last_error_message())
@@ -294,6 +311,7 @@ def la_gdn_fwd_ex(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, fi
     opts = _options(beta, beta_sigmoid, a_log, dt_bias)
     opts.num_householder = int(num_householder)
     token_major_strides(opts, k, v, beta)
+    opts.cu_seqlens_int64 = _cu_int64(cu_seqlens)
     N = cu_seqlens.numel() - 1
     T = q.shape[0]
     HV, V = v.shape[-2], v.shape[-1]
@@ -333,6 +351,7 @@ def la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state=None, end_state=Non
     opts = _options(beta, beta_sigmoid, a_log, dt_bias)
     opts.num_householder = int(num_householder)
     token_major_strides(opts, k, v, beta)
+    opts.cu_seqlens_int64 = _cu_int64(cu_seqlens)
     N = cu_seqlens.numel() - 1
     HV, V = v.shape[-2], v.shape[-1]
     K = k.shape[-1]

@@ -369,7 +369,9 @@ la::Prob make_prob(const la_gdn_desc *d, int l2norm)
     return p;
 }
 
-la_status launch(const la::Prob &p, void *workspace, size_t workspace_bytes, bool summary, hipStream_t stream)
+// cu64: cu_seqlens given as int64 (p.cu is then replaced by the workspace's int32 copy).
+la_status launch(la::Prob p, void *workspace, size_t workspace_bytes, bool summary, hipStream_t stream,
+                 const int64_t *cu64 = nullptr)
 {
     const la::WsLayout L = la::workspace_layout(p.N, p.T * p.nh, p.HK, p.HV, p.K, p.V, summary);
     if (p.N == 0) return LA_OK;  // nothing to compute and nothing to write
@@ -379,7 +381,15 @@ la_status launch(const la::Prob &p, void *workspace, size_t workspace_bytes, boo
     if (workspace_bytes < L.total)
         return fail(LA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
     const la::Ws w = la::carve_workspace(workspace, L, summary);
-    const hipError_t e = la::run_pipeline(p, w, summary, stream, current_hook());
+    const la::LaunchHook *hook = current_hook();
+    if (cu64) {
+        if (hook) hook->before(LA_KERNEL_SCHED, stream, hook->ctx);
+        const hipError_t ec = la::convert_cu64(cu64, w.cu32, p.N + 1, stream);
+        if (hook) hook->after(LA_KERNEL_SCHED, stream, hook->ctx);
+        if (ec != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(ec));
+        p.cu = w.cu32;
+    }
+    const hipError_t e = la::run_pipeline(p, w, summary, stream, hook);
     if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return LA_OK;
 }
@@ -407,6 +417,7 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     L.PF = take(summary ? 0 : (size_t)(C * HV) * 6 * la::kFrag);
     L.UF = take((size_t)(C * HV) * 64 * V * 4);           // 64 x V fp32
     L.SC = take((size_t)(C * HV) * la::kScalars * 4);
+    L.cu32 = take(sizeof(int32_t) * (size_t)(N + 1));
     L.total = off;
     return L;
 }
@@ -423,6 +434,7 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.PF = summary ? nullptr : reinterpret_cast<uint4 *>(b + L.PF);
     w.UF = reinterpret_cast<float4 *>(b + L.UF);
     w.SC = reinterpret_cast<float *>(b + L.SC);
+    w.cu32 = reinterpret_cast<int32_t *>(b + L.cu32);
     return w;
 }
 
@@ -455,7 +467,7 @@ la_status la_gdn_fwd(const la_gdn_desc *desc, const void *q, const void *k, cons
 }
 
 la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
-                           const void *beta, const int32_t *cu_seqlens, const float *initial_state, void *out,
+                           const void *beta, const void *cu_seqlens, const float *initial_state, void *out,
                            float *final_state, int l2norm, const la_gdn_options *fusion, void *workspace,
                            size_t workspace_bytes, hipStream_t stream)
 {
@@ -470,8 +482,10 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
+    const bool cu64 = fusion && fusion->cu_seqlens_int64;
     if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
-    if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & (cu64 ? 7u : 3u)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not %d-byte aligned", cu64 ? 8 : 4);
     if ((st = check_f32("initial_state", initial_state, false)) != LA_OK) return st;
     if ((st = check_f32("final_state", final_state, false)) != LA_OK) return st;
     if ((st = check_checkpoints(fusion, false)) != LA_OK) return st;
@@ -483,12 +497,13 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     p.g = g;
     set_beta_and_fusion(p, beta, fusion);
     set_update_strides(p, fusion);
-    p.cu = cu_seqlens;
+    p.cu = cu64 ? nullptr : static_cast<const int32_t *>(cu_seqlens);
     p.s0 = initial_state;
     p.o = static_cast<__bf16 *>(out);
     p.sT = final_state;
     p.trans = nullptr;
-    return launch(p, workspace, workspace_bytes, false, stream);
+    return launch(p, workspace, workspace_bytes, false, stream,
+                  cu64 ? static_cast<const int64_t *>(cu_seqlens) : nullptr);
 }
 
 la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, const float *g, const float *beta,
@@ -500,7 +515,7 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
 }
 
 la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
-                               const void *beta, const int32_t *cu_seqlens, const float *start_state,
+                               const void *beta, const void *cu_seqlens, const float *start_state,
                                float *end_state, float *transition, int l2norm, const la_gdn_options *fusion,
                                void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
@@ -513,8 +528,10 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
     if ((st = check_kvb(d, k, v, fusion)) != LA_OK) return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
+    const bool cu64 = fusion && fusion->cu_seqlens_int64;
     if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
-    if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & (cu64 ? 7u : 3u)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not %d-byte aligned", cu64 ? 8 : 4);
     if ((st = check_f32("start_state", start_state, false)) != LA_OK) return st;
     if ((st = check_f32("end_state", end_state, true)) != LA_OK) return st;
     if ((st = check_f32("transition", transition, true)) != LA_OK) return st;
@@ -527,12 +544,13 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
     p.g = g;
     set_beta_and_fusion(p, beta, fusion);
     set_update_strides(p, fusion);
-    p.cu = cu_seqlens;
+    p.cu = cu64 ? nullptr : static_cast<const int32_t *>(cu_seqlens);
     p.s0 = start_state;
     p.o = nullptr;
     p.sT = end_state;
     p.trans = transition;
-    return launch(p, workspace, workspace_bytes, true, stream);
+    return launch(p, workspace, workspace_bytes, true, stream,
+                  cu64 ? static_cast<const int64_t *>(cu_seqlens) : nullptr);
 }
 
 int32_t la_gdn_device_status(const void *workspace, hipStream_t stream)

@@ -62,11 +62,12 @@ struct Ws {
     float4 *UF;        // [chunk, HV][V/32][token tile][4]  U~ = T diag(beta) V, fp32 accumulator tiles
     float *SC;         // [chunk, HV, kScalars]  per token: d = 2^(gam_n - gam) r_k at 0,
                        // sq = scale r_q 2^gam at 64 (forward); gl = 2^gam_n at 192
+    int32_t *cu32;     // [N + 1]  int32 copy of int64 cu_seqlens (when given as int64)
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, total;
+    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, cu32, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
                           bool summary);
@@ -78,6 +79,10 @@ struct LaunchHook {
     void (*after)(int kernel_id, hipStream_t s, void *ctx);
     void *ctx;
 };
+
+// Copies int64 cu_seqlens [n] to int32 on `stream`; an entry outside 0 .. INT32_MAX
+// becomes -1, which the scheduler's validation reports as malformed cu_seqlens.
+hipError_t convert_cu64(const int64_t *src, int32_t *dst, int n, hipStream_t stream);
 
 // Enqueues the whole pipeline (scheduler, intra, inter) on `stream`.
 hipError_t run_pipeline(const Prob &p, const Ws &w, bool summary, hipStream_t stream,

@@ -21,6 +21,7 @@
 // exponent above is <= 0, so no factor can overflow.
 //
 // The kernels, all on the caller's stream:
+//   k_cu64      (int64 cu_seqlens only) the int32 copy the other kernels read
 //   k_sched     one workgroup, for more than 64 sequences: validates cu_seqlens,
 //               builds the chunk table and the longest-first order of sequences
 //               (for at most 64, every wave of k_intra maps its own chunks from
@@ -1549,6 +1550,24 @@ template <int K, int V>
 __global__ __launch_bounds__(256) void k_inter_sum_gdp(Prob p, Ws w)
 {
     inter_body<K, V, true, false, true>(p, w);
+}
+
+// int64 cu_seqlens to the int32 copy the other kernels read (the "Linear Attention"
+// page lists int64 offsets beside int32); entries outside the int32 range become -1,
+// which the scheduler's validation reports as malformed.
+__global__ __launch_bounds__(256) void k_cu64(const int64_t *src, int32_t *dst, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+        const int64_t v = src[i];
+        dst[i] = (v < 0 || v > INT32_MAX) ? -1 : (int32_t)v;
+    }
+}
+
+hipError_t convert_cu64(const int64_t *src, int32_t *dst, int n, hipStream_t stream)
+{
+    if (n > 0) hipLaunchKernelGGL(k_cu64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, dst, n);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -184,6 +184,13 @@ la_status la_gdn_summary(const la_gdn_desc *desc, const void *k, const void *v, 
  *                 rows; otherwise LA_ERR_INVALID_ARGUMENT.  Token or update strides of
  *                 2^23 elements or more (update-major: the row stride times n) are
  *                 declined with LA_ERR_UNSUPPORTED.
+ *
+ * Offsets (the "Linear Attention" page lists int32 and int64 cu_seqlens):
+ *   cu_seqlens_int64  nonzero: cu_seqlens points at int64 [N + 1] (8-byte aligned,
+ *                 else LA_ERR_INVALID_ARGUMENT); a first kernel copies it to int32 in
+ *                 the workspace, and an entry outside 0 .. 2^31 - 1 makes the call
+ *                 one with malformed cu_seqlens (device status, nothing written).
+ *                 Zero: int32 as for la_gdn_fwd.
  */
 typedef struct {
     int32_t beta_sigmoid;
@@ -198,6 +205,7 @@ typedef struct {
     int64_t k_stride_update;
     int64_t v_stride_update;
     int64_t beta_stride_update;
+    int32_t cu_seqlens_int64;
 } la_gdn_options;
 
 /* Workspace bytes for la_gdn_fwd_ex / la_gdn_summary_ex with these options (NULL:
@@ -207,18 +215,19 @@ size_t la_gdn_workspace_bytes_ex(const la_gdn_desc *desc, int is_summary, const 
 /*
  * la_gdn_fwd and la_gdn_summary with the options above (options NULL: the
  * plain calls).  Arguments, errors and outputs are those of the plain calls;
- * `beta` is bf16 or fp32 as options->beta_sigmoid says.  A dt_bias without
+ * `beta` is bf16 or fp32 as options->beta_sigmoid says, and `cu_seqlens` int32 or
+ * int64 as options->cu_seqlens_int64 says.  A dt_bias without
  * a_log, a misaligned a_log, dt_bias, beta or checkpoints, or a series without
  * a buffer, is LA_ERR_INVALID_ARGUMENT; a series requested from the summary,
  * or every n that is not a multiple of 64, is LA_ERR_UNSUPPORTED.
  */
 la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, const void *v,
-                        const float *g, const void *beta, const int32_t *cu_seqlens,
+                        const float *g, const void *beta, const void *cu_seqlens,
                         const float *initial_state, void *out, float *final_state, int l2norm,
                         const la_gdn_options *options, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
 la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *v, const float *g,
-                            const void *beta, const int32_t *cu_seqlens, const float *start_state,
+                            const void *beta, const void *cu_seqlens, const float *start_state,
                             float *end_state, float *transition, int l2norm,
                             const la_gdn_options *options, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);

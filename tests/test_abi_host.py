@@ -306,3 +306,19 @@ def test_token_major_descriptor_from_views():
         1, HK * K, HV * V, HV)
     with pytest.raises(ValueError, match="num_householder"):
         la.make_desc(k, v, g, beta, 1, q=q, num_householder=2)
+
+
+def test_int64_offsets_alignment_checked(lib):
+    """int64 cu_seqlens must be 8-byte aligned (int32 ones 4-byte)."""
+    d = _desc()
+    a = _fwd_args(cu=(1 << 20) + 4)
+    o = la.Options()
+    o.cu_seqlens_int64 = 1
+    rc = lib.la_gdn_fwd_ex(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["out"],
+                           a["fin"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    assert rc == la.LA_ERR_INVALID_ARGUMENT and "8-byte aligned" in la.la_last_error_message()
+    rc = lib.la_gdn_summary_ex(ctypes.byref(d), a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["fin"],
+                               a["out"], 1, ctypes.byref(o), a["ws"], a["wsb"], None)
+    assert rc == la.LA_ERR_INVALID_ARGUMENT and "8-byte aligned" in la.la_last_error_message()
+    with pytest.raises(ValueError, match="int32 or int64"):
+        la._cu_int64(torch.zeros(3, dtype=torch.int16))
