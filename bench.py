@@ -51,6 +51,8 @@ VARIANTS = {
     "series64": "with the state series every 64 tokens (bf16 rows)",
     "series64-fp32": "with the state series every 64 tokens (fp32 rows)",
     "gdp2": "Gated Delta Product, 2 Householder updates per token (k, v, beta update-major)",
+    "summary-bwd": "the span summary's mirror for the state gradient (la_gdn_summary_bwd: output and "
+                   "end-state gradients in, start-state gradient out)",
 }
 
 
@@ -163,7 +165,11 @@ def main(argv=None):
     variant = args.variant
     prob = make_problem(wl) if wl == 2 else make_problem(wl, device="cuda")
     summary = prob.summary
-    if variant != "plain" and summary:
+    if variant == "summary-bwd":
+        if not summary:
+            print("--variant summary-bwd applies to the span summary workload (5)", file=sys.stderr)
+            return 2
+    elif variant != "plain" and summary:
         print("--variant applies to the forward workloads (1 to 4)", file=sys.stderr)
         return 2
     lengths = prob.lengths()
@@ -195,6 +201,12 @@ def main(argv=None):
 
     copies = max(1, args.copies) if by0 < (1 << 30) else 1
     sets = []
+    bwd_in = None
+    if variant == "summary-bwd":
+        gen = torch.Generator(device="cuda").manual_seed(wl)
+        bwd_in = (torch.randn((T, HV, V), generator=gen, device=dev).to(torch.bfloat16),
+                  torch.randn((N, HV, K, V), generator=gen, device=dev))
+        prob = dataclasses.replace(prob, q=torch.randn(prob.k.shape, generator=gen, device=dev).to(torch.bfloat16))
     for ic in range(copies):
         g = fresh_copy(prob)
         if summary:
@@ -211,7 +223,10 @@ def main(argv=None):
 
     def step(i):
         g, out, fin, ws, ck = sets[i % len(sets)]
-        if summary:
+        if variant == "summary-bwd":
+            la.la_gdn_summary_bwd(g.q, g.k, g.g, g.beta, g.cu_seqlens, bwd_in[0], bwd_in[1], d_start_state=fin,
+                                  workspace=ws, stream=stream)
+        elif summary:
             la.la_gdn_summary(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state, end_state=fin,
                               transition=out, l2norm=True, workspace=ws, stream=stream)
         elif variant == "plain":
@@ -277,12 +292,17 @@ def main(argv=None):
     value = T * args.steps / elapsed
 
     by, fl = algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, True, **count_kw)
+    if variant == "summary-bwd":
+        # q, k (bf16 per q/k head), d_out (bf16), g, beta per value head; the end- and
+        # start-state gradients; per token-head 6 K V flops (X, k^T X and the update)
+        by = T * (2 * HK * K * 2 + HV * V * 2 + 2 * HV * 4) + 2 * N * HV * K * V * 4
+        fl = 6 * T * HV * K * V
     inter_us = kern["k_inter"]["avg_us"]
     # the dominant kernel's roofline: the path's algorithmic bytes (one launch
     # processes every token-head of the batch) over that kernel's launch time;
     # the span summary sits at the ridge and is priced on bf16 MFMA flops
     step_s = ms_per_step * 1e-3
-    if summary:
+    if summary and variant != "summary-bwd":
         roof = {"bound": "mfma", "kernel": "k_inter", "achieved": fl / (inter_us * 1e-6) / 1e12,
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:

@@ -46,7 +46,7 @@ LA_KERNEL_COUNT = 3
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
     "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex", "la_gdn_workspace_bytes_ex",
-    "la_gdn_device_status",
+    "la_gdn_summary_bwd", "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
 
@@ -120,6 +120,8 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
     lib.la_gdn_summary_ex.restype = ctypes.c_int
     lib.la_gdn_summary_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
+    lib.la_gdn_summary_bwd.restype = ctypes.c_int
+    lib.la_gdn_summary_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     lib.la_gdn_device_status.restype = i32
     lib.la_gdn_device_status.argtypes = [vp, vp]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -368,6 +370,29 @@ def la_gdn_summary_ex(k, v, g, beta, cu_seqlens, start_state=None, end_state=Non
                                  int(bool(l2norm)), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
     return end_state, transition
+
+
+def la_gdn_summary_bwd(q, k, g, beta, cu_seqlens, d_out, d_end_state=None, d_start_state=None,
+                       l2norm: bool = True, scale: Optional[float] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The span summary's mirror for the state gradient: dL/dS_start for the output
+    gradients d_out [T, HV, V] (bf16) and d_end_state [N, HV, K, V] (fp32, None: zeros)."""
+    lib = load_library()
+    N = cu_seqlens.numel() - 1
+    HV, V = d_out.shape[1], d_out.shape[2]
+    K = k.shape[2]
+    if d_out.dtype != torch.bfloat16 or cu_seqlens.dtype != torch.int32:
+        raise ValueError("d_out must be bf16 and cu_seqlens int32")
+    if d_start_state is None:
+        d_start_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=d_out.device)
+    # the descriptor's v strides are unused here; d_out takes the o strides
+    desc = make_desc(k, d_out, g, beta, N, q=q, out=d_out, scale=scale)
+    if workspace is None:
+        workspace = alloc_workspace(desc, True, d_out.device)
+    _check(lib.la_gdn_summary_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                  _ptr(d_out), _ptr(d_end_state), _ptr(d_start_state), int(bool(l2norm)),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+    return d_start_state
 
 
 def la_gdn_device_status(workspace: torch.Tensor, stream=None) -> int:

@@ -553,6 +553,55 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
                   cu64 ? static_cast<const int64_t *>(cu_seqlens) : nullptr);
 }
 
+la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void *k, const float *g,
+                             const float *beta, const int32_t *cu_seqlens, const void *d_out,
+                             const float *d_end_state, float *d_start_state, int l2norm, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream)
+{
+    g_error.clear();
+    la_status st = check_desc(desc);
+    if (st != LA_OK) return st;
+    const la_gdn_desc &d = *desc;
+    const int64_t T = d.total_tokens;
+    if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
+    if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
+    if ((st = check_thd("d_out", d_out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK)
+        return st;
+    if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if ((st = check_beta_and_fusion(beta, d, nullptr)) != LA_OK) return st;
+    if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+    if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((st = check_f32("d_end_state", d_end_state, false)) != LA_OK) return st;
+    if ((st = check_f32("d_start_state", d_start_state, true)) != LA_OK) return st;
+
+    la::Prob p = make_prob(desc, l2norm);
+    p.q = static_cast<const __bf16 *>(q);
+    p.k = static_cast<const __bf16 *>(k);
+    p.g = g;
+    p.beta = beta;
+    p.cu = cu_seqlens;
+    if (p.N == 0) return LA_OK;
+    // the status word, then the row norms (2 T HK floats): within the summary's workspace
+    const size_t need = 256 + sizeof(float) * 2 * (size_t)(T * d.num_qk_heads);
+    const size_t have_min = la::workspace_layout(p.N, p.T, p.HK, p.HV, p.K, p.V, true).total;
+    if (!workspace) return fail(LA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < have_min || workspace_bytes < need)
+        return fail(LA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                    have_min > need ? have_min : need);
+    la::SbwdArgs a{};
+    a.p = &p;
+    a.d_out = static_cast<const __bf16 *>(d_out);
+    a.d_end = d_end_state;
+    a.d_start = d_start_state;
+    a.status = static_cast<int32_t *>(workspace);
+    a.rn = reinterpret_cast<float *>(static_cast<char *>(workspace) + 256);
+    const hipError_t e = la::run_summary_bwd(a, stream, current_hook());
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
 int32_t la_gdn_device_status(const void *workspace, hipStream_t stream)
 {
     if (!workspace) {

@@ -84,6 +84,19 @@ struct LaunchHook {
 // becomes -1, which the scheduler's validation reports as malformed cu_seqlens.
 hipError_t convert_cu64(const int64_t *src, int32_t *dst, int n, hipStream_t stream);
 
+// Span summary's state-gradient mirror: dS_start from the span's output gradients and
+// dS_end.  `rn` holds 2 T HK floats of workspace (the row norms), `status` the device
+// status word.
+struct SbwdArgs {
+    const Prob *p;                    // q, k, g, beta, cu, strides, scale, l2norm (o strides: d_out)
+    const __bf16 *d_out;              // [T, HV, V] with the o strides
+    const float *d_end;               // [N, HV, K, V] or null (zeros)
+    float *d_start;                   // [N, HV, K, V]
+    float *rn;                        // [T HK][2] inverse norms of the q and k rows
+    int32_t *status;
+};
+hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t stream, const LaunchHook *hook);
+
 // Enqueues the whole pipeline (scheduler, intra, inter) on `stream`.
 hipError_t run_pipeline(const Prob &p, const Ws &w, bool summary, hipStream_t stream,
                         const LaunchHook *hook);

@@ -22,6 +22,8 @@
 //
 // The kernels, all on the caller's stream:
 //   k_cu64      (int64 cu_seqlens only) the int32 copy the other kernels read
+//   k_sbwd_prep, k_sbwd  the summary's mirror for the state gradient (row norms and
+//               cu_seqlens validation, then the reverse recurrence token by token)
 //   k_sched     one workgroup, for more than 64 sequences: validates cu_seqlens,
 //               builds the chunk table and the longest-first order of sequences
 //               (for at most 64, every wave of k_intra maps its own chunks from
@@ -1618,6 +1620,122 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// The span summary's mirror for the state gradient (the "Linear Attention" page,
+// "Summaries": <op>_summary_bwd).  With L = sum_t <do_t, o_t> + <dS_end, S_end> and the
+// step M_t = exp(g_t) (I - beta_t k_t k_t^T) (symmetric), the gradient of the start state
+// follows the reverse recurrence
+//     D <- dS_end;   for t = last .. first:  X = D + scale q_t do_t^T,  D = M_t X
+// (q, k normalised), dS_start = D.  First version: token by token, one workgroup per
+// (sequence, value head, 32 value columns), D in registers (K / 8 rows per thread), and
+// k^T X reduced over the rows through LDS (one barrier per token).
+
+// Inverse row norms of q and k (one wave per (token, q/k head) row), and, in the last
+// workgroup, the validation of cu_seqlens into the status word.
+template <int K>
+__global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, const float *unused, float *rn, int32_t *status)
+{
+    (void)unused;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (blockIdx.x == gridDim.x - 1) {
+        if (wv != 0) return;
+        bool bad = false;
+        for (int i = lane; i <= p.N; i += 64) {
+            const int c = p.cu[i];
+            if (i == 0 && c != 0) bad = true;
+            if (i == p.N && (int64_t)c != p.T) bad = true;
+            if (i < p.N && p.cu[i + 1] < c) bad = true;
+        }
+        const bool any = __ballot(bad) != 0;
+        if (lane == 0) status[0] = any ? LA_DEVICE_BAD_CU_SEQLENS : LA_DEVICE_OK;
+        return;
+    }
+    const int64_t row = (int64_t)blockIdx.x * 4 + wv;   // token row * HK + hk
+    if (row >= p.T * p.HK) return;
+    const int64_t t = row / p.HK, hk = row % p.HK;
+    float sq = 0.f, sk = 0.f;
+    for (int e = lane; e < K; e += 64) {
+        const float qv = bf2f(p.q[t * p.qst + hk * p.qsh + e]);
+        const float kv = bf2f(p.k[t * p.kst + hk * p.ksh + e]);
+        sq += qv * qv;
+        sk += kv * kv;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        sq += __shfl_xor(sq, off, 64);
+        sk += __shfl_xor(sk, off, 64);
+    }
+    if (lane == 0) {
+        rn[2 * row] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+        rn[2 * row + 1] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+    }
+}
+
+template <int K>
+__global__ __launch_bounds__(256) void k_sbwd(Prob p, const __bf16 *d_out, const float *d_end, float *d_start,
+                                              const float *rn, const int32_t *status)
+{
+    constexpr int R = K / 8;                 // rows per thread
+    const int NT = p.V / 32;
+    const int tile = blockIdx.x % NT, unit = blockIdx.x / NT;
+    const int n = unit / p.HV, h = unit % p.HV, hk = h / (p.HV / p.HK);
+    if (status[0] != LA_DEVICE_OK) return;   // malformed cu_seqlens: write nothing
+    const int c = threadIdx.x & 31, g8 = threadIdx.x >> 5, r0 = g8 * R, col = 32 * tile + c;
+    const int start = p.cu[n], end = p.cu[n + 1];
+    const int64_t sbase = ((int64_t)n * p.HV + h) * K * p.V + col;
+    float D[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) D[i] = d_end ? d_end[sbase + (int64_t)(r0 + i) * p.V] : 0.f;
+    __shared__ float part[2][8][32];
+    int it = 0;
+    for (int t = end - 1; t >= start; --t, ++it) {
+        const float rq = rn[2 * ((int64_t)t * p.HK + hk)] * p.scale, rk = rn[2 * ((int64_t)t * p.HK + hk) + 1];
+        const float a = expf(p.g[(int64_t)t * p.gst + h]), b = p.beta[(int64_t)t * p.bst + h];
+        const float dv = bf2f(d_out[(int64_t)t * p.ost + (int64_t)h * p.osh + col]);
+        const __bf16 *qr = p.q + (int64_t)t * p.qst + (int64_t)hk * p.qsh + r0;
+        const __bf16 *kr = p.k + (int64_t)t * p.kst + (int64_t)hk * p.ksh + r0;
+        float kv[R], sp = 0.f;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            D[i] = fmaf(bf2f(qr[i]) * rq, dv, D[i]);   // X = D + scale q^ do^T
+            kv[i] = bf2f(kr[i]) * rk;
+            sp = fmaf(kv[i], D[i], sp);
+        }
+        part[it & 1][g8][c] = sp;
+        __syncthreads();
+        float w = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w += part[it & 1][j][c];   // (k^T X)[col], rows in order
+        const float bw = b * w;
+#pragma unroll
+        for (int i = 0; i < R; ++i) D[i] = a * fmaf(-kv[i], bw, D[i]);   // D = exp(g) (X - beta k^ (k^T X))
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) d_start[sbase + (int64_t)(r0 + i) * p.V] = D[i];
+}
+
+hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t s, const LaunchHook *hook)
+{
+    const Prob &p = *a.p;
+    if (p.N == 0) return hipSuccess;
+    const int64_t rows = p.T * p.HK;
+    const unsigned prep_blocks = (unsigned)((rows + 3) / 4) + 1;
+    const unsigned blocks = (unsigned)((int64_t)p.N * p.HV * (p.V / 32));
+    if (hook) hook->before(LA_KERNEL_SCHED, s, hook->ctx);
+    if (p.K == 64)
+        hipLaunchKernelGGL(k_sbwd_prep<64>, dim3(prep_blocks), dim3(256), 0, s, p, nullptr, a.rn, a.status);
+    else
+        hipLaunchKernelGGL(k_sbwd_prep<128>, dim3(prep_blocks), dim3(256), 0, s, p, nullptr, a.rn, a.status);
+    if (hook) hook->after(LA_KERNEL_SCHED, s, hook->ctx);
+    if (hook) hook->before(LA_KERNEL_INTER, s, hook->ctx);
+    if (p.K == 64)
+        hipLaunchKernelGGL(k_sbwd<64>, dim3(blocks), dim3(256), 0, s, p, a.d_out, a.d_end, a.d_start, a.rn, a.status);
+    else
+        hipLaunchKernelGGL(k_sbwd<128>, dim3(blocks), dim3(256), 0, s, p, a.d_out, a.d_end, a.d_start, a.rn, a.status);
+    if (hook) hook->after(LA_KERNEL_INTER, s, hook->ctx);
+    return hipGetLastError();
+}
 
 hipError_t run_pipeline(const Prob &p, const Ws &w, bool summary, hipStream_t s, const LaunchHook *hook)
 {

@@ -233,6 +233,31 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
                             hipStream_t stream);
 
 /*
+ * The span summary's mirror for the state gradient (the "Linear Attention" page,
+ * "Summaries": <op>_summary_bwd, which with the summary implements context
+ * parallelism over sequence spans).  For each sequence (span) and value head, with
+ * the outputs o_t = scale S_t^T q_t of the forward over the span and
+ * L = sum_t <d_out_t, o_t> + <d_end_state, S_end>, returns d_start_state = dL/dS_start:
+ * the reverse recurrence D <- d_end_state, then for the span's tokens from last to first
+ * D <- exp(g_t) (I - beta_t k_t k_t^T) (D + scale q_t d_out_t^T) (q, k normalised as in
+ * the forward).  It does not depend on v or on the start state.
+ *   q, k           device, bf16 [T, HK, K] as for la_gdn_fwd
+ *   g, beta        device, fp32 [T, HV] (plain natural-log gate, fp32 beta)
+ *   cu_seqlens     device, int32 [N + 1]
+ *   d_out          device, bf16 [T, HV, V], strides o_stride_t / o_stride_h of desc
+ *   d_end_state    device, fp32 [N, HV, K, V], or NULL for zeros
+ *   d_start_state  device, fp32 [N, HV, K, V], written
+ *   workspace      at least la_gdn_workspace_bytes(desc, 1) bytes, 256-byte aligned
+ * Errors as for la_gdn_summary (a malformed cu_seqlens writes nothing and sets the
+ * device status).  First version: token by token on the GPU (one workgroup per
+ * (sequence, value head, 32 value columns)).
+ */
+la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void *k, const float *g,
+                             const float *beta, const int32_t *cu_seqlens, const void *d_out,
+                             const float *d_end_state, float *d_start_state, int l2norm, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Reads the status word the last call on this workspace left (LA_DEVICE_*
  * bits).  Synchronises the stream.  Returns -1 if the read itself failed.
  */

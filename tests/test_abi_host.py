@@ -322,3 +322,20 @@ def test_int64_offsets_alignment_checked(lib):
     assert rc == la.LA_ERR_INVALID_ARGUMENT and "8-byte aligned" in la.la_last_error_message()
     with pytest.raises(ValueError, match="int32 or int64"):
         la._cu_int64(torch.zeros(3, dtype=torch.int16))
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(q=None), la.LA_ERR_INVALID_ARGUMENT, "q is NULL"),
+    (dict(k=(1 << 20) + 8), la.LA_ERR_INVALID_ARGUMENT, "k base pointer"),
+    (dict(out=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "d_out base pointer"),
+    (dict(fin=None), la.LA_ERR_INVALID_ARGUMENT, "d_start_state is NULL"),
+    (dict(s0=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "d_end_state"),
+    (dict(wsb=1024), la.LA_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+])
+def test_summary_bwd_argument_checks(lib, over, status, needle):
+    """la_gdn_summary_bwd checks its arguments on the host before any launch."""
+    d = _desc()
+    a = _fwd_args(**over)
+    rc = lib.la_gdn_summary_bwd(ctypes.byref(d), a["q"], a["k"], a["g"], a["beta"], a["cu"], a["out"], a["s0"],
+                                a["fin"], 1, a["ws"], a["wsb"], None)
+    assert rc == status and needle in la.la_last_error_message(), la.la_last_error_message()
