@@ -1672,6 +1672,34 @@ __global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, const float *unused, 
     }
 }
 
+// One token's operands for a thread of k_sbwd: its K / 8 rows of q and k (16-byte loads),
+// the row norms, gate, beta and its column of d_out.
+template <int R>
+struct SbwdTok {
+    uint4 q[R / 8], k[R / 8];
+    float rq, rk, g, b, dv;
+};
+
+template <int R>
+__device__ __forceinline__ SbwdTok<R> sbwd_load(const Prob &p, const __bf16 *d_out, const float *rn, int64_t t,
+                                                int h, int hk, int r0, int col)
+{
+    SbwdTok<R> x;
+    const uint4 *qr = reinterpret_cast<const uint4 *>(p.q + t * p.qst + (int64_t)hk * p.qsh + r0);
+    const uint4 *kr = reinterpret_cast<const uint4 *>(p.k + t * p.kst + (int64_t)hk * p.ksh + r0);
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j) {
+        x.q[j] = qr[j];
+        x.k[j] = kr[j];
+    }
+    x.rq = rn[2 * (t * p.HK + hk)];
+    x.rk = rn[2 * (t * p.HK + hk) + 1];
+    x.g = p.g[t * p.gst + h];
+    x.b = p.beta[t * p.bst + h];
+    x.dv = bf2f(d_out[t * p.ost + (int64_t)h * p.osh + col]);
+    return x;
+}
+
 template <int K>
 __global__ __launch_bounds__(256) void k_sbwd(Prob p, const __bf16 *d_out, const float *d_end, float *d_start,
                                               const float *rn, const int32_t *status)
@@ -1688,28 +1716,33 @@ __global__ __launch_bounds__(256) void k_sbwd(Prob p, const __bf16 *d_out, const
 #pragma unroll
     for (int i = 0; i < R; ++i) D[i] = d_end ? d_end[sbase + (int64_t)(r0 + i) * p.V] : 0.f;
     __shared__ float part[2][8][32];
+    // the next token's operands are loaded while this token is computed
+    SbwdTok<R> cur{};
+    if (end > start) cur = sbwd_load<R>(p, d_out, rn, end - 1, h, hk, r0, col);
     int it = 0;
     for (int t = end - 1; t >= start; --t, ++it) {
-        const float rq = rn[2 * ((int64_t)t * p.HK + hk)] * p.scale, rk = rn[2 * ((int64_t)t * p.HK + hk) + 1];
-        const float a = expf(p.g[(int64_t)t * p.gst + h]), b = p.beta[(int64_t)t * p.bst + h];
-        const float dv = bf2f(d_out[(int64_t)t * p.ost + (int64_t)h * p.osh + col]);
-        const __bf16 *qr = p.q + (int64_t)t * p.qst + (int64_t)hk * p.qsh + r0;
-        const __bf16 *kr = p.k + (int64_t)t * p.kst + (int64_t)hk * p.ksh + r0;
+        const SbwdTok<R> nxt = t > start ? sbwd_load<R>(p, d_out, rn, t - 1, h, hk, r0, col) : cur;
+        // the row norms and scale fold into per-token scalars: X = D + (scale r_q do) q and
+        // D = exp(g) (X - (beta r_k^2 (k^T X)) k) with the raw rows q, k
+        const float sq = cur.rq * p.scale * cur.dv, a = expf(cur.g);
         float kv[R], sp = 0.f;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            D[i] = fmaf(bf2f(qr[i]) * rq, dv, D[i]);   // X = D + scale q^ do^T
-            kv[i] = bf2f(kr[i]) * rk;
+            const bf16x8 q8 = __builtin_bit_cast(bf16x8, cur.q[i / 8]);
+            const bf16x8 k8 = __builtin_bit_cast(bf16x8, cur.k[i / 8]);
+            D[i] = fmaf(bf2f(q8[i % 8]), sq, D[i]);
+            kv[i] = bf2f(k8[i % 8]);
             sp = fmaf(kv[i], D[i], sp);
         }
         part[it & 1][g8][c] = sp;
         __syncthreads();
         float w = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w += part[it & 1][j][c];   // (k^T X)[col], rows in order
-        const float bw = b * w;
+        for (int j = 0; j < 8; ++j) w += part[it & 1][j][c];   // (k^T X)[col] of the raw k, rows in order
+        const float bw = cur.b * cur.rk * cur.rk * w;
 #pragma unroll
-        for (int i = 0; i < R; ++i) D[i] = a * fmaf(-kv[i], bw, D[i]);   // D = exp(g) (X - beta k^ (k^T X))
+        for (int i = 0; i < R; ++i) D[i] = a * fmaf(-kv[i], bw, D[i]);
+        cur = nxt;
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) d_start[sbase + (int64_t)(r0 + i) * p.V] = D[i];
