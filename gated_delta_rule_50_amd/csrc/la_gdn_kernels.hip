@@ -429,11 +429,12 @@ __device__ __forceinline__ void vm_wait_n(int n)
 // ---------------------------------------------------------------------------
 // k_intra: one workgroup of 4 waves per (chunk, value head) item, persistent
 // (three workgroups per CU walk the items chunk-major).  Per item:
-//   1. k, v, g and beta of the chunk go straight into LDS with buffer loads (rows
+//   1. k, q, g and beta of the chunk go straight into LDS with buffer loads (rows
 //      past the chunk's end are out of the buffer's range and read as zeros; the
 //      16-byte pieces of a row are XOR-swizzled by the row, through the choice of
 //      source address, so that the operand reads below are free of bank
-//      conflicts).  Only k, g and beta are waited for here: v lands during 2 and 3.
+//      conflicts).  The k rows are issued one item ahead (into sK as soon as the
+//      previous item's W products have read it); v lands during 2 and 3.
 //   2. the Gram tiles G = K K^T (32 x 32 tiles on or below the diagonal) on bf16
 //      MFMA; r_k from the diagonal of G; the chunk-local inclusive gate cumsum gam
 //      (log2 units).  Then A = [s < t] beta_t 2^(gam_t - gam_s) r_k,t r_k,s G goes
@@ -588,27 +589,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // loads share that XCD's L2.  A bijection on the first 8 G floor(groups / 8) items
     // (the rest keep their index); with G = 1 it is the identity.
     const int groups = items / G, full = (groups & ~7) * G;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    struct Item { int ci, h, hk, start, len; };
+    auto item_info = [&](int it) {
         int r = it;
         if (G > 1 && it < full) {
             const int u = it >> 3;
             r = __builtin_amdgcn_readfirstlane((8 * (u / G) + (it & 7)) * G + u % G);
         }
-        const int ci = __builtin_amdgcn_readfirstlane(r / p.HV);
-        const int h = __builtin_amdgcn_readfirstlane(r % p.HV), hk = __builtin_amdgcn_readfirstlane(h / G);
-        int start, len;
+        Item x;
+        x.ci = __builtin_amdgcn_readfirstlane(r / p.HV);
+        x.h = __builtin_amdgcn_readfirstlane(r % p.HV);
+        x.hk = __builtin_amdgcn_readfirstlane(x.h / G);
         if (small) {
             // chunk ci belongs to the last sequence whose first chunk id is <= ci (never an
             // empty one: an empty sequence shares its first id with the next)
-            const uint64_t owns = __ballot(lane < p.N && sm.first <= ci);
+            const uint64_t owns = __ballot(lane < p.N && sm.first <= x.ci);
             const int n = 63 - __builtin_clzll(owns);
-            start = __builtin_amdgcn_readfirstlane(__shfl(sm.start, n, 64) + kChunk * (ci - __shfl(sm.first, n, 64)));
-            len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, n, 64) - start));
+            x.start = __builtin_amdgcn_readfirstlane(__shfl(sm.start, n, 64) + kChunk * (x.ci - __shfl(sm.first, n, 64)));
+            x.len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, n, 64) - x.start));
         } else {
-            const int4 ch = w.chunks[ci];
-            start = __builtin_amdgcn_readfirstlane(ch.y);
-            len = __builtin_amdgcn_readfirstlane(ch.z);
+            const int4 ch = w.chunks[x.ci];
+            x.start = __builtin_amdgcn_readfirstlane(ch.y);
+            x.len = __builtin_amdgcn_readfirstlane(ch.z);
         }
+        return x;
+    };
+    // The k rows of an item into sK.  They are issued one item ahead: for the first item
+    // here, for the next one as soon as the W products have read sK, so that their latency
+    // overlaps the U~ products and the stores.
+    auto issue_k = [&](const Item &x) {
+        if (!GDP) {
+            intra_load_tile<K>(sK, p.k + (int64_t)x.start * p.kst + (int64_t)x.hk * p.ksh, 2u * (uint32_t)p.kst, x.len,
+                               wave, lane, 4);
+        } else {
+            const int tb = __builtin_amdgcn_readfirstlane(x.start / p.nh);
+            intra_load_urows<K>(sK, p.k + (int64_t)tb * p.kst + (int64_t)x.hk * p.ksh, (int)p.kst, (int)p.kstu,
+                                x.start - tb * p.nh, x.len, p.nh, p.inv_nh, wave, lane, 4);
+        }
+    };
+    if ((int)blockIdx.x < items) issue_k(item_info(blockIdx.x));
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const Item item = item_info(it);
+        const int ci = item.ci, h = item.h, hk = item.hk, start = item.start, len = item.len;
         const int64_t ch_h = (int64_t)ci * p.HV + h;
         // The lane index for the lane masks of this item (the scan, the diagonal of G and
         // the causal masks of A, P^T and T) goes through an empty asm, so that the compiler
@@ -618,16 +640,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         asm volatile("" : "+v"(lm));
         const int cm = lm & 31, hm = lm >> 5;
 
-        // ---- 1: k, q, g, beta into LDS
+        // ---- 1: q, g, beta into LDS (k is on its way: issued one item ahead)
         // Gated Delta Product: the chunk's first token and its first update row within it
         const int tb = GDP ? __builtin_amdgcn_readfirstlane(start / p.nh) : start;
         const int phase = start - tb * p.nh;
-        if (!GDP)
-            intra_load_tile<K>(sK, p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst, len,
-                               wave, lane, 4);
-        else
-            intra_load_urows<K>(sK, p.k + (int64_t)tb * p.kst + (int64_t)hk * p.ksh, (int)p.kst, (int)p.kstu, phase,
-                                len, p.nh, p.inv_nh, wave, lane, 4);
         if (FWD) {
             if (!GDP) {
                 intra_load_tile<K>(sX, p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
@@ -907,6 +923,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                     }
                 }
             }
+            // every wave is done with sK: the next item's k rows go there now
+            lds_barrier();
+            if (it + (int)gridDim.x < items) issue_k(item_info(it + gridDim.x));
             bf16x8 th[4], tl[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
