@@ -76,3 +76,45 @@ def test_summary_graph_replays_match_eager():
         e_e, t_e = la.la_gdn_summary(p.k, p.v, p.g, p.beta, p.cu_seqlens, start_state=p.state)
         torch.cuda.synchronize()
         assert torch.equal(e_g, e_e) and torch.equal(t_g, t_e), f"replay {rep}"
+
+
+def test_summary_bwd_and_int64_offsets_graph_replays_match_eager():
+    """la_gdn_summary_bwd, and the forward with int64 cu_seqlens (its conversion kernel
+    included), captured and replayed on new inputs."""
+    lengths = (100, 0, 300, 64)
+    p = custom_problem(lengths, hk=2, hv=4, dk=128, dv=64, seed=330, with_state=True).to("cuda")
+    N, HV, K, V, T = p.num_seqs, p.num_v_heads, p.head_dim_k, p.head_dim_v, p.total_tokens
+    gen = torch.Generator(device="cuda").manual_seed(331)
+    d_out = torch.randn((T, HV, V), generator=gen, device="cuda").to(torch.bfloat16)
+    d_end = torch.randn((N, HV, K, V), generator=gen, device="cuda")
+    d_start = torch.empty((N, HV, K, V), dtype=torch.float32, device="cuda")
+    cu64 = p.cu_seqlens.to(torch.int64)
+    out = torch.empty((T, HV, V), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((N, HV, K, V), dtype=torch.float32, device="cuda")
+    desc = la.make_desc(p.k, p.v, p.g, p.beta, N, q=p.q, out=out)
+    ws_b = la.alloc_workspace(desc, True, "cuda")
+    ws_f = la.alloc_workspace(desc, False, "cuda")
+
+    def call():
+        la.la_gdn_summary_bwd(p.q, p.k, p.g, p.beta, p.cu_seqlens, d_out, d_end, d_start_state=d_start,
+                              workspace=ws_b)
+        la.la_gdn_fwd(p.q, p.k, p.v, p.g, p.beta, cu64, initial_state=p.state, out=out, final_state=fin,
+                      workspace=ws_f)
+
+    call()
+    torch.cuda.synchronize()
+    note("graph capture of la_gdn_summary_bwd and la_gdn_fwd with int64 offsets")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _load(p, custom_problem(lengths, hk=2, hv=4, dk=128, dv=64, seed=340 + rep, with_state=True).to("cuda"))
+        d_out.copy_(torch.randn((T, HV, V), generator=gen, device="cuda").to(torch.bfloat16))
+        graph.replay()
+        torch.cuda.synchronize()
+        s_g, o_g, f_g = d_start.clone(), out.clone(), fin.clone()
+        s_e = la.la_gdn_summary_bwd(p.q, p.k, p.g, p.beta, p.cu_seqlens, d_out, d_end)
+        o_e, f_e = la.la_gdn_fwd(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, initial_state=p.state)
+        torch.cuda.synchronize()
+        assert torch.equal(s_g, s_e) and torch.equal(o_g, o_e) and torch.equal(f_g, f_e), f"replay {rep}"
