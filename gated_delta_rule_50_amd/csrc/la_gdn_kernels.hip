@@ -1653,9 +1653,8 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
 // Inverse row norms of q and k (one wave per (token, q/k head) row), and, in the last
 // workgroup, the validation of cu_seqlens into the status word.
 template <int K>
-__global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, const float *unused, float *rn, int32_t *status)
+__global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, float *rn, int32_t *status)
 {
-    (void)unused;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     if (blockIdx.x == gridDim.x - 1) {
         if (wv != 0) return;
@@ -1776,9 +1775,9 @@ hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t s, const LaunchHook *h
     const unsigned blocks = (unsigned)((int64_t)p.N * p.HV * (p.V / 32));
     if (hook) hook->before(LA_KERNEL_SCHED, s, hook->ctx);
     if (p.K == 64)
-        hipLaunchKernelGGL(k_sbwd_prep<64>, dim3(prep_blocks), dim3(256), 0, s, p, nullptr, a.rn, a.status);
+        hipLaunchKernelGGL(k_sbwd_prep<64>, dim3(prep_blocks), dim3(256), 0, s, p, a.rn, a.status);
     else
-        hipLaunchKernelGGL(k_sbwd_prep<128>, dim3(prep_blocks), dim3(256), 0, s, p, nullptr, a.rn, a.status);
+        hipLaunchKernelGGL(k_sbwd_prep<128>, dim3(prep_blocks), dim3(256), 0, s, p, a.rn, a.status);
     if (hook) hook->after(LA_KERNEL_SCHED, s, hook->ctx);
     if (hook) hook->before(LA_KERNEL_INTER, s, hook->ctx);
     if (p.K == 64)
