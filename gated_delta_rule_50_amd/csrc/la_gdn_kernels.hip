@@ -1650,7 +1650,7 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
 // (sequence, value head, 32 value columns), D in registers (K / 8 rows per thread), and
 // k^T X reduced over the rows through LDS (one barrier per token).
 
-// Inverse row norms of q and k (one wave per (token, q/k head) row), and, in the last
+// Inverse row norms of q and k (K / 8 lanes per (token, q/k head) row), and, in the last
 // workgroup, the validation of cu_seqlens into the status word.
 template <int K>
 __global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, float *rn, int32_t *status)
@@ -1669,22 +1669,22 @@ __global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, float *rn, int32_t *s
         if (lane == 0) status[0] = any ? LA_DEVICE_BAD_CU_SEQLENS : LA_DEVICE_OK;
         return;
     }
-    const int64_t row = (int64_t)blockIdx.x * 4 + wv;   // token row * HK + hk
-    if (row >= p.T * p.HK) return;
-    const int64_t t = row / p.HK, hk = row % p.HK;
+    // K / 8 lanes per row (8 bf16 each, one 16-byte load of q and of k), 512 / K rows per wave
+    constexpr int LPR = K / 8, RPW = 64 / LPR;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + wv) * RPW + lane / LPR;   // token row * HK + hk
+    const int piece = lane % LPR;
     float sq = 0.f, sk = 0.f;
-    for (int e = lane; e < K; e += 64) {
-        const float qv = bf2f(p.q[t * p.qst + hk * p.qsh + e]);
-        const float kv = bf2f(p.k[t * p.kst + hk * p.ksh + e]);
-        sq += qv * qv;
-        sk += kv * kv;
+    if (row < p.T * p.HK) {
+        const int64_t t = row / p.HK, hk = row % p.HK;
+        sq = sumsq8(*reinterpret_cast<const uint4 *>(p.q + t * p.qst + hk * p.qsh + 8 * piece));
+        sk = sumsq8(*reinterpret_cast<const uint4 *>(p.k + t * p.kst + hk * p.ksh + 8 * piece));
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = LPR / 2; off >= 1; off >>= 1) {
         sq += __shfl_xor(sq, off, 64);
         sk += __shfl_xor(sk, off, 64);
     }
-    if (lane == 0) {
+    if (row < p.T * p.HK && piece == 0) {
         rn[2 * row] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
         rn[2 * row + 1] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
     }
@@ -1770,8 +1770,8 @@ hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t s, const LaunchHook *h
 {
     const Prob &p = *a.p;
     if (p.N == 0) return hipSuccess;
-    const int64_t rows = p.T * p.HK;
-    const unsigned prep_blocks = (unsigned)((rows + 3) / 4) + 1;
+    const int64_t rows = p.T * p.HK, rows_per_block = 4 * (512 / p.K);
+    const unsigned prep_blocks = (unsigned)((rows + rows_per_block - 1) / rows_per_block) + 1;
     const unsigned blocks = (unsigned)((int64_t)p.N * p.HV * (p.V / 32));
     if (hook) hook->before(LA_KERNEL_SCHED, s, hook->ctx);
     if (p.K == 64)
