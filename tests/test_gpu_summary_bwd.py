@@ -88,3 +88,26 @@ def test_summary_bwd_bad_cu_seqlens_writes_nothing():
         assert bool((out == 3.0).all())
     la.la_gdn_summary_bwd(g.q, g.k, g.g, g.beta, g.cu_seqlens, d_out.cuda(), d_end.cuda(), workspace=ws)
     assert la.la_gdn_device_status(ws) == la.LA_DEVICE_OK
+
+
+def test_summary_bwd_strided_views_equal_contiguous_bitwise():
+    """q, k and d_out as column slices of wider per-token buffers (the strides of the
+    descriptor), against contiguous copies: the same bits."""
+    p = _problem((40, 0, 150), 64, 128, seed=131)
+    d_out, d_end = _inputs(p, 132)
+    g = p.to("cuda")
+    T, HK, K = p.k.shape
+    HV, V = d_out.shape[1], d_out.shape[2]
+    wide = torch.zeros((T, 2 * HK * K + 16), dtype=torch.bfloat16, device="cuda")
+    wide[:, :HK * K] = g.q.reshape(T, HK * K)
+    wide[:, HK * K + 8:2 * HK * K + 8] = g.k.reshape(T, HK * K)
+    q_v = wide[:, :HK * K].view(T, HK, K)
+    k_v = wide[:, HK * K + 8:2 * HK * K + 8].view(T, HK, K)
+    dwide = torch.zeros((T, HV, V + 8), dtype=torch.bfloat16, device="cuda")
+    dwide[:, :, :V] = d_out.cuda()
+    d_v = dwide[:, :, :V]
+    note("summary bwd: strided q, k, d_out")
+    a = la.la_gdn_summary_bwd(g.q, g.k, g.g, g.beta, g.cu_seqlens, d_out.cuda(), d_end.cuda())
+    b = la.la_gdn_summary_bwd(q_v, k_v, g.g, g.beta, g.cu_seqlens, d_v, d_end.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
