@@ -105,9 +105,10 @@ def measured_traffic(kernel_src: str):
     return int(1024 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]))
 
 
-def cpu_baseline(problem, min_seconds: float = 1.0, max_reps: int = 64):
+def cpu_baseline(problem, min_seconds: float = 10.0, max_reps: int = 400):
     """The fp64 oracle over the whole workload (all 48 (sequence, head) units),
-    on the host cores, repeated until about min_seconds of wall time."""
+    on the host cores, repeated until about min_seconds of wall time (a bounded
+    sample of CPU work, so that the default run still finishes in about a minute)."""
     import oracle
     o = oracle.Oracle(problem)
     nt = oracle.default_threads()
