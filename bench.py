@@ -10,9 +10,10 @@ resident in HBM.  Steps rotate over several copies of the inputs, outputs and
 workspaces (more bytes than the 256 MiB Infinity Cache holds), so each step
 reads its operands from HBM rather than from the cache.
 
-Prints one JSON line: tokens/s of the whole job, the roofline of the dominant
-kernel (k_inter) from per-kernel HIP-event timing on the launch stream, and
-the fp64 CPU oracle timed on the host cores as a baseline.
+Prints one JSON line: tokens/s of the whole job, the roofline of one call (the
+algorithmic bytes over the summed launch times of the call's kernels, each
+from HIP events on the launch stream), and the fp64 CPU oracle timed on the
+host cores as a baseline.
 """
 from __future__ import annotations
 
@@ -90,9 +91,10 @@ def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final, nh
     return by, fl
 
 
-def measured_traffic(kernel_src: str):
-    """HBM bytes per k_inter launch from the committed counter record, or None
-    when the kernel source changed since the counters were taken."""
+def measured_traffic(kernel_src: str, kernels):
+    """HBM bytes of one call (FETCH_SIZE + WRITE_SIZE of each of its kernels, calibrated)
+    from the committed counter record, or None when the kernel source changed since
+    the counters were taken (the record is then stale and must be measured again)."""
     import hashlib
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -102,13 +104,36 @@ def measured_traffic(kernel_src: str):
         return None
     if rec.get("kernel_source_sha256") != h:
         return None
-    return int(1024 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]))
+    per = rec.get("kernels", {})
+    if any(k not in per for k in kernels):
+        return None
+    return int(sum(1024 * (per[k]["fetch_kib"] * rec["fetch_scale"] + per[k]["write_kib"] * rec["write_scale"])
+                   for k in kernels))
+
+
+def host_cpu():
+    """The host's logical CPU count, the CPUs this process may run on, and the CPU model."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return os.cpu_count() or 1, usable, model
 
 
 def cpu_baseline(problem, min_seconds: float = 10.0, max_reps: int = 400):
     """The fp64 oracle over the whole workload (all 48 (sequence, head) units),
     on the host cores, repeated until about min_seconds of wall time (a bounded
-    sample of CPU work, so that the default run still finishes in about a minute)."""
+    sample of CPU work, so that the default run still finishes in about a minute).
+    The oracle runs on the host's CPU share of one GPU (16 threads, or fewer when
+    fewer CPUs are usable); the host's CPU count and model are reported beside it."""
     import oracle
     o = oracle.Oracle(problem)
     nt = oracle.default_threads()
@@ -121,10 +146,12 @@ def cpu_baseline(problem, min_seconds: float = 10.0, max_reps: int = 400):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps:
             break
+    ncpu, usable, model = host_cpu()
     return {"value": reps * problem.total_tokens / dt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "host_cpus": ncpu, "usable_cpus": usable, "cpu_model": model,
             "sample": f"the whole workload ({problem.num_seqs * problem.num_v_heads} (sequence, head) units, "
                       f"{problem.total_tokens} tokens, fp64 token recurrence) run {reps} times: "
-                      f"{dt:.2f} s wall on {nt} threads"}
+                      f"{dt:.2f} s wall on {nt} threads ({usable} usable of {ncpu} logical CPUs, {model})"}
 
 
 def main(argv=None):
@@ -298,23 +325,26 @@ def main(argv=None):
         # start-state gradients; per token-head 6 K V flops (X, k^T X and the update)
         by = T * (2 * HK * K * 2 + HV * V * 2 + 2 * HV * 4) + 2 * N * HV * K * V * 4
         fl = 6 * T * HV * K * V
-    inter_us = kern["k_inter"]["avg_us"]
-    # the dominant kernel's roofline: the path's algorithmic bytes (one launch
-    # processes every token-head of the batch) over that kernel's launch time;
-    # the span summary sits at the ridge and is priced on bf16 MFMA flops
+    # Roofline of the call: the path's algorithmic bytes (or flops) over the GPU time of
+    # all the kernels one call launches, each timed with HIP events on the launch
+    # stream (their sum is what rocprofv3 reports for the same kernels).  The span
+    # summary sits at the ridge and is priced on bf16 MFMA flops.
+    launched = [k for k, v in kern.items() if v["launches"] > 0]
+    call_us = sum(kern[k]["avg_us"] for k in launched)
     step_s = ms_per_step * 1e-3
     if summary and variant != "summary-bwd":
-        roof = {"bound": "mfma", "kernel": "k_inter", "achieved": fl / (inter_us * 1e-6) / 1e12,
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": fl / (call_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
     else:
-        roof = {"bound": "hbm", "kernel": "k_inter", "achieved": by / (inter_us * 1e-6) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": by / (call_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # the committed counter record covers the default workload only
-    roof["traffic"] = measured_traffic(os.path.join(ROOT, "gated_delta_rule_50_amd", "csrc",
-                                                    "la_gdn_kernels.hip")) if wl == 2 and variant == "plain" else None
-    roof.update({"algorithmic_bytes_per_launch": by, "algorithmic_flops_per_launch": fl,
-                 "avg_launch_us": inter_us})
+    # measured HBM bytes of the call's kernels (the committed counter record covers the
+    # default workload only)
+    roof["traffic"] = (measured_traffic(os.path.join(ROOT, "gated_delta_rule_50_amd", "csrc", "la_gdn_kernels.hip"),
+                                        launched) if wl == 2 and variant == "plain" else None)
+    roof.update({"kernel": " + ".join(launched) + " (one call)", "algorithmic_bytes_per_launch": by,
+                 "algorithmic_flops_per_launch": fl, "avg_launch_us": call_us,
+                 "kernel_avg_us": {k: kern[k]["avg_us"] for k in launched}})
 
     rec = {
         "metric": METRIC,

@@ -42,6 +42,13 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The kernels address the rows of one chunk (and the 4-byte rows of g and beta) from the
+// chunk's first row with 32-bit byte offsets: 66 rows of a 16-bit tensor, or 64 of a
+// 32-bit one, at a token stride below 2^24 elements stay below 2^32 bytes.
+constexpr int64_t kMaxTokenStride = int64_t(1) << 24;
+
+int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
+
 // Descriptor checks shared by both calls and by the workspace query.
 la_status check_desc(const la_gdn_desc *d)
 {
@@ -73,7 +80,7 @@ la_status check_desc(const la_gdn_desc *d)
 // A bf16 [T, heads, dim] operand: 16-byte base, unit innermost stride (implied),
 // outer strides multiples of 8 elements and large enough not to overlap rows.
 la_status check_thd(const char *name, const void *ptr, int64_t st_t, int64_t st_h, int heads, int dim,
-                    int64_t T)
+                    int64_t T, bool offsets32 = true)
 {
     if (!ptr) return fail(LA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
     if (!aligned16(ptr)) return fail(LA_ERR_INVALID_ARGUMENT, "%s base pointer is not 16-byte aligned", name);
@@ -86,6 +93,10 @@ la_status check_thd(const char *name, const void *ptr, int64_t st_t, int64_t st_
                     (long long)st_h, dim);
     if (T > 1 && st_t < (int64_t)(heads - 1) * st_h + dim)
         return fail(LA_ERR_INVALID_ARGUMENT, "%s token stride %lld overlaps its heads", name, (long long)st_t);
+    if (offsets32 && T > 1 && st_t >= kMaxTokenStride)
+        return fail(LA_ERR_UNSUPPORTED,
+                    "%s token stride %lld: strides of 2^24 elements or more are not supported (the kernels "
+                    "address the rows of a chunk with 32-bit byte offsets)", name, (long long)st_t);
     return LA_OK;
 }
 
@@ -96,6 +107,10 @@ la_status check_rows(const char *name, const void *ptr, int64_t st_t, int heads,
     if (T > 1 && st_t < heads)
         return fail(LA_ERR_INVALID_ARGUMENT, "%s token stride %lld is smaller than num_v_heads %d", name,
                     (long long)st_t, heads);
+    if (T > 1 && st_t >= kMaxTokenStride)
+        return fail(LA_ERR_UNSUPPORTED,
+                    "%s token stride %lld: strides of 2^24 elements or more are not supported (the kernels "
+                    "address the rows of a chunk with 32-bit byte offsets)", name, (long long)st_t);
     return LA_OK;
 }
 
@@ -120,6 +135,10 @@ la_status check_beta_and_fusion(const void *beta, const la_gdn_desc &d, const la
     if (T > 1 && !token_major(f) && d.beta_stride_t < d.num_v_heads)
         return fail(LA_ERR_INVALID_ARGUMENT, "beta token stride %lld is smaller than num_v_heads %d",
                     (long long)d.beta_stride_t, d.num_v_heads);
+    if (T > 1 && !token_major(f) && d.beta_stride_t >= kMaxTokenStride)
+        return fail(LA_ERR_UNSUPPORTED,
+                    "beta token stride %lld: strides of 2^24 elements or more are not supported (the kernels "
+                    "address the rows of a chunk with 32-bit byte offsets)", (long long)d.beta_stride_t);
     if (!f) return LA_OK;
     if (f->dt_bias && !f->a_log) return fail(LA_ERR_INVALID_ARGUMENT, "dt_bias is given without a_log");
     la_status st = check_f32("a_log", f->a_log, false);
@@ -240,6 +259,33 @@ la_status check_checkpoints(const la_gdn_options *f, bool summary)
     if ((a & (f->checkpoint_fp32 ? 3u : 1u)) != 0)
         return fail(LA_ERR_INVALID_ARGUMENT, "checkpoints is not %d-byte aligned", f->checkpoint_fp32 ? 4 : 2);
     return LA_OK;
+}
+
+// With one token (one update row) a tensor's token stride is never used to reach a second
+// row, and the argument checks accept any value for it (a broadcast view has 0).  The
+// kernels size each chunk's buffer range as rows x token stride, so such a stride would
+// read the row as zeros: it is replaced by the row's own extent, which gives the same
+// addresses for the one row and puts every padding row past the range.  Runs after
+// set_update_strides (update-row strides of the Gated Delta Product).
+void normalize_single_token(la::Prob &p, const la_gdn_options *f)
+{
+    if (p.T != 1) return;
+    p.qst = round8((int64_t)(p.HK - 1) * p.qsh + p.K);
+    p.ost = round8((int64_t)(p.HV - 1) * p.osh + p.V);
+    p.gst = p.HV;
+    const int64_t ek = round8((int64_t)(p.HK - 1) * p.ksh + p.K);
+    const int64_t ev = round8((int64_t)(p.HV - 1) * p.vsh + p.V);
+    if (p.nh == 1) {
+        p.kst = p.kstu = ek;
+        p.vst = p.vstu = ev;
+        p.bst = p.bstu = p.HV;
+    } else if (token_major(f)) {
+        // one token: its update rows are kstu apart; a token stride of n update strides
+        // puts every row of a following (absent) token past the range
+        p.kst = p.nh * p.kstu;
+        p.vst = p.nh * p.vstu;
+        p.bst = p.nh * p.bstu;
+    }
 }
 
 void set_beta_and_fusion(la::Prob &p, const void *beta, const la_gdn_options *f)
@@ -479,7 +525,8 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     if ((st = check_householder(d, fusion)) != LA_OK) return st;
     if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
     if ((st = check_kvb(d, k, v, fusion)) != LA_OK) return st;
-    if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK) return st;
+    if ((st = check_thd("out", out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T, false)) != LA_OK)
+        return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, fusion)) != LA_OK) return st;
     const bool cu64 = fusion && fusion->cu_seqlens_int64;
@@ -497,6 +544,7 @@ la_status la_gdn_fwd_ex(const la_gdn_desc *desc, const void *q, const void *k, c
     p.g = g;
     set_beta_and_fusion(p, beta, fusion);
     set_update_strides(p, fusion);
+    normalize_single_token(p, fusion);
     p.cu = cu64 ? nullptr : static_cast<const int32_t *>(cu_seqlens);
     p.s0 = initial_state;
     p.o = static_cast<__bf16 *>(out);
@@ -544,6 +592,7 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
     p.g = g;
     set_beta_and_fusion(p, beta, fusion);
     set_update_strides(p, fusion);
+    normalize_single_token(p, fusion);
     p.cu = cu64 ? nullptr : static_cast<const int32_t *>(cu_seqlens);
     p.s0 = start_state;
     p.o = nullptr;
@@ -565,7 +614,8 @@ la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void 
     const int64_t T = d.total_tokens;
     if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
     if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
-    if ((st = check_thd("d_out", d_out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK)
+    if ((st = check_thd("d_out", d_out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T, false)) !=
+        LA_OK)
         return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, nullptr)) != LA_OK) return st;

@@ -494,6 +494,16 @@ __device__ __forceinline__ void intra_load_qrows(lds_u32x4 *dst, const void *bas
     }
 }
 
+// Gated Delta Product: bytes of q rows in range from token tb on.  A chunk of 64 update
+// rows touches at most 64 / nh + 2 tokens, so the range stops at 66 tokens (or the end of
+// q): with token strides below 2^24 elements (the host declines larger ones) it fits in
+// 32 bits however long the batch is.
+__device__ __forceinline__ uint32_t gdp_q_range(const Prob &p, int tb)
+{
+    const int64_t rows = p.T - tb < 66 ? p.T - tb : 66;
+    return (uint32_t)rows * 2u * (uint32_t)p.qst;
+}
+
 // Gated Delta Product: element offset of update row tb nh + rel (0 <= rel < 128) from row
 // 0 of token tb: rel / nh tokens of stride st and rel % nh updates of stride su (update-major
 // rows: st = nh su).  The quotient goes through the reciprocal: (rel + 1/2) / nh lies at
@@ -650,7 +660,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                    len, wave, lane, 4);
             } else {
                 intra_load_qrows<K>(sX, p.q + (int64_t)tb * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
-                                    (uint32_t)(p.T - tb) * 2u * (uint32_t)p.qst, start, len, p.nh, tb, wave, lane, 4);
+                                    gdp_q_range(p, tb), start, len, p.nh, tb, wave, lane, 4);
             }
         }
         float blogit = 0.f;   // beta logit of update row `lane` (beta16 only)
@@ -1112,7 +1122,7 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
             // b + phase - nh of token tb + a + 1.
             const int tb = __builtin_amdgcn_readfirstlane(cur.tb), phase = __builtin_amdgcn_readfirstlane(cur.phase);
             const int thr = p.nh - phase;
-            const uint32_t rs = 2u * (uint32_t)p.qst, nrec = (uint32_t)(p.T - tb) * rs;
+            const uint32_t rs = 2u * (uint32_t)p.qst, nrec = gdp_q_range(p, tb);
             const i32x4 rQ = make_rsrc(p.q + (int64_t)tb * p.qst + (int64_t)x.hk * p.qsh, nrec);
 #pragma unroll
             for (int i = 0; i < C::FQ / 2; ++i) {

@@ -80,6 +80,9 @@ def _load():
 
 
 def default_threads() -> int:
+    """Threads for the oracle: the CPUs this process may use, at most OMP_NUM_THREADS
+    and at most 16, the host's CPU share of one GPU on an MI355X node (the benchmark
+    reports the host's CPU count and model beside the figure)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover

@@ -1,0 +1,169 @@
+"""A numpy model of the chunked method the HIP kernels use (test infrastructure).
+
+The chunked evaluation of the Gated DeltaNet recurrence (the cuDNN "Linear
+Attention" page describes the op as evaluated in chunks; the cudnn-frontend PR
+"Further reduce FROST LA CPU overhead + fully support all L2norm, beta, gate
+fusion" names its steps: a chunk-local cumulative gate, the intra-chunk UT/WY
+solve that returns w, u and A, and the inter-chunk state pass).  Per (sequence,
+value head) and per chunk of n <= 64 tokens with start state S0 (K x V), with
+k^ = r_k k, q^ = scale r_q q and gam the chunk-local inclusive cumsum of g:
+
+    A[t, s] = beta_t exp(gam_t - gam_s) (k^_t . k^_s)      for s < t, else 0
+    T       = (I + A)^-1                                   (unit lower triangular)
+    W       = T diag(beta exp(gam)) K^,   U~ = T diag(beta) V
+    U       = U~ - W S0
+    O       = diag(exp(gam)) Q^ S0 + (Mask o Q^ K^T) U,   Mask[t, s] = exp(gam_t - gam_s), s <= t
+    S_n     = exp(gam_n) S0 + K^T diag(exp(gam_n - gam)) U
+
+Unrolling the token recurrence over a chunk gives these formulas exactly, so in
+fp64 this model must equal the token-by-token oracle to rounding (the test pins
+it at 1e-12).  `Rounding` selects where the model rounds to bf16 or fp32, at
+the points where the kernels do, so that the error of a kernel design can be
+predicted before it runs.  The model shares nothing with the HIP path: it is
+written from the formulas above.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+
+CHUNK = 64
+
+
+def bf16(x) -> np.ndarray:
+    """Round to bf16 (round to nearest, ties to even) through fp32; returned as fp64."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def unit_lower_inverse(A: np.ndarray) -> np.ndarray:
+    """(I + A)^-1 for strictly lower-triangular A ([..., n, n]) by forward substitution,
+    column by column: x_i = e_i - sum_{k<i} A[i, k] x_k, one row at a time."""
+    n = A.shape[-1]
+    T = np.zeros_like(A)
+    for i in range(n):
+        T[..., i, i] = 1.0
+        if i:
+            T[..., i, :i] = -np.einsum("...k,...kj->...j", A[..., i, :i], T[..., :i, :i])
+    return T
+
+
+@dataclasses.dataclass
+class Rounding:
+    """Where the model rounds.  exact: none at all (fp64 throughout).  Otherwise the
+    kernel design: W and P^T in bf16, T diag(beta) as a bf16 hi/lo pair (so U~ is
+    about fp32), S rounded to bf16 as the operand of W S and Q S, diag(d) U rounded to
+    bf16 as the operand of the state update, U rounded to bf16 as the operand of P U,
+    states kept in fp32, o rounded to bf16.  ut_bf16 instead rounds U~ itself to bf16
+    (the plain all-bf16 design)."""
+    exact: bool = True
+    ut_bf16: bool = False
+
+    def r16(self, x):
+        return x if self.exact else bf16(x)
+
+    def r32(self, x):
+        return x if self.exact else f32(x)
+
+
+EXACT = Rounding(exact=True)
+KERNEL = Rounding(exact=False)
+ALL_BF16 = Rounding(exact=False, ut_bf16=True)
+
+
+def _masked_exp(gam: np.ndarray, strict: bool) -> np.ndarray:
+    """exp(gam_t - gam_s) for s < t (strict) or s <= t, zero elsewhere; [..., n, n]."""
+    n = gam.shape[-1]
+    keep = np.tril(np.ones((n, n), dtype=bool), -1 if strict else 0)
+    diff = gam[..., :, None] - gam[..., None, :]
+    return np.exp(np.where(keep, diff, -np.inf))
+
+
+def chunked_sequence(q, k, v, g, beta, S0, scale: float, l2norm: bool, rounding: Rounding = EXACT,
+                     chunk: int = CHUNK) -> Tuple[Optional[np.ndarray], np.ndarray]:
+    """One sequence, all value heads at once.
+
+    q, k: [L, H, K] (q may be None: no output), v: [L, H, V], g, beta: [L, H], S0:
+    [H, K, V] (fp64 values).  The heads here are value heads: grouped q/k heads are
+    expanded by the caller.  Returns o [L, H, V] (or None) and the final state."""
+    L, H, _ = k.shape
+    V = v.shape[2]
+    rnd = rounding
+    rk = 1.0 / np.sqrt(np.sum(k * k, axis=2) + 1e-6) if l2norm else np.ones((L, H))
+    rq = (1.0 / np.sqrt(np.sum(q * q, axis=2) + 1e-6) if l2norm else np.ones((L, H))) if q is not None else None
+    S = np.array(S0, dtype=np.float64)
+    o = np.zeros((L, H, V)) if q is not None else None
+    for c0 in range(0, L, chunk):
+        c1 = min(c0 + chunk, L)
+        # heads first: [H, n, .]
+        Kc = np.transpose(k[c0:c1], (1, 0, 2))
+        Vc = np.transpose(v[c0:c1], (1, 0, 2))
+        b = beta[c0:c1].T
+        gam = np.cumsum(g[c0:c1].T, axis=1)
+        r = rk[c0:c1].T
+        Kh = r[:, :, None] * Kc
+        A = b[:, :, None] * _masked_exp(gam, strict=True) * (Kh @ np.transpose(Kh, (0, 2, 1)))
+        T = unit_lower_inverse(A)
+        # W = T diag(beta e^gam r_k) K (raw K), U~ = T diag(beta) V
+        Tw = rnd.r16(T * (b * np.exp(gam) * r)[:, None, :])
+        W = rnd.r16(Tw @ Kc)
+        TB = T * b[:, None, :]
+        if rnd.exact:
+            Ut = TB @ Vc
+        elif rnd.ut_bf16:
+            Ut = bf16(TB @ Vc)
+        else:
+            hi = bf16(TB)
+            lo = bf16(TB - hi)
+            Ut = f32(hi @ Vc + lo @ Vc)
+        Sb = rnd.r16(S)
+        U = rnd.r32(Ut - W @ Sb)
+        gn = gam[:, -1]
+        d = np.exp(gn[:, None] - gam) * r
+        if q is not None:
+            Qc = np.transpose(q[c0:c1], (1, 0, 2))
+            sq = scale * rq[c0:c1].T * np.exp(gam)
+            P = rnd.r16(scale * rq[c0:c1].T[:, :, None] * r[:, None, :] * _masked_exp(gam, strict=False)
+                        * (Qc @ np.transpose(Kc, (0, 2, 1))))
+            oc = sq[:, :, None] * (Qc @ Sb) + P @ rnd.r16(U)
+            o[c0:c1] = np.transpose(rnd.r16(oc), (1, 0, 2))
+        S = rnd.r32(np.exp(gn)[:, None, None] * S + np.transpose(Kc, (0, 2, 1)) @ rnd.r16(d[:, :, None] * U))
+    return o, S
+
+
+def chunked_forward(problem, rounding: Rounding = EXACT, scale: Optional[float] = None):
+    """Every sequence of a workloads.Problem: o [T, HV, V] (None for a summary problem)
+    and final states [N, HV, K, V], from the problem's initial state (or zeros)."""
+    p = problem
+    k = p.k.float().double().numpy()
+    v = p.v.float().double().numpy()
+    q = p.q.float().double().numpy() if p.q is not None else None
+    g = p.g.double().numpy()
+    beta = p.beta.double().numpy()
+    HK, HV = k.shape[1], v.shape[1]
+    K, V = k.shape[2], v.shape[2]
+    rep = np.arange(HV) // (HV // HK)
+    sc = K ** -0.5 if scale is None else scale
+    cu = p.cu_seqlens.tolist()
+    N = len(cu) - 1
+    o = np.zeros((cu[-1], HV, V)) if q is not None else None
+    fin = np.zeros((N, HV, K, V))
+    for n in range(N):
+        a, e = cu[n], cu[n + 1]
+        S0 = p.state[n].double().numpy() if p.state is not None else np.zeros((HV, K, V))
+        if e == a:
+            fin[n] = S0
+            continue
+        on, fin[n] = chunked_sequence(None if q is None else q[a:e][:, rep], k[a:e][:, rep], v[a:e], g[a:e],
+                                      beta[a:e], S0, sc, p.l2norm, rounding)
+        if o is not None:
+            o[a:e] = on
+    return o, fin

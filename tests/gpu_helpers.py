@@ -75,6 +75,63 @@ def assert_o_state(out, fin, ref, tol_o=TOL_O, tol_s=TOL_STATE):
         assert_rows_close(f64(fin).reshape(-1, K * V), ref["state"].reshape(-1, K * V), tol_s, "final states")
 
 
+def assert_states(x, ref, tol, what):
+    """[..., K, V] fp32 states (final states, series entries) against the oracle's:
+    whole-tensor rel-L2 and one K x V state per row."""
+    ref = np.asarray(ref)
+    K, V = ref.shape[-2:]
+    e = rel_l2(f64(x), ref)
+    assert e <= tol, f"{what}: rel-L2 {e:.3e} > {tol}"
+    assert_rows_close(f64(x).reshape(-1, K * V), ref.reshape(-1, K * V), tol, what)
+
+
+def assert_summary(end, tr, ref, tol=TOL_STATE, check_transition=True):
+    """End states and transitions against the oracle's: whole-tensor rel-L2 and row by
+    row (one (sequence, head) state or transition per row)."""
+    K, V = ref["state"].shape[-2:]
+    ee = rel_l2(f64(end), ref["state"])
+    assert ee <= tol, f"end state rel-L2 {ee:.3e} > {tol}"
+    assert_rows_close(f64(end).reshape(-1, K * V), ref["state"].reshape(-1, K * V), tol, "end states")
+    if check_transition:
+        et = rel_l2(f64(tr), ref["transition"])
+        assert et <= tol, f"transition rel-L2 {et:.3e} > {tol}"
+        assert_rows_close(f64(tr).reshape(-1, K * K), ref["transition"].reshape(-1, K * K), tol, "transitions")
+
+
+class UnitTally:
+    """Whole-tensor rel-L2 and row bounds accumulated unit by unit, for tensors too
+    large to assemble in fp64 twice (every unit of the long-context and span
+    workloads)."""
+
+    def __init__(self, tol, what):
+        self.tol, self.what = tol, what
+        self.num = self.den = 0.0
+        self.err, self.nrm, self.tag = [], [], []
+
+    def add(self, x, ref, tag, per_unit=True):
+        x = np.asarray(x, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+        ref = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+        d = np.linalg.norm(x - ref, axis=1)
+        n = np.linalg.norm(ref, axis=1)
+        self.num += float(np.sum(d * d))
+        self.den += float(np.sum(n * n))
+        self.err.append(d)
+        self.nrm.append(n)
+        self.tag.append(tag)
+        if per_unit and n.size:
+            e = float(np.sqrt(np.sum(d * d)) / max(np.sqrt(np.sum(n * n)), 1e-300))
+            assert e <= self.tol, f"{self.what} of unit {tag}: rel-L2 {e:.3e} > {self.tol}"
+
+    def check(self):
+        e = float(np.sqrt(self.num) / max(np.sqrt(self.den), 1e-300))
+        assert e <= self.tol, f"{self.what}: rel-L2 {e:.3e} > {self.tol}"
+        err, nrm = np.concatenate(self.err), np.concatenate(self.nrm)
+        rms = float(np.sqrt(np.mean(nrm ** 2))) if nrm.size else 0.0
+        bad = np.nonzero(~(err <= ROW_FACTOR * self.tol * (nrm + rms)))[0]
+        assert bad.size == 0, f"{self.what}: {bad.size} rows beyond {ROW_FACTOR} x {self.tol}"
+        return e
+
+
 def check_fwd_full(p, tol_o=TOL_O, tol_s=TOL_STATE, initial_state=True):
     """Whole-tensor rel-L2 of o and final state against the oracle, and row by row."""
     note(f"fwd full: {p.name} T={p.total_tokens} N={p.num_seqs}")

@@ -137,6 +137,46 @@ def test_stride_checks(lib, field, value, needle):
     assert needle in la.la_last_error_message()
 
 
+@pytest.mark.parametrize("field", ["q_stride_t", "k_stride_t", "v_stride_t", "g_stride_t", "beta_stride_t"])
+def test_huge_token_strides_declined(lib, field):
+    """Token strides of 2^24 elements or more would wrap the kernels' 32-bit offsets
+    within a chunk: declined before any launch, in both calls that read the tensor."""
+    a = _fwd_args()
+    d = _desc(**{field: 1 << 24})
+    rc = lib.la_gdn_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None,
+                        a["out"], a["fin"], 1, a["ws"], a["wsb"], None)
+    assert rc == la.LA_ERR_UNSUPPORTED, la.la_last_error_message()
+    assert "2^24" in la.la_last_error_message() and field.split("_")[0] in la.la_last_error_message()
+    if field != "q_stride_t":
+        rc = lib.la_gdn_summary(ctypes.byref(d), a["k"], a["v"], a["g"], a["beta"], a["cu"], None, a["fin"],
+                                a["out"], 1, a["ws"], a["wsb"], None)
+        assert rc == la.LA_ERR_UNSUPPORTED and "2^24" in la.la_last_error_message()
+    # one below the limit passes the stride checks (the call then stops at the fake workspace size)
+    d = _desc(**{field: (1 << 24) - 8})
+    rc = lib.la_gdn_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None,
+                        a["out"], a["fin"], 1, a["ws"], 1024, None)
+    assert rc == la.LA_ERR_WORKSPACE_TOO_SMALL, la.la_last_error_message()
+
+
+def test_output_token_stride_is_not_limited(lib):
+    """o rows are addressed with 64-bit offsets: a huge output stride is accepted."""
+    a = _fwd_args()
+    d = _desc(o_stride_t=1 << 30)
+    rc = lib.la_gdn_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None,
+                        a["out"], a["fin"], 1, a["ws"], 1024, None)
+    assert rc == la.LA_ERR_WORKSPACE_TOO_SMALL, la.la_last_error_message()
+
+
+def test_single_token_any_token_stride(lib):
+    """With one token the token strides are never used (a broadcast view has 0): the
+    checks accept them, and the library replaces them by the rows' own extents."""
+    a = _fwd_args()
+    d = _desc(N=1, T=1, q_stride_t=0, k_stride_t=0, v_stride_t=0, o_stride_t=0, g_stride_t=0, beta_stride_t=0)
+    rc = lib.la_gdn_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], None,
+                        a["out"], a["fin"], 1, a["ws"], 1024, None)
+    assert rc == la.LA_ERR_WORKSPACE_TOO_SMALL, la.la_last_error_message()
+
+
 def test_summary_requires_outputs(lib):
     A = 1 << 20
     d = _desc()

@@ -1,0 +1,90 @@
+"""The chunked method, checked on the CPU against the fp64 token-by-token oracle.
+
+The HIP kernels evaluate the recurrence in 64-token chunks (intra-chunk UT/WY
+solve, inter-chunk state pass).  The model in chunked_model.py writes that
+algebra out in numpy: in fp64 it must equal the oracle to 1e-12 (the chunked
+form is an identity, not an approximation), and its triangular solve must equal
+numpy.linalg.solve.  With bf16 rounding injected where the kernels round, the
+model predicts the kernels' error against the oracle; the precision of the
+kernel design (U~ in fp32 through a bf16 hi/lo pair) is recorded here.
+"""
+import numpy as np
+import pytest
+
+from chunked_model import ALL_BF16, EXACT, KERNEL, chunked_forward, unit_lower_inverse
+from oracle import Oracle, rel_l2
+from workloads import custom_problem, make_problem
+
+
+def test_unit_lower_inverse_equals_linalg_solve():
+    rng = np.random.default_rng(0)
+    for n in (1, 2, 17, 64):
+        A = np.tril(rng.normal(size=(3, n, n)) * 0.3, -1)
+        T = unit_lower_inverse(A)
+        ref = np.linalg.solve(np.eye(n)[None] + A, np.broadcast_to(np.eye(n), (3, n, n)))
+        assert np.max(np.abs(T - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+        assert np.allclose(np.tril(T), T) and np.all(np.diagonal(T, axis1=1, axis2=2) == 1.0)
+
+
+@pytest.mark.parametrize("lengths,hk,hv,dk,dv,l2norm,state", [
+    ((1, 63, 64, 65, 130, 200), 2, 4, 64, 64, True, True),
+    ((300,), 1, 2, 128, 128, True, False),
+    ((129, 0, 70), 2, 2, 64, 128, False, True),
+])
+def test_exact_chunked_model_equals_the_token_recurrence(lengths, hk, hv, dk, dv, l2norm, state):
+    p = custom_problem(lengths, hk=hk, hv=hv, dk=dk, dv=dv, seed=11, with_state=state, l2norm=l2norm)
+    if not l2norm:
+        import dataclasses
+        p = dataclasses.replace(p, k=(p.k.float() / 8).bfloat16(), q=(p.q.float() / 8).bfloat16())
+    o, fin = chunked_forward(p, EXACT)
+    ref = Oracle(p).run_all()
+    assert rel_l2(o, ref["o"]) <= 1e-12
+    assert rel_l2(fin, ref["state"]) <= 1e-12
+
+
+def test_exact_chunked_model_slow_decay_with_initial_state():
+    # the slow-decay companion of the dense batch, cut to two sequences: the initial
+    # state reaches o and the final state
+    p = custom_problem((700, 64), hk=1, hv=4, dk=128, dv=128, seed=12, with_state=True, g_div=4096.0,
+                       beta_div=64.0)
+    o, fin = chunked_forward(p, EXACT)
+    ref = Oracle(p).run_all()
+    assert rel_l2(o, ref["o"]) <= 1e-12 and rel_l2(fin, ref["state"]) <= 1e-12
+
+
+def test_planted_mistakes_in_the_model_are_caught():
+    """The pin is not vacuous: the chunked algebra with a transposed triangular factor,
+    or with the decays inside a chunk left out, is far from the oracle."""
+    import chunked_model as cm
+    p = custom_problem((130,), hk=1, hv=1, dk=64, dv=64, seed=13, with_state=True)
+    ref = Oracle(p).run_all()
+    orig_inv, orig_mask = cm.unit_lower_inverse, cm._masked_exp
+    try:
+        cm.unit_lower_inverse = lambda A: np.transpose(orig_inv(A), (0, 2, 1))
+        o, fin = chunked_forward(p, EXACT)
+        assert rel_l2(fin, ref["state"]) > 1e-2
+        cm.unit_lower_inverse = orig_inv
+        cm._masked_exp = lambda gam, strict: np.where(orig_mask(gam, strict) > 0, 1.0, 0.0)
+        o, fin = chunked_forward(p, EXACT)
+        assert rel_l2(o, ref["o"]) > 1e-2
+    finally:
+        cm.unit_lower_inverse, cm._masked_exp = orig_inv, orig_mask
+    o, fin = chunked_forward(p, EXACT)
+    assert rel_l2(fin, ref["state"]) <= 1e-12
+
+
+def test_kernel_rounding_plan_on_the_varlen_workload():
+    """The kernels' rounding points on the varlen workload (T = 4096, H = 16,
+    K = V = 128): final states and o well inside the tolerances (5e-3 and 1e-2).
+    Recorded: kernel design about 1.8e-3 (final) and 2.9e-3 (o); U~ itself in bf16
+    about twice the final-state error."""
+    p = make_problem(2)
+    ref = Oracle(p).run_all()
+    o, fin = chunked_forward(p, KERNEL)
+    es, eo = rel_l2(fin, ref["state"]), rel_l2(o, ref["o"])
+    print(f"kernel rounding: final {es:.2e}, o {eo:.2e}")
+    assert es <= 2.5e-3 and eo <= 4e-3
+    o2, fin2 = chunked_forward(p, ALL_BF16)
+    es2 = rel_l2(fin2, ref["state"])
+    print(f"U~ in bf16: final {es2:.2e}, o {rel_l2(o2, ref['o']):.2e}")
+    assert es2 > 1.3 * es

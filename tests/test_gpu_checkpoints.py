@@ -10,7 +10,7 @@ import gated_delta_rule_50_amd as la
 from oracle import Oracle, rel_l2
 from workloads import custom_problem, fused_problem, make_problem
 
-from gpu_helpers import TOL_O, TOL_STATE, assert_o_state, f64, gpu_fwd, note
+from gpu_helpers import TOL_O, TOL_STATE, assert_o_state, assert_states, f64, gpu_fwd, note
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def test_series_fp32_against_oracle(every, dk, dv):
     out, fin, ck = fwd_ck(p, every)
     ref = Oracle(p).run_all(checkpoint_every=every)
     assert ck.shape[0] == ref["checkpoints"].shape[0] == la.checkpoint_entries(p.cu_seqlens, every)
-    assert rel_l2(f64(ck), ref["checkpoints"]) <= TOL_STATE
+    assert_states(ck, ref["checkpoints"], TOL_STATE, "state series")
     assert_o_state(out, fin, ref)
     # entry 0 of every non-empty sequence is its initial state, bit for bit
     lens = [1, 63, 64, 65, 0, 200, 257]
@@ -51,7 +51,7 @@ def test_series_bf16_rows_and_outputs_unchanged():
     out, fin, ck = fwd_ck(p, 64, torch.bfloat16)
     assert ck.dtype == torch.bfloat16
     ref = Oracle(p).run_all(checkpoint_every=64)
-    assert rel_l2(f64(ck), ref["checkpoints"]) <= TOL_CK_BF16
+    assert_states(ck, ref["checkpoints"], TOL_CK_BF16, "state series")
     o0, f0 = gpu_fwd(p)
     assert torch.equal(out, o0) and torch.equal(fin, f0)
 
@@ -63,7 +63,7 @@ def test_series_capacity_limits_writes():
     note("series capacity")
     out, fin, ck = fwd_ck(p, 64, checkpoints=buf)
     ref = Oracle(p).run_all(checkpoint_every=64)["checkpoints"]
-    assert rel_l2(f64(ck), ref[:full - 2]) <= TOL_STATE
+    assert_states(ck, ref[:full - 2], TOL_STATE, "state series")
 
 
 def test_series_varlen_h16_and_fused_transforms():
@@ -71,10 +71,10 @@ def test_series_varlen_h16_and_fused_transforms():
     note("series varlen H=16")
     out, fin, ck = fwd_ck(p, 64)
     ref = Oracle(p).run_all(checkpoint_every=64)
-    assert rel_l2(f64(ck), ref["checkpoints"]) <= TOL_STATE
+    assert_states(ck, ref["checkpoints"], TOL_STATE, "state series")
     q = fused_problem((300, 129), hk=2, hv=4, dk=128, dv=128, seed=74, with_state=True)
     note("series with fused gate and beta")
     out, fin, ck = fwd_ck(q, 128)
     ref = Oracle(q).run_all(checkpoint_every=128)
-    assert rel_l2(f64(ck), ref["checkpoints"]) <= TOL_STATE
+    assert_states(ck, ref["checkpoints"], TOL_STATE, "state series")
     assert_o_state(out, None, ref)

@@ -10,7 +10,7 @@ import gated_delta_rule_50_amd as la
 from oracle import Oracle, rel_l2
 from workloads import custom_problem, fused_problem, gdp_problem
 
-from gpu_helpers import TOL_O, TOL_STATE, assert_o_state, f64, note
+from gpu_helpers import TOL_O, TOL_STATE, assert_o_state, assert_states, f64, note
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def test_series_many_sequences():
     torch.cuda.synchronize()
     ref = Oracle(p).run_all(checkpoint_every=64)
     assert ck.shape[0] == ref["checkpoints"].shape[0]
-    assert rel_l2(f64(ck), ref["checkpoints"]) <= TOL_STATE
+    assert_states(ck, ref["checkpoints"], TOL_STATE, "state series")
     assert_o_state(out, None, ref)
 
 

@@ -1,9 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Tolerances: rel-L2 <= 1e-2 for the bf16 output o and <= 5e-3 for fp32 final
-states, end states and transitions.  Small problems compare every element;
-the full-size workloads compare sampled (sequence, head) units, which the
-oracle computes one by one, plus properties that hold at any size.
+states, end states and transitions, over the whole tensor and, within five
+times that, row by row (one token-head of o, one (sequence, head) state or
+transition).  Every element of every workload is compared, the long-context
+and span workloads unit by unit, plus properties that hold at any size.
 """
 import dataclasses
 
@@ -15,7 +16,8 @@ import gated_delta_rule_50_amd as la
 from oracle import Oracle, rel_l2
 from workloads import Problem, custom_problem, make_problem
 
-from gpu_helpers import TOL_O, TOL_STATE, assert_rows_close, check_fwd_full, f64, gpu_fwd, gpu_summary, note
+from gpu_helpers import (TOL_O, TOL_STATE, UnitTally, assert_o_state, assert_rows_close, assert_summary,
+                         check_fwd_full, f64, gpu_fwd, gpu_summary, note)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,8 +47,7 @@ def test_no_l2norm_custom_scale():
     note("no l2norm, scale 0.3")
     out, fin = gpu_fwd(p, scale=0.3)
     ref = Oracle(p, scale=0.3).run_all()
-    assert rel_l2(f64(out), ref["o"]) <= TOL_O
-    assert rel_l2(f64(fin), ref["state"]) <= TOL_STATE
+    assert_o_state(out, fin, ref)
 
 
 def test_summary_small_slow_decay():
@@ -55,8 +56,7 @@ def test_summary_small_slow_decay():
     note("summary small slow decay")
     end, tr = gpu_summary(p)
     ref = Oracle(p).run_all(want_o=False, want_transition=True)
-    assert rel_l2(f64(end), ref["state"]) <= TOL_STATE
-    assert rel_l2(f64(tr), ref["transition"]) <= TOL_STATE
+    assert_summary(end, tr, ref)
     assert np.abs(ref["transition"]).max() > 0.05   # not vacuous
 
 
@@ -66,8 +66,7 @@ def test_summary_small_k64():
     note("summary K=64 V=128")
     end, tr = gpu_summary(p)
     ref = Oracle(p).run_all(want_o=False, want_transition=True)
-    assert rel_l2(f64(end), ref["state"]) <= TOL_STATE
-    assert rel_l2(f64(tr), ref["transition"]) <= TOL_STATE
+    assert_summary(end, tr, ref)
 
 
 def test_empty_sequences_and_identity_transition():
@@ -75,7 +74,7 @@ def test_empty_sequences_and_identity_transition():
     note("empty sequences fwd")
     out, fin = gpu_fwd(p)
     ref = Oracle(p).run_all()
-    assert rel_l2(f64(fin), ref["state"]) <= TOL_STATE
+    assert_o_state(out, fin, ref)
     for n in (0, 2, 4):
         assert torch.equal(fin[n].cpu(), p.state[n])
     ps = dataclasses.replace(p, q=None, summary=True)
@@ -96,6 +95,7 @@ def test_config3_grouped_heads_initial_state():
     first = np.concatenate([np.arange(n * 4096, n * 4096 + 64) for n in range(8)])
     e1 = rel_l2(f64(out)[first], ref["o"][first])
     assert e1 <= TOL_O, e1
+    assert_rows_close(f64(out)[first], ref["o"][first], TOL_O, "first-chunk o rows")
 
 
 def test_config3_slow_decay_companion():
@@ -106,54 +106,71 @@ def test_config3_slow_decay_companion():
     assert rel_l2(no_s0, ref["o"][:4096, 0]) > 0.1
 
 
-def _sample_units(p, units):
-    o = Oracle(p)
-    return o.run_units(units, want_o=True)
+def _all_units_longest_first(o: Oracle):
+    units = o.all_units()
+    lens = o.lengths()
+    units.sort(key=lambda u: -lens[u[0]])
+    return units
 
 
-def test_config4_ragged_long_context_sampled():
+def test_config4_ragged_long_context_every_unit():
+    """Every one of the 65 x 32 (sequence, head) units against the oracle: each unit's o
+    and final state within the tolerance on its own (so that a short sequence cannot
+    hide under the 65536-token one), the whole tensors, and every row."""
     p = make_problem(4)
     note(f"config 4 T={p.total_tokens}")
     out, fin = gpu_fwd(p, initial_state=False)
-    lens = p.lengths()
-    N = len(lens)
-    long_seq = N - 1
-    short = [0, 1] + [i for i in range(2, N - 1) if lens[i] % 64][:3]
-    units = [(long_seq, 0), (long_seq, 31)] + [(s, h) for s, h in zip(short, (3, 7, 11, 19, 27))]
-    ref = _sample_units(p, units)
+    orc = Oracle(p, use_initial_state=False)
+    units = _all_units_longest_first(orc)
+    note(f"config 4 oracle over {len(units)} units")
+    ref = orc.run_units(units, want_o=True)
     cu = p.cu_seqlens.tolist()
-    o64, f64_ = f64(out), f64(fin)
+    out_c, fin_c = out.cpu(), fin.cpu()
+    to, ts = UnitTally(TOL_O, "o"), UnitTally(TOL_STATE, "final state")
     for (n, h), ro, rs in zip(units, ref["o"], ref["state"]):
-        eo = rel_l2(o64[cu[n]:cu[n + 1], h], ro)
-        es = rel_l2(f64_[n, h], rs)
-        assert eo <= TOL_O and es <= TOL_STATE, (n, h, lens[n], eo, es)
-        assert_rows_close(o64[cu[n]:cu[n + 1], h], ro, TOL_O, f"o rows of unit {(n, h)}")
+        to.add(out_c[cu[n]:cu[n + 1], h].double().numpy(), ro, (n, h))
+        ts.add(fin_c[n, h].double().numpy().reshape(1, -1), rs.reshape(1, -1), (n, h))
+    print(f"config 4: o rel-L2 {to.check():.3e}, final state rel-L2 {ts.check():.3e}", flush=True)
 
 
-def test_config5_summary_sampled():
+def test_config5_summary_every_unit():
+    """All 32 x 16 units of the span summary.  Under this gate the exact transition
+    underflows to 0 even in fp64 (e^(sum g) over 8192 tokens), so the transition is
+    checked to be 0 here and compared in earnest on the slow-decay companion below."""
     p = make_problem(5)
     note(f"config 5 T={p.total_tokens}")
     end, tr = gpu_summary(p)
-    units = [(0, 0), (13, 5), (31, 15)]
-    ref = Oracle(p).run_units(units, want_o=False, want_transition=True)
+    orc = Oracle(p)
+    units = _all_units_longest_first(orc)
+    note(f"config 5 oracle over {len(units)} units")
+    ref = orc.run_units(units, want_o=False, want_transition=True)
+    end_c, tr_c = end.cpu(), tr.cpu()
+    te = UnitTally(TOL_STATE, "end state")
     for (n, h), rs, rt in zip(units, ref["state"], ref["transition"]):
-        assert rel_l2(f64(end[n, h]), rs) <= TOL_STATE
-        # under this gate the transition underflows to zero: compare absolutely
-        assert np.abs(f64(tr[n, h]) - rt).max() <= 1e-30
+        te.add(end_c[n, h].double().numpy().reshape(1, -1), rs.reshape(1, -1), (n, h))
+        assert np.abs(rt).max() <= 1e-30
+        assert float(tr_c[n, h].abs().max()) <= 1e-30, (n, h)
+    print(f"config 5: end state rel-L2 {te.check():.3e}", flush=True)
 
 
 def test_config5_companion_summary_and_composition():
-    """Slow-decay companion: sampled units against the oracle, and the fold of
-    all 32 span summaries against one forward pass over the concatenated spans."""
+    """Slow-decay companion: every unit's end state and transition against the oracle,
+    and the fold of all 32 span summaries against one forward pass over the
+    concatenated spans."""
     p = make_problem(5, companion=True)
     note("config 5 companion summary")
     end, tr = gpu_summary(p)
-    units = [(0, 0), (17, 9)]
-    ref = Oracle(p).run_units(units, want_o=False, want_transition=True)
+    orc = Oracle(p)
+    units = _all_units_longest_first(orc)
+    note(f"config 5 companion oracle over {len(units)} units")
+    ref = orc.run_units(units, want_o=False, want_transition=True)
+    end_c, tr_c = end.cpu(), tr.cpu()
+    te, tt = UnitTally(TOL_STATE, "end state"), UnitTally(TOL_STATE, "transition")
     for (n, h), rs, rt in zip(units, ref["state"], ref["transition"]):
-        assert rel_l2(f64(end[n, h]), rs) <= TOL_STATE
-        assert rel_l2(f64(tr[n, h]), rt) <= TOL_STATE
-    assert np.abs(ref["transition"][0]).max() > 0.05
+        te.add(end_c[n, h].double().numpy().reshape(1, -1), rs.reshape(1, -1), (n, h))
+        tt.add(tr_c[n, h].double().numpy().reshape(1, -1), rt.reshape(1, -1), (n, h))
+    print(f"config 5': end state rel-L2 {te.check():.3e}, transition rel-L2 {tt.check():.3e}", flush=True)
+    assert max(float(np.abs(rt).max()) for rt in ref["transition"]) > 0.05   # not vacuous
     # zero-start spans, folded with the transitions
     note("config 5 companion zero-start summary + fold")
     span_end, span_tr = gpu_summary(p, start_state=False)
@@ -166,6 +183,7 @@ def test_config5_companion_summary_and_composition():
     note("config 5 companion unsplit forward")
     _, fin = gpu_fwd(whole)
     assert rel_l2(f64(X), f64(fin[0])) <= TOL_STATE
+    assert_rows_close(f64(X).reshape(16, -1), f64(fin[0]).reshape(16, -1), TOL_STATE, "folded states")
 
 
 # ----------------------------------------------------------------------------
@@ -270,7 +288,32 @@ def test_final_state_null_and_chaining():
         ref = Oracle(p).run_all()
         assert rel_l2(f64(torch.cat([oa, ob])), ref["o"]) <= TOL_O
         assert rel_l2(f64(fb), ref["state"]) <= TOL_STATE
+        assert_o_state(torch.cat([oa, ob]), fb, ref)
     g = p.to("cuda")
     out, fin = la.la_gdn_fwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
                              output_final_state=False)
     assert fin is None and torch.equal(out, o_full)
+
+
+def test_single_token_with_zero_token_strides():
+    """One token given as broadcast views (token stride 0) for every operand, and the
+    output written through a stride-0 view: the same bits as contiguous tensors, and the
+    oracle's values (a single-token decode step)."""
+    p = custom_problem((1,), hk=2, hv=4, dk=128, dv=128, seed=30, with_state=True)
+    g = p.to("cuda")
+
+    def zero_t(t):
+        return torch.as_strided(t, t.shape, (0,) + tuple(t.stride()[1:]))
+
+    out = torch.empty((1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    note("single token, token strides 0")
+    o0, f0 = la.la_gdn_fwd(zero_t(g.q), zero_t(g.k), zero_t(g.v), zero_t(g.g), zero_t(g.beta), g.cu_seqlens,
+                           initial_state=g.state, out=zero_t(out))
+    o1, f1 = gpu_fwd(p)
+    assert torch.equal(o0, o1) and torch.equal(f0, f1)
+    assert_o_state(o0, f0, Oracle(p).run_all())
+    end0, tr0 = la.la_gdn_summary(zero_t(g.k), zero_t(g.v), zero_t(g.g), zero_t(g.beta), g.cu_seqlens,
+                                  start_state=g.state)
+    end1, tr1 = gpu_summary(dataclasses.replace(p, q=None, summary=True))
+    torch.cuda.synchronize()
+    assert torch.equal(end0, end1) and torch.equal(tr0, tr1)
