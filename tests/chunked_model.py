@@ -167,3 +167,148 @@ def chunked_forward(problem, rounding: Rounding = EXACT, scale: Optional[float] 
         if o is not None:
             o[a:e] = on
     return o, fin
+
+
+def chunked_backward_sequence(q, k, v, g, beta, S0, dO, dS_final, scale: float, l2norm: bool,
+                              rounding: Rounding = EXACT, chunk: int = CHUNK):
+    """Gradients of one sequence (all value heads at once) by the chunked method: the
+    forward above run again to get each chunk's start state, then the chunks in reverse
+    with the end-state gradient dS carried from chunk to chunk,
+        dU  = diag(exp(gam_n - gam)) K^ dS + P^T dO
+        dS0 = exp(gam_n) dS + Q^T diag(exp(gam)) dO - W^T dU
+    and, per chunk, the gradients of everything the forward formed from q, k, v, beta
+    and gam (through P, W, U~, T = (I + A)^-1 with dA = -T^T dT T^T, and the decays),
+    then through the chunk-local cumsum to g and through the row norms to q and k.
+    Shapes as chunked_sequence, plus dO [L, H, V] and dS_final [H, K, V].  Returns dq, dk
+    [L, H, K] (per value head; the caller sums a head group), dv [L, H, V], dg, dbeta
+    [L, H] and the start-state gradient [H, K, V]."""
+    L, H, K = k.shape
+    V = v.shape[2]
+    rnd = rounding
+    rk = 1.0 / np.sqrt(np.sum(k * k, axis=2) + 1e-6) if l2norm else np.ones((L, H))
+    rq = 1.0 / np.sqrt(np.sum(q * q, axis=2) + 1e-6) if l2norm else np.ones((L, H))
+    tr = lambda x: np.transpose(x, (0, 2, 1))
+    # forward again: every chunk's start state
+    starts = []
+    S = np.array(S0, dtype=np.float64)
+    for c0 in range(0, L, chunk):
+        starts.append(S)
+        c1 = min(c0 + chunk, L)
+        _, S = chunked_sequence(None, k[c0:c1], v[c0:c1], g[c0:c1], beta[c0:c1], S, scale, l2norm, rounding,
+                                chunk)
+    dq = np.zeros((L, H, K))
+    dk = np.zeros((L, H, K))
+    dv = np.zeros((L, H, V))
+    dg = np.zeros((L, H))
+    db = np.zeros((L, H))
+    dS = np.array(dS_final, dtype=np.float64)
+    for ci in range(len(starts) - 1, -1, -1):
+        c0 = ci * chunk
+        c1 = min(c0 + chunk, L)
+        S0c = starts[ci]
+        Kc = np.transpose(k[c0:c1], (1, 0, 2))             # [H, n, K]
+        Qc = np.transpose(q[c0:c1], (1, 0, 2))
+        Vc = np.transpose(v[c0:c1], (1, 0, 2))
+        dOc = np.transpose(dO[c0:c1], (1, 0, 2))
+        b = beta[c0:c1].T
+        gam = np.cumsum(g[c0:c1].T, axis=1)
+        r, s_q = rk[c0:c1].T, rq[c0:c1].T
+        Kh = r[:, :, None] * Kc
+        Qh = scale * s_q[:, :, None] * Qc
+        eg = np.exp(gam)
+        gn = gam[:, -1]
+        d = np.exp(gn[:, None] - gam)
+        Eg = _masked_exp(gam, strict=True)
+        G = Kh @ tr(Kh)
+        A = b[:, :, None] * Eg * G
+        T = unit_lower_inverse(A)
+        f = b * eg
+        W = T @ (f[:, :, None] * Kh)
+        U = T @ (b[:, :, None] * Vc) - W @ S0c
+        M = _masked_exp(gam, strict=False)
+        P = M * (Qh @ tr(Kh))
+        # the carried gradient
+        dU = d[:, :, None] * (Kh @ dS) + tr(P) @ dOc
+        dS_prev = np.exp(gn)[:, None, None] * dS + tr(Qh) @ (eg[:, :, None] * dOc) - tr(W) @ dU
+        # q, k through P and the output's state term; k through the state update
+        dP = M * (dOc @ tr(U))
+        dQh = eg[:, :, None] * (dOc @ tr(S0c)) + dP @ Kh
+        UdS = U @ tr(dS)                                    # [H, n, K]
+        dKh = tr(dP) @ Qh + d[:, :, None] * UdS
+        # W = T diag(f) K^ and U~ = T diag(beta) V
+        dW = -(dU @ tr(S0c))
+        X1 = tr(T) @ dW
+        X2 = tr(T) @ dU
+        dKh += f[:, :, None] * X1
+        df = np.sum(X1 * Kh, axis=2)
+        dVc = b[:, :, None] * X2
+        dbc = np.sum(X2 * Vc, axis=2) + df * eg
+        dgam = df * f
+        dT = dW @ tr(f[:, :, None] * Kh) + dU @ tr(b[:, :, None] * Vc)
+        dA = -(tr(T) @ dT @ tr(T)) * np.tril(np.ones_like(A[0]), -1)
+        dGm = dA * b[:, :, None] * Eg
+        dKh += (dGm + tr(dGm)) @ Kh
+        dbc += np.sum(dA * Eg * G, axis=2)
+        aA = dA * A
+        dgam += np.sum(aA, axis=2) - np.sum(aA, axis=1)
+        pP = (dOc @ tr(U)) * P                          # dP o P (zero outside the mask)
+        dgam += np.sum(pP, axis=2) - np.sum(pP, axis=1)
+        dgam += eg * np.sum((Qh @ S0c) * dOc, axis=2)
+        F = d * np.sum(Kh * UdS, axis=2)
+        dgam -= F
+        dgam[:, -1] += np.sum(F, axis=1) + np.exp(gn) * np.sum(dS * S0c, axis=(1, 2))
+        # chunk-local cumsum, then the row norms
+        dgc = np.cumsum(dgam[:, ::-1], axis=1)[:, ::-1]
+        if l2norm:
+            dKc = r[:, :, None] * dKh - (r ** 3 * np.sum(Kc * dKh, axis=2))[:, :, None] * Kc
+            dQc = scale * (s_q[:, :, None] * dQh - (s_q ** 3 * np.sum(Qc * dQh, axis=2))[:, :, None] * Qc)
+        else:
+            dKc = dKh
+            dQc = scale * dQh
+        dq[c0:c1] = np.transpose(dQc, (1, 0, 2))
+        dk[c0:c1] = np.transpose(dKc, (1, 0, 2))
+        dv[c0:c1] = np.transpose(dVc, (1, 0, 2))
+        dg[c0:c1] = dgc.T
+        db[c0:c1] = dbc.T
+        dS = dS_prev
+    return dq, dk, dv, dg, db, dS
+
+
+def chunked_backward(problem, d_o, d_final=None, rounding: Rounding = EXACT, scale: Optional[float] = None):
+    """Gradients of a workloads.Problem's forward (plain gate and beta) for upstream
+    gradients d_o [T, HV, V] and d_final [N, HV, K, V] (None: zeros), by the chunked
+    method: dq, dk [T, HK, K] (summed over each head group), dv [T, HV, V], dg, dbeta
+    [T, HV] and d_init [N, HV, K, V]."""
+    p = problem
+    k = p.k.float().double().numpy()
+    v = p.v.float().double().numpy()
+    q = p.q.float().double().numpy()
+    g = p.g.double().numpy()
+    beta = p.beta.double().numpy()
+    HK, HV = k.shape[1], v.shape[1]
+    K, V = k.shape[2], v.shape[2]
+    G = HV // HK
+    rep = np.arange(HV) // G
+    sc = K ** -0.5 if scale is None else scale
+    cu = p.cu_seqlens.tolist()
+    N = len(cu) - 1
+    T = cu[-1]
+    d_o = np.asarray(d_o, dtype=np.float64)
+    out = {"dq": np.zeros((T, HK, K)), "dk": np.zeros((T, HK, K)), "dv": np.zeros((T, HV, V)),
+           "dg": np.zeros((T, HV)), "dbeta": np.zeros((T, HV)), "d_init": np.zeros((N, HV, K, V))}
+    for n in range(N):
+        a, e = cu[n], cu[n + 1]
+        dF = np.zeros((HV, K, V)) if d_final is None else np.asarray(d_final[n], dtype=np.float64)
+        if e == a:
+            out["d_init"][n] = dF
+            continue
+        S0 = p.state[n].double().numpy() if p.state is not None else np.zeros((HV, K, V))
+        dq, dk, dv, dg, db, di = chunked_backward_sequence(q[a:e][:, rep], k[a:e][:, rep], v[a:e], g[a:e],
+                                                           beta[a:e], S0, d_o[a:e], dF, sc, p.l2norm, rounding)
+        out["dq"][a:e] = dq.reshape(e - a, HK, G, K).sum(axis=2)
+        out["dk"][a:e] = dk.reshape(e - a, HK, G, K).sum(axis=2)
+        out["dv"][a:e] = dv
+        out["dg"][a:e] = dg
+        out["dbeta"][a:e] = db
+        out["d_init"][n] = di
+    return out

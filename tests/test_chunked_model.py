@@ -88,3 +88,30 @@ def test_kernel_rounding_plan_on_the_varlen_workload():
     es2 = rel_l2(fin2, ref["state"])
     print(f"U~ in bf16: final {es2:.2e}, o {rel_l2(o2, ref['o']):.2e}")
     assert es2 > 1.3 * es
+
+
+@pytest.mark.parametrize("lengths,hk,hv,dk,dv,l2norm", [
+    ((1, 63, 64, 65, 130), 2, 4, 64, 64, True),
+    ((200, 0, 70), 1, 1, 64, 128, False),
+    ((129,), 2, 2, 128, 64, True),
+])
+def test_exact_chunked_backward_equals_the_oracle_backward(lengths, hk, hv, dk, dv, l2norm):
+    """The chunked backward (reverse chunk pass for the state gradient, then every
+    chunk's gradients through P, W, U~, T = (I + A)^-1 and the decays) equals the
+    oracle's token-by-token backward, itself pinned by autograd and central differences."""
+    import dataclasses
+
+    import torch
+
+    import oracle
+    from chunked_model import chunked_backward
+    p = custom_problem(lengths, hk=hk, hv=hv, dk=dk, dv=dv, seed=14, with_state=True, l2norm=l2norm)
+    if not l2norm:
+        p = dataclasses.replace(p, k=(p.k.float() / 8).bfloat16(), q=(p.q.float() / 8).bfloat16())
+    gen = torch.Generator().manual_seed(15)
+    dO = torch.randn((p.total_tokens, hv, dv), generator=gen).double().numpy()
+    dF = torch.randn((p.num_seqs, hv, dk, dv), generator=gen).double().numpy()
+    ref = oracle.backward(p, d_o=dO, d_final=dF)
+    got = chunked_backward(p, dO, dF)
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "d_init"):
+        assert rel_l2(got[name], ref[name]) <= 1e-12, name
