@@ -46,7 +46,7 @@ LA_KERNEL_COUNT = 3
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
     "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex", "la_gdn_workspace_bytes_ex",
-    "la_gdn_summary_bwd", "la_gdn_device_status",
+    "la_gdn_summary_bwd", "la_gdn_fwd_noalloc", "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
 
@@ -122,6 +122,8 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_summary_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
     lib.la_gdn_summary_bwd.restype = ctypes.c_int
     lib.la_gdn_summary_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.la_gdn_fwd_noalloc.restype = ctypes.c_int
+    lib.la_gdn_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.la_gdn_device_status.restype = i32
     lib.la_gdn_device_status.argtypes = [vp, vp]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -231,6 +233,23 @@ def la_gdn_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final
     _check(lib.la_gdn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                           _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
                           int(bool(l2norm)), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, final_state
+
+
+def la_gdn_fwd_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None, out=None, final_state=None,
+                       l2norm: bool = True, scale: Optional[float] = None, stream=None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """la_gdn_fwd with the library's fixed scratch array as the workspace (no device
+    allocation in the call).  `out` (and `final_state`, if wanted) must be given; the
+    binding allocates nothing either.  Calls that overlap on one GPU race on the array."""
+    if out is None:
+        raise ValueError("la_gdn_fwd_noalloc: pass out (and final_state): the call allocates nothing")
+    lib = load_library()
+    N = cu_seqlens.numel() - 1
+    desc = make_desc(k, v, g, beta, N, q=q, out=out, scale=scale)
+    _check(lib.la_gdn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                  int(bool(l2norm)), _stream(stream)))
     return out, final_state
 
 

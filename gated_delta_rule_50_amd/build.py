@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libla_gdn.so")
-SOURCES = [os.path.join(CSRC, "la_gdn_kernels.hip"), os.path.join(CSRC, "la_gdn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "la_gdn_kernels.hip"), os.path.join(CSRC, "la_gdn_api.cpp"),
+           os.path.join(CSRC, "la_gdn_noalloc.hip")]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions
 # (the host pass warns that it does not know the feature; that is harmless).

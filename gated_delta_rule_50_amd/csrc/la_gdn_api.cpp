@@ -444,6 +444,8 @@ la_status launch(la::Prob p, void *workspace, size_t workspace_bytes, bool summa
 
 namespace la {
 
+la_status fail_message(la_status st, const char *msg) { return fail(st, "%s", msg); }
+
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V, bool summary)
 {
     (void)HK;

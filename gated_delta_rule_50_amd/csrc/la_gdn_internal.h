@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "la_gdn.h"
+
 namespace la {
 
 constexpr int kChunk = 64;            // tokens per chunk; chunks restart at every sequence start
@@ -96,6 +98,9 @@ struct SbwdArgs {
     int32_t *status;
 };
 hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t stream, const LaunchHook *hook);
+
+// Sets the calling thread's error message (la_last_error_message) and returns st.
+la_status fail_message(la_status st, const char *msg);
 
 // Enqueues the whole pipeline (scheduler, intra, inter) on `stream`.
 hipError_t run_pipeline(const Prob &p, const Ws &w, bool summary, hipStream_t stream,

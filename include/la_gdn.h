@@ -258,6 +258,25 @@ la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void 
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * la_gdn_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Arguments and
+ * results are those of la_gdn_fwd (the same checks, kernels and bits) without the
+ * workspace: the library's own fixed scratch array serves as it.  That array is 64 MiB
+ * per device, held from the first launch on that device until the process ends; a
+ * problem whose la_gdn_workspace_bytes(desc, 0) exceeds it is declined with
+ * LA_ERR_WORKSPACE_TOO_SMALL before any launch.  The call allocates nothing (no
+ * hipMalloc or hipFree, no allocating library routine); its first call on a device
+ * looks the array's address up once.  Every call on one GPU shares the array, which
+ * keeps the last call's contents (the kernels need nothing in it to start at zero):
+ * calls that overlap on one GPU race.  The device status word lives in the array, so
+ * la_gdn_device_status cannot read it; a malformed cu_seqlens still writes nothing.
+ */
+la_status la_gdn_fwd_noalloc(const la_gdn_desc *desc, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const int32_t *cu_seqlens,
+                             const float *initial_state, void *out, float *final_state, int l2norm,
+                             hipStream_t stream);
+
+/*
  * Reads the status word the last call on this workspace left (LA_DEVICE_*
  * bits).  Synchronises the stream.  Returns -1 if the read itself failed.
  */
