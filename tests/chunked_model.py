@@ -227,33 +227,43 @@ def chunked_backward_sequence(q, k, v, g, beta, S0, dO, dS_final, scale: float, 
         U = T @ (b[:, :, None] * Vc) - W @ S0c
         M = _masked_exp(gam, strict=False)
         P = M * (Qh @ tr(Kh))
-        # the carried gradient
-        dU = d[:, :, None] * (Kh @ dS) + tr(P) @ dOc
-        dS_prev = np.exp(gn)[:, None, None] * dS + tr(Qh) @ (eg[:, :, None] * dOc) - tr(W) @ dU
+        # the carried gradient (B(.): where the kernels round an MFMA operand to bf16)
+        B = rnd.r16
+        if not rnd.exact:
+            Tw = B(T * (f * r)[:, None, :])
+            W = B(Tw @ Kc)                                  # as the forward's intra pass forms it
+            TB = T * b[:, None, :]
+            hi = bf16(TB)
+            Ut = f32(hi @ Vc + bf16(TB - hi) @ Vc)
+            U = f32(Ut - W @ B(S0c))
+        dU = d[:, :, None] * (Kh @ B(dS)) + B(tr(P)) @ dOc
+        dS_prev = (np.exp(gn)[:, None, None] * dS + tr(Qc) @ B(scale * (s_q * eg)[:, :, None] * dOc)
+                   - tr(W) @ B(dU))
         # q, k through P and the output's state term; k through the state update
-        dP = M * (dOc @ tr(U))
-        dQh = eg[:, :, None] * (dOc @ tr(S0c)) + dP @ Kh
-        UdS = U @ tr(dS)                                    # [H, n, K]
-        dKh = tr(dP) @ Qh + d[:, :, None] * UdS
+        dP = M * (dOc @ tr(B(U)))
+        dQh = eg[:, :, None] * (dOc @ tr(B(S0c))) + B(dP * r[:, None, :]) @ Kc
+        UdS = B(U) @ tr(B(dS))                              # [H, n, K]
+        dKh = tr(B(dP * scale * s_q[:, :, None])) @ Qc + d[:, :, None] * UdS
         # W = T diag(f) K^ and U~ = T diag(beta) V
-        dW = -(dU @ tr(S0c))
-        X1 = tr(T) @ dW
-        X2 = tr(T) @ dU
+        Tb = B(T)
+        dW = -(B(dU) @ tr(B(S0c)))
+        X1 = tr(Tb) @ B(dW)
+        X2 = tr(Tb) @ B(dU)
         dKh += f[:, :, None] * X1
         df = np.sum(X1 * Kh, axis=2)
         dVc = b[:, :, None] * X2
         dbc = np.sum(X2 * Vc, axis=2) + df * eg
         dgam = df * f
-        dT = dW @ tr(f[:, :, None] * Kh) + dU @ tr(b[:, :, None] * Vc)
-        dA = -(tr(T) @ dT @ tr(T)) * np.tril(np.ones_like(A[0]), -1)
+        dT = (B(dW) @ tr(Kc)) * (f * r)[:, None, :] + (B(dU) @ tr(Vc)) * b[:, None, :]
+        dA = -(tr(Tb) @ B(B(dT) @ tr(Tb))) * np.tril(np.ones_like(A[0]), -1)
         dGm = dA * b[:, :, None] * Eg
-        dKh += (dGm + tr(dGm)) @ Kh
+        dKh += B(dGm * r[:, None, :]) @ Kc + B(tr(dGm) * r[:, None, :]) @ Kc
         dbc += np.sum(dA * Eg * G, axis=2)
         aA = dA * A
         dgam += np.sum(aA, axis=2) - np.sum(aA, axis=1)
-        pP = (dOc @ tr(U)) * P                          # dP o P (zero outside the mask)
+        pP = (dOc @ tr(B(U))) * P                       # dP o P (zero outside the mask)
         dgam += np.sum(pP, axis=2) - np.sum(pP, axis=1)
-        dgam += eg * np.sum((Qh @ S0c) * dOc, axis=2)
+        dgam += eg * np.sum((Qh @ B(S0c)) * dOc, axis=2)
         F = d * np.sum(Kh * UdS, axis=2)
         dgam -= F
         dgam[:, -1] += np.sum(F, axis=1) + np.exp(gn) * np.sum(dS * S0c, axis=(1, 2))
