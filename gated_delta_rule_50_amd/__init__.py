@@ -19,6 +19,8 @@ Entry points with the C names take torch tensors:
     la_gdn_summary_ex(..., beta_sigmoid=False, a_log=None, dt_bias=None, ...):
         the same with the gate / beta transforms fused into the kernels and, for the
         forward, the state series
+    la_gdn_bwd(q, k, v, g, beta, cu_seqlens, d_out, initial_state=None, d_final_state=None, ...)
+        -> dict of dq, dk, dv, dg, dbeta, d_initial_state (fp32): the full backward
     la_gdn_workspace_bytes(...), la_gdn_device_status(workspace),
     la_last_error_message(), la_gdn_profile_enable(on), la_gdn_profile_read(id)
 """
@@ -40,13 +42,13 @@ LA_ERR_WORKSPACE_TOO_SMALL = 3
 LA_ERR_HIP = 4
 LA_DEVICE_OK = 0
 LA_DEVICE_BAD_CU_SEQLENS = 1
-LA_KERNEL_SCHED, LA_KERNEL_INTRA, LA_KERNEL_INTER = 0, 1, 2
-LA_KERNEL_COUNT = 3
+LA_KERNEL_SCHED, LA_KERNEL_INTRA, LA_KERNEL_INTER, LA_KERNEL_BWD_INTRA = 0, 1, 2, 3
+LA_KERNEL_COUNT = 4
 
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
     "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex", "la_gdn_workspace_bytes_ex",
-    "la_gdn_summary_bwd", "la_gdn_fwd_noalloc", "la_gdn_device_status",
+    "la_gdn_summary_bwd", "la_gdn_bwd_workspace_bytes", "la_gdn_bwd", "la_gdn_fwd_noalloc", "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
 
@@ -122,6 +124,10 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_summary_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, op, vp, sz, vp]
     lib.la_gdn_summary_bwd.restype = ctypes.c_int
     lib.la_gdn_summary_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.la_gdn_bwd_workspace_bytes.restype = sz
+    lib.la_gdn_bwd_workspace_bytes.argtypes = [dp]
+    lib.la_gdn_bwd.restype = ctypes.c_int
+    lib.la_gdn_bwd.argtypes = [dp] + [vp] * 15 + [ctypes.c_int, vp, sz, vp]
     lib.la_gdn_fwd_noalloc.restype = ctypes.c_int
     lib.la_gdn_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.la_gdn_device_status.restype = i32
@@ -412,6 +418,46 @@ def la_gdn_summary_bwd(q, k, g, beta, cu_seqlens, d_out, d_end_state=None, d_sta
                                   _ptr(d_out), _ptr(d_end_state), _ptr(d_start_state), int(bool(l2norm)),
                                   _ptr(workspace), workspace.numel(), _stream(stream)))
     return d_start_state
+
+
+def la_gdn_bwd_workspace_bytes(desc: Desc) -> int:
+    n = load_library().la_gdn_bwd_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise LaError(LA_ERR_INVALID_ARGUMENT, la_last_error_message())
+    return int(n)
+
+
+def la_gdn_bwd(q, k, v, g, beta, cu_seqlens, d_out, initial_state=None, d_final_state=None,
+               l2norm: bool = True, scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None, out: Optional[dict] = None) -> dict:
+    """Gradients of la_gdn_fwd for the upstream gradients d_out [T, HV, V] (bf16) and
+    d_final_state [N, HV, K, V] (fp32, None: zeros).  Returns a dict of fp32 tensors dq, dk
+    [T, HK, K], dv [T, HV, V], dg, dbeta [T, HV] and d_initial_state [N, HV, K, V] (`out`
+    may hold preallocated ones)."""
+    lib = load_library()
+    if d_out.dtype != torch.bfloat16 or cu_seqlens.dtype != torch.int32 or beta.dtype != torch.float32:
+        raise ValueError("d_out must be bf16, cu_seqlens int32 and beta fp32")
+    N = cu_seqlens.numel() - 1
+    T, HK, K = k.shape
+    HV, V = v.shape[1], v.shape[2]
+    dev = v.device
+    shapes = {"dq": (T, HK, K), "dk": (T, HK, K), "dv": (T, HV, V), "dg": (T, HV), "dbeta": (T, HV),
+              "d_initial_state": (N, HV, K, V)}
+    res = dict(out or {})
+    for name, shp in shapes.items():
+        if name not in res:
+            res[name] = torch.empty(shp, dtype=torch.float32, device=dev)
+        t = res[name]
+        if t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {shp}")
+    desc = make_desc(k, v, g, beta, N, q=q, out=d_out, scale=scale)
+    if workspace is None:
+        workspace = torch.empty(la_gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    _check(lib.la_gdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                          _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(res["dq"]), _ptr(res["dk"]),
+                          _ptr(res["dv"]), _ptr(res["dg"]), _ptr(res["dbeta"]), _ptr(res["d_initial_state"]),
+                          int(bool(l2norm)), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return res
 
 
 def la_gdn_device_status(workspace: torch.Tensor, stream=None) -> int:

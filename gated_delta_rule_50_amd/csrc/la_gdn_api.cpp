@@ -446,10 +446,12 @@ namespace la {
 
 la_status fail_message(la_status st, const char *msg) { return fail(st, "%s", msg); }
 
-WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V, bool summary)
+WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V, bool summary,
+                          int bwd)
 {
     (void)HK;
     WsLayout L{};
+    const bool fwd_ops = bwd != 1;          // the forward's operands (forward, summary, full backward)
     const int64_t C = (T + 63) / 64 + N;   // chunk ids
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -461,11 +463,22 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     L.seq_info = take(sizeof(int4) * (size_t)N);
     L.chunks = take(sizeof(int4) * (size_t)C);
     L.order = take(sizeof(int32_t) * (size_t)N);
-    L.WF = take((size_t)(C * HV) * 64 * K * 2);           // 64 x K bf16
-    L.PF = take(summary ? 0 : (size_t)(C * HV) * 6 * la::kFrag);
-    L.UF = take((size_t)(C * HV) * 64 * V * 4);           // 64 x V fp32
-    L.SC = take((size_t)(C * HV) * la::kScalars * 4);
+    const size_t items = (size_t)(C * HV);
+    L.WF = take(fwd_ops ? items * 64 * K * 2 : 0);        // 64 x K bf16
+    L.PF = take(summary || !fwd_ops ? 0 : items * 6 * la::kFrag);
+    L.UF = take(fwd_ops ? items * 64 * V * 4 : 0);        // 64 x V fp32
+    L.SC = take(items * la::kScalars * 4);
     L.cu32 = take(sizeof(int32_t) * (size_t)(N + 1));
+    L.WTF = take(bwd ? items * 64 * K * 2 : 0);
+    L.PTF = take(bwd ? items * 6 * la::kFrag : 0);
+    L.TB = take(bwd == 2 ? items * 64 * 64 * 2 : 0);
+    L.SB = take(bwd == 2 ? items * la::kScalars * 4 : 0);
+    L.CK = take(bwd == 2 ? items * K * V * 4 : 0);
+    L.DSN = take(bwd == 2 ? items * K * V * 4 : 0);
+    L.DU = take(bwd == 2 ? items * 64 * V * 4 : 0);
+    L.OB = take(bwd == 2 ? (size_t)T * HV * V * 2 : 0);
+    L.DQH = take(bwd == 2 ? (size_t)T * HV * K * 4 : 0);
+    L.DKH = take(bwd == 2 ? (size_t)T * HV * K * 4 : 0);
     L.total = off;
     return L;
 }
@@ -483,6 +496,16 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.UF = reinterpret_cast<float4 *>(b + L.UF);
     w.SC = reinterpret_cast<float *>(b + L.SC);
     w.cu32 = reinterpret_cast<int32_t *>(b + L.cu32);
+    w.WTF = reinterpret_cast<uint4 *>(b + L.WTF);
+    w.PTF = reinterpret_cast<uint4 *>(b + L.PTF);
+    w.TB = reinterpret_cast<uint4 *>(b + L.TB);
+    w.SB = reinterpret_cast<float *>(b + L.SB);
+    w.CK = reinterpret_cast<float *>(b + L.CK);
+    w.DSN = reinterpret_cast<float *>(b + L.DSN);
+    w.DU = reinterpret_cast<float *>(b + L.DU);
+    w.OB = reinterpret_cast<__bf16 *>(b + L.OB);
+    w.DQH = reinterpret_cast<float *>(b + L.DQH);
+    w.DKH = reinterpret_cast<float *>(b + L.DKH);
     return w;
 }
 
@@ -616,8 +639,7 @@ la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void 
     const int64_t T = d.total_tokens;
     if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
     if ((st = check_thd("k", k, d.k_stride_t, d.k_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
-    if ((st = check_thd("d_out", d_out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T, false)) !=
-        LA_OK)
+    if ((st = check_thd("d_out", d_out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK)
         return st;
     if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
     if ((st = check_beta_and_fusion(beta, d, nullptr)) != LA_OK) return st;
@@ -632,24 +654,90 @@ la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void 
     p.g = g;
     p.beta = beta;
     p.cu = cu_seqlens;
+    normalize_single_token(p, nullptr);
     if (p.N == 0) return LA_OK;
-    // the status word, then the row norms (2 T HK floats): within the summary's workspace
-    const size_t need = 256 + sizeof(float) * 2 * (size_t)(T * d.num_qk_heads);
+    // the reverse pass's operands fit in the summary's workspace (the size the header names)
     const size_t have_min = la::workspace_layout(p.N, p.T, p.HK, p.HV, p.K, p.V, true).total;
     if (!workspace) return fail(LA_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(LA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    if (workspace_bytes < have_min || workspace_bytes < need)
-        return fail(LA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes,
-                    have_min > need ? have_min : need);
-    la::SbwdArgs a{};
-    a.p = &p;
+    if (workspace_bytes < have_min)
+        return fail(LA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, have_min);
+    const la::WsLayout L = la::workspace_layout(p.N, p.T, p.HK, p.HV, p.K, p.V, false, 1);
+    const la::Ws w = la::carve_workspace(workspace, L, false);
+    const hipError_t e = la::run_summary_bwd(p, w, static_cast<const __bf16 *>(d_out), d_end_state, d_start_state,
+                                             stream, current_hook());
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
+size_t la_gdn_bwd_workspace_bytes(const la_gdn_desc *desc)
+{
+    if (check_desc(desc) != LA_OK) return 0;
+    return la::workspace_layout(desc->num_seqs, desc->total_tokens, desc->num_qk_heads, desc->num_v_heads,
+                                desc->head_dim_k, desc->head_dim_v, false, 2)
+        .total;
+}
+
+la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                     const float *d_final_state, float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                     float *d_initial_state, int l2norm, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream)
+{
+    g_error.clear();
+    la_status st = check_desc(desc);
+    if (st != LA_OK) return st;
+    const la_gdn_desc &d = *desc;
+    const int64_t T = d.total_tokens;
+    if ((st = check_thd("q", q, d.q_stride_t, d.q_stride_h, d.num_qk_heads, d.head_dim_k, T)) != LA_OK) return st;
+    if ((st = check_kvb(d, k, v, nullptr)) != LA_OK) return st;
+    if ((st = check_thd("d_out", d_out, d.o_stride_t, d.o_stride_h, d.num_v_heads, d.head_dim_v, T)) != LA_OK)
+        return st;
+    if ((st = check_rows("g", g, d.g_stride_t, d.num_v_heads, T)) != LA_OK) return st;
+    if ((st = check_beta_and_fusion(beta, d, nullptr)) != LA_OK) return st;
+    if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+    if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if ((st = check_f32("initial_state", initial_state, false)) != LA_OK) return st;
+    if ((st = check_f32("d_final_state", d_final_state, false)) != LA_OK) return st;
+    if ((st = check_f32("dq", dq, true)) != LA_OK) return st;
+    if ((st = check_f32("dk", dk, true)) != LA_OK) return st;
+    if ((st = check_f32("dv", dv, true)) != LA_OK) return st;
+    if ((st = check_f32("dg", dg, true)) != LA_OK) return st;
+    if ((st = check_f32("dbeta", dbeta, true)) != LA_OK) return st;
+    if ((st = check_f32("d_initial_state", d_initial_state, true)) != LA_OK) return st;
+
+    la::Prob p = make_prob(desc, l2norm);
+    p.q = static_cast<const __bf16 *>(q);
+    p.k = static_cast<const __bf16 *>(k);
+    p.v = static_cast<const __bf16 *>(v);
+    p.g = g;
+    p.beta = beta;
+    p.kstu = p.kst;
+    p.vstu = p.vst;
+    p.bstu = p.bst;
+    p.inv_nh = 1.0f;
+    p.cu = cu_seqlens;
+    p.s0 = initial_state;
+    normalize_single_token(p, nullptr);
+    if (p.N == 0) return LA_OK;
+    const la::WsLayout L = la::workspace_layout(p.N, p.T, p.HK, p.HV, p.K, p.V, false, 2);
+    if (!workspace) return fail(LA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.total)
+        return fail(LA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+    const la::Ws w = la::carve_workspace(workspace, L, false);
+    la::BwdArgs a{};
     a.d_out = static_cast<const __bf16 *>(d_out);
-    a.d_end = d_end_state;
-    a.d_start = d_start_state;
-    a.status = static_cast<int32_t *>(workspace);
-    a.rn = reinterpret_cast<float *>(static_cast<char *>(workspace) + 256);
-    const hipError_t e = la::run_summary_bwd(a, stream, current_hook());
+    a.d_final = d_final_state;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dg = dg;
+    a.dbeta = dbeta;
+    a.d_init = d_initial_state;
+    const hipError_t e = la::run_backward(p, w, a, stream, current_hook());
     if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return LA_OK;
 }
@@ -717,7 +805,7 @@ la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *laun
 
 const char *la_gdn_kernel_name(int32_t kernel_id)
 {
-    static const char *names[LA_KERNEL_COUNT] = {"k_sched", "k_intra", "k_inter"};
+    static const char *names[LA_KERNEL_COUNT] = {"k_sched", "k_intra", "k_inter", "k_bwd_intra"};
     return (kernel_id >= 0 && kernel_id < LA_KERNEL_COUNT) ? names[kernel_id] : "";
 }
 

@@ -65,14 +65,28 @@ struct Ws {
     float *SC;         // [chunk, HV, kScalars]  per token: d = 2^(gam_n - gam) r_k at 0,
                        // sq = scale r_q 2^gam at 64 (forward); gl = 2^gam_n at 192
     int32_t *cu32;     // [N + 1]  int32 copy of int64 cu_seqlens (when given as int64)
+    // backward only (see workspace_layout's `bwd`):
+    uint4 *WTF;        // [chunk, HV][K/32 key tiles][4 token steps]  -W^T A fragments (tokens in
+                       // accumulator order)
+    uint4 *PTF;        // [chunk, HV][3 causal tiles (s, t) = (0,0), (0,1), (1,1)][2]  P^T A fragments
+    uint4 *TB;         // [chunk, HV][64 x 64]  T = (I + A)^-1 in bf16, row-major (full backward)
+    float *SB;         // [chunk, HV, kScalars]  gam (log2) at 0, r_k at 64, r_q at 128, beta at 192
+    float *CK;         // [chunk, HV, K, V]  fp32 state at each chunk's start (full backward)
+    float *DSN;        // [chunk, HV, K, V]  gradient of each chunk's end state (full backward)
+    float *DU;         // [chunk, HV, 64, V]  gradient of each chunk's U (full backward)
+    __bf16 *OB;        // [T, HV, V]  the recomputed forward's output (unused, full backward)
+    float *DQH, *DKH;  // [T, HV, K]  per value head: gradients of the scaled, normalised q and k rows
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.
+// `bwd`: 0 forward or summary; 1 the span summary's state-gradient mirror (the reverse
+// pass's operands only); 2 the full backward (the forward's operands, the reverse pass's,
+// and the per-chunk states and gradients the backward's intra pass reads).
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, cu32, total;
+    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, cu32, WTF, PTF, TB, SB, CK, DSN, DU, OB, DQH, DKH, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
-                          bool summary);
+                          bool summary, int bwd = 0);
 Ws carve_workspace(void *base, const WsLayout &L, bool summary);
 
 // Launch-time timing hook: called before and after each kernel with its id.
@@ -87,17 +101,21 @@ struct LaunchHook {
 hipError_t convert_cu64(const int64_t *src, int32_t *dst, int n, hipStream_t stream);
 
 // Span summary's state-gradient mirror: dS_start from the span's output gradients and
-// dS_end.  `rn` holds 2 T HK floats of workspace (the row norms), `status` the device
-// status word.
-struct SbwdArgs {
-    const Prob *p;                    // q, k, g, beta, cu, strides, scale, l2norm (o strides: d_out)
-    const __bf16 *d_out;              // [T, HV, V] with the o strides
-    const float *d_end;               // [N, HV, K, V] or null (zeros)
-    float *d_start;                   // [N, HV, K, V]
-    float *rn;                        // [T HK][2] inverse norms of the q and k rows
-    int32_t *status;
+// dS_end (the intra pass in its reverse-operand mode, then the reverse chunk pass), on the
+// workspace carved with bwd = 1.  d_out takes p's o strides.
+hipError_t run_summary_bwd(const Prob &p, const Ws &w, const __bf16 *d_out, const float *d_end, float *d_start,
+                           hipStream_t stream, const LaunchHook *hook);
+
+// The full backward: gradients of the forward for upstream gradients of o and of the final
+// states (the recomputed forward, the reverse chunk pass and the backward's intra pass) on
+// the workspace carved with bwd = 2.  d_out takes p's o strides; every output is contiguous
+// fp32: dq, dk [T, HK, K], dv [T, HV, V], dg, dbeta [T, HV], d_init [N, HV, K, V].
+struct BwdArgs {
+    const __bf16 *d_out;
+    const float *d_final;             // or null (zeros)
+    float *dq, *dk, *dv, *dg, *dbeta, *d_init;
 };
-hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t stream, const LaunchHook *hook);
+hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_t stream, const LaunchHook *hook);
 
 // Sets the calling thread's error message (la_last_error_message) and returns st.
 la_status fail_message(la_status st, const char *msg);

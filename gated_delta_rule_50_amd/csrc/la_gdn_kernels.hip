@@ -562,9 +562,15 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int K, int V, bool FWD, bool GDP>
+// BW selects what the pass writes for a backward: 0 the forward's operands (plain forward
+// and summary); 1 the reverse pass's operands only (-W^T and P^T fragments and the
+// scalars, no v: the span summary's state-gradient mirror); 2 both sets, plus T in bf16 and
+// the per-token factors (gam, r_k, r_q, beta) for the backward's intra pass.
+template <int K, int V, bool FWD, bool GDP, int BW = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_intra(Prob p, Ws w)
 {
+    static_assert(BW == 0 || (FWD && !GDP), "the backward's operands come from the plain forward's pass");
+    constexpr bool WANT_V = BW != 1;                // v, U~ and the forward's -W and P^T
     constexpr int PK = K / 8, PV = V / 8;           // 16-byte pieces per k / v row
     constexpr int DX = K > V ? K : V;
     constexpr int PX = DX / 8;
@@ -711,7 +717,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         // ---- 2b: Gram tiles.  wave 0: G(0,0), P^T(0,0); wave 1: G(1,0); wave 2: G(1,1),
         // P^T(1,1); wave 3: P^T(0,1) and the gate cumsum.  Tile (m, n): rows 32 m.., columns 32 n..
-        f32x16 Gt = {}, Pt = {};
+        f32x16 Gt = {}, Pt = {}, Pq = {};
         const int gm = wave == 0 ? 0 : 1, gn = wave == 2 ? 1 : 0;   // G tile of waves 0..2
         const int pm = wave == 2 ? 1 : 0, pn = wave == 0 ? 0 : 1;   // P^T tile of waves 0, 2, 3
         if (wave < 3) {
@@ -719,10 +725,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int s = 0; s < K / 16; ++s)
                 Gt = mfma32(lds_row8<PK>(sK, 32 * gm + c, 16 * s + 8 * hh), lds_row8<PK>(sK, 32 * gn + c, 16 * s + 8 * hh), Gt);
         }
-        if (FWD && wave != 1) {
+        if (FWD && WANT_V && wave != 1) {
 #pragma unroll
             for (int s = 0; s < K / 16; ++s)
                 Pt = mfma32(lds_row8<PK>(sK, 32 * pm + c, 16 * s + 8 * hh), lds_row8<PK>(sX, 32 * pn + c, 16 * s + 8 * hh), Pt);
+        }
+        if (BW && wave != 1) {
+            // the same tile transposed, P = Q K^T (rows tokens t, columns s): its registers
+            // 8 js .. 8 js + 7 are the A operand of P^T (lane s, tokens t in accumulator order)
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s)
+                Pq = mfma32(lds_row8<PK>(sX, 32 * pn + c, 16 * s + 8 * hh), lds_row8<PK>(sK, 32 * pm + c, 16 * s + 8 * hh), Pq);
         }
         if (wave == 3) {
             // the gate and beta transforms fused into the prologue (the cudnn-frontend PR
@@ -758,7 +771,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
         // ---- 2c: v into q's space (every q read is done); per-token factors and the inter
         // pass's scalars (wave 1); A^T (waves 0..2); P^T out (waves 0, 2, 3)
-        if (!GDP)
+        if (!WANT_V) {
+        } else if (!GDP)
             intra_load_tile<V>(sX, p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst, len,
                                wave, lane, 4);
         else
@@ -773,6 +787,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             sc[t] = exp2_hw(gl - gm_t) * rk;                                         // d (0 past the end)
             sc[64 + t] = (FWD && t < len) ? p.scale * s_rq[t] * exp2_hw(gm_t) : 0.f;   // sq
             if (t == 0) sc[192] = exp2_hw(gl);
+            if (BW == 2) {
+                // the backward's intra pass: gam (log2 units), r_k, r_q, beta per token
+                float *sb = w.SB + ch_h * kScalars;
+                sb[t] = gm_t;
+                sb[64 + t] = rk;
+                sb[128 + t] = s_rq[t];
+                sb[192 + t] = s_b[t];
+            }
         }
         if (wave < 3) {
             // A[t][s] for this lane's column s and rows t = 32 gm + 8 j + 4 hh + i, stored as A^T[s][t..]
@@ -793,7 +815,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 *reinterpret_cast<lds_f32x4 *>(sAT + s * TS + t0) = a;
             }
         }
-        if (FWD && wave != 1) {
+        if (BW && wave != 1) {
+            // P tile (t tile pn, s tile pm): lane (c, hh) holds column s = 32 pm + c, rows
+            // t = 32 pn + 8 j + 4 hh + i; written as the A fragments of P^T, [s tile + t tile][js]
+            const int sI = 32 * pm + c;
+            const float gs = s_gam[sI], rs = s_rk[sI] * p.scale;
+            f32x16 pv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t0 = 32 * pn + 8 * j + 4 * hh;
+                const f32x4 gt = *reinterpret_cast<const lds_f32x4 *>(s_gam + t0);
+                const f32x4 rq = *reinterpret_cast<const lds_f32x4 *>(s_rq + t0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = exp2_hw(32 * pm + cm <= 32 * pn + 8 * j + 4 * hm + i ? gt[i] - gs : kNegInf);
+                    pv[4 * j + i] = rq[i] * rs * e * Pq[4 * j + i];
+                }
+            }
+#pragma unroll
+            for (int js = 0; js < 2; ++js)
+                w.PTF[(ch_h * 6 + 2 * (pm + pn) + js) * 64 + lane] = __builtin_bit_cast(uint4, pack32(pv, js));
+        }
+        if (FWD && WANT_V && wave != 1) {
             // P^T tile (pm, pn): lane (c, hh) holds column t = 32 pn + c, rows s = 32 pm + 8 j + 4 hh + i;
             // registers 8 js .. 8 js + 7 are the B operand of token tile pn, step 2 pm + js
             const int t = 32 * pn + c;
@@ -888,6 +931,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             }
         }
 
+        if (BW == 2) {
+            // T (unit lower triangular) in bf16, row-major 64 x 64, for the backward's intra pass
+            const int row = tid >> 2, c0 = 16 * (tid & 3);
+            bf16x8 tv[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tv[e >> 3][e & 7] = f2bf(c0 + e <= row ? sAT[row * TS + c0 + e] : 0.f);
+            uint4 *dst = w.TB + ch_h * (64 * 64 / 8) + row * 8 + 2 * (tid & 3);
+            dst[0] = __builtin_bit_cast(uint4, tv[0]);
+            dst[1] = __builtin_bit_cast(uint4, tv[1]);
+        }
+
         // ---- 4: -W (W^T = K^T Tw^T: rows key columns, columns tokens; registers 8 js ..
         // 8 js + 7 are the A operand rows of W for one reduction step) and U~ = Thi V + Tlo V,
         // with Tw = T diag(beta 2^gam r_k) and T diag(beta) = Thi + Tlo (bf16) formed in
@@ -923,19 +977,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int i = 0; i < (2 * (K / 32)) / 4; ++i) {
                     const int nb = 2 * i + (wave >> 1);
-                    f32x16 acc = {};
+                    if (WANT_V) {
+                        f32x16 acc = {};
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) acc = mfma32(lds_tr32s<PK, false>(sK, 16 * s, 32 * nb, lane), tw[s], acc);
+                        for (int s = 0; s < 4; ++s) acc = mfma32(lds_tr32s<PK, false>(sK, 16 * s, 32 * nb, lane), tw[s], acc);
 #pragma unroll
-                    for (int js = 0; js < 2; ++js) {
-                        const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
-                        w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+                        for (int js = 0; js < 2; ++js) {
+                            const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
+                            w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+                        }
+                    }
+                    if (BW) {
+                        // W = Tw K itself (operands swapped): rows tokens of tile m in accumulator
+                        // order, lane = key column, so registers 8 js .. 8 js + 7 are the A operand
+                        // of W^T for token step 2 m + js; written negated, [key tile][token step]
+                        f32x16 acc = {};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) acc = mfma32(tw[s], lds_tr32s<PK, false>(sK, 16 * s, 32 * nb, lane), acc);
+#pragma unroll
+                        for (int js = 0; js < 2; ++js)
+                            w.WTF[((ch_h * (K / 32) + nb) * 4 + 2 * m + js) * 64 + lane] = neg_bf16(pack32(acc, js));
                     }
                 }
             }
             // every wave is done with sK: the next item's k rows go there now
             lds_barrier();
             if (it + (int)gridDim.x < items) issue_k(item_info(it + gridDim.x));
+            if (!WANT_V) {
+                lds_barrier();
+                continue;
+            }
             bf16x8 th[4], tl[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -1651,151 +1722,844 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// The span summary's mirror for the state gradient (the "Linear Attention" page,
-// "Summaries": <op>_summary_bwd).  With L = sum_t <do_t, o_t> + <dS_end, S_end> and the
-// step M_t = exp(g_t) (I - beta_t k_t k_t^T) (symmetric), the gradient of the start state
-// follows the reverse recurrence
-//     D <- dS_end;   for t = last .. first:  X = D + scale q_t do_t^T,  D = M_t X
-// (q, k normalised), dS_start = D.  First version: token by token, one workgroup per
-// (sequence, value head, 32 value columns), D in registers (K / 8 rows per thread), and
-// k^T X reduced over the rows through LDS (one barrier per token).
+// k_bwd_inter: the reverse chunk pass of the backward, and the span summary's mirror for the
+// state gradient (the "Linear Attention" page, "Summaries": <op>_summary_bwd).  With
+// L = sum_t <dO_t, o_t> + <dS_end, S_end>, the gradient dS of a chunk's end state gives
+// that of its start state (the chunked form of the forward's formulas at the top, read
+// backwards):
+//     dU  = diag(d) K dS + P^T dO                      (d = 2^(gam_n - gam) r_k)
+//     dS0 = 2^(gam_n) dS + Q^T diag(sq) dO + (-W)^T dU  (sq = scale r_q 2^gam)
+// One workgroup of 4 waves per (sequence, value head, 32 value columns), over the chunks
+// from last to first:
+//   state waves kh = 0, 1 own the rows of key half kh of dS (accumulator tiles) and carry
+//     the chain: Z_kh = K_kh dS_kh over both token tiles (their half of the reduction over
+//     keys), swapped through LDS so that both hold dU; the P^T dO and Q^T diag(sq) dO
+//     terms, which do not depend on dS, are formed before the swap.  They read every
+//     operand from LDS and issue no loads, so no wait of theirs covers a load in flight.
+//   loader waves (2, 3) put chunk c - 1's raw k, q and dO rows, scalars, and -W^T and P^T
+//     fragments (written by the intra pass in this pass's operand order) into LDS at the
+//     start of chunk c (two buffers) and wait for them before the chunk's second barrier.
+// FULL (the full backward) also stores each chunk's end-state gradient and dU for the
+// backward's intra pass.
 
-// Inverse row norms of q and k (K / 8 lanes per (token, q/k head) row), and, in the last
-// workgroup, the validation of cu_seqlens into the status word.
-template <int K>
-__global__ __launch_bounds__(256) void k_sbwd_prep(Prob p, float *rn, int32_t *status)
+template <int K, int V, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_inter(
+    Prob p, Ws w, const __bf16 *d_out, const float *d_end, float *d_start)
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    if (blockIdx.x == gridDim.x - 1) {
-        if (wv != 0) return;
-        bool bad = false;
-        for (int i = lane; i <= p.N; i += 64) {
-            const int c = p.cu[i];
-            if (i == 0 && c != 0) bad = true;
-            if (i == p.N && (int64_t)c != p.T) bad = true;
-            if (i < p.N && p.cu[i + 1] < c) bad = true;
+    constexpr int KH = K / 2, NR = KH / 32, NKS = KH / 16, PPR = K / 8;
+    constexpr int NT = V / 32;
+    constexpr int FK = K / 8;                    // fragments of a 64-row k or q tile
+    constexpr int NKL = FK / 2;                  // k (or q) tile loads per loader wave
+    constexpr int FWT = (K / 32) * 4;            // -W^T fragments per chunk
+    constexpr int oK = 0, oQ = FK, oD = 2 * FK, oS = oD + 4, oWT = oS + 1, oPT = oWT + FWT, NF = oPT + 6;
+    __shared__ u32x4 sB0[NF * 64], sB1[NF * 64];
+    __shared__ u32x4 sZ[2 * 2 * 4 * 64];        // Z partials: [kh][token tile][j][lane]
+    lds_u32x4 *const b0 = (lds_u32x4 *)sB0, *const b1 = (lds_u32x4 *)sB1;
+    auto buf = [&](int c) { return (c & 1) ? b1 : b0; };
+    lds_u32x4 *const xZ = (lds_u32x4 *)sZ;
+
+    if (w.hdr[0] != LA_DEVICE_OK) return;        // malformed cu_seqlens: write nothing
+    const int U = p.N * p.HV;
+    // blocks of 8 units x NT tiles, the tiles of one unit on one XCD (as the forward)
+    const int bi = blockIdx.x;
+    const int grp = bi / (8 * NT), rem = bi % (8 * NT);
+    const int ug = min(8, U - 8 * grp);
+    const int tile = rem / ug;
+    const int u = 8 * grp + rem % ug;
+    const int n = w.order[u / p.HV];
+    const int h = u % p.HV;
+    const int hk = h / (p.HV / p.HK);
+    const int4 si = w.seq_info[n];
+    const int seq_start = si.x, seq_len = si.y, cid0 = si.z;
+    const int nch = (seq_len + kChunk - 1) / kChunk;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
+
+    if (wave >= 2) {
+        // ------------------------------------------------------------ loader waves
+        const int lh = wave - 2;
+        uint32_t koff[NKL], qoff[NKL], doff[2];
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            const int sI = (2 * i + lh) * 64 + lane;
+            const int row = sI / PPR, pc = (sI % PPR) ^ (row % PPR);
+            koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
+            qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
         }
-        const bool any = __ballot(bad) != 0;
-        if (lane == 0) status[0] = any ? LA_DEVICE_BAD_CU_SEQLENS : LA_DEVICE_OK;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int sI = (2 * i + lh) * 64 + lane;
+            const int row = sI / 4, pc = (sI % 4) ^ (row % 4);
+            doff[i] = (uint32_t)row * 2u * (uint32_t)p.ost + 16u * (uint32_t)pc;
+        }
+        const uint32_t lo16 = (uint32_t)lane * 16u;
+        // chunk ci's k, q and dO rows, scalars, -W^T and P^T fragments into `eb`
+        auto issue = [&](lds_u32x4 *eb, int ci) {
+            const int start = seq_start + kChunk * ci, len = min(kChunk, seq_len - kChunk * ci);
+            const int64_t chh = (int64_t)(cid0 + ci) * p.HV + h;
+            const i32x4 rK = make_rsrc(p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, (uint32_t)len * 2u * (uint32_t)p.kst);
+#pragma unroll
+            for (int i = 0; i < NKL; ++i) b2l(rK, eb, oK + 2 * i + lh, koff[i], 0);
+            const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, (uint32_t)len * 2u * (uint32_t)p.qst);
+#pragma unroll
+            for (int i = 0; i < NKL; ++i) b2l(rQ, eb, oQ + 2 * i + lh, qoff[i], 0);
+            const i32x4 rD = make_rsrc(d_out + (int64_t)start * p.ost + (int64_t)h * p.osh + 32 * tile,
+                                       (uint32_t)len * 2u * (uint32_t)p.ost);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) b2l(rD, eb, oD + 2 * i + lh, doff[i], 0);
+            const i32x4 rW = make_rsrc(reinterpret_cast<const char *>(w.WTF) + chh * FWT * kFrag, FWT * kFrag);
+#pragma unroll
+            for (int i = 0; i < FWT / 2; ++i) {
+                const int f = lh * (FWT / 2) + i;
+                b2l(rW, eb, oWT + f, lo16, f * kFrag);
+            }
+            const i32x4 rP = make_rsrc(reinterpret_cast<const char *>(w.PTF) + chh * 6 * kFrag, 6 * kFrag);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) b2l(rP, eb, oPT + 3 * lh + i, lo16, (3 * lh + i) * kFrag);
+            if (lh == 0) b2l(make_rsrc(w.SC + chh * kScalars, kScalars * 4), eb, oS, lo16, 0);
+        };
+        // Chunk ci's operands land in buffer ci % 2.  At the start of chunk ci (after B2 of chunk
+        // ci + 1, whose buffer is then dead) the loaders issue chunk ci - 1's; before B2 of
+        // chunk ci they wait for them.
+        if (nch > 0) issue(buf(nch - 1), nch - 1);
+        vm_wait<0>();
+        lds_barrier();
+        for (int ci = nch - 1; ci >= 0; --ci) {
+            if (ci >= 1) issue(buf(ci - 1), ci - 1);
+            lds_barrier();                                    // B1
+            vm_wait<0>();                                     // all of chunk ci - 1
+            lds_barrier();                                    // B2
+        }
         return;
     }
-    // K / 8 lanes per row (8 bf16 each, one 16-byte load of q and of k), 512 / K rows per wave
-    constexpr int LPR = K / 8, RPW = 64 / LPR;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + wv) * RPW + lane / LPR;   // token row * HK + hk
-    const int piece = lane % LPR;
-    float sq = 0.f, sk = 0.f;
-    if (row < p.T * p.HK) {
-        const int64_t t = row / p.HK, hk = row % p.HK;
-        sq = sumsq8(*reinterpret_cast<const uint4 *>(p.q + t * p.qst + hk * p.qsh + 8 * piece));
-        sk = sumsq8(*reinterpret_cast<const uint4 *>(p.k + t * p.kst + hk * p.ksh + 8 * piece));
+
+    // ---------------------------------------------------------------- state waves
+    __builtin_amdgcn_s_setprio(3);
+    const int kh = wave;
+    const int row0 = kh * KH;                            // first key row of this wave
+    const int col = 32 * tile + c;                       // this lane's value column
+    const int64_t unit = (int64_t)n * p.HV + h;
+    f32x16 D[NR];                                        // dS rows row0 .. row0 + KH - 1
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            D[r][e] = d_end ? d_end[(unit * K + row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V + col] : 0.f;
+    lds_barrier();
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        const lds_u32x4 *eb = buf(ci);
+        const lds_u32x2 *ew = reinterpret_cast<const lds_u32x2 *>(eb);
+        const lds_float *scl = reinterpret_cast<const lds_float *>(eb + oS * 64);
+        const int64_t chh = (int64_t)(cid0 + ci) * p.HV + h;
+        // dS as bf16 B operands (keys in accumulator order)
+        bf16x8 Sb[NKS];
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) Sb[kk] = pack32(D[kk >> 1], kk & 1);
+        if (FULL) {
+            // this chunk's end-state gradient, for the backward's intra pass
+            float *dst = w.DSN + chh * K * V + col;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) dst[(int64_t)(row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V] = D[r][e];
+        }
+        // Z[o] = K (token tile m = o ^ kh, keys of this half) dS_kh; A operands are k rows with the
+        // keys in accumulator order (two 8-byte reads of the swizzled tile)
+        f32x16 Z[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            Z[o] = f32x16{};
+            const int rowt = 32 * (o ^ kh) + c;
+#pragma unroll
+            for (int kk = 0; kk < NKS; ++kk) {
+                const int ck = row0 + 16 * kk + 4 * hh;
+                const u32x2 a0 = ew[oK * 128 + (swz<PPR>(rowt, ck) >> 3)];
+                const u32x2 a1 = ew[oK * 128 + (swz<PPR>(rowt, ck + 8) >> 3)];
+                Z[o] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}), Sb[kk], Z[o]);
+            }
+        }
+        // dO as B operands (tokens in accumulator order), token steps 0..3
+        bf16x8 Do[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) Do[st] = lds_tr32s<4, true>(eb + oD * 64, 16 * st, 0, lane);
+        // G2 = P^T dO for both token tiles (P causal: s tile m needs t tiles m .. 1)
+        f32x16 Gz[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int m = o ^ kh;
+            Gz[o] = f32x16{};
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt)
+                if (pt >= m) {
+#pragma unroll
+                    for (int js = 0; js < 2; ++js)
+                        Gz[o] = mfma32(__builtin_bit_cast(bf16x8, eb[(oPT + 2 * (m + pt) + js) * 64 + lane]), Do[2 * pt + js],
+                                       Gz[o]);
+                }
+        }
+        // the decay of dS, then Q^T diag(sq) dO of this key half
+        const float gl = scl[192];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) D[r][e] *= gl;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const f32x4 s0 = *reinterpret_cast<const lds_f32x4 *>(scl + 64 + 16 * st + 4 * hh);
+            const f32x4 s1 = *reinterpret_cast<const lds_f32x4 *>(scl + 64 + 16 * st + 8 + 4 * hh);
+            bf16x8 Ds;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Ds[i] = f2bf(bf2f(Do[st][i]) * s0[i]);
+                Ds[4 + i] = f2bf(bf2f(Do[st][4 + i]) * s1[i]);
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) D[r] = mfma32(lds_tr32s<PPR, true>(eb + oQ * 64, 16 * st, row0 + 32 * r, lane), Ds, D[r]);
+        }
+        // swap the Z partials
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xZ[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
+                    __builtin_bit_cast(u32x4, f32x4{Z[o][4 * j], Z[o][4 * j + 1], Z[o][4 * j + 2], Z[o][4 * j + 3]});
+        lds_barrier();                                        // B1
+        // dU = diag(d) (Z_0 + Z_1) + P^T dO for both token tiles; D += (-W)^T dU
+        bf16x8 Ub[4];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int m = o ^ kh;
+            f32x16 du;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 zo = __builtin_bit_cast(f32x4, xZ[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
+                const f32x4 dj = *reinterpret_cast<const lds_f32x4 *>(scl + 32 * m + 8 * j + 4 * hh);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) du[4 * j + e] = (Z[o][4 * j + e] + zo[e]) * dj[e] + Gz[o][4 * j + e];
+            }
+            if (FULL && o == 0) {
+                float *dst = w.DU + (chh * 64 + 32 * m) * V + col;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) dst[(int64_t)(8 * (e >> 2) + 4 * hh + (e & 3)) * V] = du[e];
+            }
+            Ub[2 * m] = pack32(du, 0);
+            Ub[2 * m + 1] = pack32(du, 1);
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int ts = 0; ts < 4; ++ts)
+                D[r] = mfma32(__builtin_bit_cast(bf16x8, eb[(oWT + (kh * NR + r) * 4 + ts) * 64 + lane]), Ub[ts], D[r]);
+        lds_barrier();                                        // B2
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            d_start[(unit * K + row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V + col] = D[r][e];
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_intra: the backward's intra pass, one workgroup of 4 waves per (chunk, value head).
+// Given the chunk's start state S0 (the recomputed forward's fp32 series), the gradient dS
+// of its end state and dU (both from the reverse pass), it differentiates everything the
+// forward formed inside the chunk (the formulas at the top of this file; k^ = r_k k and
+// q^ = scale r_q q, f = beta 2^gam, M[t][s] = 2^(gam_t - gam_s) for s <= t):
+//   U   = U~ + (-W) S0                       dP  = dO U^T
+//   dq^ = diag(2^gam) dO S0^T + (M o dP) k^  dk^ = (M o dP)^T q^ + diag(2^(gam_n-gam)) U dS^T
+//   dW  = -dU S0^T                           dT  = dW (diag(f) k^)^T + dU (diag(beta) V)^T
+//   dk^ += diag(f) T^T dW                    dv  = diag(beta) T^T dU
+//   dA  = -T^T (dT T^T), strictly lower      dk^ += (dGm + dGm^T) k^,  dGm = dA o beta_t E
+// with E[t][s] = 2^(gam_t - gam_s) (s < t), and per token the gradients of beta and of the
+// chunk-local cumulative gate (every place gam enters: A, P, W, the output's 2^gam, the
+// state update's 2^(gam_n - gam) and 2^gam_n), summed back to g in reverse token order.
+// The q^ and k^ gradients go out per value head (fp32); k_bwd_qk sums each head group and
+// applies the row norms.  All products are bf16 MFMA with fp32 accumulation; each wave owns
+// token tile (wave & 1) and the column tiles (wave >> 1) + 2 i of every 64-row result.
+// Stage A holds S0 and dS in LDS (bf16); stage B reuses that space for q, v, T and the
+// masked dP tiles; stage C for dT T^T and the dA tiles.
+
+template <int PPR>
+__device__ __forceinline__ int swz_e(int row, int col)
+{
+    return swz<PPR>(row, col & ~3) + 2 * (col & 3);
+}
+
+// Sum over the 32 lanes that share lane >> 5 (one row of an accumulator tile).
+__device__ __forceinline__ float sum32(float x)
+{
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// A 32 x 32 accumulator tile (rows r0 + 8 j + 4 hh + i in register 4 j + i, column c0 + lane % 32)
+// into a swizzled bf16 tile of PPR 16-byte pieces per row.
+template <int PPR>
+__device__ __forceinline__ void store_tile_bf16(lds_char *tile, const f32x16 &x, int r0, int c0, int lane)
+{
+    const int c = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        *reinterpret_cast<lds_bf16 *>(tile + swz_e<PPR>(r0 + 8 * (e >> 2) + 4 * hh + (e & 3), c0 + c)) = f2bf(x[e]);
+}
+
+template <int PPR>
+__device__ __forceinline__ float lds_elem(const lds_char *tile, int row, int col)
+{
+    return bf2f(*reinterpret_cast<const lds_bf16 *>(tile + swz_e<PPR>(row, col)));
+}
+
+// fp32 rows (row-major, `cols` floats apart) into a swizzled bf16 tile; returns this thread's
+// share of sum(a * b) when `dot` is given (then `a` and `b` are both converted).
+template <int PPR>
+__device__ __forceinline__ float load_f32_tile(lds_char *dst, const float *src, int rows, int cols, int tid,
+                                               lds_char *dst2 = nullptr, const float *src2 = nullptr)
+{
+    float dot = 0.f;
+    const int n4 = rows * cols / 4;
+    for (int idx = tid; idx < n4; idx += 256) {
+        const int row = idx / (cols / 4), c4 = 4 * (idx % (cols / 4));
+        const float4 a = *reinterpret_cast<const float4 *>(src + (int64_t)row * cols + c4);
+        bf16x4 va = {f2bf(a.x), f2bf(a.y), f2bf(a.z), f2bf(a.w)};
+        *reinterpret_cast<lds_bf16x4 *>(dst + swz<PPR>(row, c4)) = va;
+        if (src2) {
+            const float4 b = *reinterpret_cast<const float4 *>(src2 + (int64_t)row * cols + c4);
+            bf16x4 vb = {f2bf(b.x), f2bf(b.y), f2bf(b.z), f2bf(b.w)};
+            *reinterpret_cast<lds_bf16x4 *>(dst2 + swz<PPR>(row, c4)) = vb;
+            dot += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+        }
+    }
+    return dot;
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_intra(
+    Prob p, Ws w, const __bf16 *d_out, float *dv_out, float *dg_out, float *db_out)
+{
+    constexpr int PK = K / 8, PV = V / 8, NKT = K / 32, NVT = V / 32, KS = K / 16, VS = V / 16;
+    constexpr int NKS = K / 32;                             // steps of 16 keys per key half (-W fragments)
+    constexpr int szK = 64 * K * 2, szV = 64 * V * 2, sz64 = 64 * 64 * 2, szS = K * V * 2;
+    constexpr int R1B = 2 * szS > szK + szV + 4 * sz64 ? 2 * szS : szK + szV + 4 * sz64;
+    constexpr int oK = 0, oDO = oK + szK, oR1 = oDO + szV, oDU = oR1 + R1B, oU = oDU + szV, oDW = oU + szV;
+    constexpr int oEnd = oDW + szK;
+    constexpr int oS0 = oR1, oDS = oR1 + szS;                            // stage A
+    constexpr int oQ = oR1, oVv = oQ + szK, oT = oVv + szV, oR = oT + sz64, oR2 = oR + sz64, oDT = oR2 + sz64;
+    constexpr int oY = oQ, oZ = oVv, oZ3 = oR;                           // stage C
+    enum { XV, DF, DAEG, AAR, AAC, PPR_, PPC, QX, KX, NPART };
+    __shared__ __attribute__((aligned(16))) char smem[oEnd];
+    __shared__ __attribute__((aligned(16))) float ssc[6 * 64];   // gam2, r_k, r_q, beta, 2^gam, 2^(gam_n - gam)
+    __shared__ float part[NPART][2][64];
+    __shared__ float sdot[4], sdg[64];
+    lds_char *const L = (lds_char *)smem;
+    const lds_u32x4 *const tK = (const lds_u32x4 *)(L + oK);
+    const lds_u32x4 *const tDO = (const lds_u32x4 *)(L + oDO);
+    const lds_u32x4 *const tDU = (const lds_u32x4 *)(L + oDU);
+    const lds_u32x4 *const tU = (const lds_u32x4 *)(L + oU);
+    const lds_u32x4 *const tDW = (const lds_u32x4 *)(L + oDW);
+    const lds_u32x4 *const tS0 = (const lds_u32x4 *)(L + oS0);
+    const lds_u32x4 *const tDS = (const lds_u32x4 *)(L + oDS);
+    const lds_u32x4 *const tQ = (const lds_u32x4 *)(L + oQ);
+    const lds_u32x4 *const tV = (const lds_u32x4 *)(L + oVv);
+    const lds_u32x4 *const tT = (const lds_u32x4 *)(L + oT);
+    const lds_u32x4 *const tR = (const lds_u32x4 *)(L + oR);
+    const lds_u32x4 *const tR2 = (const lds_u32x4 *)(L + oR2);
+    const lds_u32x4 *const tDT = (const lds_u32x4 *)(L + oDT);
+    const lds_u32x4 *const tY = (const lds_u32x4 *)(L + oY);
+    const lds_u32x4 *const tZ = (const lds_u32x4 *)(L + oZ);
+    const lds_u32x4 *const tZ3 = (const lds_u32x4 *)(L + oZ3);
+    lds_float *const s_gam = (lds_float *)ssc, *const s_rk = s_gam + 64, *const s_rq = s_gam + 128;
+    lds_float *const s_b = s_gam + 192, *const s_eg = s_gam + 256, *const s_dd = s_gam + 320;
+
+    if (w.hdr[0] != LA_DEVICE_OK) return;
+    const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tm = wave & 1, half = wave >> 1;
+    // the item: chunk ci of the chunk table, value head h
+    const int ci = blockIdx.x / p.HV, h = blockIdx.x % p.HV, hk = h / (p.HV / p.HK);
+    int start, len;
+    if (p.N <= 64) {
+        const SmallMap sm = small_map(p, w, false);
+        if (ci >= sm.total) return;
+        const uint64_t owns = __ballot(lane < p.N && sm.first <= ci);
+        const int sq_ = 63 - __builtin_clzll(owns);
+        start = __builtin_amdgcn_readfirstlane(__shfl(sm.start, sq_, 64) + kChunk * (ci - __shfl(sm.first, sq_, 64)));
+        len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, sq_, 64) - start));
+    } else {
+        if (ci >= w.hdr[1]) return;
+        const int4 ch = w.chunks[ci];
+        start = __builtin_amdgcn_readfirstlane(ch.y);
+        len = __builtin_amdgcn_readfirstlane(ch.z);
+    }
+    const int64_t chh = (int64_t)ci * p.HV + h;
+
+    // ---- stage A loads: k and dO rows (buffer loads into LDS), the scalars, S0, dS and dU
+    intra_load_tile<K>((lds_u32x4 *)(L + oK), p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst,
+                       len, wave, lane, 4);
+    intra_load_tile<V>((lds_u32x4 *)(L + oDO), d_out + (int64_t)start * p.ost + (int64_t)h * p.osh,
+                       2u * (uint32_t)p.ost, len, wave, lane, 4);
+    if (tid < 64) {
+        const float *sb = w.SB + chh * kScalars;
+        const float gam = sb[tid], gn = sb[len - 1];
+        s_gam[tid] = gam;
+        s_rk[tid] = sb[64 + tid];
+        s_rq[tid] = sb[128 + tid];
+        s_b[tid] = sb[192 + tid];
+        s_eg[tid] = exp2_hw(gam);
+        s_dd[tid] = exp2_hw(tid < len ? gn - gam : kNegInf);
+    }
+    float dot = load_f32_tile<PV>(L + oS0, w.CK + chh * K * V, K, V, tid, L + oDS, w.DSN + chh * K * V);
+    load_f32_tile<PV>(L + oDU, w.DU + chh * 64 * V, 64, V, tid);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (lane == 0) sdot[wave] = dot;
+    vm_wait<0>();
+    lds_barrier();
+
+    // ---- A1: U = U~ + (-W) S0 for tiles (tm, value tile half + 2 i); U~ enters the accumulator
+    {
+        bf16x8 Wf[KS];
+#pragma unroll
+        for (int kg = 0; kg < KS; ++kg)
+            Wf[kg] = __builtin_bit_cast(bf16x8, w.WF[(chh * (K / 8) + ((kg / NKS) * 2 + tm) * NKS + kg % NKS) * 64 + lane]);
+#pragma unroll
+        for (int i = 0; i < NVT / 2; ++i) {
+            const int vt = half + 2 * i;
+            f32x16 acc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 u4 = w.UF[(((chh * (V / 32) + vt) * 2 + tm) * 4 + j) * 64 + lane];
+                acc[4 * j] = u4.x;
+                acc[4 * j + 1] = u4.y;
+                acc[4 * j + 2] = u4.z;
+                acc[4 * j + 3] = u4.w;
+            }
+#pragma unroll
+            for (int kg = 0; kg < KS; ++kg) acc = mfma32(Wf[kg], lds_tr32s<PV, true>(tS0, 16 * kg, 32 * vt, lane), acc);
+            store_tile_bf16<PV>(L + oU, acc, 32 * tm, 32 * vt, lane);
+        }
+    }
+    // ---- A2, A4: dO S0^T (the output's state term of dq^, rows scaled by 2^gam) and dW = -dU S0^T
+    f32x16 dQ[NKT / 2], dK[NKT / 2];
+#pragma unroll
+    for (int i = 0; i < NKT / 2; ++i) {
+        const int kt = half + 2 * i;
+        f32x16 a = {}, b = {};
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+            const bf16x8 sv = lds_row8<PV>(tS0, 32 * kt + c, 16 * s + 8 * hh);
+            a = mfma32(lds_row8<PV>(tDO, 32 * tm + c, 16 * s + 8 * hh), sv, a);
+            b = mfma32(lds_row8<PV>(tDU, 32 * tm + c, 16 * s + 8 * hh), sv, b);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            a[e] *= s_eg[32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)];
+            b[e] = -b[e];
+        }
+        dQ[i] = a;
+        store_tile_bf16<PK>(L + oDW, b, 32 * tm, 32 * kt, lane);
+    }
+    lds_barrier();                                            // U and dW published
+    // ---- A3: diag(2^(gam_n - gam)) U dS^T (the state update's term of dk^), and F = its row dot with k^
+    {
+        float prod[16] = {};
+#pragma unroll
+        for (int i = 0; i < NKT / 2; ++i) {
+            const int kt = half + 2 * i;
+            f32x16 a = {};
+#pragma unroll
+            for (int s = 0; s < VS; ++s)
+                a = mfma32(lds_row8<PV>(tU, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PV>(tDS, 32 * kt + c, 16 * s + 8 * hh), a);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                a[e] *= s_dd[row];
+                prod[e] += a[e] * lds_elem<PK>(L + oK, row, 32 * kt + c);
+            }
+            dK[i] = a;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float r = sum32(prod[e]);
+            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (c == 0) part[KX][half][row] = r * s_rk[row];
+        }
+    }
+    // ---- A5, B1: dT's first term dW (diag(f r_k) K)^T and dP = dO U^T, tile (tm, half)
+    f32x16 dT = {}, dP = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        dT = mfma32(lds_row8<PK>(tDW, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), dT);
+#pragma unroll
+    for (int s = 0; s < VS; ++s)
+        dP = mfma32(lds_row8<PV>(tDO, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PV>(tU, 32 * half + c, 16 * s + 8 * hh), dP);
+    {
+        const int sc_ = 32 * half + c;
+        const float fr = s_b[sc_] * s_eg[sc_] * s_rk[sc_];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dT[e] *= fr;
+    }
+    lds_barrier();                                            // S0 and dS are dead: stage B loads reuse their space
+    intra_load_tile<K>((lds_u32x4 *)(L + oQ), p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
+                       len, wave, lane, 4);
+    intra_load_tile<V>((lds_u32x4 *)(L + oVv), p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst,
+                       len, wave, lane, 4);
+    intra_load_tile<64>((lds_u32x4 *)(L + oT), w.TB + chh * (64 * 64 / 8), 128u, 64, wave, lane, 4);
+    vm_wait<0>();
+    lds_barrier();
+    // ---- B0: the output's state term of dgam: scale r_q rowdot(q, 2^gam dO S0^T)
+    {
+        float prod[16] = {};
+#pragma unroll
+        for (int i = 0; i < NKT / 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                prod[e] += dQ[i][e] * lds_elem<PK>(L + oQ, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float r = sum32(prod[e]);
+            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (c == 0) part[QX][half][row] = r * p.scale * s_rq[row];
+        }
+    }
+    // ---- B2: P = M o (q^ k^T) for tile (tm, half); dP o P sums; R = M o dP r_k,s and R2 = M o dP scale r_q,t
+    {
+        f32x16 qk = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qk = mfma32(lds_row8<PK>(tQ, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), qk);
+        const int sI = 32 * half + c;
+        const float gs = s_gam[sI], rs = s_rk[sI];
+        f32x16 R, R2;
+        float colsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int t = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const float m = exp2_hw(sI <= t ? s_gam[t] - gs : kNegInf);
+            const float pv = p.scale * s_rq[t] * rs * m * qk[e];
+            const float pp = dP[e] * pv;
+            colsum += pp;
+            const float rsum = sum32(pp);
+            if (c == 0) part[PPR_][half][t] = rsum;
+            R[e] = m * dP[e] * rs;
+            R2[e] = m * dP[e] * p.scale * s_rq[t];
+        }
+        colsum += __shfl_xor(colsum, 32, 64);
+        if (hh == 0) part[PPC][tm][sI] = colsum;
+        store_tile_bf16<8>(L + oR, R, 32 * tm, 32 * half, lane);
+        store_tile_bf16<8>(L + oR2, R2, 32 * tm, 32 * half, lane);
+    }
+    // ---- B3: dT's second term dU (diag(beta) V)^T; dT published in bf16
+    {
+        f32x16 a = {};
+#pragma unroll
+        for (int s = 0; s < VS; ++s)
+            a = mfma32(lds_row8<PV>(tDU, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PV>(tV, 32 * half + c, 16 * s + 8 * hh), a);
+        const float bs = s_b[32 * half + c];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dT[e] += a[e] * bs;
+        store_tile_bf16<8>(L + oDT, dT, 32 * tm, 32 * half, lane);
+    }
+    // ---- B4: X2 = T^T dU (rows s of tile tm): dv = diag(beta) X2 and rowdot(X2, v) into dbeta
+    {
+        float prod[16] = {};
+#pragma unroll
+        for (int i = 0; i < NVT / 2; ++i) {
+            const int vt = half + 2 * i;
+            f32x16 a = {};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                a = mfma32(lds_tr32s<8, false>(tT, 16 * st, 32 * tm, lane), lds_tr32s<PV, false>(tDU, 16 * st, 32 * vt, lane), a);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                prod[e] += a[e] * lds_elem<PV>(L + oVv, row, 32 * vt + c);
+                if (row < len) dv_out[((int64_t)(start + row) * p.HV + h) * V + 32 * vt + c] = s_b[row] * a[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float r = sum32(prod[e]);
+            if (c == 0) part[XV][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+        }
+    }
+    // ---- B5: X1 = T^T dW: dk^ += diag(f) X1 and df = r_k rowdot(X1, k)
+    {
+        float prod[16] = {};
+#pragma unroll
+        for (int i = 0; i < NKT / 2; ++i) {
+            const int kt = half + 2 * i;
+            f32x16 a = {};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                a = mfma32(lds_tr32s<8, false>(tT, 16 * st, 32 * tm, lane), lds_tr32s<PK, false>(tDW, 16 * st, 32 * kt, lane), a);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                prod[e] += a[e] * lds_elem<PK>(L + oK, row, 32 * kt + c);
+                dK[i][e] += s_b[row] * s_eg[row] * a[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float r = sum32(prod[e]);
+            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (c == 0) part[DF][half][row] = r * s_rk[row];
+        }
+    }
+    lds_barrier();                                            // R, R2 and dT published
+    // ---- B7, B8: dq^ += R k, dk^ += R2^T q
+#pragma unroll
+    for (int i = 0; i < NKT / 2; ++i) {
+        const int kt = half + 2 * i;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            dQ[i] = mfma32(lds_row8<8>(tR, 32 * tm + c, 16 * st + 8 * hh), lds_tr32s<PK, false>(tK, 16 * st, 32 * kt, lane), dQ[i]);
+            dK[i] = mfma32(lds_tr32s<8, false>(tR2, 16 * st, 32 * tm, lane), lds_tr32s<PK, false>(tQ, 16 * st, 32 * kt, lane), dK[i]);
+        }
+    }
+    // ---- C1: Y = dT T^T, tile (tm, half)
+    {
+        f32x16 y = {};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            y = mfma32(lds_row8<8>(tDT, 32 * tm + c, 16 * st + 8 * hh), lds_row8<8>(tT, 32 * half + c, 16 * st + 8 * hh), y);
+        lds_barrier();                                        // q, v, R and R2 are dead: Y, Z, Z3 reuse them
+        store_tile_bf16<8>(L + oY, y, 32 * tm, 32 * half, lane);
+    }
+    lds_barrier();
+    // ---- C2: dA = -T^T Y (strictly lower), tile (rows a of tile tm, columns b of tile half), with
+    // the Gram tile of k: A = beta_a E r_a r_b (k_a . k_b); dbeta, dgam sums; Z, Z3 = dGm r_b, dGm r_a
+    {
+        f32x16 da = {}, gk = {};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            da = mfma32(lds_tr32s<8, false>(tT, 16 * st, 32 * tm, lane), lds_tr32s<8, false>(tY, 16 * st, 32 * half, lane), da);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            gk = mfma32(lds_row8<PK>(tK, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), gk);
+        const int b = 32 * half + c;
+        const float gb = s_gam[b], rb = s_rk[b];
+        f32x16 Z, Z3;
+        float colsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const float E = exp2_hw(b < a ? s_gam[a] - gb : kNegInf);
+            const float dam = b < a ? -da[e] : 0.f;
+            const float ghat = s_rk[a] * rb * gk[e];
+            const float aA = dam * s_b[a] * E * ghat;
+            colsum += aA;
+            const float rs1 = sum32(aA), rs2 = sum32(dam * E * ghat);
+            if (c == 0) {
+                part[AAR][half][a] = rs1;
+                part[DAEG][half][a] = rs2;
+            }
+            const float dgm = dam * s_b[a] * E;
+            Z[e] = dgm * rb;
+            Z3[e] = dgm * s_rk[a];
+        }
+        colsum += __shfl_xor(colsum, 32, 64);
+        if (hh == 0) part[AAC][tm][b] = colsum;
+        store_tile_bf16<8>(L + oZ, Z, 32 * tm, 32 * half, lane);
+        store_tile_bf16<8>(L + oZ3, Z3, 32 * tm, 32 * half, lane);
+    }
+    lds_barrier();
+    // ---- C3: dk^ += Z k + Z3^T k; the q^ and k^ gradients out
+#pragma unroll
+    for (int i = 0; i < NKT / 2; ++i) {
+        const int kt = half + 2 * i;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bf16x8 kb = lds_tr32s<PK, false>(tK, 16 * st, 32 * kt, lane);
+            dK[i] = mfma32(lds_row8<8>(tZ, 32 * tm + c, 16 * st + 8 * hh), kb, dK[i]);
+            dK[i] = mfma32(lds_tr32s<8, false>(tZ3, 16 * st, 32 * tm, lane), kb, dK[i]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (row < len) {
+                const int64_t at = ((int64_t)(start + row) * p.HV + h) * K + 32 * kt + c;
+                w.DQH[at] = dQ[i][e];
+                w.DKH[at] = dK[i][e];
+            }
+        }
+    }
+    lds_barrier();                                            // every partial sum written
+    // ---- per token: dbeta and dgam, then dg by the reverse cumulative sum within the chunk
+    if (tid < 64) {
+        const int t = tid;
+        const float df = part[DF][0][t] + part[DF][1][t];
+        const float f = s_b[t] * s_eg[t];
+        const float db = part[XV][0][t] + part[XV][1][t] + df * s_eg[t] + part[DAEG][0][t] + part[DAEG][1][t];
+        const float F = part[KX][0][t] + part[KX][1][t];
+        float dgam = df * f + (part[AAR][0][t] + part[AAR][1][t]) - (part[AAC][0][t] + part[AAC][1][t]) +
+                     (part[PPR_][0][t] + part[PPR_][1][t]) - (part[PPC][0][t] + part[PPC][1][t]) +
+                     (part[QX][0][t] + part[QX][1][t]) - F;
+        // the last token also carries sum F and 2^gam_n <dS, S0>
+        float Fs = t < len ? F : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) Fs += __shfl_xor(Fs, off, 64);
+        if (t == len - 1) dgam += Fs + exp2_hw(s_gam[t]) * (sdot[0] + sdot[1] + sdot[2] + sdot[3]);
+        sdg[t] = t < len ? dgam : 0.f;
+        if (t < len) db_out[(int64_t)(start + t) * p.HV + h] = db;
+    }
+    lds_barrier();
+    if (tid < len) {
+        float acc = 0.f;
+        for (int u = len - 1; u >= tid; --u) acc += sdg[u];
+        dg_out[(int64_t)(start + tid) * p.HV + h] = acc;
+    }
+}
+
+// dq and dk from the per-value-head gradients of q^ and k^: the sum over each head group
+// (fixed order), then through the row norms (q^ = scale r_q q, k^ = r_k k,
+// r = 1 / sqrt(sum x^2 + 1e-6)): dx = r dx^ - r^3 (x . dx^) x (times scale for q).  K / 8
+// lanes per (token, q/k head) row, 8 elements each.
+template <int K>
+__global__ __launch_bounds__(256) void k_bwd_qk(Prob p, const Ws w, float *dq, float *dk)
+{
+    constexpr int LPR = K / 8, RPB = 256 / LPR;
+    if (w.hdr[0] != LA_DEVICE_OK) return;                                  // malformed cu_seqlens: write nothing
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;    // token * HK + hk
+    const int piece = threadIdx.x % LPR;
+    const bool live = row < p.T * p.HK;
+    const int64_t t = live ? row / p.HK : 0;
+    const int hk = live ? (int)(row % p.HK) : 0;
+    const int G = p.HV / p.HK;
+    float gq[8] = {}, gk[8] = {}, xq[8], xk[8];
+    if (live) {
+        for (int j = 0; j < G; ++j) {
+            const float *a = w.DQH + ((t * p.HV + hk * G + j) * K + 8 * piece);
+            const float *b = w.DKH + ((t * p.HV + hk * G + j) * K + 8 * piece);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gq[e] += a[e];
+                gk[e] += b[e];
+            }
+        }
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8 *>(p.q + t * p.qst + (int64_t)hk * p.qsh + 8 * piece);
+        const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(p.k + t * p.kst + (int64_t)hk * p.ksh + 8 * piece);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xq[e] = bf2f(q8[e]);
+            xk[e] = bf2f(k8[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+    }
+    float sq = 0.f, sk = 0.f, dqx = 0.f, dkx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sq = fmaf(xq[e], xq[e], sq);
+        sk = fmaf(xk[e], xk[e], sk);
+        dqx = fmaf(xq[e], gq[e], dqx);
+        dkx = fmaf(xk[e], gk[e], dkx);
     }
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) {
         sq += __shfl_xor(sq, off, 64);
         sk += __shfl_xor(sk, off, 64);
+        dqx += __shfl_xor(dqx, off, 64);
+        dkx += __shfl_xor(dkx, off, 64);
     }
-    if (row < p.T * p.HK && piece == 0) {
-        rn[2 * row] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-        rn[2 * row + 1] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+    if (!live) return;
+    const float rq = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f, rk = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+    const float cq = p.l2norm ? rq * rq * rq * dqx : 0.f, ck = p.l2norm ? rk * rk * rk * dkx : 0.f;
+    float *oq = dq + (t * p.HK + hk) * K + 8 * piece;
+    float *ok = dk + (t * p.HK + hk) * K + 8 * piece;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        oq[e] = p.scale * (rq * gq[e] - cq * xq[e]);
+        ok[e] = rk * gk[e] - ck * xk[e];
     }
 }
 
-// One token's operands for a thread of k_sbwd: its K / 8 rows of q and k (16-byte loads),
-// the row norms, gate, beta and its column of d_out.
-template <int R>
-struct SbwdTok {
-    uint4 q[R / 8], k[R / 8];
-    float rq, rk, g, b, dv;
-};
-
-template <int R>
-__device__ __forceinline__ SbwdTok<R> sbwd_load(const Prob &p, const __bf16 *d_out, const float *rn, int64_t t,
-                                                int h, int hk, int r0, int col)
+hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_t s, const LaunchHook *hook)
 {
-    SbwdTok<R> x;
-    const uint4 *qr = reinterpret_cast<const uint4 *>(p.q + t * p.qst + (int64_t)hk * p.qsh + r0);
-    const uint4 *kr = reinterpret_cast<const uint4 *>(p.k + t * p.kst + (int64_t)hk * p.ksh + r0);
-#pragma unroll
-    for (int j = 0; j < R / 8; ++j) {
-        x.q[j] = qr[j];
-        x.k[j] = kr[j];
-    }
-    x.rq = rn[2 * (t * p.HK + hk)];
-    x.rk = rn[2 * (t * p.HK + hk) + 1];
-    x.g = p.g[t * p.gst + h];
-    x.b = p.beta[t * p.bst + h];
-    x.dv = bf2f(d_out[t * p.ost + (int64_t)h * p.osh + col]);
-    return x;
-}
-
-template <int K>
-__global__ __launch_bounds__(256) void k_sbwd(Prob p, const __bf16 *d_out, const float *d_end, float *d_start,
-                                              const float *rn, const int32_t *status)
-{
-    constexpr int R = K / 8;                 // rows per thread
-    const int NT = p.V / 32;
-    const int tile = blockIdx.x % NT, unit = blockIdx.x / NT;
-    const int n = unit / p.HV, h = unit % p.HV, hk = h / (p.HV / p.HK);
-    if (status[0] != LA_DEVICE_OK) return;   // malformed cu_seqlens: write nothing
-    const int c = threadIdx.x & 31, g8 = threadIdx.x >> 5, r0 = g8 * R, col = 32 * tile + c;
-    const int start = p.cu[n], end = p.cu[n + 1];
-    const int64_t sbase = ((int64_t)n * p.HV + h) * K * p.V + col;
-    float D[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) D[i] = d_end ? d_end[sbase + (int64_t)(r0 + i) * p.V] : 0.f;
-    __shared__ float part[2][8][32];
-    // the next token's operands are loaded while this token is computed
-    SbwdTok<R> cur{};
-    if (end > start) cur = sbwd_load<R>(p, d_out, rn, end - 1, h, hk, r0, col);
-    int it = 0;
-    for (int t = end - 1; t >= start; --t, ++it) {
-        const SbwdTok<R> nxt = t > start ? sbwd_load<R>(p, d_out, rn, t - 1, h, hk, r0, col) : cur;
-        // the row norms and scale fold into per-token scalars: X = D + (scale r_q do) q and
-        // D = exp(g) (X - (beta r_k^2 (k^T X)) k) with the raw rows q, k
-        const float sq = cur.rq * p.scale * cur.dv, a = expf(cur.g);
-        float kv[R], sp = 0.f;
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const bf16x8 q8 = __builtin_bit_cast(bf16x8, cur.q[i / 8]);
-            const bf16x8 k8 = __builtin_bit_cast(bf16x8, cur.k[i / 8]);
-            D[i] = fmaf(bf2f(q8[i % 8]), sq, D[i]);
-            kv[i] = bf2f(k8[i % 8]);
-            sp = fmaf(kv[i], D[i], sp);
-        }
-        part[it & 1][g8][c] = sp;
-        __syncthreads();
-        float w = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w += part[it & 1][j][c];   // (k^T X)[col] of the raw k, rows in order
-        const float bw = cur.b * cur.rk * cur.rk * w;
-#pragma unroll
-        for (int i = 0; i < R; ++i) D[i] = a * fmaf(-kv[i], bw, D[i]);
-        cur = nxt;
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i) d_start[sbase + (int64_t)(r0 + i) * p.V] = D[i];
-}
-
-hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t s, const LaunchHook *hook)
-{
-    const Prob &p = *a.p;
+    auto before = [&](int id) { if (hook) hook->before(id, s, hook->ctx); };
+    auto after = [&](int id) { if (hook) hook->after(id, s, hook->ctx); };
     if (p.N == 0) return hipSuccess;
-    const int64_t rows = p.T * p.HK, rows_per_block = 4 * (512 / p.K);
-    const unsigned prep_blocks = (unsigned)((rows + rows_per_block - 1) / rows_per_block) + 1;
+    if (p.N > 64) {
+        before(LA_KERNEL_SCHED);
+        hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, s, p, w);
+        after(LA_KERNEL_SCHED);
+    }
+    const int64_t items = (int64_t)p.max_chunks * p.HV;
+    const int grid = (int)(items < p.intra_grid ? items : p.intra_grid);
+    const unsigned inter_blocks = (unsigned)((int64_t)p.N * p.HV * (p.V / 32));
+    const unsigned qk_blocks = (unsigned)((p.T * p.HK + 256 / (p.K / 8) - 1) / (256 / (p.K / 8)));
+    // the forward again, with the state at every chunk start (fp32, indexed by chunk id)
+    Prob pf = p;
+    pf.ck_every = kChunk;
+    pf.ck_fp32 = 1;
+    pf.ck = w.CK;
+    pf.ck_cap = p.max_chunks;
+    pf.o = w.OB;
+    pf.ost = (int64_t)p.HV * p.V;
+    pf.osh = p.V;
+    pf.sT = nullptr;
+#define LA_BWD(KK, VV)                                                                                         \
+    if (p.K == KK && p.V == VV) {                                                                              \
+        before(LA_KERNEL_INTRA);                                                                               \
+        if (grid > 0)                                                                                          \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<KK, VV, true, false, 2>), dim3(grid), dim3(256), 0, s, p, w); \
+        after(LA_KERNEL_INTRA);                                                                                \
+        before(LA_KERNEL_INTER);                                                                               \
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<KK, VV>), dim3(inter_blocks), dim3(384), 0, s, pf, w);   \
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true>), dim3(inter_blocks), dim3(256), 0, s, p, w, \
+                           a.d_out, a.d_final, a.d_init);                                                      \
+        after(LA_KERNEL_INTER);                                                                                \
+        before(LA_KERNEL_BWD_INTRA);                                                                           \
+        if (items > 0)                                                                                         \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV>), dim3((unsigned)items), dim3(256), 0, s, p, w, \
+                               a.d_out, a.dv, a.dg, a.dbeta);                                                  \
+        if (qk_blocks > 0)                                                                                     \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_qk<KK>), dim3(qk_blocks), dim3(256), 0, s, p, w, a.dq, a.dk); \
+        after(LA_KERNEL_BWD_INTRA);                                                                            \
+        return hipGetLastError();                                                                              \
+    }
+    LA_BWD(64, 64)
+    LA_BWD(64, 128)
+    LA_BWD(128, 64)
+    LA_BWD(128, 128)
+#undef LA_BWD
+    return hipErrorInvalidValue;
+}
+
+hipError_t run_summary_bwd(const Prob &p, const Ws &w, const __bf16 *d_out, const float *d_end, float *d_start,
+                           hipStream_t s, const LaunchHook *hook)
+{
+    auto before = [&](int id) { if (hook) hook->before(id, s, hook->ctx); };
+    auto after = [&](int id) { if (hook) hook->after(id, s, hook->ctx); };
+    if (p.N == 0) return hipSuccess;
+    if (p.N > 64) {
+        before(LA_KERNEL_SCHED);
+        hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, s, p, w);
+        after(LA_KERNEL_SCHED);
+    }
+    const int64_t items = (int64_t)p.max_chunks * p.HV;
+    const int grid = (int)(items < p.intra_grid ? items : p.intra_grid);
     const unsigned blocks = (unsigned)((int64_t)p.N * p.HV * (p.V / 32));
-    if (hook) hook->before(LA_KERNEL_SCHED, s, hook->ctx);
-    if (p.K == 64)
-        hipLaunchKernelGGL(k_sbwd_prep<64>, dim3(prep_blocks), dim3(256), 0, s, p, a.rn, a.status);
-    else
-        hipLaunchKernelGGL(k_sbwd_prep<128>, dim3(prep_blocks), dim3(256), 0, s, p, a.rn, a.status);
-    if (hook) hook->after(LA_KERNEL_SCHED, s, hook->ctx);
-    if (hook) hook->before(LA_KERNEL_INTER, s, hook->ctx);
-    if (p.K == 64)
-        hipLaunchKernelGGL(k_sbwd<64>, dim3(blocks), dim3(256), 0, s, p, a.d_out, a.d_end, a.d_start, a.rn, a.status);
-    else
-        hipLaunchKernelGGL(k_sbwd<128>, dim3(blocks), dim3(256), 0, s, p, a.d_out, a.d_end, a.d_start, a.rn, a.status);
-    if (hook) hook->after(LA_KERNEL_INTER, s, hook->ctx);
-    return hipGetLastError();
+#define LA_SBWD(KK, VV)                                                                                  \
+    if (p.K == KK && p.V == VV) {                                                                        \
+        before(LA_KERNEL_INTRA);                                                                         \
+        if (grid > 0)                                                                                    \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<KK, VV, true, false, 1>), dim3(grid), dim3(256), 0, s, p, w); \
+        after(LA_KERNEL_INTRA);                                                                          \
+        before(LA_KERNEL_INTER);                                                                         \
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, false>), dim3(blocks), dim3(256), 0, s, p, w, d_out, \
+                           d_end, d_start);                                                              \
+        after(LA_KERNEL_INTER);                                                                          \
+        return hipGetLastError();                                                                        \
+    }
+    LA_SBWD(64, 64)
+    LA_SBWD(64, 128)
+    LA_SBWD(128, 64)
+    LA_SBWD(128, 128)
+#undef LA_SBWD
+    return hipErrorInvalidValue;
 }
 
 hipError_t run_pipeline(const Prob &p, const Ws &w, bool summary, hipStream_t s, const LaunchHook *hook)

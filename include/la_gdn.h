@@ -249,13 +249,42 @@ la_status la_gdn_summary_ex(const la_gdn_desc *desc, const void *k, const void *
  *   d_start_state  device, fp32 [N, HV, K, V], written
  *   workspace      at least la_gdn_workspace_bytes(desc, 1) bytes, 256-byte aligned
  * Errors as for la_gdn_summary (a malformed cu_seqlens writes nothing and sets the
- * device status).  First version: token by token on the GPU (one workgroup per
+ * device status).  Evaluated in chunks: the intra pass forms -W^T and P^T per (chunk, head),
+ * then the reverse chunk pass of la_gdn_bwd carries the state gradient (one workgroup per
  * (sequence, value head, 32 value columns)).
  */
 la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void *k, const float *g,
                              const float *beta, const int32_t *cu_seqlens, const void *d_out,
                              const float *d_end_state, float *d_start_state, int l2norm, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The full backward of la_gdn_fwd (the "Linear Attention" page: "Every variant has a
+ * forward, a full backward"; its "Example" ends in o.sum().backward()).  For upstream
+ * gradients d_out of o and d_final_state of the final states, the gradients of
+ * L = sum <d_out, o> + sum <d_final_state, final_state> with respect to every input:
+ *   q, k, v, g, beta, cu_seqlens, initial_state, l2norm   as for la_gdn_fwd (plain inputs:
+ *                  fp32 beta, natural-log gate, int32 cu_seqlens)
+ *   d_out          device, bf16 [T, HV, V], strides o_stride_t / o_stride_h of desc
+ *   d_final_state  device, fp32 [N, HV, K, V], or NULL for zeros
+ *   dq, dk         device, fp32 [T, HK, K] contiguous, written (summed over the value heads
+ *                  that share a q/k head, in a fixed order)
+ *   dv             device, fp32 [T, HV, V] contiguous, written
+ *   dg, dbeta      device, fp32 [T, HV] contiguous, written (dg: gradient of the natural-log gate)
+ *   d_initial_state  device, fp32 [N, HV, K, V], written (zero-start inputs still get it)
+ *   workspace      at least la_gdn_bwd_workspace_bytes(desc) bytes, 256-byte aligned
+ * The forward is run again inside the call (its output is not needed; its state at every
+ * chunk start is kept in the workspace), then a reverse pass over the chunks carries the
+ * state gradient and a parallel pass forms each chunk's gradients.  Deterministic and batch
+ * invariant like the forward.  Errors as for la_gdn_fwd; a malformed cu_seqlens writes
+ * nothing and sets the device status.
+ */
+size_t la_gdn_bwd_workspace_bytes(const la_gdn_desc *desc);
+la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const float *initial_state,
+                     const void *d_out, const float *d_final_state, float *dq, float *dk, float *dv,
+                     float *dg, float *dbeta, float *d_initial_state, int l2norm, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * la_gdn_fwd for callers that cannot allocate device memory: code under HIP graph
@@ -298,7 +327,8 @@ const char *la_last_error_message(void);
 #define LA_KERNEL_INTRA 1   /* prologue (q/k norms, gate cumsum) + intra-chunk UT/WY */
 #define LA_KERNEL_INTER 2   /* sequential inter-chunk state and output pass (any of its variants:
                                forward, summary, with the state series, Gated Delta Product) */
-#define LA_KERNEL_COUNT 3
+#define LA_KERNEL_BWD_INTRA 3   /* the backward's intra pass and its q/k gradient reduction */
+#define LA_KERNEL_COUNT 4
 la_status la_gdn_profile_enable(int enable);
 la_status la_gdn_profile_read(int32_t kernel_id, double *total_ms, int64_t *launches);
 const char *la_gdn_kernel_name(int32_t kernel_id);

@@ -252,6 +252,40 @@ void summary_bwd()
                              (float *)a.fin.p, 1, a.ws.p, 64, nullptr) == LA_ERR_WORKSPACE_TOO_SMALL);
 }
 
+void full_backward()
+{
+    const la_gdn_desc d = desc(3, 700, 2, 4, 128, 64);
+    Args a(d, false);
+    const size_t wsb = la_gdn_bwd_workspace_bytes(&d);
+    CHECK(wsb > a.wsb);
+    Buf ws(wsb), dq(4 * 700 * 2 * 128), dk(4 * 700 * 2 * 128), dv(4 * 700 * 4 * 64), dg(4 * 700 * 4),
+        db(4 * 700 * 4), di(4 * 3 * 4 * 128 * 64);
+    auto call = [&](const void *dout, float *dqp, void *w, size_t n) {
+        return la_gdn_bwd(&d, a.q.p, a.k.p, a.v.p, (float *)a.g.p, (float *)a.b.p, (int32_t *)a.cu.p, nullptr, dout,
+                          nullptr, dqp, (float *)dk.p, (float *)dv.p, (float *)dg.p, (float *)db.p, (float *)di.p, 1, w,
+                          n, nullptr);
+    };
+    const int before = g_stub.bwd_calls;
+    CHECK(call(a.o.p, (float *)dq.p, ws.p, wsb) == LA_OK && g_stub.bwd_calls == before + 1);
+    // every region of the backward's workspace lies inside it
+    const char *lo = ws.c(), *hi = ws.c() + wsb;
+    const char *parts[] = {reinterpret_cast<const char *>(g_stub.last_ws.WTF),
+                           reinterpret_cast<const char *>(g_stub.last_ws.PTF),
+                           reinterpret_cast<const char *>(g_stub.last_ws.TB),
+                           reinterpret_cast<const char *>(g_stub.last_ws.SB),
+                           reinterpret_cast<const char *>(g_stub.last_ws.CK),
+                           reinterpret_cast<const char *>(g_stub.last_ws.DSN),
+                           reinterpret_cast<const char *>(g_stub.last_ws.DU),
+                           reinterpret_cast<const char *>(g_stub.last_ws.OB),
+                           reinterpret_cast<const char *>(g_stub.last_ws.DQH),
+                           reinterpret_cast<const char *>(g_stub.last_ws.DKH)};
+    for (const char *p : parts) CHECK(p >= lo && p < hi);
+    CHECK(call(nullptr, (float *)dq.p, ws.p, wsb) == LA_ERR_INVALID_ARGUMENT);
+    CHECK(call(a.o.p, nullptr, ws.p, wsb) == LA_ERR_INVALID_ARGUMENT);
+    CHECK(call(a.o.p, (float *)dq.p, ws.p, wsb - 1) == LA_ERR_WORKSPACE_TOO_SMALL);
+    CHECK(call(a.o.p, (float *)dq.p, nullptr, wsb) == LA_ERR_INVALID_ARGUMENT);
+}
+
 void status_and_profiler()
 {
     Buf ws(256);
@@ -280,6 +314,7 @@ int main()
     single_token_strides();
     declines();
     summary_bwd();
+    full_backward();
     status_and_profiler();
     std::printf("abi_driver: %d checks passed\n", g_checks);
     return 0;

@@ -35,10 +35,19 @@ hipError_t convert_cu64(const int64_t *, int32_t *, int, hipStream_t)
     return hipSuccess;
 }
 
-hipError_t run_summary_bwd(const SbwdArgs &a, hipStream_t, const LaunchHook *)
+hipError_t run_summary_bwd(const Prob &p, const Ws &, const __bf16 *, const float *, float *, hipStream_t,
+                           const LaunchHook *)
 {
     g_stub.sbwd_calls += 1;
-    g_stub.last = *a.p;
+    g_stub.last = p;
+    return hipSuccess;
+}
+
+hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &, hipStream_t, const LaunchHook *)
+{
+    g_stub.bwd_calls += 1;
+    g_stub.last = p;
+    g_stub.last_ws = w;
     return hipSuccess;
 }
 

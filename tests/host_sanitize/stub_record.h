@@ -7,6 +7,7 @@ struct StubRecord {
     int pipeline_calls = 0;
     int cu64_calls = 0;
     int sbwd_calls = 0;
+    int bwd_calls = 0;
     bool last_summary = false;
     la::Prob last{};
     la::Ws last_ws{};

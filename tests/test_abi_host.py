@@ -205,7 +205,7 @@ def test_binding_checks_layout():
 
 def test_profiler_ids(lib):
     names = [la.la_gdn_kernel_name(i) for i in range(la.LA_KERNEL_COUNT)]
-    assert names == ["k_sched", "k_intra", "k_inter"]
+    assert names == ["k_sched", "k_intra", "k_inter", "k_bwd_intra"]
     assert la.la_gdn_kernel_name(99) == ""
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.la_gdn_profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == la.LA_ERR_INVALID_ARGUMENT
@@ -379,3 +379,37 @@ def test_summary_bwd_argument_checks(lib, over, status, needle):
     rc = lib.la_gdn_summary_bwd(ctypes.byref(d), a["q"], a["k"], a["g"], a["beta"], a["cu"], a["out"], a["s0"],
                                 a["fin"], 1, a["ws"], a["wsb"], None)
     assert rc == status and needle in la.la_last_error_message(), la.la_last_error_message()
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(dout=None), la.LA_ERR_INVALID_ARGUMENT, "d_out is NULL"),
+    (dict(dq=None), la.LA_ERR_INVALID_ARGUMENT, "dq is NULL"),
+    (dict(dk=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "dk is not 4-byte"),
+    (dict(dv=None), la.LA_ERR_INVALID_ARGUMENT, "dv is NULL"),
+    (dict(dg=None), la.LA_ERR_INVALID_ARGUMENT, "dg is NULL"),
+    (dict(dbeta=None), la.LA_ERR_INVALID_ARGUMENT, "dbeta is NULL"),
+    (dict(dinit=None), la.LA_ERR_INVALID_ARGUMENT, "d_initial_state is NULL"),
+    (dict(dfin=(1 << 20) + 1), la.LA_ERR_INVALID_ARGUMENT, "d_final_state"),
+    (dict(ws=None), la.LA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
+    (dict(wsb=1024), la.LA_ERR_WORKSPACE_TOO_SMALL, "needed"),
+])
+def test_bwd_argument_checks(lib, over, status, needle):
+    """la_gdn_bwd checks its gradients' pointers and its workspace before any launch."""
+    A = 1 << 20
+    a = dict(dout=A, dfin=None, dq=A, dk=A, dv=A, dg=A, dbeta=A, dinit=A, ws=A, wsb=1 << 40)
+    a.update(over)
+    d = _desc()
+    rc = lib.la_gdn_bwd(ctypes.byref(d), A, A, A, A, A, A, None, a["dout"], a["dfin"], a["dq"], a["dk"], a["dv"],
+                        a["dg"], a["dbeta"], a["dinit"], 1, a["ws"], a["wsb"], None)
+    assert rc == status, la.la_last_error_message()
+    assert needle in la.la_last_error_message()
+
+
+def test_bwd_workspace_bytes(lib):
+    """The backward's workspace holds the forward's operands, the reverse pass's, the state
+    at every chunk start and the chunk-end state gradients (fp32 K x V each per (chunk, head))."""
+    d = _desc(T=1000)
+    n = la.la_gdn_bwd_workspace_bytes(d)
+    chunks = (1000 + 63) // 64 + 2
+    assert n >= la.la_gdn_workspace_bytes(d, False) + chunks * 4 * 2 * 128 * 128 * 4
+    assert lib.la_gdn_bwd_workspace_bytes(ctypes.byref(_desc(head_dim_k=96))) == 0

@@ -1,0 +1,147 @@
+"""GPU parity of the full backward (la_gdn_bwd) against the fp64 oracle's backward, which is
+pinned by torch autograd and central differences (test_oracle_pins.py).
+
+Tolerance: rel-L2 <= 1e-2 for every gradient (dq, dk, dv, dg, dbeta, d_initial_state), over
+the whole tensor and, within five times that, row by row.  The chunked fp64 model with the
+kernels' bf16 rounding points (chunked_model.py) predicts about 2.5e-3 on these inputs.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_50_amd as la
+import oracle
+from oracle import rel_l2
+from workloads import Problem, custom_problem, make_problem
+
+from gpu_helpers import assert_rows_close, f64, note
+
+pytestmark = pytest.mark.gpu
+
+TOL_BWD = 1e-2
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "d_init")
+
+
+def upstream(p, seed, with_final=True):
+    gen = torch.Generator().manual_seed(seed)
+    T, HV, V = p.v.shape
+    K = p.k.shape[2]
+    d_out = torch.randn((T, HV, V), generator=gen).to(torch.bfloat16)
+    d_fin = torch.randn((p.num_seqs, HV, K, V), generator=gen) if with_final else None
+    return d_out, d_fin
+
+
+def gpu_bwd(p, d_out, d_fin, scale=None, initial_state=True):
+    g = p.to("cuda")
+    res = la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, d_out.cuda(),
+                        initial_state=g.state if initial_state else None,
+                        d_final_state=None if d_fin is None else d_fin.cuda(), l2norm=p.l2norm, scale=scale)
+    torch.cuda.synchronize()
+    res["d_init"] = res.pop("d_initial_state")
+    return res
+
+
+def check_bwd(p, seed, scale=None, with_final=True, tol=TOL_BWD):
+    note(f"bwd: {p.name} T={p.total_tokens} N={p.num_seqs} HK={p.num_qk_heads} HV={p.num_v_heads} "
+         f"K={p.head_dim_k} V={p.head_dim_v} l2norm={p.l2norm}")
+    d_out, d_fin = upstream(p, seed, with_final)
+    got = gpu_bwd(p, d_out, d_fin, scale=scale)
+    pp = p if p.state is not None else dataclasses.replace(p, state=None)
+    ref = oracle.backward(pp, d_o=d_out.double().numpy(), d_final=None if d_fin is None else d_fin.double().numpy(),
+                          scale=scale)
+    errs = {}
+    for name in NAMES:
+        x, r = f64(got[name]), ref[name]
+        e = rel_l2(x, r)
+        errs[name] = e
+        assert np.isfinite(e) and e <= tol, f"{name}: rel-L2 {e:.3e} > {tol}"
+        if r.ndim >= 2 and r.size:
+            last = r.shape[-1] if name not in ("d_init",) else r.shape[-1] * r.shape[-2]
+            assert_rows_close(x.reshape(-1, last), r.reshape(-1, last), tol, f"{name} rows")
+    print("bwd rel-L2: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    return got, ref
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_backward_ragged_all_head_dims(dk, dv):
+    # ragged lengths with a length-1, an exact-chunk and a partial-chunk sequence, grouped
+    # heads (2 q/k heads, 4 value heads) and an initial state
+    check_bwd(custom_problem((1, 63, 64, 65, 130, 200), hk=2, hv=4, dk=dk, dv=dv, seed=201, with_state=True), 202)
+
+
+def test_backward_slow_decay_every_chunk_matters():
+    # gate / 4096 and beta / 64: the state and its gradient reach across all 12 chunks
+    p = custom_problem((700, 64), hk=1, hv=4, dk=128, dv=128, seed=203, with_state=True, g_div=4096.0,
+                       beta_div=64.0)
+    got, ref = check_bwd(p, 204)
+    # not vacuous: the initial state's gradient of the first sequence differs from the end
+    # gradient it would be with the tokens' contributions dropped
+    assert np.linalg.norm(ref["d_init"][0]) > 0.5
+
+
+def test_backward_varlen_workload():
+    # the varlen workload's shapes: T = 4096 (1000 / 1500 / 1596), H = 16, K = V = 128
+    check_bwd(make_problem(2), 205)
+
+
+def test_backward_no_l2norm_custom_scale_no_final_gradient():
+    p = custom_problem((70, 130), hk=1, hv=2, dk=64, dv=64, seed=206, l2norm=False, with_state=True)
+    p = dataclasses.replace(p, k=(p.k.float() / 8).to(torch.bfloat16), q=(p.q.float() / 8).to(torch.bfloat16))
+    check_bwd(p, 207, scale=0.3, with_final=False)
+
+
+def test_backward_zero_initial_state_and_empty_sequences():
+    p = custom_problem((0, 5, 0, 129, 0), hk=2, hv=2, dk=128, dv=128, seed=208)
+    got, ref = check_bwd(p, 209)
+    d_out, d_fin = upstream(p, 209)
+    # an empty sequence passes the final-state gradient through to the initial state
+    for n in (0, 2, 4):
+        assert torch.equal(got["d_init"][n].cpu(), d_fin[n])
+
+
+def test_backward_many_sequences():
+    # more than 64 sequences: the scheduler kernel's chunk table
+    lens = [(i * 37) % 150 for i in range(70)]
+    check_bwd(custom_problem(lens, hk=2, hv=4, dk=64, dv=64, seed=210, with_state=True), 211)
+
+
+def test_backward_deterministic_and_batch_invariant():
+    p = custom_problem((100, 257, 64), hk=2, hv=4, dk=128, dv=128, seed=212, with_state=True)
+    d_out, d_fin = upstream(p, 213)
+    note("bwd: two identical calls")
+    a = gpu_bwd(p, d_out, d_fin)
+    b = gpu_bwd(p, d_out, d_fin)
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), name
+    # sequence 1 alone gives the same bits as inside the batch
+    cu = p.cu_seqlens.tolist()
+    sl = slice(cu[1], cu[2])
+    alone = Problem("alone", torch.tensor([0, cu[2] - cu[1]], dtype=torch.int32), p.q[sl].contiguous(),
+                    p.k[sl].contiguous(), p.v[sl].contiguous(), p.g[sl].contiguous(), p.beta[sl].contiguous(),
+                    p.state[1:2].clone())
+    note("bwd: one sequence alone")
+    c = gpu_bwd(alone, d_out[sl].contiguous(), d_fin[1:2].contiguous())
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.equal(c[name], a[name][sl]), name
+    assert torch.equal(c["d_init"][0], a["d_init"][1])
+
+
+def test_backward_bad_cu_seqlens_writes_nothing():
+    p = custom_problem((10, 20), hk=1, hv=1, dk=64, dv=64, seed=214)
+    g = p.to("cuda")
+    d_out, _ = upstream(p, 215, with_final=False)
+    desc = la.make_desc(g.k, g.v, g.g, g.beta, 2, q=g.q, out=d_out)
+    ws = torch.empty(la.la_gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    for bad in ([0, 25, 20], [1, 10, 30], [0, 10, 31]):
+        note(f"bwd: bad cu_seqlens {bad}")
+        out = {"dq": torch.full((30, 1, 64), 3.0, device="cuda"), "dk": torch.full((30, 1, 64), 3.0, device="cuda"),
+               "dv": torch.full((30, 1, 64), 3.0, device="cuda"), "dg": torch.full((30, 1), 3.0, device="cuda"),
+               "dbeta": torch.full((30, 1), 3.0, device="cuda"),
+               "d_initial_state": torch.full((2, 1, 64, 64), 3.0, device="cuda")}
+        la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, torch.tensor(bad, dtype=torch.int32, device="cuda"),
+                      d_out.cuda(), workspace=ws, out=out)
+        assert la.la_gdn_device_status(ws) == la.LA_DEVICE_BAD_CU_SEQLENS
+        for t in out.values():
+            assert bool((t == 3.0).all())

@@ -111,3 +111,10 @@ def test_summary_bwd_strided_views_equal_contiguous_bitwise():
     b = la.la_gdn_summary_bwd(q_v, k_v, g.g, g.beta, g.cu_seqlens, d_v, d_end.cuda())
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_summary_bwd_slow_decay_every_chunk_matters():
+    # gate / 4096 and beta / 64: the start-state gradient depends on every chunk of the span
+    # (under the faster gates above only the first chunks reach it)
+    p = custom_problem((2000, 300), hk=2, hv=4, dk=128, dv=128, seed=133, g_div=4096.0, beta_div=64.0)
+    _check(p, seed=134)
