@@ -54,7 +54,30 @@ VARIANTS = {
     "gdp2": "Gated Delta Product, 2 Householder updates per token (k, v, beta update-major)",
     "summary-bwd": "the span summary's mirror for the state gradient (la_gdn_summary_bwd: output and "
                    "end-state gradients in, start-state gradient out)",
+    "bwd": "the full backward (la_gdn_bwd: output and final-state gradients in; dq, dk, dv, dg, dbeta and "
+           "the initial-state gradient out, fp32)",
 }
+
+
+def backward_counts(lengths, HK, HV, K, V, with_init):
+    """Bytes and flops of the full backward (intermediates excluded).
+
+    Bytes: q, k, v and the output gradient (bf16), g and beta (fp32) read; dq, dk, dv,
+    dg and dbeta (fp32) written; per sequence and head the final-state gradient read,
+    the initial-state gradient written and the initial state read when given.  Flops of
+    the chunked method, masked tiles counted whole: the forward again (as
+    algorithmic_counts), the reverse chunk pass (K dS, P^T dO, Q^T dO, W^T dU:
+    2 (3 K V + C V) per token-head) and the intra pass (U, dO S0^T, dU S0^T, U dS^T:
+    8 K V; eight 64 x 64 x K products, three 64 x 64 x V and two 64 x 64 x 64:
+    2 C (8 K + 3 V + 2 C) per token-head)."""
+    T = sum(lengths)
+    N = len(lengths)
+    C = CHUNK
+    by = (T * (2 * HK * K * 2 + 2 * HV * V * 2 + 2 * HV * 4 + 2 * HK * K * 4 + HV * V * 4 + 2 * HV * 4)
+          + N * HV * K * V * 4 * (2 + int(with_init)))
+    _, fwd = algorithmic_counts(lengths, HK, HV, K, V, False, with_init, True)
+    fl = fwd + T * HV * (2 * (3 * K * V + C * V) + 8 * K * V + 2 * C * (8 * K + 3 * V + 2 * C))
+    return by, fl
 
 
 def algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, with_final, nh=1, beta_bytes=4,
@@ -200,6 +223,9 @@ def main(argv=None):
     elif variant != "plain" and summary:
         print("--variant applies to the forward workloads (1 to 4)", file=sys.stderr)
         return 2
+    if variant == "bwd" and wl == 4:
+        print("--variant bwd runs on the workloads 1, 2 and 3", file=sys.stderr)
+        return 2
     lengths = prob.lengths()
     T, HK, HV, K, V = prob.total_tokens, prob.num_qk_heads, prob.num_v_heads, prob.head_dim_k, prob.head_dim_v
     N = prob.num_seqs
@@ -230,6 +256,10 @@ def main(argv=None):
     copies = max(1, args.copies) if by0 < (1 << 30) else 1
     sets = []
     bwd_in = None
+    if variant == "bwd":
+        gen = torch.Generator(device="cuda").manual_seed(wl)
+        bwd_in = (torch.randn((T, HV, V), generator=gen, device=dev).to(torch.bfloat16),
+                  torch.randn((N, HV, K, V), generator=gen, device=dev))
     if variant == "summary-bwd":
         gen = torch.Generator(device="cuda").manual_seed(wl)
         bwd_in = (torch.randn((T, HV, V), generator=gen, device=dev).to(torch.bfloat16),
@@ -244,6 +274,14 @@ def main(argv=None):
             out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=dev)
             desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out, num_householder=nh)
         fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
+        if variant == "bwd":
+            desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=bwd_in[0])
+            ws = torch.empty(la.la_gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+            grads = {"dq": torch.empty((T, HK, K), device=dev), "dk": torch.empty((T, HK, K), device=dev),
+                     "dv": torch.empty((T, HV, V), device=dev), "dg": torch.empty((T, HV), device=dev),
+                     "dbeta": torch.empty((T, HV), device=dev), "d_initial_state": fin}
+            sets.append((g, grads, fin, ws, None))
+            continue
         ws = torch.empty(la.la_gdn_workspace_bytes_ex(desc, summary, nh), dtype=torch.uint8, device=dev)
         ck = torch.empty((n_ck, HV, K, V), dtype=ck_dtype, device=dev) if every else None
         sets.append((g, out, fin, ws, ck))
@@ -251,7 +289,10 @@ def main(argv=None):
 
     def step(i):
         g, out, fin, ws, ck = sets[i % len(sets)]
-        if variant == "summary-bwd":
+        if variant == "bwd":
+            la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, bwd_in[0], initial_state=g.state,
+                          d_final_state=bwd_in[1], workspace=ws, stream=stream, out=out)
+        elif variant == "summary-bwd":
             la.la_gdn_summary_bwd(g.q, g.k, g.g, g.beta, g.cu_seqlens, bwd_in[0], bwd_in[1], d_start_state=fin,
                                   workspace=ws, stream=stream)
         elif summary:
@@ -322,9 +363,13 @@ def main(argv=None):
     by, fl = algorithmic_counts(lengths, HK, HV, K, V, summary, with_init, True, **count_kw)
     if variant == "summary-bwd":
         # q, k (bf16 per q/k head), d_out (bf16), g, beta per value head; the end- and
-        # start-state gradients; per token-head 6 K V flops (X, k^T X and the update)
+        # start-state gradients.  Flops of the chunked method: per q/k-head token the Gram
+        # and q k^T products (2 * 2 C K), per value-head token W (2 C K) and the reverse
+        # chunk pass (2 (3 K V + C V))
         by = T * (2 * HK * K * 2 + HV * V * 2 + 2 * HV * 4) + 2 * N * HV * K * V * 4
-        fl = 6 * T * HV * K * V
+        fl = T * (HK * 2 * 2 * CHUNK * K + HV * (2 * CHUNK * K + 2 * (3 * K * V + CHUNK * V)))
+    elif variant == "bwd":
+        by, fl = backward_counts(lengths, HK, HV, K, V, with_init)
     # Roofline of the call: the path's algorithmic bytes (or flops) over the GPU time of
     # all the kernels one call launches, each timed with HIP events on the launch
     # stream (their sum is what rocprofv3 reports for the same kernels).  The span

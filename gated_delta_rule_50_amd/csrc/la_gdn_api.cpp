@@ -700,8 +700,10 @@ la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, cons
     if (!aligned4(cu_seqlens)) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
     if ((st = check_f32("initial_state", initial_state, false)) != LA_OK) return st;
     if ((st = check_f32("d_final_state", d_final_state, false)) != LA_OK) return st;
-    if ((st = check_f32("dq", dq, true)) != LA_OK) return st;
-    if ((st = check_f32("dk", dk, true)) != LA_OK) return st;
+    if (!dq) return fail(LA_ERR_INVALID_ARGUMENT, "dq is NULL");
+    if (!dk) return fail(LA_ERR_INVALID_ARGUMENT, "dk is NULL");
+    if (!aligned16(dq) || !aligned16(dk))
+        return fail(LA_ERR_INVALID_ARGUMENT, "dq and dk must be 16-byte aligned (they are written with 128-bit stores)");
     if ((st = check_f32("dv", dv, true)) != LA_OK) return st;
     if ((st = check_f32("dg", dg, true)) != LA_OK) return st;
     if ((st = check_f32("dbeta", dbeta, true)) != LA_OK) return st;

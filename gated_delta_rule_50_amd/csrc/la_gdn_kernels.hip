@@ -2010,24 +2010,36 @@ __device__ __forceinline__ float lds_elem(const lds_char *tile, int row, int col
     return bf2f(*reinterpret_cast<const lds_bf16 *>(tile + swz_e<PPR>(row, col)));
 }
 
-// fp32 rows (row-major, `cols` floats apart) into a swizzled bf16 tile; returns this thread's
-// share of sum(a * b) when `dot` is given (then `a` and `b` are both converted).
-template <int PPR>
-__device__ __forceinline__ float load_f32_tile(lds_char *dst, const float *src, int rows, int cols, int tid,
-                                               lds_char *dst2 = nullptr, const float *src2 = nullptr)
+// fp32 rows (ROWS x COLS, row-major) into a swizzled bf16 tile (COLS / 8 pieces per row), by
+// the 256 threads of the block in batches of 8 float4 loads per thread, all issued before
+// any is used; with `src2`, a second matrix of the same shape into `dst2` alongside, and the
+// thread's share of sum(src * src2) returned.
+template <int ROWS, int COLS>
+__device__ __forceinline__ float load_f32_tile(lds_char *dst, const float *src, int tid, lds_char *dst2 = nullptr,
+                                               const float *src2 = nullptr)
 {
+    constexpr int PPR = COLS / 8, N4 = ROWS * COLS / 4 / 256, B = N4 < 8 ? N4 : 8;
+    static_assert(N4 % B == 0, "whole batches");
     float dot = 0.f;
-    const int n4 = rows * cols / 4;
-    for (int idx = tid; idx < n4; idx += 256) {
-        const int row = idx / (cols / 4), c4 = 4 * (idx % (cols / 4));
-        const float4 a = *reinterpret_cast<const float4 *>(src + (int64_t)row * cols + c4);
-        bf16x4 va = {f2bf(a.x), f2bf(a.y), f2bf(a.z), f2bf(a.w)};
-        *reinterpret_cast<lds_bf16x4 *>(dst + swz<PPR>(row, c4)) = va;
-        if (src2) {
-            const float4 b = *reinterpret_cast<const float4 *>(src2 + (int64_t)row * cols + c4);
-            bf16x4 vb = {f2bf(b.x), f2bf(b.y), f2bf(b.z), f2bf(b.w)};
-            *reinterpret_cast<lds_bf16x4 *>(dst2 + swz<PPR>(row, c4)) = vb;
-            dot += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+#pragma unroll
+    for (int b0 = 0; b0 < N4; b0 += B) {
+        float4 a[B], c[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int idx = tid + 256 * (b0 + j), row = idx / (COLS / 4), c4 = 4 * (idx % (COLS / 4));
+            a[j] = *reinterpret_cast<const float4 *>(src + (int64_t)row * COLS + c4);
+            if (src2) c[j] = *reinterpret_cast<const float4 *>(src2 + (int64_t)row * COLS + c4);
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int idx = tid + 256 * (b0 + j), row = idx / (COLS / 4), c4 = 4 * (idx % (COLS / 4));
+            bf16x4 va = {f2bf(a[j].x), f2bf(a[j].y), f2bf(a[j].z), f2bf(a[j].w)};
+            *reinterpret_cast<lds_bf16x4 *>(dst + swz<PPR>(row, c4)) = va;
+            if (src2) {
+                bf16x4 vc = {f2bf(c[j].x), f2bf(c[j].y), f2bf(c[j].z), f2bf(c[j].w)};
+                *reinterpret_cast<lds_bf16x4 *>(dst2 + swz<PPR>(row, c4)) = vc;
+                dot += a[j].x * c[j].x + a[j].y * c[j].y + a[j].z * c[j].z + a[j].w * c[j].w;
+            }
         }
     }
     return dot;
@@ -2108,8 +2120,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         s_eg[tid] = exp2_hw(gam);
         s_dd[tid] = exp2_hw(tid < len ? gn - gam : kNegInf);
     }
-    float dot = load_f32_tile<PV>(L + oS0, w.CK + chh * K * V, K, V, tid, L + oDS, w.DSN + chh * K * V);
-    load_f32_tile<PV>(L + oDU, w.DU + chh * 64 * V, 64, V, tid);
+    float dot = load_f32_tile<K, V>(L + oS0, w.CK + chh * K * V, tid, L + oDS, w.DSN + chh * K * V);
+    load_f32_tile<64, V>(L + oDU, w.DU + chh * 64 * V, tid);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (lane == 0) sdot[wave] = dot;
@@ -2429,14 +2441,14 @@ __global__ __launch_bounds__(256) void k_bwd_qk(Prob p, const Ws w, float *dq, f
     const int G = p.HV / p.HK;
     float gq[8] = {}, gk[8] = {}, xq[8], xk[8];
     if (live) {
+        const float4 *a = reinterpret_cast<const float4 *>(w.DQH + ((t * p.HV + hk * G) * K + 8 * piece));
+        const float4 *b = reinterpret_cast<const float4 *>(w.DKH + ((t * p.HV + hk * G) * K + 8 * piece));
         for (int j = 0; j < G; ++j) {
-            const float *a = w.DQH + ((t * p.HV + hk * G + j) * K + 8 * piece);
-            const float *b = w.DKH + ((t * p.HV + hk * G + j) * K + 8 * piece);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                gq[e] += a[e];
-                gk[e] += b[e];
-            }
+            const float4 a0 = a[j * (K / 4)], a1 = a[j * (K / 4) + 1], b0 = b[j * (K / 4)], b1 = b[j * (K / 4) + 1];
+            gq[0] += a0.x; gq[1] += a0.y; gq[2] += a0.z; gq[3] += a0.w;
+            gq[4] += a1.x; gq[5] += a1.y; gq[6] += a1.z; gq[7] += a1.w;
+            gk[0] += b0.x; gk[1] += b0.y; gk[2] += b0.z; gk[3] += b0.w;
+            gk[4] += b1.x; gk[5] += b1.y; gk[6] += b1.z; gk[7] += b1.w;
         }
         const bf16x8 q8 = *reinterpret_cast<const bf16x8 *>(p.q + t * p.qst + (int64_t)hk * p.qsh + 8 * piece);
         const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(p.k + t * p.kst + (int64_t)hk * p.ksh + 8 * piece);
@@ -2467,13 +2479,18 @@ __global__ __launch_bounds__(256) void k_bwd_qk(Prob p, const Ws w, float *dq, f
     if (!live) return;
     const float rq = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f, rk = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
     const float cq = p.l2norm ? rq * rq * rq * dqx : 0.f, ck = p.l2norm ? rk * rk * rk * dkx : 0.f;
-    float *oq = dq + (t * p.HK + hk) * K + 8 * piece;
-    float *ok = dk + (t * p.HK + hk) * K + 8 * piece;
+    float oq[8], ok[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         oq[e] = p.scale * (rq * gq[e] - cq * xq[e]);
         ok[e] = rk * gk[e] - ck * xk[e];
     }
+    float4 *dq4 = reinterpret_cast<float4 *>(dq + (t * p.HK + hk) * K + 8 * piece);
+    float4 *dk4 = reinterpret_cast<float4 *>(dk + (t * p.HK + hk) * K + 8 * piece);
+    dq4[0] = make_float4(oq[0], oq[1], oq[2], oq[3]);
+    dq4[1] = make_float4(oq[4], oq[5], oq[6], oq[7]);
+    dk4[0] = make_float4(ok[0], ok[1], ok[2], ok[3]);
+    dk4[1] = make_float4(ok[4], ok[5], ok[6], ok[7]);
 }
 
 hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_t s, const LaunchHook *hook)

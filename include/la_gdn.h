@@ -267,8 +267,8 @@ la_status la_gdn_summary_bwd(const la_gdn_desc *desc, const void *q, const void 
  *                  fp32 beta, natural-log gate, int32 cu_seqlens)
  *   d_out          device, bf16 [T, HV, V], strides o_stride_t / o_stride_h of desc
  *   d_final_state  device, fp32 [N, HV, K, V], or NULL for zeros
- *   dq, dk         device, fp32 [T, HK, K] contiguous, written (summed over the value heads
- *                  that share a q/k head, in a fixed order)
+ *   dq, dk         device, fp32 [T, HK, K] contiguous, 16-byte aligned, written (summed over
+ *                  the value heads that share a q/k head, in a fixed order)
  *   dv             device, fp32 [T, HV, V] contiguous, written
  *   dg, dbeta      device, fp32 [T, HV] contiguous, written (dg: gradient of the natural-log gate)
  *   d_initial_state  device, fp32 [N, HV, K, V], written (zero-start inputs still get it)

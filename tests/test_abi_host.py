@@ -384,7 +384,8 @@ def test_summary_bwd_argument_checks(lib, over, status, needle):
 @pytest.mark.parametrize("over,status,needle", [
     (dict(dout=None), la.LA_ERR_INVALID_ARGUMENT, "d_out is NULL"),
     (dict(dq=None), la.LA_ERR_INVALID_ARGUMENT, "dq is NULL"),
-    (dict(dk=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "dk is not 4-byte"),
+    (dict(dk=(1 << 20) + 4), la.LA_ERR_INVALID_ARGUMENT, "16-byte aligned"),
+    (dict(dv=(1 << 20) + 2), la.LA_ERR_INVALID_ARGUMENT, "dv is not 4-byte"),
     (dict(dv=None), la.LA_ERR_INVALID_ARGUMENT, "dv is NULL"),
     (dict(dg=None), la.LA_ERR_INVALID_ARGUMENT, "dg is NULL"),
     (dict(dbeta=None), la.LA_ERR_INVALID_ARGUMENT, "dbeta is NULL"),

@@ -55,3 +55,13 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_backward_counts_varlen():
+    # per token-head at H = 16, K = V = 128: q, k, v, dO in bf16 (4 x 256 B), g, beta (8 B)
+    # read; dq, dk, dv in fp32 (3 x 512 B), dg, dbeta (8 B) written: 2576 B; plus per (sequence,
+    # head) the final-state gradient read and the initial-state gradient written.  Flops: the
+    # forward (180,224), the reverse chunk pass (114,688) and the intra pass (327,680)
+    by, fl = bench.backward_counts(config_lengths(2), 16, 16, 128, 128, False)
+    assert by == 4096 * 16 * 2576 + 48 * 2 * 128 * 128 * 4
+    assert fl == 4096 * 16 * (180224 + 114688 + 327680)

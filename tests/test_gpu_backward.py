@@ -145,3 +145,10 @@ def test_backward_bad_cu_seqlens_writes_nothing():
         assert la.la_gdn_device_status(ws) == la.LA_DEVICE_BAD_CU_SEQLENS
         for t in out.values():
             assert bool((t == 3.0).all())
+
+
+def test_backward_dense_batch_slow_decay_companion():
+    # the dense batch's shapes (8 x 4096 tokens, HK = 4, HV = 16, K = V = 128, initial state)
+    # on its slow-decay companion, where the initial state and the gradients reach across
+    # every chunk of each sequence
+    check_bwd(make_problem(3, companion=True), 216)

@@ -118,3 +118,40 @@ def test_summary_bwd_and_int64_offsets_graph_replays_match_eager():
         o_e, f_e = la.la_gdn_fwd(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, initial_state=p.state)
         torch.cuda.synchronize()
         assert torch.equal(s_g, s_e) and torch.equal(o_g, o_e) and torch.equal(f_g, f_e), f"replay {rep}"
+
+
+def test_backward_graph_replays_match_eager():
+    p = custom_problem((100, 257, 64), hk=2, hv=4, dk=128, dv=128, seed=330, with_state=True).to("cuda")
+    T, HK, HV, K, V, N = p.total_tokens, p.num_qk_heads, p.num_v_heads, p.head_dim_k, p.head_dim_v, p.num_seqs
+    gen = torch.Generator(device="cuda").manual_seed(331)
+    d_out = torch.randn((T, HV, V), generator=gen, device="cuda").to(torch.bfloat16)
+    d_fin = torch.randn((N, HV, K, V), generator=gen, device="cuda")
+    grads = {"dq": torch.empty((T, HK, K), device="cuda"), "dk": torch.empty((T, HK, K), device="cuda"),
+             "dv": torch.empty((T, HV, V), device="cuda"), "dg": torch.empty((T, HV), device="cuda"),
+             "dbeta": torch.empty((T, HV), device="cuda"), "d_initial_state": torch.empty((N, HV, K, V), device="cuda")}
+    desc = la.make_desc(p.k, p.v, p.g, p.beta, N, q=p.q, out=d_out)
+    ws = torch.empty(la.la_gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+
+    def call():
+        la.la_gdn_bwd(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, d_out, initial_state=p.state, d_final_state=d_fin,
+                      workspace=ws, out=grads)
+
+    call()
+    torch.cuda.synchronize()
+    note("graph capture of la_gdn_bwd")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _load(p, custom_problem((100, 257, 64), hk=2, hv=4, dk=128, dv=128, seed=332 + rep,
+                                with_state=True).to("cuda"))
+        d_out.copy_(torch.randn((T, HV, V), generator=gen, device="cuda").to(torch.bfloat16))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: t.clone() for k, t in grads.items()}
+        eager = la.la_gdn_bwd(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, d_out, initial_state=p.state,
+                              d_final_state=d_fin)
+        torch.cuda.synchronize()
+        for k in got:
+            assert torch.equal(got[k], eager[k]), f"replay {rep}: {k}"
