@@ -466,7 +466,7 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     const size_t items = (size_t)(C * HV);
     L.WF = take(fwd_ops ? items * 64 * K * 2 : 0);        // 64 x K bf16
     L.PF = take(summary || !fwd_ops ? 0 : items * 6 * la::kFrag);
-    L.UF = take(fwd_ops ? items * 64 * V * 4 : 0);        // 64 x V fp32
+    L.UH = take(fwd_ops ? items * 64 * V * 2 : 0);        // 64 x V fp16
     L.SC = take(items * la::kScalars * 4);
     L.cu32 = take(sizeof(int32_t) * (size_t)(N + 1));
     L.WTF = take(bwd ? items * 64 * K * 2 : 0);
@@ -493,7 +493,7 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.order = reinterpret_cast<int32_t *>(b + L.order);
     w.WF = reinterpret_cast<uint4 *>(b + L.WF);
     w.PF = summary ? nullptr : reinterpret_cast<uint4 *>(b + L.PF);
-    w.UF = reinterpret_cast<float4 *>(b + L.UF);
+    w.UH = reinterpret_cast<uint2 *>(b + L.UH);
     w.SC = reinterpret_cast<float *>(b + L.SC);
     w.cu32 = reinterpret_cast<int32_t *>(b + L.cu32);
     w.WTF = reinterpret_cast<uint4 *>(b + L.WTF);

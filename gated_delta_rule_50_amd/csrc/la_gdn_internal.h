@@ -12,7 +12,7 @@ namespace la {
 constexpr int kChunk = 64;            // tokens per chunk; chunks restart at every sequence start
 constexpr int kSortMax = 8192;        // sequences the scheduler orders longest-first (more: batch order)
 constexpr int kFrag = 64 * 16;        // bytes of one MFMA operand fragment (64 lanes x 16 bytes)
-constexpr int kScalars = 256;         // fp32 per (chunk, v-head): d[64], sq[64], gl (one fragment)
+constexpr int kScalars = 256;         // fp32 per (chunk, v-head): d[64], sq[64], U~ scales, gl (one fragment)
 
 // Problem description as the kernels see it (element strides, device pointers).
 struct Prob {
@@ -61,9 +61,12 @@ struct Ws {
     int32_t *order;    // [N]  sequences, longest first (ties: lower index first)
     uint4 *WF;         // [chunk, HV][key half][token tile][step]  -W, W = T diag(beta 2^gam r_k) K, A fragments
     uint4 *PF;         // [chunk, HV][6]  P^T (masked decayed scaled q k^T), B fragments, forward only
-    float4 *UF;        // [chunk, HV][V/32][token tile][4]  U~ = T diag(beta) V, fp32 accumulator tiles
+    uint2 *UH;         // [chunk, HV][V/32][token tile][4]  U~ = T diag(beta) V as 32 x 32 accumulator
+                       // tiles in fp16, four per lane, each tile scaled by 2^(15 - E) (E: the exponent
+                       // with the tile's largest magnitude in [2^(E-1), 2^E))
     float *SC;         // [chunk, HV, kScalars]  per token: d = 2^(gam_n - gam) r_k at 0,
-                       // sq = scale r_q 2^gam at 64 (forward); gl = 2^gam_n at 192
+                       // sq = scale r_q 2^gam at 64 (forward); gl = 2^gam_n at 192; the U~ tiles'
+                       // E - 15 (int bits) at 128 + 2 (value tile) + token tile
     int32_t *cu32;     // [N + 1]  int32 copy of int64 cu_seqlens (when given as int64)
     // backward only (see workspace_layout's `bwd`):
     uint4 *WTF;        // [chunk, HV][K/32 key tiles][4 token steps]  -W^T A fragments (tokens in
@@ -83,7 +86,7 @@ struct Ws {
 // pass's operands only); 2 the full backward (the forward's operands, the reverse pass's,
 // and the per-chunk states and gradients the backward's intra pass reads).
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, WF, PF, UF, SC, cu32, WTF, PTF, TB, SB, CK, DSN, DU, OB, DQH, DKH, total;
+    size_t hdr, seq_info, chunks, order, WF, PF, UH, SC, cu32, WTF, PTF, TB, SB, CK, DSN, DU, OB, DQH, DKH, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
                           bool summary, int bwd = 0);

@@ -383,6 +383,40 @@ typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+
+// U~ hand-over in fp16: each 32 x 32 accumulator tile is scaled by 2^(15 - E), E the
+// exponent with the tile's largest magnitude in [2^(E-1), 2^E), so that it lands in
+// [2^14, 2^15) and every element keeps fp16's 11-bit significand (round to nearest even).
+// Returns E - 15, the same in every lane (0 - 15 for an all-zero tile).
+__device__ __forceinline__ int f16_tile_shift(const f32x16 &acc)
+{
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(acc[e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    return __builtin_amdgcn_frexp_expf(a) - 15;
+}
+
+// Registers 4 j .. 4 j + 3 of a tile, scaled by 2^-sh and rounded to fp16.
+__device__ __forceinline__ uint2 f16_pack4(const f32x16 &acc, int j, int sh)
+{
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_ldexpf(acc[4 * j + e], -sh);
+    return __builtin_bit_cast(uint2, __builtin_convertvector(x, f16x4));
+}
+
+// Back to fp32 (exact): four fp16 values times 2^sh.
+__device__ __forceinline__ f32x4 f16_unpack4(u32x2 h, int sh)
+{
+    const f32x4 x = __builtin_convertvector(__builtin_bit_cast(f16x4, h), f32x4);
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_amdgcn_ldexpf(x[e], sh);
+    return r;
+}
 typedef __attribute__((address_space(3))) __bf16 lds_bf16;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
@@ -1029,10 +1063,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                     acc = mfma32(th[s], vb, acc);
                     acc = mfma32(tl[s], vb, acc);
                 }
+                const int sh = f16_tile_shift(acc);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    w.UF[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] =
-                        make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+                    w.UH[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] = f16_pack4(acc, j, sh);
+                if (lane == 0) w.SC[ch_h * kScalars + 128 + 2 * ct + m] = __int_as_float(sh);
             }
         }
         lds_barrier();   // the next item's loads overwrite sK, sX and the scalars
@@ -1093,12 +1128,12 @@ struct InterCfg {
     static constexpr int NKS = KH / 16;           // reduction steps over a key half
     static constexpr int PPR = K / 8;             // 16-byte pieces per k or q row
     // operands in the workspace, per (chunk, head), in 1 KiB fragments: -W
-    // [kh][token tile][step] (FW), U~ [value tile][token tile][j] (FU per value tile),
-    // both loaded by the state waves straight into registers.  In LDS: raw k (64 x K
+    // [kh][token tile][step] (FW), loaded by the state waves straight into registers, and
+    // U~ [value tile][token tile][j] in fp16 (FU per value tile).  In LDS: U~, raw k (64 x K
     // bf16, pieces swizzled by row) in its own array; raw q (same layout), P^T (tile
     // 0 steps 0..1, tile 1 steps 0..3) and the scalars (d[64], sq[64], 2^(gam_n) at
     // 192) in the other.
-    static constexpr int FW = 4 * NKS, FU = 8, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
+    static constexpr int FW = 4 * NKS, FU = 4, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
     static constexpr int oU = 0, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
     static constexpr int FK = K / 8, oK = 0, NFL = FK;
     static constexpr int NKL = FK / 2;            // k tile loads per loader wave
@@ -1208,7 +1243,7 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
         n += C::FQ / 2 + 3;
     }
     if (!x.ptile) {
-        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UF) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
+        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UH) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
                                    C::FU * kFrag);
 #pragma unroll
         for (int i = 0; i < C::FU / 2; ++i) {
@@ -1518,9 +1553,11 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         f32x16 X[2];
         X[1] = f32x16{};
         if (!x.ptile) {
+            const lds_u32x2 *uh = reinterpret_cast<const lds_u32x2 *>(eb + C::oU * 64) + kh * 4 * 64;
+            const int sh = __float_as_int(reinterpret_cast<const lds_float *>(eb + C::oS * 64)[128 + 2 * x.tile + kh]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 u4 = __builtin_bit_cast(f32x4, eb[(C::oU + 4 * kh + j) * 64 + lane]);
+                const f32x4 u4 = f16_unpack4(uh[j * 64 + lane], sh);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) X[0][4 * j + e] = u4[e];
             }
@@ -2137,14 +2174,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < NVT / 2; ++i) {
             const int vt = half + 2 * i;
+            const int sh = __float_as_int(w.SC[chh * kScalars + 128 + 2 * vt + tm]);
             f32x16 acc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float4 u4 = w.UF[(((chh * (V / 32) + vt) * 2 + tm) * 4 + j) * 64 + lane];
-                acc[4 * j] = u4.x;
-                acc[4 * j + 1] = u4.y;
-                acc[4 * j + 2] = u4.z;
-                acc[4 * j + 3] = u4.w;
+                const uint2 h = w.UH[(((chh * (V / 32) + vt) * 2 + tm) * 4 + j) * 64 + lane];
+                const f32x4 u4 = f16_unpack4(__builtin_bit_cast(u32x2, h), sh);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * j + e] = u4[e];
             }
 #pragma unroll
             for (int kg = 0; kg < KS; ++kg) acc = mfma32(Wf[kg], lds_tr32s<PV, true>(tS0, 16 * kg, 32 * vt, lane), acc);

@@ -44,6 +44,23 @@ def f32(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
+def f16_tiles(x: np.ndarray, tile: int = 32) -> np.ndarray:
+    """x [..., n, m] (fp32 values) rounded to fp16 per tile x tile block, each block scaled
+    first by the power of two 2^(15 - E), E the exponent with max|block| in [2^(E-1), 2^E),
+    and scaled back exactly afterwards (all-zero blocks stay zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    n, m = x.shape[-2:]
+    for r0 in range(0, n, tile):
+        for c0 in range(0, m, tile):
+            blk = x[..., r0:r0 + tile, c0:c0 + tile]
+            amax = np.max(np.abs(blk), axis=(-2, -1), keepdims=True)
+            e = np.frexp(amax)[1]
+            scaled = np.ldexp(blk, 15 - e).astype(np.float32).astype(np.float16)
+            out[..., r0:r0 + tile, c0:c0 + tile] = np.ldexp(scaled.astype(np.float64), e - 15)
+    return out
+
+
 def unit_lower_inverse(A: np.ndarray) -> np.ndarray:
     """(I + A)^-1 for strictly lower-triangular A ([..., n, n]) by forward substitution,
     column by column: x_i = e_i - sum_{k<i} A[i, k] x_k, one row at a time."""
@@ -63,9 +80,12 @@ class Rounding:
     about fp32), S rounded to bf16 as the operand of W S and Q S, diag(d) U rounded to
     bf16 as the operand of the state update, U rounded to bf16 as the operand of P U,
     states kept in fp32, o rounded to bf16.  ut_bf16 instead rounds U~ itself to bf16
-    (the plain all-bf16 design)."""
+    (the plain all-bf16 design); ut_f16 rounds the about-fp32 U~ to fp16 after scaling
+    each 32 x 32 tile (32 tokens, 32 value columns) by a power of two that puts its
+    largest magnitude in [2^14, 2^15) (the kernels' hand-over format)."""
     exact: bool = True
     ut_bf16: bool = False
+    ut_f16: bool = False
 
     def r16(self, x):
         return x if self.exact else bf16(x)
@@ -77,6 +97,7 @@ class Rounding:
 EXACT = Rounding(exact=True)
 KERNEL = Rounding(exact=False)
 ALL_BF16 = Rounding(exact=False, ut_bf16=True)
+KERNEL_F16 = Rounding(exact=False, ut_f16=True)
 
 
 def _masked_exp(gam: np.ndarray, strict: bool) -> np.ndarray:
@@ -124,6 +145,8 @@ def chunked_sequence(q, k, v, g, beta, S0, scale: float, l2norm: bool, rounding:
             hi = bf16(TB)
             lo = bf16(TB - hi)
             Ut = f32(hi @ Vc + lo @ Vc)
+            if rnd.ut_f16:
+                Ut = f16_tiles(Ut)
         Sb = rnd.r16(S)
         U = rnd.r32(Ut - W @ Sb)
         gn = gam[:, -1]
@@ -235,6 +258,8 @@ def chunked_backward_sequence(q, k, v, g, beta, S0, dO, dS_final, scale: float, 
             TB = T * b[:, None, :]
             hi = bf16(TB)
             Ut = f32(hi @ Vc + bf16(TB - hi) @ Vc)
+            if rnd.ut_f16:
+                Ut = f16_tiles(Ut)
             U = f32(Ut - W @ B(S0c))
         dU = d[:, :, None] * (Kh @ B(dS)) + B(tr(P)) @ dOc
         dS_prev = (np.exp(gn)[:, None, None] * dS + tr(Qc) @ B(scale * (s_q * eg)[:, :, None] * dOc)

@@ -103,7 +103,7 @@ void valid_calls()
     const char *lo = a.ws.c(), *hi = a.ws.c() + a.wsb;
     const char *parts[] = {reinterpret_cast<const char *>(g_stub.last_ws.hdr),
                            reinterpret_cast<const char *>(g_stub.last_ws.WF),
-                           reinterpret_cast<const char *>(g_stub.last_ws.UF),
+                           reinterpret_cast<const char *>(g_stub.last_ws.UH),
                            reinterpret_cast<const char *>(g_stub.last_ws.SC),
                            reinterpret_cast<const char *>(g_stub.last_ws.cu32)};
     for (const char *p : parts) CHECK(p >= lo && p < hi);

@@ -61,10 +61,10 @@ def test_workspace_bytes(lib):
     fwd = la.la_gdn_workspace_bytes(d, False)
     summ = la.la_gdn_workspace_bytes(d, True)
     assert fwd > 0 and summ > 0
-    # per (chunk, v-head): -W (64 x K bf16), U~ (64 x V fp32), P^T (forward: six 1 KiB
+    # per (chunk, v-head): -W (64 x K bf16), U~ (64 x V fp16), P^T (forward: six 1 KiB
     # fragments, the causal 32 x 32 tiles), per-token scalars (1 KiB)
     chunks = (100 + 63) // 64 + 2
-    assert fwd >= chunks * 4 * (64 * (2 * 128 + 4 * 128) + 6 * 1024 + 1024)
+    assert fwd >= chunks * 4 * (64 * (2 * 128 + 2 * 128) + 6 * 1024 + 1024)
     assert summ < fwd                      # no P
     bigger = la.la_gdn_workspace_bytes(_desc(T=1000), False)
     assert bigger > fwd

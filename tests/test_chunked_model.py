@@ -11,7 +11,7 @@ kernel design (U~ in fp32 through a bf16 hi/lo pair) is recorded here.
 import numpy as np
 import pytest
 
-from chunked_model import ALL_BF16, EXACT, KERNEL, chunked_forward, unit_lower_inverse
+from chunked_model import ALL_BF16, EXACT, KERNEL, KERNEL_F16, chunked_forward, f16_tiles, unit_lower_inverse
 from oracle import Oracle, rel_l2
 from workloads import custom_problem, make_problem
 
@@ -88,6 +88,38 @@ def test_kernel_rounding_plan_on_the_varlen_workload():
     es2 = rel_l2(fin2, ref["state"])
     print(f"U~ in bf16: final {es2:.2e}, o {rel_l2(o2, ref['o']):.2e}")
     assert es2 > 1.3 * es
+    # the kernels' fp16 hand-over of U~ (power-of-two scale per 32 x 32 tile) costs
+    # under 2 % of the final-state error of the fp32 hand-over
+    o3, fin3 = chunked_forward(p, KERNEL_F16)
+    es3, eo3 = rel_l2(fin3, ref["state"]), rel_l2(o3, ref["o"])
+    print(f"U~ in scaled fp16: final {es3:.2e}, o {eo3:.2e}")
+    assert es3 <= 1.02 * es and eo3 <= 1.02 * eo
+
+
+def test_f16_tiles_rounding():
+    """The scaled fp16 tiles: every element within 2^-11 relative (fp16's unit roundoff)
+    wherever it is within 2^28 of its tile's largest magnitude, powers of two and zero
+    tiles exact, tiles independent, and values far above fp16's range kept."""
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(3, 64, 96)) * np.exp(rng.normal(size=(3, 64, 96)) * 3)
+    x = x.astype(np.float32).astype(np.float64)
+    x[0, :32, :32] = 0.0
+    x[1, 32:, 32:64] = 2.0 ** rng.integers(-60, 60, size=(32, 32))
+    x[2, :32, 64:] *= 1e30
+    y = f16_tiles(x)
+    for b in range(3):
+        for r in range(0, 64, 32):
+            for c in range(0, 96, 32):
+                t, u = x[b, r:r + 32, c:c + 32], y[b, r:r + 32, c:c + 32]
+                amax = np.max(np.abs(t))
+                keep = np.abs(t) >= amax * 2.0 ** -28
+                assert np.all(np.abs(u - t)[keep] <= 2.0 ** -11 * np.abs(t)[keep])
+                assert np.all(np.abs(u - t) <= 2.0 ** -11 * amax)
+    assert np.all(y[0, :32, :32] == 0.0)
+    big = x[1, 32:, 32:64]
+    exact = np.abs(big) >= np.max(np.abs(big)) * 2.0 ** -24
+    assert np.array_equal(y[1, 32:, 32:64][exact], big[exact])
+    assert np.isfinite(y).all() and np.max(np.abs(y[2, :32, 64:])) > 1e29
 
 
 @pytest.mark.parametrize("lengths,hk,hv,dk,dv,l2norm", [
