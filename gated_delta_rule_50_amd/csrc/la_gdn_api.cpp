@@ -402,6 +402,16 @@ la::Prob make_prob(const la_gdn_desc *d, int l2norm)
     p.nh = 1;
     p.max_chunks = (int32_t)((d->total_tokens + 63) / 64 + d->num_seqs);
     p.intra_grid = 3 * device_cu_count();
+    {
+        // The operands the intra pass hands to the inter pass (-W, U~, P^T, scalars per
+        // (chunk, value head)): while they fit in about half of the 256 MiB Infinity Cache
+        // the inter pass reads them from there; beyond that, non-temporal stores keep them
+        // from displacing the cache's other lines and measured faster (k_inter at 8 x 4096
+        // tokens, HV = 16: 229 -> 207 us; at 4096 tokens: 34.7 -> 38.0 us the other way).
+        const int64_t per_item = 64 * (int64_t)(d->head_dim_k + d->head_dim_v) * 2 + 7 * la::kFrag;
+        const int64_t ops = (int64_t)p.max_chunks * d->num_v_heads * per_item;
+        p.stream_ops = ops > ((int64_t)128 << 20) ? 1 : 0;
+    }
     p.qst = d->q_stride_t;
     p.qsh = d->q_stride_h;
     p.kst = d->k_stride_t;

@@ -23,6 +23,9 @@ struct Prob {
     int32_t l2norm;
     int32_t max_chunks;               // upper bound on chunks: ceil(T nh / 64) + N
     int32_t intra_grid;               // workgroups of the persistent intra-chunk kernel
+    int32_t stream_ops;               // the plain forward's and the summary's intra pass writes the
+                                      // inter pass's operands with non-temporal stores (set when
+                                      // they outgrow the Infinity Cache)
     const __bf16 *q, *k, *v;
     int64_t qst, qsh, kst, ksh, vst, vsh, ost, osh, gst, bst;
     const float *g, *beta;            // beta: fp32, or null when beta16 is set

@@ -385,6 +385,14 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 
+// A store of one of the inter pass's operands, non-temporal for NT.
+template <bool NT, typename T>
+__device__ __forceinline__ void st_op(T *dst, T v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, dst);
+    else *dst = v;
+}
+
 // U~ hand-over in fp16: each 32 x 32 accumulator tile is scaled by 2^(15 - E), E the
 // exponent with the tile's largest magnitude in [2^(E-1), 2^E), so that it lands in
 // [2^14, 2^15) and every element keeps fp16's 11-bit significand (round to nearest even).
@@ -599,11 +607,13 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
 // BW selects what the pass writes for a backward: 0 the forward's operands (plain forward
 // and summary); 1 the reverse pass's operands only (-W^T and P^T fragments and the
 // scalars, no v: the span summary's state-gradient mirror); 2 both sets, plus T in bf16 and
-// the per-token factors (gam, r_k, r_q, beta) for the backward's intra pass.
-template <int K, int V, bool FWD, bool GDP, int BW = 0>
+// the per-token factors (gam, r_k, r_q, beta) for the backward's intra pass.  NT: the
+// forward's operands (-W, U~, P^T) are written with non-temporal stores.
+template <int K, int V, bool FWD, bool GDP, int BW = 0, bool NT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_intra(Prob p, Ws w)
 {
     static_assert(BW == 0 || (FWD && !GDP), "the backward's operands come from the plain forward's pass");
+    static_assert(!NT || (BW == 0 && !GDP), "non-temporal operand stores: plain forward and summary");
     constexpr bool WANT_V = BW != 1;                // v, U~ and the forward's -W and P^T
     constexpr int PK = K / 8, PV = V / 8;           // 16-byte pieces per k / v row
     constexpr int DX = K > V ? K : V;
@@ -677,20 +687,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                 x.start - tb * p.nh, x.len, p.nh, p.inv_nh, wave, lane, 4);
         }
     };
-    if ((int)blockIdx.x < items) issue_k(item_info(blockIdx.x));
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const Item item = item_info(it);
-        const int ci = item.ci, h = item.h, hk = item.hk, start = item.start, len = item.len;
-        const int64_t ch_h = (int64_t)ci * p.HV + h;
-        // The lane index for the lane masks of this item (the scan, the diagonal of G and
-        // the causal masks of A, P^T and T) goes through an empty asm, so that the compiler
-        // forms those masks where they are used instead of hoisting all of them out of the
-        // item loop, where they do not fit in the scalar registers and are spilled.
-        int lm = lane;
-        asm volatile("" : "+v"(lm));
-        const int cm = lm & 31, hm = lm >> 5;
-
-        // ---- 1: q, g, beta into LDS (k is on its way: issued one item ahead)
+    // q (forward), g and beta of an item into LDS, issued one item ahead like k (once the
+    // previous item's last reads of sX and the scalars are done); wave 3 also takes the
+    // per-lane values that do not go through LDS.
+    struct Pre {
+        float blogit;   // beta logit of update row `lane` (beta16 only)
+        float graw;     // Gated Delta Product: the gate of update row `lane`'s token at its first update
+        bool gfirst;    // update row `lane` is its token's first update (always, for GDN)
+    };
+    Pre pre{0.f, 0.f, true};
+    auto issue_qgb = [&](const Item &x) {
+        const int start = __builtin_amdgcn_readfirstlane(x.start), len = __builtin_amdgcn_readfirstlane(x.len);
+        const int h = __builtin_amdgcn_readfirstlane(x.h), hk = __builtin_amdgcn_readfirstlane(x.hk);
         // Gated Delta Product: the chunk's first token and its first update row within it
         const int tb = GDP ? __builtin_amdgcn_readfirstlane(start / p.nh) : start;
         const int phase = start - tb * p.nh;
@@ -703,21 +711,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                     gdp_q_range(p, tb), start, len, p.nh, tb, wave, lane, 4);
             }
         }
-        float blogit = 0.f;   // beta logit of update row `lane` (beta16 only)
-        float graw = 0.f;     // Gated Delta Product: the gate of update row `lane`'s token at its first update
-        bool gfirst = true;   // update row `lane` is its token's first update (always, for GDN)
+        pre.blogit = 0.f;
+        pre.graw = 0.f;
+        pre.gfirst = true;
         if (wave == 3) {
             if (!GDP) {
                 const i32x4 rg = make_rsrc(p.g + (int64_t)start * p.gst + h, (uint32_t)len * 4u * (uint32_t)p.gst);
                 b2l_dword(rg, s_g, (uint32_t)lane * 4u * (uint32_t)p.gst);
             } else {
                 const int u = start + lane;
-                gfirst = u % p.nh == 0;
-                if (lane < len && gfirst) graw = p.g[(int64_t)(u / p.nh) * p.gst + h];
+                pre.gfirst = u % p.nh == 0;
+                if (lane < len && pre.gfirst) pre.graw = p.g[(int64_t)(u / p.nh) * p.gst + h];
             }
             if (!GDP) {
                 if (p.beta16) {
-                    if (lane < len) blogit = bf2f(p.beta16[(int64_t)(start + lane) * p.bst + h]);
+                    if (lane < len) pre.blogit = bf2f(p.beta16[(int64_t)(start + lane) * p.bst + h]);
                 } else {
                     const i32x4 rb = make_rsrc(p.beta + (int64_t)start * p.bst + h, (uint32_t)len * 4u * (uint32_t)p.bst);
                     b2l_dword(rb, s_b, (uint32_t)lane * 4u * (uint32_t)p.bst);
@@ -726,7 +734,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 // update row start + lane, from row 0 of token tb
                 const uint32_t bo = upd_off(phase + lane, p.nh, p.inv_nh, (int)p.bst, (int)p.bstu);
                 if (p.beta16) {
-                    if (lane < len) blogit = bf2f(p.beta16[(int64_t)tb * p.bst + bo + h]);
+                    if (lane < len) pre.blogit = bf2f(p.beta16[(int64_t)tb * p.bst + bo + h]);
                 } else {
                     const uint32_t nrec = __builtin_amdgcn_readfirstlane(
                         4u * (upd_off(phase + len - 1, p.nh, p.inv_nh, (int)p.bst, (int)p.bstu) + 1));
@@ -735,6 +743,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 }
             }
         }
+    };
+    if ((int)blockIdx.x < items) {
+        const Item first = item_info(blockIdx.x);
+        issue_k(first);
+        issue_qgb(first);
+    }
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const Item item = item_info(it);
+        const int ci = item.ci, h = item.h, hk = item.hk, start = item.start, len = item.len;
+        const int64_t ch_h = (int64_t)ci * p.HV + h;
+        // The lane index for the lane masks of this item (the scan, the diagonal of G and
+        // the causal masks of A, P^T and T) goes through an empty asm, so that the compiler
+        // forms those masks where they are used instead of hoisting all of them out of the
+        // item loop, where they do not fit in the scalar registers and are spilled.
+        int lm = lane;
+        asm volatile("" : "+v"(lm));
+        const int cm = lm & 31, hm = lm >> 5;
+
+        // ---- 1: q, g, beta (and k) were issued one item ahead
+        const int tb = GDP ? __builtin_amdgcn_readfirstlane(start / p.nh) : start;
+        const int phase = start - tb * p.nh;
+        const float blogit = pre.blogit, graw = pre.graw;
+        const bool gfirst = pre.gfirst;
         vm_wait<0>();
         lds_barrier();
 
@@ -890,7 +921,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
             for (int js = 0; js < 2; ++js) {
                 const int f = (pn == 0 ? 0 : 2) + 2 * pm + js;
-                w.PF[(ch_h * 6 + f) * 64 + lane] = __builtin_bit_cast(uint4, pack32(pv, js));
+                st_op<NT>(reinterpret_cast<u32x4 *>(&w.PF[(ch_h * 6 + f) * 64 + lane]), __builtin_bit_cast(u32x4, pack32(pv, js)));
             }
         }
         lds_barrier();
@@ -1018,7 +1049,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                         for (int js = 0; js < 2; ++js) {
                             const int kg = 2 * nb + js, kh = kg / NKS, kk = kg % NKS;
-                            w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane] = neg_bf16(pack32(acc, js));
+                            st_op<NT>(reinterpret_cast<u32x4 *>(&w.WF[(ch_h * (K / 8) + (kh * 2 + m) * NKS + kk) * 64 + lane]),
+                                  __builtin_bit_cast(u32x4, neg_bf16(pack32(acc, js))));
                         }
                     }
                     if (BW) {
@@ -1036,9 +1068,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             }
             // every wave is done with sK: the next item's k rows go there now
             lds_barrier();
-            if (it + (int)gridDim.x < items) issue_k(item_info(it + gridDim.x));
+            const bool more = it + (int)gridDim.x < items;
+            const Item nxt = item_info(more ? it + gridDim.x : it);
+            if (more) issue_k(nxt);
             if (!WANT_V) {
-                lds_barrier();
+                if (more) issue_qgb(nxt);   // sX and the scalars are done with too
                 continue;
             }
             bf16x8 th[4], tl[4];
@@ -1053,8 +1087,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                     tl[s][e] = f2bf(o[e] - bf2f(hi));
                 }
             }
+            constexpr int NU = (2 * (V / 32)) / 4;
 #pragma unroll
-            for (int i = 0; i < (2 * (V / 32)) / 4; ++i) {
+            for (int i = 0; i < NU; ++i) {
                 const int ct = 2 * i + (wave >> 1);
                 f32x16 acc = {};
 #pragma unroll
@@ -1063,14 +1098,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                     acc = mfma32(th[s], vb, acc);
                     acc = mfma32(tl[s], vb, acc);
                 }
+                if (i == NU - 1) {
+                    // every wave is done with sX (v) and the scalars: the next item's q, g
+                    // and beta go there now, under this item's last stores
+                    lds_barrier();
+                    if (more) issue_qgb(nxt);
+                }
                 const int sh = f16_tile_shift(acc);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    w.UH[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane] = f16_pack4(acc, j, sh);
+                    st_op<NT>(reinterpret_cast<u32x2 *>(&w.UH[(((ch_h * (V / 32) + ct) * 2 + m) * 4 + j) * 64 + lane]),
+                          __builtin_bit_cast(u32x2, f16_pack4(acc, j, sh)));
                 if (lane == 0) w.SC[ch_h * kScalars + 128 + 2 * ct + m] = __int_as_float(sh);
             }
         }
-        lds_barrier();   // the next item's loads overwrite sK, sX and the scalars
     }
 }
 
@@ -1295,6 +1336,27 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
     }
 }
 
+// Workgroup b of a chunk pass -> (sequence, value head, 32-column tile).  Blocks go in
+// groups of 8 (sequence, q/k head) units x G value heads x NT tiles: consecutive blocks go
+// to different XCDs, and the G NT workgroups of one (sequence, q/k head), which read the
+// same k and q rows (and, per value head, the same -W), to the same XCD, where they are
+// dispatched together and share its L2.  Units start longest sequence first.
+struct UnitOfBlock {
+    int n, h, tile;
+};
+__device__ __forceinline__ UnitOfBlock unit_of_block(const Prob &p, const Ws &w, int b, int NT)
+{
+    const int G = p.HV / p.HK, per = G * NT, UK = p.N * p.HK;
+    const int grp = b / (8 * per), rem = b % (8 * per);
+    const int ug = min(8, UK - 8 * grp);
+    const int uk = 8 * grp + rem % ug, inner = rem / ug;
+    UnitOfBlock r;
+    r.tile = inner % NT;
+    r.n = w.order[uk / p.HK];
+    r.h = (uk % p.HK) * G + inner / NT;
+    return r;
+}
+
 template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false>
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
@@ -1311,16 +1373,8 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     lds_u32x4 *const xX = (lds_u32x4 *)sX, *const xS = (lds_u32x4 *)sS, *const xU = (lds_u32x4 *)sU;
 
     if (w.hdr[0] != LA_DEVICE_OK) return;
-    const int U = p.N * p.HV;
-    // blocks of 8 units x NT tiles; consecutive blocks go to different XCDs, and
-    // the NT tiles of one unit (which read the same W, k and q) to the same one
-    const int b = blockIdx.x;
-    const int grp = b / (8 * C::NT), rem = b % (8 * C::NT);
-    const int ug = min(8, U - 8 * grp);
-    const int tile = rem / ug;
-    const int u = 8 * grp + rem % ug;
-    const int n = w.order[u / p.HV];
-    const int h = u % p.HV;
+    const UnitOfBlock ub = unit_of_block(p, w, blockIdx.x, C::NT);
+    const int n = ub.n, h = ub.h, tile = ub.tile;
     const int4 si = w.seq_info[n];
 
     InterCtx<K, V, SUMMARY> x;
@@ -1733,6 +1787,8 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
         before(LA_KERNEL_INTRA);
         if (p.nh > 1)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<K, V, !SUMMARY, true>), dim3(grid), dim3(256), 0, s, p, w);
+        else if (p.stream_ops)
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<K, V, !SUMMARY, false, 0, true>), dim3(grid), dim3(256), 0, s, p, w);
         else
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<K, V, !SUMMARY, false>), dim3(grid), dim3(256), 0, s, p, w);
         after(LA_KERNEL_INTRA);
@@ -1796,15 +1852,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lds_u32x4 *const xZ = (lds_u32x4 *)sZ;
 
     if (w.hdr[0] != LA_DEVICE_OK) return;        // malformed cu_seqlens: write nothing
-    const int U = p.N * p.HV;
-    // blocks of 8 units x NT tiles, the tiles of one unit on one XCD (as the forward)
-    const int bi = blockIdx.x;
-    const int grp = bi / (8 * NT), rem = bi % (8 * NT);
-    const int ug = min(8, U - 8 * grp);
-    const int tile = rem / ug;
-    const int u = 8 * grp + rem % ug;
-    const int n = w.order[u / p.HV];
-    const int h = u % p.HV;
+    const UnitOfBlock ub = unit_of_block(p, w, blockIdx.x, NT);   // as the forward
+    const int n = ub.n, h = ub.h, tile = ub.tile;
     const int hk = h / (p.HV / p.HK);
     const int4 si = w.seq_info[n];
     const int seq_start = si.x, seq_len = si.y, cid0 = si.z;
