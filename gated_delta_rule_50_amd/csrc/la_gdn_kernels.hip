@@ -2071,12 +2071,49 @@ __device__ __forceinline__ int swz_e(int row, int col)
     return swz<PPR>(row, col & ~3) + 2 * (col & 3);
 }
 
-// Sum over the 32 lanes that share lane >> 5 (one row of an accumulator tile).
-__device__ __forceinline__ float sum32(float x)
+// Lane exchanges within each group of 32 lanes: partner lane c ^ 16 (swizzle, bit mode
+// and 0x1f, xor 0x10), c ^ 15 (row mirror), c ^ 7 (half-row mirror), c ^ 2 and c ^ 1 (quad
+// permutations).
+__device__ __forceinline__ float xch16(float x)
 {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
+}
+__device__ __forceinline__ float xch15(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xch7(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xch2(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xch1(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, true));
+}
+
+// Row sums of an accumulator tile: register e of every lane summed over the 32 lanes that
+// share lane >> 5 (the 32 columns of the tile's row 8 (e >> 2) + 4 hh + (e & 3)), for all 16
+// registers at once.  Each step exchanges half of the remaining values with a partner lane
+// that differs in the next lane bit (masks 16, 15, 7, 2, 1: independent, so the partial sums
+// cover all 32 lanes) and keeps the half that bit selects; lane c ends with the sum of
+// register c >> 1 (the same bits in lanes c and c ^ 1).  16 exchanges instead of 80.
+__device__ __forceinline__ float rowsum32(const float (&v)[16], int lane)
+{
+    const int c = lane & 31;
+    const bool b4 = c & 16, b3 = c & 8, b2 = c & 4, b1 = c & 2;
+    float a[8], b[4], d[2];
 #pragma unroll
-    for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    for (int i = 0; i < 8; ++i) a[i] = (b4 ? v[i + 8] : v[i]) + xch16(b4 ? v[i] : v[i + 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (b3 ? a[i + 4] : a[i]) + xch15(b3 ? a[i] : a[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d[i] = (b2 ? b[i + 2] : b[i]) + xch7(b2 ? b[i] : b[i + 2]);
+    const float e = (b1 ? d[1] : d[0]) + xch2(b1 ? d[0] : d[1]);
+    return e + xch1(e);
 }
 
 // A 32 x 32 accumulator tile (rows r0 + 8 j + 4 hh + i in register 4 j + i, column c0 + lane % 32)
@@ -2096,37 +2133,43 @@ __device__ __forceinline__ float lds_elem(const lds_char *tile, int row, int col
     return bf2f(*reinterpret_cast<const lds_bf16 *>(tile + swz_e<PPR>(row, col)));
 }
 
-// fp32 rows (ROWS x COLS, row-major) into a swizzled bf16 tile (COLS / 8 pieces per row), by
-// the 256 threads of the block in batches of 8 float4 loads per thread, all issued before
-// any is used; with `src2`, a second matrix of the same shape into `dst2` alongside, and the
-// thread's share of sum(src * src2) returned.
-template <int ROWS, int COLS>
-__device__ __forceinline__ float load_f32_tile(lds_char *dst, const float *src, int tid, lds_char *dst2 = nullptr,
-                                               const float *src2 = nullptr)
+// The backward intra pass's fp32 operands from the workspace into swizzled bf16 tiles: S0 and
+// dS (K x V, row-major) and dU (64 x V), by the 256 threads of the block with every float4
+// load issued before the first is used (one memory latency instead of one per batch).
+// Returns the thread's share of sum(S0 * dS).
+template <int K, int V>
+__device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, lds_char *dDS, const float *DS,
+                                              lds_char *dDU, const float *DU, int tid)
 {
-    constexpr int PPR = COLS / 8, N4 = ROWS * COLS / 4 / 256, B = N4 < 8 ? N4 : 8;
-    static_assert(N4 % B == 0, "whole batches");
+    constexpr int PPR = V / 8, N1 = K * V / 4 / 256, N2 = 64 * V / 4 / 256;
+    float4 a[N1], c[N1], u[N2];
+#pragma unroll
+    for (int j = 0; j < N1; ++j) {
+        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
+        a[j] = *reinterpret_cast<const float4 *>(S0 + (int64_t)row * V + c4);
+        c[j] = *reinterpret_cast<const float4 *>(DS + (int64_t)row * V + c4);
+    }
+#pragma unroll
+    for (int j = 0; j < N2; ++j) {
+        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
+        u[j] = *reinterpret_cast<const float4 *>(DU + (int64_t)row * V + c4);
+    }
+    auto put = [&](lds_char *dst, int row, int c4, const float4 &x) {
+        const bf16x4 v4 = {f2bf(x.x), f2bf(x.y), f2bf(x.z), f2bf(x.w)};
+        *reinterpret_cast<lds_bf16x4 *>(dst + swz<PPR>(row, c4)) = v4;
+    };
     float dot = 0.f;
 #pragma unroll
-    for (int b0 = 0; b0 < N4; b0 += B) {
-        float4 a[B], c[B];
+    for (int j = 0; j < N1; ++j) {
+        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
+        put(dS0, row, c4, a[j]);
+        put(dDS, row, c4, c[j]);
+        dot += a[j].x * c[j].x + a[j].y * c[j].y + a[j].z * c[j].z + a[j].w * c[j].w;
+    }
 #pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int idx = tid + 256 * (b0 + j), row = idx / (COLS / 4), c4 = 4 * (idx % (COLS / 4));
-            a[j] = *reinterpret_cast<const float4 *>(src + (int64_t)row * COLS + c4);
-            if (src2) c[j] = *reinterpret_cast<const float4 *>(src2 + (int64_t)row * COLS + c4);
-        }
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int idx = tid + 256 * (b0 + j), row = idx / (COLS / 4), c4 = 4 * (idx % (COLS / 4));
-            bf16x4 va = {f2bf(a[j].x), f2bf(a[j].y), f2bf(a[j].z), f2bf(a[j].w)};
-            *reinterpret_cast<lds_bf16x4 *>(dst + swz<PPR>(row, c4)) = va;
-            if (src2) {
-                bf16x4 vc = {f2bf(c[j].x), f2bf(c[j].y), f2bf(c[j].z), f2bf(c[j].w)};
-                *reinterpret_cast<lds_bf16x4 *>(dst2 + swz<PPR>(row, c4)) = vc;
-                dot += a[j].x * c[j].x + a[j].y * c[j].y + a[j].z * c[j].z + a[j].w * c[j].w;
-            }
-        }
+    for (int j = 0; j < N2; ++j) {
+        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
+        put(dDU, row, c4, u[j]);
     }
     return dot;
 }
@@ -2148,7 +2191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __attribute__((aligned(16))) char smem[oEnd];
     __shared__ __attribute__((aligned(16))) float ssc[6 * 64];   // gam2, r_k, r_q, beta, 2^gam, 2^(gam_n - gam)
     __shared__ float part[NPART][2][64];
-    __shared__ float sdot[4], sdg[64];
+    __shared__ float sdot[4];
     lds_char *const L = (lds_char *)smem;
     const lds_u32x4 *const tK = (const lds_u32x4 *)(L + oK);
     const lds_u32x4 *const tDO = (const lds_u32x4 *)(L + oDO);
@@ -2206,8 +2249,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         s_eg[tid] = exp2_hw(gam);
         s_dd[tid] = exp2_hw(tid < len ? gn - gam : kNegInf);
     }
-    float dot = load_f32_tile<K, V>(L + oS0, w.CK + chh * K * V, tid, L + oDS, w.DSN + chh * K * V);
-    load_f32_tile<64, V>(L + oDU, w.DU + chh * 64 * V, tid);
+    float dot = load_stage_a<K, V>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, L + oDU,
+                                   w.DU + chh * 64 * V, tid);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (lane == 0) sdot[wave] = dot;
@@ -2276,11 +2319,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             dK[i] = a;
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float r = sum32(prod[e]);
-            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (c == 0) part[KX][half][row] = r * s_rk[row];
+        {
+            const float r = rowsum32(prod, lane);
+            const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if ((c & 1) == 0) part[KX][half][row] = r * s_rk[row];
         }
     }
     // ---- A5, B1: dT's first term dW (diag(f r_k) K)^T and dP = dO U^T, tile (tm, half)
@@ -2313,11 +2355,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 prod[e] += dQ[i][e] * lds_elem<PK>(L + oQ, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float r = sum32(prod[e]);
-            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (c == 0) part[QX][half][row] = r * p.scale * s_rq[row];
+        {
+            const float r = rowsum32(prod, lane);
+            const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if ((c & 1) == 0) part[QX][half][row] = r * p.scale * s_rq[row];
         }
     }
     // ---- B2: P = M o (q^ k^T) for tile (tm, half); dP o P sums; R = M o dP r_k,s and R2 = M o dP scale r_q,t
@@ -2329,7 +2370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int sI = 32 * half + c;
         const float gs = s_gam[sI], rs = s_rk[sI];
         f32x16 R, R2;
-        float colsum = 0.f;
+        float colsum = 0.f, ppv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int t = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
@@ -2337,10 +2378,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const float pv = p.scale * s_rq[t] * rs * m * qk[e];
             const float pp = dP[e] * pv;
             colsum += pp;
-            const float rsum = sum32(pp);
-            if (c == 0) part[PPR_][half][t] = rsum;
+            ppv[e] = pp;
             R[e] = m * dP[e] * rs;
             R2[e] = m * dP[e] * p.scale * s_rq[t];
+        }
+        {
+            const float r = rowsum32(ppv, lane);
+            const int e = c >> 1;
+            if ((c & 1) == 0) part[PPR_][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
         }
         colsum += __shfl_xor(colsum, 32, 64);
         if (hh == 0) part[PPC][tm][sI] = colsum;
@@ -2375,10 +2420,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (row < len) dv_out[((int64_t)(start + row) * p.HV + h) * V + 32 * vt + c] = s_b[row] * a[e];
             }
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float r = sum32(prod[e]);
-            if (c == 0) part[XV][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+        {
+            const float r = rowsum32(prod, lane);
+            const int e = c >> 1;
+            if ((c & 1) == 0) part[XV][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
         }
     }
     // ---- B5: X1 = T^T dW: dk^ += diag(f) X1 and df = r_k rowdot(X1, k)
@@ -2398,11 +2443,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 dK[i][e] += s_b[row] * s_eg[row] * a[e];
             }
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float r = sum32(prod[e]);
-            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (c == 0) part[DF][half][row] = r * s_rk[row];
+        {
+            const float r = rowsum32(prod, lane);
+            const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if ((c & 1) == 0) part[DF][half][row] = r * s_rk[row];
         }
     }
     lds_barrier();                                            // R, R2 and dT published
@@ -2439,7 +2483,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int b = 32 * half + c;
         const float gb = s_gam[b], rb = s_rk[b];
         f32x16 Z, Z3;
-        float colsum = 0.f;
+        float colsum = 0.f, v1[16], v2[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
@@ -2448,14 +2492,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const float ghat = s_rk[a] * rb * gk[e];
             const float aA = dam * s_b[a] * E * ghat;
             colsum += aA;
-            const float rs1 = sum32(aA), rs2 = sum32(dam * E * ghat);
-            if (c == 0) {
-                part[AAR][half][a] = rs1;
-                part[DAEG][half][a] = rs2;
-            }
+            v1[e] = aA;
+            v2[e] = dam * E * ghat;
             const float dgm = dam * s_b[a] * E;
             Z[e] = dgm * rb;
             Z3[e] = dgm * s_rk[a];
+        }
+        {
+            const float r1 = rowsum32(v1, lane), r2 = rowsum32(v2, lane);
+            const int e = c >> 1, a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if ((c & 1) == 0) {
+                part[AAR][half][a] = r1;
+                part[DAEG][half][a] = r2;
+            }
         }
         colsum += __shfl_xor(colsum, 32, 64);
         if (hh == 0) part[AAC][tm][b] = colsum;
@@ -2499,14 +2548,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) Fs += __shfl_xor(Fs, off, 64);
         if (t == len - 1) dgam += Fs + exp2_hw(s_gam[t]) * (sdot[0] + sdot[1] + sdot[2] + sdot[3]);
-        sdg[t] = t < len ? dgam : 0.f;
         if (t < len) db_out[(int64_t)(start + t) * p.HV + h] = db;
-    }
-    lds_barrier();
-    if (tid < len) {
-        float acc = 0.f;
-        for (int u = len - 1; u >= tid; --u) acc += sdg[u];
-        dg_out[(int64_t)(start + tid) * p.HV + h] = acc;
+        // dg: the reverse cumulative sum of dgam within the chunk (zeros past its end), by a
+        // suffix scan across the wave
+        float acc = t < len ? dgam : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(acc, off, 64);
+            if (t + off < 64) acc += y;
+        }
+        if (t < len) dg_out[(int64_t)(start + t) * p.HV + h] = acc;
     }
 }
 
