@@ -485,7 +485,7 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     L.SB = take(bwd == 2 ? items * la::kScalars * 4 : 0);
     L.CK = take(bwd == 2 ? items * K * V * 4 : 0);
     L.DSN = take(bwd == 2 ? items * K * V * 4 : 0);
-    L.DU = take(bwd == 2 ? items * 64 * V * 4 : 0);
+    L.DU = take(bwd == 2 ? items * 64 * V * 2 : 0);
     L.OB = take(bwd == 2 ? (size_t)T * HV * V * 2 : 0);
     L.DQH = take(bwd == 2 ? (size_t)T * HV * K * 4 : 0);
     L.DKH = take(bwd == 2 ? (size_t)T * HV * K * 4 : 0);
@@ -512,7 +512,7 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.SB = reinterpret_cast<float *>(b + L.SB);
     w.CK = reinterpret_cast<float *>(b + L.CK);
     w.DSN = reinterpret_cast<float *>(b + L.DSN);
-    w.DU = reinterpret_cast<float *>(b + L.DU);
+    w.DU = reinterpret_cast<__bf16 *>(b + L.DU);
     w.OB = reinterpret_cast<__bf16 *>(b + L.OB);
     w.DQH = reinterpret_cast<float *>(b + L.DQH);
     w.DKH = reinterpret_cast<float *>(b + L.DKH);

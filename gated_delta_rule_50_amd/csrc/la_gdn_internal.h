@@ -79,7 +79,7 @@ struct Ws {
     float *SB;         // [chunk, HV, kScalars]  gam (log2) at 0, r_k at 64, r_q at 128, beta at 192
     float *CK;         // [chunk, HV, K, V]  fp32 state at each chunk's start (full backward)
     float *DSN;        // [chunk, HV, K, V]  gradient of each chunk's end state (full backward)
-    float *DU;         // [chunk, HV, 64, V]  gradient of each chunk's U (full backward)
+    __bf16 *DU;        // [chunk, HV, 64, V]  gradient of each chunk's U in bf16, row-major (full backward)
     __bf16 *OB;        // [T, HV, V]  the recomputed forward's output (unused, full backward)
     float *DQH, *DKH;  // [T, HV, K]  per value head: gradients of the scaled, normalised q and k rows
 };

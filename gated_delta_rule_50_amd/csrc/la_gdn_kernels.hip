@@ -2024,9 +2024,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int e = 0; e < 4; ++e) du[4 * j + e] = (Z[o][4 * j + e] + zo[e]) * dj[e] + Gz[o][4 * j + e];
             }
             if (FULL && o == 0) {
-                float *dst = w.DU + (chh * 64 + 32 * m) * V + col;
+                // in bf16, the operand precision the backward's intra pass reads it in
+                __bf16 *dst = w.DU + (chh * 64 + 32 * m) * V + col;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) dst[(int64_t)(8 * (e >> 2) + 4 * hh + (e & 3)) * V] = du[e];
+                for (int e = 0; e < 16; ++e) dst[(int64_t)(8 * (e >> 2) + 4 * hh + (e & 3)) * V] = f2bf(du[e]);
             }
             Ub[2 * m] = pack32(du, 0);
             Ub[2 * m + 1] = pack32(du, 1);
@@ -2133,26 +2134,20 @@ __device__ __forceinline__ float lds_elem(const lds_char *tile, int row, int col
     return bf2f(*reinterpret_cast<const lds_bf16 *>(tile + swz_e<PPR>(row, col)));
 }
 
-// The backward intra pass's fp32 operands from the workspace into swizzled bf16 tiles: S0 and
-// dS (K x V, row-major) and dU (64 x V), by the 256 threads of the block with every float4
-// load issued before the first is used (one memory latency instead of one per batch).
-// Returns the thread's share of sum(S0 * dS).
+// The backward intra pass's fp32 operands S0 and dS (K x V, row-major, in the workspace) into
+// swizzled bf16 tiles, by the 256 threads of the block with every float4 load issued before
+// the first is used (one memory latency instead of one per batch).  Returns the thread's
+// share of sum(S0 * dS).
 template <int K, int V>
-__device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, lds_char *dDS, const float *DS,
-                                              lds_char *dDU, const float *DU, int tid)
+__device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, lds_char *dDS, const float *DS, int tid)
 {
-    constexpr int PPR = V / 8, N1 = K * V / 4 / 256, N2 = 64 * V / 4 / 256;
-    float4 a[N1], c[N1], u[N2];
+    constexpr int PPR = V / 8, N1 = K * V / 4 / 256;
+    float4 a[N1], c[N1];
 #pragma unroll
     for (int j = 0; j < N1; ++j) {
         const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
         a[j] = *reinterpret_cast<const float4 *>(S0 + (int64_t)row * V + c4);
         c[j] = *reinterpret_cast<const float4 *>(DS + (int64_t)row * V + c4);
-    }
-#pragma unroll
-    for (int j = 0; j < N2; ++j) {
-        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
-        u[j] = *reinterpret_cast<const float4 *>(DU + (int64_t)row * V + c4);
     }
     auto put = [&](lds_char *dst, int row, int c4, const float4 &x) {
         const bf16x4 v4 = {f2bf(x.x), f2bf(x.y), f2bf(x.z), f2bf(x.w)};
@@ -2165,11 +2160,6 @@ __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, ld
         put(dS0, row, c4, a[j]);
         put(dDS, row, c4, c[j]);
         dot += a[j].x * c[j].x + a[j].y * c[j].y + a[j].z * c[j].z + a[j].w * c[j].w;
-    }
-#pragma unroll
-    for (int j = 0; j < N2; ++j) {
-        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
-        put(dDU, row, c4, u[j]);
     }
     return dot;
 }
@@ -2234,11 +2224,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     const int64_t chh = (int64_t)ci * p.HV + h;
 
-    // ---- stage A loads: k and dO rows (buffer loads into LDS), the scalars, S0, dS and dU
+    // ---- stage A loads: k, dO and dU rows (buffer loads into LDS), the scalars, S0 and dS
     intra_load_tile<K>((lds_u32x4 *)(L + oK), p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst,
                        len, wave, lane, 4);
     intra_load_tile<V>((lds_u32x4 *)(L + oDO), d_out + (int64_t)start * p.ost + (int64_t)h * p.osh,
                        2u * (uint32_t)p.ost, len, wave, lane, 4);
+    intra_load_tile<V>((lds_u32x4 *)(L + oDU), w.DU + chh * 64 * V, 2u * (uint32_t)V, 64, wave, lane, 4);
+    // A1's register operands (-W fragments, the U~ tiles and their scales), issued with the rest
+    bf16x8 Wf[KS];
+    uint2 uh[NVT / 2][4];
+    int ush[NVT / 2];
+#pragma unroll
+    for (int kg = 0; kg < KS; ++kg)
+        Wf[kg] = __builtin_bit_cast(bf16x8, w.WF[(chh * (K / 8) + ((kg / NKS) * 2 + tm) * NKS + kg % NKS) * 64 + lane]);
+#pragma unroll
+    for (int i = 0; i < NVT / 2; ++i) {
+        const int vt = half + 2 * i;
+        ush[i] = __float_as_int(w.SC[chh * kScalars + 128 + 2 * vt + tm]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) uh[i][j] = w.UH[(((chh * (V / 32) + vt) * 2 + tm) * 4 + j) * 64 + lane];
+    }
     if (tid < 64) {
         const float *sb = w.SB + chh * kScalars;
         const float gam = sb[tid], gn = sb[len - 1];
@@ -2249,8 +2254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         s_eg[tid] = exp2_hw(gam);
         s_dd[tid] = exp2_hw(tid < len ? gn - gam : kNegInf);
     }
-    float dot = load_stage_a<K, V>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, L + oDU,
-                                   w.DU + chh * 64 * V, tid);
+    float dot = load_stage_a<K, V>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (lane == 0) sdot[wave] = dot;
@@ -2259,19 +2263,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- A1: U = U~ + (-W) S0 for tiles (tm, value tile half + 2 i); U~ enters the accumulator
     {
-        bf16x8 Wf[KS];
-#pragma unroll
-        for (int kg = 0; kg < KS; ++kg)
-            Wf[kg] = __builtin_bit_cast(bf16x8, w.WF[(chh * (K / 8) + ((kg / NKS) * 2 + tm) * NKS + kg % NKS) * 64 + lane]);
 #pragma unroll
         for (int i = 0; i < NVT / 2; ++i) {
             const int vt = half + 2 * i;
-            const int sh = __float_as_int(w.SC[chh * kScalars + 128 + 2 * vt + tm]);
             f32x16 acc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint2 h = w.UH[(((chh * (V / 32) + vt) * 2 + tm) * 4 + j) * 64 + lane];
-                const f32x4 u4 = f16_unpack4(__builtin_bit_cast(u32x2, h), sh);
+                const f32x4 u4 = f16_unpack4(__builtin_bit_cast(u32x2, uh[i][j]), ush[i]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[4 * j + e] = u4[e];
             }
