@@ -487,8 +487,11 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     L.DSN = take(bwd == 2 ? items * K * V * 4 : 0);
     L.DU = take(bwd == 2 ? items * 64 * V * 2 : 0);
     L.OB = take(bwd == 2 ? (size_t)T * HV * V * 2 : 0);
-    L.DQH = take(bwd == 2 ? (size_t)T * HV * K * 4 : 0);
-    L.DKH = take(bwd == 2 ? (size_t)T * HV * K * 4 : 0);
+    // per-value-head q and k gradients, summed over each head group afterwards (with one
+    // value head per q/k head the intra pass writes dq and dk itself)
+    const bool qk_sums = bwd == 2 && HV != HK;
+    L.DQH = take(qk_sums ? (size_t)T * HV * K * 4 : 0);
+    L.DKH = take(qk_sums ? (size_t)T * HV * K * 4 : 0);
     L.total = off;
     return L;
 }

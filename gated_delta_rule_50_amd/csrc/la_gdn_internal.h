@@ -82,6 +82,7 @@ struct Ws {
     __bf16 *DU;        // [chunk, HV, 64, V]  gradient of each chunk's U in bf16, row-major (full backward)
     __bf16 *OB;        // [T, HV, V]  the recomputed forward's output (unused, full backward)
     float *DQH, *DKH;  // [T, HV, K]  per value head: gradients of the scaled, normalised q and k rows
+                       // (only with HV > HK: head groups to sum)
 };
 
 // Byte layout of the workspace; offsets are 256-byte aligned.

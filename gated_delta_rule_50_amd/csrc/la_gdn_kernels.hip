@@ -442,12 +442,23 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
 // bytes land at fragment byte 16 l).  Written as asm so that the compiler neither
 // tracks these loads nor adds waits for them: every wait for them is explicit.
 // M0 needs one wait state before the load that uses it.
+// The descriptor and the offsets are wave-uniform by contract; they go through readfirstlane
+// so that the compiler keeps them in scalar registers, as the instruction needs, also where
+// register pressure made it hold them in vector registers.
+__device__ __forceinline__ i32x4 uniform_rsrc(i32x4 r)
+{
+    i32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    return u;
+}
+
 __device__ __forceinline__ void b2l(i32x4 rsrc, lds_u32x4 *buf, int f, uint32_t voff, uint32_t soff)
 {
-    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(buf + f * 64);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(buf + f * 64));
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(dst), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "s"(dst), "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");
 }
 
@@ -496,10 +507,10 @@ __device__ __forceinline__ void vm_wait_n(int n)
 
 __device__ __forceinline__ void b2l_dword(i32x4 rsrc, lds_float *dst, uint32_t voff)
 {
-    const uint32_t d = (uint32_t)reinterpret_cast<uintptr_t>(dst);
+    const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(dst));
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :
-                 : "s"(d), "v"(voff), "s"(rsrc)
+                 : "s"(d), "v"(voff), "s"(uniform_rsrc(rsrc))
                  : "memory", "m0");
 }
 
@@ -2166,7 +2177,7 @@ __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, ld
 
 template <int K, int V>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_intra(
-    Prob p, Ws w, const __bf16 *d_out, float *dv_out, float *dg_out, float *db_out)
+    Prob p, Ws w, const __bf16 *d_out, float *dv_out, float *dg_out, float *db_out, float *dq_out, float *dk_out)
 {
     constexpr int PK = K / 8, PV = V / 8, NKT = K / 32, NVT = V / 32, KS = K / 16, VS = V / 16;
     constexpr int NKS = K / 32;                             // steps of 16 keys per key half (-W fragments)
@@ -2177,7 +2188,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int oS0 = oR1, oDS = oR1 + szS;                            // stage A
     constexpr int oQ = oR1, oVv = oQ + szK, oT = oVv + szV, oR = oT + sz64, oR2 = oR + sz64, oDT = oR2 + sz64;
     constexpr int oY = oQ, oZ = oVv, oZ3 = oR;                           // stage C
-    enum { XV, DF, DAEG, AAR, AAC, PPR_, PPC, QX, KX, NPART };
+    enum { XV, DF, DAEG, AAR, AAC, PPR_, PPC, QX, KX, QD, KD, NPART };
     __shared__ __attribute__((aligned(16))) char smem[oEnd];
     __shared__ __attribute__((aligned(16))) float ssc[6 * 64];   // gam2, r_k, r_q, beta, 2^gam, 2^(gam_n - gam)
     __shared__ float part[NPART][2][64];
@@ -2458,6 +2469,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dK[i] = mfma32(lds_tr32s<8, false>(tR2, 16 * st, 32 * tm, lane), lds_tr32s<PK, false>(tQ, 16 * st, 32 * kt, lane), dK[i]);
         }
     }
+    // one q/k head per value head: the row norms' chain rule is applied here (dq_out set), and
+    // the row dots (q . dq^) it needs are taken while q is still in LDS (dq^ is final)
+    const bool fuse_qk = dq_out != nullptr;
+    __bf16 xq[NKT / 2][16];   // the q elements of this lane's dq^ entries, for the chain rule below
+    if (fuse_qk) {
+        float prod[16] = {};
+#pragma unroll
+        for (int i = 0; i < NKT / 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float x = lds_elem<PK>(L + oQ, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
+                xq[i][e] = f2bf(x);   // x is a bf16 value: exact
+                prod[e] += dQ[i][e] * x;
+            }
+        const float r = rowsum32(prod, lane);
+        const int e = c >> 1;
+        if ((c & 1) == 0) part[QD][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+    }
     // ---- C1: Y = dT T^T, tile (tm, half)
     {
         f32x16 y = {};
@@ -2520,17 +2549,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dK[i] = mfma32(lds_row8<8>(tZ, 32 * tm + c, 16 * st + 8 * hh), kb, dK[i]);
             dK[i] = mfma32(lds_tr32s<8, false>(tZ3, 16 * st, 32 * tm, lane), kb, dK[i]);
         }
+        if (!fuse_qk) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (row < len) {
-                const int64_t at = ((int64_t)(start + row) * p.HV + h) * K + 32 * kt + c;
-                w.DQH[at] = dQ[i][e];
-                w.DKH[at] = dK[i][e];
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                if (row < len) {
+                    const int64_t at = ((int64_t)(start + row) * p.HV + h) * K + 32 * kt + c;
+                    w.DQH[at] = dQ[i][e];
+                    w.DKH[at] = dK[i][e];
+                }
             }
         }
     }
+    if (fuse_qk) {
+        float prod[16] = {};
+#pragma unroll
+        for (int i = 0; i < NKT / 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                prod[e] += dK[i][e] * lds_elem<PK>(L + oK, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
+        const float r = rowsum32(prod, lane);
+        const int e = c >> 1;
+        if ((c & 1) == 0) part[KD][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+    }
     lds_barrier();                                            // every partial sum written
+    if (fuse_qk) {
+        // dx = r dx^ - r^3 (x . dx^) x (times scale for q; r = 1 without the norm): q from the
+        // registers taken above, k rows from LDS
+        float rq[16], rk[16], cq[16], ck[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+            rq[e] = s_rq[row];
+            rk[e] = s_rk[row];
+            cq[e] = p.l2norm ? rq[e] * rq[e] * rq[e] * (part[QD][0][row] + part[QD][1][row]) : 0.f;
+            ck[e] = p.l2norm ? rk[e] * rk[e] * rk[e] * (part[KD][0][row] + part[KD][1][row]) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NKT / 2; ++i) {
+            const int col = 32 * (half + 2 * i) + c;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                if (row < len) {
+                    const float xk = lds_elem<PK>(L + oK, row, col);
+                    const int64_t at = ((int64_t)(start + row) * p.HK + hk) * K + col;
+                    dq_out[at] = p.scale * (rq[e] * dQ[i][e] - cq[e] * bf2f(xq[i][e]));
+                    dk_out[at] = rk[e] * dK[i][e] - ck[e] * xk;
+                }
+            }
+        }
+    }
     // ---- per token: dbeta and dgam, then dg by the reverse cumulative sum within the chunk
     if (tid < 64) {
         const int t = tid;
@@ -2642,6 +2711,8 @@ hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_
     const int grid = (int)(items < p.intra_grid ? items : p.intra_grid);
     const unsigned inter_blocks = (unsigned)((int64_t)p.N * p.HV * (p.V / 32));
     const unsigned qk_blocks = (unsigned)((p.T * p.HK + 256 / (p.K / 8) - 1) / (256 / (p.K / 8)));
+    // one value head per q/k head: no head-group sums, the intra pass writes dq and dk itself
+    const bool fuse_qk = p.HV == p.HK;
     // the forward again, with the state at every chunk start (fp32, indexed by chunk id)
     Prob pf = p;
     pf.ck_every = kChunk;
@@ -2666,8 +2737,8 @@ hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_
         before(LA_KERNEL_BWD_INTRA);                                                                           \
         if (items > 0)                                                                                         \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV>), dim3((unsigned)items), dim3(256), 0, s, p, w, \
-                               a.d_out, a.dv, a.dg, a.dbeta);                                                  \
-        if (qk_blocks > 0)                                                                                     \
+                               a.d_out, a.dv, a.dg, a.dbeta, fuse_qk ? a.dq : nullptr, fuse_qk ? a.dk : nullptr); \
+        if (!fuse_qk && qk_blocks > 0)                                                                         \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_qk<KK>), dim3(qk_blocks), dim3(256), 0, s, p, w, a.dq, a.dk); \
         after(LA_KERNEL_BWD_INTRA);                                                                            \
         return hipGetLastError();                                                                              \

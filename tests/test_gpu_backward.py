@@ -86,8 +86,10 @@ def test_backward_varlen_workload():
     check_bwd(make_problem(2), 205)
 
 
-def test_backward_no_l2norm_custom_scale_no_final_gradient():
-    p = custom_problem((70, 130), hk=1, hv=2, dk=64, dv=64, seed=206, l2norm=False, with_state=True)
+@pytest.mark.parametrize("hk,hv", [(1, 2), (2, 2)])
+def test_backward_no_l2norm_custom_scale_no_final_gradient(hk, hv):
+    # hk = hv: one value head per q/k head, where the intra pass applies the q/k chain itself
+    p = custom_problem((70, 130), hk=hk, hv=hv, dk=64, dv=64, seed=206, l2norm=False, with_state=True)
     p = dataclasses.replace(p, k=(p.k.float() / 8).to(torch.bfloat16), q=(p.q.float() / 8).to(torch.bfloat16))
     check_bwd(p, 207, scale=0.3, with_final=False)
 
@@ -99,6 +101,12 @@ def test_backward_zero_initial_state_and_empty_sequences():
     # an empty sequence passes the final-state gradient through to the initial state
     for n in (0, 2, 4):
         assert torch.equal(got["d_init"][n].cpu(), d_fin[n])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_backward_one_value_head_per_qk_head(dk, dv):
+    # G = 1 with ragged lengths and an initial state: dq and dk come straight from the intra pass
+    check_bwd(custom_problem((1, 63, 64, 65, 130, 200), hk=3, hv=3, dk=dk, dv=dv, seed=217, with_state=True), 218)
 
 
 def test_backward_many_sequences():
