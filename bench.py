@@ -56,6 +56,8 @@ VARIANTS = {
                    "end-state gradients in, start-state gradient out)",
     "bwd": "the full backward (la_gdn_bwd: output and final-state gradients in; dq, dk, dv, dg, dbeta and "
            "the initial-state gradient out, fp32)",
+    "bwd-series": "the full backward given the forward's fp32 state series every 64 tokens (la_gdn_bwd_ex: "
+                  "the forward's state pass is not run again; the series is counted as read)",
 }
 
 
@@ -223,7 +225,7 @@ def main(argv=None):
     elif variant != "plain" and summary:
         print("--variant applies to the forward workloads (1 to 4)", file=sys.stderr)
         return 2
-    if variant == "bwd" and wl == 4:
+    if variant.startswith("bwd") and wl == 4:
         print("--variant bwd runs on the workloads 1, 2 and 3", file=sys.stderr)
         return 2
     lengths = prob.lengths()
@@ -256,7 +258,7 @@ def main(argv=None):
     copies = max(1, args.copies) if by0 < (1 << 30) else 1
     sets = []
     bwd_in = None
-    if variant == "bwd":
+    if variant.startswith("bwd"):
         gen = torch.Generator(device="cuda").manual_seed(wl)
         bwd_in = (torch.randn((T, HV, V), generator=gen, device=dev).to(torch.bfloat16),
                   torch.randn((N, HV, K, V), generator=gen, device=dev))
@@ -274,13 +276,18 @@ def main(argv=None):
             out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=dev)
             desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=out, num_householder=nh)
         fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev)
-        if variant == "bwd":
+        if variant.startswith("bwd"):
             desc = la.make_desc(g.k, g.v, g.g, g.beta, N, q=g.q, out=bwd_in[0])
             ws = torch.empty(la.la_gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
             grads = {"dq": torch.empty((T, HK, K), device=dev), "dk": torch.empty((T, HK, K), device=dev),
                      "dv": torch.empty((T, HV, V), device=dev), "dg": torch.empty((T, HV), device=dev),
                      "dbeta": torch.empty((T, HV), device=dev), "d_initial_state": fin}
-            sets.append((g, grads, fin, ws, None))
+            series = None
+            if variant == "bwd-series":
+                # the forward's state series, made once before the timed region
+                _, _, series = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                                checkpoint_every_n_tokens=64, checkpoint_dtype=torch.float32)
+            sets.append((g, grads, fin, ws, series))
             continue
         ws = torch.empty(la.la_gdn_workspace_bytes_ex(desc, summary, nh), dtype=torch.uint8, device=dev)
         ck = torch.empty((n_ck, HV, K, V), dtype=ck_dtype, device=dev) if every else None
@@ -289,9 +296,9 @@ def main(argv=None):
 
     def step(i):
         g, out, fin, ws, ck = sets[i % len(sets)]
-        if variant == "bwd":
+        if variant.startswith("bwd"):
             la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, bwd_in[0], initial_state=g.state,
-                          d_final_state=bwd_in[1], workspace=ws, stream=stream, out=out)
+                          d_final_state=bwd_in[1], workspace=ws, stream=stream, out=out, chunk_states=ck)
         elif variant == "summary-bwd":
             la.la_gdn_summary_bwd(g.q, g.k, g.g, g.beta, g.cu_seqlens, bwd_in[0], bwd_in[1], d_start_state=fin,
                                   workspace=ws, stream=stream)
@@ -368,8 +375,10 @@ def main(argv=None):
         # chunk pass (2 (3 K V + C V))
         by = T * (2 * HK * K * 2 + HV * V * 2 + 2 * HV * 4) + 2 * N * HV * K * V * 4
         fl = T * (HK * 2 * 2 * CHUNK * K + HV * (2 * CHUNK * K + 2 * (3 * K * V + CHUNK * V)))
-    elif variant == "bwd":
+    elif variant.startswith("bwd"):
         by, fl = backward_counts(lengths, HK, HV, K, V, with_init)
+        if variant == "bwd-series":
+            by += la.checkpoint_entries(prob.cu_seqlens, 64) * HV * K * V * 4
     # Roofline of the call: the path's algorithmic bytes (or flops) over the GPU time of
     # all the kernels one call launches, each timed with HIP events on the launch
     # stream (their sum is what rocprofv3 reports for the same kernels).  The span

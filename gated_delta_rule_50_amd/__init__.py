@@ -48,7 +48,7 @@ LA_KERNEL_COUNT = 4
 # Every symbol include/la_gdn.h declares.
 EXPORTED_SYMBOLS = (
     "la_gdn_workspace_bytes", "la_gdn_fwd", "la_gdn_summary", "la_gdn_fwd_ex", "la_gdn_summary_ex", "la_gdn_workspace_bytes_ex",
-    "la_gdn_summary_bwd", "la_gdn_bwd_workspace_bytes", "la_gdn_bwd", "la_gdn_fwd_noalloc", "la_gdn_device_status",
+    "la_gdn_summary_bwd", "la_gdn_bwd_workspace_bytes", "la_gdn_bwd", "la_gdn_bwd_ex", "la_gdn_fwd_noalloc", "la_gdn_device_status",
     "la_last_error_message", "la_gdn_profile_enable", "la_gdn_profile_read", "la_gdn_kernel_name",
 )
 
@@ -128,6 +128,8 @@ def load_library(path: str = LIB_PATH):
     lib.la_gdn_bwd_workspace_bytes.argtypes = [dp]
     lib.la_gdn_bwd.restype = ctypes.c_int
     lib.la_gdn_bwd.argtypes = [dp] + [vp] * 15 + [ctypes.c_int, vp, sz, vp]
+    lib.la_gdn_bwd_ex.restype = ctypes.c_int
+    lib.la_gdn_bwd_ex.argtypes = [dp] + [vp] * 16 + [ctypes.c_int, vp, sz, vp]
     lib.la_gdn_fwd_noalloc.restype = ctypes.c_int
     lib.la_gdn_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.la_gdn_device_status.restype = i32
@@ -429,11 +431,13 @@ def la_gdn_bwd_workspace_bytes(desc: Desc) -> int:
 
 def la_gdn_bwd(q, k, v, g, beta, cu_seqlens, d_out, initial_state=None, d_final_state=None,
                l2norm: bool = True, scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-               stream=None, out: Optional[dict] = None) -> dict:
+               stream=None, out: Optional[dict] = None, chunk_states: Optional[torch.Tensor] = None) -> dict:
     """Gradients of la_gdn_fwd for the upstream gradients d_out [T, HV, V] (bf16) and
     d_final_state [N, HV, K, V] (fp32, None: zeros).  Returns a dict of fp32 tensors dq, dk
     [T, HK, K], dv [T, HV, V], dg, dbeta [T, HV] and d_initial_state [N, HV, K, V] (`out`
-    may hold preallocated ones)."""
+    may hold preallocated ones).  chunk_states: the forward's fp32 state series every 64
+    tokens (la_gdn_fwd_ex with checkpoint_every_n_tokens=64, checkpoint_dtype fp32), which
+    spares the forward's state pass (la_gdn_bwd_ex)."""
     lib = load_library()
     if d_out.dtype != torch.bfloat16 or cu_seqlens.dtype != torch.int32 or beta.dtype != torch.float32:
         raise ValueError("d_out must be bf16, cu_seqlens int32 and beta fp32")
@@ -453,10 +457,21 @@ def la_gdn_bwd(q, k, v, g, beta, cu_seqlens, d_out, initial_state=None, d_final_
     desc = make_desc(k, v, g, beta, N, q=q, out=d_out, scale=scale)
     if workspace is None:
         workspace = torch.empty(la_gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    _check(lib.la_gdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                          _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(res["dq"]), _ptr(res["dk"]),
-                          _ptr(res["dv"]), _ptr(res["dg"]), _ptr(res["dbeta"]), _ptr(res["d_initial_state"]),
-                          int(bool(l2norm)), _ptr(workspace), workspace.numel(), _stream(stream)))
+    grads = (_ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dg"]), _ptr(res["dbeta"]),
+             _ptr(res["d_initial_state"]))
+    if chunk_states is None:
+        _check(lib.la_gdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                              _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), *grads, int(bool(l2norm)),
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        C = checkpoint_entries(cu_seqlens, 64)
+        if (chunk_states.dtype != torch.float32 or tuple(chunk_states.shape) != (C, HV, K, V)
+                or not chunk_states.is_contiguous()):
+            raise ValueError(f"chunk_states must be a contiguous fp32 tensor of shape {(C, HV, K, V)}")
+        _check(lib.la_gdn_bwd_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(cu_seqlens), _ptr(initial_state), _ptr(chunk_states), _ptr(d_out),
+                                 _ptr(d_final_state), *grads, int(bool(l2norm)), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
     return res
 
 

@@ -692,11 +692,11 @@ size_t la_gdn_bwd_workspace_bytes(const la_gdn_desc *desc)
         .total;
 }
 
-la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
-                     const float *d_final_state, float *dq, float *dk, float *dv, float *dg, float *dbeta,
-                     float *d_initial_state, int l2norm, void *workspace, size_t workspace_bytes,
-                     hipStream_t stream)
+static la_status bwd_impl(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const int32_t *cu_seqlens, const float *initial_state,
+                          const float *chunk_states, const void *d_out, const float *d_final_state, float *dq,
+                          float *dk, float *dv, float *dg, float *dbeta, float *d_initial_state, int l2norm,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     g_error.clear();
     la_status st = check_desc(desc);
@@ -721,6 +721,8 @@ la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, cons
     if ((st = check_f32("dg", dg, true)) != LA_OK) return st;
     if ((st = check_f32("dbeta", dbeta, true)) != LA_OK) return st;
     if ((st = check_f32("d_initial_state", d_initial_state, true)) != LA_OK) return st;
+    if (chunk_states && !aligned16(chunk_states))
+        return fail(LA_ERR_INVALID_ARGUMENT, "chunk_states must be 16-byte aligned (it is read with 128-bit loads)");
 
     la::Prob p = make_prob(desc, l2norm);
     p.q = static_cast<const __bf16 *>(q);
@@ -752,9 +754,30 @@ la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, cons
     a.dg = dg;
     a.dbeta = dbeta;
     a.d_init = d_initial_state;
+    a.chunk_states = chunk_states;
     const hipError_t e = la::run_backward(p, w, a, stream, current_hook());
     if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return LA_OK;
+}
+
+la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const float *initial_state, const void *d_out,
+                     const float *d_final_state, float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                     float *d_initial_state, int l2norm, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream)
+{
+    return bwd_impl(desc, q, k, v, g, beta, cu_seqlens, initial_state, nullptr, d_out, d_final_state, dq, dk, dv, dg,
+                    dbeta, d_initial_state, l2norm, workspace, workspace_bytes, stream);
+}
+
+la_status la_gdn_bwd_ex(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const int32_t *cu_seqlens, const float *initial_state,
+                        const float *chunk_states, const void *d_out, const float *d_final_state, float *dq,
+                        float *dk, float *dv, float *dg, float *dbeta, float *d_initial_state, int l2norm,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return bwd_impl(desc, q, k, v, g, beta, cu_seqlens, initial_state, chunk_states, d_out, d_final_state, dq, dk,
+                    dv, dg, dbeta, d_initial_state, l2norm, workspace, workspace_bytes, stream);
 }
 
 int32_t la_gdn_device_status(const void *workspace, hipStream_t stream)

@@ -121,6 +121,7 @@ struct BwdArgs {
     const __bf16 *d_out;
     const float *d_final;             // or null (zeros)
     float *dq, *dk, *dv, *dg, *dbeta, *d_init;
+    const float *chunk_states;        // the fp32 state at every chunk start, or null (run the forward again)
 };
 hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_t stream, const LaunchHook *hook);
 

@@ -2697,8 +2697,12 @@ __global__ __launch_bounds__(256) void k_bwd_qk(Prob p, const Ws w, float *dq, f
     dk4[1] = make_float4(ok[4], ok[5], ok[6], ok[7]);
 }
 
-hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_t s, const LaunchHook *hook)
+hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStream_t s, const LaunchHook *hook)
 {
+    // the chunk-start states: the caller's (the forward's fp32 series every 64 tokens, the
+    // same rows the forward run again would write), or the workspace's
+    Ws w = w_in;
+    if (a.chunk_states) w.CK = const_cast<float *>(a.chunk_states);
     auto before = [&](int id) { if (hook) hook->before(id, s, hook->ctx); };
     auto after = [&](int id) { if (hook) hook->after(id, s, hook->ctx); };
     if (p.N == 0) return hipSuccess;
@@ -2730,7 +2734,8 @@ hipError_t run_backward(const Prob &p, const Ws &w, const BwdArgs &a, hipStream_
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<KK, VV, true, false, 2>), dim3(grid), dim3(256), 0, s, p, w); \
         after(LA_KERNEL_INTRA);                                                                                \
         before(LA_KERNEL_INTER);                                                                               \
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<KK, VV>), dim3(inter_blocks), dim3(384), 0, s, pf, w);   \
+        if (!a.chunk_states)                                                                                   \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<KK, VV>), dim3(inter_blocks), dim3(384), 0, s, pf, w); \
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true>), dim3(inter_blocks), dim3(256), 0, s, p, w, \
                            a.d_out, a.d_final, a.d_init);                                                      \
         after(LA_KERNEL_INTER);                                                                                \

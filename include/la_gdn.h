@@ -287,6 +287,24 @@ la_status la_gdn_bwd(const la_gdn_desc *desc, const void *q, const void *k, cons
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * la_gdn_bwd reusing the forward's states ("Linear Attention" page, "States and
+ * checkpoints": the forward can return its state every n tokens for the backward):
+ *   chunk_states   device, fp32 [C, HV, K, V], 16-byte aligned, C = sum over sequences of
+ *                  ceil(length / 64): the state at the start of every 64-token chunk, in
+ *                  sequence order, which la_gdn_fwd_ex writes as its state series with
+ *                  checkpoint_every_n_tokens = 64 and fp32 rows from the same inputs and
+ *                  initial states; NULL: as la_gdn_bwd (the forward is run again for them)
+ * Every other argument as la_gdn_bwd; with the series given, the results are those of
+ * la_gdn_bwd bit for bit, and the forward's state pass is not run again.  The series is
+ * read, never written, and must not change until the call has run on its stream.
+ */
+la_status la_gdn_bwd_ex(const la_gdn_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const int32_t *cu_seqlens, const float *initial_state,
+                        const float *chunk_states, const void *d_out, const float *d_final_state, float *dq,
+                        float *dk, float *dv, float *dg, float *dbeta, float *d_initial_state, int l2norm,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * la_gdn_fwd for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Arguments and
  * results are those of la_gdn_fwd (the same checks, kernels and bits) without the

@@ -406,6 +406,18 @@ def test_bwd_argument_checks(lib, over, status, needle):
     assert needle in la.la_last_error_message()
 
 
+def test_bwd_ex_chunk_states_checks(lib):
+    """la_gdn_bwd_ex: a misaligned chunk-state series is declined before any launch; NULL
+    takes la_gdn_bwd's path (the call then stops at the fake workspace's size)."""
+    A = 1 << 20
+    d = _desc()
+    args = lambda cs, wsb: (ctypes.byref(d), A, A, A, A, A, A, None, cs, A, None, A, A, A, A, A, A, 1, A, wsb, None)
+    assert lib.la_gdn_bwd_ex(*args(A + 4, 1 << 40)) == la.LA_ERR_INVALID_ARGUMENT
+    assert "chunk_states" in la.la_last_error_message()
+    assert lib.la_gdn_bwd_ex(*args(None, 1024)) == la.LA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.la_gdn_bwd_ex(*args(A, 1024)) == la.LA_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_bwd_workspace_bytes(lib):
     """The backward's workspace holds the forward's operands, the reverse pass's, the state
     at every chunk start and the chunk-end state gradients (fp32 K x V each per (chunk, head))."""

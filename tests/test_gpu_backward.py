@@ -160,3 +160,22 @@ def test_backward_dense_batch_slow_decay_companion():
     # on its slow-decay companion, where the initial state and the gradients reach across
     # every chunk of each sequence
     check_bwd(make_problem(3, companion=True), 216)
+
+
+@pytest.mark.parametrize("hk,hv", [(2, 2), (2, 4)])
+def test_backward_from_the_forward_state_series_bitwise(hk, hv):
+    # la_gdn_bwd_ex with the forward's fp32 series every 64 tokens: the forward's state pass is
+    # skipped and every gradient equals la_gdn_bwd's bit for bit
+    p = custom_problem((1, 63, 64, 65, 130, 200, 0), hk=hk, hv=hv, dk=128, dv=128, seed=219, with_state=True)
+    g = p.to("cuda")
+    d_out, d_fin = upstream(p, 220)
+    d_out, d_fin = d_out.cuda(), d_fin.cuda()
+    note(f"bwd_ex: series hk={hk} hv={hv}")
+    _, _, series = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                    checkpoint_every_n_tokens=64, checkpoint_dtype=torch.float32)
+    a = la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, d_out, initial_state=g.state, d_final_state=d_fin)
+    b = la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, d_out, initial_state=g.state, d_final_state=d_fin,
+                      chunk_states=series)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
