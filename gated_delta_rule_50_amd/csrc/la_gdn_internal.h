@@ -41,6 +41,8 @@ struct Prob {
                                       // kst = nh kstu; token-major [T, nh, H, D] views: any)
     int32_t ck_every;                 // state series every ck_every tokens (a multiple of 64), 0: none
     int32_t ck_fp32;                  // series rows in fp32 (else bf16)
+    int32_t ck_quad;                  // fp32 series in the row-quad layout (the backward's own chunk
+                                      // states; the public series is row-major)
     void *ck;                         // [ck_cap, HV, K, V] series, sequences in batch order
     int64_t ck_cap;                   // entries the caller allocated
     const int32_t *cu;
@@ -77,8 +79,8 @@ struct Ws {
     uint4 *PTF;        // [chunk, HV][3 causal tiles (s, t) = (0,0), (0,1), (1,1)][2]  P^T A fragments
     uint4 *TB;         // [chunk, HV][64 x 64]  T = (I + A)^-1 in bf16, row-major (full backward)
     float *SB;         // [chunk, HV, kScalars]  gam (log2) at 0, r_k at 64, r_q at 128, beta at 192
-    float *CK;         // [chunk, HV, K, V]  fp32 state at each chunk's start (full backward)
-    float *DSN;        // [chunk, HV, K, V]  gradient of each chunk's end state (full backward)
+    float *CK;         // [chunk, HV, K, V]  fp32 state at each chunk's start, row-quad layout (full backward)
+    float *DSN;        // [chunk, HV, K, V]  gradient of each chunk's end state, row-quad layout (full backward)
     __bf16 *DU;        // [chunk, HV, 64, V]  gradient of each chunk's U in bf16, row-major (full backward)
     __bf16 *OB;        // [T, HV, V]  the recomputed forward's output (unused, full backward)
     float *DQH, *DKH;  // [T, HV, K]  per value head: gradients of the scaled, normalised q and k rows

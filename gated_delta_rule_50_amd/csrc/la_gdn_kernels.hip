@@ -416,6 +416,15 @@ __device__ __forceinline__ uint2 f16_pack4(const f32x16 &acc, int j, int sh)
     return __builtin_bit_cast(uint2, __builtin_convertvector(x, f16x4));
 }
 
+// Row-quad layout of a K x V fp32 state (the backward's chunk-start states and chunk-end
+// state gradients): element (row, col) at ((row / 4) V + col) 4 + row % 4, so that rows
+// 4 m .. 4 m + 3 of one column, which an accumulator lane holds in four consecutive
+// registers, are one 16-byte store, and a 4 x 4 block is four 16-byte loads.
+__device__ __forceinline__ int64_t quad_off(int row, int col, int V)
+{
+    return ((int64_t)(row >> 2) * V + col) * 4 + (row & 3);
+}
+
 // Back to fp32 (exact): four fp16 values times 2^sh.
 __device__ __forceinline__ f32x4 f16_unpack4(u32x2 h, int sh)
 {
@@ -1593,14 +1602,21 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         if (CK && p.ck_fp32 && (kChunk * ci) % p.ck_every == 0) {
             const int64_t e = ck_base + (int64_t)kChunk * ci / p.ck_every;
             if (e < p.ck_cap) {
-                const int64_t base = ((e * p.HV + h) * K) * V;
+                float *base = static_cast<float *>(p.ck) + ((e * p.HV + h) * K) * V;
+                if (p.ck_quad) {
 #pragma unroll
-                for (int r = 0; r < NR; ++r)
+                    for (int r = 0; r < NR; ++r)
 #pragma unroll
-                    for (int ee = 0; ee < 16; ++ee) {
-                        const int64_t at = base + (int64_t)(row0 + 32 * r + 8 * (ee >> 2) + 4 * hh + (ee & 3)) * V + col;
-                        static_cast<float *>(p.ck)[at] = S[r][ee];
-                    }
+                        for (int j = 0; j < 4; ++j)
+                            *reinterpret_cast<f32x4 *>(base + quad_off(row0 + 32 * r + 8 * j + 4 * hh, col, V)) =
+                                f32x4{S[r][4 * j], S[r][4 * j + 1], S[r][4 * j + 2], S[r][4 * j + 3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r)
+#pragma unroll
+                        for (int ee = 0; ee < 16; ++ee)
+                            base[(int64_t)(row0 + 32 * r + 8 * (ee >> 2) + 4 * hh + (ee & 3)) * V + col] = S[r][ee];
+                }
             }
         }
         // ---- K^T of this key half (A operands: state rows, tokens in accumulator order,
@@ -1953,12 +1969,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) Sb[kk] = pack32(D[kk >> 1], kk & 1);
         if (FULL) {
-            // this chunk's end-state gradient, for the backward's intra pass
-            float *dst = w.DSN + chh * K * V + col;
+            // this chunk's end-state gradient, for the backward's intra pass (row-quad layout)
+            float *dst = w.DSN + chh * K * V;
 #pragma unroll
             for (int r = 0; r < NR; ++r)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) dst[(int64_t)(row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V] = D[r][e];
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<f32x4 *>(dst + quad_off(row0 + 32 * r + 8 * j + 4 * hh, col, V)) =
+                        f32x4{D[r][4 * j], D[r][4 * j + 1], D[r][4 * j + 2], D[r][4 * j + 3]};
         }
         // Z[o] = K (token tile m = o ^ kh, keys of this half) dS_kh; A operands are k rows with the
         // keys in accumulator order (two 8-byte reads of the swizzled tile)
@@ -2145,32 +2163,45 @@ __device__ __forceinline__ float lds_elem(const lds_char *tile, int row, int col
     return bf2f(*reinterpret_cast<const lds_bf16 *>(tile + swz_e<PPR>(row, col)));
 }
 
-// The backward intra pass's fp32 operands S0 and dS (K x V, row-major, in the workspace) into
-// swizzled bf16 tiles, by the 256 threads of the block with every float4 load issued before
-// the first is used (one memory latency instead of one per batch).  Returns the thread's
-// share of sum(S0 * dS).
-template <int K, int V>
+// The backward intra pass's fp32 operands S0 (row-major, or in the row-quad layout for
+// S0_QUAD) and dS (row-quad layout) into swizzled bf16 tiles, by the 256 threads of the block
+// in 4 x 4 blocks (four 16-byte loads of each matrix per block), with every load issued
+// before the first is used (one memory latency instead of one per batch).  Returns the
+// thread's share of sum(S0 * dS), summed in the same order for either S0 layout.
+template <int K, int V, bool S0_QUAD>
 __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, lds_char *dDS, const float *DS, int tid)
 {
-    constexpr int PPR = V / 8, N1 = K * V / 4 / 256;
-    float4 a[N1], c[N1];
+    constexpr int PPR = V / 8, NB = K * V / 16 / 256;
+    float4 a[NB][4], b[NB][4];
 #pragma unroll
-    for (int j = 0; j < N1; ++j) {
-        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
-        a[j] = *reinterpret_cast<const float4 *>(S0 + (int64_t)row * V + c4);
-        c[j] = *reinterpret_cast<const float4 *>(DS + (int64_t)row * V + c4);
+    for (int j = 0; j < NB; ++j) {
+        const int blk = tid + 256 * j, rq = blk / (V / 4), c4 = 4 * (blk % (V / 4));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // S0_QUAD: column c4 + u, rows 4 rq .. 4 rq + 3; else row 4 rq + u, columns c4 .. c4 + 3
+            a[j][u] = *reinterpret_cast<const float4 *>(S0 + (S0_QUAD ? ((int64_t)rq * V + c4 + u) * 4
+                                                                      : (int64_t)(4 * rq + u) * V + c4));
+            b[j][u] = *reinterpret_cast<const float4 *>(DS + ((int64_t)rq * V + c4 + u) * 4);
+        }
     }
-    auto put = [&](lds_char *dst, int row, int c4, const float4 &x) {
-        const bf16x4 v4 = {f2bf(x.x), f2bf(x.y), f2bf(x.z), f2bf(x.w)};
-        *reinterpret_cast<lds_bf16x4 *>(dst + swz<PPR>(row, c4)) = v4;
-    };
+    auto el = [](const float4 &x, int i) { return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w; };
     float dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < N1; ++j) {
-        const int idx = tid + 256 * j, row = idx / (V / 4), c4 = 4 * (idx % (V / 4));
-        put(dS0, row, c4, a[j]);
-        put(dDS, row, c4, c[j]);
-        dot += a[j].x * c[j].x + a[j].y * c[j].y + a[j].z * c[j].z + a[j].w * c[j].w;
+    for (int j = 0; j < NB; ++j) {
+        const int blk = tid + 256 * j, rq = blk / (V / 4), c4 = 4 * (blk % (V / 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float s[4], d[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s[u] = S0_QUAD ? el(a[j][u], i) : el(a[j][i], u);
+                d[u] = el(b[j][u], i);
+                dot += s[u] * d[u];
+            }
+            const int row = 4 * rq + i;
+            *reinterpret_cast<lds_bf16x4 *>(dS0 + swz<PPR>(row, c4)) = bf16x4{f2bf(s[0]), f2bf(s[1]), f2bf(s[2]), f2bf(s[3])};
+            *reinterpret_cast<lds_bf16x4 *>(dDS + swz<PPR>(row, c4)) = bf16x4{f2bf(d[0]), f2bf(d[1]), f2bf(d[2]), f2bf(d[3])};
+        }
     }
     return dot;
 }
@@ -2265,7 +2296,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         s_eg[tid] = exp2_hw(gam);
         s_dd[tid] = exp2_hw(tid < len ? gn - gam : kNegInf);
     }
-    float dot = load_stage_a<K, V>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid);
+    float dot = p.ck_quad ? load_stage_a<K, V, true>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid)
+                          : load_stage_a<K, V, false>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (lane == 0) sdot[wave] = dot;
@@ -2721,6 +2753,10 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
     Prob pf = p;
     pf.ck_every = kChunk;
     pf.ck_fp32 = 1;
+    pf.ck_quad = 1;
+    // the intra pass reads the chunk-start states in the layout they come in
+    Prob pb = p;
+    pb.ck_quad = a.chunk_states ? 0 : 1;
     pf.ck = w.CK;
     pf.ck_cap = p.max_chunks;
     pf.o = w.OB;
@@ -2741,7 +2777,7 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
         after(LA_KERNEL_INTER);                                                                                \
         before(LA_KERNEL_BWD_INTRA);                                                                           \
         if (items > 0)                                                                                         \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV>), dim3((unsigned)items), dim3(256), 0, s, p, w, \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV>), dim3((unsigned)items), dim3(256), 0, s, pb, w, \
                                a.d_out, a.dv, a.dg, a.dbeta, fuse_qk ? a.dq : nullptr, fuse_qk ? a.dk : nullptr); \
         if (!fuse_qk && qk_blocks > 0)                                                                         \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_qk<KK>), dim3(qk_blocks), dim3(256), 0, s, p, w, a.dq, a.dk); \
