@@ -486,7 +486,6 @@ WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t 
     L.CK = take(bwd == 2 ? items * K * V * 4 : 0);
     L.DSN = take(bwd == 2 ? items * K * V * 4 : 0);
     L.DU = take(bwd == 2 ? items * 64 * V * 2 : 0);
-    L.OB = take(bwd == 2 ? (size_t)T * HV * V * 2 : 0);
     // per-value-head q and k gradients, summed over each head group afterwards (with one
     // value head per q/k head the intra pass writes dq and dk itself)
     const bool qk_sums = bwd == 2 && HV != HK;
@@ -516,7 +515,6 @@ Ws carve_workspace(void *base, const WsLayout &L, bool summary)
     w.CK = reinterpret_cast<float *>(b + L.CK);
     w.DSN = reinterpret_cast<float *>(b + L.DSN);
     w.DU = reinterpret_cast<__bf16 *>(b + L.DU);
-    w.OB = reinterpret_cast<__bf16 *>(b + L.OB);
     w.DQH = reinterpret_cast<float *>(b + L.DQH);
     w.DKH = reinterpret_cast<float *>(b + L.DKH);
     return w;

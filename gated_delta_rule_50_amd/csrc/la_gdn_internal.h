@@ -82,7 +82,6 @@ struct Ws {
     float *CK;         // [chunk, HV, K, V]  fp32 state at each chunk's start, row-quad layout (full backward)
     float *DSN;        // [chunk, HV, K, V]  gradient of each chunk's end state, row-quad layout (full backward)
     __bf16 *DU;        // [chunk, HV, 64, V]  gradient of each chunk's U in bf16, row-major (full backward)
-    __bf16 *OB;        // [T, HV, V]  the recomputed forward's output (unused, full backward)
     float *DQH, *DKH;  // [T, HV, K]  per value head: gradients of the scaled, normalised q and k rows
                        // (only with HV > HK: head groups to sum)
 };
@@ -92,7 +91,7 @@ struct Ws {
 // pass's operands only); 2 the full backward (the forward's operands, the reverse pass's,
 // and the per-chunk states and gradients the backward's intra pass reads).
 struct WsLayout {
-    size_t hdr, seq_info, chunks, order, WF, PF, UH, SC, cu32, WTF, PTF, TB, SB, CK, DSN, DU, OB, DQH, DKH, total;
+    size_t hdr, seq_info, chunks, order, WF, PF, UH, SC, cu32, WTF, PTF, TB, SB, CK, DSN, DU, DQH, DKH, total;
 };
 WsLayout workspace_layout(int64_t N, int64_t T, int64_t HK, int64_t HV, int64_t K, int64_t V,
                           bool summary, int bwd = 0);

@@ -1264,7 +1264,7 @@ __device__ __forceinline__ int inter_issue_k(const Prob &p, lds_u32x4 *lb, int c
 // scalars (loader 0) into `eb`.  Returns the number of loads.
 // Gated Delta Product: qoff holds the token offsets of the pieces' rows (a of row = a nh + b)
 // for a chunk that starts at its token's first update, kb the b and krow the row of each.
-template <int K, int V, bool SUMMARY, bool GDP>
+template <int K, int V, bool SUMMARY, bool GDP, bool NOOUT = false>
 __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
                                                   const InterCtx<K, V, SUMMARY> &x,
                                                   const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ],
@@ -1275,7 +1275,7 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
     const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
     const uint32_t lo16 = (uint32_t)x.lane * 16u;
     int n = 0;
-    if (C::FWD) {
+    if (C::FWD && !NOOUT) {
         const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
         if (!GDP) {
             const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)x.hk * p.qsh,
@@ -1377,9 +1377,12 @@ __device__ __forceinline__ UnitOfBlock unit_of_block(const Prob &p, const Ws &w,
     return r;
 }
 
-template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false>
+// NOOUT (with CK, fp32 rows): the states only, no outputs (the backward's run of the forward):
+// the output waves take part in the barriers only, the loaders skip q and P^T.
+template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false, bool NOOUT = false>
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
+    static_assert(!NOOUT || (CK && !SUMMARY && !GDP), "states only: the forward with the fp32 series");
     using C = InterCfg<K, V, SUMMARY>;
     constexpr int NR = C::NR, NKS = C::NKS;
     __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64], sE2[C::NFE * 64];   // q, P^T, scalars: three buffers
@@ -1462,11 +1465,11 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         int na = 0, nb = 0;
         if (nch > 0) {
             na = inter_issue_k<K, V, SUMMARY, GDP>(p, l0, 0, lh, x, koff, kb, cur);
-            nb = inter_issue_output<K, V, SUMMARY, GDP>(p, w, e0, 0, lh, x, qoff, kb, krow, cur);
+            nb = inter_issue_output<K, V, SUMMARY, GDP, NOOUT>(p, w, e0, 0, lh, x, qoff, kb, krow, cur);
             if (GDP) cur.advance(q64, r64, p.nh);
             if (nch > 1) {
                 inter_issue_k<K, V, SUMMARY, GDP>(p, l1, 1, lh, x, koff, kb, cur);
-                inter_issue_output<K, V, SUMMARY, GDP>(p, w, e1, 1, lh, x, qoff, kb, krow, cur);
+                inter_issue_output<K, V, SUMMARY, GDP, NOOUT>(p, w, e1, 1, lh, x, qoff, kb, krow, cur);
                 if (GDP) cur.advance(q64, r64, p.nh);
             }
             vm_wait_n(nch > 1 ? na + nb : 0);                 // all of chunk 0
@@ -1474,7 +1477,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const bool more2 = ci + 2 < nch;
-            if (more2) inter_issue_output<K, V, SUMMARY, GDP>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff, kb, krow, cur);
+            if (more2) inter_issue_output<K, V, SUMMARY, GDP, NOOUT>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff, kb, krow, cur);
             lds_barrier();                                    // B1
             if (more2) {
                 inter_issue_k<K, V, SUMMARY, GDP>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff, kb, cur);
@@ -1486,6 +1489,15 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         return;
     }
 
+    if (NOOUT && wave >= 2) {
+        // the output waves' barriers, nothing else
+        lds_barrier();
+        for (int ci = 0; ci < nch; ++ci) {
+            lds_barrier();                                    // B1
+            lds_barrier();                                    // B2
+        }
+        return;
+    }
     if (C::FWD && wave >= 2) {
         // ------------------------------------------------------------ output waves
         const int t = wave - 2;
@@ -1650,7 +1662,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
             Sb[kk] = pack32(S[kk >> 1], kk & 1);
-            if (C::FWD) xS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
+            if (C::FWD && !NOOUT) xS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
         }
         // ---- X_kh = [U~] + (-W)_kh S_kh, published for the other state wave
 #pragma unroll
@@ -1694,7 +1706,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             }
             Ud[2 * o] = pack32(ud, 0);
             Ud[2 * o + 1] = pack32(ud, 1);
-            if (C::FWD && o == 0) {
+            if (C::FWD && !NOOUT && o == 0) {
                 xU[(2 * kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
                 xU[(2 * kh + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
             }
@@ -1756,6 +1768,13 @@ template <int K, int V>
 __global__ __launch_bounds__(384) void k_inter_ck(Prob p, Ws w)
 {
     inter_body<K, V, false, true>(p, w);
+}
+
+// The backward's run of the forward: the fp32 state at every chunk start, no outputs.
+template <int K, int V>
+__global__ __launch_bounds__(384) void k_inter_states(Prob p, Ws w)
+{
+    inter_body<K, V, false, true, false, true>(p, w);
 }
 
 template <int K, int V>
@@ -2759,9 +2778,7 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
     pb.ck_quad = a.chunk_states ? 0 : 1;
     pf.ck = w.CK;
     pf.ck_cap = p.max_chunks;
-    pf.o = w.OB;
-    pf.ost = (int64_t)p.HV * p.V;
-    pf.osh = p.V;
+    pf.o = nullptr;
     pf.sT = nullptr;
 #define LA_BWD(KK, VV)                                                                                         \
     if (p.K == KK && p.V == VV) {                                                                              \
@@ -2771,7 +2788,7 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
         after(LA_KERNEL_INTRA);                                                                                \
         before(LA_KERNEL_INTER);                                                                               \
         if (!a.chunk_states)                                                                                   \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<KK, VV>), dim3(inter_blocks), dim3(384), 0, s, pf, w); \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_states<KK, VV>), dim3(inter_blocks), dim3(384), 0, s, pf, w); \
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true>), dim3(inter_blocks), dim3(256), 0, s, p, w, \
                            a.d_out, a.d_final, a.d_init);                                                      \
         after(LA_KERNEL_INTER);                                                                                \

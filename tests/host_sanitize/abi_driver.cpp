@@ -276,7 +276,6 @@ void full_backward()
                            reinterpret_cast<const char *>(g_stub.last_ws.CK),
                            reinterpret_cast<const char *>(g_stub.last_ws.DSN),
                            reinterpret_cast<const char *>(g_stub.last_ws.DU),
-                           reinterpret_cast<const char *>(g_stub.last_ws.OB),
                            reinterpret_cast<const char *>(g_stub.last_ws.DQH),
                            reinterpret_cast<const char *>(g_stub.last_ws.DKH)};
     for (const char *p : parts) CHECK(p >= lo && p < hi);
