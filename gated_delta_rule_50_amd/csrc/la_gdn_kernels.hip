@@ -393,6 +393,30 @@ __device__ __forceinline__ void st_op(T *dst, T v)
     else *dst = v;
 }
 
+// Lane exchanges within each group of 32 lanes: partner lane c ^ 16 (swizzle, bit mode
+// and 0x1f, xor 0x10), c ^ 15 (row mirror), c ^ 7 (half-row mirror), c ^ 2 and c ^ 1 (quad
+// permutations).
+__device__ __forceinline__ float xch16(float x)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
+}
+__device__ __forceinline__ float xch15(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xch7(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xch2(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float xch1(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, true));
+}
+
 // U~ hand-over in fp16: each 32 x 32 accumulator tile is scaled by 2^(15 - E), E the
 // exponent with the tile's largest magnitude in [2^(E-1), 2^E), so that it lands in
 // [2^14, 2^15) and every element keeps fp16's 11-bit significand (round to nearest even).
@@ -402,9 +426,16 @@ __device__ __forceinline__ int f16_tile_shift(const f32x16 &acc)
     float a = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(acc[e]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-    return __builtin_amdgcn_frexp_expf(a) - 15;
+    // the largest over each 32-lane half by lane exchanges (masks 1, 2, 7, 15 and 16 span the
+    // half), then over the two halves from lanes 0 and 32
+    a = fmaxf(a, xch1(a));
+    a = fmaxf(a, xch2(a));
+    a = fmaxf(a, xch7(a));
+    a = fmaxf(a, xch15(a));
+    a = fmaxf(a, xch16(a));
+    const float m = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)));
+    return __builtin_amdgcn_frexp_expf(m) - 15;
 }
 
 // Registers 4 j .. 4 j + 3 of a tile, scaled by 2^-sh and rounded to fp16.
@@ -796,8 +827,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
             for (int i = 0; i < PK / 4; ++i)
                 s2 += sumsq8(__builtin_bit_cast(uint4, lds_row8<PK>(sX, row, 8 * (4 * i + (lane & 3)))));
-            s2 += __shfl_xor(s2, 1, 64);
-            s2 += __shfl_xor(s2, 2, 64);
+            s2 += xch1(s2);
+            s2 += xch2(s2);
             if ((lane & 3) == 0) s_rq[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f) : 0.f;
         }
         // ---- 2b: Gram tiles.  wave 0: G(0,0), P^T(0,0); wave 1: G(1,0); wave 2: G(1,1),
@@ -2118,30 +2149,6 @@ template <int PPR>
 __device__ __forceinline__ int swz_e(int row, int col)
 {
     return swz<PPR>(row, col & ~3) + 2 * (col & 3);
-}
-
-// Lane exchanges within each group of 32 lanes: partner lane c ^ 16 (swizzle, bit mode
-// and 0x1f, xor 0x10), c ^ 15 (row mirror), c ^ 7 (half-row mirror), c ^ 2 and c ^ 1 (quad
-// permutations).
-__device__ __forceinline__ float xch16(float x)
-{
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
-}
-__device__ __forceinline__ float xch15(float x)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float xch7(float x)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float xch2(float x)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float xch1(float x)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, true));
 }
 
 // Row sums of an accumulator tile: register e of every lane summed over the 32 lanes that
