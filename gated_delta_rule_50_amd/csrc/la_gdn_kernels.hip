@@ -1210,11 +1210,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // the decayed erase steps; there are no outputs and no output waves (the loader
 // waves are waves 2, 3).
 
-template <int K, int V, bool SUMMARY>
+template <int K, int V, bool SUMMARY, int TP = 1>
 struct InterCfg {
     static constexpr bool FWD = !SUMMARY;
     static constexpr int VA = SUMMARY ? V + K : V;
-    static constexpr int NT = VA / 32;            // workgroups (32-column tiles) per (sequence, head)
+    static constexpr int NT = VA / (32 * TP);     // workgroups (TP 32-column tiles each) per (sequence, head)
     static constexpr int KH = K / 2;              // state rows per state wave
     static constexpr int NR = KH / 32;            // 32-row accumulator tiles per state wave
     static constexpr int NKS = KH / 16;           // reduction steps over a key half
@@ -1225,13 +1225,15 @@ struct InterCfg {
     // bf16, pieces swizzled by row) in its own array; raw q (same layout), P^T (tile
     // 0 steps 0..1, tile 1 steps 0..3) and the scalars (d[64], sq[64], 2^(gam_n) at
     // 192) in the other.
-    static constexpr int FW = 4 * NKS, FU = 4, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
+    static constexpr int FW = 4 * NKS, FU = 4 * TP, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
     static constexpr int oU = 0, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
     static constexpr int FK = K / 8, oK = 0, NFL = FK;
     static constexpr int NKL = FK / 2;            // k tile loads per loader wave
-    // waves: 0, 1 state, (forward) 2, 3 output, then the two loader waves; the summary has
-    // no outputs, so its workgroup is 4 waves and two fit on a CU (LDS 75 KiB at K = V = 128)
-    static constexpr int LW = FWD ? 4 : 2;        // first loader wave
+    // waves: 0 .. 2 TP - 1 state (key half w & 1, tile w >> 1), (forward) two output waves,
+    // then the two loader waves; the summary has no outputs, so its workgroup is 4 waves and
+    // two fit on a CU
+    static constexpr int SW = 2 * TP;             // state waves
+    static constexpr int LW = FWD ? SW + 2 : SW;  // first loader wave
     static constexpr int THREADS = 64 * (LW + 2);
     static constexpr int NQ = NKL;                // q tile loads per loader wave (forward)
 };
@@ -1239,6 +1241,7 @@ struct InterCfg {
 template <int K, int V, bool SUMMARY>
 struct InterCtx {
     int nch, seq_start, seq_len, cid0, h, hk, tile, lane;
+    int vt0;          // the workgroup's first 32-column value tile
     bool ptile;
 };
 
@@ -1295,14 +1298,14 @@ __device__ __forceinline__ int inter_issue_k(const Prob &p, lds_u32x4 *lb, int c
 // scalars (loader 0) into `eb`.  Returns the number of loads.
 // Gated Delta Product: qoff holds the token offsets of the pieces' rows (a of row = a nh + b)
 // for a chunk that starts at its token's first update, kb the b and krow the row of each.
-template <int K, int V, bool SUMMARY, bool GDP, bool NOOUT = false>
+template <int K, int V, bool SUMMARY, bool GDP, bool NOOUT = false, int TP = 1>
 __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, lds_u32x4 *eb, int ci, int lh,
                                                   const InterCtx<K, V, SUMMARY> &x,
                                                   const uint32_t (&qoff)[InterCfg<K, V, SUMMARY>::NQ],
                                                   const int (&kb)[InterCfg<K, V, SUMMARY>::NKL],
                                                   const int (&krow)[InterCfg<K, V, SUMMARY>::NKL], UCursor cur)
 {
-    using C = InterCfg<K, V, SUMMARY>;
+    using C = InterCfg<K, V, SUMMARY, TP>;
     const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
     const uint32_t lo16 = (uint32_t)x.lane * 16u;
     int n = 0;
@@ -1335,7 +1338,7 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
         n += C::FQ / 2 + 3;
     }
     if (!x.ptile) {
-        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UH) + (chh * (V / 32) + x.tile) * C::FU * kFrag,
+        const i32x4 rU = make_rsrc(reinterpret_cast<const char *>(w.UH) + (chh * (V / 32) + x.vt0) * 4 * kFrag,
                                    C::FU * kFrag);
 #pragma unroll
         for (int i = 0; i < C::FU / 2; ++i) {
@@ -1356,7 +1359,8 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
 // to o.  Lane (c, hh) holds value columns 8 j + 4 hh .. + 3 of token 32 t + c.
 template <int K, int V, bool SUMMARY, bool GDP>
 __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU, const f32x16 &Y, const bf16x8 (&Pf)[4],
-                                             float sq, int t, int o_start, int o_len, const InterCtx<K, V, SUMMARY> &x)
+                                             float sq, int t, int o_start, int o_len, const InterCtx<K, V, SUMMARY> &x,
+                                             int vt)
 {
     const int lane = x.lane, c = lane & 31, hh = lane >> 5;
     f32x16 O;
@@ -1377,7 +1381,7 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
         else if (u % p.nh == p.nh - 1) orow = u / p.nh;
     }
     if (orow >= 0) {
-        __bf16 *ob = p.o + (int64_t)orow * p.ost + (int64_t)x.h * p.osh + 32 * x.tile + 4 * hh;
+        __bf16 *ob = p.o + (int64_t)orow * p.ost + (int64_t)x.h * p.osh + 32 * vt + 4 * hh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 o4 = {O[4 * j], O[4 * j + 1], O[4 * j + 2], O[4 * j + 3]};
@@ -1410,21 +1414,29 @@ __device__ __forceinline__ UnitOfBlock unit_of_block(const Prob &p, const Ws &w,
 
 // NOOUT (with CK, fp32 rows): the states only, no outputs (the backward's run of the forward):
 // the output waves take part in the barriers only, the loaders skip q and P^T.
-template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false, bool NOOUT = false>
+// TP = 2 (the plain forward at large batch): two 32-column tiles per workgroup, so that a
+// batch needs half the workgroups, with four state waves (key half x tile), the output waves
+// covering both tiles, and the output operands double- instead of triple-buffered (LDS).
+template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false, bool NOOUT = false, int TP = 1>
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     static_assert(!NOOUT || (CK && !SUMMARY && !GDP), "states only: the forward with the fp32 series");
-    using C = InterCfg<K, V, SUMMARY>;
+    static_assert(TP == 1 || (!SUMMARY && !CK && !GDP && !NOOUT), "two tiles per workgroup: the plain forward");
+    using C = InterCfg<K, V, SUMMARY, TP>;
     constexpr int NR = C::NR, NKS = C::NKS;
-    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64], sE2[C::NFE * 64];   // q, P^T, scalars: three buffers
+    constexpr int NEB = TP == 1 ? 3 : 2;                   // output-operand buffers
+    __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64], sE2[NEB == 3 ? C::NFE * 64 : 1];   // q, U~, P^T, scalars
     __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // raw k: two buffers
-    __shared__ u32x4 sX[2 * 8 * 64];                       // X partials: [kh][m][j][lane]
-    __shared__ u32x4 sS[C::FWD ? 2 * NKS * 64 : 1];        // S (bf16 operands): [kh][step][lane]
-    __shared__ u32x4 sU[C::FWD ? 4 * 64 : 1];              // U_new (bf16 operands): [token step][lane]
+    __shared__ u32x4 sX[TP * 2 * 8 * 64];                  // X partials: [tile][kh][m][j][lane]
+    __shared__ u32x4 sS[C::FWD ? TP * 2 * NKS * 64 : 1];   // S (bf16 operands): [tile][kh][step][lane]
+    __shared__ u32x4 sU[C::FWD ? TP * 4 * 64 : 1];         // U_new (bf16 operands): [tile][token step][lane]
     lds_u32x4 *const e0 = (lds_u32x4 *)sE0, *const e1 = (lds_u32x4 *)sE1, *const e2 = (lds_u32x4 *)sE2;
-    auto ebuf = [&](int c) { const int r = c % 3; return r == 0 ? e0 : (r == 1 ? e1 : e2); };
+    auto ebuf = [&](int c) {
+        if (NEB == 2) return (c & 1) ? e1 : e0;
+        const int r = c % 3;
+        return r == 0 ? e0 : (r == 1 ? e1 : e2);
+    };
     lds_u32x4 *const l0 = (lds_u32x4 *)sL0, *const l1 = (lds_u32x4 *)sL1;
-    lds_u32x4 *const xX = (lds_u32x4 *)sX, *const xS = (lds_u32x4 *)sS, *const xU = (lds_u32x4 *)sU;
 
     if (w.hdr[0] != LA_DEVICE_OK) return;
     const UnitOfBlock ub = unit_of_block(p, w, blockIdx.x, C::NT);
@@ -1439,6 +1451,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     x.h = h;
     x.hk = h / (p.HV / p.HK);
     x.tile = tile;
+    x.vt0 = TP * tile;
     x.lane = threadIdx.x & 63;
     x.ptile = SUMMARY && 32 * tile >= V;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1494,13 +1507,36 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         // chunk c (the state waves have read chunk c's k by then) its k rows; before B2
         // of chunk c the loaders wait for all of chunk c + 1's.
         int na = 0, nb = 0;
+        if (NEB == 2) {
+            // two output-operand buffers: chunk c + 1's are issued at the start of chunk c
+            // (after B2 of chunk c - 1, when chunk c - 1's are dead), its k rows one chunk
+            // earlier, after B1 of chunk c - 1; before B2 of chunk c the loaders wait for
+            // all of chunk c + 1's
+            if (nch > 0) {
+                na = inter_issue_k<K, V, SUMMARY, GDP>(p, l0, 0, lh, x, koff, kb, cur);
+                nb = inter_issue_output<K, V, SUMMARY, GDP, NOOUT, TP>(p, w, e0, 0, lh, x, qoff, kb, krow, cur);
+                if (nch > 1) inter_issue_k<K, V, SUMMARY, GDP>(p, l1, 1, lh, x, koff, kb, cur);
+                vm_wait_n(nch > 1 ? na : 0);                  // all of chunk 0
+            }
+            lds_barrier();
+            for (int ci = 0; ci < nch; ++ci) {
+                const bool more1 = ci + 1 < nch, more2 = ci + 2 < nch;
+                if (more1)
+                    inter_issue_output<K, V, SUMMARY, GDP, NOOUT, TP>(p, w, ebuf(ci + 1), ci + 1, lh, x, qoff, kb, krow, cur);
+                lds_barrier();                                // B1
+                if (more2) inter_issue_k<K, V, SUMMARY, GDP>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff, kb, cur);
+                vm_wait_n(more2 ? na : 0);                    // all of chunk ci + 1
+                lds_barrier();                                // B2
+            }
+            return;
+        }
         if (nch > 0) {
             na = inter_issue_k<K, V, SUMMARY, GDP>(p, l0, 0, lh, x, koff, kb, cur);
-            nb = inter_issue_output<K, V, SUMMARY, GDP, NOOUT>(p, w, e0, 0, lh, x, qoff, kb, krow, cur);
+            nb = inter_issue_output<K, V, SUMMARY, GDP, NOOUT, TP>(p, w, e0, 0, lh, x, qoff, kb, krow, cur);
             if (GDP) cur.advance(q64, r64, p.nh);
             if (nch > 1) {
                 inter_issue_k<K, V, SUMMARY, GDP>(p, l1, 1, lh, x, koff, kb, cur);
-                inter_issue_output<K, V, SUMMARY, GDP, NOOUT>(p, w, e1, 1, lh, x, qoff, kb, krow, cur);
+                inter_issue_output<K, V, SUMMARY, GDP, NOOUT, TP>(p, w, e1, 1, lh, x, qoff, kb, krow, cur);
                 if (GDP) cur.advance(q64, r64, p.nh);
             }
             vm_wait_n(nch > 1 ? na + nb : 0);                 // all of chunk 0
@@ -1508,7 +1544,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const bool more2 = ci + 2 < nch;
-            if (more2) inter_issue_output<K, V, SUMMARY, GDP, NOOUT>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff, kb, krow, cur);
+            if (more2) inter_issue_output<K, V, SUMMARY, GDP, NOOUT, TP>(p, w, ebuf(ci + 2), ci + 2, lh, x, qoff, kb, krow, cur);
             lds_barrier();                                    // B1
             if (more2) {
                 inter_issue_k<K, V, SUMMARY, GDP>(p, (ci & 1) ? l1 : l0, ci + 2, lh, x, koff, kb, cur);
@@ -1520,7 +1556,8 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         return;
     }
 
-    if (NOOUT && wave >= 2) {
+    lds_u32x4 *const xX = (lds_u32x4 *)sX, *const xS = (lds_u32x4 *)sS, *const xU = (lds_u32x4 *)sU;
+    if (NOOUT && wave >= C::SW) {
         // the output waves' barriers, nothing else
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
@@ -1529,10 +1566,10 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         }
         return;
     }
-    if (C::FWD && wave >= 2) {
+    if (C::FWD && wave >= C::SW) {
         // ------------------------------------------------------------ output waves
-        const int t = wave - 2;
-        f32x16 Y = {};
+        const int t = wave - C::SW;
+        f32x16 Y[TP] = {};
         bf16x8 Pf[4];
         float sq = 0.f;
         int o_start = 0, o_len = 0;
@@ -1540,7 +1577,12 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         for (int ci = 0; ci < nch; ++ci) {
             const lds_u32x4 *eb = ebuf(ci);
             // the previous chunk's output (its U_new was published before the last B2)
-            if (ci > 0) inter_output<K, V, SUMMARY, GDP>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+            if (ci > 0) {
+#pragma unroll
+                for (int tp = 0; tp < TP; ++tp)
+                    inter_output<K, V, SUMMARY, GDP>(p, xU + tp * 4 * 64, Y[tp], Pf, sq, t, o_start, o_len, x,
+                                                     x.vt0 + tp);
+            }
             lds_barrier();                                    // B1: S of chunk ci is published
             // operands of chunk ci (they stay in their buffer until the next chunk
             // starts): q as B operands over all state rows (accumulator order within
@@ -1562,10 +1604,13 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
                                               : bf16x8{};
                 sq = reinterpret_cast<const lds_float *>(eb + C::oS * 64)[64 + 32 * t + c];
             }
-            Y = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < 2 * NKS; ++kk)
-                Y = mfma32(__builtin_bit_cast(bf16x8, xS[kk * 64 + lane]), Qf[kk], Y);
+            for (int tp = 0; tp < TP; ++tp) {
+                Y[tp] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 2 * NKS; ++kk)
+                    Y[tp] = mfma32(__builtin_bit_cast(bf16x8, xS[(tp * 2 * NKS + kk) * 64 + lane]), Qf[kk], Y[tp]);
+            }
             if (CK && !p.ck_fp32 && (kChunk * ci) % p.ck_every == 0) {
                 // the chunk-start state as bf16 rows: output wave t writes key steps
                 // t NKS .. t NKS + NKS - 1; lane (c, hh) of step kk holds column c, keys
@@ -1587,15 +1632,22 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             o_len = min(kChunk, x.seq_len - kChunk * ci);
             lds_barrier();                                    // B2: U_new of chunk ci is published
         }
-        if (nch > 0) inter_output<K, V, SUMMARY, GDP>(p, xU, Y, Pf, sq, t, o_start, o_len, x);
+        if (nch > 0) {
+#pragma unroll
+            for (int tp = 0; tp < TP; ++tp)
+                inter_output<K, V, SUMMARY, GDP>(p, xU + tp * 4 * 64, Y[tp], Pf, sq, t, o_start, o_len, x, x.vt0 + tp);
+        }
         return;
     }
 
     // ---------------------------------------------------------------- state waves
     // (they carry the sequential chain: first claim on their SIMDs' issue slots)
     __builtin_amdgcn_s_setprio(3);
-    const int kh = wave;
-    const int col = 32 * tile + c;                      // this lane's state column
+    const int kh = wave & 1, tp = wave >> 1;            // key half, tile of the workgroup
+    const int vt = x.vt0 + tp;                          // this wave's 32-column value tile
+    const int col = 32 * vt + c;                        // this lane's state column
+    // this wave's tile's X partials, S and U_new operands
+    lds_u32x4 *const tX = xX + tp * 2 * 8 * 64, *const tS = xS + tp * 2 * NKS * 64, *const tU = xU + tp * 4 * 64;
     const int row0 = kh * C::KH;                        // first state row of this wave
     const int64_t unit = (int64_t)n * p.HV + h;
     f32x16 S[NR];
@@ -1677,8 +1729,8 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         f32x16 X[2];
         X[1] = f32x16{};
         if (!x.ptile) {
-            const lds_u32x2 *uh = reinterpret_cast<const lds_u32x2 *>(eb + C::oU * 64) + kh * 4 * 64;
-            const int sh = __float_as_int(reinterpret_cast<const lds_float *>(eb + C::oS * 64)[128 + 2 * x.tile + kh]);
+            const lds_u32x2 *uh = reinterpret_cast<const lds_u32x2 *>(eb + C::oU * 64) + (tp * 2 + kh) * 4 * 64;
+            const int sh = __float_as_int(reinterpret_cast<const lds_float *>(eb + C::oS * 64)[128 + 2 * vt + kh]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x4 u4 = f16_unpack4(uh[j * 64 + lane], sh);
@@ -1693,7 +1745,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
             Sb[kk] = pack32(S[kk >> 1], kk & 1);
-            if (C::FWD && !NOOUT) xS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
+            if (C::FWD && !NOOUT) tS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
         }
         // ---- X_kh = [U~] + (-W)_kh S_kh, published for the other state wave
 #pragma unroll
@@ -1714,7 +1766,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         for (int o = 0; o < 2; ++o)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xX[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
+                tX[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
                     __builtin_bit_cast(u32x4, f32x4{X[o][4 * j], X[o][4 * j + 1], X[o][4 * j + 2], X[o][4 * j + 3]});
         lds_barrier();                                        // B1
         if (ci + 2 < nch) load_w(R, ci + 2);
@@ -1727,7 +1779,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             f32x16 un, ud;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 xo = __builtin_bit_cast(f32x4, xX[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
+                const f32x4 xo = __builtin_bit_cast(f32x4, tX[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
                 const f32x4 dj = *reinterpret_cast<const lds_f32x4 *>(scl + 32 * m + 8 * j + 4 * hh);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1738,8 +1790,8 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             Ud[2 * o] = pack32(ud, 0);
             Ud[2 * o + 1] = pack32(ud, 1);
             if (C::FWD && !NOOUT && o == 0) {
-                xU[(2 * kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
-                xU[(2 * kh + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
+                tU[(2 * kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
+                tU[(2 * kh + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
             }
         }
         // ---- own rows: S <- (2^(gam_n) S) + K^T diag(d) U_new
@@ -1783,6 +1835,15 @@ __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 {
     static_assert(InterCfg<K, V, false>::THREADS == 384, "forward: 6 waves");
     inter_body<K, V, false>(p, w);
+}
+
+// The plain forward with two 32-column tiles per workgroup (8 waves, 150 KiB of LDS at
+// K = V = 128): for batches that need more than one round of the one-tile workgroups.
+template <int K, int V>
+__global__ __launch_bounds__(512) void k_inter_wide(Prob p, Ws w)
+{
+    static_assert(InterCfg<K, V, false, 2>::THREADS == 512, "forward, two tiles: 8 waves");
+    inter_body<K, V, false, false, false, false, 2>(p, w);
 }
 
 // The Gated Delta Product's forward: q rows and o rows mapped from update rows to
@@ -1882,6 +1943,14 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_gdp<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else if (p.ck_every > 0)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else if (blocks > p.intra_grid / 3 && blocks <= 2 * (p.intra_grid / 3))
+            // one-tile workgroups (one fits a CU) for up to two rounds of the CUs: two tiles
+            // per workgroup, one round, each chunk step about 1.6x as long (dense batch of 8 x
+            // 4096 tokens, HV = 16: 202 -> 162 us).  With more rounds the longest sequence's
+            // chain decides, and its steps are shorter with one tile (the ragged batch with a
+            // 65,536-token sequence, H = 32: 2478 us with one tile, 2536 us with two).
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_wide<K, V>), dim3((unsigned)(blocks / 2)),
+                               dim3(InterCfg<K, V, false, 2>::THREADS), 0, s, p, w);
         else
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         after(LA_KERNEL_INTER);

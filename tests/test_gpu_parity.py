@@ -217,6 +217,28 @@ def test_batch_invariance_bitwise_config4():
         assert torch.equal(fp[j], fin[n]), n
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
+def test_two_tile_inter_pass_equals_one_tile_bitwise(dk, dv):
+    # 40 sequences, 2 (V = 128) or 4 (V = 64) value heads: 320 one-tile inter workgroups, more
+    # than the 256 CUs and at most twice as many, so the batch runs the two-tile inter
+    # kernel; each sequence alone runs the one-tile one.  Same bits, and the batch within the
+    # tolerances of the oracle.
+    lens = [(i * 53) % 300 + 1 for i in range(40)]
+    hv = 2 if dv == 128 else 4
+    p = custom_problem(lens, hk=hv // 2, hv=hv, dk=dk, dv=dv, seed=27, with_state=True)
+    note(f"two-tile inter pass dk={dk} dv={dv}")
+    out, fin = check_fwd_full(p)[:2]
+    cu = p.cu_seqlens.tolist()
+    for n in [0, 7, 39]:
+        sl = slice(cu[n], cu[n + 1])
+        alone = Problem("alone", torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32),
+                        p.q[sl].contiguous(), p.k[sl].contiguous(), p.v[sl].contiguous(),
+                        p.g[sl].contiguous(), p.beta[sl].contiguous(), p.state[n:n + 1].clone())
+        oa, fa = gpu_fwd(alone)
+        assert torch.equal(oa, out[sl]), n
+        assert torch.equal(fa[0], fin[n]), n
+
+
 def test_repeat_calls_bitwise_identical():
     p = make_problem(2)
     note("repeat calls")
