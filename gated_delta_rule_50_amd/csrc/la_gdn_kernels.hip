@@ -831,17 +831,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             s2 += xch2(s2);
             if ((lane & 3) == 0) s_rq[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f) : 0.f;
         }
-        // ---- 2b: Gram tiles.  wave 0: G(0,0), P^T(0,0); wave 1: G(1,0); wave 2: G(1,1),
-        // P^T(1,1); wave 3: P^T(0,1) and the gate cumsum.  Tile (m, n): rows 32 m.., columns 32 n..
+        // ---- 2b: Gram tiles.  wave 0: G(0,0); wave 1: G(1,0); wave 2: G(1,1); P^T(0,0) on wave
+        // 1 (the reverse pass's operand mode: wave 0), P^T(1,1) on wave 2, P^T(0,1) on wave 3,
+        // which also scans the gate.  Tile (m, n): rows 32 m.., columns 32 n..  The forward's
+        // P^T tiles are scaled and stored by waves 1..3 while wave 0 inverts T's diagonal blocks.
         f32x16 Gt = {}, Pt = {}, Pq = {};
         const int gm = wave == 0 ? 0 : 1, gn = wave == 2 ? 1 : 0;   // G tile of waves 0..2
-        const int pm = wave == 2 ? 1 : 0, pn = wave == 0 ? 0 : 1;   // P^T tile of waves 0, 2, 3
+        const int pw = BW ? 1 : 0;                                   // the wave without a P^T tile
+        const int pm = wave == 2 ? 1 : 0, pn = wave < 2 ? 0 : 1;     // P^T tile of the others
         if (wave < 3) {
 #pragma unroll
             for (int s = 0; s < K / 16; ++s)
                 Gt = mfma32(lds_row8<PK>(sK, 32 * gm + c, 16 * s + 8 * hh), lds_row8<PK>(sK, 32 * gn + c, 16 * s + 8 * hh), Gt);
         }
-        if (FWD && WANT_V && wave != 1) {
+        if (FWD && WANT_V && wave != pw) {
 #pragma unroll
             for (int s = 0; s < K / 16; ++s)
                 Pt = mfma32(lds_row8<PK>(sK, 32 * pm + c, 16 * s + 8 * hh), lds_row8<PK>(sX, 32 * pn + c, 16 * s + 8 * hh), Pt);
@@ -952,9 +955,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int js = 0; js < 2; ++js)
                 w.PTF[(ch_h * 6 + 2 * (pm + pn) + js) * 64 + lane] = __builtin_bit_cast(uint4, pack32(pv, js));
         }
-        if (FWD && WANT_V && wave != 1) {
-            // P^T tile (pm, pn): lane (c, hh) holds column t = 32 pn + c, rows s = 32 pm + 8 j + 4 hh + i;
-            // registers 8 js .. 8 js + 7 are the B operand of token tile pn, step 2 pm + js
+        // P^T tile (pm, pn) scaled, masked and stored: lane (c, hh) holds column t = 32 pn + c,
+        // rows s = 32 pm + 8 j + 4 hh + i; registers 8 js .. 8 js + 7 are the B operand of token
+        // tile pn, step 2 pm + js
+        auto store_pt = [&]() {
             const int t = 32 * pn + c;
             const float gt = s_gam[t], rq = s_rq[t] * p.scale;
             f32x16 pv;
@@ -974,7 +978,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const int f = (pn == 0 ? 0 : 2) + 2 * pm + js;
                 st_op<NT>(reinterpret_cast<u32x4 *>(&w.PF[(ch_h * 6 + f) * 64 + lane]), __builtin_bit_cast(u32x4, pack32(pv, js)));
             }
-        }
+        };
+        if (BW && FWD && WANT_V && wave != pw) store_pt();
         lds_barrier();
 
         // ---- 3a: diagonal blocks D_b = (I + A_bb)^-1 (wave 0; lane 16 b + cc holds column cc of D_b)
@@ -1001,6 +1006,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) sAT[(o + i) * TS + o + cc] = x[i];
+        } else if (!BW && FWD && WANT_V) {
+            store_pt();
         }
         lds_barrier();
 
