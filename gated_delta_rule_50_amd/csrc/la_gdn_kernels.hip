@@ -889,7 +889,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         lds_barrier();
 
         // ---- 2c: v into q's space (every q read is done); per-token factors and the inter
-        // pass's scalars (wave 1); A^T (waves 0..2); P^T out (waves 0, 2, 3)
+        // pass's scalars; A^T (waves 0..2); the reverse pass's operand mode's P^T out
         if (!WANT_V) {
         } else if (!GDP)
             intra_load_tile<V>(sX, p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst, len,
@@ -898,7 +898,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             intra_load_urows<V>(sX, p.v + (int64_t)tb * p.vst + (int64_t)h * p.vsh, (int)p.vst, (int)p.vstu, phase,
                                 len, p.nh, p.inv_nh, wave, lane, 4);
         const float gl = s_gam[len - 1];
-        if (wave == 1) {
+        // the per-token factors and the inter pass's scalars: wave 3 in the forward (free
+        // here: its P^T tile is stored later), wave 1 in the reverse pass's operand mode
+        if (wave == (BW ? 1 : 3)) {
             const int t = lane;
             const float gm_t = s_gam[t], rk = s_rk[t];
             s_fw[t] = s_b[t] * exp2_hw(gm_t) * rk;
