@@ -306,12 +306,30 @@ __device__ __forceinline__ uint2 lds_tr(const void *p)
     return __builtin_bit_cast(uint2, r);
 }
 
+// The bf16 operand tiles (64 rows of PPR 16-byte pieces) keep piece j of row r in
+// slot j ^ swz_mask(r).  The LDS has 64 banks of 4 bytes, so a 256-byte row (PPR 16)
+// covers every bank once and a 128-byte row (PPR 8) half of them.  The mask makes
+// both access patterns conflict-free:
+//   row reads (one piece of 16 consecutive rows per 16 lanes): the mask is a
+//     bijection on those rows (with PPR 8, on the 8 rows of each parity);
+//   transposed reads (4 consecutive rows x 4 aligned pieces per 32 lanes): the 4
+//     rows' masks differ in the bits above the low two (with PPR 8, the two rows
+//     of each parity do), so the 16 (row, piece) pairs land in 16 distinct slots.
+// XOR by the row index alone (r % PPR) leaves the transposed reads 4-way conflicted.
+template <int PPR>
+__device__ __forceinline__ int swz_mask(int row)
+{
+    if constexpr (PPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else if constexpr (PPR == 8) return (((row >> 1) & 1) << 2) | (((row >> 3) & 1) << 1) | ((row >> 2) & 1);
+    else return row % PPR;
+}
+
 // Byte offset of element (row, col) (col a multiple of 4) in a 64 x (8 PPR) bf16
 // tile stored as 16-byte pieces with the piece index XOR-swizzled by the row.
 template <int PPR>
 __device__ __forceinline__ int swz(int row, int col)
 {
-    return (row * PPR + ((col >> 3) ^ (row % PPR))) * 16 + ((col & 7) >> 2) * 8;
+    return (row * PPR + ((col >> 3) ^ swz_mask<PPR>(row))) * 16 + ((col & 7) >> 2) * 8;
 }
 
 
@@ -565,7 +583,7 @@ __device__ __forceinline__ void intra_load_tile(lds_u32x4 *dst, const void *base
     const i32x4 r = make_rsrc(base, (uint32_t)len * rs);
     for (int i = wave; i < PPR; i += nw) {
         const int s = 64 * i + lane, row = s / PPR, pp = s % PPR;
-        b2l(r, dst, i, (uint32_t)row * rs + 16u * (uint32_t)(pp ^ (row % PPR)), 0);
+        b2l(r, dst, i, (uint32_t)row * rs + 16u * (uint32_t)(pp ^ swz_mask<PPR>(row)), 0);
     }
 }
 
@@ -583,7 +601,7 @@ __device__ __forceinline__ void intra_load_qrows(lds_u32x4 *dst, const void *bas
         const int s = 64 * i + lane, row = s / PPR, pp = s % PPR;
         const int u = start + row;
         const bool last = row < len && u % nh == nh - 1;
-        b2l(r, dst, i, last ? (uint32_t)(u / nh - tb) * rs + 16u * (uint32_t)(pp ^ (row % PPR)) : nrec, 0);
+        b2l(r, dst, i, last ? (uint32_t)(u / nh - tb) * rs + 16u * (uint32_t)(pp ^ swz_mask<PPR>(row)) : nrec, 0);
     }
 }
 
@@ -623,7 +641,7 @@ __device__ __forceinline__ void intra_load_urows(lds_u32x4 *dst, const __bf16 *t
     for (int i = wave; i < PPR; i += nw) {
         const int s = 64 * i + lane, row = s / PPR, pp = s % PPR;
         b2l(r, dst, i,
-            row < len ? 2u * upd_off(phase + row, nh, inv_nh, st, su) + 16u * (uint32_t)(pp ^ (row % PPR)) : nrec, 0);
+            row < len ? 2u * upd_off(phase + row, nh, inv_nh, st, su) + 16u * (uint32_t)(pp ^ swz_mask<PPR>(row)) : nrec, 0);
     }
 }
 
@@ -631,7 +649,7 @@ __device__ __forceinline__ void intra_load_urows(lds_u32x4 *dst, const __bf16 *t
 template <int PPR>
 __device__ __forceinline__ bf16x8 lds_row8(const lds_u32x4 *tile, int row, int c0)
 {
-    return __builtin_bit_cast(bf16x8, tile[row * PPR + ((c0 >> 3) ^ (row % PPR))]);
+    return __builtin_bit_cast(bf16x8, tile[row * PPR + ((c0 >> 3) ^ swz_mask<PPR>(row))]);
 }
 
 // Transposed reads from a swizzled bf16 tile M (64 rows, PPR pieces per row):
@@ -1487,13 +1505,13 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         // ------------------------------------------------------------ loader waves
         const int lh = wave - C::LW;
         // source offsets of this lane's 16-byte pieces of the k and q tiles (LDS piece
-        // (row, j) holds source piece j ^ (row % PPR) of the row)
+        // (row, j) holds source piece j ^ swz_mask(row) of the row)
         uint32_t qoff[C::NQ], koff[C::NKL];
         int kb[C::NKL], krow[C::NKL];
 #pragma unroll
         for (int i = 0; i < C::NKL; ++i) {
             const int s = (2 * i + lh) * 64 + lane;
-            const int row = s / C::PPR, pc = (s % C::PPR) ^ (row % C::PPR);
+            const int row = s / C::PPR, pc = (s % C::PPR) ^ swz_mask<C::PPR>(row);
             krow[i] = row;
             if (!GDP) {
                 kb[i] = 0;
@@ -2023,14 +2041,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
             const int sI = (2 * i + lh) * 64 + lane;
-            const int row = sI / PPR, pc = (sI % PPR) ^ (row % PPR);
+            const int row = sI / PPR, pc = (sI % PPR) ^ swz_mask<PPR>(row);
             koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
             qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int sI = (2 * i + lh) * 64 + lane;
-            const int row = sI / 4, pc = (sI % 4) ^ (row % 4);
+            const int row = sI / 4, pc = (sI % 4) ^ swz_mask<4>(row);
             doff[i] = (uint32_t)row * 2u * (uint32_t)p.ost + 16u * (uint32_t)pc;
         }
         const uint32_t lo16 = (uint32_t)lane * 16u;
