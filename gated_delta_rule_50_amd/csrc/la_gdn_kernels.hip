@@ -75,17 +75,18 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float bf2f(__bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ __bf16 f2bf(float x) { return static_cast<__bf16>(x); }
 
-// Sum of squares of the 8 bf16 values packed in a 16-byte word.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Sum of squares of the 8 bf16 values packed in a 16-byte word: four two-term bf16 dot
+// products (v_dot2c_f32_bf16) accumulated in fp32 (bf16 products are exact in fp32).
 __device__ __forceinline__ float sumsq8(uint4 u)
 {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(w[i] << 16);
-        const float hi = __uint_as_float(w[i] & 0xffff0000u);
-        s = fmaf(lo, lo, s);
-        s = fmaf(hi, hi, s);
+        const bf16x2 x = __builtin_bit_cast(bf16x2, w[i]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
     }
     return s;
 }
@@ -838,16 +839,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         vm_wait<0>();
         lds_barrier();
 
-        // ---- 2a: r_q from the q rows (16 rows per wave, 4 lanes per row)
-        if (FWD) {
+        // ---- 2a: r_q and r_k from the q and k rows (16 rows per wave, 4 lanes per row)
+        {
             const int row = 16 * wave + (lane >> 2);
-            float s2 = 0.f;
+            auto rnorm = [&](const lds_u32x4 *tile) {
+                float s2 = 0.f;
 #pragma unroll
-            for (int i = 0; i < PK / 4; ++i)
-                s2 += sumsq8(__builtin_bit_cast(uint4, lds_row8<PK>(sX, row, 8 * (4 * i + (lane & 3)))));
-            s2 += xch1(s2);
-            s2 += xch2(s2);
-            if ((lane & 3) == 0) s_rq[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f) : 0.f;
+                for (int i = 0; i < PK / 4; ++i)
+                    s2 += sumsq8(__builtin_bit_cast(uint4, lds_row8<PK>(tile, row, 8 * (4 * i + (lane & 3)))));
+                s2 += xch1(s2);
+                s2 += xch2(s2);
+                return row < len ? (p.l2norm ? 1.0f / sqrtf(s2 + 1e-6f) : 1.0f) : 0.f;
+            };
+            if (FWD) {
+                const float rq = rnorm(sX);
+                if ((lane & 3) == 0) s_rq[row] = rq;
+            }
+            const float rk = rnorm(sK);
+            if ((lane & 3) == 0) s_rk[row] = rk;
         }
         // ---- 2b: Gram tiles.  wave 0: G(0,0); wave 1: G(1,0); wave 2: G(1,1); P^T(0,0) on wave
         // 1 (the reverse pass's operand mode: wave 0), P^T(1,1) on wave 2, P^T(0,1) on wave 3,
@@ -893,16 +902,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 if (lm >= off) xg += y;
             }
             s_gam[lane] = xg;
-        }
-        // r_k from the diagonal of the diagonal G tiles: lane (c, hh) holds row c of its
-        // tile in register 4 j + i with 8 j + 4 hh + i = c
-        if (wave == 0 || wave == 2) {
-            float dg = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (8 * (e >> 2) + 4 * hm + (e & 3) == cm) dg = Gt[e];
-            const int row = 32 * gm + c;
-            if (((c >> 2) & 1) == hh) s_rk[row] = row < len ? (p.l2norm ? 1.0f / sqrtf(dg + 1e-6f) : 1.0f) : 0.f;
         }
         lds_barrier();
 
@@ -1153,17 +1152,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 if (more) issue_qgb(nxt);   // sX and the scalars are done with too
                 continue;
             }
+            // hi = bf16(x) two at a time (one conversion per pair), read back by a shift or a
+            // mask; lo = bf16(x - hi), x - hi being exact
             bf16x8 th[4], tl[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 float o[8];
                 trow(s, s_b, o);
+                u32x4 hv, lv;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const __bf16 hi = f2bf(o[e]);
-                    th[s][e] = hi;
-                    tl[s][e] = f2bf(o[e] - bf2f(hi));
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t hp = __builtin_bit_cast(uint32_t, bf16x2{f2bf(o[2 * e]), f2bf(o[2 * e + 1])});
+                    asm volatile("" : "+v"(hp));   // the low half by a shift, not a second conversion
+                    const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xffff0000u);
+                    hv[e] = hp;
+                    lv[e] = __builtin_bit_cast(uint32_t, bf16x2{f2bf(o[2 * e] - h0), f2bf(o[2 * e + 1] - h1)});
                 }
+                th[s] = __builtin_bit_cast(bf16x8, hv);
+                tl[s] = __builtin_bit_cast(bf16x8, lv);
             }
             constexpr int NU = (2 * (V / 32)) / 4;
 #pragma unroll
