@@ -1727,6 +1727,8 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     auto chunk_step = [&](int ci, StateOps &R) {
         const lds_u32x4 *eb = ebuf(ci);
         const lds_u32x4 *lb = (ci & 1) ? l1 : l0;
+        // (stored here, at the start of the step, not at the end of the previous one: stores
+        // issued after this wave's -W loads would be waited for with them at the loop head)
         if (CK && p.ck_fp32 && (kChunk * ci) % p.ck_every == 0) {
             const int64_t e = ck_base + (int64_t)kChunk * ci / p.ck_every;
             if (e < p.ck_cap) {
@@ -2110,6 +2112,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             D[r][e] = d_end ? d_end[(unit * K + row0 + 32 * r + 8 * (e >> 2) + 4 * hh + (e & 3)) * V + col] : 0.f;
+    // chunk cj's end-state gradient (dS as it enters chunk cj's step), for the backward's intra
+    // pass in the row-quad layout.  Stored at the end of chunk cj + 1's step (the last chunk's
+    // before the loop), when the loaders' operand loads have landed: stored at the start of the
+    // step, beside the loaders' next issue, the stores delayed those loads (dense batch 440 ->
+    // 398 us).
+    auto store_dsn = [&](int cj) {
+        if (FULL) {
+            float *dst = w.DSN + ((int64_t)(cid0 + cj) * p.HV + h) * K * V;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<f32x4 *>(dst + quad_off(row0 + 32 * r + 8 * j + 4 * hh, col, V)) =
+                        f32x4{D[r][4 * j], D[r][4 * j + 1], D[r][4 * j + 2], D[r][4 * j + 3]};
+        }
+    };
+    if (nch > 0) store_dsn(nch - 1);
     lds_barrier();
     for (int ci = nch - 1; ci >= 0; --ci) {
         const lds_u32x4 *eb = buf(ci);
@@ -2120,16 +2139,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bf16x8 Sb[NKS];
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) Sb[kk] = pack32(D[kk >> 1], kk & 1);
-        if (FULL) {
-            // this chunk's end-state gradient, for the backward's intra pass (row-quad layout)
-            float *dst = w.DSN + chh * K * V;
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<f32x4 *>(dst + quad_off(row0 + 32 * r + 8 * j + 4 * hh, col, V)) =
-                        f32x4{D[r][4 * j], D[r][4 * j + 1], D[r][4 * j + 2], D[r][4 * j + 3]};
-        }
         // Z[o] = K (token tile m = o ^ kh, keys of this half) dS_kh; A operands are k rows with the
         // keys in accumulator order (two 8-byte reads of the swizzled tile)
         f32x16 Z[2];
@@ -2191,8 +2200,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 xZ[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
                     __builtin_bit_cast(u32x4, f32x4{Z[o][4 * j], Z[o][4 * j + 1], Z[o][4 * j + 2], Z[o][4 * j + 3]});
         lds_barrier();                                        // B1
-        // dU = diag(d) (Z_0 + Z_1) + P^T dO for both token tiles; D += (-W)^T dU
-        bf16x8 Ub[4];
+        // dU = diag(d) (Z_0 + Z_1) + P^T dO for both token tiles (own tile first: only addresses
+        // depend on kh, never a register index); D += (-W)^T dU
+        bf16x8 Ub[2][2];
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
             const int m = o ^ kh;
@@ -2204,20 +2214,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) du[4 * j + e] = (Z[o][4 * j + e] + zo[e]) * dj[e] + Gz[o][4 * j + e];
             }
-            if (FULL && o == 0) {
-                // in bf16, the operand precision the backward's intra pass reads it in
-                __bf16 *dst = w.DU + (chh * 64 + 32 * m) * V + col;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) dst[(int64_t)(8 * (e >> 2) + 4 * hh + (e & 3)) * V] = f2bf(du[e]);
-            }
-            Ub[2 * m] = pack32(du, 0);
-            Ub[2 * m + 1] = pack32(du, 1);
+            Ub[o][0] = pack32(du, 0);
+            Ub[o][1] = pack32(du, 1);
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int ts = 0; ts < 4; ++ts)
-                D[r] = mfma32(__builtin_bit_cast(bf16x8, eb[(oWT + (kh * NR + r) * 4 + ts) * 64 + lane]), Ub[ts], D[r]);
+            for (int o = 0; o < 2; ++o)
+#pragma unroll
+                for (int js = 0; js < 2; ++js)
+                    D[r] = mfma32(__builtin_bit_cast(bf16x8, eb[(oWT + (kh * NR + r) * 4 + 2 * (o ^ kh) + js) * 64 + lane]),
+                                  Ub[o][js], D[r]);
+        if (FULL) {
+            // dU of this wave's token tile in bf16 (the operand precision the backward's intra
+            // pass reads it in), from its packed operands, at the end of the step like dS
+            __bf16 *dst = w.DU + (chh * 64 + 32 * kh) * V + col;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dst[(int64_t)(8 * (e >> 2) + 4 * hh + (e & 3)) * V] = Ub[0][e >> 3][e & 7];
+        }
+        if (ci >= 1) store_dsn(ci - 1);
         lds_barrier();                                        // B2
     }
 #pragma unroll
