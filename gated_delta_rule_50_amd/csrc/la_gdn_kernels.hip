@@ -1390,10 +1390,17 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
 
 // Output wave t: O^T of its token tile of the chunk whose Y^T it holds, stored
 // to o.  Lane (c, hh) holds value columns 8 j + 4 hh .. + 3 of token 32 t + c.
+// One output tile, computed and held until its store (so that the store can be issued
+// away from the loaders' operand loads).
+struct OutTile {
+    uint2 v[4];
+    __bf16 *ob;       // row start of this lane's 8-column group, or null (no row)
+};
+
 template <int K, int V, bool SUMMARY, bool GDP>
-__device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU, const f32x16 &Y, const bf16x8 (&Pf)[4],
-                                             float sq, int t, int o_start, int o_len, const InterCtx<K, V, SUMMARY> &x,
-                                             int vt)
+__device__ __forceinline__ OutTile inter_output(const Prob &p, const lds_u32x4 *xU, const f32x16 &Y, const bf16x8 (&Pf)[4],
+                                                float sq, int t, int o_start, int o_len, const InterCtx<K, V, SUMMARY> &x,
+                                                int vt)
 {
     const int lane = x.lane, c = lane & 31, hh = lane >> 5;
     f32x16 O;
@@ -1413,14 +1420,22 @@ __device__ __forceinline__ void inter_output(const Prob &p, const lds_u32x4 *xU,
         if (!GDP) orow = u;
         else if (u % p.nh == p.nh - 1) orow = u / p.nh;
     }
-    if (orow >= 0) {
-        __bf16 *ob = p.o + (int64_t)orow * p.ost + (int64_t)x.h * p.osh + 32 * vt + 4 * hh;
+    OutTile r;
+    r.ob = orow >= 0 ? p.o + (int64_t)orow * p.ost + (int64_t)x.h * p.osh + 32 * vt + 4 * hh : nullptr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f32x4 o4 = {O[4 * j], O[4 * j + 1], O[4 * j + 2], O[4 * j + 3]};
-            const uint4 u = __builtin_bit_cast(uint4, pack_b(o4, o4));
-            *reinterpret_cast<uint2 *>(ob + 8 * j) = make_uint2(u.x, u.y);
-        }
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 o4 = {O[4 * j], O[4 * j + 1], O[4 * j + 2], O[4 * j + 3]};
+        const uint4 w4 = __builtin_bit_cast(uint4, pack_b(o4, o4));
+        r.v[j] = make_uint2(w4.x, w4.y);
+    }
+    return r;
+}
+
+__device__ __forceinline__ void store_out(const OutTile &r)
+{
+    if (r.ob) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2 *>(r.ob + 8 * j) = r.v[j];
     }
 }
 
@@ -1606,15 +1621,23 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         bf16x8 Pf[4];
         float sq = 0.f;
         int o_start = 0, o_len = 0;
+        // With two tiles per workgroup the output tiles are stored at the end of the step, away
+        // from the loaders' operand loads issued at its start (dense batch: k_inter_wide 160 ->
+        // 148 us); with one tile, where the step is shorter, right away (the varlen batch's
+        // k_inter measured 34.3 -> 35.3 us the other way).
+        constexpr bool LATE = TP > 1;
+        OutTile ot[TP];
         lds_barrier();
         for (int ci = 0; ci < nch; ++ci) {
             const lds_u32x4 *eb = ebuf(ci);
             // the previous chunk's output (its U_new was published before the last B2)
             if (ci > 0) {
 #pragma unroll
-                for (int tp = 0; tp < TP; ++tp)
-                    inter_output<K, V, SUMMARY, GDP>(p, xU + tp * 4 * 64, Y[tp], Pf, sq, t, o_start, o_len, x,
-                                                     x.vt0 + tp);
+                for (int tp = 0; tp < TP; ++tp) {
+                    ot[tp] = inter_output<K, V, SUMMARY, GDP>(p, xU + tp * 4 * 64, Y[tp], Pf, sq, t, o_start, o_len, x,
+                                                              x.vt0 + tp);
+                    if (!LATE) store_out(ot[tp]);
+                }
             }
             lds_barrier();                                    // B1: S of chunk ci is published
             // operands of chunk ci (they stay in their buffer until the next chunk
@@ -1661,6 +1684,10 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
                     }
                 }
             }
+            if (LATE && ci > 0) {
+#pragma unroll
+                for (int tp = 0; tp < TP; ++tp) store_out(ot[tp]);
+            }
             o_start = x.seq_start + kChunk * ci;
             o_len = min(kChunk, x.seq_len - kChunk * ci);
             lds_barrier();                                    // B2: U_new of chunk ci is published
@@ -1668,7 +1695,8 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
         if (nch > 0) {
 #pragma unroll
             for (int tp = 0; tp < TP; ++tp)
-                inter_output<K, V, SUMMARY, GDP>(p, xU + tp * 4 * 64, Y[tp], Pf, sq, t, o_start, o_len, x, x.vt0 + tp);
+                store_out(inter_output<K, V, SUMMARY, GDP>(p, xU + tp * 4 * 64, Y[tp], Pf, sq, t, o_start, o_len, x,
+                                                           x.vt0 + tp));
         }
         return;
     }
