@@ -1891,8 +1891,9 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     }
 }
 
-// The forward's workgroup (6 waves) takes 153 KiB of LDS at K = V = 128, one per CU.
-// The summary's (4 waves: no output waves) takes 75 KiB, two per CU.
+// The forward's workgroup (6 waves) takes 141 KiB of LDS at K = V = 128, one per CU (the
+// two-tile one, 8 waves, 150 KiB).  The summary's (4 waves: no output waves) takes 63 KiB,
+// two per CU.
 template <int K, int V>
 __global__ __launch_bounds__(384) void k_inter(Prob p, Ws w)
 {
