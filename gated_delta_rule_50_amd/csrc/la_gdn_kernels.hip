@@ -1243,9 +1243,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // the decayed erase steps; there are no outputs and no output waves (the loader
 // waves are waves 2, 3).
 
-template <int K, int V, bool SUMMARY, int TP = 1>
+template <int K, int V, bool SUMMARY, int TP = 1, bool NOOUT = false>
 struct InterCfg {
     static constexpr bool FWD = !SUMMARY;
+    static constexpr bool OUT = FWD && !NOOUT;    // output waves and their operands (q, P^T)
     static constexpr int VA = SUMMARY ? V + K : V;
     static constexpr int NT = VA / (32 * TP);     // workgroups (TP 32-column tiles each) per (sequence, head)
     static constexpr int KH = K / 2;              // state rows per state wave
@@ -1258,7 +1259,7 @@ struct InterCfg {
     // bf16, pieces swizzled by row) in its own array; raw q (same layout), P^T (tile
     // 0 steps 0..1, tile 1 steps 0..3) and the scalars (d[64], sq[64], 2^(gam_n) at
     // 192) in the other.
-    static constexpr int FW = 4 * NKS, FU = 4 * TP, FQ = FWD ? K / 8 : 0, FP = FWD ? 6 : 0, FS = 1;
+    static constexpr int FW = 4 * NKS, FU = 4 * TP, FQ = OUT ? K / 8 : 0, FP = OUT ? 6 : 0, FS = 1;
     static constexpr int oU = 0, oQ = oU + FU, oP = oQ + FQ, oS = oP + FP, NFE = oS + FS;
     static constexpr int FK = K / 8, oK = 0, NFL = FK;
     static constexpr int NKL = FK / 2;            // k tile loads per loader wave
@@ -1266,7 +1267,7 @@ struct InterCfg {
     // then the two loader waves; the summary has no outputs, so its workgroup is 4 waves and
     // two fit on a CU
     static constexpr int SW = 2 * TP;             // state waves
-    static constexpr int LW = FWD ? SW + 2 : SW;  // first loader wave
+    static constexpr int LW = OUT ? SW + 2 : SW;  // first loader wave
     static constexpr int THREADS = 64 * (LW + 2);
     static constexpr int NQ = NKL;                // q tile loads per loader wave (forward)
 };
@@ -1338,11 +1339,11 @@ __device__ __forceinline__ int inter_issue_output(const Prob &p, const Ws &w, ld
                                                   const int (&kb)[InterCfg<K, V, SUMMARY>::NKL],
                                                   const int (&krow)[InterCfg<K, V, SUMMARY>::NKL], UCursor cur)
 {
-    using C = InterCfg<K, V, SUMMARY, TP>;
+    using C = InterCfg<K, V, SUMMARY, TP, NOOUT>;
     const int64_t chh = (int64_t)(x.cid0 + ci) * p.HV + x.h;
     const uint32_t lo16 = (uint32_t)x.lane * 16u;
     int n = 0;
-    if (C::FWD && !NOOUT) {
+    if (C::OUT) {
         const int start = x.seq_start + kChunk * ci, len = min(kChunk, x.seq_len - kChunk * ci);
         if (!GDP) {
             const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)x.hk * p.qsh,
@@ -1461,7 +1462,7 @@ __device__ __forceinline__ UnitOfBlock unit_of_block(const Prob &p, const Ws &w,
 }
 
 // NOOUT (with CK, fp32 rows): the states only, no outputs (the backward's run of the forward):
-// the output waves take part in the barriers only, the loaders skip q and P^T.
+// no output waves (the loaders are waves 2, 3, as in the summary) and no q or P^T.
 // TP = 2 (the plain forward at large batch): two 32-column tiles per workgroup, so that a
 // batch needs half the workgroups, with four state waves (key half x tile), the output waves
 // covering both tiles, and the output operands double- instead of triple-buffered (LDS).
@@ -1470,14 +1471,14 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     static_assert(!NOOUT || (CK && !SUMMARY && !GDP), "states only: the forward with the fp32 series");
     static_assert(TP == 1 || (!SUMMARY && !CK && !GDP && !NOOUT), "two tiles per workgroup: the plain forward");
-    using C = InterCfg<K, V, SUMMARY, TP>;
+    using C = InterCfg<K, V, SUMMARY, TP, NOOUT>;
     constexpr int NR = C::NR, NKS = C::NKS;
     constexpr int NEB = TP == 1 ? 3 : 2;                   // output-operand buffers
     __shared__ u32x4 sE0[C::NFE * 64], sE1[C::NFE * 64], sE2[NEB == 3 ? C::NFE * 64 : 1];   // q, U~, P^T, scalars
     __shared__ u32x4 sL0[C::NFL * 64], sL1[C::NFL * 64];   // raw k: two buffers
     __shared__ u32x4 sX[TP * 2 * 8 * 64];                  // X partials: [tile][kh][m][j][lane]
-    __shared__ u32x4 sS[C::FWD ? TP * 2 * NKS * 64 : 1];   // S (bf16 operands): [tile][kh][step][lane]
-    __shared__ u32x4 sU[C::FWD ? TP * 4 * 64 : 1];         // U_new (bf16 operands): [tile][token step][lane]
+    __shared__ u32x4 sS[C::OUT ? TP * 2 * NKS * 64 : 1];   // S (bf16 operands): [tile][kh][step][lane]
+    __shared__ u32x4 sU[C::OUT ? TP * 4 * 64 : 1];         // U_new (bf16 operands): [tile][token step][lane]
     lds_u32x4 *const e0 = (lds_u32x4 *)sE0, *const e1 = (lds_u32x4 *)sE1, *const e2 = (lds_u32x4 *)sE2;
     auto ebuf = [&](int c) {
         if (NEB == 2) return (c & 1) ? e1 : e0;
@@ -1537,12 +1538,12 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             if (!GDP) {
                 kb[i] = 0;
                 koff[i] = (uint32_t)row * 2u * (uint32_t)p.kst + 16u * (uint32_t)pc;
-                if (C::FWD) qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
+                if (C::OUT) qoff[i] = (uint32_t)row * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
             } else {
                 const int a = row / p.nh;
                 kb[i] = row - a * p.nh;
                 koff[i] = 2u * (uint32_t)(a * (int)p.kst + kb[i] * (int)p.kstu) + 16u * (uint32_t)pc;
-                if (C::FWD) qoff[i] = (uint32_t)a * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
+                if (C::OUT) qoff[i] = (uint32_t)a * 2u * (uint32_t)p.qst + 16u * (uint32_t)pc;
             }
         }
         // Gated Delta Product: the cursor of the next chunk to issue (chunk 0 starts at the
@@ -1605,16 +1606,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     }
 
     lds_u32x4 *const xX = (lds_u32x4 *)sX, *const xS = (lds_u32x4 *)sS, *const xU = (lds_u32x4 *)sU;
-    if (NOOUT && wave >= C::SW) {
-        // the output waves' barriers, nothing else
-        lds_barrier();
-        for (int ci = 0; ci < nch; ++ci) {
-            lds_barrier();                                    // B1
-            lds_barrier();                                    // B2
-        }
-        return;
-    }
-    if (C::FWD && wave >= C::SW) {
+    if (C::OUT && wave >= C::SW) {
         // ------------------------------------------------------------ output waves
         const int t = wave - C::SW;
         f32x16 Y[TP] = {};
@@ -1808,7 +1800,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 #pragma unroll
         for (int kk = 0; kk < NKS; ++kk) {
             Sb[kk] = pack32(S[kk >> 1], kk & 1);
-            if (C::FWD && !NOOUT) tS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
+            if (C::OUT) tS[(kh * NKS + kk) * 64 + lane] = __builtin_bit_cast(u32x4, Sb[kk]);
         }
         // ---- X_kh = [U~] + (-W)_kh S_kh, published for the other state wave
 #pragma unroll
@@ -1852,7 +1844,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
             }
             Ud[2 * o] = pack32(ud, 0);
             Ud[2 * o + 1] = pack32(ud, 1);
-            if (C::FWD && !NOOUT && o == 0) {
+            if (C::OUT && o == 0) {
                 tU[(2 * kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 0));
                 tU[(2 * kh + 1) * 64 + lane] = __builtin_bit_cast(u32x4, pack32(un, 1));
             }
@@ -1926,10 +1918,12 @@ __global__ __launch_bounds__(384) void k_inter_ck(Prob p, Ws w)
     inter_body<K, V, false, true>(p, w);
 }
 
-// The backward's run of the forward: the fp32 state at every chunk start, no outputs.
+// The backward's run of the forward: the fp32 state at every chunk start, no outputs, so no
+// output waves and no q or P^T buffers (4 waves, 63 KiB of LDS at K = V = 128: two per CU).
 template <int K, int V>
-__global__ __launch_bounds__(384) void k_inter_states(Prob p, Ws w)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_inter_states(Prob p, Ws w)
 {
+    static_assert(InterCfg<K, V, false, 1, true>::THREADS == 256, "states only: 4 waves");
     inter_body<K, V, false, true, false, true>(p, w);
 }
 
@@ -2941,7 +2935,7 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
         after(LA_KERNEL_INTRA);                                                                                \
         before(LA_KERNEL_INTER);                                                                               \
         if (!a.chunk_states)                                                                                   \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_states<KK, VV>), dim3(inter_blocks), dim3(384), 0, s, pf, w); \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_states<KK, VV>), dim3(inter_blocks), dim3(256), 0, s, pf, w); \
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true>), dim3(inter_blocks), dim3(256), 0, s, p, w, \
                            a.d_out, a.d_final, a.d_init);                                                      \
         after(LA_KERNEL_INTER);                                                                                \
