@@ -669,6 +669,31 @@ __device__ __forceinline__ bf16x8 lds_tr32s(const lds_u32x4 *tile, int t0, int c
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
+// lds_tr32s<PPR, true> with the lane's part of the two addresses precomputed: for t0 a
+// multiple of 16 and c0 a multiple of 32, the swizzle mask depends on the lane's row within
+// 16 only, and the piece index (c0 / 8 + x) ^ mask splits into a part of c0 and one of the
+// lane, so the byte offset is tr_lane_off(...) + 16 PPR t0.  Returns the two offsets.
+template <int PPR>
+__device__ __forceinline__ uint2 tr_lane_off(int c0, int lane)
+{
+    const int lam = lane & 15, hh = lane >> 5;
+    const int x = 2 * ((lane >> 4) & 1) + ((lam & 3) >> 1), h8 = 8 * (lam & 1);
+    uint32_t off[2];
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+        const int rr = 4 * hh + (lam >> 2) + 8 * part;      // the row within 16 (accumulator order)
+        const int piece = ((c0 >> 3) | x) ^ swz_mask<PPR>(rr);
+        off[part] = (uint32_t)((rr * PPR + piece) * 16 + h8);
+    }
+    return make_uint2(off[0], off[1]);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr32s_at(const lds_char *b, uint2 off)
+{
+    const uint2 lo = lds_tr(b + off.x), hi = lds_tr(b + off.y);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -1702,6 +1727,15 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     // this wave's tile's X partials, S and U_new operands
     lds_u32x4 *const tX = xX + tp * 2 * 8 * 64, *const tS = xS + tp * 2 * NKS * 64, *const tU = xU + tp * 4 * 64;
     const int row0 = kh * C::KH;                        // first state row of this wave
+    // the lane's part of the K^T transpose-read addresses (the chunk's token step adds a
+    // uniform 16 PPR t0), computed once instead of in every chunk step (about 50 fewer VALU
+    // instructions per step on the chain and 12 fewer VGPRs; k_inter 34.2 -> 34.0 us at the
+    // varlen workload, k_inter_sum 1427 -> 1413 us at the summary one).  The kernel with the
+    // fp32 series measured 49.8 -> 51.5 us that way and keeps the per-step form.
+    constexpr bool KTR = !CK;
+    uint2 ktr[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) ktr[r] = tr_lane_off<C::PPR>(row0 + 32 * r, lane);
     const int64_t unit = (int64_t)n * p.HV + h;
     f32x16 S[NR];
     if (!x.ptile) {
@@ -1779,7 +1813,9 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 #pragma unroll
                 for (int js = 0; js < 2; ++js)
                     Kf[r][2 * o + js] =
-                        lds_tr32s<C::PPR, true>(lb + C::oK * 64, 16 * (2 * (o ^ kh) + js), row0 + 32 * r, lane);
+                        KTR ? lds_tr32s_at(reinterpret_cast<const lds_char *>(lb + C::oK * 64) +
+                                               16 * C::PPR * 16 * (2 * (o ^ kh) + js), ktr[r])
+                            : lds_tr32s<C::PPR, true>(lb + C::oK * 64, 16 * (2 * (o ^ kh) + js), row0 + 32 * r, lane);
         // U~ enters through the accumulator of the wave whose token tile it is
         f32x16 X[2];
         X[1] = f32x16{};
