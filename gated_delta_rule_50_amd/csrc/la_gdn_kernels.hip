@@ -2467,6 +2467,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         len = __builtin_amdgcn_readfirstlane(ch.z);
     }
     const int64_t chh = (int64_t)ci * p.HV + h;
+    // With several rounds of items (one workgroup per CU), the first round starts in 8 phases
+    // about an eighth of an item apart (blocks 8 apart share an XCD, so each XCD gets every
+    // phase): the CUs then run their items back to back out of step, instead of all issuing
+    // their ~200 KiB of stage-A loads at the same moment of every round.  At K = V = 128
+    // (about 34 us per item) the phase step is 127 x 64 clocks: varlen backward 168 -> 152 us,
+    // dense batch 1081 -> 1019 us (8 phases of 64 x 64 clocks gained less, 16 or 32 phases of
+    // 127 x 64 clocks lost part of it again).  Single-round launches start at once.
+    if ((int)gridDim.x > 2 * (p.intra_grid / 3) && (int)blockIdx.x < p.intra_grid / 3) {
+        constexpr int STEP = K * V >= 16384 ? 127 : (K * V >= 8192 ? 64 : 32);
+        const int ph = ((int)blockIdx.x >> 3) & 7;
+        for (int i = 0; i < ph; ++i) __builtin_amdgcn_s_sleep(STEP);
+    }
 
     // ---- stage A loads: k, dO and dU rows (buffer loads into LDS), the scalars, S0 and dS
     intra_load_tile<K>((lds_u32x4 *)(L + oK), p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst,
