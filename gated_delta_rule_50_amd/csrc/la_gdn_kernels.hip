@@ -2365,6 +2365,21 @@ __device__ __forceinline__ float lds_elem(const lds_char *tile, int row, int col
     return bf2f(*reinterpret_cast<const lds_bf16 *>(tile + swz_e<PPR>(row, col)));
 }
 
+// The 16 elements of a swizzled bf16 tile that an accumulator lane (c, hh) holds of a 32 x 32
+// block (rows r0 + 8 j + 4 hh + i in register 4 j + i, column c0 + c; r0 and c0 multiples of
+// 32): two transposed reads in accumulator order instead of 16 two-byte reads.
+template <int PPR>
+__device__ __forceinline__ void acc_elems(const lds_char *tile, int r0, int c0, int lane, float (&x)[16])
+{
+    const bf16x8 a = lds_tr32s<PPR, true>(reinterpret_cast<const lds_u32x4 *>(tile), r0, c0, lane);
+    const bf16x8 b = lds_tr32s<PPR, true>(reinterpret_cast<const lds_u32x4 *>(tile), r0 + 16, c0, lane);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = bf2f(a[e]);
+        x[8 + e] = bf2f(b[e]);
+    }
+}
+
 // The backward intra pass's fp32 operands S0 (row-major, or in the row-quad layout for
 // S0_QUAD) and dS (row-quad layout) into swizzled bf16 tiles, by the 256 threads of the block
 // in 4 x 4 blocks (four 16-byte loads of each matrix per block), with every load issued
@@ -2566,11 +2581,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int s = 0; s < VS; ++s)
                 a = mfma32(lds_row8<PV>(tU, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PV>(tDS, 32 * kt + c, 16 * s + 8 * hh), a);
+            float xk[16];
+            acc_elems<PK>(L + oK, 32 * tm, 32 * kt, lane, xk);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
                 a[e] *= s_dd[row];
-                prod[e] += a[e] * lds_elem<PK>(L + oK, row, 32 * kt + c);
+                prod[e] += a[e] * xk[e];
             }
             dK[i] = a;
         }
@@ -2606,10 +2623,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i)
+        for (int i = 0; i < NKT / 2; ++i) {
+            float xq_[16];
+            acc_elems<PK>(L + oQ, 32 * tm, 32 * (half + 2 * i), lane, xq_);
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                prod[e] += dQ[i][e] * lds_elem<PK>(L + oQ, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
+            for (int e = 0; e < 16; ++e) prod[e] += dQ[i][e] * xq_[e];
+        }
         {
             const float r = rowsum32(prod, lane);
             const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
@@ -2668,10 +2687,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int st = 0; st < 4; ++st)
                 a = mfma32(lds_tr32s<8, false>(tT, 16 * st, 32 * tm, lane), lds_tr32s<PV, false>(tDU, 16 * st, 32 * vt, lane), a);
+            float xv[16];
+            acc_elems<PV>(L + oVv, 32 * tm, 32 * vt, lane, xv);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-                prod[e] += a[e] * lds_elem<PV>(L + oVv, row, 32 * vt + c);
+                prod[e] += a[e] * xv[e];
                 if (row < len) dv_out[((int64_t)(start + row) * p.HV + h) * V + 32 * vt + c] = s_b[row] * a[e];
             }
         }
@@ -2691,10 +2712,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int st = 0; st < 4; ++st)
                 a = mfma32(lds_tr32s<8, false>(tT, 16 * st, 32 * tm, lane), lds_tr32s<PK, false>(tDW, 16 * st, 32 * kt, lane), a);
+            float xk[16];
+            acc_elems<PK>(L + oK, 32 * tm, 32 * kt, lane, xk);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-                prod[e] += a[e] * lds_elem<PK>(L + oK, row, 32 * kt + c);
+                prod[e] += a[e] * xk[e];
                 dK[i][e] += s_b[row] * s_eg[row] * a[e];
             }
         }
@@ -2722,13 +2745,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (fuse_qk) {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i)
+        for (int i = 0; i < NKT / 2; ++i) {
+            float x[16];
+            acc_elems<PK>(L + oQ, 32 * tm, 32 * (half + 2 * i), lane, x);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float x = lds_elem<PK>(L + oQ, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
-                xq[i][e] = f2bf(x);   // x is a bf16 value: exact
-                prod[e] += dQ[i][e] * x;
+                xq[i][e] = f2bf(x[e]);   // x is a bf16 value: exact
+                prod[e] += dQ[i][e] * x[e];
             }
+        }
         const float r = rowsum32(prod, lane);
         const int e = c >> 1;
         if ((c & 1) == 0) part[QD][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
@@ -2810,10 +2835,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (fuse_qk) {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i)
+        for (int i = 0; i < NKT / 2; ++i) {
+            float xk[16];
+            acc_elems<PK>(L + oK, 32 * tm, 32 * (half + 2 * i), lane, xk);
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                prod[e] += dK[i][e] * lds_elem<PK>(L + oK, 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3), 32 * (half + 2 * i) + c);
+            for (int e = 0; e < 16; ++e) prod[e] += dK[i][e] * xk[e];
+        }
         const float r = rowsum32(prod, lane);
         const int e = c >> 1;
         if ((c & 1) == 0) part[KD][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
@@ -2834,11 +2861,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < NKT / 2; ++i) {
             const int col = 32 * (half + 2 * i) + c;
+            float xks[16];
+            acc_elems<PK>(L + oK, 32 * tm, 32 * (half + 2 * i), lane, xks);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
                 if (row < len) {
-                    const float xk = lds_elem<PK>(L + oK, row, col);
+                    const float xk = xks[e];
                     const int64_t at = ((int64_t)(start + row) * p.HK + hk) * K + col;
                     dq_out[at] = p.scale * (rq[e] * dQ[i][e] - cq[e] * bf2f(xq[i][e]));
                     dk_out[at] = rk[e] * dK[i][e] - ck[e] * xk;
