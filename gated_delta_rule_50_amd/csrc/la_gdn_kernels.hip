@@ -2317,7 +2317,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // state update's 2^(gam_n - gam) and 2^gam_n), summed back to g in reverse token order.
 // The q^ and k^ gradients go out per value head (fp32); k_bwd_qk sums each head group and
 // applies the row norms.  All products are bf16 MFMA with fp32 accumulation; each wave owns
-// token tile (wave & 1) and the column tiles (wave >> 1) + 2 i of every 64-row result.
+// token tile (wave & 1) and the column tiles (wave >> 1) + 2 i of every 64-row result.  At
+// K = V = 128 the workgroup is 8 waves (two per SIMD, the only workgroup on its CU): waves w
+// and w + 4 split the K- and V-wide products by column tile and take the 64 x 64 ones
+// (dT and Y; dP, P, the Gram tile and dA) by product, so that a phase's chain of dependent
+// LDS reads and products is about half as long per wave.
 // Stage A holds S0 and dS in LDS (bf16); stage B reuses that space for q, v, T and the
 // masked dP tiles; stage C for dT T^T and the dA tiles.
 
@@ -2381,18 +2385,19 @@ __device__ __forceinline__ void acc_elems(const lds_char *tile, int r0, int c0, 
 }
 
 // The backward intra pass's fp32 operands S0 (row-major, or in the row-quad layout for
-// S0_QUAD) and dS (row-quad layout) into swizzled bf16 tiles, by the 256 threads of the block
+// S0_QUAD) and dS (row-quad layout) into swizzled bf16 tiles, by the NT threads of the block
 // in 4 x 4 blocks (four 16-byte loads of each matrix per block), with every load issued
 // before the first is used (one memory latency instead of one per batch).  Returns the
 // thread's share of sum(S0 * dS), summed in the same order for either S0 layout.
-template <int K, int V, bool S0_QUAD>
+template <int K, int V, bool S0_QUAD, int NT>
 __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, lds_char *dDS, const float *DS, int tid)
 {
-    constexpr int PPR = V / 8, NB = K * V / 16 / 256;
+    constexpr int PPR = V / 8, NB = K * V / 16 / NT;
+    static_assert(NB * NT * 16 == K * V, "whole 4 x 4 blocks per thread");
     float4 a[NB][4], b[NB][4];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-        const int blk = tid + 256 * j, rq = blk / (V / 4), c4 = 4 * (blk % (V / 4));
+        const int blk = tid + NT * j, rq = blk / (V / 4), c4 = 4 * (blk % (V / 4));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             // S0_QUAD: column c4 + u, rows 4 rq .. 4 rq + 3; else row 4 rq + u, columns c4 .. c4 + 3
@@ -2405,7 +2410,7 @@ __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, ld
     float dot = 0.f;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-        const int blk = tid + 256 * j, rq = blk / (V / 4), c4 = 4 * (blk % (V / 4));
+        const int blk = tid + NT * j, rq = blk / (V / 4), c4 = 4 * (blk % (V / 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float s[4], d[4];
@@ -2423,11 +2428,15 @@ __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, ld
     return dot;
 }
 
-template <int K, int V>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_intra(
+template <int K, int V, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_bwd_intra(
     Prob p, Ws w, const __bf16 *d_out, float *dv_out, float *dg_out, float *db_out, float *dq_out, float *dk_out)
 {
     constexpr int PK = K / 8, PV = V / 8, NKT = K / 32, NVT = V / 32, KS = K / 16, VS = V / 16;
+    // NW = 8: two waves per (token tile, column tile) pair, which split the K- and V-wide
+    // products by column tile (IK, IV per wave) and share the 64 x 64 ones by product
+    static_assert(NW == 4 || (NW == 8 && NKT % 4 == 0 && NVT % 4 == 0), "4 waves, or 8 with 4k column tiles");
+    constexpr int NQ = NW / 4, IK = NKT / (2 * NQ), IV = NVT / (2 * NQ);
     constexpr int NKS = K / 32;                             // steps of 16 keys per key half (-W fragments)
     constexpr int szK = 64 * K * 2, szV = 64 * V * 2, sz64 = 64 * 64 * 2, szS = K * V * 2;
     constexpr int R1B = 2 * szS > szK + szV + 4 * sz64 ? 2 * szS : szK + szV + 4 * sz64;
@@ -2439,8 +2448,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     enum { XV, DF, DAEG, AAR, AAC, PPR_, PPC, QX, KX, QD, KD, NPART };
     __shared__ __attribute__((aligned(16))) char smem[oEnd];
     __shared__ __attribute__((aligned(16))) float ssc[6 * 64];   // gam2, r_k, r_q, beta, 2^gam, 2^(gam_n - gam)
-    __shared__ float part[NPART][2][64];
-    __shared__ float sdot[4];
+    __shared__ float part[NPART][2 * NQ][64];   // per-token partial sums: [column tile half + 2 qw] or [tile]
+    __shared__ float sdot[NW];
     lds_char *const L = (lds_char *)smem;
     const lds_u32x4 *const tK = (const lds_u32x4 *)(L + oK);
     const lds_u32x4 *const tDO = (const lds_u32x4 *)(L + oDO);
@@ -2464,7 +2473,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (w.hdr[0] != LA_DEVICE_OK) return;
     const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tm = wave & 1, half = wave >> 1;
+    const int tm = wave & 1, half = (wave >> 1) & 1, qw = wave >> 2, pw = half + 2 * qw;
+    // 64 x 64 products: dT (A5, B3) and Y (C1) on the waves with qw = 0, dP (B1, B2), the
+    // Gram tile and dA (C2) on those with qw = 1 (all on the one set of 4 waves for NW = 4)
+    const bool wT = NQ == 1 || qw == 0, wP = NQ == 1 || qw == 1;
+    // the wave's i-th column tile of a K- or V-wide result
+    auto ctile = [&](int i) { return half + 2 * (NQ * i + qw); };
     // the item: chunk ci of the chunk table, value head h
     const int ci = blockIdx.x / p.HV, h = blockIdx.x % p.HV, hk = h / (p.HV / p.HK);
     int start, len;
@@ -2485,32 +2499,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // With several rounds of items (one workgroup per CU), the first round starts in 8 phases
     // about an eighth of an item apart (blocks 8 apart share an XCD, so each XCD gets every
     // phase): the CUs then run their items back to back out of step, instead of all issuing
-    // their ~200 KiB of stage-A loads at the same moment of every round.  At K = V = 128
-    // (about 34 us per item) the phase step is 127 x 64 clocks: varlen backward 168 -> 152 us,
-    // dense batch 1081 -> 1019 us (8 phases of 64 x 64 clocks gained less, 16 or 32 phases of
-    // 127 x 64 clocks lost part of it again).  Single-round launches start at once.
+    // their ~200 KiB of stage-A loads at the same moment of every round.  With 4 waves at
+    // K = V = 128 (about 34 us per item) a phase step of 127 x 64 clocks took the varlen
+    // backward from 168 to 152 us and the dense batch from 1081 to 1019 us (8 phases of 64 x 64
+    // clocks gained less, 16 or 32 phases of 127 x 64 clocks lost part of it again); the
+    // 8-wave items (about 25 us) take 96 x 64 (64: 132 -> 124 us varlen; 127 or 160: slower).
+    // Single-round launches start at once.
     if ((int)gridDim.x > 2 * (p.intra_grid / 3) && (int)blockIdx.x < p.intra_grid / 3) {
-        constexpr int STEP = K * V >= 16384 ? 127 : (K * V >= 8192 ? 64 : 32);
+        constexpr int STEP = NW == 8 ? 96 : (K * V >= 8192 ? 64 : 32);
         const int ph = ((int)blockIdx.x >> 3) & 7;
         for (int i = 0; i < ph; ++i) __builtin_amdgcn_s_sleep(STEP);
     }
 
     // ---- stage A loads: k, dO and dU rows (buffer loads into LDS), the scalars, S0 and dS
     intra_load_tile<K>((lds_u32x4 *)(L + oK), p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst,
-                       len, wave, lane, 4);
+                       len, wave, lane, NW);
     intra_load_tile<V>((lds_u32x4 *)(L + oDO), d_out + (int64_t)start * p.ost + (int64_t)h * p.osh,
-                       2u * (uint32_t)p.ost, len, wave, lane, 4);
-    intra_load_tile<V>((lds_u32x4 *)(L + oDU), w.DU + chh * 64 * V, 2u * (uint32_t)V, 64, wave, lane, 4);
+                       2u * (uint32_t)p.ost, len, wave, lane, NW);
+    intra_load_tile<V>((lds_u32x4 *)(L + oDU), w.DU + chh * 64 * V, 2u * (uint32_t)V, 64, wave, lane, NW);
     // A1's register operands (-W fragments, the U~ tiles and their scales), issued with the rest
     bf16x8 Wf[KS];
-    uint2 uh[NVT / 2][4];
-    int ush[NVT / 2];
+    uint2 uh[IV][4];
+    int ush[IV];
 #pragma unroll
     for (int kg = 0; kg < KS; ++kg)
         Wf[kg] = __builtin_bit_cast(bf16x8, w.WF[(chh * (K / 8) + ((kg / NKS) * 2 + tm) * NKS + kg % NKS) * 64 + lane]);
 #pragma unroll
-    for (int i = 0; i < NVT / 2; ++i) {
-        const int vt = half + 2 * i;
+    for (int i = 0; i < IV; ++i) {
+        const int vt = ctile(i);
         ush[i] = __float_as_int(w.SC[chh * kScalars + 128 + 2 * vt + tm]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) uh[i][j] = w.UH[(((chh * (V / 32) + vt) * 2 + tm) * 4 + j) * 64 + lane];
@@ -2525,8 +2541,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         s_eg[tid] = exp2_hw(gam);
         s_dd[tid] = exp2_hw(tid < len ? gn - gam : kNegInf);
     }
-    float dot = p.ck_quad ? load_stage_a<K, V, true>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid)
-                          : load_stage_a<K, V, false>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid);
+    float dot = p.ck_quad ? load_stage_a<K, V, true, 64 * NW>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid)
+                          : load_stage_a<K, V, false, 64 * NW>(L + oS0, w.CK + chh * K * V, L + oDS, w.DSN + chh * K * V, tid);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (lane == 0) sdot[wave] = dot;
@@ -2536,8 +2552,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- A1: U = U~ + (-W) S0 for tiles (tm, value tile half + 2 i); U~ enters the accumulator
     {
 #pragma unroll
-        for (int i = 0; i < NVT / 2; ++i) {
-            const int vt = half + 2 * i;
+        for (int i = 0; i < IV; ++i) {
+            const int vt = ctile(i);
             f32x16 acc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -2551,10 +2567,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
     // ---- A2, A4: dO S0^T (the output's state term of dq^, rows scaled by 2^gam) and dW = -dU S0^T
-    f32x16 dQ[NKT / 2], dK[NKT / 2];
+    f32x16 dQ[IK], dK[IK];
 #pragma unroll
-    for (int i = 0; i < NKT / 2; ++i) {
-        const int kt = half + 2 * i;
+    for (int i = 0; i < IK; ++i) {
+        const int kt = ctile(i);
         f32x16 a = {}, b = {};
 #pragma unroll
         for (int s = 0; s < VS; ++s) {
@@ -2575,8 +2591,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i) {
-            const int kt = half + 2 * i;
+        for (int i = 0; i < IK; ++i) {
+            const int kt = ctile(i);
             f32x16 a = {};
 #pragma unroll
             for (int s = 0; s < VS; ++s)
@@ -2594,49 +2610,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const float r = rowsum32(prod, lane);
             const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if ((c & 1) == 0) part[KX][half][row] = r * s_rk[row];
+            if ((c & 1) == 0) part[KX][pw][row] = r * s_rk[row];
         }
     }
     // ---- A5, B1: dT's first term dW (diag(f r_k) K)^T and dP = dO U^T, tile (tm, half)
     f32x16 dT = {}, dP = {};
+    if (wT) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-        dT = mfma32(lds_row8<PK>(tDW, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), dT);
-#pragma unroll
-    for (int s = 0; s < VS; ++s)
-        dP = mfma32(lds_row8<PV>(tDO, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PV>(tU, 32 * half + c, 16 * s + 8 * hh), dP);
-    {
+        for (int s = 0; s < KS; ++s)
+            dT = mfma32(lds_row8<PK>(tDW, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), dT);
         const int sc_ = 32 * half + c;
         const float fr = s_b[sc_] * s_eg[sc_] * s_rk[sc_];
 #pragma unroll
         for (int e = 0; e < 16; ++e) dT[e] *= fr;
     }
+    if (wP) {
+#pragma unroll
+        for (int s = 0; s < VS; ++s)
+            dP = mfma32(lds_row8<PV>(tDO, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PV>(tU, 32 * half + c, 16 * s + 8 * hh), dP);
+    }
     lds_barrier();                                            // S0 and dS are dead: stage B loads reuse their space
     intra_load_tile<K>((lds_u32x4 *)(L + oQ), p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, 2u * (uint32_t)p.qst,
-                       len, wave, lane, 4);
+                       len, wave, lane, NW);
     intra_load_tile<V>((lds_u32x4 *)(L + oVv), p.v + (int64_t)start * p.vst + (int64_t)h * p.vsh, 2u * (uint32_t)p.vst,
-                       len, wave, lane, 4);
-    intra_load_tile<64>((lds_u32x4 *)(L + oT), w.TB + chh * (64 * 64 / 8), 128u, 64, wave, lane, 4);
+                       len, wave, lane, NW);
+    intra_load_tile<64>((lds_u32x4 *)(L + oT), w.TB + chh * (64 * 64 / 8), 128u, 64, wave, lane, NW);
     vm_wait<0>();
     lds_barrier();
     // ---- B0: the output's state term of dgam: scale r_q rowdot(q, 2^gam dO S0^T)
     {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i) {
+        for (int i = 0; i < IK; ++i) {
             float xq_[16];
-            acc_elems<PK>(L + oQ, 32 * tm, 32 * (half + 2 * i), lane, xq_);
+            acc_elems<PK>(L + oQ, 32 * tm, 32 * ctile(i), lane, xq_);
 #pragma unroll
             for (int e = 0; e < 16; ++e) prod[e] += dQ[i][e] * xq_[e];
         }
         {
             const float r = rowsum32(prod, lane);
             const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if ((c & 1) == 0) part[QX][half][row] = r * p.scale * s_rq[row];
+            if ((c & 1) == 0) part[QX][pw][row] = r * p.scale * s_rq[row];
         }
     }
     // ---- B2: P = M o (q^ k^T) for tile (tm, half); dP o P sums; R = M o dP r_k,s and R2 = M o dP scale r_q,t
-    {
+    if (wP) {
         f32x16 qk = {};
 #pragma unroll
         for (int s = 0; s < KS; ++s)
@@ -2667,7 +2685,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         store_tile_bf16<8>(L + oR2, R2, 32 * tm, 32 * half, lane);
     }
     // ---- B3: dT's second term dU (diag(beta) V)^T; dT published in bf16
-    {
+    if (wT) {
         f32x16 a = {};
 #pragma unroll
         for (int s = 0; s < VS; ++s)
@@ -2681,8 +2699,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NVT / 2; ++i) {
-            const int vt = half + 2 * i;
+        for (int i = 0; i < IV; ++i) {
+            const int vt = ctile(i);
             f32x16 a = {};
 #pragma unroll
             for (int st = 0; st < 4; ++st)
@@ -2699,15 +2717,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const float r = rowsum32(prod, lane);
             const int e = c >> 1;
-            if ((c & 1) == 0) part[XV][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+            if ((c & 1) == 0) part[XV][pw][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
         }
     }
     // ---- B5: X1 = T^T dW: dk^ += diag(f) X1 and df = r_k rowdot(X1, k)
     {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i) {
-            const int kt = half + 2 * i;
+        for (int i = 0; i < IK; ++i) {
+            const int kt = ctile(i);
             f32x16 a = {};
 #pragma unroll
             for (int st = 0; st < 4; ++st)
@@ -2724,14 +2742,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         {
             const float r = rowsum32(prod, lane);
             const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if ((c & 1) == 0) part[DF][half][row] = r * s_rk[row];
+            if ((c & 1) == 0) part[DF][pw][row] = r * s_rk[row];
         }
     }
     lds_barrier();                                            // R, R2 and dT published
     // ---- B7, B8: dq^ += R k, dk^ += R2^T q
 #pragma unroll
-    for (int i = 0; i < NKT / 2; ++i) {
-        const int kt = half + 2 * i;
+    for (int i = 0; i < IK; ++i) {
+        const int kt = ctile(i);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             dQ[i] = mfma32(lds_row8<8>(tR, 32 * tm + c, 16 * st + 8 * hh), lds_tr32s<PK, false>(tK, 16 * st, 32 * kt, lane), dQ[i]);
@@ -2741,13 +2759,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // one q/k head per value head: the row norms' chain rule is applied here (dq_out set), and
     // the row dots (q . dq^) it needs are taken while q is still in LDS (dq^ is final)
     const bool fuse_qk = dq_out != nullptr;
-    __bf16 xq[NKT / 2][16];   // the q elements of this lane's dq^ entries, for the chain rule below
+    __bf16 xq[IK][16];   // the q elements of this lane's dq^ entries, for the chain rule below
     if (fuse_qk) {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i) {
+        for (int i = 0; i < IK; ++i) {
             float x[16];
-            acc_elems<PK>(L + oQ, 32 * tm, 32 * (half + 2 * i), lane, x);
+            acc_elems<PK>(L + oQ, 32 * tm, 32 * ctile(i), lane, x);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 xq[i][e] = f2bf(x[e]);   // x is a bf16 value: exact
@@ -2756,64 +2774,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         const float r = rowsum32(prod, lane);
         const int e = c >> 1;
-        if ((c & 1) == 0) part[QD][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+        if ((c & 1) == 0) part[QD][pw][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
     }
-    // ---- C1: Y = dT T^T, tile (tm, half)
+    // ---- C1: Y = dT T^T, tile (tm, half); the Gram tile of k that C2 needs, tile (tm, half)
+    f32x16 gk = {};
     {
         f32x16 y = {};
+        if (wT) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-            y = mfma32(lds_row8<8>(tDT, 32 * tm + c, 16 * st + 8 * hh), lds_row8<8>(tT, 32 * half + c, 16 * st + 8 * hh), y);
+            for (int st = 0; st < 4; ++st)
+                y = mfma32(lds_row8<8>(tDT, 32 * tm + c, 16 * st + 8 * hh), lds_row8<8>(tT, 32 * half + c, 16 * st + 8 * hh), y);
+        }
+        if (wP) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                gk = mfma32(lds_row8<PK>(tK, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), gk);
+        }
         lds_barrier();                                        // q, v, R and R2 are dead: Y, Z, Z3 reuse them
-        store_tile_bf16<8>(L + oY, y, 32 * tm, 32 * half, lane);
+        if (wT) store_tile_bf16<8>(L + oY, y, 32 * tm, 32 * half, lane);
     }
     lds_barrier();
     // ---- C2: dA = -T^T Y (strictly lower), tile (rows a of tile tm, columns b of tile half), with
-    // the Gram tile of k: A = beta_a E r_a r_b (k_a . k_b); dbeta, dgam sums; Z, Z3 = dGm r_b, dGm r_a
+    // the Gram tile of k: A = beta_a E r_a r_b (k_a . k_b); dbeta, dgam sums; Z, Z3 = dGm r_b, dGm r_a.
+    // Both wave groups form dA; the one with the Gram tile takes the sums, the other Z and Z3.
     {
-        f32x16 da = {}, gk = {};
+        f32x16 da = {};
 #pragma unroll
         for (int st = 0; st < 4; ++st)
             da = mfma32(lds_tr32s<8, false>(tT, 16 * st, 32 * tm, lane), lds_tr32s<8, false>(tY, 16 * st, 32 * half, lane), da);
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            gk = mfma32(lds_row8<PK>(tK, 32 * tm + c, 16 * s + 8 * hh), lds_row8<PK>(tK, 32 * half + c, 16 * s + 8 * hh), gk);
         const int b = 32 * half + c;
         const float gb = s_gam[b], rb = s_rk[b];
-        f32x16 Z, Z3;
-        float colsum = 0.f, v1[16], v2[16];
+        if (wP) {
+            float colsum = 0.f, v1[16], v2[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            const float E = exp2_hw(b < a ? s_gam[a] - gb : kNegInf);
-            const float dam = b < a ? -da[e] : 0.f;
-            const float ghat = s_rk[a] * rb * gk[e];
-            const float aA = dam * s_b[a] * E * ghat;
-            colsum += aA;
-            v1[e] = aA;
-            v2[e] = dam * E * ghat;
-            const float dgm = dam * s_b[a] * E;
-            Z[e] = dgm * rb;
-            Z3[e] = dgm * s_rk[a];
-        }
-        {
-            const float r1 = rowsum32(v1, lane), r2 = rowsum32(v2, lane);
-            const int e = c >> 1, a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if ((c & 1) == 0) {
-                part[AAR][half][a] = r1;
-                part[DAEG][half][a] = r2;
+            for (int e = 0; e < 16; ++e) {
+                const int a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                const float E = exp2_hw(b < a ? s_gam[a] - gb : kNegInf);
+                const float dam = b < a ? -da[e] : 0.f;
+                const float ghat = s_rk[a] * rb * gk[e];
+                const float aA = dam * s_b[a] * E * ghat;
+                colsum += aA;
+                v1[e] = aA;
+                v2[e] = dam * E * ghat;
             }
+            {
+                const float r1 = rowsum32(v1, lane), r2 = rowsum32(v2, lane);
+                const int e = c >> 1, a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                if ((c & 1) == 0) {
+                    part[AAR][half][a] = r1;
+                    part[DAEG][half][a] = r2;
+                }
+            }
+            colsum += __shfl_xor(colsum, 32, 64);
+            if (hh == 0) part[AAC][tm][b] = colsum;
         }
-        colsum += __shfl_xor(colsum, 32, 64);
-        if (hh == 0) part[AAC][tm][b] = colsum;
-        store_tile_bf16<8>(L + oZ, Z, 32 * tm, 32 * half, lane);
-        store_tile_bf16<8>(L + oZ3, Z3, 32 * tm, 32 * half, lane);
+        if (wT) {
+            f32x16 Z, Z3;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int a = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
+                const float E = exp2_hw(b < a ? s_gam[a] - gb : kNegInf);
+                const float dam = b < a ? -da[e] : 0.f;
+                const float dgm = dam * s_b[a] * E;
+                Z[e] = dgm * rb;
+                Z3[e] = dgm * s_rk[a];
+            }
+            store_tile_bf16<8>(L + oZ, Z, 32 * tm, 32 * half, lane);
+            store_tile_bf16<8>(L + oZ3, Z3, 32 * tm, 32 * half, lane);
+        }
     }
     lds_barrier();
     // ---- C3: dk^ += Z k + Z3^T k; the q^ and k^ gradients out
 #pragma unroll
-    for (int i = 0; i < NKT / 2; ++i) {
-        const int kt = half + 2 * i;
+    for (int i = 0; i < IK; ++i) {
+        const int kt = ctile(i);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const bf16x8 kb = lds_tr32s<PK, false>(tK, 16 * st, 32 * kt, lane);
@@ -2835,17 +2869,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (fuse_qk) {
         float prod[16] = {};
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i) {
+        for (int i = 0; i < IK; ++i) {
             float xk[16];
-            acc_elems<PK>(L + oK, 32 * tm, 32 * (half + 2 * i), lane, xk);
+            acc_elems<PK>(L + oK, 32 * tm, 32 * ctile(i), lane, xk);
 #pragma unroll
             for (int e = 0; e < 16; ++e) prod[e] += dK[i][e] * xk[e];
         }
         const float r = rowsum32(prod, lane);
         const int e = c >> 1;
-        if ((c & 1) == 0) part[KD][half][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+        if ((c & 1) == 0) part[KD][pw][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
     }
     lds_barrier();                                            // every partial sum written
+    // a per-token sum over the column tiles (wsum: the K- and V-wide results' partials, one
+    // per wave pair) or over the two 32-token tiles (psum: the 64 x 64 ones)
+    auto wsum = [&](int x, int t) {
+        float r = part[x][0][t];
+#pragma unroll
+        for (int j = 1; j < 2 * NQ; ++j) r += part[x][j][t];
+        return r;
+    };
+    auto psum = [&](int x, int t) { return part[x][0][t] + part[x][1][t]; };
     if (fuse_qk) {
         // dx = r dx^ - r^3 (x . dx^) x (times scale for q; r = 1 without the norm): q from the
         // registers taken above, k rows from LDS
@@ -2855,14 +2898,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
             rq[e] = s_rq[row];
             rk[e] = s_rk[row];
-            cq[e] = p.l2norm ? rq[e] * rq[e] * rq[e] * (part[QD][0][row] + part[QD][1][row]) : 0.f;
-            ck[e] = p.l2norm ? rk[e] * rk[e] * rk[e] * (part[KD][0][row] + part[KD][1][row]) : 0.f;
+            cq[e] = p.l2norm ? rq[e] * rq[e] * rq[e] * wsum(QD, row) : 0.f;
+            ck[e] = p.l2norm ? rk[e] * rk[e] * rk[e] * wsum(KD, row) : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < NKT / 2; ++i) {
-            const int col = 32 * (half + 2 * i) + c;
+        for (int i = 0; i < IK; ++i) {
+            const int col = 32 * ctile(i) + c;
             float xks[16];
-            acc_elems<PK>(L + oK, 32 * tm, 32 * (half + 2 * i), lane, xks);
+            acc_elems<PK>(L + oK, 32 * tm, 32 * ctile(i), lane, xks);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
@@ -2878,18 +2921,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- per token: dbeta and dgam, then dg by the reverse cumulative sum within the chunk
     if (tid < 64) {
         const int t = tid;
-        const float df = part[DF][0][t] + part[DF][1][t];
+        const float df = wsum(DF, t);
         const float f = s_b[t] * s_eg[t];
-        const float db = part[XV][0][t] + part[XV][1][t] + df * s_eg[t] + part[DAEG][0][t] + part[DAEG][1][t];
-        const float F = part[KX][0][t] + part[KX][1][t];
-        float dgam = df * f + (part[AAR][0][t] + part[AAR][1][t]) - (part[AAC][0][t] + part[AAC][1][t]) +
-                     (part[PPR_][0][t] + part[PPR_][1][t]) - (part[PPC][0][t] + part[PPC][1][t]) +
-                     (part[QX][0][t] + part[QX][1][t]) - F;
+        const float db = wsum(XV, t) + df * s_eg[t] + part[DAEG][0][t] + part[DAEG][1][t];
+        const float F = wsum(KX, t);
+        float dgam = df * f + psum(AAR, t) - psum(AAC, t) + psum(PPR_, t) - psum(PPC, t) + wsum(QX, t) - F;
         // the last token also carries sum F and 2^gam_n <dS, S0>
         float Fs = t < len ? F : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) Fs += __shfl_xor(Fs, off, 64);
-        if (t == len - 1) dgam += Fs + exp2_hw(s_gam[t]) * (sdot[0] + sdot[1] + sdot[2] + sdot[3]);
+        if (t == len - 1) {
+            float sd = sdot[0];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) sd += sdot[j];
+            dgam += Fs + exp2_hw(s_gam[t]) * sd;
+        }
         if (t < len) db_out[(int64_t)(start + t) * p.HV + h] = db;
         // dg: the reverse cumulative sum of dgam within the chunk (zeros past its end), by a
         // suffix scan across the wave
@@ -3004,6 +3050,8 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
     pf.ck_cap = p.max_chunks;
     pf.o = nullptr;
     pf.sT = nullptr;
+// waves of the backward's intra workgroup: 8 where both K and V split into four 32-column tiles
+#define BWD_NW(KK, VV) ((KK) % 128 == 0 && (VV) % 128 == 0 ? 8 : 4)
 #define LA_BWD(KK, VV)                                                                                         \
     if (p.K == KK && p.V == VV) {                                                                              \
         before(LA_KERNEL_INTRA);                                                                               \
@@ -3018,8 +3066,9 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
         after(LA_KERNEL_INTER);                                                                                \
         before(LA_KERNEL_BWD_INTRA);                                                                           \
         if (items > 0)                                                                                         \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV>), dim3((unsigned)items), dim3(256), 0, s, pb, w, \
-                               a.d_out, a.dv, a.dg, a.dbeta, fuse_qk ? a.dq : nullptr, fuse_qk ? a.dk : nullptr); \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV, BWD_NW(KK, VV)>), dim3((unsigned)items),      \
+                               dim3(64 * BWD_NW(KK, VV)), 0, s, pb, w, a.d_out, a.dv, a.dg, a.dbeta,           \
+                               fuse_qk ? a.dq : nullptr, fuse_qk ? a.dk : nullptr);                           \
         if (!fuse_qk && qk_blocks > 0)                                                                         \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_qk<KK>), dim3(qk_blocks), dim3(256), 0, s, p, w, a.dq, a.dk); \
         after(LA_KERNEL_BWD_INTRA);                                                                            \
@@ -3030,6 +3079,7 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
     LA_BWD(128, 64)
     LA_BWD(128, 128)
 #undef LA_BWD
+#undef BWD_NW
     return hipErrorInvalidValue;
 }
 
