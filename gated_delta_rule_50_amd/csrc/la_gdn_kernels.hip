@@ -2450,6 +2450,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     __shared__ __attribute__((aligned(16))) float ssc[6 * 64];   // gam2, r_k, r_q, beta, 2^gam, 2^(gam_n - gam)
     __shared__ float part[NPART][2 * NQ][64];   // per-token partial sums: [column tile half + 2 qw] or [tile]
     __shared__ float sdot[NW];
+    __shared__ float pf_sink[NW == 8 ? NW * 64 : 1];   // landing slots of the next item's cache-line touches
     lds_char *const L = (lds_char *)smem;
     const lds_u32x4 *const tK = (const lds_u32x4 *)(L + oK);
     const lds_u32x4 *const tDO = (const lds_u32x4 *)(L + oDO);
@@ -2481,16 +2482,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     auto ctile = [&](int i) { return half + 2 * (NQ * i + qw); };
     // the item: chunk ci of the chunk table, value head h
     const int ci = blockIdx.x / p.HV, h = blockIdx.x % p.HV, hk = h / (p.HV / p.HK);
-    int start, len;
+    int start, len, total;
     if (p.N <= 64) {
         const SmallMap sm = small_map(p, w, false);
+        total = sm.total;
         if (ci >= sm.total) return;
         const uint64_t owns = __ballot(lane < p.N && sm.first <= ci);
         const int sq_ = 63 - __builtin_clzll(owns);
         start = __builtin_amdgcn_readfirstlane(__shfl(sm.start, sq_, 64) + kChunk * (ci - __shfl(sm.first, sq_, 64)));
         len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, sq_, 64) - start));
     } else {
-        if (ci >= w.hdr[1]) return;
+        total = w.hdr[1];
+        if (ci >= total) return;
         const int4 ch = w.chunks[ci];
         start = __builtin_amdgcn_readfirstlane(ch.y);
         len = __builtin_amdgcn_readfirstlane(ch.z);
@@ -2637,6 +2640,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     intra_load_tile<64>((lds_u32x4 *)(L + oT), w.TB + chh * (64 * 64 / 8), 128u, 64, wave, lane, NW);
     vm_wait<0>();
     lds_barrier();
+    // With several rounds of items, the item R = (CUs) on from this one (blocks R apart share an
+    // XCD; the next round runs it there) has its S0 and dS cache lines touched now, one dword
+    // per 128-byte line into a never-read LDS slot, so that its stage-A loads find them in the
+    // L2 or the Infinity Cache.  Nothing waits for these loads until the end of the kernel.
+    if (NW == 8) {
+        const int R = p.intra_grid / 3, nb = (int)blockIdx.x + R;
+        if ((int)gridDim.x > R && nb < (int)gridDim.x && nb / p.HV < total) {
+            const i32x4 rS = make_rsrc(w.CK + (int64_t)nb * K * V, (uint32_t)(K * V * 4));
+            const i32x4 rD = make_rsrc(w.DSN + (int64_t)nb * K * V, (uint32_t)(K * V * 4));
+#pragma unroll
+            for (int j = 0; j < K * V * 4 / 128 / (64 * NW); ++j) {
+                const uint32_t off = (uint32_t)(tid + 64 * NW * j) * 128u;
+                b2l_dword(rS, (lds_float *)(pf_sink + 64 * wave), off);
+                b2l_dword(rD, (lds_float *)(pf_sink + 64 * wave), off);
+            }
+        }
+    }
     // ---- B0: the output's state term of dgam: scale r_q rowdot(q, 2^gam dO S0^T)
     {
         float prod[16] = {};
@@ -2947,6 +2967,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         }
         if (t < len) dg_out[(int64_t)(start + t) * p.HV + h] = acc;
     }
+    if (NW == 8) vm_wait<0>();   // the touches land in LDS: done before the workgroup ends
 }
 
 // dq and dk from the per-value-head gradients of q^ and k^: the sum over each head group
