@@ -179,3 +179,32 @@ def test_backward_from_the_forward_state_series_bitwise(hk, hv):
     torch.cuda.synchronize()
     for name in a:
         assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_series_bitwise_several_rounds():
+    # the varlen workload (1040 (chunk, head) items: several rounds of the backward's intra
+    # workgroups, whose items also touch the cache lines of the item a round on, here in the
+    # caller's series up to its last chunk): la_gdn_bwd_ex equals la_gdn_bwd bit for bit
+    p = make_problem(2)
+    g = p.to("cuda")
+    d_out, d_fin = upstream(p, 221)
+    d_out, d_fin = d_out.cuda(), d_fin.cuda()
+    note("bwd_ex: series, varlen workload")
+    _, _, series = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                    checkpoint_every_n_tokens=64, checkpoint_dtype=torch.float32)
+    a = la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, d_out, initial_state=g.state, d_final_state=d_fin)
+    b = la.la_gdn_bwd(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, d_out, initial_state=g.state, d_final_state=d_fin,
+                      chunk_states=series)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("hk,hv", [(2, 4), (4, 4)])
+def test_backward_many_sequences_full_head_dims(hk, hv):
+    # more than 64 sequences at K = V = 128 (the scheduler kernel's chunk table, the 8-wave
+    # backward intra workgroup) and more (chunk, head) items than two per CU, so that the
+    # intra pass runs several rounds; grouped heads (head-group sums) and one value head per
+    # q/k head (the chain rule in the intra pass)
+    lens = [(i * 97) % 300 for i in range(70)]
+    check_bwd(custom_problem(lens, hk=hk, hv=hv, dk=128, dv=128, seed=222, with_state=True), 223)
