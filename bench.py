@@ -195,6 +195,10 @@ def main(argv=None):
                          + "; ".join(f"{k}: {v}" for k, v in VARIANTS.items() if v))
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--measure-copy", action="store_true",
+                    help="also time a 1 GiB device-to-device copy (best of 5, events) and report its read + "
+                         "write rate in path.copy_gbs: the streaming rate HBM gives in practice, beside the "
+                         "8 TB/s peak the roofline fractions use")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -314,6 +318,22 @@ def main(argv=None):
                              dt_bias=g.dt_bias, checkpoint_every_n_tokens=every, checkpoints=ck,
                              num_householder=nh, workspace=ws, stream=stream)
 
+    copy_gbs = None
+    if args.measure_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        copy_gbs = 2 * (1 << 30) / (best * 1e-3) / 1e9
+        del src, dst
+
     if args.calibrate_copy_mib > 0:
         nbytes = args.calibrate_copy_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -424,6 +444,8 @@ def main(argv=None):
                  "mfma_frac": fl / step_s / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                  "kernels": kern},
     }
+    if copy_gbs is not None:
+        rec["path"]["copy_gbs"] = copy_gbs
     if not args.no_cpu_baseline and wl == 2 and variant == "plain":
         rec["cpu_baseline"] = cpu_baseline(prob)
     print(json.dumps(rec), flush=True)

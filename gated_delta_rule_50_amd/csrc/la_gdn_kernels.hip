@@ -1528,13 +1528,15 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     x.vt0 = TP * tile;
     x.lane = threadIdx.x & 63;
     x.ptile = SUMMARY && 32 * tile >= V;
-    // Roles by wave: with two 4-wave workgroups per CU (the summary, the states-only forward)
-    // the hardware puts a workgroup's waves 0..3 on SIMDs s, s + 2, s + 1, s + 3 of a fixed
-    // cycle and, for most CUs, the other workgroup's one step further on, so the state roles
-    // go to hardware waves 0 and 2 (and the loaders to 1 and 3): the two workgroups' state
-    // waves then sit on four different SIMDs instead of sharing one.
+    // Roles by wave: with two 4-wave workgroups per CU the hardware puts a workgroup's waves
+    // 0..3 on SIMDs s, s + 2, s + 1, s + 3 of a fixed cycle and, for most CUs, the other
+    // workgroup's one step further on, so in the states-only forward the state roles go to
+    // hardware waves 0 and 2 (and the loaders to 1 and 3): the two workgroups' state waves
+    // then sit on four different SIMDs instead of sharing one (dense batch: 612 -> 606 us with
+    // the reverse pass).  The summary keeps waves 0 and 1 (the same remap measured 0-2 %
+    // slower there).
     const int hwave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wave = C::THREADS == 256 ? ((hwave & 1) << 1) | (hwave >> 1) : hwave;
+    const int wave = NOOUT ? ((hwave & 1) << 1) | (hwave >> 1) : hwave;
     const int lane = x.lane, c = lane & 31, hh = lane >> 5;
     const int nch = x.nch;
 
