@@ -2443,7 +2443,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     constexpr int PK = K / 8, PV = V / 8, NKT = K / 32, NVT = V / 32, KS = K / 16, VS = V / 16;
     // NW = 8: two waves per (token tile, column tile) pair, which split the K- and V-wide
     // products by column tile (IK, IV per wave) and share the 64 x 64 ones by product
-    static_assert(NW == 4 || (NW == 8 && NKT % 4 == 0 && NVT % 4 == 0), "4 waves, or 8 with 4k column tiles");
+    static_assert(NW == 4 || (NW == 8 && NKT % 4 == 0 && NVT % 4 == 0), "8 waves need K and V in multiples of 128");
     constexpr int NQ = NW / 4, IK = NKT / (2 * NQ), IV = NVT / (2 * NQ);
     constexpr int NKS = K / 32;                             // steps of 16 keys per key half (-W fragments)
     constexpr int szK = 64 * K * 2, szV = 64 * V * 2, sz64 = 64 * 64 * 2, szS = K * V * 2;
