@@ -2436,7 +2436,7 @@ __device__ __forceinline__ float load_stage_a(lds_char *dS0, const float *S0, ld
     return dot;
 }
 
-template <int K, int V, int NW>
+template <int K, int V, int NW, bool GL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_bwd_intra(
     Prob p, Ws w, const __bf16 *d_out, float *dv_out, float *dg_out, float *db_out, float *dq_out, float *dk_out)
 {
@@ -2444,6 +2444,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // NW = 8: two waves per (token tile, column tile) pair, which split the K- and V-wide
     // products by column tile (IK, IV per wave) and share the 64 x 64 ones by product
     static_assert(NW == 4 || (NW == 8 && NKT % 4 == 0 && NVT % 4 == 0), "8 waves need K and V in multiples of 128");
+    static_assert(!GL || NW == 8, "the head-group loop runs on the 8-wave workgroup");
     constexpr int NQ = NW / 4, IK = NKT / (2 * NQ), IV = NVT / (2 * NQ);
     constexpr int NKS = K / 32;                             // steps of 16 keys per key half (-W fragments)
     constexpr int szK = 64 * K * 2, szV = 64 * V * 2, sz64 = 64 * 64 * 2, szS = K * V * 2;
@@ -2480,22 +2481,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     lds_float *const s_b = s_gam + 192, *const s_eg = s_gam + 256, *const s_dd = s_gam + 320;
 
     if (w.hdr[0] != LA_DEVICE_OK) return;
-    const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, hh = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tm = wave & 1, half = (wave >> 1) & 1, qw = wave >> 2, pw = half + 2 * qw;
-    // 64 x 64 products: dT (A5, B3) and Y (C1) on the waves with qw = 0, dP (B1, B2), the
-    // Gram tile and dA (C2) on those with qw = 1 (all on the one set of 4 waves for NW = 4)
-    const bool wT = NQ == 1 || qw == 0, wP = NQ == 1 || qw == 1;
-    // the wave's i-th column tile of a K- or V-wide result
-    auto ctile = [&](int i) { return half + 2 * (NQ * i + qw); };
-    // the item: chunk ci of the chunk table, value head h
-    const int ci = blockIdx.x / p.HV, h = blockIdx.x % p.HV, hk = h / (p.HV / p.HK);
+    const int lane0 = threadIdx.x & 63;
+    // the item: chunk ci of the chunk table and value head h0; GL: q/k head hk and its G value
+    // heads h0 .. h0 + G - 1, one after another, with dq^ and dk^ summed over them in registers
+    const int G = p.HV / p.HK, NH = GL ? G : 1;
+    const int ci = GL ? (int)blockIdx.x / p.HK : (int)blockIdx.x / p.HV;
+    const int hk = GL ? (int)blockIdx.x % p.HK : ((int)blockIdx.x % p.HV) / G;
+    const int h0 = GL ? hk * G : (int)blockIdx.x % p.HV;
     int start, len, total;
     if (p.N <= 64) {
         const SmallMap sm = small_map(p, w, false);
         total = sm.total;
         if (ci >= sm.total) return;
-        const uint64_t owns = __ballot(lane < p.N && sm.first <= ci);
+        const uint64_t owns = __ballot(lane0 < p.N && sm.first <= ci);
         const int sq_ = 63 - __builtin_clzll(owns);
         start = __builtin_amdgcn_readfirstlane(__shfl(sm.start, sq_, 64) + kChunk * (ci - __shfl(sm.first, sq_, 64)));
         len = __builtin_amdgcn_readfirstlane(min(kChunk, __shfl(sm.end, sq_, 64) - start));
@@ -2506,7 +2504,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         start = __builtin_amdgcn_readfirstlane(ch.y);
         len = __builtin_amdgcn_readfirstlane(ch.z);
     }
-    const int64_t chh = (int64_t)ci * p.HV + h;
     // With several rounds of items (one workgroup per CU), the first round starts in 8 phases
     // about an eighth of an item apart (blocks 8 apart share an XCD, so each XCD gets every
     // phase): the CUs then run their items back to back out of step, instead of all issuing
@@ -2514,17 +2511,40 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // K = V = 128 (about 34 us per item) a phase step of 127 x 64 clocks took the varlen
     // backward from 168 to 152 us and the dense batch from 1081 to 1019 us (8 phases of 64 x 64
     // clocks gained less, 16 or 32 phases of 127 x 64 clocks lost part of it again); the
-    // 8-wave items (about 25 us) take 96 x 64 (64: 132 -> 124 us varlen; 127 or 160: slower).
-    // Single-round launches start at once.
+    // 8-wave items (about 25 us per value head) take 96 x 64 per head (64: 132 -> 124 us
+    // varlen; 127 or 160: slower).  Single-round launches start at once.
     if ((int)gridDim.x > 2 * (p.intra_grid / 3) && (int)blockIdx.x < p.intra_grid / 3) {
         constexpr int STEP = NW == 8 ? 96 : (K * V >= 8192 ? 64 : 32);
         const int ph = ((int)blockIdx.x >> 3) & 7;
-        for (int i = 0; i < ph; ++i) __builtin_amdgcn_s_sleep(STEP);
+        for (int i = 0; i < ph * NH; ++i) __builtin_amdgcn_s_sleep(STEP);
     }
+    const bool fuse_qk = dq_out != nullptr;
+    f32x16 dQ[IK], dK[IK];   // dq^ and dk^ (GL: summed over the heads done so far)
+    // GL: this lane's row dot of q with dq^ as the previous heads left it (the output's state
+    // term of this head's dgam is the row dot of q with what this head's A2 adds to it)
+    float qprev = 0.f;
+    for (int j = 0; j < NH; ++j) {
+    // GL: the thread and wave indices pass through an empty asm per head, so that the compiler
+    // forms the many lane-dependent LDS addresses of a head inside the loop instead of hoisting
+    // them all out of it, where they would stay live across the whole loop (and spill)
+    int tid_ = threadIdx.x, wave_ = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (GL) asm volatile("" : "+v"(tid_), "+s"(wave_));
+    const int tid = tid_, lane = tid & 63, c = lane & 31, hh = lane >> 5, wave = wave_;
+    const int tm = wave & 1, half = (wave >> 1) & 1, qw = wave >> 2, pw = half + 2 * qw;
+    // 64 x 64 products: dT (A5, B3) and Y (C1) on the waves with qw = 0, dP (B1, B2), the
+    // Gram tile and dA (C2) on those with qw = 1 (all on the one set of 4 waves for NW = 4)
+    const bool wT = NQ == 1 || qw == 0, wP = NQ == 1 || qw == 1;
+    // the wave's i-th column tile of a K- or V-wide result
+    auto ctile = [&](int i) { return half + 2 * (NQ * i + qw); };
+    __bf16 xq[IK][16];   // the q elements of this lane's dq^ entries, for the chain rule below
+    const int h = h0 + j;
+    const int64_t chh = (int64_t)ci * p.HV + h;
 
-    // ---- stage A loads: k, dO and dU rows (buffer loads into LDS), the scalars, S0 and dS
-    intra_load_tile<K>((lds_u32x4 *)(L + oK), p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh, 2u * (uint32_t)p.kst,
-                       len, wave, lane, NW);
+    // ---- stage A loads: k (once per item), dO and dU rows (buffer loads into LDS), the
+    // scalars, S0 and dS
+    if (j == 0)
+        intra_load_tile<K>((lds_u32x4 *)(L + oK), p.k + (int64_t)start * p.kst + (int64_t)hk * p.ksh,
+                           2u * (uint32_t)p.kst, len, wave, lane, NW);
     intra_load_tile<V>((lds_u32x4 *)(L + oDO), d_out + (int64_t)start * p.ost + (int64_t)h * p.osh,
                        2u * (uint32_t)p.ost, len, wave, lane, NW);
     intra_load_tile<V>((lds_u32x4 *)(L + oDU), w.DU + chh * 64 * V, 2u * (uint32_t)V, 64, wave, lane, NW);
@@ -2578,7 +2598,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         }
     }
     // ---- A2, A4: dO S0^T (the output's state term of dq^, rows scaled by 2^gam) and dW = -dU S0^T
-    f32x16 dQ[IK], dK[IK];
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
         const int kt = ctile(i);
@@ -2594,7 +2613,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             a[e] *= s_eg[32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)];
             b[e] = -b[e];
         }
-        dQ[i] = a;
+        dQ[i] = GL && j > 0 ? dQ[i] + a : a;
         store_tile_bf16<PK>(L + oDW, b, 32 * tm, 32 * kt, lane);
     }
     lds_barrier();                                            // U and dW published
@@ -2616,7 +2635,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
                 a[e] *= s_dd[row];
                 prod[e] += a[e] * xk[e];
             }
-            dK[i] = a;
+            dK[i] = GL && j > 0 ? dK[i] + a : a;
         }
         {
             const float r = rowsum32(prod, lane);
@@ -2651,12 +2670,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // With several rounds of items, the item R = (CUs) on from this one (blocks R apart share an
     // XCD; the next round runs it there) has its S0 and dS cache lines touched now, one dword
     // per 128-byte line into a never-read LDS slot, so that its stage-A loads find them in the
-    // L2 or the Infinity Cache.  Nothing waits for these loads until the end of the kernel.
+    // L2 or the Infinity Cache.  GL: the item's next value head first (its stage-A wait is the
+    // first to cover these loads), then the next item's first head; otherwise only the end of
+    // the kernel waits for them.
     if (NW == 8) {
-        const int R = p.intra_grid / 3, nb = (int)blockIdx.x + R;
-        if ((int)gridDim.x > R && nb < (int)gridDim.x && nb / p.HV < total) {
-            const i32x4 rS = make_rsrc(w.CK + (int64_t)nb * K * V, (uint32_t)(K * V * 4));
-            const i32x4 rD = make_rsrc(w.DSN + (int64_t)nb * K * V, (uint32_t)(K * V * 4));
+        int64_t nchh = -1;
+        if (j + 1 < NH) {
+            nchh = chh + 1;
+        } else {
+            const int R = p.intra_grid / 3, nb = (int)blockIdx.x + R;
+            if ((int)gridDim.x > R && nb < (int)gridDim.x && nb / (GL ? p.HK : p.HV) < total)
+                nchh = GL ? (int64_t)(nb / p.HK) * p.HV + (int64_t)(nb % p.HK) * G : (int64_t)nb;
+        }
+        if (nchh >= 0) {
+            const i32x4 rS = make_rsrc(w.CK + nchh * K * V, (uint32_t)(K * V * 4));
+            const i32x4 rD = make_rsrc(w.DSN + nchh * K * V, (uint32_t)(K * V * 4));
 #pragma unroll
             for (int j = 0; j < K * V * 4 / 128 / (64 * NW); ++j) {
                 const uint32_t off = (uint32_t)(tid + 64 * NW * j) * 128u;
@@ -2665,7 +2693,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             }
         }
     }
-    // ---- B0: the output's state term of dgam: scale r_q rowdot(q, 2^gam dO S0^T)
+    // ---- B0: the output's state term of dgam: scale r_q rowdot(q, 2^gam dO S0^T) (dq^ holds
+    // that term of this head and, with GL, the earlier heads' sum, whose row dot is qprev)
     {
         float prod[16] = {};
 #pragma unroll
@@ -2676,7 +2705,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             for (int e = 0; e < 16; ++e) prod[e] += dQ[i][e] * xq_[e];
         }
         {
-            const float r = rowsum32(prod, lane);
+            const float r = rowsum32(prod, lane) - qprev;
             const int e = c >> 1, row = 32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3);
             if ((c & 1) == 0) part[QX][pw][row] = r * p.scale * s_rq[row];
         }
@@ -2784,10 +2813,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             dK[i] = mfma32(lds_tr32s<8, false>(tR2, 16 * st, 32 * tm, lane), lds_tr32s<PK, false>(tQ, 16 * st, 32 * kt, lane), dK[i]);
         }
     }
-    // one q/k head per value head: the row norms' chain rule is applied here (dq_out set), and
-    // the row dots (q . dq^) it needs are taken while q is still in LDS (dq^ is final)
-    const bool fuse_qk = dq_out != nullptr;
-    __bf16 xq[IK][16];   // the q elements of this lane's dq^ entries, for the chain rule below
+    // one q/k head per value head, or the last head of the group: the row norms' chain rule is
+    // applied here (dq_out set), and the row dots (q . dq^) it needs are taken while q is still
+    // in LDS (dq^ is final)
     if (fuse_qk) {
         float prod[16] = {};
 #pragma unroll
@@ -2802,7 +2830,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         }
         const float r = rowsum32(prod, lane);
         const int e = c >> 1;
-        if ((c & 1) == 0) part[QD][pw][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+        if (j == NH - 1) {
+            if ((c & 1) == 0) part[QD][pw][32 * tm + 8 * (e >> 2) + 4 * hh + (e & 3)] = r;
+        } else {
+            qprev = r;
+        }
     }
     // ---- C1: Y = dT T^T, tile (tm, half); the Gram tile of k that C2 needs, tile (tm, half)
     f32x16 gk = {};
@@ -2894,7 +2926,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             }
         }
     }
-    if (fuse_qk) {
+    if (fuse_qk && j == NH - 1) {
         float prod[16] = {};
 #pragma unroll
         for (int i = 0; i < IK; ++i) {
@@ -2917,7 +2949,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         return r;
     };
     auto psum = [&](int x, int t) { return part[x][0][t] + part[x][1][t]; };
-    if (fuse_qk) {
+    if (fuse_qk && j == NH - 1) {
         // dx = r dx^ - r^3 (x . dx^) x (times scale for q; r = 1 without the norm): q from the
         // registers taken above, k rows from LDS
         float rq[16], rk[16], cq[16], ck[16];
@@ -2974,6 +3006,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             if (t + off < 64) acc += y;
         }
         if (t < len) dg_out[(int64_t)(start + t) * p.HV + h] = acc;
+    }
+    if (j + 1 < NH) lds_barrier();   // this head's sums and scalars are read before the next head's
     }
     if (NW == 8) vm_wait<0>();   // the touches land in LDS: done before the workgroup ends
 }
@@ -3067,6 +3101,15 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
     const unsigned qk_blocks = (unsigned)((p.T * p.HK + 256 / (p.K / 8) - 1) / (256 / (p.K / 8)));
     // one value head per q/k head: no head-group sums, the intra pass writes dq and dk itself
     const bool fuse_qk = p.HV == p.HK;
+    // K = V = 128 with head groups: one workgroup takes the G value heads of a (chunk, q/k
+    // head) one after another and sums dq^ and dk^ in registers, so that the per-value-head
+    // fp32 gradients never go through memory and k_bwd_qk does not run (dense batch of 8 x 4096
+    // tokens, HK = 4, HV = 16: intra pass with k_bwd_qk 897 -> 769 us), unless its coarser
+    // items would cost the CUs more than 1.3 times the rounds of single-head items (what the
+    // saved head-group pass and gradient traffic cost, about 0.3 of a round per round there)
+    const int64_t cus = p.intra_grid / 3, G = p.HV / p.HK;
+    const int64_t items_g = (int64_t)p.max_chunks * p.HK;
+    const bool group_loop = G > 1 && cus > 0 && 10 * G * ((items_g + cus - 1) / cus) <= 13 * ((items + cus - 1) / cus);
     // the forward again, with the state at every chunk start (fp32, indexed by chunk id)
     Prob pf = p;
     pf.ck_every = kChunk;
@@ -3094,11 +3137,19 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
                            a.d_out, a.d_final, a.d_init);                                                      \
         after(LA_KERNEL_INTER);                                                                                \
         before(LA_KERNEL_BWD_INTRA);                                                                           \
-        if (items > 0)                                                                                         \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV, BWD_NW(KK, VV)>), dim3((unsigned)items),      \
+        bool looped = false;                                                                                   \
+        if constexpr (BWD_NW(KK, VV) == 8) {                                                                   \
+            if (group_loop && items_g > 0) {                                                                   \
+                hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV, 8, true>), dim3((unsigned)items_g),       \
+                                   dim3(512), 0, s, pb, w, a.d_out, a.dv, a.dg, a.dbeta, a.dq, a.dk);         \
+                looped = true;                                                                                 \
+            }                                                                                                  \
+        }                                                                                                      \
+        if (!looped && items > 0)                                                                              \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_intra<KK, VV, BWD_NW(KK, VV), false>), dim3((unsigned)items), \
                                dim3(64 * BWD_NW(KK, VV)), 0, s, pb, w, a.d_out, a.dv, a.dg, a.dbeta,           \
                                fuse_qk ? a.dq : nullptr, fuse_qk ? a.dk : nullptr);                           \
-        if (!fuse_qk && qk_blocks > 0)                                                                         \
+        if (!fuse_qk && !looped && qk_blocks > 0)                                                              \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_qk<KK>), dim3(qk_blocks), dim3(256), 0, s, p, w, a.dq, a.dk); \
         after(LA_KERNEL_BWD_INTRA);                                                                            \
         return hipGetLastError();                                                                              \
