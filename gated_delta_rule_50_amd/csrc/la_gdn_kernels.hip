@@ -2082,19 +2082,23 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
 //     start of chunk c (two buffers) and wait for them before the chunk's second barrier.
 // FULL (the full backward) also stores each chunk's end-state gradient and dU for the
 // backward's intra pass.
+// TP = 2: two 32-column tiles per workgroup (four state waves, key half x tile, and the two
+// loaders; the k, q, -W^T and P^T operands shared), for batches that would need more than
+// one round of the one-tile workgroups (158 KiB of LDS at K = V = 128).
 
-template <int K, int V, bool FULL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_inter(
+template <int K, int V, bool FULL, int TP = 1>
+__global__ __launch_bounds__(64 * (2 * TP + 2)) __attribute__((amdgpu_waves_per_eu(TP, TP))) void k_bwd_inter(
     Prob p, Ws w, const __bf16 *d_out, const float *d_end, float *d_start)
 {
     constexpr int KH = K / 2, NR = KH / 32, NKS = KH / 16, PPR = K / 8;
-    constexpr int NT = V / 32;
+    constexpr int NT = V / 32 / TP;              // workgroups per (sequence, head)
     constexpr int FK = K / 8;                    // fragments of a 64-row k or q tile
     constexpr int NKL = FK / 2;                  // k (or q) tile loads per loader wave
     constexpr int FWT = (K / 32) * 4;            // -W^T fragments per chunk
-    constexpr int oK = 0, oQ = FK, oD = 2 * FK, oS = oD + 4, oWT = oS + 1, oPT = oWT + FWT, NF = oPT + 6;
+    constexpr int oK = 0, oQ = FK, oD = 2 * FK, oS = oD + 4 * TP, oWT = oS + 1, oPT = oWT + FWT, NF = oPT + 6;
+    constexpr int SW = 2 * TP;                   // state waves; the loaders are waves SW, SW + 1
     __shared__ u32x4 sB0[NF * 64], sB1[NF * 64];
-    __shared__ u32x4 sZ[2 * 2 * 4 * 64];        // Z partials: [kh][token tile][j][lane]
+    __shared__ u32x4 sZ[TP * 2 * 2 * 4 * 64];   // Z partials: [tile][kh][token tile][j][lane]
     lds_u32x4 *const b0 = (lds_u32x4 *)sB0, *const b1 = (lds_u32x4 *)sB1;
     auto buf = [&](int c) { return (c & 1) ? b1 : b0; };
     lds_u32x4 *const xZ = (lds_u32x4 *)sZ;
@@ -2109,9 +2113,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c = lane & 31, hh = lane >> 5;
 
-    if (wave >= 2) {
+    if (wave >= SW) {
         // ------------------------------------------------------------ loader waves
-        const int lh = wave - 2;
+        const int lh = wave - SW;
         uint32_t koff[NKL], qoff[NKL], doff[2];
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
@@ -2137,10 +2141,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const i32x4 rQ = make_rsrc(p.q + (int64_t)start * p.qst + (int64_t)hk * p.qsh, (uint32_t)len * 2u * (uint32_t)p.qst);
 #pragma unroll
             for (int i = 0; i < NKL; ++i) b2l(rQ, eb, oQ + 2 * i + lh, qoff[i], 0);
-            const i32x4 rD = make_rsrc(d_out + (int64_t)start * p.ost + (int64_t)h * p.osh + 32 * tile,
-                                       (uint32_t)len * 2u * (uint32_t)p.ost);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) b2l(rD, eb, oD + 2 * i + lh, doff[i], 0);
+            for (int tp = 0; tp < TP; ++tp) {
+                const i32x4 rD = make_rsrc(d_out + (int64_t)start * p.ost + (int64_t)h * p.osh + 32 * (TP * tile + tp),
+                                           (uint32_t)len * 2u * (uint32_t)p.ost);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) b2l(rD, eb, oD + 4 * tp + 2 * i + lh, doff[i], 0);
+            }
             const i32x4 rW = make_rsrc(reinterpret_cast<const char *>(w.WTF) + chh * FWT * kFrag, FWT * kFrag);
 #pragma unroll
             for (int i = 0; i < FWT / 2; ++i) {
@@ -2169,9 +2176,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---------------------------------------------------------------- state waves
     __builtin_amdgcn_s_setprio(3);
-    const int kh = wave;
+    const int kh = wave & 1, tp = wave >> 1;
     const int row0 = kh * KH;                            // first key row of this wave
-    const int col = 32 * tile + c;                       // this lane's value column
+    const int col = 32 * (TP * tile + tp) + c;           // this lane's value column
+    lds_u32x4 *const tZ = xZ + tp * (2 * 2 * 4 * 64);     // this tile's Z partials
     const int64_t unit = (int64_t)n * p.HV + h;
     f32x16 D[NR];                                        // dS rows row0 .. row0 + KH - 1
 #pragma unroll
@@ -2224,7 +2232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // dO as B operands (tokens in accumulator order), token steps 0..3
         bf16x8 Do[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) Do[st] = lds_tr32s<4, true>(eb + oD * 64, 16 * st, 0, lane);
+        for (int st = 0; st < 4; ++st) Do[st] = lds_tr32s<4, true>(eb + (oD + 4 * tp) * 64, 16 * st, 0, lane);
         // G2 = P^T dO for both token tiles (P causal: s tile m needs t tiles m .. 1)
         f32x16 Gz[2];
 #pragma unroll
@@ -2264,7 +2272,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int o = 0; o < 2; ++o)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xZ[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
+                tZ[((kh * 2 + (o ^ kh)) * 4 + j) * 64 + lane] =
                     __builtin_bit_cast(u32x4, f32x4{Z[o][4 * j], Z[o][4 * j + 1], Z[o][4 * j + 2], Z[o][4 * j + 3]});
         lds_barrier();                                        // B1
         // dU = diag(d) (Z_0 + Z_1) + P^T dO for both token tiles (own tile first: only addresses
@@ -2276,7 +2284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             f32x16 du;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 zo = __builtin_bit_cast(f32x4, xZ[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
+                const f32x4 zo = __builtin_bit_cast(f32x4, tZ[(((kh ^ 1) * 2 + m) * 4 + j) * 64 + lane]);
                 const f32x4 dj = *reinterpret_cast<const lds_f32x4 *>(scl + 32 * m + 8 * j + 4 * hh);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) du[4 * j + e] = (Z[o][4 * j + e] + zo[e]) * dj[e] + Gz[o][4 * j + e];
@@ -3081,6 +3089,17 @@ __global__ __launch_bounds__(256) void k_bwd_qk(Prob p, const Ws w, float *dq, f
     dk4[1] = make_float4(ok[4], ok[5], ok[6], ok[7]);
 }
 
+// The reverse pass with two 32-column tiles per workgroup: for batches whose one-tile
+// workgroups (one per CU) would need more than one round of the CUs.  Its chunk step runs
+// both tiles in about the time of one (dense batch of 8 x 4096 tokens, HV = 16: 363 ->
+// 223 us; 32 spans of 8192 tokens: 1807 -> 1094 us; the ragged batch with a 65,536-token
+// sequence at H = 32: whole backward 18.4 -> 17.9 ms).
+static bool bwd_wide(int64_t blocks, const Prob &p)
+{
+    const int64_t cus = p.intra_grid / 3;
+    return (p.V / 32) % 2 == 0 && blocks > cus;
+}
+
 hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStream_t s, const LaunchHook *hook)
 {
     // the chunk-start states: the caller's (the forward's fp32 series every 64 tokens, the
@@ -3133,8 +3152,12 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
         before(LA_KERNEL_INTER);                                                                               \
         if (!a.chunk_states)                                                                                   \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_states<KK, VV>), dim3(inter_blocks), dim3(256), 0, s, pf, w); \
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true>), dim3(inter_blocks), dim3(256), 0, s, p, w, \
-                           a.d_out, a.d_final, a.d_init);                                                      \
+        if (bwd_wide(inter_blocks, p))                                                                         \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true, 2>), dim3(inter_blocks / 2), dim3(384), 0, s, \
+                               p, w, a.d_out, a.d_final, a.d_init);                                            \
+        else                                                                                                   \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true>), dim3(inter_blocks), dim3(256), 0, s, p, w, \
+                               a.d_out, a.d_final, a.d_init);                                                  \
         after(LA_KERNEL_INTER);                                                                                \
         before(LA_KERNEL_BWD_INTRA);                                                                           \
         bool looped = false;                                                                                   \
@@ -3184,8 +3207,12 @@ hipError_t run_summary_bwd(const Prob &p, const Ws &w, const __bf16 *d_out, cons
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<KK, VV, true, false, 1>), dim3(grid), dim3(256), 0, s, p, w); \
         after(LA_KERNEL_INTRA);                                                                          \
         before(LA_KERNEL_INTER);                                                                         \
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, false>), dim3(blocks), dim3(256), 0, s, p, w, d_out, \
-                           d_end, d_start);                                                              \
+        if (bwd_wide(blocks, p))                                                                         \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, false, 2>), dim3(blocks / 2), dim3(384), 0, s, p, w, \
+                               d_out, d_end, d_start);                                                   \
+        else                                                                                             \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, false>), dim3(blocks), dim3(256), 0, s, p, w, \
+                               d_out, d_end, d_start);                                                   \
         after(LA_KERNEL_INTER);                                                                          \
         return hipGetLastError();                                                                        \
     }

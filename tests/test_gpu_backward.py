@@ -208,3 +208,9 @@ def test_backward_many_sequences_full_head_dims(hk, hv):
     # q/k head (the chain rule in the intra pass)
     lens = [(i * 97) % 300 for i in range(70)]
     check_bwd(custom_problem(lens, hk=hk, hv=hv, dk=128, dv=128, seed=222, with_state=True), 223)
+
+
+def test_backward_two_tile_reverse_pass():
+    # 5 sequences x 16 heads x 4 value tiles = 320 one-tile reverse-pass workgroups (more than
+    # one per CU, at most two): the reverse pass takes two 32-column tiles per workgroup
+    check_bwd(custom_problem((130, 64, 1, 300, 77), hk=4, hv=16, dk=128, dv=128, seed=224, with_state=True), 225)

@@ -118,3 +118,12 @@ def test_summary_bwd_slow_decay_every_chunk_matters():
     # (under the faster gates above only the first chunks reach it)
     p = custom_problem((2000, 300), hk=2, hv=4, dk=128, dv=128, seed=133, g_div=4096.0, beta_div=64.0)
     _check(p, seed=134)
+
+
+def test_summary_bwd_two_tile_workgroups():
+    # 5 spans x 16 heads x 4 value tiles = 320 one-tile workgroups, more than one per CU and at
+    # most two: the reverse pass runs with two 32-column tiles per workgroup (slow decay, so
+    # that every chunk reaches the start-state gradient)
+    p = custom_problem((130, 64, 1, 300, 77), hk=4, hv=16, dk=128, dv=128, seed=135, g_div=4096.0,
+                       beta_div=64.0)
+    _check(p, seed=136)
