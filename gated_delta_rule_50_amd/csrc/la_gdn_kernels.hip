@@ -1495,7 +1495,7 @@ template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false, bool NO
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     static_assert(!NOOUT || (CK && !SUMMARY && !GDP), "states only: the forward with the fp32 series");
-    static_assert(TP == 1 || (!SUMMARY && !CK && !GDP && !NOOUT), "two tiles per workgroup: the plain forward");
+    static_assert(TP == 1 || (!CK && !GDP && !NOOUT), "two tiles per workgroup: the plain forward or the summary");
     using C = InterCfg<K, V, SUMMARY, TP, NOOUT>;
     constexpr int NR = C::NR, NKS = C::NKS;
     constexpr int NEB = TP == 1 ? 3 : 2;                   // output-operand buffers
@@ -1527,7 +1527,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     x.tile = tile;
     x.vt0 = TP * tile;
     x.lane = threadIdx.x & 63;
-    x.ptile = SUMMARY && 32 * tile >= V;
+    x.ptile = SUMMARY && 32 * x.vt0 >= V;   // the workgroup's tiles are all P columns or all S columns
     // Roles by wave: with two 4-wave workgroups per CU the hardware puts a workgroup's waves
     // 0..3 on SIMDs s, s + 2, s + 1, s + 3 of a fixed cycle and, for most CUs, the other
     // workgroup's one step further on, so in the states-only forward the state roles go to
@@ -1978,6 +1978,17 @@ __global__ __launch_bounds__(256) void k_inter_sum(Prob p, Ws w)
     inter_body<K, V, true>(p, w);
 }
 
+// The summary with two 32-column tiles per workgroup (6 waves: four state waves, key half x
+// tile, and the two loaders, the raw k rows shared; 82 KiB of LDS at K = V = 128, one
+// workgroup per CU): for batches that need more than one round of the one-tile workgroups.
+template <int K, int V>
+__global__ __launch_bounds__(384) void k_inter_sum_wide(Prob p, Ws w)
+{
+    static_assert(InterCfg<K, V, true, 2>::THREADS == 384, "summary, two tiles: 6 waves");
+    static_assert((V / 32) % 2 == 0, "the S and P columns split into whole pairs of tiles");
+    inter_body<K, V, true, false, false, false, 2>(p, w);
+}
+
 // The Gated Delta Product's summary: k rows addressed by token and update.
 template <int K, int V>
 __global__ __launch_bounds__(256) void k_inter_sum_gdp(Prob p, Ws w)
@@ -2039,6 +2050,9 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
         const dim3 threads(InterCfg<K, V, SUMMARY>::THREADS);
         if (SUMMARY && p.nh > 1)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum_gdp<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else if (SUMMARY && (V / 32) % 2 == 0 && blocks > 2 * (p.intra_grid / 3))
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum_wide<K, V>), dim3((unsigned)(blocks / 2)),
+                               dim3(InterCfg<K, V, true, 2>::THREADS), 0, s, p, w);
         else if (SUMMARY)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else if (p.nh > 1)
