@@ -1495,7 +1495,7 @@ template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false, bool NO
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     static_assert(!NOOUT || (CK && !SUMMARY && !GDP), "states only: the forward with the fp32 series");
-    static_assert(TP == 1 || (!CK && !GDP && !NOOUT), "two tiles per workgroup: the plain forward or the summary");
+    static_assert(TP == 1 || (!GDP && (!CK || NOOUT)), "two tiles per workgroup: the plain forward, the summary or the states only");
     using C = InterCfg<K, V, SUMMARY, TP, NOOUT>;
     constexpr int NR = C::NR, NKS = C::NKS;
     constexpr int NEB = TP == 1 ? 3 : 2;                   // output-operand buffers
@@ -1536,7 +1536,7 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
     // the reverse pass).  The summary keeps waves 0 and 1 (the same remap measured 0-2 %
     // slower there).
     const int hwave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wave = NOOUT ? ((hwave & 1) << 1) | (hwave >> 1) : hwave;
+    const int wave = NOOUT && TP == 1 ? ((hwave & 1) << 1) | (hwave >> 1) : hwave;
     const int lane = x.lane, c = lane & 31, hh = lane >> 5;
     const int nch = x.nch;
 
@@ -1969,6 +1969,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 {
     static_assert(InterCfg<K, V, false, 1, true>::THREADS == 256, "states only: 4 waves");
     inter_body<K, V, false, true, false, true>(p, w);
+}
+
+// The states only with two 32-column tiles per workgroup (6 waves, 82 KiB, one per CU): for
+// batches that need more than one round of the CUs' one-tile workgroups.
+template <int K, int V>
+__global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_inter_states_wide(Prob p, Ws w)
+{
+    static_assert(InterCfg<K, V, false, 2, true>::THREADS == 384, "states only, two tiles: 6 waves");
+    inter_body<K, V, false, true, false, true, 2>(p, w);
 }
 
 template <int K, int V>
@@ -3164,7 +3173,10 @@ hipError_t run_backward(const Prob &p, const Ws &w_in, const BwdArgs &a, hipStre
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_intra<KK, VV, true, false, 2>), dim3(grid), dim3(256), 0, s, p, w); \
         after(LA_KERNEL_INTRA);                                                                                \
         before(LA_KERNEL_INTER);                                                                               \
-        if (!a.chunk_states)                                                                                   \
+        if (!a.chunk_states && (VV / 32) % 2 == 0 && inter_blocks > (unsigned)(p.intra_grid / 3))              \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_states_wide<KK, VV>), dim3(inter_blocks / 2), dim3(384), 0, s, \
+                               pf, w);                                                                         \
+        else if (!a.chunk_states)                                                                              \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_states<KK, VV>), dim3(inter_blocks), dim3(256), 0, s, pf, w); \
         if (bwd_wide(inter_blocks, p))                                                                         \
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_bwd_inter<KK, VV, true, 2>), dim3(inter_blocks / 2), dim3(384), 0, s, \
