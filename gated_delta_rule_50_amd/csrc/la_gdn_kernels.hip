@@ -22,8 +22,6 @@
 //
 // The kernels, all on the caller's stream:
 //   k_cu64      (int64 cu_seqlens only) the int32 copy the other kernels read
-//   k_sbwd_prep, k_sbwd  the summary's mirror for the state gradient (row norms and
-//               cu_seqlens validation, then the reverse recurrence token by token)
 //   k_sched     one workgroup, for more than 64 sequences: validates cu_seqlens,
 //               builds the chunk table and the longest-first order of sequences
 //               (for at most 64, every wave of k_intra maps its own chunks from
@@ -41,7 +39,16 @@
 //               series) and k_inter_gdp (Gated Delta Product: q and o rows mapped
 //               from update rows to tokens, k rows by token and update) and
 //               k_inter_sum_gdp (its summary); k_intra has a Gated Delta Product
-//               variant in the same way (k, v and beta rows by token and update)
+//               variant in the same way (k, v and beta rows by token and update).
+//               k_inter_wide and k_inter_sum_wide take two 32-column tiles per
+//               workgroup, for batches that need more rounds of the CUs
+//   backward    k_intra again (both operand sets), k_inter_states (the forward's
+//               recurrence again, the fp32 state at every chunk start; two-tile
+//               k_inter_states_wide), k_bwd_inter (the reverse chunk pass carrying the
+//               state gradient, also the summary's mirror for the state gradient),
+//               k_bwd_intra (per (chunk, head) or per (chunk, q/k head group): every
+//               gradient of the chunk's algebra) and k_bwd_qk (head-group sums and
+//               the row norms' chain rule, where k_bwd_intra does not do them)
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 for the bf16 products and v_mfma_f32_16x16x4_f32
 // for the fp32 block products of the triangular solve (lane layouts with the
@@ -2354,8 +2361,9 @@ __global__ __launch_bounds__(64 * (2 * TP + 2)) __attribute__((amdgpu_waves_per_
 // with E[t][s] = 2^(gam_t - gam_s) (s < t), and per token the gradients of beta and of the
 // chunk-local cumulative gate (every place gam enters: A, P, W, the output's 2^gam, the
 // state update's 2^(gam_n - gam) and 2^gam_n), summed back to g in reverse token order.
-// The q^ and k^ gradients go out per value head (fp32); k_bwd_qk sums each head group and
-// applies the row norms.  All products are bf16 MFMA with fp32 accumulation; each wave owns
+// The q^ and k^ gradients go out per value head (fp32) and k_bwd_qk sums each head group and
+// applies the row norms; with one value head per q/k head, or (GL) a whole head group per
+// workgroup, this kernel applies them itself.  All products are bf16 MFMA with fp32 accumulation; each wave owns
 // token tile (wave & 1) and the column tiles (wave >> 1) + 2 i of every 64-row result.  At
 // K = V = 128 the workgroup is 8 waves (two per SIMD, the only workgroup on its CU): waves w
 // and w + 4 split the K- and V-wide products by column tile and take the 64 x 64 ones
