@@ -69,6 +69,19 @@ def test_summary_small_k64():
     assert_summary(end, tr, ref)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_summary_two_tile_workgroups_all_head_dims(dk, dv):
+    # 70 spans x 2 heads x (K + V) / 32 tiles: more than two one-tile workgroups per CU, so
+    # the summary runs two 32-column tiles per workgroup (S and P column pairs)
+    lengths = [(i * 53) % 200 for i in range(70)]
+    p = custom_problem(lengths, hk=1, hv=2, dk=dk, dv=dv, seed=26, with_state=True, summary=True,
+                       g_div=512.0, beta_div=8.0)
+    note(f"summary two-tile workgroups K={dk} V={dv}")
+    end, tr = gpu_summary(p)
+    ref = Oracle(p).run_all(want_o=False, want_transition=True)
+    assert_summary(end, tr, ref)
+
+
 def test_empty_sequences_and_identity_transition():
     p = custom_problem((0, 5, 0, 70, 0), hk=1, hv=2, dk=64, dv=64, seed=25, with_state=True)
     note("empty sequences fwd")
