@@ -80,6 +80,15 @@ def test_summary_two_tile_workgroups_all_head_dims(dk, dv):
     end, tr = gpu_summary(p)
     ref = Oracle(p).run_all(want_o=False, want_transition=True)
     assert_summary(end, tr, ref)
+    # a span alone runs the one-tile workgroups: the same bits
+    cu = p.cu_seqlens.tolist()
+    for n in [1, 7, 69]:
+        sl = slice(cu[n], cu[n + 1])
+        alone = dataclasses.replace(p, name="alone", cu_seqlens=torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32),
+                                    k=p.k[sl].contiguous(), v=p.v[sl].contiguous(), g=p.g[sl].contiguous(),
+                                    beta=p.beta[sl].contiguous(), state=p.state[n:n + 1].clone())
+        ea, ta = gpu_summary(alone)
+        assert torch.equal(ea[0], end[n]) and torch.equal(ta[0], tr[n]), n
 
 
 def test_empty_sequences_and_identity_transition():
