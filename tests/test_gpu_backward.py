@@ -211,6 +211,20 @@ def test_backward_many_sequences_full_head_dims(hk, hv):
 
 
 def test_backward_two_tile_reverse_pass():
-    # 5 sequences x 16 heads x 4 value tiles = 320 one-tile reverse-pass workgroups (more than
-    # one per CU, at most two): the reverse pass takes two 32-column tiles per workgroup
-    check_bwd(custom_problem((130, 64, 1, 300, 77), hk=4, hv=16, dk=128, dv=128, seed=224, with_state=True), 225)
+    # 5 sequences x 16 heads x 4 value tiles = 320 one-tile workgroups of the states-only
+    # forward and the reverse pass, more than one per CU: both take two 32-column tiles per
+    # workgroup.  A sequence alone (64 workgroups, one tile each) gives the same bits.
+    p = custom_problem((130, 64, 1, 300, 77), hk=4, hv=16, dk=128, dv=128, seed=224, with_state=True)
+    got, _ = check_bwd(p, 225)
+    d_out, d_fin = upstream(p, 225)
+    cu = p.cu_seqlens.tolist()
+    for n in [0, 3]:
+        sl = slice(cu[n], cu[n + 1])
+        alone = Problem("alone", torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32), p.q[sl].contiguous(),
+                        p.k[sl].contiguous(), p.v[sl].contiguous(), p.g[sl].contiguous(), p.beta[sl].contiguous(),
+                        p.state[n:n + 1].clone())
+        note(f"bwd: sequence {n} alone")
+        c = gpu_bwd(alone, d_out[sl].contiguous(), d_fin[n:n + 1].contiguous())
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert torch.equal(c[name], got[name][sl]), (n, name)
+        assert torch.equal(c["d_init"][0], got["d_init"][n]), n
