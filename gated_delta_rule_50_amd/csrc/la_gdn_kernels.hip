@@ -1502,7 +1502,7 @@ template <int K, int V, bool SUMMARY, bool CK = false, bool GDP = false, bool NO
 __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
 {
     static_assert(!NOOUT || (CK && !SUMMARY && !GDP), "states only: the forward with the fp32 series");
-    static_assert(TP == 1 || (!GDP && (!CK || NOOUT)), "two tiles per workgroup: the plain forward, the summary or the states only");
+    static_assert(TP == 1 || !GDP, "two tiles per workgroup: not the Gated Delta Product");
     using C = InterCfg<K, V, SUMMARY, TP, NOOUT>;
     constexpr int NR = C::NR, NKS = C::NKS;
     constexpr int NEB = TP == 1 ? 3 : 2;                   // output-operand buffers
@@ -1705,14 +1705,17 @@ __device__ __forceinline__ void inter_body(const Prob &p, const Ws &w)
                 // 16 kk + 4 hh + e (slots e) and 16 kk + 8 + 4 hh + e (slots 4 + e)
                 const int64_t e = ck_base + (int64_t)kChunk * ci / p.ck_every;
                 if (e < p.ck_cap) {
-                    __bf16 *dst = static_cast<__bf16 *>(p.ck) + ((e * p.HV + x.h) * K) * V + 32 * x.tile + c;
 #pragma unroll
-                    for (int i = 0; i < NKS; ++i) {
-                        const int kk = t * NKS + i;
-                        const bf16x8 sv = __builtin_bit_cast(bf16x8, xS[kk * 64 + lane]);
+                    for (int tp = 0; tp < TP; ++tp) {
+                        __bf16 *dst = static_cast<__bf16 *>(p.ck) + ((e * p.HV + x.h) * K) * V + 32 * (x.vt0 + tp) + c;
 #pragma unroll
-                        for (int slot = 0; slot < 8; ++slot)
-                            dst[(int64_t)(16 * kk + 8 * (slot >> 2) + 4 * hh + (slot & 3)) * V] = sv[slot];
+                        for (int i = 0; i < NKS; ++i) {
+                            const int kk = t * NKS + i;
+                            const bf16x8 sv = __builtin_bit_cast(bf16x8, xS[(tp * 2 * NKS + kk) * 64 + lane]);
+#pragma unroll
+                            for (int slot = 0; slot < 8; ++slot)
+                                dst[(int64_t)(16 * kk + 8 * (slot >> 2) + 4 * hh + (slot & 3)) * V] = sv[slot];
+                        }
                     }
                 }
             }
@@ -1969,6 +1972,14 @@ __global__ __launch_bounds__(384) void k_inter_ck(Prob p, Ws w)
     inter_body<K, V, false, true>(p, w);
 }
 
+// The same with two 32-column tiles per workgroup (8 waves), on the plain forward's terms.
+template <int K, int V>
+__global__ __launch_bounds__(512) void k_inter_ck_wide(Prob p, Ws w)
+{
+    static_assert(InterCfg<K, V, false, 2>::THREADS == 512, "forward, two tiles: 8 waves");
+    inter_body<K, V, false, true, false, false, 2>(p, w);
+}
+
 // The backward's run of the forward: the fp32 state at every chunk start, no outputs, so no
 // output waves and no q or P^T buffers (4 waves, 63 KiB of LDS at K = V = 128: two per CU).
 template <int K, int V>
@@ -2073,6 +2084,9 @@ hipError_t launch_all(const Prob &p, const Ws &w, hipStream_t s, const LaunchHoo
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_sum<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else if (p.nh > 1)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_gdp<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
+        else if (p.ck_every > 0 && blocks > p.intra_grid / 3 && blocks <= 2 * (p.intra_grid / 3))
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck_wide<K, V>), dim3((unsigned)(blocks / 2)),
+                               dim3(InterCfg<K, V, false, 2>::THREADS), 0, s, p, w);
         else if (p.ck_every > 0)
             hipLaunchKernelGGL(HIP_KERNEL_NAME(k_inter_ck<K, V>), dim3((unsigned)blocks), threads, 0, s, p, w);
         else if (blocks > p.intra_grid / 3 && blocks <= 2 * (p.intra_grid / 3))

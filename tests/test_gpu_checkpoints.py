@@ -78,3 +78,29 @@ def test_series_varlen_h16_and_fused_transforms():
     ref = Oracle(q).run_all(checkpoint_every=128)
     assert_states(ck, ref["checkpoints"], TOL_STATE, "state series")
     assert_o_state(out, None, ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_series_two_tile_workgroups(dtype):
+    # 40 sequences x 2 value heads x 4 value tiles = 320 one-tile inter workgroups, more than
+    # one per CU and at most two: the forward with the series runs two 32-column tiles per
+    # workgroup.  Against the oracle, and sequences alone (one tile per workgroup) bit for bit.
+    lens = [(i * 53) % 300 + 1 for i in range(40)]
+    p = custom_problem(lens, hk=1, hv=2, dk=128, dv=128, seed=74, with_state=True)
+    note(f"series two-tile workgroups {dtype}")
+    out, fin, ck = fwd_ck(p, 64, dtype)
+    ref = Oracle(p).run_all(checkpoint_every=64)
+    assert_states(ck, ref["checkpoints"], TOL_STATE if dtype == torch.float32 else TOL_CK_BF16, "state series")
+    assert_o_state(out, fin, ref)
+    cu = p.cu_seqlens.tolist()
+    base = [0]
+    for L in lens:
+        base.append(base[-1] + -(-L // 64))
+    for n in [0, 9, 39]:
+        sl = slice(cu[n], cu[n + 1])
+        alone = type(p)("alone", torch.tensor([0, lens[n]], dtype=torch.int32), p.q[sl].contiguous(),
+                        p.k[sl].contiguous(), p.v[sl].contiguous(), p.g[sl].contiguous(), p.beta[sl].contiguous(),
+                        p.state[n:n + 1].clone())
+        oa, fa, ca = fwd_ck(alone, 64, dtype)
+        assert torch.equal(oa, out[sl]) and torch.equal(fa[0], fin[n]), n
+        assert torch.equal(ca, ck[base[n]:base[n + 1]]), n
