@@ -1,6 +1,7 @@
 """A seeded sweep of random shapes and options against the fp64 oracle: the forward (plain,
 with the fused gate and beta transforms, or with the state series), the span summary, the
-full backward and the summary's state-gradient mirror.  Each case draws its own sequence
+full backward, the summary's state-gradient mirror and the Gated Delta Product (forward and
+summary, 2 to 4 updates per token).  Each case draws its own sequence
 lengths (empty, single-token, partial-chunk, whole-chunk and multi-chunk sequences),
 head counts (grouped or not), head dims and initial state from a generator seeded by the
 case number, so that the kernel variants (one or two tiles per inter workgroup, grouped
@@ -17,7 +18,7 @@ import torch
 import gated_delta_rule_50_amd as la
 import oracle
 from oracle import Oracle, rel_l2
-from workloads import custom_problem, fused_problem
+from workloads import custom_problem, fused_problem, gdp_problem
 
 from gpu_helpers import TOL_STATE, assert_o_state, assert_rows_close, assert_states, assert_summary, f64, note
 
@@ -171,3 +172,29 @@ def test_random_summary_bwd(case):
     torch.cuda.synchronize()
     ref = oracle.backward(p, d_o=d_out.double().numpy(), d_final=d_end.double().numpy())["d_init"]
     _grads_close({"d_init": got}, {"d_init": ref}, ("d_init",), TOL_STATE)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_gated_delta_product(case):
+    rng = np.random.default_rng(9000 + case)
+    lens = _lengths(rng, int(rng.integers(1, 9)))
+    nh = int(rng.choice([2, 3, 4]))
+    hk, hv = _heads(rng, 8)
+    dk, dv = _dims(rng)
+    with_state = bool(rng.random() < 0.6)
+    summary = case % 4 == 3
+    # the summary on slow decay, so that its transitions stay well away from zero
+    p = gdp_problem(lens, nh, hk=hk, hv=hv, dk=dk, dv=dv, seed=9100 + case, with_state=with_state,
+                    summary=summary, g_div=4096.0 if summary else 1.0, beta_div=64.0 if summary else 1.0)
+    note(f"random gdp {case}: n={nh} summary={summary} lens={lens} HK={hk} HV={hv} K={dk} V={dv} state={with_state}")
+    g = p.to("cuda")
+    if summary:
+        end, tr = la.la_gdn_summary_ex(g.k, g.v, g.g, g.beta, g.cu_seqlens, start_state=g.state,
+                                       num_householder=nh)
+        torch.cuda.synchronize()
+        assert_summary(end, tr, Oracle(p).run_all(want_o=False, want_transition=True))
+    else:
+        out, fin, _ = la.la_gdn_fwd_ex(g.q, g.k, g.v, g.g, g.beta, g.cu_seqlens, initial_state=g.state,
+                                       num_householder=nh)
+        torch.cuda.synchronize()
+        assert_o_state(out, fin, Oracle(p).run_all())
